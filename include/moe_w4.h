@@ -1,0 +1,209 @@
+/*
+ * moe_w4.h -- C ABI of libmoe_w4.so: the mixture-of-experts layer of a
+ * single-model inference engine with 4-bit weights, for one AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The layer follows the page "Perplexity's Lily engine beats MLX by 35% on
+ * M5 Max" (the architecture paragraph): expert routing, a prefix scan over
+ * the expert histogram, a scatter of tokens into expert order and a tile
+ * block map are built on the GPU in one submission, then a grouped expert
+ * GEMM dequantises the 4-bit weights inside the kernel so that expanded
+ * 16-bit weights never reach memory.  SwiGLU and a routing-weighted combine
+ * finish the layer.
+ *
+ * Conventions (every entry point):
+ *  - Pointers named as device pointers must be device memory of the current
+ *    HIP device; everything is contiguous and row-major.  The caller owns
+ *    every buffer, workspaces included; the library allocates nothing, frees
+ *    nothing, never synchronises and never reads device memory on the host.
+ *  - `stream` is a hipStream_t (NULL = the legacy default stream).  Calls only
+ *    enqueue work on it and return; results are ready when the stream is.
+ *  - Errors: a negative moe_status.  Argument errors are detected on the host
+ *    before anything is enqueued, and leave every output untouched; a failed
+ *    launch returns MOE_ERR_HIP.  moe_last_error() gives a thread-local
+ *    message for the last failing call of the calling thread.  Device faults
+ *    surface at the caller's next synchronisation.
+ *  - T = 0 is valid and enqueues nothing.
+ *  - Supported sizes: 1 <= E <= 256, 1 <= top_k <= min(E, 16), group size
+ *    G in {32, 64, 128}; H % 256 == 0, I % 128 == 0, H % G == 0, I % G == 0;
+ *    T * top_k < 2^31.  Pointers to packed weights, activations, h, outputs
+ *    and workspaces must be 16-byte aligned.
+ *  - Logits may contain -inf (never selected while top_k finite logits
+ *    exist); NaN logits give unspecified routing.
+ *  - Activations and the hidden vector are carried in fp16 inside the
+ *    grouped GEMM: |x| and |h| must stay below 65504.
+ *
+ * Notation: T tokens, H hidden size, I expert intermediate size, E experts,
+ * top_k experts per token, G quantisation group size, P = T * top_k
+ * (token, choice) pairs, pair p = t * top_k + j.
+ */
+#ifndef MOE_W4_H
+#define MOE_W4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_NULL = -1,        /* a required pointer is NULL */
+  MOE_ERR_SHAPE = -2,       /* sizes negative or inconsistent */
+  MOE_ERR_UNSUPPORTED = -3, /* valid but outside the supported sizes above */
+  MOE_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned */
+  MOE_ERR_WORKSPACE = -5,   /* workspace smaller than the query returns */
+  MOE_ERR_HIP = -6          /* a HIP launch failed */
+} moe_status;
+
+/* Static description of a status code (never NULL). */
+const char* moe_status_string(int status);
+/* Thread-local detail of the calling thread's last failed call ("" if none). */
+const char* moe_last_error(void);
+/* Library version string. */
+const char* moe_version(void);
+
+/* Layer sizes. */
+typedef struct {
+  int32_t T, H, I, E, top_k, group_size;
+} moe_dims;
+
+/* One bank of 4-bit weights for all E experts, device pointers.
+ *  qweight: uint32 [E][N][K/8]; code k' = 8w + j of row n is bits 4j..4j+3
+ *           of word w (lowest nibble first), an unsigned value q in 0..15.
+ *  scales, biases: bf16 bits [E][N][K/G]; group g covers k' in [gG, gG+G).
+ *  Weight W[e][n][k'] = q * scale[e][n][k'/G] + bias[e][n][k'/G].
+ * gate and up banks have N = I, K = H; the down bank has N = H, K = I. */
+typedef struct {
+  const uint32_t* qweight;
+  const uint16_t* scales;
+  const uint16_t* biases;
+} moe_w4_bank;
+
+/* One layer's weights (device pointers). */
+typedef struct {
+  moe_dims dims;
+  const uint16_t* router_weight; /* bf16 [E][H], or NULL when logits are given */
+  moe_w4_bank gate, up, down;
+} moe_layer;
+
+/* ------------------------------------------------------------------ S0, S1 --
+ * Expert routing.
+ * If router_weight != NULL, first computes the router linear layer
+ *   logits[t][e] = sum_h x[t][h] * router_weight[e][h]
+ * (bf16 inputs, fp32 accumulation, no bias) into `logits`; otherwise `logits`
+ * is an input and `x` may be NULL.  Then, per token, selects the top_k
+ * experts by (logit descending, expert index ascending) into
+ * topk_ids[t][j] (j = 0 is the largest) and writes the combine weights
+ *   topk_weights[t][j] = exp(l_j - l_0) / sum_i exp(l_i - l_0)   (fp32),
+ * the softmax over the top_k selected logits.
+ * Device pointers: x bf16 [T][H]; router_weight bf16 [E][H]; logits fp32
+ * [T][E]; topk_ids int32 [T][top_k]; topk_weights fp32 [T][top_k]. */
+int moe_route(const uint16_t* x, const uint16_t* router_weight, float* logits, int32_t T,
+              int32_t H, int32_t E, int32_t top_k, int32_t* topk_ids, float* topk_weights,
+              void* stream);
+
+/* ----------------------------------------------------------------- S2 - S5 --
+ * Upper bound on the number of tiles of the block map (host-only):
+ *   floor(P / block_m) + min(E, P). */
+int64_t moe_max_blocks(int32_t T, int32_t top_k, int32_t E, int32_t block_m);
+/* Bytes of workspace moe_build_blocks needs (host-only). */
+size_t moe_build_blocks_workspace_bytes(int32_t T, int32_t top_k, int32_t E);
+
+/* Expert histogram, prefix scan, scatter and tile block map, all on the GPU
+ * with no host round trip.  Input topk_ids int32 [T][top_k] (values < E).
+ * Outputs (device, int32):
+ *   counts[E]          number of pairs routed to each expert
+ *   offsets[E + 1]     exclusive prefix sum of counts; offsets[E] = P
+ *   sorted_pairs[P]    slot -> pair; the slots of expert e are
+ *                      [offsets[e], offsets[e+1]) in increasing pair order
+ *                      (a stable counting sort, deterministic)
+ *   pair_slot[P]       pair -> slot (the inverse permutation)
+ *   blocks[max][3]     tiles (expert, first slot, rows), experts ascending,
+ *                      rows <= block_m, none for empty experts; entries past
+ *                      num_blocks are unspecified
+ *   num_blocks[1]      number of tiles written
+ * block_m >= 1.  workspace: device, >= moe_build_blocks_workspace_bytes. */
+int moe_build_blocks(const int32_t* topk_ids, int32_t T, int32_t top_k, int32_t E,
+                     int32_t block_m, int32_t* counts, int32_t* offsets, int32_t* sorted_pairs,
+                     int32_t* pair_slot, int32_t* blocks, int32_t* num_blocks, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------ S6, S7 --
+ * Grouped W4 GEMM over the block map, dequantisation fused (the packed codes
+ * are expanded in registers only).
+ *
+ * MOE_GEMM_GATE_UP_SWIGLU: for every slot s of every tile (expert e), with
+ *   token t = sorted_pairs[s] / top_k,
+ *     g = W_gate[e] x[t],  u = W_up[e] x[t],  out[s][n] = silu(g_n) * u_n
+ *   silu(z) = z / (1 + exp(-z)); a = x bf16 [T][K]; out = h fp16 [P][N];
+ *   N = I, K = H; bank0 = gate, bank1 = up.
+ * MOE_GEMM_DOWN: for every slot s of every tile (expert e), pair
+ *   p = sorted_pairs[s],
+ *     out[s][n] = topk_weights[p] * (W_down[e] h[s])_n
+ *   a = h fp16 [P][K] (slot order); out = y_sorted fp32 [P][N]; N = H,
+ *   K = I; bank0 = down; bank1 unused.
+ * T <= 8 runs a bandwidth-bound GEMV-style kernel that reads each touched
+ * expert's packed rows once; larger T runs fp16 MFMA tiles of block_m rows
+ * (block_m in {32, 64, 128}, equal to the block map's).  Slots outside every
+ * tile are not written.  workspace: device, >=
+ * moe_w4_grouped_gemm_workspace_bytes(args). */
+typedef enum { MOE_GEMM_GATE_UP_SWIGLU = 0, MOE_GEMM_DOWN = 1 } moe_gemm_mode;
+
+typedef struct {
+  int32_t mode;                /* moe_gemm_mode */
+  int32_t T, top_k, E;         /* P = T * top_k rows */
+  int32_t N, K, group_size;
+  int32_t block_m;
+  const void* a;               /* see the modes above */
+  moe_w4_bank bank0, bank1;
+  const int32_t* sorted_pairs; /* [P] */
+  const float* topk_weights;   /* [P], MOE_GEMM_DOWN only */
+  const int32_t* blocks;       /* [max_blocks][3] */
+  const int32_t* num_blocks;   /* [1] */
+  void* out;
+  void* workspace;
+  size_t workspace_bytes;
+} moe_w4_gemm_args;
+
+size_t moe_w4_grouped_gemm_workspace_bytes(const moe_w4_gemm_args* args);
+int moe_w4_grouped_gemm(const moe_w4_gemm_args* args, void* stream);
+
+/* -------------------------------------------------------------- whole layer --
+ * y[t] = sum_j topk_weights[t][j] * W_down[e] (silu(W_gate[e] x[t]) * W_up[e] x[t]),
+ * e = topk_ids[t][j], summed in j order in fp32 (S8, deterministic).
+ * Runs S0 (when layer->router_weight != NULL; router_logits must then be
+ * NULL) or takes router_logits fp32 [T][E], then S1 - S8 on one stream with
+ * no host round trip.  x bf16 [T][H]; y fp32 [T][H] (overwritten).
+ * info (host struct, may be NULL) receives the block size used and device
+ * pointers into the workspace where the routing structures were written.
+ * workspace: device, >= moe_ffn_workspace_bytes(&layer->dims, has_router). */
+typedef struct {
+  int32_t block_m;
+  int32_t path;                 /* 0 = MFMA tiles, 1 = GEMV (T <= 8) */
+  const float* logits;          /* [T][E] (the input, or the router output) */
+  const int32_t* topk_ids;      /* [T][top_k] */
+  const float* topk_weights;    /* [T][top_k] */
+  const int32_t* counts;        /* [E] */
+  const int32_t* offsets;       /* [E + 1] */
+  const int32_t* sorted_pairs;  /* [P] */
+  const int32_t* pair_slot;     /* [P] */
+  const int32_t* blocks;        /* [max_blocks][3] */
+  const int32_t* num_blocks;    /* [1] */
+  const uint16_t* h;            /* fp16 [P][I], slot order */
+  const float* y_sorted;        /* fp32 [P][H], slot order, weighted */
+} moe_route_info;
+
+/* Tile rows moe_ffn_forward uses for these sizes (host-only). */
+int32_t moe_ffn_block_m(const moe_dims* dims);
+size_t moe_ffn_workspace_bytes(const moe_dims* dims, int32_t has_router);
+int moe_ffn_forward(const moe_layer* layer, const uint16_t* x, const float* router_logits,
+                    float* y, moe_route_info* info, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_W4_H */

@@ -1,0 +1,209 @@
+"""torch-tensor wrappers over the C entry points of libmoe_w4.so.
+
+Argument marshalling only: tensors are checked for device, dtype and
+contiguity, outputs and workspaces are allocated with torch, and the call is
+enqueued on torch's current stream.  Every step of the layer runs in the HIP
+kernels of the library.
+"""
+
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import torch
+
+from . import _lib
+from ._lib import MOE_GEMM_DOWN, MOE_GEMM_GATE_UP_SWIGLU, Bank, Dims, GemmArgs, Layer, RouteInfo
+
+__all__ = ["route", "build_blocks", "w4_grouped_gemm", "ffn_forward", "ffn_workspace_bytes",
+           "ffn_block_m", "max_blocks", "MOE_GEMM_GATE_UP_SWIGLU", "MOE_GEMM_DOWN"]
+
+
+def _L():
+    return _lib.load()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dev(t: Optional[torch.Tensor], name: str, dtype=None) -> int:
+    if t is None:
+        return 0
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _bank(b, name: str) -> Bank:
+    return Bank(_dev(b.qweight, f"{name}.qweight", torch.int32),
+                _dev(b.scales, f"{name}.scales", torch.bfloat16),
+                _dev(b.biases, f"{name}.biases", torch.bfloat16))
+
+
+def max_blocks(T: int, top_k: int, E: int, block_m: int) -> int:
+    return int(_L().moe_max_blocks(T, top_k, E, block_m))
+
+
+def route(top_k: int, logits: Optional[torch.Tensor] = None, x: Optional[torch.Tensor] = None,
+          router_weight: Optional[torch.Tensor] = None):
+    """S0 (when ``router_weight`` is given) and S1.  Returns
+    ``(topk_ids int32 [T, k], topk_weights fp32 [T, k], logits fp32 [T, E])``."""
+    if router_weight is not None:
+        T, H = x.shape
+        E = router_weight.shape[0]
+        logits = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    else:
+        T, E = logits.shape
+        H = 0
+    dev = logits.device
+    ids = torch.empty((T, top_k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, top_k), dtype=torch.float32, device=dev)
+    st = _L().moe_route(_dev(x, "x", torch.bfloat16), _dev(router_weight, "router_weight", torch.bfloat16),
+                        _dev(logits, "logits", torch.float32), T, H, E, top_k,
+                        ids.data_ptr(), w.data_ptr(), _stream())
+    _lib.check(st, "moe_route")
+    return ids, w, logits
+
+
+def build_blocks(topk_ids: torch.Tensor, E: int, block_m: int) -> dict:
+    """S2-S5.  Returns counts, offsets, sorted_pairs, pair_slot, blocks
+    ``[max_blocks, 3]`` (rows past num_blocks unspecified) and num_blocks
+    (a 1-element device tensor)."""
+    T, k = topk_ids.shape
+    P = T * k
+    dev = topk_ids.device
+    mb = max(1, max_blocks(T, k, E, block_m))
+    out = dict(
+        counts=torch.empty(E, dtype=torch.int32, device=dev),
+        offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+        sorted_pairs=torch.empty(P, dtype=torch.int32, device=dev),
+        pair_slot=torch.empty(P, dtype=torch.int32, device=dev),
+        blocks=torch.empty((mb, 3), dtype=torch.int32, device=dev),
+        num_blocks=torch.zeros(1, dtype=torch.int32, device=dev),
+    )
+    wsb = int(_L().moe_build_blocks_workspace_bytes(T, k, E))
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    st = _L().moe_build_blocks(_dev(topk_ids, "topk_ids", torch.int32), T, k, E, block_m,
+                               out["counts"].data_ptr(), out["offsets"].data_ptr(),
+                               out["sorted_pairs"].data_ptr(), out["pair_slot"].data_ptr(),
+                               out["blocks"].data_ptr(), out["num_blocks"].data_ptr(),
+                               ws.data_ptr(), wsb, _stream())
+    _lib.check(st, "moe_build_blocks")
+    return out
+
+
+def w4_grouped_gemm(mode: int, a: torch.Tensor, bank0, bank1, sorted_pairs: torch.Tensor,
+                    blocks: torch.Tensor, num_blocks: torch.Tensor, *, T: int, top_k: int, E: int,
+                    group_size: int, block_m: int, topk_weights: Optional[torch.Tensor] = None,
+                    out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """S6 (mode MOE_GEMM_GATE_UP_SWIGLU: a = x bf16 [T, H], returns h fp16
+    [P, I]) or S7 (MOE_GEMM_DOWN: a = h fp16 [P, I], returns y_sorted fp32
+    [P, H]).  Slots outside every tile are left as they were in ``out``."""
+    gate_up = mode == MOE_GEMM_GATE_UP_SWIGLU
+    E_, N, K8 = bank0.qweight.shape
+    K = K8 * 8
+    P = T * top_k
+    if out is None:
+        out = torch.empty((P, N), dtype=torch.float16 if gate_up else torch.float32, device=a.device)
+    args = GemmArgs(mode=mode, T=T, top_k=top_k, E=E, N=N, K=K, group_size=group_size,
+                    block_m=block_m,
+                    a=_dev(a, "a", torch.bfloat16 if gate_up else torch.float16),
+                    bank0=_bank(bank0, "bank0"),
+                    bank1=_bank(bank1, "bank1") if bank1 is not None else Bank(0, 0, 0),
+                    sorted_pairs=_dev(sorted_pairs, "sorted_pairs", torch.int32),
+                    topk_weights=_dev(topk_weights, "topk_weights", torch.float32),
+                    blocks=_dev(blocks, "blocks", torch.int32),
+                    num_blocks=_dev(num_blocks, "num_blocks", torch.int32),
+                    out=_dev(out, "out", torch.float16 if gate_up else torch.float32))
+    wsb = int(_L().moe_w4_grouped_gemm_workspace_bytes(ctypes.byref(args)))
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=a.device)
+    args.workspace = ws.data_ptr()
+    args.workspace_bytes = wsb
+    _lib.check(_L().moe_w4_grouped_gemm(ctypes.byref(args), _stream()), "moe_w4_grouped_gemm")
+    return out
+
+
+def _dims(layer, T: int) -> Dims:
+    return Dims(T, layer.H, layer.I, layer.E, layer.k, layer.G)
+
+
+def ffn_block_m(layer, T: Optional[int] = None) -> int:
+    d = _dims(layer, layer.T if T is None else T)
+    return int(_L().moe_ffn_block_m(ctypes.byref(d)))
+
+
+def ffn_workspace_bytes(layer, T: Optional[int] = None) -> int:
+    d = _dims(layer, layer.T if T is None else T)
+    return int(_L().moe_ffn_workspace_bytes(ctypes.byref(d), int(layer.router_weight is not None)))
+
+
+def make_layer_struct(layer, T: int) -> Layer:
+    return Layer(_dims(layer, T),
+                 _dev(layer.router_weight, "router_weight", torch.bfloat16),
+                 _bank(layer.gate, "gate"), _bank(layer.up, "up"), _bank(layer.down, "down"))
+
+
+def ffn_forward(layer, x: Optional[torch.Tensor] = None, logits: Optional[torch.Tensor] = None,
+                y: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                info: bool = False):
+    """The whole layer (S0/S1-S8) for a ``synth.MoELayer`` whose tensors are on
+    the device.  ``x`` and ``logits`` default to the layer's own.  Returns y
+    fp32 [T, H], plus a dict of routing-structure views into the workspace
+    when ``info`` is true."""
+    x = layer.x if x is None else x
+    T, H = x.shape
+    if layer.router_weight is None and logits is None:
+        logits = layer.logits
+    if y is None:
+        y = torch.empty((T, H), dtype=torch.float32, device=x.device)
+    wsb = ffn_workspace_bytes(layer, T)
+    if workspace is None:
+        workspace = torch.empty(max(wsb, 1), dtype=torch.uint8, device=x.device)
+    if workspace.numel() < wsb:
+        raise ValueError("workspace too small")
+    lay = make_layer_struct(layer, T)
+    ri = RouteInfo()
+    st = _L().moe_ffn_forward(ctypes.byref(lay), _dev(x, "x", torch.bfloat16),
+                              _dev(logits, "logits", torch.float32) if layer.router_weight is None else 0,
+                              _dev(y, "y", torch.float32), ctypes.byref(ri),
+                              _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream())
+    _lib.check(st, "moe_ffn_forward")
+    if not info:
+        return y
+    return y, _info_views(ri, workspace, layer, T, logits)
+
+
+def _info_views(ri: RouteInfo, ws: torch.Tensor, layer, T: int, logits) -> dict:
+    base = ws.data_ptr()
+    P = T * layer.k
+    mb = max(1, max_blocks(T, layer.k, layer.E, ri.block_m))
+
+    def view(ptr, numel, dtype, shape):
+        if ptr == 0 or numel == 0:
+            return torch.empty(shape, dtype=dtype, device=ws.device)
+        off = ptr - base
+        nbytes = numel * torch.empty((), dtype=dtype).element_size()
+        return ws[off:off + nbytes].view(dtype).reshape(shape)
+
+    out = dict(
+        block_m=ri.block_m, path=ri.path,
+        topk_ids=view(ri.topk_ids, P, torch.int32, (T, layer.k)),
+        topk_weights=view(ri.topk_weights, P, torch.float32, (T, layer.k)),
+        counts=view(ri.counts, layer.E, torch.int32, (layer.E,)),
+        offsets=view(ri.offsets, layer.E + 1, torch.int32, (layer.E + 1,)),
+        sorted_pairs=view(ri.sorted_pairs, P, torch.int32, (P,)),
+        pair_slot=view(ri.pair_slot, P, torch.int32, (P,)),
+        blocks=view(ri.blocks, mb * 3, torch.int32, (mb, 3)),
+        num_blocks=view(ri.num_blocks, 1, torch.int32, (1,)),
+        h=view(ri.h, P * layer.I, torch.float16, (P, layer.I)),
+        y_sorted=view(ri.y_sorted, P * layer.H, torch.float32, (P, layer.H)),
+    )
+    out["logits"] = (view(ri.logits, T * layer.E, torch.float32, (T, layer.E))
+                     if layer.router_weight is not None else logits)
+    return out

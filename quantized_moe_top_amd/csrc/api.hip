@@ -1,0 +1,312 @@
+// api.hip -- host side of libmoe_w4.so: the C entry points declared in
+// include/moe_w4.h.  Every argument is checked on the host before anything
+// is enqueued; kernels are then enqueued on the caller's stream, in order,
+// with no synchronisation and no device-to-host copy (page "Perplexity's
+// Lily engine beats MLX by 35% on M5 Max", architecture paragraph: the
+// routing steps stay in one GPU submission).
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "internal.h"
+
+namespace {
+
+thread_local char g_error[512];
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_error, sizeof g_error, fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_error[0] = 0;
+  return MOE_OK;
+}
+
+int hip_status(hipError_t err, const char* where) {
+  if (err == hipSuccess) return ok();
+  return fail(MOE_ERR_HIP, "%s: %s", where, hipGetErrorString(err));
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+size_t round_up(size_t x) { return (x + 255) & ~(size_t)255; }
+
+int64_t max_blocks(int64_t P, int E, int block_m) {
+  if (P <= 0 || block_m <= 0) return 0;
+  return P / block_m + (P < E ? P : E);
+}
+
+// Checks shared by every entry point: counts and routing sizes.
+int check_routing(int64_t T, int64_t E, int64_t k) {
+  if (T < 0 || E < 1 || k < 1) return fail(MOE_ERR_SHAPE, "need T >= 0, E >= 1, top_k >= 1");
+  if (E > 256) return fail(MOE_ERR_UNSUPPORTED, "E = %lld > 256", (long long)E);
+  if (k > E || k > 16) return fail(MOE_ERR_UNSUPPORTED, "top_k = %lld exceeds min(E, 16)", (long long)k);
+  if (T * k >= (int64_t)1 << 31) return fail(MOE_ERR_UNSUPPORTED, "T * top_k >= 2^31");
+  return MOE_OK;
+}
+
+int check_bank(const moe_w4_bank& b, const char* name) {
+  if (!b.qweight || !b.scales || !b.biases) return fail(MOE_ERR_NULL, "%s bank has a NULL pointer", name);
+  if (!aligned16(b.qweight)) return fail(MOE_ERR_ALIGN, "%s qweight not 16-byte aligned", name);
+  return MOE_OK;
+}
+
+int check_group(int64_t G, int64_t K, const char* what) {
+  if (G != 32 && G != 64 && G != 128) return fail(MOE_ERR_UNSUPPORTED, "group size %lld not in {32, 64, 128}", (long long)G);
+  if (K % G) return fail(MOE_ERR_SHAPE, "%s = %lld not a multiple of the group size", what, (long long)K);
+  return MOE_OK;
+}
+
+int gemm_block_ok(int T, int block_m) {
+  if (block_m < 1) return fail(MOE_ERR_SHAPE, "block_m must be >= 1");
+  if (T > moe::kGemvMaxTokens && block_m != 32 && block_m != 64 && block_m != 128)
+    return fail(MOE_ERR_UNSUPPORTED, "block_m = %d not in {32, 64, 128}", block_m);
+  return MOE_OK;
+}
+
+size_t gemm_workspace(int mode, int64_t T, int64_t K) {
+  return mode == MOE_GEMM_GATE_UP_SWIGLU ? round_up((size_t)T * K * 2) : 0;
+}
+
+// Workspace layout of moe_ffn_forward.
+struct FfnLayout {
+  size_t logits, ids, w, counts, offsets, sorted_pairs, pair_slot, blocks, num_blocks, scratch,
+      xh, h, y_sorted, total;
+};
+
+FfnLayout ffn_layout(const moe_dims& d, bool has_router, int block_m) {
+  const size_t T = d.T, H = d.H, I = d.I, E = d.E, P = (size_t)d.T * d.top_k;
+  FfnLayout L{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += round_up(bytes);
+    return at;
+  };
+  L.logits = take(has_router ? T * E * 4 : 0);
+  L.ids = take(P * 4);
+  L.w = take(P * 4);
+  L.counts = take(E * 4);
+  L.offsets = take((E + 1) * 4);
+  L.sorted_pairs = take(P * 4);
+  L.pair_slot = take(P * 4);
+  L.blocks = take((size_t)max_blocks((int64_t)P, d.E, block_m) * 12);
+  L.num_blocks = take(4);
+  L.scratch = take((size_t)moe::build_blocks_chunks((int64_t)P) * E * 4);
+  L.xh = take(T * H * 2);
+  L.h = take(P * I * 2);
+  L.y_sorted = take(P * H * 4);
+  L.total = o;
+  return L;
+}
+
+int check_dims(const moe_dims* d) {
+  if (!d) return fail(MOE_ERR_NULL, "dims is NULL");
+  int st = check_routing(d->T, d->E, d->top_k);
+  if (st) return st;
+  if (d->H <= 0 || d->I <= 0) return fail(MOE_ERR_SHAPE, "H and I must be positive");
+  if (d->H % 256) return fail(MOE_ERR_UNSUPPORTED, "H = %d not a multiple of 256", d->H);
+  if (d->I % 128) return fail(MOE_ERR_UNSUPPORTED, "I = %d not a multiple of 128", d->I);
+  if ((st = check_group(d->group_size, d->H, "H"))) return st;
+  if ((st = check_group(d->group_size, d->I, "I"))) return st;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "a required pointer is NULL";
+    case MOE_ERR_SHAPE: return "sizes negative or inconsistent";
+    case MOE_ERR_UNSUPPORTED: return "sizes outside the supported range";
+    case MOE_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+const char* moe_last_error(void) { return g_error; }
+
+const char* moe_version(void) { return "moe_w4 0.1 gfx950"; }
+
+int moe_route(const uint16_t* x, const uint16_t* router_weight, float* logits, int32_t T,
+              int32_t H, int32_t E, int32_t top_k, int32_t* topk_ids, float* topk_weights,
+              void* stream) {
+  int st = check_routing(T, E, top_k);
+  if (st) return st;
+  if (T == 0) return ok();  // empty tensors may carry NULL data pointers
+  if (!logits || !topk_ids || !topk_weights) return fail(MOE_ERR_NULL, "logits/topk_ids/topk_weights NULL");
+  if (router_weight) {
+    if (!x) return fail(MOE_ERR_NULL, "x is NULL while router_weight is given");
+    if (H <= 0 || H % 16) return fail(MOE_ERR_UNSUPPORTED, "H = %d not a positive multiple of 16", H);
+    if (!aligned16(x) || !aligned16(router_weight)) return fail(MOE_ERR_ALIGN, "x or router_weight not 16-byte aligned");
+  }
+  hipStream_t s = (hipStream_t)stream;
+  if (router_weight) {
+    hipError_t err = moe::launch_router_gemm(x, router_weight, logits, T, H, E, s);
+    if (err != hipSuccess) return hip_status(err, "router_gemm");
+  }
+  return hip_status(moe::launch_topk(logits, T, E, top_k, topk_ids, topk_weights, s), "topk");
+}
+
+int64_t moe_max_blocks(int32_t T, int32_t top_k, int32_t E, int32_t block_m) {
+  return max_blocks((int64_t)T * top_k, E, block_m);
+}
+
+size_t moe_build_blocks_workspace_bytes(int32_t T, int32_t top_k, int32_t E) {
+  const int64_t P = (int64_t)(T > 0 ? T : 0) * (top_k > 0 ? top_k : 0);
+  return round_up((size_t)moe::build_blocks_chunks(P) * (size_t)(E > 0 ? E : 0) * 4);
+}
+
+int moe_build_blocks(const int32_t* topk_ids, int32_t T, int32_t top_k, int32_t E,
+                     int32_t block_m, int32_t* counts, int32_t* offsets, int32_t* sorted_pairs,
+                     int32_t* pair_slot, int32_t* blocks, int32_t* num_blocks, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  int st = check_routing(T, E, top_k);
+  if (st) return st;
+  if (block_m < 1) return fail(MOE_ERR_SHAPE, "block_m must be >= 1");
+  if (T == 0) return ok();
+  if (!topk_ids || !counts || !offsets || !sorted_pairs || !pair_slot || !blocks || !num_blocks)
+    return fail(MOE_ERR_NULL, "an input or output pointer is NULL");
+  const size_t need = moe_build_blocks_workspace_bytes(T, top_k, E);
+  if (need && !workspace) return fail(MOE_ERR_NULL, "workspace is NULL");
+  if (workspace_bytes < need) return fail(MOE_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
+  return hip_status(moe::launch_build_blocks(topk_ids, T * top_k, E, block_m, counts, offsets,
+                                             sorted_pairs, pair_slot, blocks, num_blocks,
+                                             (int32_t*)workspace, (hipStream_t)stream),
+                    "build_blocks");
+}
+
+size_t moe_w4_grouped_gemm_workspace_bytes(const moe_w4_gemm_args* a) {
+  if (!a || a->T <= 0 || a->K <= 0) return 0;
+  return gemm_workspace(a->mode, a->T, a->K);
+}
+
+int moe_w4_grouped_gemm(const moe_w4_gemm_args* a, void* stream) {
+  if (!a) return fail(MOE_ERR_NULL, "args is NULL");
+  if (a->mode != MOE_GEMM_GATE_UP_SWIGLU && a->mode != MOE_GEMM_DOWN)
+    return fail(MOE_ERR_SHAPE, "unknown mode %d", a->mode);
+  const bool gate_up = a->mode == MOE_GEMM_GATE_UP_SWIGLU;
+  int st = check_routing(a->T, a->E, a->top_k);
+  if (st) return st;
+  if (a->N <= 0 || a->K <= 0) return fail(MOE_ERR_SHAPE, "N and K must be positive");
+  if ((st = check_group(a->group_size, a->K, "K"))) return st;
+  if (a->K % 64) return fail(MOE_ERR_UNSUPPORTED, "K = %d not a multiple of 64", a->K);
+  if (a->N % (gate_up ? 128 : 256))
+    return fail(MOE_ERR_UNSUPPORTED, "N = %d not a multiple of %d", a->N, gate_up ? 128 : 256);
+  if ((st = gemm_block_ok(a->T, a->block_m))) return st;
+  if (a->T == 0) return ok();
+  if (!a->a || !a->sorted_pairs || !a->blocks || !a->num_blocks || !a->out)
+    return fail(MOE_ERR_NULL, "a/sorted_pairs/blocks/num_blocks/out NULL");
+  if (!gate_up && !a->topk_weights) return fail(MOE_ERR_NULL, "topk_weights NULL");
+  if ((st = check_bank(a->bank0, gate_up ? "gate" : "down"))) return st;
+  if (gate_up && (st = check_bank(a->bank1, "up"))) return st;
+  if (!aligned16(a->a) || !aligned16(a->out)) return fail(MOE_ERR_ALIGN, "a or out not 16-byte aligned");
+  const size_t need = gemm_workspace(a->mode, a->T, a->K);
+  if (need && (!a->workspace || !aligned16(a->workspace)))
+    return fail(a->workspace ? MOE_ERR_ALIGN : MOE_ERR_NULL, "workspace NULL or misaligned");
+  if (a->workspace_bytes < need) return fail(MOE_ERR_WORKSPACE, "workspace %zu < %zu bytes", a->workspace_bytes, need);
+  hipStream_t s = (hipStream_t)stream;
+  moe::GemmArgs g{a->mode, a->T, a->top_k, a->E, a->N, a->K, a->group_size, a->block_m,
+                  (const moe::half_t*)a->a, a->bank0, a->bank1, a->sorted_pairs,
+                  a->topk_weights, a->blocks, a->num_blocks, a->out};
+  if (gate_up) {
+    hipError_t err = moe::launch_stage_x((const uint16_t*)a->a, (moe::half_t*)a->workspace,
+                                         (int64_t)a->T * a->K, s);
+    if (err != hipSuccess) return hip_status(err, "stage_x");
+    g.a = (const moe::half_t*)a->workspace;
+  }
+  const hipError_t err = a->T <= moe::kGemvMaxTokens ? moe::launch_w4_gemv(g, s) : moe::launch_w4_mfma(g, s);
+  return hip_status(err, "w4_grouped_gemm");
+}
+
+int32_t moe_ffn_block_m(const moe_dims* d) {
+  if (!d || d->E <= 0) return 0;
+  if (d->T <= moe::kGemvMaxTokens) return moe::kGemvMaxTokens;
+  const int64_t avg = (int64_t)d->T * d->top_k / d->E;
+  return avg <= 16 ? 32 : avg <= 64 ? 64 : 128;
+}
+
+size_t moe_ffn_workspace_bytes(const moe_dims* d, int32_t has_router) {
+  if (!d || check_dims(d) != MOE_OK) return 0;
+  return ffn_layout(*d, has_router != 0, moe_ffn_block_m(d)).total;
+}
+
+int moe_ffn_forward(const moe_layer* layer, const uint16_t* x, const float* router_logits,
+                    float* y, moe_route_info* info, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  if (!layer) return fail(MOE_ERR_NULL, "layer is NULL");
+  const moe_dims& d = layer->dims;
+  int st = check_dims(&d);
+  if (st) return st;
+  const bool has_router = layer->router_weight != nullptr;
+  const int block_m = moe_ffn_block_m(&d);
+  if (d.T == 0) {  // empty tensors may carry NULL data pointers
+    if (info) *info = moe_route_info{block_m, 1, router_logits, nullptr, nullptr, nullptr, nullptr,
+                                     nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
+    return ok();
+  }
+  if (has_router == (router_logits != nullptr))
+    return fail(MOE_ERR_SHAPE, "give exactly one of layer->router_weight and router_logits");
+  if (!x || !y) return fail(MOE_ERR_NULL, "x or y is NULL");
+  if (!aligned16(x) || !aligned16(y)) return fail(MOE_ERR_ALIGN, "x or y not 16-byte aligned");
+  if (has_router && !aligned16(layer->router_weight)) return fail(MOE_ERR_ALIGN, "router_weight not 16-byte aligned");
+  if ((st = check_bank(layer->gate, "gate")) || (st = check_bank(layer->up, "up")) ||
+      (st = check_bank(layer->down, "down")))
+    return st;
+  const FfnLayout L = ffn_layout(d, has_router, block_m);
+  if (!workspace) return fail(MOE_ERR_NULL, "workspace is NULL");
+  if ((uintptr_t)workspace & 255u) return fail(MOE_ERR_ALIGN, "workspace not 256-byte aligned");
+  if (workspace_bytes < L.total) return fail(MOE_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, L.total);
+
+  char* ws = (char*)workspace;
+  float* logits = has_router ? (float*)(ws + L.logits) : (float*)router_logits;
+  int32_t* ids = (int32_t*)(ws + L.ids);
+  float* w = (float*)(ws + L.w);
+  int32_t* counts = (int32_t*)(ws + L.counts);
+  int32_t* offsets = (int32_t*)(ws + L.offsets);
+  int32_t* sorted_pairs = (int32_t*)(ws + L.sorted_pairs);
+  int32_t* pair_slot = (int32_t*)(ws + L.pair_slot);
+  int32_t* blocks = (int32_t*)(ws + L.blocks);
+  int32_t* num_blocks = (int32_t*)(ws + L.num_blocks);
+  moe::half_t* xh = (moe::half_t*)(ws + L.xh);
+  moe::half_t* h = (moe::half_t*)(ws + L.h);
+  float* y_sorted = (float*)(ws + L.y_sorted);
+  const bool gemv = d.T <= moe::kGemvMaxTokens;
+  if (info) {
+    *info = moe_route_info{block_m, gemv ? 1 : 0, logits, ids, w, counts, offsets, sorted_pairs,
+                           pair_slot, blocks, num_blocks, (const uint16_t*)h, y_sorted};
+  }
+
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t err;
+  const int P = d.T * d.top_k;
+  if (has_router && (err = moe::launch_router_gemm(x, layer->router_weight, logits, d.T, d.H, d.E, s)) != hipSuccess)
+    return hip_status(err, "router_gemm");
+  if ((err = moe::launch_topk(logits, d.T, d.E, d.top_k, ids, w, s)) != hipSuccess)
+    return hip_status(err, "topk");
+  if ((err = moe::launch_build_blocks(ids, P, d.E, block_m, counts, offsets, sorted_pairs, pair_slot,
+                                      blocks, num_blocks, (int32_t*)(ws + L.scratch), s)) != hipSuccess)
+    return hip_status(err, "build_blocks");
+  if ((err = moe::launch_stage_x(x, xh, (int64_t)d.T * d.H, s)) != hipSuccess)
+    return hip_status(err, "stage_x");
+  moe::GemmArgs g1{MOE_GEMM_GATE_UP_SWIGLU, d.T, d.top_k, d.E, d.I, d.H, d.group_size, block_m,
+                   xh, layer->gate, layer->up, sorted_pairs, w, blocks, num_blocks, h};
+  moe::GemmArgs g2{MOE_GEMM_DOWN, d.T, d.top_k, d.E, d.H, d.I, d.group_size, block_m,
+                   h, layer->down, layer->down, sorted_pairs, w, blocks, num_blocks, y_sorted};
+  err = gemv ? moe::launch_w4_gemv(g1, s) : moe::launch_w4_mfma(g1, s);
+  if (err != hipSuccess) return hip_status(err, "gate_up");
+  err = gemv ? moe::launch_w4_gemv(g2, s) : moe::launch_w4_mfma(g2, s);
+  if (err != hipSuccess) return hip_status(err, "down");
+  return hip_status(moe::launch_combine(y_sorted, pair_slot, y, d.T, d.H, d.top_k, s), "combine");
+}
+
+}  // extern "C"

@@ -1,0 +1,59 @@
+"""Shared helpers of the GPU parity tests (not collected by pytest)."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+# The floating-point bar for the layer output (and, applied the same way, for
+# the intermediate h): relative L2 error <= 5e-3 and max abs error <= 2e-2 *
+# rms of the oracle's tensor.
+REL_L2_MAX = 5e-3
+MAX_ABS_OVER_RMS = 2e-2
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def f32_ulp(x) -> np.ndarray:
+    x = np.abs(np.asarray(x, np.float32))
+    return np.spacing(np.maximum(x, np.float32(np.finfo(np.float32).tiny))).astype(np.float64)
+
+
+def assert_fp_close(got, ref, what: str, rms_ref: float | None = None):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite values"
+    err = got - ref
+    nref = np.linalg.norm(ref)
+    rel = np.linalg.norm(err) / nref if nref > 0 else np.linalg.norm(err)
+    rms = rms_ref if rms_ref is not None else float(np.sqrt(np.mean(ref ** 2)))
+    mx = float(np.abs(err).max()) if err.size else 0.0
+    say(f"  {what}: relL2 {rel:.3e}  maxabs {mx:.3e}  (bound {MAX_ABS_OVER_RMS * rms:.3e}, rms {rms:.3e})")
+    assert rel <= REL_L2_MAX, f"{what}: relative L2 {rel:.3e} > {REL_L2_MAX}"
+    assert mx <= MAX_ABS_OVER_RMS * rms + 1e-30, f"{what}: max abs {mx:.3e} > {MAX_ABS_OVER_RMS} * rms {rms:.3e}"
+    return rel, mx
+
+
+def assert_weights_close(got, ref):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert np.all(np.abs(got - ref) <= 4 * f32_ulp(ref) + 1e-30), np.abs(got - ref).max()
+
+
+def cpu(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().numpy()
+
+
+def router_error_bound(x: torch.Tensor, wr: torch.Tensor) -> np.ndarray:
+    """Forward error bound of an fp32 sum of H exact products in any order,
+    gamma_H * sum_h |x_h Wr_eh| with gamma_H = H u / (1 - H u), u = 2^-24,
+    plus one ulp for the oracle's own final rounding to fp32."""
+    H = x.shape[1]
+    u = 2.0 ** -24
+    gamma = H * u / (1 - H * u)
+    s = (x.double().abs() @ wr.double().abs().T).numpy()
+    return gamma * s
