@@ -1,0 +1,297 @@
+"""Throughput of the W4 mixture-of-experts layer on one MI355X.
+
+``python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]``
+
+One step is one whole layer (router when the workload has one, top-k
+routing, histogram / scan / scatter / block map, the two grouped W4 GEMMs
+with SwiGLU, and the combine) over one batch of T synthetic tokens, enqueued
+by ``moe_ffn_forward_timed`` on one stream.  Inputs are resident in HBM
+before timing starts.  Weights are rotated over enough device copies of the
+layer (>= 1 GiB in total) that every step reads its experts cold from HBM
+rather than from the 256 MB Infinity Cache; decode workloads also rotate
+over a pool of independent logit sets, so the touched experts change every
+step.
+
+Prints one JSON line.  ``value`` is tokens/s = T * K / (elapsed of the K
+timed steps).  ``roofline`` is for the kernel with the largest average
+duration among the single-kernel stages, from its algorithmic bytes (or
+flops) per launch and its average duration between the stage events
+recorded on its own stream during the timed steps.  ``cpu_baseline`` times
+the CPU oracle on a bounded sample of the same workload on the host cores.
+"""
+
+from __future__ import annotations
+
+import argparse
+import dataclasses
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "W4 MoE-layer tokens/s at T=512 & 8192 prefill, T=1/8 decode; % roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_FP16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 / bf16 MFMA
+ROTATE_BYTES = 1 << 30
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="prefill_t512")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="minimum CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+# ------------------------------------------------------------------ work --
+def expert_bytes(lay) -> dict:
+    """Packed bytes per expert of each bank: codes (4 bits each) + bf16
+    scale and bias per group."""
+    H, I, G = lay.H, lay.I, lay.G
+    bank = lambda N, K: N * K // 2 + 2 * 2 * N * K // G
+    return {"gate_up": 2 * bank(lay.I, lay.H), "down": bank(lay.H, lay.I)}
+
+
+def algorithmic(lay, touched: int) -> dict:
+    """Bytes each single-kernel stage must move at minimum given its inputs
+    and outputs, and its flops.  P = T * k pairs."""
+    T, H, I, E, k = lay.T, lay.H, lay.I, lay.E, lay.k
+    P = T * k
+    eb = expert_bytes(lay)
+    return {
+        # x (fp16 operand copy) read + touched experts' gate and up banks + h fp16 written
+        "gate_up": dict(bytes=touched * eb["gate_up"] + T * H * 2 + P * I * 2,
+                        flops=4 * P * H * I),
+        # h read + touched experts' down bank + weighted y_sorted fp32 written
+        "down": dict(bytes=touched * eb["down"] + P * I * 2 + P * H * 4, flops=2 * P * H * I),
+        # y_sorted read + pair_slot read + y written
+        "combine": dict(bytes=P * H * 4 + P * 4 + T * H * 4, flops=P * H),
+        # x bf16 read + fp16 copy written
+        "stage_x": dict(bytes=T * H * 2 * 2, flops=0),
+    }
+
+
+def layer_work(lay, touched: int) -> dict:
+    """The whole layer's algorithmic flops and bytes: touched experts'
+    packed weights, x, the logits or router weight, and y."""
+    T, H, I, E, k = lay.T, lay.H, lay.I, lay.E, lay.k
+    eb = expert_bytes(lay)
+    flops = 6 * T * k * H * I + (2 * T * H * E if lay.router_weight is not None else 0)
+    byts = touched * (eb["gate_up"] + eb["down"]) + T * H * 2 + T * H * 4
+    byts += E * H * 2 if lay.router_weight is not None else T * E * 4
+    return dict(flops=flops, bytes=byts)
+
+
+# ---------------------------------------------------------- traffic file --
+def kernel_source_digest() -> str:
+    """Digest of the sources the grouped GEMM kernels are built from."""
+    h = hashlib.sha256()
+    for rel in ("quantized_moe_top_amd/csrc/gemm.hip", "quantized_moe_top_amd/csrc/gemv.hip",
+                "quantized_moe_top_amd/csrc/internal.h"):
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, stage: str):
+    """HBM bytes per launch of `stage` from the committed counter summary
+    (FETCH_SIZE + WRITE_SIZE, scaled by a plain copy kernel's reading), or
+    None when there is none or the kernels changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{stage}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if "=" in line and not line.lstrip().startswith("#"):
+                key, val = line.split("=", 1)
+                kv[key.strip()] = val.strip()
+    if kv.get("source_digest") != kernel_source_digest():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ------------------------------------------------------------------ main --
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer is "
+              "measured at one GPU's share and nothing here uses a second GPU.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from quantized_moe_top_amd import _lib, api, synth
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    _lib.load()  # raises when the HIP library is not built
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    name = args.workload
+    log(f"[bench] drawing workload {name}")
+    host = synth.make_layer(name)
+    lay = host.to(dev)
+    T, E, k = lay.T, lay.E, lay.k
+
+    # weight copies for cold reads
+    per_copy = lay.gate.nbytes + lay.up.nbytes + lay.down.nbytes + \
+        (lay.router_weight.numel() * 2 if lay.router_weight is not None else 0)
+    R = max(1, -(-ROTATE_BYTES // per_copy))
+    copies = [lay]
+    for _ in range(R - 1):
+        gate, up, down = (synth.W4Bank(b.qweight.clone(), b.scales.clone(), b.biases.clone())
+                          for b in (lay.gate, lay.up, lay.down))
+        wr = lay.router_weight.clone() if lay.router_weight is not None else None
+        copies.append(dataclasses.replace(lay, gate=gate, up=up, down=down, router_weight=wr))
+    logit_pool = None
+    if lay.logits is not None and T <= 8:
+        logit_pool = [lay.logits] + list(synth.decode_logits_pool(T, E, 63, seed=1000 + T).to(dev))
+    log(f"[bench] {R} weight copies of {per_copy / 2**20:.1f} MiB; "
+        f"logit sets {len(logit_pool) if logit_pool else 1}")
+
+    y = torch.empty((T, lay.H), dtype=torch.float32, device=dev)
+    wsb = api.ffn_workspace_bytes(lay)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    nst = _lib.MOE_NUM_STAGES
+
+    def step(i, evs=None, info=False):
+        c = copies[i % R]
+        lg = logit_pool[i % len(logit_pool)] if logit_pool else None
+        return api.ffn_forward(c, logits=lg, y=y, workspace=ws, stage_events=evs, info=info)
+
+    # touched experts per step (for the algorithmic byte counts): routing is
+    # identical for every copy; decode rotates logit sets
+    touched = []
+    for i in range(len(logit_pool) if logit_pool else 1):
+        _, inf = step(i, info=True)
+        touched.append(int((inf["counts"] > 0).sum().item()))
+    torch.cuda.synchronize()
+
+    log(f"[bench] warmup {args.warmup}")
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [api.stage_events(nst + 1) for _ in range(K)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    log(f"[bench] timing {K} steps")
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(K):
+        step(i, ev[i])
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    elapsed_ms = start.elapsed_time(end)
+    ms_per_step = elapsed_ms / K
+    value = T * K / (elapsed_ms / 1e3)
+    stage_ms = np.array([[ev[i][s].elapsed_time(ev[i][s + 1]) for s in range(nst)] for i in range(K)])
+    stage_us = {st: round(float(stage_ms[:, j].mean()) * 1e3, 3) for j, st in enumerate(_lib.STAGES)}
+    log(f"[bench] {ms_per_step * 1e3:.2f} us/step (wall {wall / K * 1e6:.2f}); stages us {stage_us}")
+
+    # roofline of the dominant single-kernel stage
+    mean_touched = float(np.mean([touched[i % len(touched)] for i in range(K)]))
+    alg = algorithmic(lay, 0)
+    alg_t = {s: dict(bytes=algorithmic(lay, 1)[s]["bytes"] - alg[s]["bytes"], flops=alg[s]["flops"])
+             for s in alg}  # bytes per touched expert
+    single = ["stage_x", "gate_up", "down", "combine"]
+    dom = max(single, key=lambda s: stage_us[s])
+    dur_s = stage_us[dom] * 1e-6
+    byts = alg[dom]["bytes"] + mean_touched * alg_t[dom]["bytes"]
+    flops = alg[dom]["flops"]
+    hbm_time = byts / (HBM_PEAK_GBS * 1e9)
+    mfma_time = flops / (MFMA_FP16_PEAK_TFLOPS * 1e12)
+    if hbm_time >= mfma_time:
+        achieved, peak, unit, bound = byts / dur_s / 1e9, HBM_PEAK_GBS, "GB/s", "hbm"
+    else:
+        achieved, peak, unit, bound = flops / dur_s / 1e12, MFMA_FP16_PEAK_TFLOPS, "TFLOP/s", "mfma"
+    traffic = measured_traffic(name, dom)
+    roofline = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+                "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": dom,
+                "algorithmic_bytes": int(byts), "algorithmic_flops": int(flops),
+                "avg_launch_us": stage_us[dom]}
+    lw = layer_work(lay, 0)
+    lw_t = layer_work(lay, 1)["bytes"] - lw["bytes"]
+    lbytes = lw["bytes"] + mean_touched * lw_t
+    t_step = ms_per_step * 1e-3
+    layer_roof = {"hbm_frac": round(lbytes / t_step / (HBM_PEAK_GBS * 1e9), 4),
+                  "mfma_frac": round(lw["flops"] / t_step / (MFMA_FP16_PEAK_TFLOPS * 1e12), 4),
+                  "bytes": int(lbytes), "flops": int(lw["flops"]), "touched_experts": mean_touched}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(host, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": K, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp16",
+        "data": "synthetic",
+        "config": {"workload": name, "T": T, "H": lay.H, "I": lay.I, "E": E, "top_k": k,
+                   "group_size": lay.G, "router": "weight" if lay.router_weight is not None else "logits",
+                   "weight_copies": R, "block_m": api.ffn_block_m(lay)},
+        "roofline": roofline, "layer_roofline": layer_roof, "stage_us": stage_us,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(host, min_seconds: float) -> dict:
+    """The CPU oracle on the host cores: the whole layer on a sample of the
+    tokens (all of them when T <= 512), with routing over every token;
+    repeated until `min_seconds` of work.  Scaled to whole-layer tokens/s."""
+    import numpy as np
+
+    import oracle
+
+    orc = oracle.get()
+    T = host.T
+    n = min(T, 512)
+    tokens = np.linspace(0, T - 1, n).round().astype(np.int32) if n < T else np.arange(T, dtype=np.int32)
+    log(f"[bench] cpu baseline: oracle on {n} of {T} tokens, {orc.num_threads()} threads")
+    t_route = t_ffn = 0.0
+    reps = 0
+    while True:
+        t0 = time.perf_counter()
+        logits = (orc.router_logits(host.x, host.router_weight) if host.router_weight is not None
+                  else np.ascontiguousarray(host.logits.numpy()))
+        ids, w = orc.route(logits, host.k)
+        orc.build_blocks(ids, host.E, 64)
+        t1 = time.perf_counter()
+        orc.ffn(host.x, ids, w, host.gate, host.up, host.down, host.G, tokens=tokens)
+        t2 = time.perf_counter()
+        t_route += t1 - t0
+        t_ffn += t2 - t1
+        reps += 1
+        if t_route + t_ffn >= min_seconds or reps >= 50:
+            break
+    per_layer = t_route / reps + (t_ffn / reps) * T / n
+    return {"value": round(T / per_layer, 2), "unit": "tokens/s", "cores": orc.num_threads(),
+            "kind": "oracle",
+            "sample": f"{reps} x (routing of all {T} tokens + layer output of {n} tokens); "
+                      f"{t_route + t_ffn:.1f} s of CPU work, scaled to the whole layer"}
+
+
+if __name__ == "__main__":
+    main()

@@ -202,6 +202,30 @@ int moe_ffn_forward(const moe_layer* layer, const uint16_t* x, const float* rout
                     float* y, moe_route_info* info, void* workspace, size_t workspace_bytes,
                     void* stream);
 
+/* ------------------------------------------------------ per-stage timing --
+ * The same layer as moe_ffn_forward (identical kernels and results), with a
+ * timing event recorded on `stream` at every stage boundary, so that a
+ * caller can measure each kernel on the stream it runs on.
+ * stage_events: host array of MOE_NUM_STAGES + 1 hipEvent_t handles created
+ * by the caller (NULL entries are skipped); events[i] is recorded just
+ * before stage i is enqueued and events[MOE_NUM_STAGES] after the last.
+ * The elapsed time between events[i] and events[i+1] is stage i.  The
+ * library only records the events; the caller owns, synchronises and
+ * destroys them.  A NULL stage_events returns MOE_ERR_NULL. */
+typedef enum {
+  MOE_STAGE_ROUTE = 0,        /* S0 router linear layer (when present) + S1 top-k */
+  MOE_STAGE_BUILD_BLOCKS = 1, /* S2 - S5 histogram, scan, scatter, block map */
+  MOE_STAGE_STAGE_X = 2,      /* activations bf16 -> fp16 operand layout */
+  MOE_STAGE_GATE_UP = 3,      /* S6 gate/up grouped GEMM + SwiGLU (S9 at T <= 8) */
+  MOE_STAGE_DOWN = 4,         /* S7 down grouped GEMM x routing weight (S9 at T <= 8) */
+  MOE_STAGE_COMBINE = 5,      /* S8 combine */
+  MOE_NUM_STAGES = 6
+} moe_stage;
+
+int moe_ffn_forward_timed(const moe_layer* layer, const uint16_t* x, const float* router_logits,
+                          float* y, moe_route_info* info, void* workspace, size_t workspace_bytes,
+                          void* const* stage_events, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

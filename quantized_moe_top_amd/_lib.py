@@ -24,8 +24,12 @@ SYMBOLS = (
     "moe_status_string", "moe_last_error", "moe_version",
     "moe_route", "moe_max_blocks", "moe_build_blocks_workspace_bytes", "moe_build_blocks",
     "moe_w4_grouped_gemm_workspace_bytes", "moe_w4_grouped_gemm",
-    "moe_ffn_block_m", "moe_ffn_workspace_bytes", "moe_ffn_forward",
+    "moe_ffn_block_m", "moe_ffn_workspace_bytes", "moe_ffn_forward", "moe_ffn_forward_timed",
 )
+
+# Stage boundaries of moe_ffn_forward_timed (enum moe_stage).
+STAGES = ("route", "build_blocks", "stage_x", "gate_up", "down", "combine")
+MOE_NUM_STAGES = len(STAGES)
 
 
 class Dims(ctypes.Structure):
@@ -92,7 +96,10 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     L.moe_ffn_workspace_bytes.argtypes = [ctypes.POINTER(Dims), c_i32]
     L.moe_ffn_forward.argtypes = [ctypes.POINTER(Layer), c_p, c_p, c_p, ctypes.POINTER(RouteInfo),
                                   c_p, c_sz, c_p]
-    for name in ("moe_route", "moe_build_blocks", "moe_w4_grouped_gemm", "moe_ffn_forward"):
+    L.moe_ffn_forward_timed.argtypes = [ctypes.POINTER(Layer), c_p, c_p, c_p,
+                                        ctypes.POINTER(RouteInfo), c_p, c_sz, c_p, c_p]
+    for name in ("moe_route", "moe_build_blocks", "moe_w4_grouped_gemm", "moe_ffn_forward",
+                 "moe_ffn_forward_timed"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L

@@ -17,7 +17,7 @@ from . import _lib
 from ._lib import MOE_GEMM_DOWN, MOE_GEMM_GATE_UP_SWIGLU, Bank, Dims, GemmArgs, Layer, RouteInfo
 
 __all__ = ["route", "build_blocks", "w4_grouped_gemm", "ffn_forward", "ffn_workspace_bytes",
-           "ffn_block_m", "max_blocks", "MOE_GEMM_GATE_UP_SWIGLU", "MOE_GEMM_DOWN"]
+           "ffn_block_m", "max_blocks", "stage_events", "MOE_GEMM_GATE_UP_SWIGLU", "MOE_GEMM_DOWN"]
 
 
 def _L():
@@ -149,13 +149,24 @@ def make_layer_struct(layer, T: int) -> Layer:
                  _bank(layer.gate, "gate"), _bank(layer.up, "up"), _bank(layer.down, "down"))
 
 
+def stage_events(n: int = _lib.MOE_NUM_STAGES + 1):
+    """``n`` timing events usable as ``ffn_forward(stage_events=...)``.  torch
+    creates an event's handle on its first record, so each is recorded once
+    here."""
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+    for e in evs:
+        e.record()
+    return evs
+
+
 def ffn_forward(layer, x: Optional[torch.Tensor] = None, logits: Optional[torch.Tensor] = None,
                 y: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                info: bool = False):
+                info: bool = False, stage_events=None):
     """The whole layer (S0/S1-S8) for a ``synth.MoELayer`` whose tensors are on
     the device.  ``x`` and ``logits`` default to the layer's own.  Returns y
     fp32 [T, H], plus a dict of routing-structure views into the workspace
-    when ``info`` is true."""
+    when ``info`` is true.  ``stage_events`` (from ``stage_events()``) runs
+    ``moe_ffn_forward_timed``, recording one event per stage boundary."""
     x = layer.x if x is None else x
     T, H = x.shape
     if layer.router_weight is None and logits is None:
@@ -169,11 +180,17 @@ def ffn_forward(layer, x: Optional[torch.Tensor] = None, logits: Optional[torch.
         raise ValueError("workspace too small")
     lay = make_layer_struct(layer, T)
     ri = RouteInfo()
-    st = _L().moe_ffn_forward(ctypes.byref(lay), _dev(x, "x", torch.bfloat16),
-                              _dev(logits, "logits", torch.float32) if layer.router_weight is None else 0,
-                              _dev(y, "y", torch.float32), ctypes.byref(ri),
-                              _dev(workspace, "workspace", torch.uint8), workspace.numel(), _stream())
-    _lib.check(st, "moe_ffn_forward")
+    args = (ctypes.byref(lay), _dev(x, "x", torch.bfloat16),
+            _dev(logits, "logits", torch.float32) if layer.router_weight is None else 0,
+            _dev(y, "y", torch.float32), ctypes.byref(ri),
+            _dev(workspace, "workspace", torch.uint8), workspace.numel())
+    if stage_events is None:
+        _lib.check(_L().moe_ffn_forward(*args, _stream()), "moe_ffn_forward")
+    else:
+        if len(stage_events) != _lib.MOE_NUM_STAGES + 1:
+            raise ValueError(f"need {_lib.MOE_NUM_STAGES + 1} stage events")
+        handles = (ctypes.c_void_p * len(stage_events))(*[e.cuda_event for e in stage_events])
+        _lib.check(_L().moe_ffn_forward_timed(*args, handles, _stream()), "moe_ffn_forward_timed")
     if not info:
         return y
     return y, _info_views(ri, workspace, layer, T, logits)

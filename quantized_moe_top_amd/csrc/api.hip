@@ -240,9 +240,19 @@ size_t moe_ffn_workspace_bytes(const moe_dims* d, int32_t has_router) {
   return ffn_layout(*d, has_router != 0, moe_ffn_block_m(d)).total;
 }
 
-int moe_ffn_forward(const moe_layer* layer, const uint16_t* x, const float* router_logits,
-                    float* y, moe_route_info* info, void* workspace, size_t workspace_bytes,
-                    void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Records stage event i (when given) on the stream before stage i runs.
+hipError_t mark(void* const* events, int i, hipStream_t s) {
+  if (!events || !events[i]) return hipSuccess;
+  return hipEventRecord((hipEvent_t)events[i], s);
+}
+
+int ffn_forward_impl(const moe_layer* layer, const uint16_t* x, const float* router_logits,
+                     float* y, moe_route_info* info, void* workspace, size_t workspace_bytes,
+                     void* const* events, hipStream_t s) {
   if (!layer) return fail(MOE_ERR_NULL, "layer is NULL");
   const moe_dims& d = layer->dims;
   int st = check_dims(&d);
@@ -286,27 +296,54 @@ int moe_ffn_forward(const moe_layer* layer, const uint16_t* x, const float* rout
                            pair_slot, blocks, num_blocks, (const uint16_t*)h, y_sorted};
   }
 
-  hipStream_t s = (hipStream_t)stream;
   hipError_t err;
   const int P = d.T * d.top_k;
+  if ((err = mark(events, MOE_STAGE_ROUTE, s)) != hipSuccess) return hip_status(err, "event");
   if (has_router && (err = moe::launch_router_gemm(x, layer->router_weight, logits, d.T, d.H, d.E, s)) != hipSuccess)
     return hip_status(err, "router_gemm");
   if ((err = moe::launch_topk(logits, d.T, d.E, d.top_k, ids, w, s)) != hipSuccess)
     return hip_status(err, "topk");
+  if ((err = mark(events, MOE_STAGE_BUILD_BLOCKS, s)) != hipSuccess) return hip_status(err, "event");
   if ((err = moe::launch_build_blocks(ids, P, d.E, block_m, counts, offsets, sorted_pairs, pair_slot,
                                       blocks, num_blocks, (int32_t*)(ws + L.scratch), s)) != hipSuccess)
     return hip_status(err, "build_blocks");
+  if ((err = mark(events, MOE_STAGE_STAGE_X, s)) != hipSuccess) return hip_status(err, "event");
   if ((err = moe::launch_stage_x(x, xh, (int64_t)d.T * d.H, s)) != hipSuccess)
     return hip_status(err, "stage_x");
   moe::GemmArgs g1{MOE_GEMM_GATE_UP_SWIGLU, d.T, d.top_k, d.E, d.I, d.H, d.group_size, block_m,
                    xh, layer->gate, layer->up, sorted_pairs, w, blocks, num_blocks, h};
   moe::GemmArgs g2{MOE_GEMM_DOWN, d.T, d.top_k, d.E, d.H, d.I, d.group_size, block_m,
                    h, layer->down, layer->down, sorted_pairs, w, blocks, num_blocks, y_sorted};
+  if ((err = mark(events, MOE_STAGE_GATE_UP, s)) != hipSuccess) return hip_status(err, "event");
   err = gemv ? moe::launch_w4_gemv(g1, s) : moe::launch_w4_mfma(g1, s);
   if (err != hipSuccess) return hip_status(err, "gate_up");
+  if ((err = mark(events, MOE_STAGE_DOWN, s)) != hipSuccess) return hip_status(err, "event");
   err = gemv ? moe::launch_w4_gemv(g2, s) : moe::launch_w4_mfma(g2, s);
   if (err != hipSuccess) return hip_status(err, "down");
-  return hip_status(moe::launch_combine(y_sorted, pair_slot, y, d.T, d.H, d.top_k, s), "combine");
+  if ((err = mark(events, MOE_STAGE_COMBINE, s)) != hipSuccess) return hip_status(err, "event");
+  if ((err = moe::launch_combine(y_sorted, pair_slot, y, d.T, d.H, d.top_k, s)) != hipSuccess)
+    return hip_status(err, "combine");
+  if ((err = mark(events, MOE_NUM_STAGES, s)) != hipSuccess) return hip_status(err, "event");
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_ffn_forward(const moe_layer* layer, const uint16_t* x, const float* router_logits,
+                    float* y, moe_route_info* info, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  return ffn_forward_impl(layer, x, router_logits, y, info, workspace, workspace_bytes, nullptr,
+                          (hipStream_t)stream);
+}
+
+int moe_ffn_forward_timed(const moe_layer* layer, const uint16_t* x, const float* router_logits,
+                          float* y, moe_route_info* info, void* workspace, size_t workspace_bytes,
+                          void* const* stage_events, void* stream) {
+  if (!stage_events) return fail(MOE_ERR_NULL, "stage_events is NULL");
+  return ffn_forward_impl(layer, x, router_logits, y, info, workspace, workspace_bytes,
+                          stage_events, (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -146,3 +146,14 @@ def test_ffn_validation(L):
     lay = Layer(Dims(0, 256, 128, 8, 2, 32), 0, bank, bank, bank)
     assert L.moe_ffn_forward(ctypes.byref(lay), A, A, A, ctypes.byref(info), A, 1 << 20, None) == OK
     assert info.block_m == 8 and info.path == 1
+
+
+def test_ffn_timed_validation(L):
+    bank = Bank(A, A, A)
+    lay = Layer(Dims(16, 256, 128, 8, 2, 32), 0, bank, bank, bank)
+    # no event array: rejected before anything is enqueued
+    assert L.moe_ffn_forward_timed(ctypes.byref(lay), A, A, A, None, A, 1 << 30, None, None) == NULL
+    # argument errors are reported exactly as by moe_ffn_forward
+    evs = (ctypes.c_void_p * (_lib.MOE_NUM_STAGES + 1))()
+    lay.dims.H = 200
+    assert L.moe_ffn_forward_timed(ctypes.byref(lay), A, A, A, None, A, 1 << 30, evs, None) == UNSUP
