@@ -53,6 +53,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum CPU time of the oracle sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after timing, run one plain device copy of 256 MiB, the reference "
+                         "kernel for scaling HBM byte counters")
     return ap.parse_args()
 
 
@@ -79,8 +82,13 @@ def algorithmic(lay, touched: int) -> dict:
         "down": dict(bytes=touched * eb["down"] + P * I * 2 + P * H * 4, flops=2 * P * H * I),
         # y_sorted read + pair_slot read + y written
         "combine": dict(bytes=P * H * 4 + P * 4 + T * H * 4, flops=P * H),
-        # x bf16 read + fp16 copy written
-        "stage_x": dict(bytes=T * H * 2 * 2, flops=0),
+        # x bf16 read + fp16 copy written, logits (or router weight) read,
+        # ids / weights written
+        "route": dict(bytes=T * H * 2 * 2 + (E * H * 2 + T * E * 4 if lay.router_weight is not None
+                                            else T * E * 4) + P * 8,
+                      flops=2 * T * H * E if lay.router_weight is not None else 0),
+        # ids read, sorted_pairs / pair_slot written
+        "build_blocks": dict(bytes=P * 4 * 3, flops=0),
     }
 
 
@@ -215,7 +223,7 @@ def main():
     alg = algorithmic(lay, 0)
     alg_t = {s: dict(bytes=algorithmic(lay, 1)[s]["bytes"] - alg[s]["bytes"], flops=alg[s]["flops"])
              for s in alg}  # bytes per touched expert
-    single = ["stage_x", "gate_up", "down", "combine"]
+    single = ["route", "build_blocks", "gate_up", "down", "combine"]
     dom = max(single, key=lambda s: stage_us[s])
     dur_s = stage_us[dom] * 1e-6
     byts = alg[dom]["bytes"] + mean_touched * alg_t[dom]["bytes"]
@@ -238,6 +246,14 @@ def main():
     layer_roof = {"hbm_frac": round(lbytes / t_step / (HBM_PEAK_GBS * 1e9), 4),
                   "mfma_frac": round(lw["flops"] / t_step / (MFMA_FP16_PEAK_TFLOPS * 1e12), 4),
                   "bytes": int(lbytes), "flops": int(lw["flops"]), "touched_experts": mean_touched}
+
+    if args.copy_calibration:
+        src = torch.empty(64 << 20, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] copy calibration: 268435456 bytes read and written")
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -99,7 +99,8 @@ typedef struct {
  *   topk_weights[t][j] = exp(l_j - l_0) / sum_i exp(l_i - l_0)   (fp32),
  * the softmax over the top_k selected logits.
  * Device pointers: x bf16 [T][H]; router_weight bf16 [E][H]; logits fp32
- * [T][E]; topk_ids int32 [T][top_k]; topk_weights fp32 [T][top_k]. */
+ * [T][E]; topk_ids int32 [T][top_k]; topk_weights fp32 [T][top_k].
+ * With a router weight, H must be a positive multiple of 128. */
 int moe_route(const uint16_t* x, const uint16_t* router_weight, float* logits, int32_t T,
               int32_t H, int32_t E, int32_t top_k, int32_t* topk_ids, float* topk_weights,
               void* stream);
@@ -136,18 +137,20 @@ int moe_build_blocks(const int32_t* topk_ids, int32_t T, int32_t top_k, int32_t 
  *
  * MOE_GEMM_GATE_UP_SWIGLU: for every slot s of every tile (expert e), with
  *   token t = sorted_pairs[s] / top_k,
- *     g = W_gate[e] x[t],  u = W_up[e] x[t],  out[s][n] = silu(g_n) * u_n
- *   silu(z) = z / (1 + exp(-z)); a = x bf16 [T][K]; out = h fp16 [P][N];
+ *     g = W_gate[e] x[t],  u = W_up[e] x[t],  h[s][n] = silu(g_n) * u_n
+ *   silu(z) = z / (1 + exp(-z)); a = x bf16 [T][K]; out = h fp16 [P][N]
+ *   in operand order: within every run of 8 columns 8c..8c+7 the stored
+ *   order is (8c+0, 8c+4, 8c+1, 8c+5, 8c+2, 8c+6, 8c+3, 8c+7);
  *   N = I, K = H; bank0 = gate, bank1 = up.
  * MOE_GEMM_DOWN: for every slot s of every tile (expert e), pair
  *   p = sorted_pairs[s],
  *     out[s][n] = topk_weights[p] * (W_down[e] h[s])_n
- *   a = h fp16 [P][K] (slot order); out = y_sorted fp32 [P][N]; N = H,
- *   K = I; bank0 = down; bank1 unused.
+ *   a = h fp16 [P][K] (slot order, operand order as written above); out =
+ *   y_sorted fp32 [P][N]; N = H, K = I; bank0 = down; bank1 unused.
  * T <= 8 runs a bandwidth-bound GEMV-style kernel that reads each touched
  * expert's packed rows once; larger T runs fp16 MFMA tiles of block_m rows
- * (block_m in {32, 64, 128}, equal to the block map's).  Slots outside every
- * tile are not written.  workspace: device, >=
+ * (block_m in {32, 64, 128}, equal to the block map's).  K % 128 == 0.
+ * Slots outside every tile are not written.  workspace: device, >=
  * moe_w4_grouped_gemm_workspace_bytes(args). */
 typedef enum { MOE_GEMM_GATE_UP_SWIGLU = 0, MOE_GEMM_DOWN = 1 } moe_gemm_mode;
 
@@ -191,7 +194,7 @@ typedef struct {
   const int32_t* pair_slot;     /* [P] */
   const int32_t* blocks;        /* [max_blocks][3] */
   const int32_t* num_blocks;    /* [1] */
-  const uint16_t* h;            /* fp16 [P][I], slot order */
+  const uint16_t* h;            /* fp16 [P][I], slot order, operand order */
   const float* y_sorted;        /* fp32 [P][H], slot order, weighted */
 } moe_route_info;
 
@@ -213,13 +216,13 @@ int moe_ffn_forward(const moe_layer* layer, const uint16_t* x, const float* rout
  * library only records the events; the caller owns, synchronises and
  * destroys them.  A NULL stage_events returns MOE_ERR_NULL. */
 typedef enum {
-  MOE_STAGE_ROUTE = 0,        /* S0 router linear layer (when present) + S1 top-k */
-  MOE_STAGE_BUILD_BLOCKS = 1, /* S2 - S5 histogram, scan, scatter, block map */
-  MOE_STAGE_STAGE_X = 2,      /* activations bf16 -> fp16 operand layout */
-  MOE_STAGE_GATE_UP = 3,      /* S6 gate/up grouped GEMM + SwiGLU (S9 at T <= 8) */
-  MOE_STAGE_DOWN = 4,         /* S7 down grouped GEMM x routing weight (S9 at T <= 8) */
-  MOE_STAGE_COMBINE = 5,      /* S8 combine */
-  MOE_NUM_STAGES = 6
+  MOE_STAGE_ROUTE = 0,        /* S0 router linear layer (when present), S1 top-k, per-chunk
+                                 expert histograms, activations to the fp16 operand layout */
+  MOE_STAGE_BUILD_BLOCKS = 1, /* S2 - S5 totals, scan, block map, stable scatter */
+  MOE_STAGE_GATE_UP = 2,      /* S6 gate/up grouped GEMM + SwiGLU (S9 at T <= 8) */
+  MOE_STAGE_DOWN = 3,         /* S7 down grouped GEMM x routing weight (S9 at T <= 8) */
+  MOE_STAGE_COMBINE = 4,      /* S8 combine */
+  MOE_NUM_STAGES = 5
 } moe_stage;
 
 int moe_ffn_forward_timed(const moe_layer* layer, const uint16_t* x, const float* router_logits,

@@ -28,7 +28,7 @@ SYMBOLS = (
 )
 
 # Stage boundaries of moe_ffn_forward_timed (enum moe_stage).
-STAGES = ("route", "build_blocks", "stage_x", "gate_up", "down", "combine")
+STAGES = ("route", "build_blocks", "gate_up", "down", "combine")
 MOE_NUM_STAGES = len(STAGES)
 
 

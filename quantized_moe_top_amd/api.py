@@ -103,8 +103,9 @@ def w4_grouped_gemm(mode: int, a: torch.Tensor, bank0, bank1, sorted_pairs: torc
                     group_size: int, block_m: int, topk_weights: Optional[torch.Tensor] = None,
                     out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """S6 (mode MOE_GEMM_GATE_UP_SWIGLU: a = x bf16 [T, H], returns h fp16
-    [P, I]) or S7 (MOE_GEMM_DOWN: a = h fp16 [P, I], returns y_sorted fp32
-    [P, H]).  Slots outside every tile are left as they were in ``out``."""
+    [P, I] in operand order) or S7 (MOE_GEMM_DOWN: a = h fp16 [P, I],
+    returns y_sorted fp32 [P, H]).  Slots outside every tile are left as they
+    were in ``out``."""
     gate_up = mode == MOE_GEMM_GATE_UP_SWIGLU
     E_, N, K8 = bank0.qweight.shape
     K = K8 * 8

@@ -55,6 +55,13 @@ def build(verbose: bool = True) -> str:
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}{res.stderr}")
+    # a kernel template whose host-side launch stub was silently dropped
+    # shows up as an undefined __device_stub__ symbol: refuse such a build
+    nm = subprocess.run(["nm", "-u", tmp], capture_output=True, text=True)
+    missing = [l.split()[-1] for l in nm.stdout.splitlines() if "__device_stub__" in l]
+    if missing:
+        os.remove(tmp)
+        raise RuntimeError(f"kernel launch stubs missing from the host pass: {missing}")
     os.replace(tmp, LIBRARY)
     if verbose:
         print(f"built {LIBRARY} from {len(sources)} sources for {ARCH}")

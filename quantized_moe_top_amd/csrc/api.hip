@@ -74,8 +74,8 @@ size_t gemm_workspace(int mode, int64_t T, int64_t K) {
 
 // Workspace layout of moe_ffn_forward.
 struct FfnLayout {
-  size_t logits, ids, w, counts, offsets, sorted_pairs, pair_slot, blocks, num_blocks, scratch,
-      xh, h, y_sorted, total;
+  size_t logits, ids, w, counts, offsets, sorted_pairs, pair_slot, blocks, num_blocks,
+      scratch, xh, h, y_sorted, total;
 };
 
 FfnLayout ffn_layout(const moe_dims& d, bool has_router, int block_m) {
@@ -96,7 +96,7 @@ FfnLayout ffn_layout(const moe_dims& d, bool has_router, int block_m) {
   L.pair_slot = take(P * 4);
   L.blocks = take((size_t)max_blocks((int64_t)P, d.E, block_m) * 12);
   L.num_blocks = take(4);
-  L.scratch = take((size_t)moe::build_blocks_chunks((int64_t)P) * E * 4);
+  L.scratch = take((size_t)moe::route_chunks(d.T) * E * 4);
   L.xh = take(T * H * 2);
   L.h = take(P * I * 2);
   L.y_sorted = take(P * H * 4);
@@ -146,15 +146,12 @@ int moe_route(const uint16_t* x, const uint16_t* router_weight, float* logits, i
   if (!logits || !topk_ids || !topk_weights) return fail(MOE_ERR_NULL, "logits/topk_ids/topk_weights NULL");
   if (router_weight) {
     if (!x) return fail(MOE_ERR_NULL, "x is NULL while router_weight is given");
-    if (H <= 0 || H % 16) return fail(MOE_ERR_UNSUPPORTED, "H = %d not a positive multiple of 16", H);
+    if (H <= 0 || H % 128) return fail(MOE_ERR_UNSUPPORTED, "H = %d not a positive multiple of 128", H);
     if (!aligned16(x) || !aligned16(router_weight)) return fail(MOE_ERR_ALIGN, "x or router_weight not 16-byte aligned");
   }
-  hipStream_t s = (hipStream_t)stream;
-  if (router_weight) {
-    hipError_t err = moe::launch_router_gemm(x, router_weight, logits, T, H, E, s);
-    if (err != hipSuccess) return hip_status(err, "router_gemm");
-  }
-  return hip_status(moe::launch_topk(logits, T, E, top_k, topk_ids, topk_weights, s), "topk");
+  return hip_status(moe::launch_route(x, router_weight, logits, T, H, E, top_k, topk_ids,
+                                      topk_weights, nullptr, nullptr, (hipStream_t)stream),
+                    "route");
 }
 
 int64_t moe_max_blocks(int32_t T, int32_t top_k, int32_t E, int32_t block_m) {
@@ -162,8 +159,8 @@ int64_t moe_max_blocks(int32_t T, int32_t top_k, int32_t E, int32_t block_m) {
 }
 
 size_t moe_build_blocks_workspace_bytes(int32_t T, int32_t top_k, int32_t E) {
-  const int64_t P = (int64_t)(T > 0 ? T : 0) * (top_k > 0 ? top_k : 0);
-  return round_up((size_t)moe::build_blocks_chunks(P) * (size_t)(E > 0 ? E : 0) * 4);
+  if (T <= 0 || top_k <= 0 || E <= 0) return 0;
+  return round_up((size_t)moe::route_chunks(T) * (size_t)E * 4);
 }
 
 int moe_build_blocks(const int32_t* topk_ids, int32_t T, int32_t top_k, int32_t E,
@@ -179,10 +176,13 @@ int moe_build_blocks(const int32_t* topk_ids, int32_t T, int32_t top_k, int32_t 
   const size_t need = moe_build_blocks_workspace_bytes(T, top_k, E);
   if (need && !workspace) return fail(MOE_ERR_NULL, "workspace is NULL");
   if (workspace_bytes < need) return fail(MOE_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
-  return hip_status(moe::launch_build_blocks(topk_ids, T * top_k, E, block_m, counts, offsets,
-                                             sorted_pairs, pair_slot, blocks, num_blocks,
-                                             (int32_t*)workspace, (hipStream_t)stream),
-                    "build_blocks");
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t err = moe::launch_chunk_hist(topk_ids, T, top_k, E, (int32_t*)workspace, s);
+  if (err != hipSuccess) return hip_status(err, "chunk_hist");
+  return hip_status(moe::launch_scan_scatter(topk_ids, T, top_k, E, (const int32_t*)workspace,
+                                             block_m, counts, offsets, sorted_pairs, pair_slot,
+                                             blocks, num_blocks, s),
+                    "scan_scatter");
 }
 
 size_t moe_w4_grouped_gemm_workspace_bytes(const moe_w4_gemm_args* a) {
@@ -199,7 +199,7 @@ int moe_w4_grouped_gemm(const moe_w4_gemm_args* a, void* stream) {
   if (st) return st;
   if (a->N <= 0 || a->K <= 0) return fail(MOE_ERR_SHAPE, "N and K must be positive");
   if ((st = check_group(a->group_size, a->K, "K"))) return st;
-  if (a->K % 64) return fail(MOE_ERR_UNSUPPORTED, "K = %d not a multiple of 64", a->K);
+  if (a->K % 128) return fail(MOE_ERR_UNSUPPORTED, "K = %d not a multiple of 128", a->K);
   if (a->N % (gate_up ? 128 : 256))
     return fail(MOE_ERR_UNSUPPORTED, "N = %d not a multiple of %d", a->N, gate_up ? 128 : 256);
   if ((st = gemm_block_ok(a->T, a->block_m))) return st;
@@ -297,19 +297,15 @@ int ffn_forward_impl(const moe_layer* layer, const uint16_t* x, const float* rou
   }
 
   hipError_t err;
-  const int P = d.T * d.top_k;
+  int32_t* chunk_hist = (int32_t*)(ws + L.scratch);
   if ((err = mark(events, MOE_STAGE_ROUTE, s)) != hipSuccess) return hip_status(err, "event");
-  if (has_router && (err = moe::launch_router_gemm(x, layer->router_weight, logits, d.T, d.H, d.E, s)) != hipSuccess)
-    return hip_status(err, "router_gemm");
-  if ((err = moe::launch_topk(logits, d.T, d.E, d.top_k, ids, w, s)) != hipSuccess)
-    return hip_status(err, "topk");
+  if ((err = moe::launch_route(x, layer->router_weight, logits, d.T, d.H, d.E, d.top_k, ids, w, xh,
+                               chunk_hist, s)) != hipSuccess)
+    return hip_status(err, "route");
   if ((err = mark(events, MOE_STAGE_BUILD_BLOCKS, s)) != hipSuccess) return hip_status(err, "event");
-  if ((err = moe::launch_build_blocks(ids, P, d.E, block_m, counts, offsets, sorted_pairs, pair_slot,
-                                      blocks, num_blocks, (int32_t*)(ws + L.scratch), s)) != hipSuccess)
-    return hip_status(err, "build_blocks");
-  if ((err = mark(events, MOE_STAGE_STAGE_X, s)) != hipSuccess) return hip_status(err, "event");
-  if ((err = moe::launch_stage_x(x, xh, (int64_t)d.T * d.H, s)) != hipSuccess)
-    return hip_status(err, "stage_x");
+  if ((err = moe::launch_scan_scatter(ids, d.T, d.top_k, d.E, chunk_hist, block_m, counts, offsets,
+                                      sorted_pairs, pair_slot, blocks, num_blocks, s)) != hipSuccess)
+    return hip_status(err, "scan_scatter");
   moe::GemmArgs g1{MOE_GEMM_GATE_UP_SWIGLU, d.T, d.top_k, d.E, d.I, d.H, d.group_size, block_m,
                    xh, layer->gate, layer->up, sorted_pairs, w, blocks, num_blocks, h};
   moe::GemmArgs g2{MOE_GEMM_DOWN, d.T, d.top_k, d.E, d.H, d.I, d.group_size, block_m,

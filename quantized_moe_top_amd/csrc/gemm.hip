@@ -2,21 +2,34 @@
 // dequantisation fused into the kernel (page "Perplexity's Lily engine beats
 // MLX by 35% on M5 Max", architecture paragraph: dequantising inside the
 // grouped GEMM keeps expanded 16-bit weights out of memory), the activation
-// staging pass, and the S8 combine.
+// staging pass of the standalone entry point, and the S8 combine.
 //
-// Tile of one workgroup (256 threads = 4 waves): BM rows (slots of one
-// expert, from the block map) x 128 output columns of the gate AND up banks
-// (S6) or x 256 columns of the down bank (S7), over the whole reduction
-// dimension in slabs of 64.  Every wave owns all BM rows and two 32-column
-// blocks, so the codes it dequantises feed BM/32 MFMAs each.
-//  - A (activations) is staged per slab in LDS, rows padded to 144 bytes so
-//    that the 16-byte fragment reads of 8 consecutive rows hit distinct banks.
-//  - B (weights) is read straight from HBM: each lane loads one 16-byte piece
-//    (32 codes of one row) per column block per slab, and dequantises it in
-//    registers against the row's fp16-converted scale and bias.
-//  - MFMA v_mfma_f32_32x32x16_f16, fp32 accumulation.
-//  - The next slab's A and B loads are issued before the current slab's
-//    MFMAs; A is double-buffered in LDS, one barrier per slab.
+// One workgroup (512 threads = 8 waves) computes a tile of BM rows (slots of
+// one expert, from the block map) x 512 weight columns: 256 columns of the
+// gate bank and the same 256 of the up bank (S6), or 512 columns of the down
+// bank (S7), over the whole reduction dimension in slabs of 64.  Wave w owns
+// all BM rows and two 32-column blocks (gate and up columns 32w.. in S6,
+// columns 64w.. in S7), so every word of codes it dequantises feeds BM/32
+// MFMAs per block.
+//
+// Operands reach LDS with global_load_lds_dwordx4 (each lane's 16 bytes
+// land at the instruction's LDS base + 16 * lane, no registers involved)
+// into a ring of 4 stages; the loads for slab s + 3 are issued while slab s
+// is computed, so three slabs of loads are in flight and the compute reads
+// only LDS.  Per slab and stage:
+//  - A: BM rows x 64 fp16 activations (operand order), 128 bytes a row, the
+//    16-byte chunk c of row r at position c ^ (r % 8).  Rows past the tile's
+//    end load a valid row whose results are never stored.
+//  - B: packed codes, [512 columns][reduction half] x 16 bytes (32 codes):
+//    one load instruction covers 32 columns x 32 contiguous bytes of each
+//    (a fully 64-column-spread layout without bank conflicts measured
+//    slower: twice the cache lines per load instruction).  Each lane
+//    dequantises its 16 bytes in registers (13 VALU instructions per 8
+//    codes) against the row's scale and bias converted to fp16.
+//  - S: per column the 32-bit words holding its scale and bias for the slab.
+// One wait (s_waitcnt on this wave's own outstanding loads, a count known
+// at compile time) and one barrier per slab; the slab loop has no branches.  MFMA v_mfma_f32_32x32x16_f16,
+// fp32 accumulation.
 // Work items (tile, column block) are spread over the 8 XCDs in contiguous
 // ranges, so the column blocks of one tile, and the tiles of one expert, run
 // on the same XCD at about the same time and share its L2.
@@ -26,7 +39,12 @@ namespace moe {
 namespace {
 
 constexpr int kSlabK = 64;
-constexpr int kLdsRow = kSlabK + 8;  // halfs per LDS row (144 bytes)
+constexpr int kStages = 4;
+constexpr int kGemmThreads = 512;
+constexpr int kGemmWaves = kGemmThreads / 64;
+constexpr int kBCols = 512;                 // weight columns per workgroup
+constexpr int kBStage = kBCols * 32;        // bytes of codes per stage
+constexpr int kSStage = kBCols * 2 * 4;     // bytes of scale and bias words per stage
 
 struct MfmaParams {
   const half_t* a;
@@ -36,15 +54,42 @@ struct MfmaParams {
   const int32_t* blocks;
   const int32_t* num_blocks;
   void* out;
-  int N, K, G, top_k, E, P, max_blocks;
+  int N, K, log2_G, top_k, E, P, max_blocks;
 };
 
+// global_load_lds_dwordx4 / _dword: each lane's 16 (4) bytes at g land in
+// LDS at l + 16 (4) * lane; l must be the same for the whole wave.
+__device__ __forceinline__ void lds_load16(const void* g, char* l) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)l, 16, 0, 0);
+}
+__device__ __forceinline__ void lds_load4(const void* g, char* l) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)l, 4, 0, 0);
+}
+
+// s_waitcnt vmcnt(n) (expcnt and lgkmcnt not waited on), then a workgroup
+// barrier.  The asm is a compiler memory barrier, so no LDS access moves
+// across it; no fence is used because a fence would also wait for the
+// loads still in flight for later slabs.
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+  asm volatile("s_barrier" ::: "memory");
+}
+
 template <int MODE, int MB>
-__global__ __launch_bounds__(256, 2) void w4_mfma_kernel(const MfmaParams p) {
+__global__ __launch_bounds__(kGemmThreads, 1) void w4_mfma_kernel(const MfmaParams p) {
+  constexpr bool GATE_UP = MODE == MOE_GEMM_GATE_UP_SWIGLU;
   constexpr int BM = MB * 32;
-  constexpr int WG_N = MODE == MOE_GEMM_GATE_UP_SWIGLU ? 128 : 256;
-  constexpr int CH = BM * (kSlabK / 8) / 256;  // 16-byte A chunks per thread per slab
-  __shared__ half_t lds_a[2][BM * kLdsRow];
+  constexpr int A_BYTES = BM * 128;                      // per stage
+  constexpr int STAGE = A_BYTES + kBStage + kSStage;
+  constexpr int A_INSTR = BM / 8;                        // 1 KiB A loads per stage
+  constexpr int A_PER_WAVE = A_INSTR >= kGemmWaves ? A_INSTR / kGemmWaves : 1;
+  constexpr int B_PER_WAVE = kBStage / 1024 / kGemmWaves;  // 2
+  constexpr int S_PER_WAVE = kSStage / 256 / kGemmWaves;   // 2 (dword loads: 256 B each)
+  constexpr int D = A_PER_WAVE + B_PER_WAVE + S_PER_WAVE;  // loads per wave per slab
+  constexpr int OUT_COLS = GATE_UP ? kBCols / 2 : kBCols; // output columns per workgroup
+  __shared__ __attribute__((aligned(16))) char lds[kStages * STAGE];
   __shared__ float row_w[BM];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -52,7 +97,8 @@ __global__ __launch_bounds__(256, 2) void w4_mfma_kernel(const MfmaParams p) {
 
   // ---- work item: XCD-contiguous ranges over (tile, column block)
   const int nblk = min(*p.num_blocks, p.max_blocks);
-  const int nbn = p.N / WG_N;
+  const int N = p.N, K = p.K;
+  const int nbn = (N + OUT_COLS - 1) / OUT_COLS;
   const int total = nblk * nbn;
   const int span = (total + kNumXcd - 1) / kNumXcd;
   const int local = blockIdx.x / kNumXcd;
@@ -63,65 +109,103 @@ __global__ __launch_bounds__(256, 2) void w4_mfma_kernel(const MfmaParams p) {
   const int e = p.blocks[3 * tile], row0 = p.blocks[3 * tile + 1], rows = p.blocks[3 * tile + 2];
   // a malformed block map is skipped, never dereferenced out of bounds
   if (e < 0 || e >= p.E || rows <= 0 || rows > BM || row0 < 0 || row0 > p.P - rows) return;
-  const int K = p.K, N = p.N;
 
-  // ---- A staging addresses (fixed rows for the whole K loop)
-  const half_t* asrc[CH];
-  int aoff[CH];
+  // ---- A loads: instruction j covers rows 8j..8j+7; lane l fills physical
+  // chunk l % 8 of row 8j + l / 8, i.e. logical chunk (l % 8) ^ (l / 8).
+  const half_t* asrc[A_PER_WAVE];
+  int a_lds[A_PER_WAVE];
 #pragma unroll
-  for (int c = 0; c < CH; c++) {
-    const int idx = tid + 256 * c, r = idx >> 3, ch = idx & 7;
-    aoff[c] = r * kLdsRow + ch * 8;
-    asrc[c] = nullptr;
-    if (r < rows) {
-      int srow = row0 + r;
-      if (MODE == MOE_GEMM_GATE_UP_SWIGLU) {
-        const int pair = p.sorted_pairs[row0 + r];
-        srow = (pair >= 0 && pair < p.P) ? pair / p.top_k : -1;
-      }
-      if (srow >= 0) asrc[c] = p.a + (size_t)srow * K + ch * 8;
+  for (int a = 0; a < A_PER_WAVE; a++) {
+    const int j = A_INSTR >= kGemmWaves ? wave + kGemmWaves * a : wave % A_INSTR;
+    const int r = 8 * j + (lane >> 3);
+    const int c = (lane & 7) ^ (lane >> 3);
+    int srow = row0 + min(r, rows - 1);
+    if (GATE_UP) {
+      const int pair = p.sorted_pairs[srow];
+      srow = (pair >= 0 && pair < p.P) ? pair / p.top_k : 0;
     }
+    asrc[a] = p.a + (size_t)srow * K + 8 * c;
+    a_lds[a] = 1024 * j;
   }
-  if (MODE == MOE_GEMM_DOWN && tid < BM) {
+  if (!GATE_UP && tid < BM) {
     const int pair = tid < rows ? p.sorted_pairs[row0 + tid] : -1;
     row_w[tid] = (pair >= 0 && pair < p.P) ? p.topk_weights[pair] : 0.0f;
   }
 
-  // ---- B addresses: column block cb of this wave
-  const uint32_t* qp[2];
-  const uint16_t* sp[2];
-  const uint16_t* bp[2];
+  // weight column bc (0..511) of this tile: bank and row of the bank
+  auto bank_col = [&](int bc, const moe_w4_bank*& bank) -> int {
+    int n;
+    if (GATE_UP) {
+      bank = ((bc >> 5) & 1) ? &p.b1 : &p.b0;
+      n = nb * OUT_COLS + (bc >> 6) * 32 + (bc & 31);
+    } else {
+      bank = &p.b0;
+      n = nb * OUT_COLS + bc;
+    }
+    return min(n, N - 1);  // columns past N load a valid row, never stored
+  };
+
+  // ---- B loads: instruction j covers columns 32j..32j+31, lane l fills
+  // column 32j + l / 2, reduction half l % 2 (16 bytes = 32 codes).
+  const uint32_t* bsrc[B_PER_WAVE];
 #pragma unroll
-  for (int cb = 0; cb < 2; cb++) {
-    const moe_w4_bank& bank = (MODE == MOE_GEMM_GATE_UP_SWIGLU && cb == 1) ? p.b1 : p.b0;
-    const int n = MODE == MOE_GEMM_GATE_UP_SWIGLU ? nb * 128 + wave * 32 + col
-                                                  : nb * 256 + wave * 64 + cb * 32 + col;
-    const size_t rowi = (size_t)e * N + n;
-    qp[cb] = bank.qweight + rowi * (K / 8) + 4 * khalf;
-    sp[cb] = bank.scales + rowi * (K / p.G);
-    bp[cb] = bank.biases + rowi * (K / p.G);
+  for (int b = 0; b < B_PER_WAVE; b++) {
+    const int j = B_PER_WAVE * wave + b;
+    const moe_w4_bank* bank;
+    const int n = bank_col(32 * j + (lane >> 1), bank);
+    bsrc[b] = bank->qweight + ((size_t)e * N + n) * (K / 8) + 4 * (lane & 1);
   }
 
-  auto load_a = [&](int s, uint4* v) {
+  // ---- scale / bias words: instruction j (0..15) covers words 64j..64j+63
+  // of the stage's 1024: scales of columns 0..511, then biases.  Lane l
+  // loads the aligned 32-bit word holding the scale (bias) of group
+  // g(s) = 64 s / G of column 64 (j % 8) + l: the two groups 2i, 2i+1 of an
+  // even-aligned pair (for G = 32 exactly the slab's two groups; K / G is
+  // even for G <= 64, and for G = 128 the word is picked by address).
+  const int log2G = p.log2_G;
+  const int gpr = K >> log2G;  // groups per row
+  const uint16_t* ssrc[S_PER_WAVE];
 #pragma unroll
-    for (int c = 0; c < CH; c++)
-      v[c] = asrc[c] ? *reinterpret_cast<const uint4*>(asrc[c] + s * kSlabK) : make_uint4(0, 0, 0, 0);
-  };
-  auto store_a = [&](int buf, const uint4* v) {
+  for (int t = 0; t < S_PER_WAVE; t++) {
+    const int j = S_PER_WAVE * wave + t;
+    const moe_w4_bank* bank;
+    const int n = bank_col(64 * (j & 7) + lane, bank);
+    ssrc[t] = (j < 8 ? bank->scales : bank->biases) + ((size_t)e * N + n) * gpr;
+  }
+  auto issue_scales = [&](int s, char* base) {
+    const int g = (s * kSlabK) >> log2G;
 #pragma unroll
-    for (int c = 0; c < CH; c++) {
-      uint4 d = MODE == MOE_GEMM_DOWN ? interleave_halves(v[c]) : v[c];
-      *reinterpret_cast<uint4*>(&lds_a[buf][aoff[c]]) = d;
+    for (int t = 0; t < S_PER_WAVE; t++) {
+      const uintptr_t a = (uintptr_t)(ssrc[t] + g) & ~(uintptr_t)3;
+      lds_load4(reinterpret_cast<const void*>(a),
+                base + A_BYTES + kBStage + 256 * (S_PER_WAVE * wave + t));
     }
   };
-  auto load_b = [&](int s, uint4* q, uint16_t* sc, uint16_t* bi) {
-    const int g = (s * kSlabK + 32 * khalf) / p.G;
+  // in compute: the 16-bit half of the loaded word that holds this lane's
+  // group; the word was loaded from the row's element index rounded down to
+  // even, so the half is that index's parity
+  size_t selem[2];
+  bool active = true;
 #pragma unroll
-    for (int cb = 0; cb < 2; cb++) {
-      q[cb] = *reinterpret_cast<const uint4*>(qp[cb] + s * (kSlabK / 8));
-      sc[cb] = sp[cb][g];
-      bi[cb] = bp[cb][g];
-    }
+  for (int cb = 0; cb < 2; cb++) {
+    const moe_w4_bank* bank;
+    const int n = bank_col(wave * 64 + cb * 32 + col, bank);
+    selem[cb] = ((size_t)e * N + n) * gpr;
+  }
+  {
+    const int first = nb * OUT_COLS + (GATE_UP ? wave * 32 : wave * 64);
+    active = first < N;  // uniform per wave
+  }
+
+  auto issue = [&](int s, int stage) {
+    char* base = lds + stage * STAGE;
+#pragma unroll
+    for (int a = 0; a < A_PER_WAVE; a++)
+      lds_load16(asrc[a] + s * kSlabK, base + a_lds[a]);
+#pragma unroll
+    for (int b = 0; b < B_PER_WAVE; b++)
+      lds_load16(bsrc[b] + s * (kSlabK / 8), base + A_BYTES + 1024 * (B_PER_WAVE * wave + b));
+    issue_scales(s, base);
   };
 
   floatx16_t acc[MB][2];
@@ -130,59 +214,59 @@ __global__ __launch_bounds__(256, 2) void w4_mfma_kernel(const MfmaParams p) {
 #pragma unroll
     for (int cb = 0; cb < 2; cb++) acc[mb][cb] = floatx16_t{};
 
-  uint4 av[CH];
-  uint4 qc[2];
-  uint16_t scl[2], bia[2];
-  load_a(0, av);
-  load_b(0, qc, scl, bia);
-  store_a(0, av);
-  __syncthreads();
-
-  const int S = K / kSlabK;
-  for (int s = 0; s < S; s++) {
-    const bool more = s + 1 < S;
-    uint4 qn[2];
-    uint16_t scn[2], bin[2];
-    if (more) {
-      load_a(s + 1, av);
-      load_b(s + 1, qn, scn, bin);
-    }
-    const half_t* abuf = lds_a[s & 1];
+  auto compute = [&](int s, int stage) {
+    const char* base = lds + stage * STAGE;
+    u32x4 q[2];
+#pragma unroll
+    for (int cb = 0; cb < 2; cb++)
+      q[cb] = *reinterpret_cast<const u32x4*>(base + A_BYTES + (wave * 64 + cb * 32 + col) * 32 +
+                                              16 * khalf);
+    const int g = (s * kSlabK + 32 * khalf) >> log2G;
     half2_t s2[2], b2[2];
 #pragma unroll
     for (int cb = 0; cb < 2; cb++) {
-      s2[cb] = bf16_pair_to_half2(scl[cb]);
-      b2[cb] = bf16_pair_to_half2(bia[cb]);
+      const int bc = wave * 64 + cb * 32 + col;
+      const uint32_t* sw = reinterpret_cast<const uint32_t*>(base + A_BYTES + kBStage);
+      const int sh = 16 * (int)((selem[cb] + g) & 1);
+      s2[cb] = bf16_pair_to_half2((sw[bc] >> sh) & 0xFFFFu);
+      b2[cb] = bf16_pair_to_half2((sw[kBCols + bc] >> sh) & 0xFFFFu);
     }
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       half8_t bf[2];
 #pragma unroll
-      for (int cb = 0; cb < 2; cb++) {
-        const uint32_t w = i == 0 ? qc[cb].x : i == 1 ? qc[cb].y : i == 2 ? qc[cb].z : qc[cb].w;
-        bf[cb] = __builtin_bit_cast(half8_t, dequant_word(w, s2[cb], b2[cb]));
-      }
+      for (int cb = 0; cb < 2; cb++)
+        bf[cb] = __builtin_bit_cast(half8_t, dequant_word(q[cb][i], s2[cb], b2[cb]));
 #pragma unroll
       for (int mb = 0; mb < MB; mb++) {
+        const int r = mb * 32 + col;
         const half8_t af = *reinterpret_cast<const half8_t*>(
-            &abuf[(mb * 32 + col) * kLdsRow + 32 * khalf + 8 * i]);
+            base + r * 128 + (((4 * khalf + i) ^ (col & 7)) << 4));
 #pragma unroll
         for (int cb = 0; cb < 2; cb++)
           acc[mb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, bf[cb], acc[mb][cb], 0, 0, 0);
       }
     }
-    if (more) store_a((s + 1) & 1, av);
-    __syncthreads();
-    if (more) {
-#pragma unroll
-      for (int cb = 0; cb < 2; cb++) {
-        qc[cb] = qn[cb];
-        scl[cb] = scn[cb];
-        bia[cb] = bin[cb];
-      }
-    }
+  };
+
+  // ---- pipeline: slab s lives in stage s % 4.  Every slab step issues the
+  // same loads (slabs past the end reload the last slab into a stage that is
+  // never read again), so when slab s is about to be computed exactly the
+  // loads of two later slabs (2 * D instructions of this wave) were issued
+  // after its own: waiting until at most 2 * D are outstanding means slab s
+  // has landed.  Right after the barrier, stage (s + 3) % 4 (computed last at
+  // slab s - 1, by every wave) is refilled with slab s + 3.
+  const int S = K / kSlabK;
+  issue(0, 0);
+  issue(min(1, S - 1), 1);
+  issue(min(2, S - 1), 2);
+  for (int s = 0; s < S; s++) {
+    wait_vm_barrier<2 * D>();
+    issue(min(s + 3, S - 1), (s + 3) & 3);
+    compute(s, s & 3);
   }
 
+  if (!active) return;
   // ---- epilogue.  Accumulator register r of lane l holds row
   // 8*(r/4) + 4*(l/32) + r%4 and column l%32 of each 32x32 block.
 #pragma unroll
@@ -191,38 +275,52 @@ __global__ __launch_bounds__(256, 2) void w4_mfma_kernel(const MfmaParams p) {
     for (int r = 0; r < 16; r++) {
       const int row = mb * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3);
       if (row >= rows) continue;
-      const size_t orow = (size_t)(row0 + row) * N;
-      if (MODE == MOE_GEMM_GATE_UP_SWIGLU) {
-        const int n = nb * 128 + wave * 32 + col;
-        reinterpret_cast<half_t*>(p.out)[orow + n] = (half_t)silu_mul(acc[mb][0][r], acc[mb][1][r]);
+      if (GATE_UP) {
+        // h in operand order: column 8g + j stored at 8g + interleaved_pos(j)
+        const int n = nb * OUT_COLS + wave * 32 + (col & ~7) + interleaved_pos(col & 7);
+        reinterpret_cast<half_t*>(p.out)[(size_t)(row0 + row) * N + n] =
+            (half_t)silu_mul(acc[mb][0][r], acc[mb][1][r]);
       } else {
         const float w = row_w[row];
+        float* orow = reinterpret_cast<float*>(p.out) + (size_t)(row0 + row) * N;
 #pragma unroll
-        for (int cb = 0; cb < 2; cb++) {
-          const int n = nb * 256 + wave * 64 + cb * 32 + col;
-          reinterpret_cast<float*>(p.out)[orow + n] = w * acc[mb][cb][r];
-        }
+        for (int cb = 0; cb < 2; cb++)
+          orow[nb * OUT_COLS + wave * 64 + cb * 32 + col] = w * acc[mb][cb][r];
       }
     }
   }
 }
 
 // x bf16 -> fp16, each 8-element chunk interleaved (0,4,1,5,2,6,3,7).
-// bf16 values inside the fp16 range convert exactly.
 __global__ __launch_bounds__(256) void stage_x_kernel(const uint4* __restrict__ in,
                                                       uint4* __restrict__ out, int64_t n8) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n8) return;
-  const uint4 v = in[i];
-  auto lo = [](uint32_t d) { return (half_t)__uint_as_float(d << 16); };
-  auto hi = [](uint32_t d) { return (half_t)__uint_as_float(d & 0xFFFF0000u); };
-  const half2_t o0 = {lo(v.x), lo(v.z)}, o1 = {hi(v.x), hi(v.z)};
-  const half2_t o2 = {lo(v.y), lo(v.w)}, o3 = {hi(v.y), hi(v.w)};
-  out[i] = make_uint4(__builtin_bit_cast(uint32_t, o0), __builtin_bit_cast(uint32_t, o1),
-                      __builtin_bit_cast(uint32_t, o2), __builtin_bit_cast(uint32_t, o3));
+  out[i] = bf16x8_to_half_interleaved(in[i]);
 }
 
-// y[t][:] = sum_j y_sorted[pair_slot[t*k + j]][:], j ascending, fp32.
+template <int MODE>
+hipError_t launch_mode(const GemmArgs& a, hipStream_t s) {
+  const int64_t P = (int64_t)a.T * a.top_k;
+  const int64_t max_blocks = P / a.block_m + (P < a.E ? P : a.E);
+  const int log2_G = a.G == 32 ? 5 : a.G == 64 ? 6 : 7;  // G in {32, 64, 128}
+  MfmaParams p{a.a, a.b0, a.b1, a.sorted_pairs, a.topk_weights, a.blocks, a.num_blocks, a.out,
+               a.N, a.K, log2_G, a.top_k, a.E, (int)P, (int)max_blocks};
+  const int out_cols = MODE == MOE_GEMM_GATE_UP_SWIGLU ? kBCols / 2 : kBCols;
+  const int64_t items = max_blocks * ((a.N + out_cols - 1) / out_cols);
+  const int64_t grid = ((items + kNumXcd - 1) / kNumXcd) * kNumXcd;
+  switch (a.block_m) {
+    case 32: w4_mfma_kernel<MODE, 1><<<grid, kGemmThreads, 0, s>>>(p); break;
+    case 64: w4_mfma_kernel<MODE, 2><<<grid, kGemmThreads, 0, s>>>(p); break;
+    case 128: w4_mfma_kernel<MODE, 4><<<grid, kGemmThreads, 0, s>>>(p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+// y[t][:] = sum_j y_sorted[pair_slot[t*k + j]][:], j ascending, fp32: the
+// k weighted expert outputs of a token added in a fixed order, so the layer
+// output is deterministic.
 __global__ __launch_bounds__(256) void combine_kernel(const float4* __restrict__ y_sorted,
                                                       const int32_t* __restrict__ pair_slot,
                                                       float4* __restrict__ y, int T, int H4,
@@ -242,24 +340,6 @@ __global__ __launch_bounds__(256) void combine_kernel(const float4* __restrict__
     acc.w += v.w;
   }
   y[i] = acc;
-}
-
-template <int MODE>
-hipError_t launch_mode(const GemmArgs& a, hipStream_t s) {
-  const int64_t P = (int64_t)a.T * a.top_k;
-  const int64_t max_blocks = P / a.block_m + (P < a.E ? P : a.E);
-  MfmaParams p{a.a, a.b0, a.b1, a.sorted_pairs, a.topk_weights, a.blocks, a.num_blocks, a.out,
-               a.N, a.K, a.G, a.top_k, a.E, (int)P, (int)max_blocks};
-  const int wg_n = MODE == MOE_GEMM_GATE_UP_SWIGLU ? 128 : 256;
-  const int64_t items = max_blocks * (a.N / wg_n);
-  const int64_t grid = ((items + kNumXcd - 1) / kNumXcd) * kNumXcd;
-  switch (a.block_m) {
-    case 32: w4_mfma_kernel<MODE, 1><<<grid, 256, 0, s>>>(p); break;
-    case 64: w4_mfma_kernel<MODE, 2><<<grid, 256, 0, s>>>(p); break;
-    case 128: w4_mfma_kernel<MODE, 4><<<grid, 256, 0, s>>>(p); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
 }
 
 }  // namespace

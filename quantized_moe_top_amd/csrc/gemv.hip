@@ -97,15 +97,16 @@ __global__ __launch_bounds__(256) void gemv_gate_up_kernel(const GemvParams p) {
       g += __shfl_xor(g, off);
       u += __shfl_xor(u, off);
     }
-    if (lane == 0 && tok[m] >= 0)
-      reinterpret_cast<half_t*>(p.out)[(size_t)(row0 + m) * p.N + n] = (half_t)silu_mul(g, u);
+    if (lane == 0 && tok[m] >= 0)  // h in operand order (see the MFMA kernel)
+      reinterpret_cast<half_t*>(p.out)[(size_t)(row0 + m) * p.N + (n & ~7) + interleaved_pos(n & 7)] =
+          (half_t)silu_mul(g, u);
   }
 }
 
 // S7 at decode sizes: a group of L lanes (L = largest power of two <=
 // min(64, K/32)) owns one output row n of the down bank; a wave covers 64/L
-// rows, a workgroup 4 waves.  a = h fp16 [P][K] in natural order, interleaved
-// in registers to match the dequantised code order.
+// rows, a workgroup 4 waves.  a = h fp16 [P][K], already in the dequantised
+// code order.
 __global__ __launch_bounds__(256) void gemv_down_kernel(const GemvParams p, int L) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int R = 64 / L;
@@ -133,8 +134,7 @@ __global__ __launch_bounds__(256) void gemv_down_kernel(const GemvParams p, int 
     for (int m = 0; m < kGemvMaxTokens; m++) {
       if (m >= rows) break;
       const uint4* hp = reinterpret_cast<const uint4*>(p.a + (size_t)(row0 + m) * K + kb);
-      uint4 hv[4] = {interleave_halves(hp[0]), interleave_halves(hp[1]), interleave_halves(hp[2]),
-                     interleave_halves(hp[3])};
+      uint4 hv[4] = {hp[0], hp[1], hp[2], hp[3]};
       acc[m] = dot32(w, hv, acc[m]);
     }
   }

@@ -16,53 +16,74 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
 typedef float floatx16_t __attribute__((ext_vector_type(16)));
+// 16 bytes as a native vector (kept in registers more reliably than uint4,
+// which is a struct)
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 constexpr int kNumXcd = 8;           // MI355X: 8 accelerator complex dies
 constexpr int kGemvMaxTokens = 8;    // T at or below this runs the GEMV path
-constexpr int kChunkPairs = 1024;    // pairs per histogram/scatter chunk
 
 __device__ __forceinline__ float bf16_bits_to_float(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }
 
-// Reorders the eight 16-bit values of a 16-byte chunk from (0..7) to
-// (0,4,1,5,2,6,3,7): the order in which the 4-bit unpack below yields the
-// codes of one packed word.  Activations are stored or staged in this order
+// Activations, and the hidden vector h, are held in "operand order": within
+// every run of 8 consecutive elements the order is (0,4,1,5,2,6,3,7), the
+// order in which the 4-bit unpack below yields the codes of one packed word,
 // so that a fragment of 8 activations lines up with one word of codes.
-__device__ __forceinline__ uint4 interleave_halves(uint4 d) {
-  uint4 o;
-  o.x = __builtin_amdgcn_perm(d.z, d.x, 0x05040100u);  // (v0, v4)
-  o.y = __builtin_amdgcn_perm(d.z, d.x, 0x07060302u);  // (v1, v5)
-  o.z = __builtin_amdgcn_perm(d.w, d.y, 0x05040100u);  // (v2, v6)
-  o.w = __builtin_amdgcn_perm(d.w, d.y, 0x07060302u);  // (v3, v7)
-  return o;
+
+// (a & mask) | magic in one VALU instruction; mask in an SGPR, magic in a
+// VGPR (a VOP3 instruction may read only one scalar operand here).
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t magic) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(mask), "v"(magic));
+  return r;
 }
 
 // Dequantises one 32-bit word of eight 4-bit codes into eight fp16 weights
 // q * scale + bias, in the interleaved order (q0,q4,q1,q5,q2,q6,q3,q7).
-// OR-ing a code into the mantissa of 1024.0h gives 1024 + q exactly; the
-// subtraction recovers q exactly and the fused multiply-add rounds once (it
-// is exact when bias = -8 * scale, because (q - 8) * scale then needs at most
-// 11 significant bits).
+// Each 16-bit half of the word holds two codes of interest at bits 0..3 and
+// 4..7 (after a shift by 8 for the other two):
+//  - OR-ing the low nibble into the mantissa of 1024.0h gives 1024 + q;
+//  - OR-ing the second nibble, still at bits 4..7, into the mantissa of
+//    64.0h gives 64 + q (the mantissa step there is 1/16);
+// both exactly.  Subtracting 1024 or 64 recovers q exactly and one fused
+// multiply-add rounds once (exactly when bias = -8 * scale, because
+// (q - 8) * scale then needs at most 11 significant bits).  13 VALU
+// instructions per word.
 __device__ __forceinline__ uint4 dequant_word(uint32_t w, half2_t s2, half2_t b2) {
-  const uint32_t m = 0x000F000Fu, magic = 0x64006400u;
-  const half2_t k1024 = {(half_t)1024.0f, (half_t)1024.0f};
-  uint32_t r[4];
-  r[0] = (w & m) | magic;
-  r[1] = ((w >> 4) & m) | magic;
-  r[2] = ((w >> 8) & m) | magic;
-  r[3] = ((w >> 12) & m) | magic;
-#pragma unroll
-  for (int i = 0; i < 4; i++) {
-    half2_t q = __builtin_bit_cast(half2_t, r[i]) - k1024;
-    half2_t v = __builtin_elementwise_fma(q, s2, b2);
-    r[i] = __builtin_bit_cast(uint32_t, v);
-  }
-  return make_uint4(r[0], r[1], r[2], r[3]);
+  const uint32_t m_lo = 0x000F000Fu, m_hi = 0x00F000F0u;
+  const uint32_t k1024 = 0x64006400u, k64 = 0x54005400u;
+  const half2_t c1024 = {(half_t)1024.0f, (half_t)1024.0f};
+  const half2_t c64 = {(half_t)64.0f, (half_t)64.0f};
+  const uint32_t w8 = w >> 8;
+  const half2_t q0 = __builtin_bit_cast(half2_t, and_or(w, m_lo, k1024)) - c1024;   // q0, q4
+  const half2_t q1 = __builtin_bit_cast(half2_t, and_or(w, m_hi, k64)) - c64;       // q1, q5
+  const half2_t q2 = __builtin_bit_cast(half2_t, and_or(w8, m_lo, k1024)) - c1024;  // q2, q6
+  const half2_t q3 = __builtin_bit_cast(half2_t, and_or(w8, m_hi, k64)) - c64;      // q3, q7
+  return make_uint4(__builtin_bit_cast(uint32_t, __builtin_elementwise_fma(q0, s2, b2)),
+                    __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(q1, s2, b2)),
+                    __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(q2, s2, b2)),
+                    __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(q3, s2, b2)));
 }
 
-__device__ __forceinline__ half2_t bf16_pair_to_half2(uint16_t s) {
+// Position of column j (0..7) of an 8-column run in the interleaved order.
+__device__ __forceinline__ int interleaved_pos(int j) { return 2 * (j & 3) + (j >> 2); }
+
+// Eight bf16 values (one 16-byte chunk) -> eight fp16 values in the
+// interleaved order above.  bf16 values inside the fp16 range convert
+// exactly.
+__device__ __forceinline__ uint4 bf16x8_to_half_interleaved(uint4 v) {
+  auto lo = [](uint32_t d) { return (half_t)__uint_as_float(d << 16); };
+  auto hi = [](uint32_t d) { return (half_t)__uint_as_float(d & 0xFFFF0000u); };
+  const half2_t o0 = {lo(v.x), lo(v.z)}, o1 = {hi(v.x), hi(v.z)};
+  const half2_t o2 = {lo(v.y), lo(v.w)}, o3 = {hi(v.y), hi(v.w)};
+  return make_uint4(__builtin_bit_cast(uint32_t, o0), __builtin_bit_cast(uint32_t, o1),
+                    __builtin_bit_cast(uint32_t, o2), __builtin_bit_cast(uint32_t, o3));
+}
+
+__device__ __forceinline__ half2_t bf16_pair_to_half2(uint32_t s) {
   half_t h = (half_t)bf16_bits_to_float(s);
   return half2_t{h, h};
 }
@@ -74,15 +95,24 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
 // ---------------------------------------------------------------- launchers --
 // Each returns hipSuccess or the launch error.  Arguments are validated by
 // the callers in api.hip.
-hipError_t launch_router_gemm(const uint16_t* x, const uint16_t* wr, float* logits, int T, int H,
-                              int E, hipStream_t s);
-hipError_t launch_topk(const float* logits, int T, int E, int k, int32_t* ids, float* w,
-                       hipStream_t s);
-hipError_t launch_build_blocks(const int32_t* ids, int P, int E, int block_m, int32_t* counts,
-                               int32_t* offsets, int32_t* sorted_pairs, int32_t* pair_slot,
-                               int32_t* blocks, int32_t* num_blocks, int32_t* scratch,
-                               hipStream_t s);
-int build_blocks_chunks(int64_t P);
+// Routing chunks: consecutive tokens handled by one routing workgroup and
+// histogrammed together (at most 256 chunks).
+int route_chunk_tokens(int64_t T);
+int route_chunks(int64_t T);
+
+// S0 (when wr) + S1 over all T tokens; with xh and chunk_hist (both or
+// neither) also the per-chunk expert histogram and the fp16 staging of x.
+hipError_t launch_route(const uint16_t* x, const uint16_t* wr, float* logits, int T, int H, int E,
+                        int k, int32_t* ids, float* w, half_t* xh, int32_t* chunk_hist,
+                        hipStream_t s);
+// Per-chunk expert histogram of caller-given ids [T][k].
+hipError_t launch_chunk_hist(const int32_t* ids, int T, int k, int E, int32_t* chunk_hist,
+                             hipStream_t s);
+// S2 (totals) - S5 from the per-chunk histograms.
+hipError_t launch_scan_scatter(const int32_t* ids, int T, int k, int E, const int32_t* chunk_hist,
+                               int block_m, int32_t* counts, int32_t* offsets,
+                               int32_t* sorted_pairs, int32_t* pair_slot, int32_t* blocks,
+                               int32_t* num_blocks, hipStream_t s);
 
 // x bf16 [T][H] -> fp16 [T][H] with every 8-chunk interleaved (see above).
 hipError_t launch_stage_x(const uint16_t* x, half_t* xh, int64_t n_elems, hipStream_t s);
@@ -101,7 +131,9 @@ struct GemmArgs {
 hipError_t launch_w4_mfma(const GemmArgs& a, hipStream_t s);
 hipError_t launch_w4_gemv(const GemmArgs& a, hipStream_t s);
 
+// S8: y[t] = sum_j y_sorted[pair_slot[t * k + j]], j ascending.
 hipError_t launch_combine(const float* y_sorted, const int32_t* pair_slot, float* y, int T,
                           int H, int k, hipStream_t s);
+
 
 }  // namespace moe

@@ -48,6 +48,19 @@ def cpu(t: torch.Tensor) -> np.ndarray:
     return t.detach().cpu().numpy()
 
 
+# Within every run of 8 columns the library stores h in the order
+# (0,4,1,5,2,6,3,7) ("operand order", include/moe_w4.h): column j of a run
+# sits at position 2*(j % 4) + j // 4.
+_H_POS = np.array([2 * (j % 4) + j // 4 for j in range(8)])
+
+
+def h_natural(h_stored: np.ndarray) -> np.ndarray:
+    """Columns of h in natural order, from the library's operand order."""
+    n = h_stored.shape[-1]
+    idx = (np.arange(n) // 8) * 8 + _H_POS[np.arange(n) % 8]
+    return h_stored[..., idx]
+
+
 def router_error_bound(x: torch.Tensor, wr: torch.Tensor) -> np.ndarray:
     """Forward error bound of an fp32 sum of H exact products in any order,
     gamma_H * sum_h |x_h Wr_eh| with gamma_H = H u / (1 - H u), u = 2^-24,

@@ -58,7 +58,8 @@ def test_max_blocks_and_workspace_queries(L):
     d.T = 16
     d.H, d.I, d.E, d.top_k, d.group_size = 256, 128, 8, 2, 32
     assert L.moe_ffn_block_m(ctypes.byref(d)) == 32
-    assert L.moe_ffn_workspace_bytes(ctypes.byref(d), 0) > 16 * 2 * 256 * 4
+    # at least x staged in fp16 and h [P, I] in fp16
+    assert L.moe_ffn_workspace_bytes(ctypes.byref(d), 0) >= 16 * 256 * 2 + 16 * 2 * 128 * 2
     d.H = 100
     assert L.moe_ffn_workspace_bytes(ctypes.byref(d), 0) == 0
 
