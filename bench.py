@@ -157,16 +157,19 @@ def main():
     name = args.workload
     log(f"[bench] drawing workload {name}")
     host = synth.make_layer(name)
-    lay = host.to(dev)
+    # the banks are packed once into the kernels' layout (load time, untimed)
+    lay = api.pack_layer(host.to(dev))
+    torch.cuda.synchronize()
     T, E, k = lay.T, lay.E, lay.k
 
     # weight copies for cold reads
-    per_copy = lay.gate.nbytes + lay.up.nbytes + lay.down.nbytes + \
+    nbytes = lambda b: (b.words.numel() + b.sb.numel()) * 4
+    per_copy = nbytes(lay.gate) + nbytes(lay.up) + nbytes(lay.down) + \
         (lay.router_weight.numel() * 2 if lay.router_weight is not None else 0)
     R = max(1, -(-ROTATE_BYTES // per_copy))
     copies = [lay]
     for _ in range(R - 1):
-        gate, up, down = (synth.W4Bank(b.qweight.clone(), b.scales.clone(), b.biases.clone())
+        gate, up, down = (dataclasses.replace(b, words=b.words.clone(), sb=b.sb.clone())
                           for b in (lay.gate, lay.up, lay.down))
         wr = lay.router_weight.clone() if lay.router_weight is not None else None
         copies.append(dataclasses.replace(lay, gate=gate, up=up, down=down, router_weight=wr))

@@ -81,11 +81,37 @@ typedef struct {
   const uint16_t* biases;
 } moe_w4_bank;
 
-/* One layer's weights (device pointers). */
+/* ------------------------------------------------------------ weight pack --
+ * The compute kernels read each bank in a tile-major layout, made once from
+ * the row-major bank above by moe_w4_pack (load time, not part of a layer
+ * call; page "Perplexity's Lily beats MLX by 1.35x by doing one thing:
+ * single-model Rust/Metal engines", section "Why one model on one chip is
+ * faster": the weights are laid out in the order the kernels read fastest).
+ *  words: uint32 [E][N/32][K/64][32 columns][2 halves][4 words]: for column
+ *         32b + c and half h of slab s, the four row-major words holding codes
+ *         64s + 32h .. 64s + 32h + 31 (same nibble order).
+ *  sb:    uint32 [E][N/32][K/G][32 columns]: bf16 scale bits in the low 16
+ *         bits, bf16 bias bits in the high 16 bits.
+ * Requires N % 32 == 0, K % 128 == 0, G in {32, 64, 128}, K % G == 0. */
+typedef struct {
+  const uint32_t* words;
+  const uint32_t* sb;
+} moe_w4_packed;
+
+/* Byte sizes of the two packed buffers of one bank (host-only; 0 for
+ * unsupported sizes). */
+size_t moe_w4_packed_words_bytes(int32_t E, int32_t N, int32_t K);
+size_t moe_w4_packed_sb_bytes(int32_t E, int32_t N, int32_t K, int32_t group_size);
+/* Packs `src` (device, row-major) into words / sb (device buffers of the
+ * sizes above, 16-byte aligned, owned by the caller) on `stream`. */
+int moe_w4_pack(const moe_w4_bank* src, int32_t E, int32_t N, int32_t K, int32_t group_size,
+                uint32_t* words, uint32_t* sb, void* stream);
+
+/* One layer's weights (device pointers), banks packed by moe_w4_pack. */
 typedef struct {
   moe_dims dims;
   const uint16_t* router_weight; /* bf16 [E][H], or NULL when logits are given */
-  moe_w4_bank gate, up, down;
+  moe_w4_packed gate, up, down;
 } moe_layer;
 
 /* ------------------------------------------------------------------ S0, S1 --
@@ -160,7 +186,7 @@ typedef struct {
   int32_t N, K, group_size;
   int32_t block_m;
   const void* a;               /* see the modes above */
-  moe_w4_bank bank0, bank1;
+  moe_w4_packed bank0, bank1;  /* packed by moe_w4_pack */
   const int32_t* sorted_pairs; /* [P] */
   const float* topk_weights;   /* [P], MOE_GEMM_DOWN only */
   const int32_t* blocks;       /* [max_blocks][3] */

@@ -22,6 +22,7 @@ MOE_GEMM_DOWN = 1
 # Exported symbols, in header order.
 SYMBOLS = (
     "moe_status_string", "moe_last_error", "moe_version",
+    "moe_w4_packed_words_bytes", "moe_w4_packed_sb_bytes", "moe_w4_pack",
     "moe_route", "moe_max_blocks", "moe_build_blocks_workspace_bytes", "moe_build_blocks",
     "moe_w4_grouped_gemm_workspace_bytes", "moe_w4_grouped_gemm",
     "moe_ffn_block_m", "moe_ffn_workspace_bytes", "moe_ffn_forward", "moe_ffn_forward_timed",
@@ -38,18 +39,24 @@ class Dims(ctypes.Structure):
 
 
 class Bank(ctypes.Structure):
+    """Row-major W4 bank (moe_w4_bank)."""
     _fields_ = [("qweight", c_p), ("scales", c_p), ("biases", c_p)]
 
 
+class Packed(ctypes.Structure):
+    """Packed W4 bank (moe_w4_packed)."""
+    _fields_ = [("words", c_p), ("sb", c_p)]
+
+
 class Layer(ctypes.Structure):
-    _fields_ = [("dims", Dims), ("router_weight", c_p), ("gate", Bank), ("up", Bank),
-                ("down", Bank)]
+    _fields_ = [("dims", Dims), ("router_weight", c_p), ("gate", Packed), ("up", Packed),
+                ("down", Packed)]
 
 
 class GemmArgs(ctypes.Structure):
     _fields_ = [("mode", c_i32), ("T", c_i32), ("top_k", c_i32), ("E", c_i32), ("N", c_i32),
                 ("K", c_i32), ("group_size", c_i32), ("block_m", c_i32), ("a", c_p),
-                ("bank0", Bank), ("bank1", Bank), ("sorted_pairs", c_p), ("topk_weights", c_p),
+                ("bank0", Packed), ("bank1", Packed), ("sorted_pairs", c_p), ("topk_weights", c_p),
                 ("blocks", c_p), ("num_blocks", c_p), ("out", c_p), ("workspace", c_p),
                 ("workspace_bytes", c_sz)]
 
@@ -81,6 +88,11 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     L.moe_status_string.argtypes = [ctypes.c_int]
     L.moe_last_error.restype = ctypes.c_char_p
     L.moe_version.restype = ctypes.c_char_p
+    L.moe_w4_packed_words_bytes.restype = c_sz
+    L.moe_w4_packed_words_bytes.argtypes = [c_i32, c_i32, c_i32]
+    L.moe_w4_packed_sb_bytes.restype = c_sz
+    L.moe_w4_packed_sb_bytes.argtypes = [c_i32, c_i32, c_i32, c_i32]
+    L.moe_w4_pack.argtypes = [ctypes.POINTER(Bank), c_i32, c_i32, c_i32, c_i32, c_p, c_p, c_p]
     L.moe_route.argtypes = [c_p, c_p, c_p, c_i32, c_i32, c_i32, c_i32, c_p, c_p, c_p]
     L.moe_max_blocks.restype = c_i64
     L.moe_max_blocks.argtypes = [c_i32, c_i32, c_i32, c_i32]
@@ -98,8 +110,8 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
                                   c_p, c_sz, c_p]
     L.moe_ffn_forward_timed.argtypes = [ctypes.POINTER(Layer), c_p, c_p, c_p,
                                         ctypes.POINTER(RouteInfo), c_p, c_sz, c_p, c_p]
-    for name in ("moe_route", "moe_build_blocks", "moe_w4_grouped_gemm", "moe_ffn_forward",
-                 "moe_ffn_forward_timed"):
+    for name in ("moe_w4_pack", "moe_route", "moe_build_blocks", "moe_w4_grouped_gemm",
+                 "moe_ffn_forward", "moe_ffn_forward_timed"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L

@@ -9,14 +9,17 @@ kernels of the library.
 from __future__ import annotations
 
 import ctypes
+import dataclasses
 from typing import Optional
 
 import torch
 
 from . import _lib
-from ._lib import MOE_GEMM_DOWN, MOE_GEMM_GATE_UP_SWIGLU, Bank, Dims, GemmArgs, Layer, RouteInfo
+from ._lib import (MOE_GEMM_DOWN, MOE_GEMM_GATE_UP_SWIGLU, Bank, Dims, GemmArgs, Layer, Packed,
+                   RouteInfo)
 
-__all__ = ["route", "build_blocks", "w4_grouped_gemm", "ffn_forward", "ffn_workspace_bytes",
+__all__ = ["pack_bank", "pack_layer", "PackedBank", "PackedLayer",
+           "route", "build_blocks", "w4_grouped_gemm", "ffn_forward", "ffn_workspace_bytes",
            "ffn_block_m", "max_blocks", "stage_events", "MOE_GEMM_GATE_UP_SWIGLU", "MOE_GEMM_DOWN"]
 
 
@@ -44,6 +47,66 @@ def _bank(b, name: str) -> Bank:
     return Bank(_dev(b.qweight, f"{name}.qweight", torch.int32),
                 _dev(b.scales, f"{name}.scales", torch.bfloat16),
                 _dev(b.biases, f"{name}.biases", torch.bfloat16))
+
+
+@dataclasses.dataclass
+class PackedBank:
+    """A W4 bank in the kernels' tile-major layout (moe_w4_pack)."""
+    words: torch.Tensor  # int32 [E * N * K / 8]
+    sb: torch.Tensor     # int32 [E * N * K / G]
+    E: int
+    N: int
+    K: int
+    G: int
+
+    def struct(self) -> Packed:
+        return Packed(_dev(self.words, "words", torch.int32), _dev(self.sb, "sb", torch.int32))
+
+
+def pack_bank(bank, G: int) -> PackedBank:
+    """Packs a row-major device bank (``synth.W4Bank``) with moe_w4_pack."""
+    E, N, K8 = bank.qweight.shape
+    K = K8 * 8
+    nw = int(_L().moe_w4_packed_words_bytes(E, N, K))
+    ns = int(_L().moe_w4_packed_sb_bytes(E, N, K, G))
+    if nw == 0 or ns == 0:
+        raise ValueError(f"unsupported bank shape for packing: E={E} N={N} K={K} G={G}")
+    dev = bank.qweight.device
+    words = torch.empty(nw // 4, dtype=torch.int32, device=dev)
+    sb = torch.empty(ns // 4, dtype=torch.int32, device=dev)
+    src = _bank(bank, "bank")
+    _lib.check(_L().moe_w4_pack(ctypes.byref(src), E, N, K, G, words.data_ptr(), sb.data_ptr(),
+                                _stream()), "moe_w4_pack")
+    return PackedBank(words, sb, E, N, K, G)
+
+
+@dataclasses.dataclass
+class PackedLayer:
+    """A device ``synth.MoELayer`` whose banks are packed for the kernels."""
+    name: str
+    T: int
+    H: int
+    I: int
+    E: int
+    k: int
+    G: int
+    x: torch.Tensor
+    logits: Optional[torch.Tensor]
+    router_weight: Optional[torch.Tensor]
+    gate: PackedBank
+    up: PackedBank
+    down: PackedBank
+
+
+def pack_layer(layer) -> PackedLayer:
+    """Packs the three banks of a device ``synth.MoELayer``."""
+    return PackedLayer(layer.name, layer.T, layer.H, layer.I, layer.E, layer.k, layer.G, layer.x,
+                       layer.logits, layer.router_weight, pack_bank(layer.gate, layer.G),
+                       pack_bank(layer.up, layer.G), pack_bank(layer.down, layer.G))
+
+
+def _packed(bank, G: int) -> PackedBank:
+    return bank if isinstance(bank, PackedBank) else pack_bank(bank, G)
 
 
 def max_blocks(T: int, top_k: int, E: int, block_m: int) -> int:
@@ -107,16 +170,17 @@ def w4_grouped_gemm(mode: int, a: torch.Tensor, bank0, bank1, sorted_pairs: torc
     returns y_sorted fp32 [P, H]).  Slots outside every tile are left as they
     were in ``out``."""
     gate_up = mode == MOE_GEMM_GATE_UP_SWIGLU
-    E_, N, K8 = bank0.qweight.shape
-    K = K8 * 8
+    bank0 = _packed(bank0, group_size)
+    bank1 = _packed(bank1, group_size) if bank1 is not None else None
+    N, K = bank0.N, bank0.K
     P = T * top_k
     if out is None:
         out = torch.empty((P, N), dtype=torch.float16 if gate_up else torch.float32, device=a.device)
     args = GemmArgs(mode=mode, T=T, top_k=top_k, E=E, N=N, K=K, group_size=group_size,
                     block_m=block_m,
                     a=_dev(a, "a", torch.bfloat16 if gate_up else torch.float16),
-                    bank0=_bank(bank0, "bank0"),
-                    bank1=_bank(bank1, "bank1") if bank1 is not None else Bank(0, 0, 0),
+                    bank0=bank0.struct(),
+                    bank1=bank1.struct() if bank1 is not None else Packed(0, 0),
                     sorted_pairs=_dev(sorted_pairs, "sorted_pairs", torch.int32),
                     topk_weights=_dev(topk_weights, "topk_weights", torch.float32),
                     blocks=_dev(blocks, "blocks", torch.int32),
@@ -144,10 +208,10 @@ def ffn_workspace_bytes(layer, T: Optional[int] = None) -> int:
     return int(_L().moe_ffn_workspace_bytes(ctypes.byref(d), int(layer.router_weight is not None)))
 
 
-def make_layer_struct(layer, T: int) -> Layer:
+def make_layer_struct(layer: PackedLayer, T: int) -> Layer:
     return Layer(_dims(layer, T),
                  _dev(layer.router_weight, "router_weight", torch.bfloat16),
-                 _bank(layer.gate, "gate"), _bank(layer.up, "up"), _bank(layer.down, "down"))
+                 layer.gate.struct(), layer.up.struct(), layer.down.struct())
 
 
 def stage_events(n: int = _lib.MOE_NUM_STAGES + 1):
@@ -163,11 +227,14 @@ def stage_events(n: int = _lib.MOE_NUM_STAGES + 1):
 def ffn_forward(layer, x: Optional[torch.Tensor] = None, logits: Optional[torch.Tensor] = None,
                 y: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                 info: bool = False, stage_events=None):
-    """The whole layer (S0/S1-S8) for a ``synth.MoELayer`` whose tensors are on
-    the device.  ``x`` and ``logits`` default to the layer's own.  Returns y
+    """The whole layer (S0/S1-S8) for a ``PackedLayer`` (a device
+    ``synth.MoELayer`` is packed first).  ``x`` and ``logits`` default to the
+    layer's own.  Returns y
     fp32 [T, H], plus a dict of routing-structure views into the workspace
     when ``info`` is true.  ``stage_events`` (from ``stage_events()``) runs
     ``moe_ffn_forward_timed``, recording one event per stage boundary."""
+    if not isinstance(layer, PackedLayer):
+        layer = pack_layer(layer)
     x = layer.x if x is None else x
     T, H = x.shape
     if layer.router_weight is None and logits is None:

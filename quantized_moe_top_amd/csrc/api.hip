@@ -49,10 +49,16 @@ int check_routing(int64_t T, int64_t E, int64_t k) {
   return MOE_OK;
 }
 
-int check_bank(const moe_w4_bank& b, const char* name) {
-  if (!b.qweight || !b.scales || !b.biases) return fail(MOE_ERR_NULL, "%s bank has a NULL pointer", name);
-  if (!aligned16(b.qweight)) return fail(MOE_ERR_ALIGN, "%s qweight not 16-byte aligned", name);
+int check_bank(const moe_w4_packed& b, const char* name) {
+  if (!b.words || !b.sb) return fail(MOE_ERR_NULL, "%s packed bank has a NULL pointer", name);
+  if (!aligned16(b.words) || !aligned16(b.sb))
+    return fail(MOE_ERR_ALIGN, "%s packed bank not 16-byte aligned", name);
   return MOE_OK;
+}
+
+bool pack_sizes_ok(int64_t E, int64_t N, int64_t K, int64_t G) {
+  return E >= 1 && E <= 256 && N > 0 && N % 32 == 0 && K > 0 && K % 128 == 0 &&
+         (G == 32 || G == 64 || G == 128) && K % G == 0;
 }
 
 int check_group(int64_t G, int64_t K, const char* what) {
@@ -152,6 +158,28 @@ int moe_route(const uint16_t* x, const uint16_t* router_weight, float* logits, i
   return hip_status(moe::launch_route(x, router_weight, logits, T, H, E, top_k, topk_ids,
                                       topk_weights, nullptr, nullptr, (hipStream_t)stream),
                     "route");
+}
+
+size_t moe_w4_packed_words_bytes(int32_t E, int32_t N, int32_t K) {
+  if (!pack_sizes_ok(E, N, K, 128)) return 0;  // any supported G divides K % 128 == 0
+  return (size_t)E * N * K / 2;
+}
+
+size_t moe_w4_packed_sb_bytes(int32_t E, int32_t N, int32_t K, int32_t group_size) {
+  if (!pack_sizes_ok(E, N, K, group_size)) return 0;
+  return (size_t)E * N * (K / group_size) * 4;
+}
+
+int moe_w4_pack(const moe_w4_bank* src, int32_t E, int32_t N, int32_t K, int32_t group_size,
+                uint32_t* words, uint32_t* sb, void* stream) {
+  if (!src || !words || !sb) return fail(MOE_ERR_NULL, "src, words or sb is NULL");
+  if (!src->qweight || !src->scales || !src->biases) return fail(MOE_ERR_NULL, "src bank has a NULL pointer");
+  if (E < 1 || N <= 0 || K <= 0) return fail(MOE_ERR_SHAPE, "need E >= 1, N > 0, K > 0");
+  if (!pack_sizes_ok(E, N, K, group_size))
+    return fail(MOE_ERR_UNSUPPORTED, "pack needs E <= 256, N %% 32 == 0, K %% 128 == 0, G in {32, 64, 128}");
+  if (!aligned16(src->qweight) || !aligned16(words) || !aligned16(sb))
+    return fail(MOE_ERR_ALIGN, "qweight, words or sb not 16-byte aligned");
+  return hip_status(moe::launch_pack(*src, E, N, K, group_size, words, sb, (hipStream_t)stream), "pack");
 }
 
 int64_t moe_max_blocks(int32_t T, int32_t top_k, int32_t E, int32_t block_m) {

@@ -20,13 +20,12 @@
 //  - A: BM rows x 64 fp16 activations (operand order), 128 bytes a row, the
 //    16-byte chunk c of row r at position c ^ (r % 8).  Rows past the tile's
 //    end load a valid row whose results are never stored.
-//  - B: packed codes, [512 columns][reduction half] x 16 bytes (32 codes):
-//    one load instruction covers 32 columns x 32 contiguous bytes of each
-//    (a fully 64-column-spread layout without bank conflicts measured
-//    slower: twice the cache lines per load instruction).  Each lane
-//    dequantises its 16 bytes in registers (13 VALU instructions per 8
-//    codes) against the row's scale and bias converted to fp16.
-//  - S: per column the 32-bit words holding its scale and bias for the slab.
+//  - B: packed codes (tile-major, see moe_w4_pack): per 32-column block one
+//    contiguous 1 KiB piece [32 columns][2 reduction halves] x 16 bytes.
+//    Each lane dequantises its 16 bytes in registers (13 VALU instructions
+//    per 8 codes) against the column's scale and bias converted to fp16.
+//  - S: per column and reduction half the packed (scale, bias) word of the
+//    slab's group, 128 contiguous bytes per 32 columns.
 // One wait (s_waitcnt on this wave's own outstanding loads, a count known
 // at compile time) and one barrier per slab; the slab loop has no branches.  MFMA v_mfma_f32_32x32x16_f16,
 // fp32 accumulation.
@@ -48,7 +47,7 @@ constexpr int kSStage = kBCols * 2 * 4;     // bytes of scale and bias words per
 
 struct MfmaParams {
   const half_t* a;
-  moe_w4_bank b0, b1;
+  moe_w4_packed b0, b1;
   const int32_t* sorted_pairs;
   const float* topk_weights;
   const int32_t* blocks;
@@ -132,66 +131,47 @@ __global__ __launch_bounds__(kGemmThreads, 1) void w4_mfma_kernel(const MfmaPara
     row_w[tid] = (pair >= 0 && pair < p.P) ? p.topk_weights[pair] : 0.0f;
   }
 
-  // weight column bc (0..511) of this tile: bank and row of the bank
-  auto bank_col = [&](int bc, const moe_w4_bank*& bank) -> int {
-    int n;
+  // packed 32-column block (index into the bank's N/32) of weight-column
+  // block jb (0..15) of this tile, and its bank: in S6 block jb holds gate
+  // (jb even) or up (jb odd) columns 32 (jb / 2).., in S7 down columns 32 jb..
+  // Blocks past N reload the last block (results never stored).
+  const int nbl = N / 32;
+  auto block_of = [&](int jb, const moe_w4_packed*& bank) -> int {
+    int n0;
     if (GATE_UP) {
-      bank = ((bc >> 5) & 1) ? &p.b1 : &p.b0;
-      n = nb * OUT_COLS + (bc >> 6) * 32 + (bc & 31);
+      bank = (jb & 1) ? &p.b1 : &p.b0;
+      n0 = nb * OUT_COLS + (jb >> 1) * 32;
     } else {
       bank = &p.b0;
-      n = nb * OUT_COLS + bc;
+      n0 = nb * OUT_COLS + jb * 32;
     }
-    return min(n, N - 1);  // columns past N load a valid row, never stored
+    return (size_t)e * nbl + (min(n0, N - 32) >> 5);
   };
 
-  // ---- B loads: instruction j covers columns 32j..32j+31, lane l fills
-  // column 32j + l / 2, reduction half l % 2 (16 bytes = 32 codes).
+  // ---- B loads: instruction j is weight-column block j, one contiguous
+  // 1 KiB packed block per slab: [32 columns][2 halves] x 16 bytes.
+  const int slabs = K / kSlabK;
   const uint32_t* bsrc[B_PER_WAVE];
 #pragma unroll
   for (int b = 0; b < B_PER_WAVE; b++) {
     const int j = B_PER_WAVE * wave + b;
-    const moe_w4_bank* bank;
-    const int n = bank_col(32 * j + (lane >> 1), bank);
-    bsrc[b] = bank->qweight + ((size_t)e * N + n) * (K / 8) + 4 * (lane & 1);
+    const moe_w4_packed* bank;
+    const int blk = block_of(j, bank);
+    bsrc[b] = bank->words + (size_t)blk * slabs * 256 + 4 * lane;
   }
 
-  // ---- scale / bias words: instruction j (0..15) covers words 64j..64j+63
-  // of the stage's 1024: scales of columns 0..511, then biases.  Lane l
-  // loads the aligned 32-bit word holding the scale (bias) of group
-  // g(s) = 64 s / G of column 64 (j % 8) + l: the two groups 2i, 2i+1 of an
-  // even-aligned pair (for G = 32 exactly the slab's two groups; K / G is
-  // even for G <= 64, and for G = 128 the word is picked by address).
+  // ---- scale / bias words: stage layout [reduction half t][512 columns];
+  // instruction t of wave w covers columns 64w..64w+63 (blocks 2w, 2w+1),
+  // 128 contiguous bytes per block, group g = (64 s + 32 t) / G.
   const int log2G = p.log2_G;
   const int gpr = K >> log2G;  // groups per row
-  const uint16_t* ssrc[S_PER_WAVE];
-#pragma unroll
-  for (int t = 0; t < S_PER_WAVE; t++) {
-    const int j = S_PER_WAVE * wave + t;
-    const moe_w4_bank* bank;
-    const int n = bank_col(64 * (j & 7) + lane, bank);
-    ssrc[t] = (j < 8 ? bank->scales : bank->biases) + ((size_t)e * N + n) * gpr;
+  const uint32_t* ssrc;
+  {
+    const moe_w4_packed* bank;
+    const int blk = block_of(2 * wave + (lane >> 5), bank);
+    ssrc = bank->sb + (size_t)blk * gpr * 32 + (lane & 31);
   }
-  auto issue_scales = [&](int s, char* base) {
-    const int g = (s * kSlabK) >> log2G;
-#pragma unroll
-    for (int t = 0; t < S_PER_WAVE; t++) {
-      const uintptr_t a = (uintptr_t)(ssrc[t] + g) & ~(uintptr_t)3;
-      lds_load4(reinterpret_cast<const void*>(a),
-                base + A_BYTES + kBStage + 256 * (S_PER_WAVE * wave + t));
-    }
-  };
-  // in compute: the 16-bit half of the loaded word that holds this lane's
-  // group; the word was loaded from the row's element index rounded down to
-  // even, so the half is that index's parity
-  size_t selem[2];
   bool active = true;
-#pragma unroll
-  for (int cb = 0; cb < 2; cb++) {
-    const moe_w4_bank* bank;
-    const int n = bank_col(wave * 64 + cb * 32 + col, bank);
-    selem[cb] = ((size_t)e * N + n) * gpr;
-  }
   {
     const int first = nb * OUT_COLS + (GATE_UP ? wave * 32 : wave * 64);
     active = first < N;  // uniform per wave
@@ -200,12 +180,14 @@ __global__ __launch_bounds__(kGemmThreads, 1) void w4_mfma_kernel(const MfmaPara
   auto issue = [&](int s, int stage) {
     char* base = lds + stage * STAGE;
 #pragma unroll
-    for (int a = 0; a < A_PER_WAVE; a++)
-      lds_load16(asrc[a] + s * kSlabK, base + a_lds[a]);
+    for (int a = 0; a < A_PER_WAVE; a++) lds_load16(asrc[a] + s * kSlabK, base + a_lds[a]);
 #pragma unroll
     for (int b = 0; b < B_PER_WAVE; b++)
-      lds_load16(bsrc[b] + s * (kSlabK / 8), base + A_BYTES + 1024 * (B_PER_WAVE * wave + b));
-    issue_scales(s, base);
+      lds_load16(bsrc[b] + s * 256, base + A_BYTES + 1024 * (B_PER_WAVE * wave + b));
+#pragma unroll
+    for (int t = 0; t < S_PER_WAVE; t++)
+      lds_load4(ssrc + ((s * kSlabK + 32 * t) >> log2G) * 32,
+                base + A_BYTES + kBStage + 2048 * t + 256 * wave);
   };
 
   floatx16_t acc[MB][2];
@@ -214,22 +196,20 @@ __global__ __launch_bounds__(kGemmThreads, 1) void w4_mfma_kernel(const MfmaPara
 #pragma unroll
     for (int cb = 0; cb < 2; cb++) acc[mb][cb] = floatx16_t{};
 
-  auto compute = [&](int s, int stage) {
+  auto compute = [&](int stage) {
     const char* base = lds + stage * STAGE;
     u32x4 q[2];
 #pragma unroll
     for (int cb = 0; cb < 2; cb++)
       q[cb] = *reinterpret_cast<const u32x4*>(base + A_BYTES + (wave * 64 + cb * 32 + col) * 32 +
                                               16 * khalf);
-    const int g = (s * kSlabK + 32 * khalf) >> log2G;
     half2_t s2[2], b2[2];
 #pragma unroll
     for (int cb = 0; cb < 2; cb++) {
-      const int bc = wave * 64 + cb * 32 + col;
-      const uint32_t* sw = reinterpret_cast<const uint32_t*>(base + A_BYTES + kBStage);
-      const int sh = 16 * (int)((selem[cb] + g) & 1);
-      s2[cb] = bf16_pair_to_half2((sw[bc] >> sh) & 0xFFFFu);
-      b2[cb] = bf16_pair_to_half2((sw[kBCols + bc] >> sh) & 0xFFFFu);
+      const uint32_t sb = reinterpret_cast<const uint32_t*>(
+          base + A_BYTES + kBStage)[khalf * kBCols + wave * 64 + cb * 32 + col];
+      s2[cb] = bf16_pair_to_half2(sb & 0xFFFFu);
+      b2[cb] = bf16_pair_to_half2(sb >> 16);
     }
 #pragma unroll
     for (int i = 0; i < 4; i++) {
@@ -256,14 +236,14 @@ __global__ __launch_bounds__(kGemmThreads, 1) void w4_mfma_kernel(const MfmaPara
   // after its own: waiting until at most 2 * D are outstanding means slab s
   // has landed.  Right after the barrier, stage (s + 3) % 4 (computed last at
   // slab s - 1, by every wave) is refilled with slab s + 3.
-  const int S = K / kSlabK;
+  const int S = slabs;
   issue(0, 0);
   issue(min(1, S - 1), 1);
   issue(min(2, S - 1), 2);
   for (int s = 0; s < S; s++) {
     wait_vm_barrier<2 * D>();
     issue(min(s + 3, S - 1), (s + 3) & 3);
-    compute(s, s & 3);
+    compute(s & 3);
   }
 
   if (!active) return;

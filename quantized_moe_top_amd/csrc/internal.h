@@ -117,11 +117,16 @@ hipError_t launch_scan_scatter(const int32_t* ids, int T, int k, int E, const in
 // x bf16 [T][H] -> fp16 [T][H] with every 8-chunk interleaved (see above).
 hipError_t launch_stage_x(const uint16_t* x, half_t* xh, int64_t n_elems, hipStream_t s);
 
+// One-time repack of a row-major bank into the tile-major layout the GEMM
+// and GEMV kernels read (include/moe_w4.h, moe_w4_pack).
+hipError_t launch_pack(const moe_w4_bank& src, int E, int N, int K, int G, uint32_t* words,
+                       uint32_t* sb, hipStream_t s);
+
 struct GemmArgs {
   int mode;  // MOE_GEMM_*
   int T, top_k, E, N, K, G, block_m;
   const half_t* a;  // gate/up: staged x (fp16, interleaved) [T][K]; down: h fp16 [P][K]
-  moe_w4_bank b0, b1;
+  moe_w4_packed b0, b1;
   const int32_t* sorted_pairs;
   const float* topk_weights;
   const int32_t* blocks;

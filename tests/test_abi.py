@@ -9,7 +9,7 @@ import re
 import pytest
 
 from quantized_moe_top_amd import _lib
-from quantized_moe_top_amd._lib import Bank, Dims, GemmArgs, Layer, RouteInfo
+from quantized_moe_top_amd._lib import Bank, Dims, GemmArgs, Layer, Packed, RouteInfo
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "moe_w4.h")
@@ -98,7 +98,7 @@ def test_build_blocks_validation(L):
 
 
 def gemm_args(**kw):
-    bank = Bank(A, A, A)
+    bank = Packed(A, A)
     a = GemmArgs(mode=0, T=64, top_k=2, E=8, N=128, K=256, group_size=32, block_m=32, a=A,
                  bank0=bank, bank1=bank, sorted_pairs=A, topk_weights=A, blocks=A, num_blocks=A,
                  out=A, workspace=A, workspace_bytes=1 << 30)
@@ -118,8 +118,8 @@ def test_gemm_validation(L):
     assert g(block_m=0) == SHAPE
     assert g(a=0) == NULL
     assert g(mode=1, N=256, topk_weights=0) == NULL
-    assert g(bank1=Bank(0, A, A)) == NULL
-    assert g(bank0=Bank(A + 8, A, A)) == ALIGN
+    assert g(bank1=Packed(0, A)) == NULL
+    assert g(bank0=Packed(A + 8, A)) == ALIGN
     assert g(out=A + 2) == ALIGN
     assert g(workspace_bytes=10) == WS
     assert g(T=0) == OK
@@ -128,7 +128,7 @@ def test_gemm_validation(L):
 
 
 def test_ffn_validation(L):
-    bank = Bank(A, A, A)
+    bank = Packed(A, A)
 
     def ffn(T=16, H=256, I=128, E=8, k=2, G=32, wr=0, logits=A, x=A, y=A, ws=A, wsb=1 << 30, gate=bank):
         lay = Layer(Dims(T, H, I, E, k, G), wr, gate, bank, bank)
@@ -140,7 +140,7 @@ def test_ffn_validation(L):
     assert ffn(logits=0) == SHAPE                   # neither
     assert ffn(x=0) == NULL
     assert ffn(y=A + 4) == ALIGN
-    assert ffn(gate=Bank(A, 0, A)) == NULL
+    assert ffn(gate=Packed(A, 0)) == NULL
     assert ffn(ws=A + 16) == ALIGN
     assert ffn(wsb=100) == WS
     info = RouteInfo()
@@ -150,7 +150,7 @@ def test_ffn_validation(L):
 
 
 def test_ffn_timed_validation(L):
-    bank = Bank(A, A, A)
+    bank = Packed(A, A)
     lay = Layer(Dims(16, 256, 128, 8, 2, 32), 0, bank, bank, bank)
     # no event array: rejected before anything is enqueued
     assert L.moe_ffn_forward_timed(ctypes.byref(lay), A, A, A, None, A, 1 << 30, None, None) == NULL
@@ -158,3 +158,21 @@ def test_ffn_timed_validation(L):
     evs = (ctypes.c_void_p * (_lib.MOE_NUM_STAGES + 1))()
     lay.dims.H = 200
     assert L.moe_ffn_forward_timed(ctypes.byref(lay), A, A, A, None, A, 1 << 30, evs, None) == UNSUP
+
+
+def test_pack_queries_and_validation(L):
+    assert L.moe_w4_packed_words_bytes(128, 512, 2048) == 128 * 512 * 2048 // 2
+    assert L.moe_w4_packed_sb_bytes(128, 512, 2048, 64) == 128 * 512 * 32 * 4
+    assert L.moe_w4_packed_words_bytes(8, 100, 256) == 0          # N % 32
+    assert L.moe_w4_packed_sb_bytes(8, 128, 192, 64) == 0         # K % 128
+    assert L.moe_w4_packed_sb_bytes(8, 128, 256, 48) == 0         # G
+    src = Bank(A, A, A)
+    pk = lambda **kw: L.moe_w4_pack(ctypes.byref(kw.pop("src", src)), kw.get("E", 8), kw.get("N", 128),
+                                    kw.get("K", 256), kw.get("G", 32), kw.get("w", A), kw.get("sb", A), None)
+    assert pk(w=0) == NULL
+    assert pk(src=Bank(A, 0, A)) == NULL
+    assert pk(N=100) == UNSUP
+    assert pk(K=192) == UNSUP
+    assert pk(G=16) == UNSUP
+    assert pk(E=0) == SHAPE
+    assert pk(w=A + 4) == ALIGN

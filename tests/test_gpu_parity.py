@@ -45,6 +45,27 @@ def compare_blocks(gpu: dict, ref: dict, tag: str):
     assert np.array_equal(cpu(gpu["blocks"])[:nb], ref["blocks"]), f"{tag}: block map differs"
 
 
+# -------------------------------------------------------------- weight pack --
+@pytest.mark.parametrize("E,N,K,G", [(3, 64, 256, 32), (2, 96, 384, 128), (4, 32, 128, 64)])
+def test_pack_layout(E, N, K, G):
+    """moe_w4_pack against the packed layout's definition (include/moe_w4.h),
+    rearranged independently with NumPy."""
+    g = torch.Generator().manual_seed(E * 1000 + N + K + G)
+    bank = synth.W4Bank(torch.randint(-2**31, 2**31 - 1, (E, N, K // 8), generator=g, dtype=torch.int64).to(torch.int32),
+                        torch.randn((E, N, K // G), generator=g).to(torch.bfloat16),
+                        torch.randn((E, N, K // G), generator=g).to(torch.bfloat16))
+    pb = api.pack_bank(bank.to(DEV), G)
+    torch.cuda.synchronize()
+    q = bank.qweight.numpy().view(np.uint32)
+    # words [E][N/32][K/64][32][2][4] from q [E][N][K/8]: column 32b + c, half h, word w -> q[.., 8s + 4h + w]
+    want = q.reshape(E, N // 32, 32, K // 64, 2, 4).transpose(0, 1, 3, 2, 4, 5).reshape(-1)
+    assert np.array_equal(cpu(pb.words).view(np.uint32), want)
+    sc = bank.scales.view(torch.int16).numpy().view(np.uint16).astype(np.uint32)
+    bi = bank.biases.view(torch.int16).numpy().view(np.uint16).astype(np.uint32)
+    sbw = (sc | (bi << 16)).reshape(E, N // 32, 32, K // G).transpose(0, 1, 3, 2).reshape(-1)
+    assert np.array_equal(cpu(pb.sb).view(np.uint32), sbw)
+
+
 # ------------------------------------------------------------------ routing --
 @pytest.mark.parametrize("name", ["tiny_t16", "decode_t1", "decode_t8", "imbalanced_t8192"])
 def test_route_given_logits(orc, name):
