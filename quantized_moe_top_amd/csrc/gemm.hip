@@ -39,11 +39,6 @@ namespace {
 
 constexpr int kSlabK = 64;
 constexpr int kStages = 4;
-constexpr int kGemmThreads = 512;
-constexpr int kGemmWaves = kGemmThreads / 64;
-constexpr int kBCols = 512;                 // weight columns per workgroup
-constexpr int kBStage = kBCols * 32;        // bytes of codes per stage
-constexpr int kSStage = kBCols * 2 * 4;     // bytes of scale and bias words per stage
 
 struct MfmaParams {
   const half_t* a;
@@ -76,16 +71,23 @@ __device__ __forceinline__ void wait_vm_barrier() {
   asm volatile("s_barrier" ::: "memory");
 }
 
-template <int MODE, int MB>
-__global__ __launch_bounds__(kGemmThreads, 1) void w4_mfma_kernel(const MfmaParams p) {
+// WAVES waves per workgroup (4 or 8): the tile covers 64 * WAVES weight
+// columns.  With 4 waves two workgroups fit a CU (LDS <= 80 KiB) for tiles of
+// up to 64 rows, so one workgroup's prologue and epilogue overlap another's
+// main loop; 128-row tiles use 8 waves (one workgroup per CU).
+template <int MODE, int MB, int WAVES>
+__global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void w4_mfma_kernel(const MfmaParams p) {
   constexpr bool GATE_UP = MODE == MOE_GEMM_GATE_UP_SWIGLU;
   constexpr int BM = MB * 32;
+  constexpr int kBCols = 64 * WAVES;                     // weight columns per workgroup
+  constexpr int kBStage = kBCols * 32;                   // bytes of codes per stage
+  constexpr int kSStage = kBCols * 2 * 4;                // bytes of scale / bias words per stage
   constexpr int A_BYTES = BM * 128;                      // per stage
   constexpr int STAGE = A_BYTES + kBStage + kSStage;
   constexpr int A_INSTR = BM / 8;                        // 1 KiB A loads per stage
-  constexpr int A_PER_WAVE = A_INSTR >= kGemmWaves ? A_INSTR / kGemmWaves : 1;
-  constexpr int B_PER_WAVE = kBStage / 1024 / kGemmWaves;  // 2
-  constexpr int S_PER_WAVE = kSStage / 256 / kGemmWaves;   // 2 (dword loads: 256 B each)
+  constexpr int A_PER_WAVE = A_INSTR >= WAVES ? A_INSTR / WAVES : 1;
+  constexpr int B_PER_WAVE = 2;                          // 1 KiB code blocks per wave
+  constexpr int S_PER_WAVE = 2;                          // 256 B scale-word loads per wave
   constexpr int D = A_PER_WAVE + B_PER_WAVE + S_PER_WAVE;  // loads per wave per slab
   constexpr int OUT_COLS = GATE_UP ? kBCols / 2 : kBCols; // output columns per workgroup
   __shared__ __attribute__((aligned(16))) char lds[kStages * STAGE];
@@ -115,7 +117,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void w4_mfma_kernel(const MfmaPara
   int a_lds[A_PER_WAVE];
 #pragma unroll
   for (int a = 0; a < A_PER_WAVE; a++) {
-    const int j = A_INSTR >= kGemmWaves ? wave + kGemmWaves * a : wave % A_INSTR;
+    const int j = A_INSTR >= WAVES ? wave + WAVES * a : wave % A_INSTR;
     const int r = 8 * j + (lane >> 3);
     const int c = (lane & 7) ^ (lane >> 3);
     int srow = row0 + min(r, rows - 1);
@@ -187,7 +189,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void w4_mfma_kernel(const MfmaPara
 #pragma unroll
     for (int t = 0; t < S_PER_WAVE; t++)
       lds_load4(ssrc + ((s * kSlabK + 32 * t) >> log2G) * 32,
-                base + A_BYTES + kBStage + 2048 * t + 256 * wave);
+                base + A_BYTES + kBStage + 4 * kBCols * t + 256 * wave);
   };
 
   floatx16_t acc[MB][2];
@@ -286,13 +288,14 @@ hipError_t launch_mode(const GemmArgs& a, hipStream_t s) {
   const int log2_G = a.G == 32 ? 5 : a.G == 64 ? 6 : 7;  // G in {32, 64, 128}
   MfmaParams p{a.a, a.b0, a.b1, a.sorted_pairs, a.topk_weights, a.blocks, a.num_blocks, a.out,
                a.N, a.K, log2_G, a.top_k, a.E, (int)P, (int)max_blocks};
-  const int out_cols = MODE == MOE_GEMM_GATE_UP_SWIGLU ? kBCols / 2 : kBCols;
+  const int bcols = a.block_m == 128 ? 512 : 256;  // 64 * waves, as in the switch below
+  const int out_cols = MODE == MOE_GEMM_GATE_UP_SWIGLU ? bcols / 2 : bcols;
   const int64_t items = max_blocks * ((a.N + out_cols - 1) / out_cols);
   const int64_t grid = ((items + kNumXcd - 1) / kNumXcd) * kNumXcd;
   switch (a.block_m) {
-    case 32: w4_mfma_kernel<MODE, 1><<<grid, kGemmThreads, 0, s>>>(p); break;
-    case 64: w4_mfma_kernel<MODE, 2><<<grid, kGemmThreads, 0, s>>>(p); break;
-    case 128: w4_mfma_kernel<MODE, 4><<<grid, kGemmThreads, 0, s>>>(p); break;
+    case 32: w4_mfma_kernel<MODE, 1, 4><<<grid, 256, 0, s>>>(p); break;
+    case 64: w4_mfma_kernel<MODE, 2, 4><<<grid, 256, 0, s>>>(p); break;
+    case 128: w4_mfma_kernel<MODE, 4, 8><<<grid, 512, 0, s>>>(p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

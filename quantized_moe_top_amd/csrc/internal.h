@@ -88,8 +88,10 @@ __device__ __forceinline__ half2_t bf16_pair_to_half2(uint32_t s) {
   return half2_t{h, h};
 }
 
+// silu(g) * u = g / (1 + e^-g) * u, with the hardware exponential and
+// reciprocal (about 1 ulp each; the result is then rounded to fp16).
 __device__ __forceinline__ float silu_mul(float g, float u) {
-  return g / (1.0f + __expf(-g)) * u;
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
 }
 
 // ---------------------------------------------------------------- launchers --
