@@ -87,12 +87,14 @@ typedef struct {
  * call; page "Perplexity's Lily beats MLX by 1.35x by doing one thing:
  * single-model Rust/Metal engines", section "Why one model on one chip is
  * faster": the weights are laid out in the order the kernels read fastest).
- *  words: uint32 [E][N/32][K/64][32 columns][2 halves][4 words]: for column
- *         32b + c and half h of slab s, the four row-major words holding codes
- *         64s + 32h .. 64s + 32h + 31 (same nibble order).
- *  sb:    uint32 [E][N/32][K/G][32 columns]: bf16 scale bits in the low 16
+ *  words: uint32 [E][N/128][K/64][4 blocks][32 columns][2 halves][4 words]:
+ *         for column 128c + 32u + cc (chunk c, block u) and half h of slab s,
+ *         the four row-major words holding codes 64s + 32h .. 64s + 32h + 31
+ *         (same nibble order); each chunk is one contiguous 4 KiB run per
+ *         slab.
+ *  sb:    uint32 [E][N/128][K/G][128 columns]: bf16 scale bits in the low 16
  *         bits, bf16 bias bits in the high 16 bits.
- * Requires N % 32 == 0, K % 128 == 0, G in {32, 64, 128}, K % G == 0. */
+ * Requires N % 128 == 0, K % 128 == 0, G in {32, 64, 128}, K % G == 0. */
 typedef struct {
   const uint32_t* words;
   const uint32_t* sb;

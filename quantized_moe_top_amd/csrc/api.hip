@@ -57,7 +57,7 @@ int check_bank(const moe_w4_packed& b, const char* name) {
 }
 
 bool pack_sizes_ok(int64_t E, int64_t N, int64_t K, int64_t G) {
-  return E >= 1 && E <= 256 && N > 0 && N % 32 == 0 && K > 0 && K % 128 == 0 &&
+  return E >= 1 && E <= 256 && N > 0 && N % 128 == 0 && K > 0 && K % 128 == 0 &&
          (G == 32 || G == 64 || G == 128) && K % G == 0;
 }
 
@@ -176,7 +176,7 @@ int moe_w4_pack(const moe_w4_bank* src, int32_t E, int32_t N, int32_t K, int32_t
   if (!src->qweight || !src->scales || !src->biases) return fail(MOE_ERR_NULL, "src bank has a NULL pointer");
   if (E < 1 || N <= 0 || K <= 0) return fail(MOE_ERR_SHAPE, "need E >= 1, N > 0, K > 0");
   if (!pack_sizes_ok(E, N, K, group_size))
-    return fail(MOE_ERR_UNSUPPORTED, "pack needs E <= 256, N %% 32 == 0, K %% 128 == 0, G in {32, 64, 128}");
+    return fail(MOE_ERR_UNSUPPORTED, "pack needs E <= 256, N %% 128 == 0, K %% 128 == 0, G in {32, 64, 128}");
   if (!aligned16(src->qweight) || !aligned16(words) || !aligned16(sb))
     return fail(MOE_ERR_ALIGN, "qweight, words or sb not 16-byte aligned");
   return hip_status(moe::launch_pack(*src, E, N, K, group_size, words, sb, (hipStream_t)stream), "pack");

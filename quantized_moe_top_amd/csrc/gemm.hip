@@ -75,7 +75,9 @@ __device__ __forceinline__ void wait_vm_barrier() {
 // columns.  With 4 waves two workgroups fit a CU (LDS <= 80 KiB) for tiles of
 // up to 64 rows, so one workgroup's prologue and epilogue overlap another's
 // main loop; 128-row tiles use 8 waves (one workgroup per CU).
-template <int MODE, int MB, int WAVES>
+// G32: group size 32, the two reduction halves of a slab have their own
+// (scale, bias) words; for G >= 64 one word serves both and is copied once.
+template <int MODE, int MB, int WAVES, bool G32>
 __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void w4_mfma_kernel(const MfmaParams p) {
   constexpr bool GATE_UP = MODE == MOE_GEMM_GATE_UP_SWIGLU;
   constexpr int BM = MB * 32;
@@ -87,7 +89,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void w4_mfma_kernel(const Mf
   constexpr int A_INSTR = BM / 8;                        // 1 KiB A loads per stage
   constexpr int A_PER_WAVE = A_INSTR >= WAVES ? A_INSTR / WAVES : 1;
   constexpr int B_PER_WAVE = 2;                          // 1 KiB code blocks per wave
-  constexpr int S_PER_WAVE = 2;                          // 256 B scale-word loads per wave
+  constexpr int S_PER_WAVE = G32 ? 2 : 1;                // 256 B scale-word loads per wave
   constexpr int D = A_PER_WAVE + B_PER_WAVE + S_PER_WAVE;  // loads per wave per slab
   constexpr int OUT_COLS = GATE_UP ? kBCols / 2 : kBCols; // output columns per workgroup
   __shared__ __attribute__((aligned(16))) char lds[kStages * STAGE];
@@ -150,8 +152,9 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void w4_mfma_kernel(const Mf
     return (size_t)e * nbl + (min(n0, N - 32) >> 5);
   };
 
-  // ---- B loads: instruction j is weight-column block j, one contiguous
-  // 1 KiB packed block per slab: [32 columns][2 halves] x 16 bytes.
+  // ---- B loads: instruction j is weight-column block j, one 1 KiB packed
+  // block per slab ([32 columns][2 halves] x 16 bytes) inside its chunk's
+  // 4 KiB run.
   const int slabs = K / kSlabK;
   const uint32_t* bsrc[B_PER_WAVE];
 #pragma unroll
@@ -159,10 +162,10 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void w4_mfma_kernel(const Mf
     const int j = B_PER_WAVE * wave + b;
     const moe_w4_packed* bank;
     const int blk = block_of(j, bank);
-    bsrc[b] = bank->words + (size_t)blk * slabs * 256 + 4 * lane;
+    bsrc[b] = bank->words + ((size_t)(blk >> 2) * slabs * 4 + (blk & 3)) * 256 + 4 * lane;
   }
 
-  // ---- scale / bias words: stage layout [reduction half t][512 columns];
+  // ---- scale / bias words: stage layout [reduction half t][kBCols columns];
   // instruction t of wave w covers columns 64w..64w+63 (blocks 2w, 2w+1),
   // 128 contiguous bytes per block, group g = (64 s + 32 t) / G.
   const int log2G = p.log2_G;
@@ -171,7 +174,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void w4_mfma_kernel(const Mf
   {
     const moe_w4_packed* bank;
     const int blk = block_of(2 * wave + (lane >> 5), bank);
-    ssrc = bank->sb + (size_t)blk * gpr * 32 + (lane & 31);
+    ssrc = bank->sb + (size_t)(blk >> 2) * gpr * 128 + (blk & 3) * 32 + (lane & 31);
   }
   bool active = true;
   {
@@ -185,10 +188,10 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void w4_mfma_kernel(const Mf
     for (int a = 0; a < A_PER_WAVE; a++) lds_load16(asrc[a] + s * kSlabK, base + a_lds[a]);
 #pragma unroll
     for (int b = 0; b < B_PER_WAVE; b++)
-      lds_load16(bsrc[b] + s * 256, base + A_BYTES + 1024 * (B_PER_WAVE * wave + b));
+      lds_load16(bsrc[b] + s * 1024, base + A_BYTES + 1024 * (B_PER_WAVE * wave + b));
 #pragma unroll
     for (int t = 0; t < S_PER_WAVE; t++)
-      lds_load4(ssrc + ((s * kSlabK + 32 * t) >> log2G) * 32,
+      lds_load4(ssrc + ((s * kSlabK + 32 * t) >> log2G) * 128,
                 base + A_BYTES + kBStage + 4 * kBCols * t + 256 * wave);
   };
 
@@ -209,7 +212,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void w4_mfma_kernel(const Mf
 #pragma unroll
     for (int cb = 0; cb < 2; cb++) {
       const uint32_t sb = reinterpret_cast<const uint32_t*>(
-          base + A_BYTES + kBStage)[khalf * kBCols + wave * 64 + cb * 32 + col];
+          base + A_BYTES + kBStage)[(G32 ? khalf : 0) * kBCols + wave * 64 + cb * 32 + col];
       s2[cb] = bf16_pair_to_half2(sb & 0xFFFFu);
       b2[cb] = bf16_pair_to_half2(sb >> 16);
     }
@@ -292,10 +295,14 @@ hipError_t launch_mode(const GemmArgs& a, hipStream_t s) {
   const int out_cols = MODE == MOE_GEMM_GATE_UP_SWIGLU ? bcols / 2 : bcols;
   const int64_t items = max_blocks * ((a.N + out_cols - 1) / out_cols);
   const int64_t grid = ((items + kNumXcd - 1) / kNumXcd) * kNumXcd;
-  switch (a.block_m) {
-    case 32: w4_mfma_kernel<MODE, 1, 4><<<grid, 256, 0, s>>>(p); break;
-    case 64: w4_mfma_kernel<MODE, 2, 4><<<grid, 256, 0, s>>>(p); break;
-    case 128: w4_mfma_kernel<MODE, 4, 8><<<grid, 512, 0, s>>>(p); break;
+  const bool g32 = a.G == 32;
+  switch (a.block_m * 2 + (g32 ? 1 : 0)) {
+    case 64: w4_mfma_kernel<MODE, 1, 4, false><<<grid, 256, 0, s>>>(p); break;
+    case 65: w4_mfma_kernel<MODE, 1, 4, true><<<grid, 256, 0, s>>>(p); break;
+    case 128: w4_mfma_kernel<MODE, 2, 4, false><<<grid, 256, 0, s>>>(p); break;
+    case 129: w4_mfma_kernel<MODE, 2, 4, true><<<grid, 256, 0, s>>>(p); break;
+    case 256: w4_mfma_kernel<MODE, 4, 8, false><<<grid, 512, 0, s>>>(p); break;
+    case 257: w4_mfma_kernel<MODE, 4, 8, true><<<grid, 512, 0, s>>>(p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -102,8 +102,9 @@ __global__ __launch_bounds__(kGemvThreads) void w4_gemv_kernel(const GemvParams 
 #pragma unroll
     for (int b = 0; b < NB; b++) {
       const moe_w4_packed& bank = b == 0 ? p.b0 : p.b1;
-      const u32x4 q = *reinterpret_cast<const u32x4*>(bank.words + (bidx * S + s) * 256 + 4 * lane);
-      const uint32_t sb = bank.sb[(bidx * gpr + g) * 32 + c];
+      const u32x4 q = *reinterpret_cast<const u32x4*>(
+          bank.words + (((bidx >> 2) * S + s) * 4 + (bidx & 3)) * 256 + 4 * lane);
+      const uint32_t sb = bank.sb[((bidx >> 2) * gpr + g) * 128 + (bidx & 3) * 32 + c];
       dequant32(q, sb, w[b]);
     }
 #pragma unroll

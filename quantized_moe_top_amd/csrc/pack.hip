@@ -5,14 +5,16 @@
 // faster": a single-model engine lays out its weights in whatever order its
 // kernels read fastest).
 //
-// Packed codes: uint32 words [E][N/32][K/64][32 columns][2 halves][4 words].
-// The 1 KiB block (e, column block b, slab s) holds, for column c = 32b + cc
-// and half h, the four words of codes k = 64s + 32h + 8w + j (word w, nibble
-// j, lowest nibble first, as in the row-major words): one 16-byte load per
-// lane per slab, and one contiguous 1 KiB block per 32 columns per slab.
-// Packed scales and biases: uint32 [E][N/32][K/G][32 columns], the bf16
-// scale in the low half and the bf16 bias in the high half, so that the 32
-// columns of a block need 128 contiguous bytes per group.
+// Packed codes: uint32 words [E][N/128][K/64][4 blocks][32 columns]
+// [2 halves][4 words].  For 128-column chunk c, slab s, 32-column block u of
+// the chunk, column cc of the block and half h, the four words hold codes
+// k = 64s + 32h + 8w + j of column 128c + 32u + cc (word w, nibble j, lowest
+// nibble first, as in the row-major words).  A 32-column block of one slab
+// is 1 KiB (one 16-byte load per lane), and the 128 columns of a chunk are
+// one contiguous 4 KiB run per slab: DRAM streams in long runs.
+// Packed scales and biases: uint32 [E][N/128][K/G][128 columns], the bf16
+// scale in the low half and the bf16 bias in the high half: 512 contiguous
+// bytes per chunk and group.
 #include "internal.h"
 
 namespace moe {
@@ -23,13 +25,14 @@ __global__ __launch_bounds__(256) void pack_codes_kernel(const uint32_t* __restr
                                                          int N, int K) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= nwords) return;
-  // i = (((e * N/32 + b) * K/64 + s) * 32 + cc) * 8 + h * 4 + w
+  // i = ((((e * N/128 + c) * K/64 + s) * 4 + u) * 32 + cc) * 8 + h * 4 + w
   const int w = (int)(i & 3), h = (int)((i >> 2) & 1), cc = (int)((i >> 3) & 31);
-  const int64_t rest = i >> 8;  // (e * N/32 + b) * K/64 + s
+  const int u = (int)((i >> 8) & 3);
+  const int64_t rest = i >> 10;  // (e * N/128 + c) * K/64 + s
   const int slabs = K / 64;
   const int s = (int)(rest % slabs);
-  const int64_t eb = rest / slabs;  // e * N/32 + b
-  const int64_t row = eb * 32 + cc;  // e * N + n
+  const int64_t ec = rest / slabs;  // e * N/128 + c
+  const int64_t row = ec * 128 + u * 32 + cc;  // e * N + n
   out[i] = q[row * (K / 8) + s * 8 + h * 4 + w];
 }
 
@@ -39,12 +42,12 @@ __global__ __launch_bounds__(256) void pack_scales_kernel(const uint16_t* __rest
                                                           int gpr) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n) return;
-  // i = ((e * N/32 + b) * gpr + g) * 32 + cc
-  const int cc = (int)(i & 31);
-  const int64_t rest = i >> 5;
+  // i = ((e * N/128 + c) * gpr + g) * 128 + cc
+  const int cc = (int)(i & 127);
+  const int64_t rest = i >> 7;
   const int g = (int)(rest % gpr);
-  const int64_t eb = rest / gpr;
-  const int64_t src = (eb * 32 + cc) * gpr + g;
+  const int64_t ec = rest / gpr;
+  const int64_t src = (ec * 128 + cc) * gpr + g;
   out[i] = (uint32_t)sc[src] | ((uint32_t)bi[src] << 16);
 }
 

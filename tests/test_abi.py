@@ -163,7 +163,8 @@ def test_ffn_timed_validation(L):
 def test_pack_queries_and_validation(L):
     assert L.moe_w4_packed_words_bytes(128, 512, 2048) == 128 * 512 * 2048 // 2
     assert L.moe_w4_packed_sb_bytes(128, 512, 2048, 64) == 128 * 512 * 32 * 4
-    assert L.moe_w4_packed_words_bytes(8, 100, 256) == 0          # N % 32
+    assert L.moe_w4_packed_words_bytes(8, 100, 256) == 0          # N % 128
+    assert L.moe_w4_packed_words_bytes(8, 96, 256) == 0
     assert L.moe_w4_packed_sb_bytes(8, 128, 192, 64) == 0         # K % 128
     assert L.moe_w4_packed_sb_bytes(8, 128, 256, 48) == 0         # G
     src = Bank(A, A, A)
@@ -172,6 +173,7 @@ def test_pack_queries_and_validation(L):
     assert pk(w=0) == NULL
     assert pk(src=Bank(A, 0, A)) == NULL
     assert pk(N=100) == UNSUP
+    assert pk(N=96) == UNSUP
     assert pk(K=192) == UNSUP
     assert pk(G=16) == UNSUP
     assert pk(E=0) == SHAPE

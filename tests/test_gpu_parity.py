@@ -46,7 +46,7 @@ def compare_blocks(gpu: dict, ref: dict, tag: str):
 
 
 # -------------------------------------------------------------- weight pack --
-@pytest.mark.parametrize("E,N,K,G", [(3, 64, 256, 32), (2, 96, 384, 128), (4, 32, 128, 64)])
+@pytest.mark.parametrize("E,N,K,G", [(3, 128, 256, 32), (2, 384, 384, 128), (4, 256, 128, 64)])
 def test_pack_layout(E, N, K, G):
     """moe_w4_pack against the packed layout's definition (include/moe_w4.h),
     rearranged independently with NumPy."""
@@ -57,12 +57,13 @@ def test_pack_layout(E, N, K, G):
     pb = api.pack_bank(bank.to(DEV), G)
     torch.cuda.synchronize()
     q = bank.qweight.numpy().view(np.uint32)
-    # words [E][N/32][K/64][32][2][4] from q [E][N][K/8]: column 32b + c, half h, word w -> q[.., 8s + 4h + w]
-    want = q.reshape(E, N // 32, 32, K // 64, 2, 4).transpose(0, 1, 3, 2, 4, 5).reshape(-1)
+    # words [E][N/128][K/64][4][32][2][4] from q [E][N][K/8]: column 128c + 32u + cc, half h,
+    # word w -> q[.., 8s + 4h + w]
+    want = q.reshape(E, N // 128, 4, 32, K // 64, 2, 4).transpose(0, 1, 4, 2, 3, 5, 6).reshape(-1)
     assert np.array_equal(cpu(pb.words).view(np.uint32), want)
     sc = bank.scales.view(torch.int16).numpy().view(np.uint16).astype(np.uint32)
     bi = bank.biases.view(torch.int16).numpy().view(np.uint16).astype(np.uint32)
-    sbw = (sc | (bi << 16)).reshape(E, N // 32, 32, K // G).transpose(0, 1, 3, 2).reshape(-1)
+    sbw = (sc | (bi << 16)).reshape(E, N // 128, 128, K // G).transpose(0, 1, 3, 2).reshape(-1)
     assert np.array_equal(cpu(pb.sb).view(np.uint32), sbw)
 
 
