@@ -5,8 +5,9 @@
 One step is one whole layer (router when the workload has one, top-k
 routing, histogram / scan / scatter / block map, the two grouped W4 GEMMs
 with SwiGLU, and the combine) over one batch of T synthetic tokens, enqueued
-by ``moe_ffn_forward_timed`` on one stream.  Inputs are resident in HBM
-before timing starts.  Weights are rotated over enough device copies of the
+by ``moe_ffn_forward`` on one stream and replayed from a HIP graph captured
+once per weight copy / logit set (``--no-graph`` times eager launches).
+Inputs are resident in HBM before timing starts.  Weights are rotated over enough device copies of the
 layer (>= 1 GiB in total) that every step reads its experts cold from HBM
 rather than from the 256 MB Infinity Cache; decode workloads also rotate
 over a pool of independent logit sets, so the touched experts change every
@@ -16,7 +17,8 @@ Prints one JSON line.  ``value`` is tokens/s = T * K / (elapsed of the K
 timed steps).  ``roofline`` is for the kernel with the largest average
 duration among the single-kernel stages, from its algorithmic bytes (or
 flops) per launch and its average duration between the stage events
-recorded on its own stream during the timed steps.  ``cpu_baseline`` times
+recorded on its own stream (``moe_ffn_forward_timed``) over a second,
+eager pass of the same steps.  ``cpu_baseline`` times
 the CPU oracle on a bounded sample of the same workload on the host cores.
 """
 
@@ -51,6 +53,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="prefill_t512")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time eager launches instead of HIP graph replays")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum CPU time of the oracle sample")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -203,23 +207,47 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
-    ev = [api.stage_events(nst + 1) for _ in range(K)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    log(f"[bench] timing {K} steps")
-    t0 = time.perf_counter()
-    start.record()
-    for i in range(K):
-        step(i, ev[i])
-    end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    elapsed_ms = start.elapsed_time(end)
+    graphs = None
+    if not args.no_graph:
+        # one graph per (weight copy, logit set) that the steps use
+        n_graphs = len(logit_pool) if logit_pool else R
+        graphs = []
+        for i in range(n_graphs):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(i)
+            graphs.append(g)
+        for i in range(min(args.warmup, n_graphs) or 1):
+            graphs[i % n_graphs].replay()
+        torch.cuda.synchronize()
+
+    def timed(run):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        start.record()
+        for i in range(K):
+            run(i)
+        end.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(end), time.perf_counter() - t0
+
+    log(f"[bench] timing {K} steps ({'eager' if graphs is None else 'graph replay'})")
+    if graphs is None:
+        elapsed_ms, wall = timed(lambda i: step(i))
+    else:
+        elapsed_ms, wall = timed(lambda i: graphs[i % len(graphs)].replay())
     ms_per_step = elapsed_ms / K
     value = T * K / (elapsed_ms / 1e3)
+
+    # per-stage durations: an eager pass of the same steps with events
+    # recorded between the stages on the layer's stream
+    ev = [api.stage_events(nst + 1) for _ in range(K)]
+    eager_ms, _ = timed(lambda i: step(i, ev[i]))
     stage_ms = np.array([[ev[i][s].elapsed_time(ev[i][s + 1]) for s in range(nst)] for i in range(K)])
     stage_us = {st: round(float(stage_ms[:, j].mean()) * 1e3, 3) for j, st in enumerate(_lib.STAGES)}
-    log(f"[bench] {ms_per_step * 1e3:.2f} us/step (wall {wall / K * 1e6:.2f}); stages us {stage_us}")
+    log(f"[bench] {ms_per_step * 1e3:.2f} us/step (wall {wall / K * 1e6:.2f}); eager with stage "
+        f"events {eager_ms / K * 1e3:.2f} us/step; stages us {stage_us}")
 
     # roofline of the dominant single-kernel stage
     mean_touched = float(np.mean([touched[i % len(touched)] for i in range(K)]))
@@ -269,8 +297,10 @@ def main():
         "data": "synthetic",
         "config": {"workload": name, "T": T, "H": lay.H, "I": lay.I, "E": E, "top_k": k,
                    "group_size": lay.G, "router": "weight" if lay.router_weight is not None else "logits",
-                   "weight_copies": R, "block_m": api.ffn_block_m(lay)},
+                   "weight_copies": R, "block_m": api.ffn_block_m(lay),
+                   "launch": "eager" if graphs is None else "hip_graph"},
         "roofline": roofline, "layer_roofline": layer_roof, "stage_us": stage_us,
+        "eager_ms_per_step": round(eager_ms / K, 6),
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

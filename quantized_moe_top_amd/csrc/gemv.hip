@@ -1,27 +1,28 @@
 // gemv.hip -- S9: the grouped W4 GEMM at decode sizes (T <= 8).  With at most
 // 8 rows per expert the product is bound by reading the packed weights, so
-// each touched expert's weights are streamed once and experts that no token
-// chose are never read.
+// each touched expert's weights are streamed once, with as many bytes in
+// flight as the chip holds, and experts that no token chose are never read.
 //
-// One workgroup (8 waves) per (tile, 32-column block).  In the packed layout
-// (see moe_w4_pack) each 64-wide reduction slab of a 32-column block is one
-// contiguous 1 KiB piece, read by one wave instruction: lane l holds 32
-// codes of column l / 2, reduction half l % 2.  The 8 waves take the slabs
-// in turn (wave w: slabs w, w + 8, ...); each lane dequantises its codes in
-// registers (same exact fp16 dequantisation as the MFMA path) and dots them
-// with the activation rows routed to the tile using v_dot2_f32_f16 (fp16
-// products, fp32 accumulation).  The two halves of a column are added with
-// one lane exchange, the 8 waves' partial sums through LDS in wave order, so
-// the result does not depend on timing.
+// One workgroup per (tile, 32-column output block): S6 reads the gate and
+// the up block, S7 the down block.  The reduction dimension is split over
+// the waves, two 64-wide slabs per wave and pass (16 waves cover K = 2048 in
+// one pass), and every wave issues all the loads of its pass at once,
+// straight into registers: the packed codes (one 1 KiB block per bank and
+// slab; lane l takes the 32 codes of column l % 32, reduction half l / 32,
+// exactly an MFMA B fragment after dequantisation), the (scale, bias) words
+// and the activation rows.  The dot products run on v_mfma_f32_32x32x16_f16
+// with the tile's rows (<= 8) in MFMA rows 0..7 and zeros above, so the VALU
+// only dequantises (same exact fp16 dequantisation as the prefill path).
+// The waves' partial sums meet in LDS and are added in wave order, so the
+// result does not depend on timing.
 #include "internal.h"
 
 namespace moe {
 namespace {
 
-constexpr int kGemvWaves = 8;
-constexpr int kGemvThreads = 64 * kGemvWaves;
+constexpr int kDecWavesMax = 16;
 
-struct GemvParams {
+struct DecParams {
   const half_t* a;
   moe_w4_packed b0, b1;
   const int32_t* sorted_pairs;
@@ -32,39 +33,17 @@ struct GemvParams {
   int N, K, log2_G, top_k, E, P, max_blocks;
 };
 
-// 32 fp16 products summed into acc.  Each vector element is copied into a
-// scalar before the bit cast: a bit cast applied to a vector-element lvalue
-// was compiled to read element 0 for every index.
-__device__ __forceinline__ float dot32(const u32x4* w, const u32x4* x, float acc) {
-#pragma unroll
-  for (int i = 0; i < 4; i++)
-#pragma unroll
-    for (int c = 0; c < 4; c++) {
-      const uint32_t wc = w[i][c], xc = x[i][c];
-      acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, wc), __builtin_bit_cast(half2_t, xc),
-                                   acc, false);
-    }
-  return acc;
-}
-
-// 32 codes (16 bytes) of one column and reduction half -> 32 fp16 weights
-// in operand order, with the packed (scale, bias) word sb.
-__device__ __forceinline__ void dequant32(const u32x4 q, uint32_t sb, u32x4* w) {
-  const half2_t s2 = bf16_pair_to_half2(sb & 0xFFFFu), b2 = bf16_pair_to_half2(sb >> 16);
-#pragma unroll
-  for (int i = 0; i < 4; i++) {
-    const uint4 d = dequant_word(q[i], s2, b2);
-    w[i] = u32x4{d.x, d.y, d.z, d.w};
-  }
-}
-
 template <int MODE>
-__global__ __launch_bounds__(kGemvThreads) void w4_gemv_kernel(const GemvParams p) {
+__global__ __launch_bounds__(64 * kDecWavesMax) void w4_gemv_kernel(const DecParams p) {
   constexpr bool GATE_UP = MODE == MOE_GEMM_GATE_UP_SWIGLU;
   constexpr int NB = GATE_UP ? 2 : 1;  // banks read: gate and up, or down
-  __shared__ float red[kGemvWaves][NB][kGemvMaxTokens][32];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int c = lane >> 1, half = lane & 1;
+  // rows 0..7 of each wave's 32x32 partial: register r < 4 of lane l holds
+  // row 4 (l / 32) + r, column l % 32
+  __shared__ float red[kDecWavesMax][NB][4][64];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nwaves = blockDim.x >> 6;
+  const int col = lane & 31, khalf = lane >> 5;
   const int nbl = p.N / 32;
   const int tile = blockIdx.x / nbl, blk = blockIdx.x % nbl;
 
@@ -76,74 +55,90 @@ __global__ __launch_bounds__(kGemvThreads) void w4_gemv_kernel(const GemvParams 
     return;
   const int K = p.K, S = K / 64, gpr = K >> p.log2_G;
 
-  // activation row of each tile row: token x (S6) or slot h (S7), both
-  // already in operand order
-  int arow[kGemvMaxTokens];
-#pragma unroll
-  for (int m = 0; m < kGemvMaxTokens; m++) {
-    int r = row0 + min(m, rows - 1);
+  // this lane's activation row (MFMA row l % 32): token x (S6) or slot h
+  // (S7), both in operand order; rows past the tile read nothing
+  const bool has_row = col < rows;
+  const half_t* arow = p.a;
+  if (has_row) {
+    int r = row0 + col;
     if (GATE_UP) {
       const int pair = p.sorted_pairs[r];
       r = (pair >= 0 && pair < p.P) ? pair / p.top_k : 0;
     }
-    arow[m] = r;
+    arow = p.a + (size_t)r * K + 32 * khalf;
   }
-
+  // packed block of this output block in each bank (chunked layout: 4 KiB
+  // runs of 128 columns per slab)
   const size_t bidx = (size_t)e * nbl + blk;
-  float acc[NB][kGemvMaxTokens];
-#pragma unroll
-  for (int b = 0; b < NB; b++)
-#pragma unroll
-    for (int m = 0; m < kGemvMaxTokens; m++) acc[b][m] = 0.0f;
-
-  for (int s = wave; s < S; s += kGemvWaves) {
-    const int g = (64 * s + 32 * half) >> p.log2_G;
-    u32x4 w[NB][4];
-#pragma unroll
-    for (int b = 0; b < NB; b++) {
-      const moe_w4_packed& bank = b == 0 ? p.b0 : p.b1;
-      const u32x4 q = *reinterpret_cast<const u32x4*>(
-          bank.words + (((bidx >> 2) * S + s) * 4 + (bidx & 3)) * 256 + 4 * lane);
-      const uint32_t sb = bank.sb[((bidx >> 2) * gpr + g) * 128 + (bidx & 3) * 32 + c];
-      dequant32(q, sb, w[b]);
-    }
-#pragma unroll
-    for (int m = 0; m < kGemvMaxTokens; m++) {
-      if (m >= rows) break;
-      const u32x4* xp =
-          reinterpret_cast<const u32x4*>(p.a + (size_t)arow[m] * K + 64 * s + 32 * half);
-      u32x4 xv[4] = {xp[0], xp[1], xp[2], xp[3]};
-#pragma unroll
-      for (int b = 0; b < NB; b++) acc[b][m] = dot32(w[b], xv, acc[b][m]);
-    }
-  }
-  // the column's two reduction halves, then the waves in order
-#pragma unroll
-  for (int b = 0; b < NB; b++)
-#pragma unroll
-    for (int m = 0; m < kGemvMaxTokens; m++) {
-      const float v = acc[b][m] + __shfl_xor(acc[b][m], 1);
-      if (half == 0) red[wave][b][m][c] = v;
-    }
-  __syncthreads();
-  if (tid >= rows * 32) return;
-  const int m = tid >> 5, cc = tid & 31;
-  float v[NB];
+  const uint32_t* wsrc[NB];
+  const uint32_t* ssrc[NB];
 #pragma unroll
   for (int b = 0; b < NB; b++) {
-    v[b] = red[0][b][m][cc];
-#pragma unroll
-    for (int w2 = 1; w2 < kGemvWaves; w2++) v[b] += red[w2][b][m][cc];
+    const moe_w4_packed& bank = b == 0 ? p.b0 : p.b1;
+    // 16-byte unit (column, half) of a block is number 2 * column + half
+    wsrc[b] = bank.words + ((bidx >> 2) * S * 4 + (bidx & 3)) * 256 + 4 * (2 * col + khalf);
+    ssrc[b] = bank.sb + (bidx >> 2) * gpr * 128 + (bidx & 3) * 32 + col;
   }
-  const int n = blk * 32 + cc;
-  if (GATE_UP) {
-    // h in operand order (see the MFMA kernel)
-    reinterpret_cast<half_t*>(p.out)[(size_t)(row0 + m) * p.N + (n & ~7) + interleaved_pos(n & 7)] =
-        (half_t)silu_mul(v[0], v[NB - 1]);
-  } else {
-    const int pair = p.sorted_pairs[row0 + m];
-    const float wgt = (pair >= 0 && pair < p.P) ? p.topk_weights[pair] : 0.0f;
-    reinterpret_cast<float*>(p.out)[(size_t)(row0 + m) * p.N + n] = wgt * v[0];
+
+  floatx16_t acc[NB];
+#pragma unroll
+  for (int b = 0; b < NB; b++) acc[b] = floatx16_t{};
+  for (int s0 = 2 * wave; s0 < S; s0 += 2 * nwaves) {
+    // all loads of the pass first: codes, (scale, bias) words, activations
+    // (S is even: K % 128 == 0)
+    u32x4 q[NB][2];
+    uint32_t sb[NB][2];
+    u32x4 x[2][4];
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+      const int s = s0 + j;
+      const int g = (64 * s + 32 * khalf) >> p.log2_G;
+#pragma unroll
+      for (int b = 0; b < NB; b++) {
+        q[b][j] = *reinterpret_cast<const u32x4*>(wsrc[b] + (size_t)s * 1024);
+        sb[b][j] = ssrc[b][(size_t)g * 128];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+        x[j][i] = has_row ? *reinterpret_cast<const u32x4*>(arow + 64 * s + 8 * i) : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int j = 0; j < 2; j++)
+#pragma unroll
+      for (int b = 0; b < NB; b++) {
+        const half2_t s2 = bf16_pair_to_half2(sb[b][j] & 0xFFFFu), b2 = bf16_pair_to_half2(sb[b][j] >> 16);
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          const uint4 d = dequant_word(q[b][j][i], s2, b2);
+          acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+              __builtin_bit_cast(half8_t, x[j][i]), __builtin_bit_cast(half8_t, d), acc[b], 0, 0, 0);
+        }
+      }
+  }
+#pragma unroll
+  for (int b = 0; b < NB; b++)
+#pragma unroll
+    for (int r = 0; r < 4; r++) red[wave][b][r][lane] = acc[b][r];
+  __syncthreads();
+  for (int t = tid; t < rows * 32; t += blockDim.x) {
+    const int m = t >> 5, cc = t & 31;
+    const int rr = m & 3, ll = cc + 32 * (m >> 2);
+    float v[NB];
+#pragma unroll
+    for (int b = 0; b < NB; b++) {
+      v[b] = red[0][b][rr][ll];
+      for (int w2 = 1; w2 < nwaves; w2++) v[b] += red[w2][b][rr][ll];
+    }
+    const int n = blk * 32 + cc;
+    if (GATE_UP) {
+      // h in operand order (see the MFMA kernel)
+      reinterpret_cast<half_t*>(p.out)[(size_t)(row0 + m) * p.N + (n & ~7) + interleaved_pos(n & 7)] =
+          (half_t)silu_mul(v[0], v[NB - 1]);
+    } else {
+      const int pair = p.sorted_pairs[row0 + m];
+      const float wgt = (pair >= 0 && pair < p.P) ? p.topk_weights[pair] : 0.0f;
+      reinterpret_cast<float*>(p.out)[(size_t)(row0 + m) * p.N + n] = wgt * v[0];
+    }
   }
 }
 
@@ -153,13 +148,15 @@ hipError_t launch_w4_gemv(const GemmArgs& a, hipStream_t s) {
   const int64_t P = (int64_t)a.T * a.top_k;
   const int64_t max_blocks = P / a.block_m + (P < a.E ? P : a.E);
   const int log2_G = a.G == 32 ? 5 : a.G == 64 ? 6 : 7;  // G in {32, 64, 128}
-  GemvParams p{a.a, a.b0, a.b1, a.sorted_pairs, a.topk_weights, a.blocks, a.num_blocks, a.out,
-               a.N, a.K, log2_G, a.top_k, a.E, (int)P, (int)max_blocks};
+  DecParams p{a.a, a.b0, a.b1, a.sorted_pairs, a.topk_weights, a.blocks, a.num_blocks, a.out,
+              a.N, a.K, log2_G, a.top_k, a.E, (int)P, (int)max_blocks};
   const int64_t grid = max_blocks * (a.N / 32);
+  // two slabs per wave and pass; K % 128 == 0
+  const int waves = (int)std::min<int64_t>(kDecWavesMax, a.K / 128);
   if (a.mode == MOE_GEMM_GATE_UP_SWIGLU)
-    w4_gemv_kernel<MOE_GEMM_GATE_UP_SWIGLU><<<grid, kGemvThreads, 0, s>>>(p);
+    w4_gemv_kernel<MOE_GEMM_GATE_UP_SWIGLU><<<grid, 64 * waves, 0, s>>>(p);
   else
-    w4_gemv_kernel<MOE_GEMM_DOWN><<<grid, kGemvThreads, 0, s>>>(p);
+    w4_gemv_kernel<MOE_GEMM_DOWN><<<grid, 64 * waves, 0, s>>>(p);
   return hipGetLastError();
 }
 

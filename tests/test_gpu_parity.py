@@ -317,3 +317,28 @@ def test_ffn_deterministic():
     nb = int(ia["num_blocks"][0])
     assert torch.equal(ia["blocks"][:nb], ib["blocks"][:nb])
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("name", ["decode_t1", "prefill_t512"])
+def test_graph_replay_matches_eager(name):
+    """The layer captured in a HIP graph (one stream, no host round trip, no
+    allocation, no memset) replays to the eager result, bit for bit, on
+    every replay, with other work on the same buffers between replays."""
+    lay = api.pack_layer(on_dev(synth.make_layer(name)))
+    other = api.pack_layer(on_dev(synth.make_custom(T=lay.T, H=lay.H, I=lay.I, E=lay.E, k=lay.k,
+                                                    G=lay.G, seed=36)))
+    ws = torch.empty(max(api.ffn_workspace_bytes(lay), api.ffn_workspace_bytes(other)),
+                     dtype=torch.uint8, device=DEV)
+    y_eager = api.ffn_forward(lay, workspace=ws).clone()
+    y = torch.empty_like(y_eager)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        api.ffn_forward(lay, y=y, workspace=ws)
+    for r in range(4):
+        y.fill_(float("nan"))
+        api.ffn_forward(other, workspace=ws)  # rewrites the shared workspace
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_eager), f"replay {r}"
