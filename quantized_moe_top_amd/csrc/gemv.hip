@@ -5,9 +5,10 @@
 //
 // One workgroup per (tile, 32-column output block): S6 reads the gate and
 // the up block, S7 the down block.  The reduction dimension is split over
-// the waves, two 64-wide slabs per wave and pass (16 waves cover K = 2048 in
-// one pass), and every wave issues all the loads of its pass at once,
-// straight into registers: the packed codes (one 1 KiB block per bank and
+// the waves, two or four 64-wide slabs per wave and pass (16 or 8 waves
+// cover K = 2048 in one pass; with four, two workgroups share a CU, so one
+// computes while the other waits on memory), and every wave issues the
+// weight loads of its pass at once, straight into registers: the packed codes (one 1 KiB block per bank and
 // slab; lane l takes the 32 codes of column l % 32, reduction half l / 32,
 // exactly an MFMA B fragment after dequantisation), the (scale, bias) words
 // and the activation rows.  The dot products run on v_mfma_f32_32x32x16_f16
@@ -33,7 +34,8 @@ struct DecParams {
   int N, K, log2_G, top_k, E, P, max_blocks;
 };
 
-template <int MODE>
+// SPW: 64-wide slabs per wave and pass.
+template <int MODE, int SPW>
 __global__ __launch_bounds__(64 * kDecWavesMax) void w4_gemv_kernel(const DecParams p) {
   constexpr bool GATE_UP = MODE == MOE_GEMM_GATE_UP_SWIGLU;
   constexpr int NB = GATE_UP ? 2 : 1;  // banks read: gate and up, or down
@@ -83,27 +85,34 @@ __global__ __launch_bounds__(64 * kDecWavesMax) void w4_gemv_kernel(const DecPar
   floatx16_t acc[NB];
 #pragma unroll
   for (int b = 0; b < NB; b++) acc[b] = floatx16_t{};
-  for (int s0 = 2 * wave; s0 < S; s0 += 2 * nwaves) {
-    // all loads of the pass first: codes, (scale, bias) words, activations
-    // (S is even: K % 128 == 0)
-    u32x4 q[NB][2];
-    uint32_t sb[NB][2];
-    u32x4 x[2][4];
+  for (int s0 = SPW * wave; s0 < S; s0 += SPW * nwaves) {
+    // the pass's codes and (scale, bias) words first (slabs past the end
+    // reload the last slab and are not multiplied), then per slab its
+    // activation fragments (L2-resident), one slab ahead
+    u32x4 q[NB][SPW];
+    uint32_t sb[NB][SPW];
 #pragma unroll
-    for (int j = 0; j < 2; j++) {
-      const int s = s0 + j;
+    for (int j = 0; j < SPW; j++) {
+      const int s = min(s0 + j, S - 1);
       const int g = (64 * s + 32 * khalf) >> p.log2_G;
 #pragma unroll
       for (int b = 0; b < NB; b++) {
         q[b][j] = *reinterpret_cast<const u32x4*>(wsrc[b] + (size_t)s * 1024);
         sb[b][j] = ssrc[b][(size_t)g * 128];
       }
+    }
+    auto load_x = [&](int s, u32x4 (&x)[4]) {
 #pragma unroll
       for (int i = 0; i < 4; i++)
-        x[j][i] = has_row ? *reinterpret_cast<const u32x4*>(arow + 64 * s + 8 * i) : u32x4{0, 0, 0, 0};
-    }
+        x[i] = has_row ? *reinterpret_cast<const u32x4*>(arow + 64 * s + 8 * i) : u32x4{0, 0, 0, 0};
+    };
+    u32x4 x[4];
+    load_x(s0, x);
 #pragma unroll
-    for (int j = 0; j < 2; j++)
+    for (int j = 0; j < SPW; j++) {
+      if (s0 + j >= S) break;  // uniform per wave
+      u32x4 xn[4];
+      load_x(min(s0 + j + 1, S - 1), xn);
 #pragma unroll
       for (int b = 0; b < NB; b++) {
         const half2_t s2 = bf16_pair_to_half2(sb[b][j] & 0xFFFFu), b2 = bf16_pair_to_half2(sb[b][j] >> 16);
@@ -111,9 +120,12 @@ __global__ __launch_bounds__(64 * kDecWavesMax) void w4_gemv_kernel(const DecPar
         for (int i = 0; i < 4; i++) {
           const uint4 d = dequant_word(q[b][j][i], s2, b2);
           acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-              __builtin_bit_cast(half8_t, x[j][i]), __builtin_bit_cast(half8_t, d), acc[b], 0, 0, 0);
+              __builtin_bit_cast(half8_t, x[i]), __builtin_bit_cast(half8_t, d), acc[b], 0, 0, 0);
         }
       }
+#pragma unroll
+      for (int i = 0; i < 4; i++) x[i] = xn[i];
+    }
   }
 #pragma unroll
   for (int b = 0; b < NB; b++)
@@ -151,12 +163,20 @@ hipError_t launch_w4_gemv(const GemmArgs& a, hipStream_t s) {
   DecParams p{a.a, a.b0, a.b1, a.sorted_pairs, a.topk_weights, a.blocks, a.num_blocks, a.out,
               a.N, a.K, log2_G, a.top_k, a.E, (int)P, (int)max_blocks};
   const int64_t grid = max_blocks * (a.N / 32);
-  // two slabs per wave and pass; K % 128 == 0
-  const int waves = (int)std::min<int64_t>(kDecWavesMax, a.K / 128);
-  if (a.mode == MOE_GEMM_GATE_UP_SWIGLU)
-    w4_gemv_kernel<MOE_GEMM_GATE_UP_SWIGLU><<<grid, 64 * waves, 0, s>>>(p);
-  else
-    w4_gemv_kernel<MOE_GEMM_DOWN><<<grid, 64 * waves, 0, s>>>(p);
+  // Enough workgroups to fill the chip twice over: four slabs per wave (two
+  // 8-wave workgroups per CU overlap one's loads with the other's MFMAs);
+  // otherwise two (up to 16 waves, as many bytes in flight per workgroup as
+  // possible).
+  const bool wide = a.K >= 1024 && grid >= 1024;
+  const int spw = wide ? 4 : 2;
+  const int waves = (int)std::max<int64_t>(1, std::min<int64_t>(kDecWavesMax, a.K / (64 * spw)));
+  if (a.mode == MOE_GEMM_GATE_UP_SWIGLU) {
+    if (wide) w4_gemv_kernel<MOE_GEMM_GATE_UP_SWIGLU, 4><<<grid, 64 * waves, 0, s>>>(p);
+    else w4_gemv_kernel<MOE_GEMM_GATE_UP_SWIGLU, 2><<<grid, 64 * waves, 0, s>>>(p);
+  } else {
+    if (wide) w4_gemv_kernel<MOE_GEMM_DOWN, 4><<<grid, 64 * waves, 0, s>>>(p);
+    else w4_gemv_kernel<MOE_GEMM_DOWN, 2><<<grid, 64 * waves, 0, s>>>(p);
+  }
   return hipGetLastError();
 }
 
