@@ -28,13 +28,17 @@ namespace {
 
 constexpr int kSub = 32;        // tokens per sub-tile
 constexpr int kRouteThreads = 512;
-constexpr int kRouterBatch = 8;  // MFMA steps whose loads are issued together
+constexpr int kRouterBatch = 16;  // MFMA steps whose loads are issued together
 
 // ------------------------------------------------------------------ S0 ---
 // logits[t][e] = sum_h x[t][h] * wr[e][h] for one 32-token x 32-expert tile
-// per workgroup.  The 8 waves split the H sums into 8 contiguous ranges;
-// their 32x32 partial tiles are added in wave order through LDS, so the
-// result does not depend on timing.  grid (ceil(T/32), ceil(E/32)).
+// per workgroup.  The 8 waves split the H sums into 8 contiguous ranges,
+// each wave issuing the loads of its whole range at once (H <= 4096: one
+// round trip); their 32x32 partial tiles are added in wave order through
+// LDS, so the result does not depend on timing.  One-dimensional grid of
+// ceil(T/32) * ceil(E/32) workgroups, expert tile fastest: the expert tiles
+// of one token tile are dispatched together, so x is read from HBM once and
+// shared through L2.
 constexpr int kRouterWaves = 8;
 __global__ __launch_bounds__(64 * kRouterWaves) void router_gemm_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, float* __restrict__ logits,
@@ -42,7 +46,8 @@ __global__ __launch_bounds__(64 * kRouterWaves) void router_gemm_kernel(
   __shared__ float red[kRouterWaves][32 * 33];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane & 31, half = lane >> 5;
-  const int t0 = blockIdx.x * 32, e0 = blockIdx.y * 32;
+  const int ne = (E + 31) / 32;
+  const int t0 = (blockIdx.x / ne) * 32, e0 = (blockIdx.x % ne) * 32;
   const int t = min(t0 + r, T - 1);  // rows past T or E read a valid row, never stored
   const int e = min(e0 + r, E - 1);
   const int steps = H / 16 / kRouterWaves;  // H % 128 == 0
@@ -57,6 +62,9 @@ __global__ __launch_bounds__(64 * kRouterWaves) void router_gemm_kernel(
       av[u] = xa[2 * (s + u)];
       bv[u] = wb[2 * (s + u)];
     }
+    // keep every load of the batch ahead of the first MFMA (one round trip),
+    // instead of the compiler's rolling schedule with a few loads in flight
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < kRouterBatch; u++)
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av[u]),
@@ -286,7 +294,7 @@ hipError_t launch_route(const uint16_t* x, const uint16_t* wr, float* logits, in
                         hipStream_t s) {
   if (T <= 0) return hipSuccess;
   if (wr) {
-    dim3 grid((T + 31) / 32, (E + 31) / 32);
+    const int64_t grid = (int64_t)((E + 31) / 32) * ((T + 31) / 32);
     router_gemm_kernel<<<grid, 64 * kRouterWaves, 0, s>>>(x, wr, logits, T, H, E);
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
