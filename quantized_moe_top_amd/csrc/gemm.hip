@@ -64,6 +64,13 @@ __device__ __forceinline__ void lds_load4(const void* g, char* l) {
 // barrier.  The asm is a compiler memory barrier, so no LDS access moves
 // across it; no fence is used because a fence would also wait for the
 // loads still in flight for later slabs.
+// s_waitcnt vmcnt(n) alone (expcnt and lgkmcnt not waited on).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vm_barrier() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -251,21 +258,42 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void w4_mfma_kernel(const Mf
     compute(s & 3);
   }
 
-  if (!active) return;
   // ---- epilogue.  Accumulator register r of lane l holds row
   // 8*(r/4) + 4*(l/32) + r%4 and column l%32 of each 32x32 block.
+  if (GATE_UP) {
+    // h = silu(gate) * up into an LDS tile [BM][OUT_COLS] (operand order:
+    // column 8g + j at 8g + interleaved_pos(j)), then out with 16-byte row
+    // stores.  The ring is free once every copy has landed (the last steps
+    // reloaded the last slab) and every wave has finished its MFMAs.
+    wait_vm<0>();
+    __syncthreads();
+    half_t* tile_h = reinterpret_cast<half_t*>(lds);
+    if (active) {
+      const int lc = wave * 32 + (col & ~7) + interleaved_pos(col & 7);
 #pragma unroll
-  for (int mb = 0; mb < MB; mb++) {
+      for (int mb = 0; mb < MB; mb++)
 #pragma unroll
-    for (int r = 0; r < 16; r++) {
-      const int row = mb * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3);
-      if (row >= rows) continue;
-      if (GATE_UP) {
-        // h in operand order: column 8g + j stored at 8g + interleaved_pos(j)
-        const int n = nb * OUT_COLS + wave * 32 + (col & ~7) + interleaved_pos(col & 7);
-        reinterpret_cast<half_t*>(p.out)[(size_t)(row0 + row) * N + n] =
-            (half_t)silu_mul(acc[mb][0][r], acc[mb][1][r]);
-      } else {
+        for (int r = 0; r < 16; r++) {
+          const int row = mb * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3);
+          tile_h[row * OUT_COLS + lc] = (half_t)silu_mul(acc[mb][0][r], acc[mb][1][r]);
+        }
+    }
+    __syncthreads();
+    const int n0 = nb * OUT_COLS;
+    const int chunks = min(OUT_COLS, N - n0) / 8;  // 16-byte pieces per row
+    for (int idx = tid; idx < rows * chunks; idx += 64 * WAVES) {
+      const int row = idx / chunks, ch = idx % chunks;
+      *reinterpret_cast<uint4*>(reinterpret_cast<half_t*>(p.out) + (size_t)(row0 + row) * N + n0 + 8 * ch) =
+          *reinterpret_cast<const uint4*>(tile_h + row * OUT_COLS + 8 * ch);
+    }
+  } else {
+    if (!active) return;
+#pragma unroll
+    for (int mb = 0; mb < MB; mb++) {
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        const int row = mb * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3);
+        if (row >= rows) continue;
         const float w = row_w[row];
         float* orow = reinterpret_cast<float*>(p.out) + (size_t)(row0 + row) * N;
 #pragma unroll
@@ -275,6 +303,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void w4_mfma_kernel(const Mf
     }
   }
 }
+
 
 // x bf16 -> fp16, each 8-element chunk interleaved (0,4,1,5,2,6,3,7).
 __global__ __launch_bounds__(256) void stage_x_kernel(const uint4* __restrict__ in,
@@ -310,7 +339,10 @@ hipError_t launch_mode(const GemmArgs& a, hipStream_t s) {
 
 // y[t][:] = sum_j y_sorted[pair_slot[t*k + j]][:], j ascending, fp32: the
 // k weighted expert outputs of a token added in a fixed order, so the layer
-// output is deterministic.
+// output is deterministic.  One thread per 16 bytes of y; all k slot indices
+// and then all k rows are loaded before the sum (KMAX >= k, guards for
+// j >= k), so a thread has k row loads in flight instead of k round trips.
+template <int KMAX>
 __global__ __launch_bounds__(256) void combine_kernel(const float4* __restrict__ y_sorted,
                                                       const int32_t* __restrict__ pair_slot,
                                                       float4* __restrict__ y, int T, int H4,
@@ -319,15 +351,24 @@ __global__ __launch_bounds__(256) void combine_kernel(const float4* __restrict__
   if (i >= (int64_t)T * H4) return;
   const int t = (int)(i / H4), c = (int)(i % H4);
   const int P = T * k;
+  int slot[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; j++) {
+    slot[j] = j < k ? pair_slot[(size_t)t * k + j] : -1;
+    if (slot[j] >= P) slot[j] = -1;  // out-of-range slots are skipped
+  }
+  float4 v[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; j++)
+    v[j] = slot[j] >= 0 ? y_sorted[(size_t)slot[j] * H4 + c] : make_float4(0.f, 0.f, 0.f, 0.f);
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int j = 0; j < k; j++) {
-    const int slot = pair_slot[(size_t)t * k + j];
-    if (slot < 0 || slot >= P) continue;
-    const float4 v = y_sorted[(size_t)slot * H4 + c];
-    acc.x += v.x;
-    acc.y += v.y;
-    acc.z += v.z;
-    acc.w += v.w;
+#pragma unroll
+  for (int j = 0; j < KMAX; j++) {
+    if (slot[j] < 0) continue;
+    acc.x += v[j].x;
+    acc.y += v[j].y;
+    acc.z += v[j].z;
+    acc.w += v[j].w;
   }
   y[i] = acc;
 }
@@ -349,9 +390,13 @@ hipError_t launch_stage_x(const uint16_t* x, half_t* xh, int64_t n_elems, hipStr
 hipError_t launch_combine(const float* y_sorted, const int32_t* pair_slot, float* y, int T,
                           int H, int k, hipStream_t s) {
   const int64_t n = (int64_t)T * (H / 4);
-  combine_kernel<<<(n + 255) / 256, 256, 0, s>>>(reinterpret_cast<const float4*>(y_sorted),
-                                                 pair_slot, reinterpret_cast<float4*>(y), T, H / 4,
-                                                 k);
+  const int64_t grid = (n + 255) / 256;
+  const float4* ys = reinterpret_cast<const float4*>(y_sorted);
+  float4* yo = reinterpret_cast<float4*>(y);
+  if (k <= 2) combine_kernel<2><<<grid, 256, 0, s>>>(ys, pair_slot, yo, T, H / 4, k);
+  else if (k <= 4) combine_kernel<4><<<grid, 256, 0, s>>>(ys, pair_slot, yo, T, H / 4, k);
+  else if (k <= 8) combine_kernel<8><<<grid, 256, 0, s>>>(ys, pair_slot, yo, T, H / 4, k);
+  else combine_kernel<16><<<grid, 256, 0, s>>>(ys, pair_slot, yo, T, H / 4, k);  // k <= 16
   return hipGetLastError();
 }
 
