@@ -38,6 +38,11 @@ namespace moe {
 namespace {
 
 constexpr int kSlabK = 64;
+
+template <int V>
+struct IntTag {
+  static constexpr int value = V;
+};
 constexpr int kStages = 4;
 
 struct MfmaParams {
@@ -97,7 +102,6 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void w4_mfma_kernel(const Mf
   constexpr int A_PER_WAVE = A_INSTR >= WAVES ? A_INSTR / WAVES : 1;
   constexpr int B_PER_WAVE = 2;                          // 1 KiB code blocks per wave
   constexpr int S_PER_WAVE = G32 ? 2 : 1;                // 256 B scale-word loads per wave
-  constexpr int D = A_PER_WAVE + B_PER_WAVE + S_PER_WAVE;  // loads per wave per slab
   constexpr int OUT_COLS = GATE_UP ? kBCols / 2 : kBCols; // output columns per workgroup
   __shared__ __attribute__((aligned(16))) char lds[kStages * STAGE];
   __shared__ float row_w[BM];
@@ -189,74 +193,89 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void w4_mfma_kernel(const Mf
     active = first < N;  // uniform per wave
   }
 
-  auto issue = [&](int s, int stage) {
-    char* base = lds + stage * STAGE;
-#pragma unroll
-    for (int a = 0; a < A_PER_WAVE; a++) lds_load16(asrc[a] + s * kSlabK, base + a_lds[a]);
-#pragma unroll
-    for (int b = 0; b < B_PER_WAVE; b++)
-      lds_load16(bsrc[b] + s * 1024, base + A_BYTES + 1024 * (B_PER_WAVE * wave + b));
-#pragma unroll
-    for (int t = 0; t < S_PER_WAVE; t++)
-      lds_load4(ssrc + ((s * kSlabK + 32 * t) >> log2G) * 128,
-                base + A_BYTES + kBStage + 4 * kBCols * t + 256 * wave);
-  };
-
   floatx16_t acc[MB][2];
 #pragma unroll
   for (int mb = 0; mb < MB; mb++)
 #pragma unroll
     for (int cb = 0; cb < 2; cb++) acc[mb][cb] = floatx16_t{};
 
-  auto compute = [&](int stage) {
-    const char* base = lds + stage * STAGE;
-    u32x4 q[2];
+  // The main loop for MBA active 32-row blocks (MBA = MB, or MB / 2 when the
+  // tile's rows fit in the first half: the copies of the other half's
+  // activations and its MFMAs are skipped; its accumulators stay zero and
+  // its rows are never stored).
+  auto pipeline = [&](auto mba) {
+    constexpr int MBA = decltype(mba)::value;
+    constexpr int APW = A_PER_WAVE * MBA / MB;  // activation copies used (rows < 32 MBA)
+    constexpr int DA = APW + B_PER_WAVE + S_PER_WAVE;
+
+    auto issue = [&](int s, int stage) {
+      char* base = lds + stage * STAGE;
 #pragma unroll
-    for (int cb = 0; cb < 2; cb++)
-      q[cb] = *reinterpret_cast<const u32x4*>(base + A_BYTES + (wave * 64 + cb * 32 + col) * 32 +
-                                              16 * khalf);
-    half2_t s2[2], b2[2];
+      for (int a = 0; a < APW; a++) lds_load16(asrc[a] + s * kSlabK, base + a_lds[a]);
 #pragma unroll
-    for (int cb = 0; cb < 2; cb++) {
-      const uint32_t sb = reinterpret_cast<const uint32_t*>(
-          base + A_BYTES + kBStage)[(G32 ? khalf : 0) * kBCols + wave * 64 + cb * 32 + col];
-      s2[cb] = bf16_pair_to_half2(sb & 0xFFFFu);
-      b2[cb] = bf16_pair_to_half2(sb >> 16);
-    }
+      for (int b = 0; b < B_PER_WAVE; b++)
+        lds_load16(bsrc[b] + s * 1024, base + A_BYTES + 1024 * (B_PER_WAVE * wave + b));
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-      half8_t bf[2];
+      for (int t = 0; t < S_PER_WAVE; t++)
+        lds_load4(ssrc + ((s * kSlabK + 32 * t) >> log2G) * 128,
+                  base + A_BYTES + kBStage + 4 * kBCols * t + 256 * wave);
+    };
+
+    auto compute = [&](int stage) {
+      const char* base = lds + stage * STAGE;
+      u32x4 q[2];
 #pragma unroll
       for (int cb = 0; cb < 2; cb++)
-        bf[cb] = __builtin_bit_cast(half8_t, dequant_word(q[cb][i], s2[cb], b2[cb]));
+        q[cb] = *reinterpret_cast<const u32x4*>(base + A_BYTES + (wave * 64 + cb * 32 + col) * 32 +
+                                                16 * khalf);
+      half2_t s2[2], b2[2];
 #pragma unroll
-      for (int mb = 0; mb < MB; mb++) {
-        const int r = mb * 32 + col;
-        const half8_t af = *reinterpret_cast<const half8_t*>(
-            base + r * 128 + (((4 * khalf + i) ^ (col & 7)) << 4));
+      for (int cb = 0; cb < 2; cb++) {
+        const uint32_t sb = reinterpret_cast<const uint32_t*>(
+            base + A_BYTES + kBStage)[(G32 ? khalf : 0) * kBCols + wave * 64 + cb * 32 + col];
+        s2[cb] = bf16_pair_to_half2(sb & 0xFFFFu);
+        b2[cb] = bf16_pair_to_half2(sb >> 16);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        half8_t bf[2];
 #pragma unroll
         for (int cb = 0; cb < 2; cb++)
-          acc[mb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, bf[cb], acc[mb][cb], 0, 0, 0);
+          bf[cb] = __builtin_bit_cast(half8_t, dequant_word(q[cb][i], s2[cb], b2[cb]));
+#pragma unroll
+        for (int mb = 0; mb < MBA; mb++) {
+          const int r = mb * 32 + col;
+          const half8_t af = *reinterpret_cast<const half8_t*>(
+              base + r * 128 + (((4 * khalf + i) ^ (col & 7)) << 4));
+#pragma unroll
+          for (int cb = 0; cb < 2; cb++)
+            acc[mb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, bf[cb], acc[mb][cb], 0, 0, 0);
+        }
       }
+    };
+
+    // slab s lives in stage s % 4.  Every slab step issues the same copies
+    // (slabs past the end reload the last slab into a stage that is never
+    // read again), so when slab s is about to be computed exactly the copies
+    // of two later slabs (2 * DA instructions of this wave) were issued after
+    // its own: waiting until at most 2 * DA are outstanding means slab s has
+    // landed.  Right after the barrier, stage (s + 3) % 4 (computed last at
+    // slab s - 1, by every wave) is refilled with slab s + 3.
+    const int S = slabs;
+    issue(0, 0);
+    issue(min(1, S - 1), 1);
+    issue(min(2, S - 1), 2);
+    for (int s = 0; s < S; s++) {
+      wait_vm_barrier<2 * DA>();
+      issue(min(s + 3, S - 1), (s + 3) & 3);
+      compute(s & 3);
     }
   };
-
-  // ---- pipeline: slab s lives in stage s % 4.  Every slab step issues the
-  // same loads (slabs past the end reload the last slab into a stage that is
-  // never read again), so when slab s is about to be computed exactly the
-  // loads of two later slabs (2 * D instructions of this wave) were issued
-  // after its own: waiting until at most 2 * D are outstanding means slab s
-  // has landed.  Right after the barrier, stage (s + 3) % 4 (computed last at
-  // slab s - 1, by every wave) is refilled with slab s + 3.
-  const int S = slabs;
-  issue(0, 0);
-  issue(min(1, S - 1), 1);
-  issue(min(2, S - 1), 2);
-  for (int s = 0; s < S; s++) {
-    wait_vm_barrier<2 * D>();
-    issue(min(s + 3, S - 1), (s + 3) & 3);
-    compute(s & 3);
-  }
+  // uniform per workgroup: every wave takes the same branch
+  if (MB > 1 && rows <= BM / 2)
+    pipeline(IntTag<(MB > 1 ? MB / 2 : 1)>{});
+  else
+    pipeline(IntTag<MB>{});
 
   // ---- epilogue.  Accumulator register r of lane l holds row
   // 8*(r/4) + 4*(l/32) + r%4 and column l%32 of each 32x32 block.
