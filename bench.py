@@ -15,8 +15,9 @@ step.
 
 Prints one JSON line.  ``value`` is tokens/s = T * K / (elapsed of the K
 timed steps).  ``roofline`` is for the kernel with the largest average
-duration among the single-kernel stages, from its algorithmic bytes (or
-flops) per launch and its average duration between the stage events
+duration among the stages that stream the layer's bulk data (the two
+grouped GEMMs and the combine), from its algorithmic bytes (or flops) per
+launch and its average duration between the stage events
 recorded on its own stream (``moe_ffn_forward_timed``) over a second,
 eager pass of the same steps.  ``cpu_baseline`` times
 the CPU oracle on a bounded sample of the same workload on the host cores.
@@ -254,8 +255,11 @@ def main():
     alg = algorithmic(lay, 0)
     alg_t = {s: dict(bytes=algorithmic(lay, 1)[s]["bytes"] - alg[s]["bytes"], flops=alg[s]["flops"])
              for s in alg}  # bytes per touched expert
-    single = ["route", "build_blocks", "gate_up", "down", "combine"]
-    dom = max(single, key=lambda s: stage_us[s])
+    # the stages that stream the layer's bulk data; routing and the block map
+    # move a few KB per token (at decode sizes a single workgroup: latency,
+    # not bandwidth) and are reported in stage_us only
+    bulk = ["gate_up", "down", "combine"]
+    dom = max(bulk, key=lambda s: stage_us[s])
     dur_s = stage_us[dom] * 1e-6
     byts = alg[dom]["bytes"] + mean_touched * alg_t[dom]["bytes"]
     flops = alg[dom]["flops"]

@@ -327,13 +327,22 @@ int ffn_forward_impl(const moe_layer* layer, const uint16_t* x, const float* rou
   hipError_t err;
   int32_t* chunk_hist = (int32_t*)(ws + L.scratch);
   if ((err = mark(events, MOE_STAGE_ROUTE, s)) != hipSuccess) return hip_status(err, "event");
-  if ((err = moe::launch_route(x, layer->router_weight, logits, d.T, d.H, d.E, d.top_k, ids, w, xh,
-                               chunk_hist, s)) != hipSuccess)
-    return hip_status(err, "route");
-  if ((err = mark(events, MOE_STAGE_BUILD_BLOCKS, s)) != hipSuccess) return hip_status(err, "event");
-  if ((err = moe::launch_scan_scatter(ids, d.T, d.top_k, d.E, chunk_hist, block_m, counts, offsets,
-                                      sorted_pairs, pair_slot, blocks, num_blocks, s)) != hipSuccess)
-    return hip_status(err, "scan_scatter");
+  if (moe::route_build_fused(d.T)) {
+    // one routing chunk: S1-S5 in one launch (the build stage is empty)
+    if ((err = moe::launch_route_build(x, layer->router_weight, logits, d.T, d.H, d.E, d.top_k, ids,
+                                       w, xh, chunk_hist, block_m, counts, offsets, sorted_pairs,
+                                       pair_slot, blocks, num_blocks, s)) != hipSuccess)
+      return hip_status(err, "route_build");
+    if ((err = mark(events, MOE_STAGE_BUILD_BLOCKS, s)) != hipSuccess) return hip_status(err, "event");
+  } else {
+    if ((err = moe::launch_route(x, layer->router_weight, logits, d.T, d.H, d.E, d.top_k, ids, w, xh,
+                                 chunk_hist, s)) != hipSuccess)
+      return hip_status(err, "route");
+    if ((err = mark(events, MOE_STAGE_BUILD_BLOCKS, s)) != hipSuccess) return hip_status(err, "event");
+    if ((err = moe::launch_scan_scatter(ids, d.T, d.top_k, d.E, chunk_hist, block_m, counts, offsets,
+                                        sorted_pairs, pair_slot, blocks, num_blocks, s)) != hipSuccess)
+      return hip_status(err, "scan_scatter");
+  }
   moe::GemmArgs g1{MOE_GEMM_GATE_UP_SWIGLU, d.T, d.top_k, d.E, d.I, d.H, d.group_size, block_m,
                    xh, layer->gate, layer->up, sorted_pairs, w, blocks, num_blocks, h};
   moe::GemmArgs g2{MOE_GEMM_DOWN, d.T, d.top_k, d.E, d.H, d.I, d.group_size, block_m,

@@ -19,7 +19,7 @@
 //     sort, deterministic).
 // moe_build_blocks, which receives the ids from the caller, runs a small
 // histogram kernel first.
-#include "internal.h"
+#include "scan_scatter.h"
 
 namespace moe {
 namespace {
@@ -41,147 +41,13 @@ __global__ __launch_bounds__(256) void chunk_hist_kernel(const int32_t* __restri
   if (tid < E) chunk_hist[(size_t)blockIdx.x * E + tid] = h[tid];
 }
 
-constexpr int kScanThreads = 512;
-constexpr int kScanWaves = kScanThreads / 64;
-
-// Exclusive scan over kScanThreads values held one per thread.
-__device__ int block_exclusive_scan(int v, int* tmp) {
-  const int tid = threadIdx.x;
-  tmp[tid] = v;
-  __syncthreads();
-  for (int off = 1; off < kScanThreads; off <<= 1) {
-    const int add = tid >= off ? tmp[tid - off] : 0;
-    __syncthreads();
-    tmp[tid] += add;
-    __syncthreads();
-  }
-  const int incl = tmp[tid];
-  __syncthreads();
-  return incl - v;
-}
-
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-}
-
 __global__ __launch_bounds__(kScanThreads) void scan_scatter_kernel(
     const int32_t* __restrict__ ids, int P, int E, int chunk_pairs, int nchunks,
     const int32_t* __restrict__ chunk_hist, int block_m, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pairs,
     int32_t* __restrict__ pair_slot, int32_t* __restrict__ blocks, int32_t* __restrict__ num_blocks) {
-  __shared__ int tmp[kScanThreads];
-  __shared__ int spre[kScanThreads], stot[kScanThreads];
-  __shared__ int wnext[kScanWaves][256];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int c = blockIdx.x;
-
-  // ---- per expert: histogram rows of the chunks before this one, and of
-  // all chunks.  Thread (g, e) sums chunks g, g + G, ... (8 loads in flight).
-  {
-    const int G = kScanThreads / E;
-    const int e = tid % E, g = tid / E;
-    int pre = 0, tot = 0;
-    if (g < G) {
-      constexpr int U = 8;
-      for (int cc0 = g; cc0 < nchunks; cc0 += G * U) {
-        int v[U];
-#pragma unroll
-        for (int u = 0; u < U; u++) {
-          const int cc = cc0 + u * G;
-          v[u] = cc < nchunks ? chunk_hist[(size_t)cc * E + e] : 0;
-        }
-#pragma unroll
-        for (int u = 0; u < U; u++) {
-          tot += v[u];
-          pre += cc0 + u * G < c ? v[u] : 0;
-        }
-      }
-    }
-    spre[tid] = pre;
-    stot[tid] = tot;
-  }
-  __syncthreads();
-  const int e = tid;
-  int pre = 0, tot = 0;
-  if (e < E) {
-    const int G = kScanThreads / E;
-    for (int g = 0; g < G; g++) {
-      pre += spre[g * E + e];
-      tot += stot[g * E + e];
-    }
-  }
-  const int off = block_exclusive_scan(tot, tmp);
-
-  if (c == 0) {
-    const int tiles = (tot + block_m - 1) / block_m;
-    const int tile0 = block_exclusive_scan(tiles, tmp);
-    if (e < E) {
-      counts[e] = tot;
-      offsets[e] = off;
-      for (int i = 0; i < tiles; i++) {
-        int32_t* b = blocks + 3 * (size_t)(tile0 + i);
-        b[0] = e;
-        b[1] = off + i * block_m;
-        b[2] = min(block_m, tot - i * block_m);
-      }
-    }
-    if (e == E - 1) {
-      offsets[E] = P;
-      num_blocks[0] = tile0 + tiles;
-    }
-  }
-
-  // ---- the chunk's pairs in one contiguous segment per wave
-  const int p0 = c * chunk_pairs;
-  const int p1 = min(P, p0 + chunk_pairs);
-  const int q = (((p1 - p0) + 64 * kScanWaves - 1) / (64 * kScanWaves)) * 64;
-  const int w0 = min(p1, p0 + wave * q), w1 = min(p1, w0 + q);
-  for (int i = lane; i < E; i += 64) wnext[wave][i] = 0;
-  __syncthreads();
-  for (int p = w0 + lane; p < w1; p += 64) {
-    const int id = ids[p];
-    if (id >= 0 && id < E) atomicAdd(&wnext[wave][id], 1);
-  }
-  __syncthreads();
-  if (e < E) {
-    int run = off + pre;
-#pragma unroll
-    for (int w = 0; w < kScanWaves; w++) {
-      const int n = wnext[w][e];
-      wnext[w][e] = run;
-      run += n;
-    }
-  }
-  __syncthreads();
-
-  int bits = 1;
-  while ((1 << bits) < E) bits++;
-  int* next = wnext[wave];
-  for (int base = w0; base < w1; base += 64) {
-    const int p = base + lane;
-    const int id = p < w1 ? ids[p] : -1;
-    const bool active = id >= 0 && id < E;
-    const int ex = active ? id : 0;
-    uint64_t match = __ballot(active);
-    for (int b = 0; b < bits; b++) {
-      const bool bit = (ex >> b) & 1;
-      const uint64_t bal = __ballot(bit);
-      match &= bit ? bal : ~bal;
-    }
-    const uint64_t below = match & ((1ull << lane) - 1ull);
-    const int rank = __popcll(below);
-    const int start = active ? next[ex] : 0;
-    wave_lds_sync();
-    if (active) {
-      const int slot = start + rank;
-      sorted_pairs[slot] = p;
-      pair_slot[p] = slot;
-      if (below == 0) next[ex] = start + __popcll(match);  // lowest lane of its group
-    }
-    wave_lds_sync();
-  }
+  scan_scatter_chunk(ids, P, E, chunk_pairs, nchunks, chunk_hist, block_m, counts, offsets,
+                     sorted_pairs, pair_slot, blocks, num_blocks, blockIdx.x);
 }
 
 }  // namespace

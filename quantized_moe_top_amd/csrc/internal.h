@@ -107,6 +107,15 @@ int route_chunks(int64_t T);
 hipError_t launch_route(const uint16_t* x, const uint16_t* wr, float* logits, int T, int H, int E,
                         int k, int32_t* ids, float* w, half_t* xh, int32_t* chunk_hist,
                         hipStream_t s);
+// T small enough for one routing chunk: S1 and S2-S5 in one launch (after the
+// router GEMM when wr is given); same outputs as launch_route followed by
+// launch_scan_scatter.
+bool route_build_fused(int64_t T);
+hipError_t launch_route_build(const uint16_t* x, const uint16_t* wr, float* logits, int T, int H,
+                              int E, int k, int32_t* ids, float* w, half_t* xh,
+                              int32_t* chunk_hist, int block_m, int32_t* counts, int32_t* offsets,
+                              int32_t* sorted_pairs, int32_t* pair_slot, int32_t* blocks,
+                              int32_t* num_blocks, hipStream_t s);
 // Per-chunk expert histogram of caller-given ids [T][k].
 hipError_t launch_chunk_hist(const int32_t* ids, int T, int k, int E, int32_t* chunk_hist,
                              hipStream_t s);

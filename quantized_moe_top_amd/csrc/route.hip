@@ -21,7 +21,7 @@
 //   3. (whole-layer mode) the chunk's expert histogram (LDS atomics: counts
 //      do not depend on order), and x bf16 -> fp16 in the interleaved order
 //      the grouped GEMM reads.
-#include "internal.h"
+#include "scan_scatter.h"
 
 namespace moe {
 namespace {
@@ -243,13 +243,13 @@ __device__ void load_logits(const RouteParams& p, int t0, int nt, float* lg) {
 }
 
 template <bool FULL, int NK>
-__global__ __launch_bounds__(kRouteThreads) void route_kernel(const RouteParams p) {
+__device__ __forceinline__ void route_chunk(const RouteParams& p, int chunk) {
   __shared__ float lg[kSub * 256];
   __shared__ int hist[256];
   const int tid = threadIdx.x, wave = tid >> 6;
   constexpr int kWaves = kRouteThreads / 64;
   if (FULL && tid < 256) hist[tid] = 0;
-  const int c0 = blockIdx.x * p.chunk_tokens;
+  const int c0 = chunk * p.chunk_tokens;
   const int c1 = min(p.T, c0 + p.chunk_tokens);
   for (int t0 = c0; t0 < c1; t0 += kSub) {
     const int nt = min(kSub, c1 - t0);
@@ -261,7 +261,32 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const RouteParams 
                      p.w + (size_t)(t0 + r) * p.k, FULL ? hist : nullptr);
     __syncthreads();
   }
-  if (FULL && tid < p.E) p.chunk_hist[(size_t)blockIdx.x * p.E + tid] = hist[tid];
+  if (FULL && tid < p.E) p.chunk_hist[(size_t)chunk * p.E + tid] = hist[tid];
+}
+
+template <bool FULL, int NK>
+__global__ __launch_bounds__(kRouteThreads) void route_kernel(const RouteParams p) {
+  route_chunk<FULL, NK>(p, blockIdx.x);
+}
+
+// Outputs of S2-S5 for the fused single-chunk kernel.
+struct BuildParams {
+  int block_m;
+  int32_t *counts, *offsets, *sorted_pairs, *pair_slot, *blocks, *num_blocks;
+};
+
+// All tokens in one chunk (decode sizes): one workgroup routes them (S1),
+// then, after a barrier that makes its ids and histogram visible to the
+// whole workgroup, builds counts, offsets, the scatter and the block map
+// (S2-S5): one launch instead of two, same results.
+template <int NK>
+__global__ __launch_bounds__(kRouteThreads) void route_build_kernel(const RouteParams p,
+                                                                    const BuildParams b) {
+  route_chunk<true, NK>(p, 0);
+  __threadfence_block();
+  __syncthreads();
+  scan_scatter_chunk(p.ids, p.T * p.k, p.E, p.chunk_tokens * p.k, 1, p.chunk_hist, b.block_m,
+                     b.counts, b.offsets, b.sorted_pairs, b.pair_slot, b.blocks, b.num_blocks, 0);
 }
 
 template <bool FULL>
@@ -302,6 +327,32 @@ hipError_t launch_route(const uint16_t* x, const uint16_t* wr, float* logits, in
   RouteParams p{x, logits, ids, w, xh, chunk_hist, T, H, E, k, route_chunk_tokens(T)};
   const int n = route_chunks(T);
   return xh ? launch_nk<true>(p, n, s) : launch_nk<false>(p, n, s);
+}
+
+bool route_build_fused(int64_t T) { return route_chunks(T) == 1; }
+
+hipError_t launch_route_build(const uint16_t* x, const uint16_t* wr, float* logits, int T, int H,
+                              int E, int k, int32_t* ids, float* w, half_t* xh,
+                              int32_t* chunk_hist, int block_m, int32_t* counts, int32_t* offsets,
+                              int32_t* sorted_pairs, int32_t* pair_slot, int32_t* blocks,
+                              int32_t* num_blocks, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  if (wr) {
+    const int64_t grid = (int64_t)((E + 31) / 32) * ((T + 31) / 32);
+    router_gemm_kernel<<<grid, 64 * kRouterWaves, 0, s>>>(x, wr, logits, T, H, E);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  RouteParams p{x, logits, ids, w, xh, chunk_hist, T, H, E, k, route_chunk_tokens(T)};
+  BuildParams b{block_m, counts, offsets, sorted_pairs, pair_slot, blocks, num_blocks};
+  switch ((E + 63) / 64) {
+    case 1: route_build_kernel<1><<<1, kRouteThreads, 0, s>>>(p, b); break;
+    case 2: route_build_kernel<2><<<1, kRouteThreads, 0, s>>>(p, b); break;
+    case 3: route_build_kernel<3><<<1, kRouteThreads, 0, s>>>(p, b); break;
+    case 4: route_build_kernel<4><<<1, kRouteThreads, 0, s>>>(p, b); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace moe
