@@ -106,7 +106,8 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void w4_mfma_kernel(const Mf
   __shared__ __attribute__((aligned(16))) char lds[kStages * STAGE];
   __shared__ float row_w[BM];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS and block addresses stay scalar
   const int col = lane & 31, khalf = lane >> 5;
 
   // ---- work item: XCD-contiguous ranges over (tile, column block)
