@@ -90,10 +90,11 @@ typedef struct {
  *  words: uint32 [E][N/128][K/64][4 blocks][32 columns][2 halves][4 words]:
  *         for column 128c + 32u + cc (chunk c, block u) and half h of slab s,
  *         the four row-major words holding codes 64s + 32h .. 64s + 32h + 31
- *         (same nibble order); each chunk is one contiguous 4 KiB run per
- *         slab.
- *  sb:    uint32 [E][N/128][K/G][128 columns]: bf16 scale bits in the low 16
- *         bits, bf16 bias bits in the high 16 bits.
+ *         (same nibble order), each word rotated left by 5 bits; each chunk
+ *         is one contiguous 4 KiB run per slab.
+ *  sb:    uint32 [E][N/128][K/G][128 columns]: the scale as fp16 in the low
+ *         16 bits, bias - 32 * scale as fp16 in the high 16 bits (rounded to
+ *         nearest; exact for bias = -8 * scale).
  * Requires N % 128 == 0, K % 128 == 0, G in {32, 64, 128}, K % G == 0. */
 typedef struct {
   const uint32_t* words;

@@ -234,8 +234,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void w4_mfma_kernel(const Mf
       for (int cb = 0; cb < 2; cb++) {
         const uint32_t sb = reinterpret_cast<const uint32_t*>(
             base + A_BYTES + kBStage)[(G32 ? khalf : 0) * kBCols + wave * 64 + cb * 32 + col];
-        s2[cb] = bf16_pair_to_half2(sb & 0xFFFFu);
-        b2[cb] = bf16_pair_to_half2(sb >> 16);
+        sb_pairs(sb, s2[cb], b2[cb]);
       }
 #pragma unroll
       for (int i = 0; i < 4; i++) {

@@ -115,7 +115,8 @@ __global__ __launch_bounds__(64 * kDecWavesMax) void w4_gemv_kernel(const DecPar
       load_x(min(s0 + j + 1, S - 1), xn);
 #pragma unroll
       for (int b = 0; b < NB; b++) {
-        const half2_t s2 = bf16_pair_to_half2(sb[b][j] & 0xFFFFu), b2 = bf16_pair_to_half2(sb[b][j] >> 16);
+        half2_t s2, b2;
+        sb_pairs(sb[b][j], s2, b2);
 #pragma unroll
         for (int i = 0; i < 4; i++) {
           const uint4 d = dequant_word(q[b][j][i], s2, b2);

@@ -41,31 +41,38 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t m
   return r;
 }
 
-// Dequantises one 32-bit word of eight 4-bit codes into eight fp16 weights
-// q * scale + bias, in the interleaved order (q0,q4,q1,q5,q2,q6,q3,q7).
-// Each 16-bit half of the word holds two codes of interest at bits 0..3 and
-// 4..7 (after a shift by 8 for the other two):
-//  - OR-ing the low nibble into the mantissa of 1024.0h gives 1024 + q;
-//  - OR-ing the second nibble, still at bits 4..7, into the mantissa of
-//    64.0h gives 64 + q (the mantissa step there is 1/16);
-// both exactly.  Subtracting 1024 or 64 recovers q exactly and one fused
-// multiply-add rounds once (exactly when bias = -8 * scale, because
-// (q - 8) * scale then needs at most 11 significant bits).  13 VALU
-// instructions per word.
+// Dequantises one packed 32-bit word of eight 4-bit codes into eight fp16
+// weights q * scale + bias, in the interleaved order (q0,q4,q1,q5,q2,q6,q3,q7).
+// The packed word is the row-major word rotated left by 5 bits, so code j
+// sits at bits (4j + 5) mod 32; a right rotation by 4k brings codes k and
+// k + 4 to bits 5..8 of the low and the high 16-bit half.  OR-ing them into
+// the mantissa of 32.0h (whose mantissa step is 1/32) gives 32 + q exactly,
+// and one fused multiply-add with the packed pair (scale, bias - 32 scale)
+// gives (32 + q) * scale + bias - 32 scale = q * scale + bias with a single
+// rounding.  bias - 32 scale is rounded to fp16 once, at pack time; with
+// bias = -8 * scale it is -40 * scale, exact (5 times an 8-bit scale fits in
+// 11 bits), and so is every weight ((q - 8) * scale needs at most 11
+// significant bits).  11 VALU instructions per word: 3 rotations, 4
+// v_and_or_b32, 4 v_pk_fma_f16.
 __device__ __forceinline__ uint4 dequant_word(uint32_t w, half2_t s2, half2_t b2) {
-  const uint32_t m_lo = 0x000F000Fu, m_hi = 0x00F000F0u;
-  const uint32_t k1024 = 0x64006400u, k64 = 0x54005400u;
-  const half2_t c1024 = {(half_t)1024.0f, (half_t)1024.0f};
-  const half2_t c64 = {(half_t)64.0f, (half_t)64.0f};
-  const uint32_t w8 = w >> 8;
-  const half2_t q0 = __builtin_bit_cast(half2_t, and_or(w, m_lo, k1024)) - c1024;   // q0, q4
-  const half2_t q1 = __builtin_bit_cast(half2_t, and_or(w, m_hi, k64)) - c64;       // q1, q5
-  const half2_t q2 = __builtin_bit_cast(half2_t, and_or(w8, m_lo, k1024)) - c1024;  // q2, q6
-  const half2_t q3 = __builtin_bit_cast(half2_t, and_or(w8, m_hi, k64)) - c64;      // q3, q7
-  return make_uint4(__builtin_bit_cast(uint32_t, __builtin_elementwise_fma(q0, s2, b2)),
-                    __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(q1, s2, b2)),
-                    __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(q2, s2, b2)),
-                    __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(q3, s2, b2)));
+  const uint32_t mask = 0x01E001E0u, k32 = 0x50005000u;  // bits 5..8 of each half; 32.0h
+  const half2_t v0 = __builtin_bit_cast(half2_t, and_or(w, mask, k32));  // q0, q4
+  const half2_t v1 = __builtin_bit_cast(half2_t, and_or(__builtin_amdgcn_alignbit(w, w, 4), mask, k32));
+  const half2_t v2 = __builtin_bit_cast(half2_t, and_or(__builtin_amdgcn_alignbit(w, w, 8), mask, k32));
+  const half2_t v3 = __builtin_bit_cast(half2_t, and_or(__builtin_amdgcn_alignbit(w, w, 12), mask, k32));
+  return make_uint4(__builtin_bit_cast(uint32_t, __builtin_elementwise_fma(v0, s2, b2)),
+                    __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(v1, s2, b2)),
+                    __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(v2, s2, b2)),
+                    __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(v3, s2, b2)));
+}
+
+// A packed (scale, bias) word -- fp16 scale in the low half, fp16
+// (bias - 32 scale) in the high half -- as the two broadcast pairs the
+// dequantisation takes.
+__device__ __forceinline__ void sb_pairs(uint32_t sb, half2_t& s2, half2_t& b2) {
+  const half2_t v = __builtin_bit_cast(half2_t, sb);
+  s2 = half2_t{v[0], v[0]};
+  b2 = half2_t{v[1], v[1]};
 }
 
 // Position of column j (0..7) of an 8-column run in the interleaved order.
@@ -81,11 +88,6 @@ __device__ __forceinline__ uint4 bf16x8_to_half_interleaved(uint4 v) {
   const half2_t o2 = {lo(v.y), lo(v.w)}, o3 = {hi(v.y), hi(v.w)};
   return make_uint4(__builtin_bit_cast(uint32_t, o0), __builtin_bit_cast(uint32_t, o1),
                     __builtin_bit_cast(uint32_t, o2), __builtin_bit_cast(uint32_t, o3));
-}
-
-__device__ __forceinline__ half2_t bf16_pair_to_half2(uint32_t s) {
-  half_t h = (half_t)bf16_bits_to_float(s);
-  return half2_t{h, h};
 }
 
 // silu(g) * u = g / (1 + e^-g) * u, with the hardware exponential and

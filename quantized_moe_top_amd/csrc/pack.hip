@@ -9,12 +9,15 @@
 // [2 halves][4 words].  For 128-column chunk c, slab s, 32-column block u of
 // the chunk, column cc of the block and half h, the four words hold codes
 // k = 64s + 32h + 8w + j of column 128c + 32u + cc (word w, nibble j, lowest
-// nibble first, as in the row-major words).  A 32-column block of one slab
-// is 1 KiB (one 16-byte load per lane), and the 128 columns of a chunk are
-// one contiguous 4 KiB run per slab: DRAM streams in long runs.
-// Packed scales and biases: uint32 [E][N/128][K/G][128 columns], the bf16
-// scale in the low half and the bf16 bias in the high half: 512 contiguous
-// bytes per chunk and group.
+// nibble first, as in the row-major words), each word rotated left by 5 bits
+// so that the dequantisation extracts two codes per instruction straight
+// into the mantissa of 32.0h.  A 32-column block of one slab is 1 KiB (one
+// 16-byte load per lane), and the 128 columns of a chunk are one contiguous
+// 4 KiB run per slab: DRAM streams in long runs.
+// Packed scales and biases: uint32 [E][N/128][K/G][128 columns], the scale
+// as fp16 in the low half and bias - 32 * scale as fp16 in the high half
+// (both rounded to nearest once, here): 512 contiguous bytes per chunk and
+// group.
 #include "internal.h"
 
 namespace moe {
@@ -33,7 +36,8 @@ __global__ __launch_bounds__(256) void pack_codes_kernel(const uint32_t* __restr
   const int s = (int)(rest % slabs);
   const int64_t ec = rest / slabs;  // e * N/128 + c
   const int64_t row = ec * 128 + u * 32 + cc;  // e * N + n
-  out[i] = q[row * (K / 8) + s * 8 + h * 4 + w];
+  const uint32_t v = q[row * (K / 8) + s * 8 + h * 4 + w];
+  out[i] = (v << 5) | (v >> 27);
 }
 
 __global__ __launch_bounds__(256) void pack_scales_kernel(const uint16_t* __restrict__ sc,
@@ -48,7 +52,10 @@ __global__ __launch_bounds__(256) void pack_scales_kernel(const uint16_t* __rest
   const int g = (int)(rest % gpr);
   const int64_t ec = rest / gpr;
   const int64_t src = (ec * 128 + cc) * gpr + g;
-  out[i] = (uint32_t)sc[src] | ((uint32_t)bi[src] << 16);
+  const float s = __uint_as_float((uint32_t)sc[src] << 16);
+  const float b = __uint_as_float((uint32_t)bi[src] << 16);
+  const half_t hs = (half_t)s, hb = (half_t)(b - 32.0f * s);
+  out[i] = (uint32_t)__builtin_bit_cast(uint16_t, hs) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
 }
 
 }  // namespace

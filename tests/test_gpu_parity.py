@@ -60,10 +60,14 @@ def test_pack_layout(E, N, K, G):
     # words [E][N/128][K/64][4][32][2][4] from q [E][N][K/8]: column 128c + 32u + cc, half h,
     # word w -> q[.., 8s + 4h + w]
     want = q.reshape(E, N // 128, 4, 32, K // 64, 2, 4).transpose(0, 1, 4, 2, 3, 5, 6).reshape(-1)
+    want = (want << np.uint32(5)) | (want >> np.uint32(27))  # each word rotated left by 5 bits
     assert np.array_equal(cpu(pb.words).view(np.uint32), want)
-    sc = bank.scales.view(torch.int16).numpy().view(np.uint16).astype(np.uint32)
-    bi = bank.biases.view(torch.int16).numpy().view(np.uint16).astype(np.uint32)
-    sbw = (sc | (bi << 16)).reshape(E, N // 128, 128, K // G).transpose(0, 1, 3, 2).reshape(-1)
+    # (scale, bias - 32 scale) as fp16, rounded to nearest from the fp32 values of the bf16 inputs
+    s32 = bank.scales.float().numpy()
+    b32 = bank.biases.float().numpy()
+    hs = s32.astype(np.float16).view(np.uint16).astype(np.uint32)
+    hb = (b32 - np.float32(32.0) * s32).astype(np.float16).view(np.uint16).astype(np.uint32)
+    sbw = (hs | (hb << 16)).reshape(E, N // 128, 128, K // G).transpose(0, 1, 3, 2).reshape(-1)
     assert np.array_equal(cpu(pb.sb).view(np.uint32), sbw)
 
 
