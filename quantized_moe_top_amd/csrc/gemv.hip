@@ -39,36 +39,32 @@ template <int MODE, int SPW>
 __global__ __launch_bounds__(64 * kDecWavesMax) void w4_gemv_kernel(const DecParams p) {
   constexpr bool GATE_UP = MODE == MOE_GEMM_GATE_UP_SWIGLU;
   constexpr int NB = GATE_UP ? 2 : 1;  // banks read: gate and up, or down
-  // rows 0..7 of each wave's 32x32 partial: register r < 4 of lane l holds
-  // row 4 (l / 32) + r, column l % 32
-  __shared__ float red[kDecWavesMax][NB][4][64];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nwaves = blockDim.x >> 6;
+  const int pass_slabs = nwaves * SPW;  // slabs per pass
+  const int xw = pass_slabs * 64;       // row stride of xs
+  // LDS, sized by the launch: xs = this pass's activation rows (<= 8 rows x
+  // xw reduction indices, operand order), staged once for all waves; red =
+  // rows 0..7 of each wave's 32x32 partial (register r < 4 of lane l holds
+  // row 4 (l / 32) + r, column l % 32), [wave][bank][r][lane]
+  extern __shared__ __attribute__((aligned(16))) char dsm[];
+  half_t* xs = reinterpret_cast<half_t*>(dsm);
+  float* red = reinterpret_cast<float*>(dsm + (size_t)kGemvMaxTokens * xw * 2);
   const int col = lane & 31, khalf = lane >> 5;
   const int nbl = p.N / 32;
   const int tile = blockIdx.x / nbl, blk = blockIdx.x % nbl;
 
-  const int nblk = min(*p.num_blocks, p.max_blocks);
-  if (tile >= nblk) return;
+  // the block count and this tile's entry are read together (the grid only
+  // covers tiles below max_blocks, inside the map's allocation)
+  const int nbm = *p.num_blocks;
   const int e = p.blocks[3 * tile], row0 = p.blocks[3 * tile + 1], rows = p.blocks[3 * tile + 2];
+  if (tile >= min(nbm, p.max_blocks)) return;
   // a malformed block map is skipped, never dereferenced out of bounds
   if (e < 0 || e >= p.E || rows <= 0 || rows > kGemvMaxTokens || row0 < 0 || row0 > p.P - rows)
     return;
   const int K = p.K, S = K / 64, gpr = K >> p.log2_G;
 
-  // this lane's activation row (MFMA row l % 32): token x (S6) or slot h
-  // (S7), both in operand order; rows past the tile read nothing
-  const bool has_row = col < rows;
-  const half_t* arow = p.a;
-  if (has_row) {
-    int r = row0 + col;
-    if (GATE_UP) {
-      const int pair = p.sorted_pairs[r];
-      r = (pair >= 0 && pair < p.P) ? pair / p.top_k : 0;
-    }
-    arow = p.a + (size_t)r * K + 32 * khalf;
-  }
   // packed block of this output block in each bank (chunked layout: 4 KiB
   // runs of 128 columns per slab)
   const size_t bidx = (size_t)e * nbl + blk;
@@ -85,15 +81,14 @@ __global__ __launch_bounds__(64 * kDecWavesMax) void w4_gemv_kernel(const DecPar
   floatx16_t acc[NB];
 #pragma unroll
   for (int b = 0; b < NB; b++) acc[b] = floatx16_t{};
-  for (int s0 = SPW * wave; s0 < S; s0 += SPW * nwaves) {
-    // the pass's codes and (scale, bias) words first (slabs past the end
-    // reload the last slab and are not multiplied), then per slab its
-    // activation fragments (L2-resident), one slab ahead
+  for (int base = 0; base < S; base += pass_slabs) {
+    // 1. this wave's codes and (scale, bias) words for the pass (slabs past
+    //    the end reload the last slab and are not multiplied)
     u32x4 q[NB][SPW];
     uint32_t sb[NB][SPW];
 #pragma unroll
     for (int j = 0; j < SPW; j++) {
-      const int s = min(s0 + j, S - 1);
+      const int s = min(base + SPW * wave + j, S - 1);
       const int g = (64 * s + 32 * khalf) >> p.log2_G;
 #pragma unroll
       for (int b = 0; b < NB; b++) {
@@ -101,18 +96,31 @@ __global__ __launch_bounds__(64 * kDecWavesMax) void w4_gemv_kernel(const DecPar
         sb[b][j] = ssrc[b][(size_t)g * 128];
       }
     }
-    auto load_x = [&](int s, u32x4 (&x)[4]) {
-#pragma unroll
-      for (int i = 0; i < 4; i++)
-        x[i] = has_row ? *reinterpret_cast<const u32x4*>(arow + 64 * s + 8 * i) : u32x4{0, 0, 0, 0};
-    };
-    u32x4 x[4];
-    load_x(s0, x);
+    // 2. the tile's activation rows for the pass into LDS, 16 bytes per
+    //    thread and step: token x rows (S6) or slots of h (S7)
+    const int nsl = min(pass_slabs, S - base);
+    const int c8n = nsl * 8;  // 16-byte pieces per row
+    for (int idx = tid; idx < rows * c8n; idx += blockDim.x) {
+      const int m = idx / c8n, c8 = idx % c8n;
+      int r = row0 + m;
+      if (GATE_UP) {
+        const int pair = p.sorted_pairs[r];
+        r = (pair >= 0 && pair < p.P) ? pair / p.top_k : 0;
+      }
+      *reinterpret_cast<uint4*>(xs + m * xw + 8 * c8) =
+          *reinterpret_cast<const uint4*>(p.a + (size_t)r * K + 64 * base + 8 * c8);
+    }
+    __syncthreads();
+    // 3. dequantise and multiply; MFMA rows past the tile are zero
 #pragma unroll
     for (int j = 0; j < SPW; j++) {
-      if (s0 + j >= S) break;  // uniform per wave
-      u32x4 xn[4];
-      load_x(min(s0 + j + 1, S - 1), xn);
+      const int sl = SPW * wave + j;  // slab within the pass
+      if (base + sl >= S) break;      // uniform per wave
+      u32x4 x[4];
+#pragma unroll
+      for (int i = 0; i < 4; i++)
+        x[i] = col < rows ? *reinterpret_cast<const u32x4*>(xs + col * xw + 64 * sl + 32 * khalf + 8 * i)
+                          : u32x4{0, 0, 0, 0};
 #pragma unroll
       for (int b = 0; b < NB; b++) {
         half2_t s2, b2;
@@ -124,14 +132,13 @@ __global__ __launch_bounds__(64 * kDecWavesMax) void w4_gemv_kernel(const DecPar
               __builtin_bit_cast(half8_t, x[i]), __builtin_bit_cast(half8_t, d), acc[b], 0, 0, 0);
         }
       }
-#pragma unroll
-      for (int i = 0; i < 4; i++) x[i] = xn[i];
     }
+    __syncthreads();  // the next pass overwrites xs
   }
 #pragma unroll
   for (int b = 0; b < NB; b++)
 #pragma unroll
-    for (int r = 0; r < 4; r++) red[wave][b][r][lane] = acc[b][r];
+    for (int r = 0; r < 4; r++) red[((wave * NB + b) * 4 + r) * 64 + lane] = acc[b][r];
   __syncthreads();
   for (int t = tid; t < rows * 32; t += blockDim.x) {
     const int m = t >> 5, cc = t & 31;
@@ -139,8 +146,8 @@ __global__ __launch_bounds__(64 * kDecWavesMax) void w4_gemv_kernel(const DecPar
     float v[NB];
 #pragma unroll
     for (int b = 0; b < NB; b++) {
-      v[b] = red[0][b][rr][ll];
-      for (int w2 = 1; w2 < nwaves; w2++) v[b] += red[w2][b][rr][ll];
+      v[b] = red[((0 * NB + b) * 4 + rr) * 64 + ll];
+      for (int w2 = 1; w2 < nwaves; w2++) v[b] += red[((w2 * NB + b) * 4 + rr) * 64 + ll];
     }
     const int n = blk * 32 + cc;
     if (GATE_UP) {
@@ -171,12 +178,15 @@ hipError_t launch_w4_gemv(const GemmArgs& a, hipStream_t s) {
   const bool wide = a.K >= 1024 && grid >= 1024;
   const int spw = wide ? 4 : 2;
   const int waves = (int)std::max<int64_t>(1, std::min<int64_t>(kDecWavesMax, a.K / (64 * spw)));
+  const int nb = a.mode == MOE_GEMM_GATE_UP_SWIGLU ? 2 : 1;
+  // LDS: activation rows of one pass + the waves' partial sums
+  const size_t lds = (size_t)kGemvMaxTokens * waves * spw * 64 * 2 + (size_t)waves * nb * 4 * 64 * 4;
   if (a.mode == MOE_GEMM_GATE_UP_SWIGLU) {
-    if (wide) w4_gemv_kernel<MOE_GEMM_GATE_UP_SWIGLU, 4><<<grid, 64 * waves, 0, s>>>(p);
-    else w4_gemv_kernel<MOE_GEMM_GATE_UP_SWIGLU, 2><<<grid, 64 * waves, 0, s>>>(p);
+    if (wide) w4_gemv_kernel<MOE_GEMM_GATE_UP_SWIGLU, 4><<<grid, 64 * waves, lds, s>>>(p);
+    else w4_gemv_kernel<MOE_GEMM_GATE_UP_SWIGLU, 2><<<grid, 64 * waves, lds, s>>>(p);
   } else {
-    if (wide) w4_gemv_kernel<MOE_GEMM_DOWN, 4><<<grid, 64 * waves, 0, s>>>(p);
-    else w4_gemv_kernel<MOE_GEMM_DOWN, 2><<<grid, 64 * waves, 0, s>>>(p);
+    if (wide) w4_gemv_kernel<MOE_GEMM_DOWN, 4><<<grid, 64 * waves, lds, s>>>(p);
+    else w4_gemv_kernel<MOE_GEMM_DOWN, 2><<<grid, 64 * waves, lds, s>>>(p);
   }
   return hipGetLastError();
 }
