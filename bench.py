@@ -241,6 +241,17 @@ def main():
     ms_per_step = elapsed_ms / K
     value = T * K / (elapsed_ms / 1e3)
 
+    # launch floor: the same number of steps replaying a graph of one
+    # one-element fill kernel (what a step of the layer costs at the very
+    # least per kernel it launches)
+    floor = torch.zeros(1, device=dev)
+    gf = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gf):
+        floor.fill_(1.0)
+    gf.replay()
+    floor_ms, _ = timed(lambda i: gf.replay())
+    launch_floor_us = floor_ms / K * 1e3
+
     # per-stage durations: an eager pass of the same steps with events
     # recorded between the stages on the layer's stream
     ev = [api.stage_events(nst + 1) for _ in range(K)]
@@ -305,6 +316,7 @@ def main():
                    "launch": "eager" if graphs is None else "hip_graph"},
         "roofline": roofline, "layer_roofline": layer_roof, "stage_us": stage_us,
         "eager_ms_per_step": round(eager_ms / K, 6),
+        "launch_floor_us": round(launch_floor_us, 3),
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
