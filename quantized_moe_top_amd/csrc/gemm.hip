@@ -4,26 +4,27 @@
 // grouped GEMM keeps expanded 16-bit weights out of memory), the activation
 // staging pass of the standalone entry point, and the S8 combine.
 //
-// One workgroup (512 threads = 8 waves) computes a tile of BM rows (slots of
-// one expert, from the block map) x 512 weight columns: 256 columns of the
-// gate bank and the same 256 of the up bank (S6), or 512 columns of the down
-// bank (S7), over the whole reduction dimension in slabs of 64.  Wave w owns
-// all BM rows and two 32-column blocks (gate and up columns 32w.. in S6,
+// One workgroup of W waves computes a tile of BM rows (slots of one expert,
+// from the block map) x 64 W weight columns: 32 W columns of the gate bank
+// and the same 32 W of the up bank (S6), or 64 W columns of the down bank
+// (S7), over the whole reduction dimension in slabs of 64.  Wave w owns all
+// BM rows and two 32-column blocks (gate and up columns 32w.. in S6,
 // columns 64w.. in S7), so every word of codes it dequantises feeds BM/32
-// MFMAs per block.
+// MFMAs per block.  W is 4 (two workgroups per CU) except for 128-row tiles
+// of S7, which take 8 waves and one workgroup per CU.
 //
 // Operands reach LDS with global_load_lds_dwordx4 (each lane's 16 bytes
 // land at the instruction's LDS base + 16 * lane, no registers involved)
-// into a ring of 4 stages; the loads for slab s + 3 are issued while slab s
-// is computed, so three slabs of loads are in flight and the compute reads
-// only LDS.  Per slab and stage:
+// into a ring of R stages (R = 4, or 3 for 128-row tiles of S6); the loads
+// for slab s + R - 1 are issued while slab s is computed, so R - 1 slabs of
+// loads are in flight and the compute reads only LDS.  Per slab and stage:
 //  - A: BM rows x 64 fp16 activations (operand order), 128 bytes a row, the
 //    16-byte chunk c of row r at position c ^ (r % 8).  Rows past the tile's
 //    end load a valid row whose results are never stored.
 //  - B: packed codes (tile-major, see moe_w4_pack): per 32-column block one
 //    contiguous 1 KiB piece [32 columns][2 reduction halves] x 16 bytes.
-//    Each lane dequantises its 16 bytes in registers (13 VALU instructions
-//    per 8 codes) against the column's scale and bias converted to fp16.
+//    Each lane dequantises its 16 bytes in registers (11 VALU instructions
+//    per 8 codes) against the column's packed fp16 scale and bias.
 //  - S: per column and reduction half the packed (scale, bias) word of the
 //    slab's group, 128 contiguous bytes per 32 columns.
 // One wait (s_waitcnt on this wave's own outstanding loads, a count known
@@ -43,7 +44,6 @@ template <int V>
 struct IntTag {
   static constexpr int value = V;
 };
-constexpr int kStages = 4;
 
 struct MfmaParams {
   const half_t* a;
@@ -89,8 +89,10 @@ __device__ __forceinline__ void wait_vm_barrier() {
 // main loop; 128-row tiles use 8 waves (one workgroup per CU).
 // G32: group size 32, the two reduction halves of a slab have their own
 // (scale, bias) words; for G >= 64 one word serves both and is copied once.
-template <int MODE, int MB, int WAVES, bool G32>
-__global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void w4_mfma_kernel(const MfmaParams p) {
+// STAGES: depth of the LDS ring (STAGES - 1 slabs in flight); WGS_PER_CU:
+// workgroups meant to share a CU (register budget).
+template <int MODE, int MB, int WAVES, bool G32, int STAGES, int WGS_PER_CU>
+__global__ __launch_bounds__(64 * WAVES, WGS_PER_CU) void w4_mfma_kernel(const MfmaParams p) {
   constexpr bool GATE_UP = MODE == MOE_GEMM_GATE_UP_SWIGLU;
   constexpr int BM = MB * 32;
   constexpr int kBCols = 64 * WAVES;                     // weight columns per workgroup
@@ -103,7 +105,7 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void w4_mfma_kernel(const Mf
   constexpr int B_PER_WAVE = 2;                          // 1 KiB code blocks per wave
   constexpr int S_PER_WAVE = G32 ? 2 : 1;                // 256 B scale-word loads per wave
   constexpr int OUT_COLS = GATE_UP ? kBCols / 2 : kBCols; // output columns per workgroup
-  __shared__ __attribute__((aligned(16))) char lds[kStages * STAGE];
+  __shared__ __attribute__((aligned(16))) char lds[STAGES * STAGE];
   __shared__ float row_w[BM];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -254,21 +256,21 @@ __global__ __launch_bounds__(64 * WAVES, 8 / WAVES) void w4_mfma_kernel(const Mf
       }
     };
 
-    // slab s lives in stage s % 4.  Every slab step issues the same copies
-    // (slabs past the end reload the last slab into a stage that is never
-    // read again), so when slab s is about to be computed exactly the copies
-    // of two later slabs (2 * DA instructions of this wave) were issued after
-    // its own: waiting until at most 2 * DA are outstanding means slab s has
-    // landed.  Right after the barrier, stage (s + 3) % 4 (computed last at
-    // slab s - 1, by every wave) is refilled with slab s + 3.
+    // slab s lives in stage s % STAGES.  Every slab step issues the same
+    // copies (slabs past the end reload the last slab into a stage that is
+    // never read again), so when slab s is about to be computed exactly the
+    // copies of STAGES - 2 later slabs ((STAGES - 2) * DA instructions of this
+    // wave) were issued after its own: waiting until at most that many are
+    // outstanding means slab s has landed.  Right after the barrier, stage
+    // (s + STAGES - 1) % STAGES (computed last at slab s - 1, by every wave)
+    // is refilled with slab s + STAGES - 1.
     const int S = slabs;
-    issue(0, 0);
-    issue(min(1, S - 1), 1);
-    issue(min(2, S - 1), 2);
+#pragma unroll
+    for (int j = 0; j < STAGES - 1; j++) issue(min(j, S - 1), j);
     for (int s = 0; s < S; s++) {
-      wait_vm_barrier<2 * DA>();
-      issue(min(s + 3, S - 1), (s + 3) & 3);
-      compute(s & 3);
+      wait_vm_barrier<(STAGES - 2) * DA>();
+      issue(min(s + STAGES - 1, S - 1), (s + STAGES - 1) % STAGES);
+      compute(s % STAGES);
     }
   };
   // uniform per workgroup: every wave takes the same branch
@@ -339,18 +341,28 @@ hipError_t launch_mode(const GemmArgs& a, hipStream_t s) {
   const int log2_G = a.G == 32 ? 5 : a.G == 64 ? 6 : 7;  // G in {32, 64, 128}
   MfmaParams p{a.a, a.b0, a.b1, a.sorted_pairs, a.topk_weights, a.blocks, a.num_blocks, a.out,
                a.N, a.K, log2_G, a.top_k, a.E, (int)P, (int)max_blocks};
-  const int bcols = a.block_m == 128 ? 512 : 256;  // 64 * waves, as in the switch below
+  // 128-row tiles: S6 with 4 waves and a 3-stage ring (two workgroups per
+  // CU, one's epilogue overlapping the other's main loop); S7 with 8 waves
+  // and 4 stages (its short reduction, K = I, prefers the deeper ring)
+  constexpr bool kWide = MODE != MOE_GEMM_GATE_UP_SWIGLU;
+  const int bcols = a.block_m == 128 && kWide ? 512 : 256;  // 64 * waves, as in the switch below
   const int out_cols = MODE == MOE_GEMM_GATE_UP_SWIGLU ? bcols / 2 : bcols;
   const int64_t items = max_blocks * ((a.N + out_cols - 1) / out_cols);
   const int64_t grid = ((items + kNumXcd - 1) / kNumXcd) * kNumXcd;
   const bool g32 = a.G == 32;
   switch (a.block_m * 2 + (g32 ? 1 : 0)) {
-    case 64: w4_mfma_kernel<MODE, 1, 4, false><<<grid, 256, 0, s>>>(p); break;
-    case 65: w4_mfma_kernel<MODE, 1, 4, true><<<grid, 256, 0, s>>>(p); break;
-    case 128: w4_mfma_kernel<MODE, 2, 4, false><<<grid, 256, 0, s>>>(p); break;
-    case 129: w4_mfma_kernel<MODE, 2, 4, true><<<grid, 256, 0, s>>>(p); break;
-    case 256: w4_mfma_kernel<MODE, 4, 8, false><<<grid, 512, 0, s>>>(p); break;
-    case 257: w4_mfma_kernel<MODE, 4, 8, true><<<grid, 512, 0, s>>>(p); break;
+    case 64: w4_mfma_kernel<MODE, 1, 4, false, 4, 2><<<grid, 256, 0, s>>>(p); break;
+    case 65: w4_mfma_kernel<MODE, 1, 4, true, 4, 2><<<grid, 256, 0, s>>>(p); break;
+    case 128: w4_mfma_kernel<MODE, 2, 4, false, 4, 2><<<grid, 256, 0, s>>>(p); break;
+    case 129: w4_mfma_kernel<MODE, 2, 4, true, 4, 2><<<grid, 256, 0, s>>>(p); break;
+    case 256:
+      if (kWide) w4_mfma_kernel<MODE, 4, 8, false, 4, 1><<<grid, 512, 0, s>>>(p);
+      else w4_mfma_kernel<MODE, 4, 4, false, 3, 2><<<grid, 256, 0, s>>>(p);
+      break;
+    case 257:
+      if (kWide) w4_mfma_kernel<MODE, 4, 8, true, 4, 1><<<grid, 512, 0, s>>>(p);
+      else w4_mfma_kernel<MODE, 4, 4, true, 3, 2><<<grid, 256, 0, s>>>(p);
+      break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
