@@ -85,8 +85,9 @@ __device__ __forceinline__ void wait_vm_barrier() {
 
 // WAVES waves per workgroup (4 or 8): the tile covers 64 * WAVES weight
 // columns.  With 4 waves two workgroups fit a CU (LDS <= 80 KiB) for tiles of
-// up to 64 rows, so one workgroup's prologue and epilogue overlap another's
-// main loop; 128-row tiles use 8 waves (one workgroup per CU).
+// up to 64 rows (and for 128-row S6 tiles), so one workgroup's prologue and
+// epilogue overlap another's main loop; 128-row S7 tiles use 8 waves (one
+// workgroup per CU).
 // G32: group size 32, the two reduction halves of a slab have their own
 // (scale, bias) words; for G >= 64 one word serves both and is copied once.
 // STAGES: depth of the LDS ring (STAGES - 1 slabs in flight); WGS_PER_CU:

@@ -11,13 +11,15 @@
 // fill the chip and the logits are deterministic.
 //
 // The routing kernel: one workgroup (8 waves) owns a chunk of consecutive
-// tokens and walks it in sub-tiles of up to 32 tokens:
-//   1. the sub-tile's logits into LDS;
-//   2. top-k per token, one wave per token, by a radix select over the
-//      order-preserving integer image of the logits: 32 rounds of a
-//      wave-wide ballot count find the k-th largest key; keys above it and
-//      the lowest-index keys equal to it are the selection; ranks among the
-//      k selected give (logit descending, index ascending) order;
+// tokens and walks it in passes of 8, 32 or 64 tokens (64, 16 or 8 lanes
+// per token):
+//   1. the pass's logits into LDS;
+//   2. top-k per token, in (logit descending, index ascending) order: for
+//      chunks of at most 8 tokens a wave per token runs a radix select
+//      (topk_token); for larger chunks a group of 16 or 8 lanes per token
+//      keeps per-lane sorted lists of 64-bit keys (logit image, inverted
+//      index) and merges them across the group by bitonic merges
+//      (topk_group), all on the VALU, so many tokens proceed at once;
 //   3. (whole-layer mode) the chunk's expert histogram (LDS atomics: counts
 //      do not depend on order), and x bf16 -> fp16 in the interleaved order
 //      the grouped GEMM reads.
@@ -26,7 +28,7 @@
 namespace moe {
 namespace {
 
-constexpr int kSub = 32;        // tokens per sub-tile
+constexpr int kLgFloats = 16384;  // LDS logits of one pass (64 KiB)
 constexpr int kRouteThreads = 512;
 constexpr int kRouterBatch = 16;  // MFMA steps whose loads are issued together
 
@@ -97,6 +99,7 @@ struct RouteParams {
   half_t* xh;           // fp16 [T][H] staged activations (whole-layer mode)
   int32_t* chunk_hist;  // [nchunks][E] (whole-layer mode)
   int T, H, E, k, chunk_tokens;
+  int lpt_log2;         // lanes per token in the top-k (log2)
 };
 
 // Order-preserving map of an fp32 bit pattern onto unsigned integers
@@ -112,8 +115,14 @@ __device__ __forceinline__ float readlane_f(float v, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
 
-// Top-k of one token whose E logits are l[0..E); the calling wave writes
-// ids[0..k) and w[0..k) and, when hist != nullptr, counts the chosen experts.
+// Top-k of one token by a whole wave (few tokens per chunk: the serial
+// chain of ballots is shorter than the merges of a lane group), the E
+// logits at l[0..E): a 32-round radix select over the order-preserving
+// keys (each round a ballot count of keys at or above the candidate) finds
+// the k-th largest key; keys above it and the lowest-index keys equal to it
+// are the selection; ranks among the selected give (logit descending, index
+// ascending) order.  The wave writes ids[0..k) and w[0..k) and, when
+// hist != nullptr, counts the chosen experts.
 template <int NK>
 __device__ void topk_token(const float* l, int E, int k, int32_t* ids, float* w, int* hist) {
   const int lane = threadIdx.x & 63;
@@ -205,6 +214,146 @@ __device__ void topk_token(const float* l, int E, int k, int32_t* ids, float* w,
   }
 }
 
+// Selection key of expert e with logit v: the order-preserving image of v
+// in the high word and ~e in the low word, so a larger key is a larger logit
+// or, between equal logits, the lower expert index (the tie rule).  Every
+// key of a real expert is above 0, the key of an empty slot.
+__device__ __forceinline__ uint64_t sel_key(float v, int e) {
+  return ((uint64_t)ordered_bits(v) << 32) | (uint32_t)~e;
+}
+__device__ __forceinline__ int key_expert(uint64_t key) { return (int)~(uint32_t)key; }
+__device__ __forceinline__ float key_logit(uint64_t key) {
+  const uint32_t u = (uint32_t)(key >> 32);
+  return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
+}
+
+// Partner value for butterfly round m of a lane group: lanes 0..m-1 and
+// m..2m-1 of every 2m-lane block are paired up.  Up to 8 the pairing runs
+// on DPP lane moves inside the VALU (quad permutations for 1 and 2, the
+// 8- and 16-lane mirrors for 4 and 8, which pair lane i with 2m - 1 - i);
+// beyond, a ds_bpermute exchange with lane ^ m.
+template <int M>
+__device__ __forceinline__ uint32_t partner32(uint32_t v) {
+  const int x = (int)v;
+  if constexpr (M == 1) return (uint32_t)__builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, true);   // quad_perm 1,0,3,2
+  else if constexpr (M == 2) return (uint32_t)__builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, true);   // quad_perm 2,3,0,1
+  else if constexpr (M == 4) return (uint32_t)__builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, true);  // row_half_mirror
+  else if constexpr (M == 8) return (uint32_t)__builtin_amdgcn_mov_dpp(x, 0x140, 0xF, 0xF, true);  // row_mirror
+  else return (uint32_t)__shfl_xor(x, M);
+}
+template <int M>
+__device__ __forceinline__ uint64_t partner64(uint64_t v) {
+  return ((uint64_t)partner32<M>((uint32_t)(v >> 32)) << 32) | partner32<M>((uint32_t)v);
+}
+
+
+// Compare-exchange: K[i] gets the larger key, K[j] the smaller.
+__device__ __forceinline__ void cex(uint64_t& a, uint64_t& b) {
+  const uint64_t x = a, y = b;
+  const bool gt = x > y;
+  a = gt ? x : y;
+  b = gt ? y : x;
+}
+
+// Sorts a bitonic sequence of L keys into descending order.
+template <int L>
+__device__ __forceinline__ void bitonic_merge_desc(uint64_t (&K)[L]) {
+#pragma unroll
+  for (int d = L / 2; d >= 1; d >>= 1)
+#pragma unroll
+    for (int i = 0; i < L; i++)
+      if ((i & d) == 0) cex(K[i], K[i + d]);
+}
+
+// Sorts L arbitrary keys into descending order (bitonic sorting network).
+template <int L>
+__device__ __forceinline__ void bitonic_sort_desc(uint64_t (&K)[L]) {
+#pragma unroll
+  for (int size = 2; size <= L; size <<= 1)
+#pragma unroll
+    for (int d = size / 2; d >= 1; d >>= 1)
+#pragma unroll
+      for (int i = 0; i < L; i++)
+        if ((i & d) == 0) {
+          if ((i & size) == 0) cex(K[i], K[i + d]);
+          else cex(K[i + d], K[i]);
+        }
+}
+
+// K = the L largest of K and P, both sorted descending: the elementwise
+// larger of K and reversed P is a bitonic sequence holding them.
+template <int L>
+__device__ __forceinline__ void merge_top(uint64_t (&K)[L], const uint64_t (&P)[L]) {
+#pragma unroll
+  for (int i = 0; i < L; i++) K[i] = K[i] > P[L - 1 - i] ? K[i] : P[L - 1 - i];
+  bitonic_merge_desc<L>(K);
+}
+
+// Butterfly rounds M, 2M, ... below LPT (unrolled at compile time).
+template <int L, int LPT, int M>
+__device__ __forceinline__ void butterfly(uint64_t (&K)[L]) {
+  if constexpr (M < LPT) {
+    uint64_t P[L];
+#pragma unroll
+    for (int i = 0; i < L; i++) P[i] = partner64<M>(K[i]);
+    merge_top<L>(K, P);
+    butterfly<L, LPT, 2 * M>(K);
+  }
+}
+
+// Top-k of one token by a group of LPT consecutive lanes (LPT in {8, 16,
+// 64}), sub = lane within the group, l = the token's E logits.
+//  1. Lane sub keeps the L largest keys (L >= k) of experts sub, sub + lpt,
+//     ..., sorted in descending order: blocks of L keys are sorted by a
+//     bitonic network and merged into the list.
+//  2. log2(lpt) butterfly rounds: a lane and its partner hold the sorted top
+//     L of disjoint expert sets and both merge them into the top L of the
+//     union, so after the last round every lane holds the token's top L in
+//     (logit descending, index ascending) order: rank j is entry j.
+//  3. Softmax over the first k logits, max-subtracted, the denominator
+//     summed in rank order; lane sub writes ranks sub, sub + lpt, ... < k
+//     and, when hist != nullptr, counts the chosen experts.
+// All branches are uniform over the group, so a group never diverges.
+template <int L, int LPT>
+__device__ __forceinline__ void topk_group(const float* l, int E, int k, int sub, int32_t* ids,
+                                           float* w, int* hist) {
+  constexpr int lpt = LPT;
+  uint64_t K[L];
+  for (int base = 0; base < E; base += L * lpt) {
+    uint64_t B[L];
+#pragma unroll
+    for (int i = 0; i < L; i++) {
+      const int e = base + sub + lpt * i;
+      B[i] = e < E ? sel_key(l[e], e) : 0;
+    }
+    bitonic_sort_desc<L>(B);
+    if (base == 0) {
+#pragma unroll
+      for (int i = 0; i < L; i++) K[i] = B[i];
+    } else {
+      merge_top<L>(K, B);
+    }
+  }
+  butterfly<L, LPT, 1>(K);
+  const float mx = key_logit(K[0]);
+  float a[L];
+  float sum = 0.0f;
+#pragma unroll
+  for (int j = 0; j < L; j++) {
+    a[j] = j < k ? expf(key_logit(K[j]) - mx) : 0.0f;
+    sum += a[j];  // rank order; the terms past k are 0
+  }
+#pragma unroll
+  for (int j = 0; j < L; j++) {
+    if (j < k && (j & (lpt - 1)) == sub) {
+      const int e = key_expert(K[j]);
+      ids[j] = e;
+      w[j] = a[j] / sum;
+      if (hist) atomicAdd(&hist[e], 1);
+    }
+  }
+}
+
 // bf16 -> fp16 of tokens [t0, t0 + nt), each 8-element chunk reordered to
 // (0,4,1,5,2,6,3,7).  Loads use clamped indices so that each batch of U is
 // issued together.
@@ -225,8 +374,9 @@ __device__ void stage_rows(const RouteParams& p, int t0, int nt) {
   }
 }
 
-// Logits of tokens [t0, t0 + nt) into lg[nt][E].
-__device__ void load_logits(const RouteParams& p, int t0, int nt, float* lg) {
+// Logits of tokens [t0, t0 + nt) into lg[nt][stride] (rows padded so that
+// the lane groups of a wave read different LDS banks).
+__device__ void load_logits(const RouteParams& p, int t0, int nt, float* lg, int stride) {
   const int n = nt * p.E;
   const float* src = p.logits + (size_t)t0 * p.E;
   constexpr int U = 8;
@@ -237,36 +387,48 @@ __device__ void load_logits(const RouteParams& p, int t0, int nt, float* lg) {
 #pragma unroll
     for (int u = 0; u < U; u++) {
       const int i = i0 + u * kRouteThreads;
-      if (i < n) lg[i] = v[u];
+      if (i < n) {
+        const int r = i / p.E;
+        lg[r * stride + (i - r * p.E)] = v[u];
+      }
     }
   }
 }
 
-template <bool FULL, int NK>
+// One chunk of tokens, in passes of kRouteThreads / LPT tokens (one group of
+// LPT lanes per token).  LPT = 64: radix select by a wave, A = ceil(E / 64)
+// keys per lane; LPT = 8 or 16: sort-merge top-k, A = L, the list length.
+template <bool FULL, int A, int LPT>
 __device__ __forceinline__ void route_chunk(const RouteParams& p, int chunk) {
-  __shared__ float lg[kSub * 256];
+  __shared__ float lg[kLgFloats];
   __shared__ int hist[256];
-  const int tid = threadIdx.x, wave = tid >> 6;
-  constexpr int kWaves = kRouteThreads / 64;
+  const int tid = threadIdx.x;
+  constexpr int tp = kRouteThreads / LPT;
+  const int stride = p.E + LPT;
+  const int grp = tid / LPT, sub = tid % LPT;
   if (FULL && tid < 256) hist[tid] = 0;
   const int c0 = chunk * p.chunk_tokens;
   const int c1 = min(p.T, c0 + p.chunk_tokens);
-  for (int t0 = c0; t0 < c1; t0 += kSub) {
-    const int nt = min(kSub, c1 - t0);
-    load_logits(p, t0, nt, lg);
+  for (int t0 = c0; t0 < c1; t0 += tp) {
+    const int nt = min(tp, c1 - t0);
+    load_logits(p, t0, nt, lg, stride);
     if (FULL) stage_rows(p, t0, nt);
     __syncthreads();
-    for (int r = wave; r < nt; r += kWaves)
-      topk_token<NK>(lg + r * p.E, p.E, p.k, p.ids + (size_t)(t0 + r) * p.k,
-                     p.w + (size_t)(t0 + r) * p.k, FULL ? hist : nullptr);
+    if (grp < nt)
+    {
+      int32_t* ids = p.ids + (size_t)(t0 + grp) * p.k;
+      float* w = p.w + (size_t)(t0 + grp) * p.k;
+      if constexpr (LPT == 64) topk_token<A>(lg + grp * stride, p.E, p.k, ids, w, FULL ? hist : nullptr);
+      else topk_group<A, LPT>(lg + grp * stride, p.E, p.k, sub, ids, w, FULL ? hist : nullptr);
+    }
     __syncthreads();
   }
   if (FULL && tid < p.E) p.chunk_hist[(size_t)chunk * p.E + tid] = hist[tid];
 }
 
-template <bool FULL, int NK>
+template <bool FULL, int A, int LPT>
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(const RouteParams p) {
-  route_chunk<FULL, NK>(p, blockIdx.x);
+  route_chunk<FULL, A, LPT>(p, blockIdx.x);
 }
 
 // Outputs of S2-S5 for the fused single-chunk kernel.
@@ -282,23 +444,43 @@ struct BuildParams {
 template <int NK>
 __global__ __launch_bounds__(kRouteThreads) void route_build_kernel(const RouteParams p,
                                                                     const BuildParams b) {
-  route_chunk<true, NK>(p, 0);
+  route_chunk<true, NK, 64>(p, 0);  // at most 8 tokens: a wave each
   __threadfence_block();
   __syncthreads();
   scan_scatter_chunk(p.ids, p.T * p.k, p.E, p.chunk_tokens * p.k, 1, p.chunk_hist, b.block_m,
                      b.counts, b.offsets, b.sorted_pairs, b.pair_slot, b.blocks, b.num_blocks, 0);
 }
 
+// List length L of the top-k: the power of two in {2, 4, 8, 16} at or above k.
+template <bool FULL, int L>
+void launch_route_group(const RouteParams& p, int nchunks, hipStream_t s) {
+  if (p.lpt_log2 == 3) route_kernel<FULL, L, 8><<<nchunks, kRouteThreads, 0, s>>>(p);
+  else route_kernel<FULL, L, 16><<<nchunks, kRouteThreads, 0, s>>>(p);
+}
+
 template <bool FULL>
-hipError_t launch_nk(const RouteParams& p, int nchunks, hipStream_t s) {
-  switch ((p.E + 63) / 64) {
-    case 1: route_kernel<FULL, 1><<<nchunks, kRouteThreads, 0, s>>>(p); break;
-    case 2: route_kernel<FULL, 2><<<nchunks, kRouteThreads, 0, s>>>(p); break;
-    case 3: route_kernel<FULL, 3><<<nchunks, kRouteThreads, 0, s>>>(p); break;
-    case 4: route_kernel<FULL, 4><<<nchunks, kRouteThreads, 0, s>>>(p); break;
-    default: return hipErrorInvalidValue;
-  }
+hipError_t launch_route_l(const RouteParams& p, int nchunks, hipStream_t s) {
+  if (p.lpt_log2 == 6) {
+    switch ((p.E + 63) / 64) {
+      case 1: route_kernel<FULL, 1, 64><<<nchunks, kRouteThreads, 0, s>>>(p); break;
+      case 2: route_kernel<FULL, 2, 64><<<nchunks, kRouteThreads, 0, s>>>(p); break;
+      case 3: route_kernel<FULL, 3, 64><<<nchunks, kRouteThreads, 0, s>>>(p); break;
+      default: route_kernel<FULL, 4, 64><<<nchunks, kRouteThreads, 0, s>>>(p); break;
+    }
+  } else if (p.k <= 2) launch_route_group<FULL, 2>(p, nchunks, s);
+  else if (p.k <= 4) launch_route_group<FULL, 4>(p, nchunks, s);
+  else if (p.k <= 8) launch_route_group<FULL, 8>(p, nchunks, s);
+  else launch_route_group<FULL, 16>(p, nchunks, s);
   return hipGetLastError();
+}
+
+// Lanes per token (log2): a wave per token (radix select) for chunks of at
+// most 8 tokens; 16 lanes for chunks of up to 32 tokens; otherwise 8
+// (passes of 64 tokens) when their logits fit the LDS rows.
+int route_lpt_log2(int chunk_tokens, int E) {
+  if (chunk_tokens <= 8) return 6;
+  if (chunk_tokens <= 32 || (kRouteThreads / 8) * (E + 8) > kLgFloats) return 4;
+  return 3;
 }
 
 }  // namespace
@@ -324,9 +506,10 @@ hipError_t launch_route(const uint16_t* x, const uint16_t* wr, float* logits, in
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  RouteParams p{x, logits, ids, w, xh, chunk_hist, T, H, E, k, route_chunk_tokens(T)};
+  const int ct = route_chunk_tokens(T);
+  RouteParams p{x, logits, ids, w, xh, chunk_hist, T, H, E, k, ct, route_lpt_log2(ct, E)};
   const int n = route_chunks(T);
-  return xh ? launch_nk<true>(p, n, s) : launch_nk<false>(p, n, s);
+  return xh ? launch_route_l<true>(p, n, s) : launch_route_l<false>(p, n, s);
 }
 
 bool route_build_fused(int64_t T) { return route_chunks(T) == 1; }
@@ -343,14 +526,14 @@ hipError_t launch_route_build(const uint16_t* x, const uint16_t* wr, float* logi
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  RouteParams p{x, logits, ids, w, xh, chunk_hist, T, H, E, k, route_chunk_tokens(T)};
+  const int ct = route_chunk_tokens(T);
+  RouteParams p{x, logits, ids, w, xh, chunk_hist, T, H, E, k, ct, route_lpt_log2(ct, E)};
   BuildParams b{block_m, counts, offsets, sorted_pairs, pair_slot, blocks, num_blocks};
   switch ((E + 63) / 64) {
     case 1: route_build_kernel<1><<<1, kRouteThreads, 0, s>>>(p, b); break;
     case 2: route_build_kernel<2><<<1, kRouteThreads, 0, s>>>(p, b); break;
     case 3: route_build_kernel<3><<<1, kRouteThreads, 0, s>>>(p, b); break;
-    case 4: route_build_kernel<4><<<1, kRouteThreads, 0, s>>>(p, b); break;
-    default: return hipErrorInvalidValue;
+    default: route_build_kernel<4><<<1, kRouteThreads, 0, s>>>(p, b); break;
   }
   return hipGetLastError();
 }

@@ -97,10 +97,14 @@ def test_route_hand_cases():
         assert np.all(np.abs(cpu(w) - exp_w) <= 4 * f32_ulp(exp_w)), case["note"]
 
 
+# T = 257, 6000 and 20000 give routing chunks of 8, 24 and 80 tokens: the
+# top-k runs with 64, 16 and 8 lanes per token (20000: a full pass of 64
+# tokens and a partial one).
+@pytest.mark.parametrize("T", [257, 6000, 20000])
 @pytest.mark.parametrize("E,k", [(8, 2), (128, 8), (256, 16), (16, 16), (5, 1), (200, 3)])
-def test_route_ties_and_inf(orc, E, k):
-    g = torch.Generator().manual_seed(E * 31 + k)
-    l = torch.randn((257, E), generator=g)
+def test_route_ties_and_inf(orc, E, k, T):
+    g = torch.Generator().manual_seed(E * 31 + k + T)
+    l = torch.randn((T, E), generator=g)
     l[::2, : E // 2] = torch.round(l[::2, : E // 2])          # many exact ties
     l[1::3] = 0.25                                           # whole rows equal
     if E > k + 4:
