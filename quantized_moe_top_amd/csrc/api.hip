@@ -80,8 +80,9 @@ size_t gemm_workspace(int mode, int64_t T, int64_t K) {
 
 // Workspace layout of moe_ffn_forward.
 struct FfnLayout {
-  size_t logits, ids, w, counts, offsets, sorted_pairs, pair_slot, blocks, num_blocks,
-      scratch, xh, h, y_sorted, total;
+  size_t logits, logits_part, ids, w, counts, offsets, sorted_pairs, pair_slot, blocks,
+      num_blocks, scratch, xh, h, y_sorted, total;
+  int router_ks;  // ranges of H the router sums separately (1: no partial sums)
 };
 
 FfnLayout ffn_layout(const moe_dims& d, bool has_router, int block_m) {
@@ -94,6 +95,8 @@ FfnLayout ffn_layout(const moe_dims& d, bool has_router, int block_m) {
     return at;
   };
   L.logits = take(has_router ? T * E * 4 : 0);
+  L.router_ks = has_router ? moe::router_ksplit(d.T, d.H, d.E) : 1;
+  L.logits_part = take(L.router_ks > 1 ? (size_t)L.router_ks * T * E * 4 : 0);
   L.ids = take(P * 4);
   L.w = take(P * 4);
   L.counts = take(E * 4);
@@ -156,7 +159,7 @@ int moe_route(const uint16_t* x, const uint16_t* router_weight, float* logits, i
     if (!aligned16(x) || !aligned16(router_weight)) return fail(MOE_ERR_ALIGN, "x or router_weight not 16-byte aligned");
   }
   return hip_status(moe::launch_route(x, router_weight, logits, T, H, E, top_k, topk_ids,
-                                      topk_weights, nullptr, nullptr, (hipStream_t)stream),
+                                      topk_weights, nullptr, nullptr, nullptr, (hipStream_t)stream),
                     "route");
 }
 
@@ -326,17 +329,18 @@ int ffn_forward_impl(const moe_layer* layer, const uint16_t* x, const float* rou
 
   hipError_t err;
   int32_t* chunk_hist = (int32_t*)(ws + L.scratch);
+  float* part = L.router_ks > 1 ? (float*)(ws + L.logits_part) : nullptr;  // router partial sums
   if ((err = mark(events, MOE_STAGE_ROUTE, s)) != hipSuccess) return hip_status(err, "event");
   if (moe::route_build_fused(d.T)) {
     // one routing chunk: S1-S5 in one launch (the build stage is empty)
     if ((err = moe::launch_route_build(x, layer->router_weight, logits, d.T, d.H, d.E, d.top_k, ids,
                                        w, xh, chunk_hist, block_m, counts, offsets, sorted_pairs,
-                                       pair_slot, blocks, num_blocks, s)) != hipSuccess)
+                                       pair_slot, blocks, num_blocks, part, s)) != hipSuccess)
       return hip_status(err, "route_build");
     if ((err = mark(events, MOE_STAGE_BUILD_BLOCKS, s)) != hipSuccess) return hip_status(err, "event");
   } else {
     if ((err = moe::launch_route(x, layer->router_weight, logits, d.T, d.H, d.E, d.top_k, ids, w, xh,
-                                 chunk_hist, s)) != hipSuccess)
+                                 chunk_hist, part, s)) != hipSuccess)
       return hip_status(err, "route");
     if ((err = mark(events, MOE_STAGE_BUILD_BLOCKS, s)) != hipSuccess) return hip_status(err, "event");
     if ((err = moe::launch_scan_scatter(ids, d.T, d.top_k, d.E, chunk_hist, block_m, counts, offsets,

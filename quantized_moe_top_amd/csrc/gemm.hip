@@ -56,33 +56,6 @@ struct MfmaParams {
   int N, K, log2_G, top_k, E, P, max_blocks;
 };
 
-// global_load_lds_dwordx4 / _dword: each lane's 16 (4) bytes at g land in
-// LDS at l + 16 (4) * lane; l must be the same for the whole wave.
-__device__ __forceinline__ void lds_load16(const void* g, char* l) {
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)l, 16, 0, 0);
-}
-__device__ __forceinline__ void lds_load4(const void* g, char* l) {
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)l, 4, 0, 0);
-}
-
-// s_waitcnt vmcnt(n) (expcnt and lgkmcnt not waited on), then a workgroup
-// barrier.  The asm is a compiler memory barrier, so no LDS access moves
-// across it; no fence is used because a fence would also wait for the
-// loads still in flight for later slabs.
-// s_waitcnt vmcnt(n) alone (expcnt and lgkmcnt not waited on).
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vm_barrier() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-  asm volatile("s_barrier" ::: "memory");
-}
-
 // WAVES waves per workgroup (4 or 8): the tile covers 64 * WAVES weight
 // columns.  With 4 waves two workgroups fit a CU (LDS <= 80 KiB) for tiles of
 // up to 64 rows (and for 128-row S6 tiles), so one workgroup's prologue and

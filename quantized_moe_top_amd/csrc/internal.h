@@ -90,6 +90,51 @@ __device__ __forceinline__ uint4 bf16x8_to_half_interleaved(uint4 v) {
                     __builtin_bit_cast(uint32_t, o2), __builtin_bit_cast(uint32_t, o3));
 }
 
+// global_load_lds_dwordx4 / _dword: each lane's 16 (4) bytes at g land in
+// LDS at l + 16 (4) * lane; l must be the same for the whole wave.
+__device__ __forceinline__ void lds_load16(const void* g, char* l) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)l, 16, 0, 0);
+}
+__device__ __forceinline__ void lds_load4(const void* g, char* l) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)l, 4, 0, 0);
+}
+
+// s_waitcnt vmcnt(n) alone (expcnt and lgkmcnt not waited on).  Loads
+// complete in issue order, so after it every load but the last n issued by
+// this wave is done (stores only add to the count, making it conservative).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// s_waitcnt vmcnt(n), then a workgroup barrier.  The asm is a compiler
+// memory barrier, so no LDS access moves across it; no fence is used because
+// a fence would also wait for the loads still in flight for later slabs.
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+  asm volatile("s_barrier" ::: "memory");
+}
+
+// 16-byte LDS read hidden from the compiler's memory model.  Reading a ring
+// that LDS-DMA copies are still filling, the compiler cannot tell the stages
+// apart and would wait for every copy in flight first; the ring's own
+// count-based wait already orders the read.  The value may be used only
+// after lds_wait on it.
+__device__ __forceinline__ u32x4 lds_read16(const void* p) {
+  u32x4 v;
+  const uint32_t off = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+  asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(off));
+  return v;
+}
+// Waits for every LDS read of this wave; the values passed become usable.
+__device__ __forceinline__ void lds_wait(u32x4& a) { asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a)); }
+__device__ __forceinline__ void lds_wait(u32x4& a, u32x4& b) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b));
+}
+
 // silu(g) * u = g / (1 + e^-g) * u, with the hardware exponential and
 // reciprocal (about 1 ulp each; the result is then rounded to fp16).
 __device__ __forceinline__ float silu_mul(float g, float u) {
@@ -104,11 +149,15 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
 int route_chunk_tokens(int64_t T);
 int route_chunks(int64_t T);
 
+// Ranges of H the router GEMM splits into when given room for partial sums
+// (part: router_ksplit * T * E floats; 1 = no split, part unused).
+int router_ksplit(int64_t T, int64_t H, int64_t E);
 // S0 (when wr) + S1 over all T tokens; with xh and chunk_hist (both or
 // neither) also the per-chunk expert histogram and the fp16 staging of x.
+// part (or nullptr): scratch for the router's partial sums.
 hipError_t launch_route(const uint16_t* x, const uint16_t* wr, float* logits, int T, int H, int E,
                         int k, int32_t* ids, float* w, half_t* xh, int32_t* chunk_hist,
-                        hipStream_t s);
+                        float* part, hipStream_t s);
 // T small enough for one routing chunk: S1 and S2-S5 in one launch (after the
 // router GEMM when wr is given); same outputs as launch_route followed by
 // launch_scan_scatter.
@@ -117,7 +166,7 @@ hipError_t launch_route_build(const uint16_t* x, const uint16_t* wr, float* logi
                               int E, int k, int32_t* ids, float* w, half_t* xh,
                               int32_t* chunk_hist, int block_m, int32_t* counts, int32_t* offsets,
                               int32_t* sorted_pairs, int32_t* pair_slot, int32_t* blocks,
-                              int32_t* num_blocks, hipStream_t s);
+                              int32_t* num_blocks, float* part, hipStream_t s);
 // Per-chunk expert histogram of caller-given ids [T][k].
 hipError_t launch_chunk_hist(const int32_t* ids, int T, int k, int E, int32_t* chunk_hist,
                              hipStream_t s);

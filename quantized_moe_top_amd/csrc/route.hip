@@ -4,11 +4,10 @@
 // Lily engine beats MLX by 35% on M5 Max", architecture paragraph: expert
 // routing runs on the GPU in the same submission as the rest of the layer.
 //
-// S0 (only when a router weight is given) is its own kernel: one
-// workgroup per 32-token x 32-expert tile of the logits, on
-// v_mfma_f32_32x32x16_bf16, with the H sums split over the workgroup's 8
-// waves and added in a fixed order, so that a few hundred tokens already
-// fill the chip and the logits are deterministic.
+// S0 (only when a router weight is given) is its own kernel (router_kernel):
+// LDS-staged bf16 MFMA tiles whose shape follows T, deterministic sums, and
+// the fp16 operand copy of x written from the staged slabs, so the routing
+// kernel then skips it.
 //
 // The routing kernel: one workgroup (8 waves) owns a chunk of consecutive
 // tokens and walks it in passes of 8, 32 or 64 tokens (64, 16 or 8 lanes
@@ -30,76 +29,247 @@ namespace {
 
 constexpr int kLgFloats = 16384;  // LDS logits of one pass (64 KiB)
 constexpr int kRouteThreads = 512;
-constexpr int kRouterBatch = 16;  // MFMA steps whose loads are issued together
 
 // ------------------------------------------------------------------ S0 ---
-// logits[t][e] = sum_h x[t][h] * wr[e][h] for one 32-token x 32-expert tile
-// per workgroup.  The 8 waves split the H sums into 8 contiguous ranges,
-// each wave issuing the loads of its whole range at once (H <= 4096: one
-// round trip); their 32x32 partial tiles are added in wave order through
-// LDS, so the result does not depend on timing.  One-dimensional grid of
-// ceil(T/32) * ceil(E/32) workgroups, expert tile fastest: the expert tiles
-// of one token tile are dispatched together, so x is read from HBM once and
-// shared through L2.
-constexpr int kRouterWaves = 8;
-__global__ __launch_bounds__(64 * kRouterWaves) void router_gemm_kernel(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, float* __restrict__ logits,
-    int T, int H, int E) {
-  __shared__ float red[kRouterWaves][32 * 33];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int r = lane & 31, half = lane >> 5;
-  const int ne = (E + 31) / 32;
-  const int t0 = (blockIdx.x / ne) * 32, e0 = (blockIdx.x % ne) * 32;
-  const int t = min(t0 + r, T - 1);  // rows past T or E read a valid row, never stored
-  const int e = min(e0 + r, E - 1);
-  const int steps = H / 16 / kRouterWaves;  // H % 128 == 0
-  const uint4* xa = reinterpret_cast<const uint4*>(x + (size_t)t * H) + half + 2 * wave * steps;
-  const uint4* wb = reinterpret_cast<const uint4*>(wr + (size_t)e * H) + half + 2 * wave * steps;
-  floatx16_t acc = {};
-  int s = 0;
-  for (; s + kRouterBatch <= steps; s += kRouterBatch) {
-    uint4 av[kRouterBatch], bv[kRouterBatch];
+// logits[t][e] = sum_h x[t][h] * wr[e][h], fp32 accumulation of the bf16
+// products on v_mfma_f32_32x32x16_bf16, and (optionally) the fp16 operand
+// copy of x.  A workgroup of 4 waves owns TMB x TEB blocks of 32 tokens x 32
+// experts over the whole of H, in slabs of 64.  Per slab its x rows and
+// router rows reach LDS by global_load_lds_dwordx4 through a ring of R
+// stages (R - 1 slabs in flight, R = 4..16: as deep as 128 KiB of LDS
+// allows, since with few workgroups per CU the copies are latency-bound);
+// each wave instruction moves 8 rows x 128
+// contiguous bytes, the 16-byte chunk c of row r landing at position
+// c ^ (r % 8), so the loads are coalesced and the fragment reads free of
+// bank conflicts.  With one block the 4 waves take one 16-wide k step of
+// every slab each and add their partial tiles in wave order at the end
+// (deterministic); with 4 or more blocks each wave owns blocks that share
+// its x rows.  The workgroups of expert tile 0 also convert every staged x
+// slab to fp16 in operand order for the grouped GEMM, so x is read from
+// HBM once.
+// s_waitcnt vmcnt(BASE + n X), then a workgroup barrier, for a runtime n in
+// [0, K].
+template <int BASE, int X, int K>
+__device__ __forceinline__ void wait_vm_barrier_n(int n) {
+  if constexpr (K == 0) {
+    wait_vm_barrier<BASE>();
+  } else {
+    if (n >= K) wait_vm_barrier<BASE + K * X>();
+    else wait_vm_barrier_n<BASE, X, K - 1>(n);
+  }
+}
+
+struct RouterParams {
+  const uint16_t* x;   // bf16 [T][H]
+  const uint16_t* wr;  // bf16 [E][H]
+  float* logits;       // fp32 [ksplit][T][E]: the logits, or partial sums over H / ksplit
+  half_t* xh;          // fp16 [T][H] operand copy, or nullptr
+  int T, H, E, n_et;   // n_et: expert tiles
+  int ksplit;          // H ranges (the grid is token tiles x n_et x ksplit)
+};
+
+template <int TMB, int TEB, int R>
+__global__ __launch_bounds__(256) void router_kernel(const RouterParams p) {
+  constexpr int NBLK = TMB * TEB;
+  static_assert(NBLK == 1 || ((TMB == 2 || TMB == 4) && (TEB == 2 || TEB == 4)), "block split");
+  constexpr bool KSPLIT = NBLK == 1;            // 4 waves share one block
+  // otherwise wave (wm, we) = (w % 2, w / 2) owns block rows MW wm .. and
+  // block columns EW we .. (a 2 x 2 grid of waves over the tile)
+  constexpr int MW = KSPLIT ? 1 : TMB / 2, EW = KSPLIT ? 1 : TEB / 2;
+  constexpr int NBW = MW * EW;                  // blocks per wave
+  constexpr int RX = 32 * TMB, RW = 32 * TEB;   // x rows, router rows per stage
+  constexpr int STAGE = (RX + RW) * 128;        // bytes per slab
+  constexpr int D = (RX + RW) / 32;             // load instructions per wave and slab
+  constexpr int X = TMB;                        // operand-copy stores per thread and slab
+  static_assert(R >= 3 && (R - 1) * (D + X) < 64, "ring depth within the vmcnt range");
+  __shared__ __attribute__((aligned(16))) char ring[R * STAGE];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kz = blockIdx.x % p.ksplit, tile = blockIdx.x / p.ksplit;
+  const int tt = tile / p.n_et, et = tile % p.n_et;
+  const int t0 = tt * RX, e0 = et * RW;
+  const int S = p.H / 64 / p.ksplit, s0 = kz * S;  // this workgroup's slabs s0 .. s0 + S - 1
+  float* const out = p.logits + (size_t)kz * p.T * p.E;
+  const bool stage_x = p.xh != nullptr && et == 0;  // uniform over the workgroup
+
+  // Load instruction q of this wave moves 8-row group g = wave + 4 q of the
+  // stage (x rows first, then router rows; rows past T or E repeat the last
+  // valid row and are never stored); lane l moves chunk (l % 8) ^ (l / 8) of
+  // row 8 g + l / 8, which lands at position l % 8 of that row.
+  const int cl = (lane & 7) ^ (lane >> 3);
+  const uint16_t* src[D];
 #pragma unroll
-    for (int u = 0; u < kRouterBatch; u++) {
-      av[u] = xa[2 * (s + u)];
-      bv[u] = wb[2 * (s + u)];
+  for (int q = 0; q < D; q++) {
+    const int r = 8 * (wave + 4 * q) + (lane >> 3);
+    src[q] = r < RX ? p.x + (size_t)min(t0 + r, p.T - 1) * p.H + 8 * cl
+                    : p.wr + (size_t)min(e0 + r - RX, p.E - 1) * p.H + 8 * cl;
+  }
+  auto issue = [&](int s, int st) {
+    char* base = ring + st * STAGE;
+#pragma unroll
+    for (int q = 0; q < D; q++) lds_load16(src[q] + 64 * (s0 + s), base + (wave + 4 * q) * 1024);
+  };
+  // MFMA fragment of the 32 rows from row0 of a stage, k step j of the slab:
+  // lane (i, half) holds row row0 + i, elements 16 j + 8 half .. + 7 (usable
+  // after lds_wait)
+  auto frag = [&](const char* base, int row0, int j) {
+    const int r = row0 + (lane & 31), c = 2 * j + (lane >> 5);
+    return lds_read16(base + r * 128 + 16 * (c ^ (r & 7)));
+  };
+  auto mfma = [](u32x4 a, u32x4 b, floatx16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  };
+
+  floatx16_t acc[NBW];
+#pragma unroll
+  for (int b = 0; b < NBW; b++) acc[b] = floatx16_t{};
+#pragma unroll
+  for (int j = 0; j < R - 1; j++) issue(min(j, S - 1), j);
+  for (int s = 0; s < S; s++) {
+    // Slab s has landed once at most the loads (and copy stores) issued after
+    // it are outstanding: every load and store completes in issue order.
+    // Issued after slab s's loads: the loads of slabs s + 1 .. s + R - 2 and
+    // the copy stores of the min(s, R - 1) slabs before s.
+    wait_vm_barrier_n<(R - 2) * D, X, R - 1>(stage_x ? min(s, R - 1) : 0);
+    issue(min(s + R - 1, S - 1), (s + R - 1) % R);
+    const char* base = ring + (s % R) * STAGE;
+    if constexpr (KSPLIT) {
+      u32x4 a = frag(base, 0, wave), b = frag(base, RX, wave);
+      lds_wait(a, b);
+      acc[0] = mfma(a, b, acc[0]);
+    } else {
+      // every fragment of the slab first, one wait, then the MFMAs
+      u32x4 a[4][MW], b[4][EW];
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+#pragma unroll
+        for (int m = 0; m < MW; m++) a[j][m] = frag(base, 32 * (MW * (wave & 1) + m), j);
+#pragma unroll
+        for (int e = 0; e < EW; e++) b[j][e] = frag(base, RX + 32 * (EW * (wave >> 1) + e), j);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+#pragma unroll
+        for (int m = 0; m < MW; m++) lds_wait(a[j][m]);
+#pragma unroll
+        for (int e = 0; e < EW; e++) lds_wait(b[j][e]);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; j++)
+#pragma unroll
+        for (int m = 0; m < MW; m++)
+#pragma unroll
+          for (int e = 0; e < EW; e++) acc[m * EW + e] = mfma(a[j][m], b[j][e], acc[m * EW + e]);
     }
-    // keep every load of the batch ahead of the first MFMA (one round trip),
-    // instead of the compiler's rolling schedule with a few loads in flight
-    __builtin_amdgcn_sched_barrier(0);
+    if (stage_x) {
+      // exactly X stores per thread, so the wait count above is exact; rows
+      // past T hold row T - 1 (clamped load) and rewrite its identical bytes
+      u32x4 d[X];
 #pragma unroll
-    for (int u = 0; u < kRouterBatch; u++)
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av[u]),
-                                                    __builtin_bit_cast(bf16x8_t, bv[u]), acc, 0, 0,
-                                                    0);
+      for (int i = 0; i < X; i++) {
+        const int r = (tid + 256 * i) >> 3, c = tid & 7;
+        d[i] = lds_read16(base + r * 128 + 16 * (c ^ (r & 7)));
+      }
+#pragma unroll
+      for (int i = 0; i < X; i++) lds_wait(d[i]);
+#pragma unroll
+      for (int i = 0; i < X; i++) {
+        const int r = (tid + 256 * i) >> 3, c = tid & 7;
+        *reinterpret_cast<uint4*>(p.xh + (size_t)min(t0 + r, p.T - 1) * p.H + 64 * (s0 + s) + 8 * c) =
+            bf16x8_to_half_interleaved(make_uint4(d[i][0], d[i][1], d[i][2], d[i][3]));
+      }
+    }
   }
-  for (; s < steps; s++)
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, xa[2 * s]),
-                                                  __builtin_bit_cast(bf16x8_t, wb[2 * s]), acc, 0, 0,
-                                                  0);
+  wait_vm<0>();  // the ring's last (repeated) loads drain before the end
+
+  // accumulator register i of lane (col, half) is row 8 (i / 4) + 4 half + i % 4
+  const int col = lane & 31, half = lane >> 5;
+  if constexpr (KSPLIT) {
+    static_assert(R * STAGE >= 4 * 32 * 33 * 4, "the wave partials reuse the ring");
+    float* red = reinterpret_cast<float*>(ring);
+    __syncthreads();  // every wave is done with the ring
 #pragma unroll
-  for (int i = 0; i < 16; i++) red[wave][(8 * (i >> 2) + 4 * half + (i & 3)) * 33 + r] = acc[i];
-  __syncthreads();
-  // thread -> (row, col) of the tile, two elements each
-  for (int idx = threadIdx.x; idx < 32 * 32; idx += 64 * kRouterWaves) {
-    const int row = idx >> 5, col = idx & 31;
-    float v = red[0][row * 33 + col];
+    for (int i = 0; i < 16; i++) red[wave * 32 * 33 + (8 * (i >> 2) + 4 * half + (i & 3)) * 33 + col] = acc[0][i];
+    __syncthreads();
+    for (int idx = tid; idx < 32 * 32; idx += 256) {
+      const int row = idx >> 5, c2 = idx & 31;
+      float v = red[row * 33 + c2];
 #pragma unroll
-    for (int w = 1; w < kRouterWaves; w++) v += red[w][row * 33 + col];
-    if (t0 + row < T && e0 + col < E) logits[(size_t)(t0 + row) * E + e0 + col] = v;
+      for (int w = 1; w < 4; w++) v += red[w * 32 * 33 + row * 33 + c2];
+      if (t0 + row < p.T && e0 + c2 < p.E) out[(size_t)(t0 + row) * p.E + e0 + c2] = v;
+    }
+  } else {
+#pragma unroll
+    for (int m = 0; m < MW; m++)
+#pragma unroll
+      for (int e2 = 0; e2 < EW; e2++) {
+        const int e = e0 + 32 * (EW * (wave >> 1) + e2) + col;
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+          const int t = t0 + 32 * (MW * (wave & 1) + m) + 8 * (i >> 2) + 4 * half + (i & 3);
+          if (t < p.T && e < p.E) out[(size_t)t * p.E + e] = acc[m * EW + e2][i];
+        }
+      }
   }
+}
+
+constexpr int kMaxSplit = 8;  // ranges of H the router may sum separately
+
+struct RouterPlan {
+  int tm, te, ksplit;
+};
+
+// Tile shape: the candidate whose busiest CU moves the fewest bytes
+// (rounds of 256 workgroups x bytes per workgroup), more workgroups on ties.
+// With the smallest tile and partial sums allowed, H is also split into up
+// to 8 ranges while that keeps the grid within two rounds of the chip.
+RouterPlan router_plan(int64_t T, int64_t H, int64_t E, bool split) {
+  const int cand[4][2] = {{1, 1}, {2, 2}, {2, 4}, {4, 4}};
+  int best = 0;
+  int64_t best_cost = -1, best_wg = 0;
+  for (int c = 0; c < 4; c++) {
+    const int64_t wg = ((T + 32 * cand[c][0] - 1) / (32 * cand[c][0])) *
+                       ((E + 32 * cand[c][1] - 1) / (32 * cand[c][1]));
+    const int64_t cost = ((wg + 255) / 256) * (int64_t)(cand[c][0] + cand[c][1]);
+    if (best_cost < 0 || cost < best_cost || (cost == best_cost && wg > best_wg)) {
+      best = c;
+      best_cost = cost;
+      best_wg = wg;
+    }
+  }
+  int ks = 1;
+  if (split && best == 0)
+    while (ks < kMaxSplit && best_wg * ks * 2 <= 512 && (H / 64) % (2 * ks) == 0) ks *= 2;
+  return RouterPlan{cand[best][0], cand[best][1], ks};
+}
+
+hipError_t launch_router(const uint16_t* x, const uint16_t* wr, float* logits, half_t* xh, int T,
+                         int H, int E, int ksplit, hipStream_t s) {
+  const RouterPlan pl = router_plan(T, H, E, ksplit > 1);
+  if (pl.ksplit != ksplit) return hipErrorInvalidValue;  // the caller sized its buffer for ksplit
+  RouterParams p{x, wr, logits, xh, T, H, E, (E + 32 * pl.te - 1) / (32 * pl.te), ksplit};
+  const int64_t grid = (int64_t)((T + 32 * pl.tm - 1) / (32 * pl.tm)) * p.n_et * ksplit;
+  if (pl.tm == 1) router_kernel<1, 1, 9><<<grid, 256, 0, s>>>(p);  // ring depths: <= 128 KiB
+  else if (pl.te == 2) router_kernel<2, 2, 8><<<grid, 256, 0, s>>>(p);
+  else if (pl.tm == 2) router_kernel<2, 4, 5><<<grid, 256, 0, s>>>(p);
+  else router_kernel<4, 4, 4><<<grid, 256, 0, s>>>(p);
+  return hipGetLastError();
 }
 
 // -------------------------------------------------------------- S1, S2 ---
 struct RouteParams {
   const uint16_t* x;    // bf16 [T][H] (staging)
-  const float* logits;  // fp32 [T][E]
+  const float* logits;  // fp32 [ksplit][T][E]: logits, or partial sums added here
+  float* logits_out;    // fp32 [T][E]: the summed logits (ksplit > 1)
+  int ksplit;
   int32_t* ids;         // [T][k]
   float* w;             // [T][k]
   half_t* xh;           // fp16 [T][H] staged activations (whole-layer mode)
   int32_t* chunk_hist;  // [nchunks][E] (whole-layer mode)
   int T, H, E, k, chunk_tokens;
   int lpt_log2;         // lanes per token in the top-k (log2)
+  bool stage_x;         // write xh here (false when the router kernel did)
 };
 
 // Order-preserving map of an fp32 bit pattern onto unsigned integers
@@ -375,21 +545,35 @@ __device__ void stage_rows(const RouteParams& p, int t0, int nt) {
 }
 
 // Logits of tokens [t0, t0 + nt) into lg[nt][stride] (rows padded so that
-// the lane groups of a wave read different LDS banks).
+// the lane groups of a wave read different LDS banks).  With partial sums
+// over ranges of H, they are added in range order (deterministic) and the
+// sums also written to logits_out.
 __device__ void load_logits(const RouteParams& p, int t0, int nt, float* lg, int stride) {
   const int n = nt * p.E;
+  const size_t part = (size_t)p.T * p.E;
   const float* src = p.logits + (size_t)t0 * p.E;
   constexpr int U = 8;
   for (int i0 = threadIdx.x; i0 < n; i0 += kRouteThreads * U) {
-    float v[U];
+    // every partial of the batch is loaded before the first add (one round
+    // trip); at most kMaxSplit ranges
+    float v[kMaxSplit][U];
 #pragma unroll
-    for (int u = 0; u < U; u++) v[u] = src[min(i0 + u * kRouteThreads, n - 1)];
+    for (int z = 0; z < kMaxSplit; z++)
+      if (z < p.ksplit)
+#pragma unroll
+        for (int u = 0; u < U; u++) v[z][u] = src[z * part + min(i0 + u * kRouteThreads, n - 1)];
+#pragma unroll
+    for (int z = 1; z < kMaxSplit; z++)
+      if (z < p.ksplit)
+#pragma unroll
+        for (int u = 0; u < U; u++) v[0][u] += v[z][u];
 #pragma unroll
     for (int u = 0; u < U; u++) {
       const int i = i0 + u * kRouteThreads;
       if (i < n) {
         const int r = i / p.E;
-        lg[r * stride + (i - r * p.E)] = v[u];
+        lg[r * stride + (i - r * p.E)] = v[0][u];
+        if (p.ksplit > 1) p.logits_out[(size_t)t0 * p.E + i] = v[0][u];
       }
     }
   }
@@ -412,7 +596,7 @@ __device__ __forceinline__ void route_chunk(const RouteParams& p, int chunk) {
   for (int t0 = c0; t0 < c1; t0 += tp) {
     const int nt = min(tp, c1 - t0);
     load_logits(p, t0, nt, lg, stride);
-    if (FULL) stage_rows(p, t0, nt);
+    if (FULL && p.stage_x) stage_rows(p, t0, nt);
     __syncthreads();
     if (grp < nt)
     {
@@ -496,18 +680,20 @@ int route_chunks(int64_t T) {
   return (int)((T + ct - 1) / ct);
 }
 
+int router_ksplit(int64_t T, int64_t H, int64_t E) { return router_plan(T, H, E, true).ksplit; }
+
 hipError_t launch_route(const uint16_t* x, const uint16_t* wr, float* logits, int T, int H, int E,
                         int k, int32_t* ids, float* w, half_t* xh, int32_t* chunk_hist,
-                        hipStream_t s) {
+                        float* part, hipStream_t s) {
   if (T <= 0) return hipSuccess;
+  const int ks = wr && part ? router_ksplit(T, H, E) : 1;
   if (wr) {
-    const int64_t grid = (int64_t)((E + 31) / 32) * ((T + 31) / 32);
-    router_gemm_kernel<<<grid, 64 * kRouterWaves, 0, s>>>(x, wr, logits, T, H, E);
-    const hipError_t err = hipGetLastError();
+    const hipError_t err = launch_router(x, wr, ks > 1 ? part : logits, xh, T, H, E, ks, s);
     if (err != hipSuccess) return err;
   }
   const int ct = route_chunk_tokens(T);
-  RouteParams p{x, logits, ids, w, xh, chunk_hist, T, H, E, k, ct, route_lpt_log2(ct, E)};
+  RouteParams p{x, ks > 1 ? part : logits, logits, ks, ids, w, xh, chunk_hist, T, H, E, k, ct,
+                route_lpt_log2(ct, E), wr == nullptr};
   const int n = route_chunks(T);
   return xh ? launch_route_l<true>(p, n, s) : launch_route_l<false>(p, n, s);
 }
@@ -518,16 +704,16 @@ hipError_t launch_route_build(const uint16_t* x, const uint16_t* wr, float* logi
                               int E, int k, int32_t* ids, float* w, half_t* xh,
                               int32_t* chunk_hist, int block_m, int32_t* counts, int32_t* offsets,
                               int32_t* sorted_pairs, int32_t* pair_slot, int32_t* blocks,
-                              int32_t* num_blocks, hipStream_t s) {
+                              int32_t* num_blocks, float* part, hipStream_t s) {
   if (T <= 0) return hipSuccess;
+  const int ks = wr && part ? router_ksplit(T, H, E) : 1;
   if (wr) {
-    const int64_t grid = (int64_t)((E + 31) / 32) * ((T + 31) / 32);
-    router_gemm_kernel<<<grid, 64 * kRouterWaves, 0, s>>>(x, wr, logits, T, H, E);
-    const hipError_t err = hipGetLastError();
+    const hipError_t err = launch_router(x, wr, ks > 1 ? part : logits, xh, T, H, E, ks, s);
     if (err != hipSuccess) return err;
   }
   const int ct = route_chunk_tokens(T);
-  RouteParams p{x, logits, ids, w, xh, chunk_hist, T, H, E, k, ct, route_lpt_log2(ct, E)};
+  RouteParams p{x, ks > 1 ? part : logits, logits, ks, ids, w, xh, chunk_hist, T, H, E, k, ct,
+                route_lpt_log2(ct, E), wr == nullptr};
   BuildParams b{block_m, counts, offsets, sorted_pairs, pair_slot, blocks, num_blocks};
   switch ((E + 63) / 64) {
     case 1: route_build_kernel<1><<<1, kRouteThreads, 0, s>>>(p, b); break;
