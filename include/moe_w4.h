@@ -224,7 +224,12 @@ typedef struct {
   const int32_t* blocks;        /* [max_blocks][3] */
   const int32_t* num_blocks;    /* [1] */
   const uint16_t* h;            /* fp16 [P][I], slot order, operand order */
-  const float* y_sorted;        /* fp32 [P][H], slot order, weighted */
+  const uint8_t* y_sorted;      /* [P][H] weighted, slot order, y_sorted_bytes
+                                   per value: 4 = fp32 (path 1); 3 = packed
+                                   24-bit (path 0): little-endian, the top 3
+                                   bytes of the fp32 pattern rounded to nearest
+                                   even (relative error <= 2^-16) */
+  int32_t y_sorted_bytes;
 } moe_route_info;
 
 /* Tile rows moe_ffn_forward uses for these sizes (host-only). */

@@ -224,6 +224,15 @@ def stage_events(n: int = _lib.MOE_NUM_STAGES + 1):
     return evs
 
 
+def unpack_y24(packed: torch.Tensor) -> torch.Tensor:
+    """fp32 values of a packed 24-bit tensor [..., 3 n] (the layer's weighted
+    expert outputs in ``info["y_sorted"]``): value i is bytes 3i .. 3i + 2,
+    little-endian, as the top 3 bytes of its fp32 pattern."""
+    b = packed.to(torch.int64).reshape(*packed.shape[:-1], -1, 3)
+    bits = (b[..., 0] << 8) | (b[..., 1] << 16) | (b[..., 2] << 24)
+    return bits.to(torch.int32).view(torch.float32)
+
+
 def ffn_forward(layer, x: Optional[torch.Tensor] = None, logits: Optional[torch.Tensor] = None,
                 y: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                 info: bool = False, stage_events=None):
@@ -287,7 +296,10 @@ def _info_views(ri: RouteInfo, ws: torch.Tensor, layer, T: int, logits) -> dict:
         blocks=view(ri.blocks, mb * 3, torch.int32, (mb, 3)),
         num_blocks=view(ri.num_blocks, 1, torch.int32, (1,)),
         h=view(ri.h, P * layer.I, torch.float16, (P, layer.I)),
-        y_sorted=view(ri.y_sorted, P * layer.H, torch.float32, (P, layer.H)),
+        # fp32, or packed 24-bit (3 bytes a value, unpack_y24 gives fp32)
+        y_sorted=(view(ri.y_sorted, P * layer.H, torch.float32, (P, layer.H))
+                  if ri.y_sorted_bytes == 4 else
+                  view(ri.y_sorted, P * layer.H * 3, torch.uint8, (P, layer.H * 3))),
     )
     out["logits"] = (view(ri.logits, T * layer.E, torch.float32, (T, layer.E))
                      if layer.router_weight is not None else logits)

@@ -108,7 +108,7 @@ FfnLayout ffn_layout(const moe_dims& d, bool has_router, int block_m) {
   L.scratch = take((size_t)moe::route_chunks(d.T) * E * 4);
   L.xh = take(T * H * 2);
   L.h = take(P * I * 2);
-  L.y_sorted = take(P * H * 4);
+  L.y_sorted = take(P * H * (d.T <= moe::kGemvMaxTokens ? 4 : 3));  // fp32 or packed 24-bit
   L.total = o;
   return L;
 }
@@ -292,7 +292,7 @@ int ffn_forward_impl(const moe_layer* layer, const uint16_t* x, const float* rou
   const int block_m = moe_ffn_block_m(&d);
   if (d.T == 0) {  // empty tensors may carry NULL data pointers
     if (info) *info = moe_route_info{block_m, 1, router_logits, nullptr, nullptr, nullptr, nullptr,
-                                     nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
+                                     nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 4};
     return ok();
   }
   if (has_router == (router_logits != nullptr))
@@ -320,11 +320,12 @@ int ffn_forward_impl(const moe_layer* layer, const uint16_t* x, const float* rou
   int32_t* num_blocks = (int32_t*)(ws + L.num_blocks);
   moe::half_t* xh = (moe::half_t*)(ws + L.xh);
   moe::half_t* h = (moe::half_t*)(ws + L.h);
-  float* y_sorted = (float*)(ws + L.y_sorted);
+  uint8_t* y_sorted = (uint8_t*)(ws + L.y_sorted);
   const bool gemv = d.T <= moe::kGemvMaxTokens;
   if (info) {
     *info = moe_route_info{block_m, gemv ? 1 : 0, logits, ids, w, counts, offsets, sorted_pairs,
-                           pair_slot, blocks, num_blocks, (const uint16_t*)h, y_sorted};
+                           pair_slot, blocks, num_blocks, (const uint16_t*)h, y_sorted,
+                           gemv ? 4 : 3};
   }
 
   hipError_t err;
@@ -350,7 +351,8 @@ int ffn_forward_impl(const moe_layer* layer, const uint16_t* x, const float* rou
   moe::GemmArgs g1{MOE_GEMM_GATE_UP_SWIGLU, d.T, d.top_k, d.E, d.I, d.H, d.group_size, block_m,
                    xh, layer->gate, layer->up, sorted_pairs, w, blocks, num_blocks, h};
   moe::GemmArgs g2{MOE_GEMM_DOWN, d.T, d.top_k, d.E, d.H, d.I, d.group_size, block_m,
-                   h, layer->down, layer->down, sorted_pairs, w, blocks, num_blocks, y_sorted};
+                   h, layer->down, layer->down, sorted_pairs, w, blocks, num_blocks, y_sorted,
+                   !gemv};
   if ((err = mark(events, MOE_STAGE_GATE_UP, s)) != hipSuccess) return hip_status(err, "event");
   err = gemv ? moe::launch_w4_gemv(g1, s) : moe::launch_w4_mfma(g1, s);
   if (err != hipSuccess) return hip_status(err, "gate_up");
@@ -358,7 +360,7 @@ int ffn_forward_impl(const moe_layer* layer, const uint16_t* x, const float* rou
   err = gemv ? moe::launch_w4_gemv(g2, s) : moe::launch_w4_mfma(g2, s);
   if (err != hipSuccess) return hip_status(err, "down");
   if ((err = mark(events, MOE_STAGE_COMBINE, s)) != hipSuccess) return hip_status(err, "event");
-  if ((err = moe::launch_combine(y_sorted, pair_slot, y, d.T, d.H, d.top_k, s)) != hipSuccess)
+  if ((err = moe::launch_combine(y_sorted, !gemv, pair_slot, y, d.T, d.H, d.top_k, s)) != hipSuccess)
     return hip_status(err, "combine");
   if ((err = mark(events, MOE_NUM_STAGES, s)) != hipSuccess) return hip_status(err, "event");
   return ok();

@@ -65,7 +65,8 @@ struct MfmaParams {
 // (scale, bias) words; for G >= 64 one word serves both and is copied once.
 // STAGES: depth of the LDS ring (STAGES - 1 slabs in flight); WGS_PER_CU:
 // workgroups meant to share a CU (register budget).
-template <int MODE, int MB, int WAVES, bool G32, int STAGES, int WGS_PER_CU>
+// PACK (S7 only): out is packed 24-bit instead of fp32.
+template <int MODE, int MB, int WAVES, bool G32, int STAGES, int WGS_PER_CU, bool PACK = false>
 __global__ __launch_bounds__(64 * WAVES, WGS_PER_CU) void w4_mfma_kernel(const MfmaParams p) {
   constexpr bool GATE_UP = MODE == MOE_GEMM_GATE_UP_SWIGLU;
   constexpr int BM = MB * 32;
@@ -281,6 +282,40 @@ __global__ __launch_bounds__(64 * WAVES, WGS_PER_CU) void w4_mfma_kernel(const M
       *reinterpret_cast<uint4*>(reinterpret_cast<half_t*>(p.out) + (size_t)(row0 + row) * N + n0 + 8 * ch) =
           *reinterpret_cast<const uint4*>(tile_h + row * OUT_COLS + 8 * ch);
     }
+  } else if constexpr (PACK) {
+    if (!active) return;
+    // Registers 4g .. 4g + 3 of a lane hold 4 consecutive rows of one
+    // column; a 4 x 4 transpose inside each lane quad (two DPP exchange
+    // steps, partners lane ^ 2 then lane ^ 1) gives lane 4q + j row j of
+    // them at columns 4q .. 4q + 3, which it weights, packs and stores as
+    // 12 bytes.
+    const int j4 = col & 3, q = col >> 2;
+    const bool hi2 = (j4 & 2) != 0, hi1 = (j4 & 1) != 0;
+    auto xchg = [](float v, int ctrl) {
+      return ctrl == 0x4E ? __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true))
+                          : __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
+    };
+    uint3* out24 = reinterpret_cast<uint3*>(p.out);
+#pragma unroll
+    for (int mb = 0; mb < MB; mb++)
+#pragma unroll
+      for (int cb = 0; cb < 2; cb++)
+#pragma unroll
+        for (int g = 0; g < 4; g++) {
+          float a0 = acc[mb][cb][4 * g], a1 = acc[mb][cb][4 * g + 1];
+          float a2 = acc[mb][cb][4 * g + 2], a3 = acc[mb][cb][4 * g + 3];
+          float r0 = xchg(hi2 ? a0 : a2, 0x4E), r1 = xchg(hi2 ? a1 : a3, 0x4E);  // quad_perm 2,3,0,1
+          if (hi2) { a0 = r0; a1 = r1; } else { a2 = r0; a3 = r1; }
+          r0 = xchg(hi1 ? a0 : a1, 0xB1);  // quad_perm 1,0,3,2
+          r1 = xchg(hi1 ? a2 : a3, 0xB1);
+          if (hi1) { a0 = r0; a2 = r1; } else { a1 = r0; a3 = r1; }
+          const int row = mb * 32 + 8 * g + 4 * khalf + j4;
+          if (row < rows) {
+            const float w = row_w[row];
+            out24[((size_t)(row0 + row) * N + nb * OUT_COLS + wave * 64 + cb * 32) / 4 + q] =
+                pack24x4(w * a0, w * a1, w * a2, w * a3);
+          }
+        }
   } else {
     if (!active) return;
 #pragma unroll
@@ -308,7 +343,7 @@ __global__ __launch_bounds__(256) void stage_x_kernel(const uint4* __restrict__ 
   out[i] = bf16x8_to_half_interleaved(in[i]);
 }
 
-template <int MODE>
+template <int MODE, bool PACK>
 hipError_t launch_mode(const GemmArgs& a, hipStream_t s) {
   const int64_t P = (int64_t)a.T * a.top_k;
   const int64_t max_blocks = P / a.block_m + (P < a.E ? P : a.E);
@@ -325,17 +360,17 @@ hipError_t launch_mode(const GemmArgs& a, hipStream_t s) {
   const int64_t grid = ((items + kNumXcd - 1) / kNumXcd) * kNumXcd;
   const bool g32 = a.G == 32;
   switch (a.block_m * 2 + (g32 ? 1 : 0)) {
-    case 64: w4_mfma_kernel<MODE, 1, 4, false, 4, 2><<<grid, 256, 0, s>>>(p); break;
-    case 65: w4_mfma_kernel<MODE, 1, 4, true, 4, 2><<<grid, 256, 0, s>>>(p); break;
-    case 128: w4_mfma_kernel<MODE, 2, 4, false, 4, 2><<<grid, 256, 0, s>>>(p); break;
-    case 129: w4_mfma_kernel<MODE, 2, 4, true, 4, 2><<<grid, 256, 0, s>>>(p); break;
+    case 64: w4_mfma_kernel<MODE, 1, 4, false, 4, 2, PACK><<<grid, 256, 0, s>>>(p); break;
+    case 65: w4_mfma_kernel<MODE, 1, 4, true, 4, 2, PACK><<<grid, 256, 0, s>>>(p); break;
+    case 128: w4_mfma_kernel<MODE, 2, 4, false, 4, 2, PACK><<<grid, 256, 0, s>>>(p); break;
+    case 129: w4_mfma_kernel<MODE, 2, 4, true, 4, 2, PACK><<<grid, 256, 0, s>>>(p); break;
     case 256:
-      if (kWide) w4_mfma_kernel<MODE, 4, 8, false, 4, 1><<<grid, 512, 0, s>>>(p);
-      else w4_mfma_kernel<MODE, 4, 4, false, 3, 2><<<grid, 256, 0, s>>>(p);
+      if (kWide) w4_mfma_kernel<MODE, 4, 8, false, 4, 1, PACK><<<grid, 512, 0, s>>>(p);
+      else w4_mfma_kernel<MODE, 4, 4, false, 3, 2, PACK><<<grid, 256, 0, s>>>(p);
       break;
     case 257:
-      if (kWide) w4_mfma_kernel<MODE, 4, 8, true, 4, 1><<<grid, 512, 0, s>>>(p);
-      else w4_mfma_kernel<MODE, 4, 4, true, 3, 2><<<grid, 256, 0, s>>>(p);
+      if (kWide) w4_mfma_kernel<MODE, 4, 8, true, 4, 1, PACK><<<grid, 512, 0, s>>>(p);
+      else w4_mfma_kernel<MODE, 4, 4, true, 3, 2, PACK><<<grid, 256, 0, s>>>(p);
       break;
     default: return hipErrorInvalidValue;
   }
@@ -344,11 +379,13 @@ hipError_t launch_mode(const GemmArgs& a, hipStream_t s) {
 
 // y[t][:] = sum_j y_sorted[pair_slot[t*k + j]][:], j ascending, fp32: the
 // k weighted expert outputs of a token added in a fixed order, so the layer
-// output is deterministic.  One thread per 16 bytes of y; all k slot indices
-// and then all k rows are loaded before the sum (KMAX >= k, guards for
-// j >= k), so a thread has k row loads in flight instead of k round trips.
-template <int KMAX>
-__global__ __launch_bounds__(256) void combine_kernel(const float4* __restrict__ y_sorted,
+// output is deterministic.  One thread per 4 columns of y (16 bytes out;
+// 16 bytes in per slot, or 12 when y_sorted is packed 24-bit); all k slot
+// indices and then all k rows are loaded before the sum (KMAX >= k, guards
+// for j >= k), so a thread has k row loads in flight instead of k round
+// trips.
+template <int KMAX, bool PACK>
+__global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y_sorted,
                                                       const int32_t* __restrict__ pair_slot,
                                                       float4* __restrict__ y, int T, int H4,
                                                       int k) {
@@ -364,8 +401,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const float4* __restrict__
   }
   float4 v[KMAX];
 #pragma unroll
-  for (int j = 0; j < KMAX; j++)
-    v[j] = slot[j] >= 0 ? y_sorted[(size_t)slot[j] * H4 + c] : make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j = 0; j < KMAX; j++) {
+    const size_t at = (size_t)slot[j] * H4 + c;
+    if (slot[j] < 0) v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+    else if constexpr (PACK) v[j] = unpack24x4(reinterpret_cast<const uint3*>(y_sorted)[at]);
+    else v[j] = reinterpret_cast<const float4*>(y_sorted)[at];
+  }
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
   for (int j = 0; j < KMAX; j++) {
@@ -381,8 +422,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const float4* __restrict__
 }  // namespace
 
 hipError_t launch_w4_mfma(const GemmArgs& a, hipStream_t s) {
-  return a.mode == MOE_GEMM_GATE_UP_SWIGLU ? launch_mode<MOE_GEMM_GATE_UP_SWIGLU>(a, s)
-                                           : launch_mode<MOE_GEMM_DOWN>(a, s);
+  if (a.mode == MOE_GEMM_GATE_UP_SWIGLU) return launch_mode<MOE_GEMM_GATE_UP_SWIGLU, false>(a, s);
+  return a.pack24 ? launch_mode<MOE_GEMM_DOWN, true>(a, s) : launch_mode<MOE_GEMM_DOWN, false>(a, s);
 }
 
 hipError_t launch_stage_x(const uint16_t* x, half_t* xh, int64_t n_elems, hipStream_t s) {
@@ -392,16 +433,22 @@ hipError_t launch_stage_x(const uint16_t* x, half_t* xh, int64_t n_elems, hipStr
   return hipGetLastError();
 }
 
-hipError_t launch_combine(const float* y_sorted, const int32_t* pair_slot, float* y, int T,
-                          int H, int k, hipStream_t s) {
+template <bool PACK>
+void launch_combine_k(const void* ys, const int32_t* pair_slot, float4* yo, int T, int H4, int k,
+                      int64_t grid, hipStream_t s) {
+  if (k <= 2) combine_kernel<2, PACK><<<grid, 256, 0, s>>>(ys, pair_slot, yo, T, H4, k);
+  else if (k <= 4) combine_kernel<4, PACK><<<grid, 256, 0, s>>>(ys, pair_slot, yo, T, H4, k);
+  else if (k <= 8) combine_kernel<8, PACK><<<grid, 256, 0, s>>>(ys, pair_slot, yo, T, H4, k);
+  else combine_kernel<16, PACK><<<grid, 256, 0, s>>>(ys, pair_slot, yo, T, H4, k);  // k <= 16
+}
+
+hipError_t launch_combine(const void* y_sorted, bool pack24, const int32_t* pair_slot, float* y,
+                          int T, int H, int k, hipStream_t s) {
   const int64_t n = (int64_t)T * (H / 4);
   const int64_t grid = (n + 255) / 256;
-  const float4* ys = reinterpret_cast<const float4*>(y_sorted);
   float4* yo = reinterpret_cast<float4*>(y);
-  if (k <= 2) combine_kernel<2><<<grid, 256, 0, s>>>(ys, pair_slot, yo, T, H / 4, k);
-  else if (k <= 4) combine_kernel<4><<<grid, 256, 0, s>>>(ys, pair_slot, yo, T, H / 4, k);
-  else if (k <= 8) combine_kernel<8><<<grid, 256, 0, s>>>(ys, pair_slot, yo, T, H / 4, k);
-  else combine_kernel<16><<<grid, 256, 0, s>>>(ys, pair_slot, yo, T, H / 4, k);  // k <= 16
+  if (pack24) launch_combine_k<true>(y_sorted, pair_slot, yo, T, H / 4, k, grid, s);
+  else launch_combine_k<false>(y_sorted, pair_slot, yo, T, H / 4, k, grid, s);
   return hipGetLastError();
 }
 

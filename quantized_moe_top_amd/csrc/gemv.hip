@@ -34,8 +34,9 @@ struct DecParams {
   int N, K, log2_G, top_k, E, P, max_blocks;
 };
 
-// SPW: 64-wide slabs per wave and pass.
-template <int MODE, int SPW>
+// SPW: 64-wide slabs per wave and pass.  PACK (S7 only): out is packed
+// 24-bit instead of fp32.
+template <int MODE, int SPW, bool PACK = false>
 __global__ __launch_bounds__(64 * kDecWavesMax) void w4_gemv_kernel(const DecParams p) {
   constexpr bool GATE_UP = MODE == MOE_GEMM_GATE_UP_SWIGLU;
   constexpr int NB = GATE_UP ? 2 : 1;  // banks read: gate and up, or down
@@ -140,6 +141,26 @@ __global__ __launch_bounds__(64 * kDecWavesMax) void w4_gemv_kernel(const DecPar
 #pragma unroll
     for (int r = 0; r < 4; r++) red[((wave * NB + b) * 4 + r) * 64 + lane] = acc[b][r];
   __syncthreads();
+  if constexpr (PACK) {
+    // 4 consecutive columns per thread, weighted, packed into 12 bytes
+    for (int t = tid; t < rows * 8; t += blockDim.x) {
+      const int m = t >> 3, q = t & 7;
+      const int rr = m & 3;
+      float v4[4];
+#pragma unroll
+      for (int c = 0; c < 4; c++) {
+        const int ll = 4 * q + c + 32 * (m >> 2);
+        float v = red[rr * 64 + ll];
+        for (int w2 = 1; w2 < nwaves; w2++) v += red[(w2 * 4 + rr) * 64 + ll];
+        v4[c] = v;
+      }
+      const int pair = p.sorted_pairs[row0 + m];
+      const float wgt = (pair >= 0 && pair < p.P) ? p.topk_weights[pair] : 0.0f;
+      reinterpret_cast<uint3*>(p.out)[((size_t)(row0 + m) * p.N + blk * 32) / 4 + q] =
+          pack24x4(wgt * v4[0], wgt * v4[1], wgt * v4[2], wgt * v4[3]);
+    }
+    return;
+  }
   for (int t = tid; t < rows * 32; t += blockDim.x) {
     const int m = t >> 5, cc = t & 31;
     const int rr = m & 3, ll = cc + 32 * (m >> 2);
@@ -184,6 +205,9 @@ hipError_t launch_w4_gemv(const GemmArgs& a, hipStream_t s) {
   if (a.mode == MOE_GEMM_GATE_UP_SWIGLU) {
     if (wide) w4_gemv_kernel<MOE_GEMM_GATE_UP_SWIGLU, 4><<<grid, 64 * waves, lds, s>>>(p);
     else w4_gemv_kernel<MOE_GEMM_GATE_UP_SWIGLU, 2><<<grid, 64 * waves, lds, s>>>(p);
+  } else if (a.pack24) {
+    if (wide) w4_gemv_kernel<MOE_GEMM_DOWN, 4, true><<<grid, 64 * waves, lds, s>>>(p);
+    else w4_gemv_kernel<MOE_GEMM_DOWN, 2, true><<<grid, 64 * waves, lds, s>>>(p);
   } else {
     if (wide) w4_gemv_kernel<MOE_GEMM_DOWN, 4><<<grid, 64 * waves, lds, s>>>(p);
     else w4_gemv_kernel<MOE_GEMM_DOWN, 2><<<grid, 64 * waves, lds, s>>>(p);

@@ -135,6 +135,25 @@ __device__ __forceinline__ void lds_wait(u32x4& a, u32x4& b) {
   asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b));
 }
 
+// Packed 24-bit values ("y24"): the top 3 bytes of an fp32 pattern after
+// rounding the low byte off to nearest even (sign, 8 exponent bits, 15
+// mantissa bits: relative error at most 2^-16), 4 values in 12 bytes,
+// little-endian.  Used for the weighted expert outputs between the down
+// projection and the combine inside the layer.
+__device__ __forceinline__ uint32_t round24(float v) {
+  const uint32_t u = __float_as_uint(v);
+  return (u + 0x7Fu + ((u >> 8) & 1u)) >> 8;
+}
+__device__ __forceinline__ uint3 pack24x4(float a, float b, float c, float d) {
+  const uint32_t p0 = round24(a), p1 = round24(b), p2 = round24(c), p3 = round24(d);
+  return make_uint3(p0 | (p1 << 24), (p1 >> 8) | (p2 << 16), (p2 >> 16) | (p3 << 8));
+}
+__device__ __forceinline__ float4 unpack24x4(uint3 w) {
+  return make_float4(__uint_as_float(w.x << 8), __uint_as_float(((w.x >> 16) & 0x0000FF00u) | (w.y << 16)),
+                     __uint_as_float(((w.y >> 8) & 0x00FFFF00u) | (w.z << 24)),
+                     __uint_as_float(w.z & 0xFFFFFF00u));
+}
+
 // silu(g) * u = g / (1 + e^-g) * u, with the hardware exponential and
 // reciprocal (about 1 ulp each; the result is then rounded to fp16).
 __device__ __forceinline__ float silu_mul(float g, float u) {
@@ -194,13 +213,15 @@ struct GemmArgs {
   const int32_t* blocks;
   const int32_t* num_blocks;
   void* out;
+  bool pack24 = false;  // down: out is packed 24-bit [P][N] instead of fp32
 };
 hipError_t launch_w4_mfma(const GemmArgs& a, hipStream_t s);
 hipError_t launch_w4_gemv(const GemmArgs& a, hipStream_t s);
 
-// S8: y[t] = sum_j y_sorted[pair_slot[t * k + j]], j ascending.
-hipError_t launch_combine(const float* y_sorted, const int32_t* pair_slot, float* y, int T,
-                          int H, int k, hipStream_t s);
+// S8: y[t] = sum_j y_sorted[pair_slot[t * k + j]], j ascending; y_sorted
+// fp32, or packed 24-bit when pack24.
+hipError_t launch_combine(const void* y_sorted, bool pack24, const int32_t* pair_slot, float* y,
+                          int T, int H, int k, hipStream_t s);
 
 
 }  // namespace moe
