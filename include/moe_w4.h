@@ -227,8 +227,9 @@ typedef struct {
   const uint8_t* y_sorted;      /* [P][H] weighted, slot order, y_sorted_bytes
                                    per value: 4 = fp32 (path 1); 3 = packed
                                    24-bit (path 0): little-endian, the top 3
-                                   bytes of the fp32 pattern rounded to nearest
-                                   even (relative error <= 2^-16) */
+                                   bytes of the fp32 pattern rounded to nearest,
+                                   ties away from zero (relative error
+                                   <= 2^-16) */
   int32_t y_sorted_bytes;
 } moe_route_info;
 

@@ -10,12 +10,11 @@
 // (S7), over the whole reduction dimension in slabs of 64.  Wave w owns all
 // BM rows and two 32-column blocks (gate and up columns 32w.. in S6,
 // columns 64w.. in S7), so every word of codes it dequantises feeds BM/32
-// MFMAs per block.  W is 4 (two workgroups per CU) except for 128-row tiles
-// of S7, which take 8 waves and one workgroup per CU.
+// MFMAs per block.  W is 4, and two workgroups share a CU.
 //
 // Operands reach LDS with global_load_lds_dwordx4 (each lane's 16 bytes
 // land at the instruction's LDS base + 16 * lane, no registers involved)
-// into a ring of R stages (R = 4, or 3 for 128-row tiles of S6); the loads
+// into a ring of R stages (R = 4, or 3 for 128-row tiles); the loads
 // for slab s + R - 1 are issued while slab s is computed, so R - 1 slabs of
 // loads are in flight and the compute reads only LDS.  Per slab and stage:
 //  - A: BM rows x 64 fp16 activations (operand order), 128 bytes a row, the
@@ -56,11 +55,10 @@ struct MfmaParams {
   int N, K, log2_G, top_k, E, P, max_blocks;
 };
 
-// WAVES waves per workgroup (4 or 8): the tile covers 64 * WAVES weight
-// columns.  With 4 waves two workgroups fit a CU (LDS <= 80 KiB) for tiles of
-// up to 64 rows (and for 128-row S6 tiles), so one workgroup's prologue and
-// epilogue overlap another's main loop; 128-row S7 tiles use 8 waves (one
-// workgroup per CU).
+// WAVES waves per workgroup: the tile covers 64 * WAVES weight columns.
+// With 4 waves two workgroups fit a CU (LDS <= 80 KiB; 128-row tiles with a
+// 3-stage ring), so one workgroup's prologue and epilogue overlap the
+// other's main loop.
 // G32: group size 32, the two reduction halves of a slab have their own
 // (scale, bias) words; for G >= 64 one word serves both and is copied once.
 // STAGES: depth of the LDS ring (STAGES - 1 slabs in flight); WGS_PER_CU:
@@ -295,7 +293,18 @@ __global__ __launch_bounds__(64 * WAVES, WGS_PER_CU) void w4_mfma_kernel(const M
       return ctrl == 0x4E ? __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true))
                           : __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
     };
-    uint3* out24 = reinterpret_cast<uint3*>(p.out);
+    // byte address of this lane's rows 4 khalf + j4 (+ 32 mb + 8 g) at
+    // columns 4q .. 4q + 3 of its 64-column slice (row stride 3 N bytes)
+    const size_t rstride = (size_t)N * 3;
+    char* const lane_out = reinterpret_cast<char*>(p.out) + (size_t)(row0 + 4 * khalf + j4) * rstride +
+                           (size_t)(nb * OUT_COLS + wave * 64 + 4 * q) * 3;
+    // the routing weights of this lane's rows after the transposes, read
+    // from LDS once
+    float wr[MB][4];
+#pragma unroll
+    for (int mb = 0; mb < MB; mb++)
+#pragma unroll
+      for (int g = 0; g < 4; g++) wr[mb][g] = row_w[mb * 32 + 8 * g + 4 * khalf + j4];
 #pragma unroll
     for (int mb = 0; mb < MB; mb++)
 #pragma unroll
@@ -304,15 +313,22 @@ __global__ __launch_bounds__(64 * WAVES, WGS_PER_CU) void w4_mfma_kernel(const M
         for (int g = 0; g < 4; g++) {
           float a0 = acc[mb][cb][4 * g], a1 = acc[mb][cb][4 * g + 1];
           float a2 = acc[mb][cb][4 * g + 2], a3 = acc[mb][cb][4 * g + 3];
+          // step 1, partner lane ^ 2: send the rows the partner keeps
           float r0 = xchg(hi2 ? a0 : a2, 0x4E), r1 = xchg(hi2 ? a1 : a3, 0x4E);  // quad_perm 2,3,0,1
-          if (hi2) { a0 = r0; a1 = r1; } else { a2 = r0; a3 = r1; }
+          a0 = hi2 ? r0 : a0;
+          a1 = hi2 ? r1 : a1;
+          a2 = hi2 ? a2 : r0;
+          a3 = hi2 ? a3 : r1;
+          // step 2, partner lane ^ 1
           r0 = xchg(hi1 ? a0 : a1, 0xB1);  // quad_perm 1,0,3,2
           r1 = xchg(hi1 ? a2 : a3, 0xB1);
-          if (hi1) { a0 = r0; a2 = r1; } else { a1 = r0; a3 = r1; }
-          const int row = mb * 32 + 8 * g + 4 * khalf + j4;
-          if (row < rows) {
-            const float w = row_w[row];
-            out24[((size_t)(row0 + row) * N + nb * OUT_COLS + wave * 64 + cb * 32) / 4 + q] =
+          a0 = hi1 ? r0 : a0;
+          a2 = hi1 ? r1 : a2;
+          a1 = hi1 ? a1 : r0;
+          a3 = hi1 ? a3 : r1;
+          if (mb * 32 + 8 * g + 4 * khalf + j4 < rows) {
+            const float w = wr[mb][g];
+            *reinterpret_cast<uint3*>(lane_out + (size_t)(mb * 32 + 8 * g) * rstride + cb * 96) =
                 pack24x4(w * a0, w * a1, w * a2, w * a3);
           }
         }
@@ -350,11 +366,10 @@ hipError_t launch_mode(const GemmArgs& a, hipStream_t s) {
   const int log2_G = a.G == 32 ? 5 : a.G == 64 ? 6 : 7;  // G in {32, 64, 128}
   MfmaParams p{a.a, a.b0, a.b1, a.sorted_pairs, a.topk_weights, a.blocks, a.num_blocks, a.out,
                a.N, a.K, log2_G, a.top_k, a.E, (int)P, (int)max_blocks};
-  // 128-row tiles: S6 with 4 waves and a 3-stage ring (two workgroups per
-  // CU, one's epilogue overlapping the other's main loop); S7 with 8 waves
-  // and 4 stages (its short reduction, K = I, prefers the deeper ring)
-  constexpr bool kWide = MODE != MOE_GEMM_GATE_UP_SWIGLU;
-  const int bcols = a.block_m == 128 && kWide ? 512 : 256;  // 64 * waves, as in the switch below
+  // 4 waves (256 weight columns) per workgroup and two workgroups per CU,
+  // so one workgroup's prologue and epilogue overlap the other's main loop;
+  // 128-row tiles use a 3-stage ring to fit two workgroups' LDS
+  const int bcols = 256;
   const int out_cols = MODE == MOE_GEMM_GATE_UP_SWIGLU ? bcols / 2 : bcols;
   const int64_t items = max_blocks * ((a.N + out_cols - 1) / out_cols);
   const int64_t grid = ((items + kNumXcd - 1) / kNumXcd) * kNumXcd;
@@ -364,14 +379,8 @@ hipError_t launch_mode(const GemmArgs& a, hipStream_t s) {
     case 65: w4_mfma_kernel<MODE, 1, 4, true, 4, 2, PACK><<<grid, 256, 0, s>>>(p); break;
     case 128: w4_mfma_kernel<MODE, 2, 4, false, 4, 2, PACK><<<grid, 256, 0, s>>>(p); break;
     case 129: w4_mfma_kernel<MODE, 2, 4, true, 4, 2, PACK><<<grid, 256, 0, s>>>(p); break;
-    case 256:
-      if (kWide) w4_mfma_kernel<MODE, 4, 8, false, 4, 1, PACK><<<grid, 512, 0, s>>>(p);
-      else w4_mfma_kernel<MODE, 4, 4, false, 3, 2, PACK><<<grid, 256, 0, s>>>(p);
-      break;
-    case 257:
-      if (kWide) w4_mfma_kernel<MODE, 4, 8, true, 4, 1, PACK><<<grid, 512, 0, s>>>(p);
-      else w4_mfma_kernel<MODE, 4, 4, true, 3, 2, PACK><<<grid, 256, 0, s>>>(p);
-      break;
+    case 256: w4_mfma_kernel<MODE, 4, 4, false, 3, 2, PACK><<<grid, 256, 0, s>>>(p); break;
+    case 257: w4_mfma_kernel<MODE, 4, 4, true, 3, 2, PACK><<<grid, 256, 0, s>>>(p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

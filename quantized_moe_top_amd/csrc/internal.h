@@ -136,17 +136,20 @@ __device__ __forceinline__ void lds_wait(u32x4& a, u32x4& b) {
 }
 
 // Packed 24-bit values ("y24"): the top 3 bytes of an fp32 pattern after
-// rounding the low byte off to nearest even (sign, 8 exponent bits, 15
-// mantissa bits: relative error at most 2^-16), 4 values in 12 bytes,
-// little-endian.  Used for the weighted expert outputs between the down
-// projection and the combine inside the layer.
-__device__ __forceinline__ uint32_t round24(float v) {
-  const uint32_t u = __float_as_uint(v);
-  return (u + 0x7Fu + ((u >> 8) & 1u)) >> 8;
-}
+// rounding the low byte off to nearest, ties away from zero (sign, 8
+// exponent bits, 15 mantissa bits: relative error at most 2^-16), 4 values
+// in 12 bytes, little-endian.  Used for the weighted expert outputs between
+// the down projection and the combine inside the layer.
+// Adding 0x80 to the sign-magnitude pattern rounds the magnitude at bit 8
+// (a carry into the exponent is the correct rounding up; past the largest
+// finite value it gives infinity).
+__device__ __forceinline__ uint32_t round24_bits(float v) { return __float_as_uint(v) + 0x80u; }
+// Bytes 1..3 of each rounded pattern, concatenated: three byte permutes.
 __device__ __forceinline__ uint3 pack24x4(float a, float b, float c, float d) {
-  const uint32_t p0 = round24(a), p1 = round24(b), p2 = round24(c), p3 = round24(d);
-  return make_uint3(p0 | (p1 << 24), (p1 >> 8) | (p2 << 16), (p2 >> 16) | (p3 << 8));
+  const uint32_t r0 = round24_bits(a), r1 = round24_bits(b), r2 = round24_bits(c), r3 = round24_bits(d);
+  // v_perm_b32(hi, lo, sel): selector byte i picks byte sel_i of {lo: 0-3, hi: 4-7}
+  return make_uint3(__builtin_amdgcn_perm(r1, r0, 0x05030201u), __builtin_amdgcn_perm(r2, r1, 0x06050302u),
+                    __builtin_amdgcn_perm(r3, r2, 0x07060503u));
 }
 __device__ __forceinline__ float4 unpack24x4(uint3 w) {
   return make_float4(__uint_as_float(w.x << 8), __uint_as_float(((w.x >> 16) & 0x0000FF00u) | (w.y << 16)),
