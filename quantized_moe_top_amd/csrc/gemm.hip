@@ -10,11 +10,11 @@
 // (S7), over the whole reduction dimension in slabs of 64.  Wave w owns all
 // BM rows and two 32-column blocks (gate and up columns 32w.. in S6,
 // columns 64w.. in S7), so every word of codes it dequantises feeds BM/32
-// MFMAs per block.  W is 4, and two workgroups share a CU.
+// MFMAs per block.  W is 4, and two or three workgroups share a CU.
 //
 // Operands reach LDS with global_load_lds_dwordx4 (each lane's 16 bytes
 // land at the instruction's LDS base + 16 * lane, no registers involved)
-// into a ring of R stages (R = 4, or 3 for 128-row tiles); the loads
+// into a ring of R stages (R = 4 for 32-row tiles, 3 otherwise); the loads
 // for slab s + R - 1 are issued while slab s is computed, so R - 1 slabs of
 // loads are in flight and the compute reads only LDS.  Per slab and stage:
 //  - A: BM rows x 64 fp16 activations (operand order), 128 bytes a row, the
@@ -56,9 +56,9 @@ struct MfmaParams {
 };
 
 // WAVES waves per workgroup: the tile covers 64 * WAVES weight columns.
-// With 4 waves two workgroups fit a CU (LDS <= 80 KiB; 128-row tiles with a
-// 3-stage ring), so one workgroup's prologue and epilogue overlap the
-// other's main loop.
+// With 4 waves several workgroups fit a CU (two of 128 rows, three of 64
+// rows with a 3-stage ring), so one workgroup's prologue and epilogue
+// overlap another's main loop.
 // G32: group size 32, the two reduction halves of a slab have their own
 // (scale, bias) words; for G >= 64 one word serves both and is copied once.
 // STAGES: depth of the LDS ring (STAGES - 1 slabs in flight); WGS_PER_CU:
@@ -70,7 +70,7 @@ __global__ __launch_bounds__(64 * WAVES, WGS_PER_CU) void w4_mfma_kernel(const M
   constexpr int BM = MB * 32;
   constexpr int kBCols = 64 * WAVES;                     // weight columns per workgroup
   constexpr int kBStage = kBCols * 32;                   // bytes of codes per stage
-  constexpr int kSStage = kBCols * 2 * 4;                // bytes of scale / bias words per stage
+  constexpr int kSStage = kBCols * 4 * (G32 ? 2 : 1);    // bytes of scale / bias words per stage
   constexpr int A_BYTES = BM * 128;                      // per stage
   constexpr int STAGE = A_BYTES + kBStage + kSStage;
   constexpr int A_INSTR = BM / 8;                        // 1 KiB A loads per stage
@@ -366,9 +366,10 @@ hipError_t launch_mode(const GemmArgs& a, hipStream_t s) {
   const int log2_G = a.G == 32 ? 5 : a.G == 64 ? 6 : 7;  // G in {32, 64, 128}
   MfmaParams p{a.a, a.b0, a.b1, a.sorted_pairs, a.topk_weights, a.blocks, a.num_blocks, a.out,
                a.N, a.K, log2_G, a.top_k, a.E, (int)P, (int)max_blocks};
-  // 4 waves (256 weight columns) per workgroup and two workgroups per CU,
-  // so one workgroup's prologue and epilogue overlap the other's main loop;
-  // 128-row tiles use a 3-stage ring to fit two workgroups' LDS
+  // 4 waves (256 weight columns) per workgroup and two or three workgroups
+  // per CU, so one workgroup's prologue and epilogue overlap another's main
+  // loop; 64- and 128-row tiles use a 3-stage ring to fit three and two
+  // workgroups' LDS (and 64-row tiles a register budget for three)
   const int bcols = 256;
   const int out_cols = MODE == MOE_GEMM_GATE_UP_SWIGLU ? bcols / 2 : bcols;
   const int64_t items = max_blocks * ((a.N + out_cols - 1) / out_cols);
@@ -377,8 +378,8 @@ hipError_t launch_mode(const GemmArgs& a, hipStream_t s) {
   switch (a.block_m * 2 + (g32 ? 1 : 0)) {
     case 64: w4_mfma_kernel<MODE, 1, 4, false, 4, 2, PACK><<<grid, 256, 0, s>>>(p); break;
     case 65: w4_mfma_kernel<MODE, 1, 4, true, 4, 2, PACK><<<grid, 256, 0, s>>>(p); break;
-    case 128: w4_mfma_kernel<MODE, 2, 4, false, 4, 2, PACK><<<grid, 256, 0, s>>>(p); break;
-    case 129: w4_mfma_kernel<MODE, 2, 4, true, 4, 2, PACK><<<grid, 256, 0, s>>>(p); break;
+    case 128: w4_mfma_kernel<MODE, 2, 4, false, 3, 3, PACK><<<grid, 256, 0, s>>>(p); break;
+    case 129: w4_mfma_kernel<MODE, 2, 4, true, 3, 3, PACK><<<grid, 256, 0, s>>>(p); break;
     case 256: w4_mfma_kernel<MODE, 4, 4, false, 3, 2, PACK><<<grid, 256, 0, s>>>(p); break;
     case 257: w4_mfma_kernel<MODE, 4, 4, true, 3, 2, PACK><<<grid, 256, 0, s>>>(p); break;
     default: return hipErrorInvalidValue;
