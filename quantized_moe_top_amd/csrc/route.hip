@@ -621,18 +621,105 @@ struct BuildParams {
   int32_t *counts, *offsets, *sorted_pairs, *pair_slot, *blocks, *num_blocks;
 };
 
-// All tokens in one chunk (decode sizes): one workgroup routes them (S1),
-// then, after a barrier that makes its ids and histogram visible to the
-// whole workgroup, builds counts, offsets, the scatter and the block map
-// (S2-S5): one launch instead of two, same results.
+constexpr int kSmallPairs = 8 * 16;  // decode sizes: T <= 8 tokens, k <= 16
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_inclusive_sum(int x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int v = __shfl_up(x, d);
+    if (lane >= d) x += v;
+  }
+  return x;
+}
+
+// All tokens in one chunk (decode sizes, at most kSmallPairs pairs): one
+// workgroup routes them (S1) and then builds S2-S5 from LDS: the expert
+// counts by LDS atomics, and one wave does the rest, with no block-wide scan:
+//   - exclusive prefix sums over the E <= 256 experts (4 consecutive experts
+//     per lane, then a wave prefix sum): offsets, and the first tile of each
+//     expert for the block map;
+//   - the stable scatter of the pairs in order, 64 at a time: lanes with the
+//     same expert are matched with ballots over the expert-id bits, and a
+//     lane's slot is its expert's next free slot plus the number of matching
+//     lanes below it (the same counting sort as the multi-chunk kernel).
 template <int NK>
 __global__ __launch_bounds__(kRouteThreads) void route_build_kernel(const RouteParams p,
                                                                     const BuildParams b) {
+  __shared__ int cnt[256];
+  __shared__ int next[256];
+  __shared__ int ids_s[kSmallPairs];
   route_chunk<true, NK, 64>(p, 0);  // at most 8 tokens: a wave each
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int P = p.T * p.k, E = p.E;
+  if (tid < 256) cnt[tid] = 0;
   __threadfence_block();
+  __syncthreads();  // ids of every wave visible
+  if (tid < P) {
+    const int id = p.ids[tid];
+    ids_s[tid] = id;
+    if (id >= 0 && id < E) atomicAdd(&cnt[id], 1);
+  }
   __syncthreads();
-  scan_scatter_chunk(p.ids, p.T * p.k, p.E, p.chunk_tokens * p.k, 1, p.chunk_hist, b.block_m,
-                     b.counts, b.offsets, b.sorted_pairs, b.pair_slot, b.blocks, b.num_blocks, 0);
+  if (tid >= 64) return;
+  // expert e = 4 lane + i
+  int c[4], tl[4], cs = 0, ts = 0;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const int e = 4 * lane + i;
+    c[i] = e < E ? cnt[e] : 0;
+    tl[i] = (c[i] + b.block_m - 1) / b.block_m;
+    cs += c[i];
+    ts += tl[i];
+  }
+  int off = wave_inclusive_sum(cs) - cs, tile = wave_inclusive_sum(ts) - ts;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const int e = 4 * lane + i;
+    if (e < E) {
+      b.counts[e] = c[i];
+      b.offsets[e] = off;
+      next[e] = off;
+      for (int j = 0; j < tl[i]; j++) {
+        int32_t* blk = b.blocks + 3 * (size_t)(tile + j);
+        blk[0] = e;
+        blk[1] = off + j * b.block_m;
+        blk[2] = min(b.block_m, c[i] - j * b.block_m);
+      }
+    }
+    off += c[i];
+    tile += tl[i];
+  }
+  if (lane == 63) {
+    b.offsets[E] = P;
+    b.num_blocks[0] = tile;  // total tiles (inclusive sum of the last lane)
+  }
+  wave_lds_sync();
+  int bits = 1;
+  while ((1 << bits) < E) bits++;
+  for (int base = 0; base < P; base += 64) {
+    const int q = base + lane;
+    const int id = q < P ? ids_s[q] : -1;
+    const bool active = id >= 0 && id < E;
+    const int ex = active ? id : 0;
+    uint64_t match = __ballot(active);
+    for (int bt = 0; bt < bits; bt++) {
+      const bool bit = (ex >> bt) & 1;
+      const uint64_t bal = __ballot(bit);
+      match &= bit ? bal : ~bal;
+    }
+    const uint64_t below = match & ((1ull << lane) - 1ull);
+    const int start = active ? next[ex] : 0;
+    wave_lds_sync();
+    if (active) {
+      const int slot = start + __popcll(below);
+      b.sorted_pairs[slot] = q;
+      b.pair_slot[q] = slot;
+      if (below == 0) next[ex] = start + __popcll(match);  // lowest lane of its group
+    }
+    wave_lds_sync();
+  }
 }
 
 // List length L of the top-k: the power of two in {2, 4, 8, 16} at or above k.

@@ -340,6 +340,17 @@ def test_ffn_router_split(orc):
         layer_output_check(orc, lay, y, info)
 
 
+def test_ffn_decode_edges(orc):
+    """Decode sizes (one-workgroup routing and block map): the most pairs it
+    takes (T = 8, k = 16), one expert chosen of two, and an odd E."""
+    for (T, E, k) in [(8, 256, 16), (1, 2, 1), (7, 5, 3)]:
+        lay = synth.make_custom(T=T, H=256, I=128, E=E, k=k, G=32, seed=50 + T + E)
+        y, info = api.ffn_forward(on_dev(lay), info=True)
+        torch.cuda.synchronize()
+        assert info["path"] == 1
+        layer_output_check(orc, lay, y, info)
+
+
 def test_ffn_t0():
     lay = synth.make_custom(T=0, H=256, I=128, E=8, k=2, G=32, seed=34)
     y = api.ffn_forward(on_dev(lay))
