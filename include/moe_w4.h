@@ -264,6 +264,27 @@ int moe_ffn_forward_timed(const moe_layer* layer, const uint16_t* x, const float
                           float* y, moe_route_info* info, void* workspace, size_t workspace_bytes,
                           void* const* stage_events, void* stream);
 
+/* ------------------------------------------- ablation: host block map --
+ * The same layer as moe_ffn_forward (same kernels, same results, bit for
+ * bit), except that S2-S5 take a host round trip, the design the pages'
+ * single-submission pipeline replaces (page "Perplexity's Lily engine
+ * beats MLX by 35% on M5 Max", architecture paragraph): after S1 the
+ * per-chunk expert histograms are copied to host_pinned and the stream is
+ * synchronised; the host computes the counts, the offsets, each chunk's
+ * first slot per expert and the block map, and uploads them; the device
+ * then only runs the stable scatter, and the GEMMs are launched with the
+ * exact tile count.  For measuring that design only; it blocks the calling
+ * thread and cannot be captured in a graph.
+ * host_pinned: pinned host memory (hipHostMalloc) of at least
+ * moe_ffn_host_blockmap_ints(&layer->dims) int32; it is read by the uploads
+ * until the stream passes them, so the caller leaves it alone until then.
+ * T <= 8 (the GEMV path) returns MOE_ERR_UNSUPPORTED. */
+size_t moe_ffn_host_blockmap_ints(const moe_dims* dims);  /* 0 if unsupported */
+int moe_ffn_forward_host_blockmap(const moe_layer* layer, const uint16_t* x,
+                                  const float* router_logits, float* y, moe_route_info* info,
+                                  void* workspace, size_t workspace_bytes, int32_t* host_pinned,
+                                  size_t host_ints, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -281,9 +281,68 @@ hipError_t mark(void* const* events, int i, hipStream_t s) {
   return hipEventRecord((hipEvent_t)events[i], s);
 }
 
+// The host round trip of the S2-S5 ablation: the per-chunk histograms come
+// to the host (the stream is synchronised), the host computes counts,
+// offsets, each chunk's first slot per expert and the block map, and uploads
+// them (first slots over the histograms); the device then only scatters,
+// and the GEMMs are launched with the exact tile count.  host stays in use
+// by the uploads until the stream passes them.
+hipError_t host_block_map(const moe_dims& d, int block_m, int32_t* host, int32_t* chunk_hist,
+                          int32_t* counts, int32_t* offsets, int32_t* blocks, int32_t* num_blocks,
+                          int64_t* tiles_out, hipStream_t s) {
+  const int E = d.E, nch = moe::route_chunks(d.T);
+  const int64_t P = (int64_t)d.T * d.top_k;
+  int32_t* hist = host;  // [nch][E], then first slots
+  int32_t* hc = hist + (size_t)nch * E;
+  int32_t* ho = hc + E;
+  int32_t* hb = ho + E + 1;
+  int32_t* hn = hb + 3 * max_blocks(P, E, block_m);
+  hipError_t err = hipMemcpyAsync(hist, chunk_hist, sizeof(int32_t) * nch * E, hipMemcpyDeviceToHost, s);
+  if (err != hipSuccess) return err;
+  if ((err = hipStreamSynchronize(s)) != hipSuccess) return err;
+  int64_t off = 0, tiles = 0;
+  for (int e = 0; e < E; e++) {
+    int64_t run = off;
+    for (int c = 0; c < nch; c++) {
+      const int32_t n = hist[(size_t)c * E + e];
+      hist[(size_t)c * E + e] = (int32_t)run;
+      run += n;
+    }
+    hc[e] = (int32_t)(run - off);
+    ho[e] = (int32_t)off;
+    for (int64_t i = 0; i * block_m < run - off; i++, tiles++) {
+      hb[3 * tiles] = e;
+      hb[3 * tiles + 1] = (int32_t)(off + i * block_m);
+      hb[3 * tiles + 2] = (int32_t)std::min<int64_t>(block_m, run - off - i * block_m);
+    }
+    off = run;
+  }
+  ho[E] = (int32_t)P;
+  *hn = (int32_t)tiles;
+  const struct { void* dst; const void* src; size_t n; } up[] = {
+      {chunk_hist, hist, sizeof(int32_t) * nch * E}, {counts, hc, sizeof(int32_t) * E},
+      {offsets, ho, sizeof(int32_t) * (E + 1)}, {blocks, hb, sizeof(int32_t) * 3 * tiles},
+      {num_blocks, hn, sizeof(int32_t)}};
+  for (const auto& u : up)
+    if (u.n && (err = hipMemcpyAsync(u.dst, u.src, u.n, hipMemcpyHostToDevice, s)) != hipSuccess) return err;
+  *tiles_out = tiles;
+  return hipSuccess;
+}
+
+// Ints of the pinned host buffer the host-block-map path uses: per-chunk
+// histograms (then first slots), counts, offsets, the block map and its size.
+size_t host_blockmap_ints(const moe_dims& d, int block_m) {
+  const int64_t P = (int64_t)d.T * d.top_k;
+  return (size_t)moe::route_chunks(d.T) * d.E + d.E + (d.E + 1) +
+         3 * (size_t)max_blocks(P, d.E, block_m) + 1;
+}
+
+// host (or nullptr): pinned host buffer of host_blockmap_ints ints; when
+// given, S2-S5 take the host round trip (see moe_ffn_forward_host_blockmap).
 int ffn_forward_impl(const moe_layer* layer, const uint16_t* x, const float* router_logits,
                      float* y, moe_route_info* info, void* workspace, size_t workspace_bytes,
-                     void* const* events, hipStream_t s) {
+                     void* const* events, hipStream_t s, int32_t* host = nullptr,
+                     size_t host_ints = 0) {
   if (!layer) return fail(MOE_ERR_NULL, "layer is NULL");
   const moe_dims& d = layer->dims;
   int st = check_dims(&d);
@@ -307,6 +366,12 @@ int ffn_forward_impl(const moe_layer* layer, const uint16_t* x, const float* rou
   if (!workspace) return fail(MOE_ERR_NULL, "workspace is NULL");
   if ((uintptr_t)workspace & 255u) return fail(MOE_ERR_ALIGN, "workspace not 256-byte aligned");
   if (workspace_bytes < L.total) return fail(MOE_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, L.total);
+  if (host) {
+    if (d.T <= moe::kGemvMaxTokens)
+      return fail(MOE_ERR_UNSUPPORTED, "the host block map path needs T > %d", moe::kGemvMaxTokens);
+    if (host_ints < host_blockmap_ints(d, block_m))
+      return fail(MOE_ERR_WORKSPACE, "host buffer %zu < %zu ints", host_ints, host_blockmap_ints(d, block_m));
+  }
 
   char* ws = (char*)workspace;
   float* logits = has_router ? (float*)(ws + L.logits) : (float*)router_logits;
@@ -330,6 +395,7 @@ int ffn_forward_impl(const moe_layer* layer, const uint16_t* x, const float* rou
 
   hipError_t err;
   int32_t* chunk_hist = (int32_t*)(ws + L.scratch);
+  int64_t grid_tiles = -1;  // host-known tile count (host block map path)
   float* part = L.router_ks > 1 ? (float*)(ws + L.logits_part) : nullptr;  // router partial sums
   if ((err = mark(events, MOE_STAGE_ROUTE, s)) != hipSuccess) return hip_status(err, "event");
   if (moe::route_build_fused(d.T)) {
@@ -344,15 +410,22 @@ int ffn_forward_impl(const moe_layer* layer, const uint16_t* x, const float* rou
                                  chunk_hist, part, s)) != hipSuccess)
       return hip_status(err, "route");
     if ((err = mark(events, MOE_STAGE_BUILD_BLOCKS, s)) != hipSuccess) return hip_status(err, "event");
+    if (host) {
+      if ((err = host_block_map(d, block_m, host, chunk_hist, counts, offsets, blocks, num_blocks,
+                                &grid_tiles, s)) != hipSuccess)
+        return hip_status(err, "host block map");
+    }
     if ((err = moe::launch_scan_scatter(ids, d.T, d.top_k, d.E, chunk_hist, block_m, counts, offsets,
-                                        sorted_pairs, pair_slot, blocks, num_blocks, s)) != hipSuccess)
+                                        sorted_pairs, pair_slot, blocks, num_blocks, s,
+                                        host ? chunk_hist : nullptr)) != hipSuccess)
       return hip_status(err, "scan_scatter");
   }
   moe::GemmArgs g1{MOE_GEMM_GATE_UP_SWIGLU, d.T, d.top_k, d.E, d.I, d.H, d.group_size, block_m,
-                   xh, layer->gate, layer->up, sorted_pairs, w, blocks, num_blocks, h};
+                   xh, layer->gate, layer->up, sorted_pairs, w, blocks, num_blocks, h, false,
+                   grid_tiles};
   moe::GemmArgs g2{MOE_GEMM_DOWN, d.T, d.top_k, d.E, d.H, d.I, d.group_size, block_m,
                    h, layer->down, layer->down, sorted_pairs, w, blocks, num_blocks, y_sorted,
-                   !gemv};
+                   !gemv, grid_tiles};
   if ((err = mark(events, MOE_STAGE_GATE_UP, s)) != hipSuccess) return hip_status(err, "event");
   err = gemv ? moe::launch_w4_gemv(g1, s) : moe::launch_w4_mfma(g1, s);
   if (err != hipSuccess) return hip_status(err, "gate_up");
@@ -375,6 +448,20 @@ int moe_ffn_forward(const moe_layer* layer, const uint16_t* x, const float* rout
                     void* stream) {
   return ffn_forward_impl(layer, x, router_logits, y, info, workspace, workspace_bytes, nullptr,
                           (hipStream_t)stream);
+}
+
+size_t moe_ffn_host_blockmap_ints(const moe_dims* d) {
+  if (!d || check_dims(d) != MOE_OK || d->T <= moe::kGemvMaxTokens) return 0;
+  return host_blockmap_ints(*d, moe_ffn_block_m(d));
+}
+
+int moe_ffn_forward_host_blockmap(const moe_layer* layer, const uint16_t* x,
+                                  const float* router_logits, float* y, moe_route_info* info,
+                                  void* workspace, size_t workspace_bytes, int32_t* host_pinned,
+                                  size_t host_ints, void* stream) {
+  if (!host_pinned) return fail(MOE_ERR_NULL, "host_pinned is NULL");
+  return ffn_forward_impl(layer, x, router_logits, y, info, workspace, workspace_bytes, nullptr,
+                          (hipStream_t)stream, host_pinned, host_ints);
 }
 
 int moe_ffn_forward_timed(const moe_layer* layer, const uint16_t* x, const float* router_logits,

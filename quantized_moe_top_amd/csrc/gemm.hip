@@ -362,7 +362,8 @@ __global__ __launch_bounds__(256) void stage_x_kernel(const uint4* __restrict__ 
 template <int MODE, bool PACK>
 hipError_t launch_mode(const GemmArgs& a, hipStream_t s) {
   const int64_t P = (int64_t)a.T * a.top_k;
-  const int64_t max_blocks = P / a.block_m + (P < a.E ? P : a.E);
+  const int64_t max_blocks = a.grid_tiles >= 0 ? a.grid_tiles : P / a.block_m + (P < a.E ? P : a.E);
+  if (max_blocks == 0) return hipSuccess;
   const int log2_G = a.G == 32 ? 5 : a.G == 64 ? 6 : 7;  // G in {32, 64, 128}
   MfmaParams p{a.a, a.b0, a.b1, a.sorted_pairs, a.topk_weights, a.blocks, a.num_blocks, a.out,
                a.N, a.K, log2_G, a.top_k, a.E, (int)P, (int)max_blocks};

@@ -192,11 +192,13 @@ hipError_t launch_route_build(const uint16_t* x, const uint16_t* wr, float* logi
 // Per-chunk expert histogram of caller-given ids [T][k].
 hipError_t launch_chunk_hist(const int32_t* ids, int T, int k, int E, int32_t* chunk_hist,
                              hipStream_t s);
-// S2 (totals) - S5 from the per-chunk histograms.
+// S2 (totals) - S5 from the per-chunk histograms; with chunk_start
+// ([chunks][E] first slots, computed by the caller) only the S4 scatter.
 hipError_t launch_scan_scatter(const int32_t* ids, int T, int k, int E, const int32_t* chunk_hist,
                                int block_m, int32_t* counts, int32_t* offsets,
                                int32_t* sorted_pairs, int32_t* pair_slot, int32_t* blocks,
-                               int32_t* num_blocks, hipStream_t s);
+                               int32_t* num_blocks, hipStream_t s,
+                               const int32_t* chunk_start = nullptr);
 
 // x bf16 [T][H] -> fp16 [T][H] with every 8-chunk interleaved (see above).
 hipError_t launch_stage_x(const uint16_t* x, half_t* xh, int64_t n_elems, hipStream_t s);
@@ -216,7 +218,8 @@ struct GemmArgs {
   const int32_t* blocks;
   const int32_t* num_blocks;
   void* out;
-  bool pack24 = false;  // down: out is packed 24-bit [P][N] instead of fp32
+  bool pack24 = false;       // down: out is packed 24-bit [P][N] instead of fp32
+  int64_t grid_tiles = -1;   // >= 0: exact tile count known on the host (grid sized to it)
 };
 hipError_t launch_w4_mfma(const GemmArgs& a, hipStream_t s);
 hipError_t launch_w4_gemv(const GemmArgs& a, hipStream_t s);

@@ -35,18 +35,24 @@ __device__ __forceinline__ void wave_lds_sync() {
 }
 
 // One workgroup of kScanThreads threads, chunk c of nchunks: see
-// build_blocks.hip for the algorithm.
+// build_blocks.hip for the algorithm.  With chunk_start (nchunks x E, the
+// first slot of chunk c's pairs of expert e, computed elsewhere) only the
+// scatter runs: no sums, no scan, no block map.
 __device__ __forceinline__ void scan_scatter_chunk(
     const int32_t* __restrict__ ids, int P, int E, int chunk_pairs, int nchunks,
     const int32_t* __restrict__ chunk_hist, int block_m, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pairs,
     int32_t* __restrict__ pair_slot, int32_t* __restrict__ blocks, int32_t* __restrict__ num_blocks,
-    int c) {
+    int c, const int32_t* __restrict__ chunk_start = nullptr) {
   __shared__ int tmp[kScanThreads];
   __shared__ int spre[kScanThreads], stot[kScanThreads];
   __shared__ int wnext[kScanWaves][256];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-
+  const int e = tid;
+  int first = 0;  // first slot of this chunk's pairs of expert e
+  if (chunk_start) {
+    if (e < E) first = chunk_start[(size_t)c * E + e];
+  } else {
   // ---- per expert: histogram rows of the chunks before this one, and of
   // all chunks.  Thread (g, e) sums chunks g, g + G, ... (8 loads in flight).
   {
@@ -73,7 +79,6 @@ __device__ __forceinline__ void scan_scatter_chunk(
     stot[tid] = tot;
   }
   __syncthreads();
-  const int e = tid;
   int pre = 0, tot = 0;
   if (e < E) {
     const int G = kScanThreads / E;
@@ -102,6 +107,8 @@ __device__ __forceinline__ void scan_scatter_chunk(
       num_blocks[0] = tile0 + tiles;
     }
   }
+  first = off + pre;
+  }
 
   // ---- the chunk's pairs in one contiguous segment per wave
   const int p0 = c * chunk_pairs;
@@ -116,7 +123,7 @@ __device__ __forceinline__ void scan_scatter_chunk(
   }
   __syncthreads();
   if (e < E) {
-    int run = off + pre;
+    int run = first;
 #pragma unroll
     for (int w = 0; w < kScanWaves; w++) {
       const int n = wnext[w][e];

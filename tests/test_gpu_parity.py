@@ -351,6 +351,30 @@ def test_ffn_decode_edges(orc):
         layer_output_check(orc, lay, y, info)
 
 
+@pytest.mark.parametrize("case", ["prefill_t512", "ragged", "imbalanced_t8192"])
+def test_ffn_host_blockmap_identical(case):
+    """The host-round-trip ablation runs the same kernels on a block map the
+    host builds: routing structures and output bit-identical to the
+    single-submission layer."""
+    if case == "ragged":
+        lay = synth.make_custom(T=333, H=512, I=256, E=16, k=2, G=64, seed=61)
+    else:
+        lay = synth.make_layer(case)
+    lay = api.pack_layer(on_dev(lay))
+    y1, i1 = api.ffn_forward(lay, info=True)
+    y1 = y1.clone()
+    ref = {k: cpu(i1[k]).copy() for k in ("counts", "offsets", "sorted_pairs", "pair_slot", "num_blocks")}
+    nb = int(ref["num_blocks"][0])
+    ref["blocks"] = cpu(i1["blocks"])[:nb].copy()
+    host = torch.empty(api.host_blockmap_ints(lay), dtype=torch.int32, pin_memory=True)
+    y2, i2 = api.ffn_forward(lay, info=True, host_blockmap=host)
+    torch.cuda.synchronize()
+    for k in ("counts", "offsets", "sorted_pairs", "pair_slot", "num_blocks"):
+        assert np.array_equal(cpu(i2[k]), ref[k]), k
+    assert np.array_equal(cpu(i2["blocks"])[:nb], ref["blocks"])
+    assert torch.equal(y1, y2)
+
+
 def test_ffn_t0():
     lay = synth.make_custom(T=0, H=256, I=128, E=8, k=2, G=32, seed=34)
     y = api.ffn_forward(on_dev(lay))
