@@ -61,7 +61,7 @@ def parse():
                     help="time eager launches only (no HIP graph replays)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="minimum CPU time of the oracle sample")
-    ap.add_argument("--ablation", choices=["host_blockmap"], default=None,
+    ap.add_argument("--ablation", choices=["host_blockmap", "unfused"], default=None,
                     help="also time the layer with the block map built on the host (a stream "
                          "synchronisation and copies mid-layer), against the same layer eager")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -333,6 +333,27 @@ def main():
             "single_submission_speedup_eager": round(host_ms / plain_ms, 3)}}
         log(f"[bench] host block map: {host_ms / K * 1e3:.2f} us/step vs eager {plain_ms / K * 1e3:.2f} "
             f"and graph {ms_per_step * 1e3:.2f}")
+
+    if args.ablation == "unfused" and api.unfused_bytes(lay) > 0:
+        # every step expands all experts' weights to fp16 in HBM, then the
+        # grouped GEMMs stream those: eager, against the fused layer eager
+        ex = torch.empty(api.unfused_bytes(lay), dtype=torch.uint8, device=dev)
+
+        def step_unfused(i):
+            c = copies[i % R]
+            lg = logit_pool[i % len(logit_pool)] if logit_pool else None
+            return api.ffn_forward(c, logits=lg, y=y, workspace=ws, expanded=ex)
+
+        for i in range(args.warmup):
+            step_unfused(i)
+        plain_ms, _ = timed(lambda i: step(i))
+        unf_ms, _ = timed(step_unfused)
+        ablations = dict(ablations or {})
+        ablations["unfused"] = {
+            "ms_per_step": round(unf_ms / K, 6),
+            "eager_fused_ms_per_step": round(plain_ms / K, 6),
+            "fused_speedup": round(unf_ms / plain_ms, 3)}
+        log(f"[bench] unfused dequant: {unf_ms / K * 1e3:.2f} us/step vs fused {plain_ms / K * 1e3:.2f}")
 
     if args.copy_calibration:
         src = torch.empty(64 << 20, dtype=torch.float32, device=dev).fill_(1.0)

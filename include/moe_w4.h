@@ -285,6 +285,22 @@ int moe_ffn_forward_host_blockmap(const moe_layer* layer, const uint16_t* x,
                                   void* workspace, size_t workspace_bytes, int32_t* host_pinned,
                                   size_t host_ints, void* stream);
 
+/* ------------------------------------------- ablation: unfused dequant --
+ * The same layer with the 4-bit dequantisation taken out of the grouped
+ * GEMMs, the design the pages' fused GEMM replaces (page "Perplexity's Lily
+ * engine beats MLX by 35% on M5 Max", architecture paragraph): every call
+ * first expands all experts' gate, up and down banks to fp16 weights in
+ * `expanded` (HBM), then runs the grouped GEMMs on those, streaming 4 times
+ * the weight bytes.  Same values, same products in the same order: the output
+ * is bit-identical to moe_ffn_forward.  For measuring that design only.
+ * expanded: device, 16-byte aligned, at least moe_ffn_unfused_bytes(dims)
+ * bytes (E * 3 * H * I * 2).  T <= 8 returns MOE_ERR_UNSUPPORTED. */
+size_t moe_ffn_unfused_bytes(const moe_dims* dims);  /* 0 if unsupported */
+int moe_ffn_forward_unfused(const moe_layer* layer, const uint16_t* x, const float* router_logits,
+                            float* y, moe_route_info* info, void* workspace,
+                            size_t workspace_bytes, void* expanded, size_t expanded_bytes,
+                            void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -27,6 +27,7 @@ SYMBOLS = (
     "moe_w4_grouped_gemm_workspace_bytes", "moe_w4_grouped_gemm",
     "moe_ffn_block_m", "moe_ffn_workspace_bytes", "moe_ffn_forward", "moe_ffn_forward_timed",
     "moe_ffn_host_blockmap_ints", "moe_ffn_forward_host_blockmap",
+    "moe_ffn_unfused_bytes", "moe_ffn_forward_unfused",
 )
 
 # Stage boundaries of moe_ffn_forward_timed (enum moe_stage).
@@ -116,8 +117,13 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     L.moe_ffn_forward_host_blockmap.argtypes = [ctypes.POINTER(Layer), c_p, c_p, c_p,
                                                 ctypes.POINTER(RouteInfo), c_p, c_sz, c_p, c_sz,
                                                 c_p]
+    L.moe_ffn_unfused_bytes.restype = c_sz
+    L.moe_ffn_unfused_bytes.argtypes = [ctypes.POINTER(Dims)]
+    L.moe_ffn_forward_unfused.argtypes = [ctypes.POINTER(Layer), c_p, c_p, c_p,
+                                          ctypes.POINTER(RouteInfo), c_p, c_sz, c_p, c_sz, c_p]
     for name in ("moe_w4_pack", "moe_route", "moe_build_blocks", "moe_w4_grouped_gemm",
-                 "moe_ffn_forward", "moe_ffn_forward_timed", "moe_ffn_forward_host_blockmap"):
+                 "moe_ffn_forward", "moe_ffn_forward_timed", "moe_ffn_forward_host_blockmap",
+                 "moe_ffn_forward_unfused"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L

@@ -233,6 +233,12 @@ def unpack_y24(packed: torch.Tensor) -> torch.Tensor:
     return bits.to(torch.int32).view(torch.float32)
 
 
+def unfused_bytes(layer, T: Optional[int] = None) -> int:
+    """Bytes of the device buffer ``ffn_forward(expanded=...)`` needs (0 when
+    T <= 8)."""
+    return int(_L().moe_ffn_unfused_bytes(ctypes.byref(_dims(layer, layer.T if T is None else T))))
+
+
 def host_blockmap_ints(layer, T: Optional[int] = None) -> int:
     """int32 elements of the pinned host buffer ``ffn_forward(host_blockmap=...)``
     needs (0 when T <= 8: the GEMV path has no host variant)."""
@@ -241,7 +247,8 @@ def host_blockmap_ints(layer, T: Optional[int] = None) -> int:
 
 def ffn_forward(layer, x: Optional[torch.Tensor] = None, logits: Optional[torch.Tensor] = None,
                 y: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                info: bool = False, stage_events=None, host_blockmap: Optional[torch.Tensor] = None):
+                info: bool = False, stage_events=None, host_blockmap: Optional[torch.Tensor] = None,
+                expanded: Optional[torch.Tensor] = None):
     """The whole layer (S0/S1-S8) for a ``PackedLayer`` (a device
     ``synth.MoELayer`` is packed first).  ``x`` and ``logits`` default to the
     layer's own.  Returns y
@@ -250,7 +257,9 @@ def ffn_forward(layer, x: Optional[torch.Tensor] = None, logits: Optional[torch.
     ``moe_ffn_forward_timed``, recording one event per stage boundary.
     ``host_blockmap`` (a pinned int32 CPU tensor of ``host_blockmap_ints``
     elements) runs the host-round-trip ablation
-    ``moe_ffn_forward_host_blockmap`` instead (it synchronises the stream)."""
+    ``moe_ffn_forward_host_blockmap`` instead (it synchronises the stream).
+    ``expanded`` (a device uint8 tensor of ``unfused_bytes``) runs the
+    unfused-dequantisation ablation ``moe_ffn_forward_unfused`` instead."""
     if not isinstance(layer, PackedLayer):
         layer = pack_layer(layer)
     x = layer.x if x is None else x
@@ -270,7 +279,11 @@ def ffn_forward(layer, x: Optional[torch.Tensor] = None, logits: Optional[torch.
             _dev(logits, "logits", torch.float32) if layer.router_weight is None else 0,
             _dev(y, "y", torch.float32), ctypes.byref(ri),
             _dev(workspace, "workspace", torch.uint8), workspace.numel())
-    if host_blockmap is not None:
+    if expanded is not None:
+        _lib.check(_L().moe_ffn_forward_unfused(*args, _dev(expanded, "expanded", torch.uint8),
+                                                expanded.numel(), _stream()),
+                   "moe_ffn_forward_unfused")
+    elif host_blockmap is not None:
         if not (host_blockmap.is_pinned() and host_blockmap.dtype == torch.int32):
             raise ValueError("host_blockmap must be a pinned int32 CPU tensor")
         _lib.check(_L().moe_ffn_forward_host_blockmap(*args, host_blockmap.data_ptr(),

@@ -329,6 +329,10 @@ hipError_t host_block_map(const moe_dims& d, int block_m, int32_t* host, int32_t
   return hipSuccess;
 }
 
+// Bytes of the fp16 weights the unfused ablation expands: gate, up and down
+// of every expert.
+size_t unfused_bytes(const moe_dims& d) { return (size_t)d.E * 3 * d.H * d.I * 2; }
+
 // Ints of the pinned host buffer the host-block-map path uses: per-chunk
 // histograms (then first slots), counts, offsets, the block map and its size.
 size_t host_blockmap_ints(const moe_dims& d, int block_m) {
@@ -342,7 +346,8 @@ size_t host_blockmap_ints(const moe_dims& d, int block_m) {
 int ffn_forward_impl(const moe_layer* layer, const uint16_t* x, const float* router_logits,
                      float* y, moe_route_info* info, void* workspace, size_t workspace_bytes,
                      void* const* events, hipStream_t s, int32_t* host = nullptr,
-                     size_t host_ints = 0) {
+                     size_t host_ints = 0, uint32_t* expanded = nullptr,
+                     size_t expanded_bytes = 0) {
   if (!layer) return fail(MOE_ERR_NULL, "layer is NULL");
   const moe_dims& d = layer->dims;
   int st = check_dims(&d);
@@ -366,6 +371,13 @@ int ffn_forward_impl(const moe_layer* layer, const uint16_t* x, const float* rou
   if (!workspace) return fail(MOE_ERR_NULL, "workspace is NULL");
   if ((uintptr_t)workspace & 255u) return fail(MOE_ERR_ALIGN, "workspace not 256-byte aligned");
   if (workspace_bytes < L.total) return fail(MOE_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, L.total);
+  if (expanded) {
+    if (d.T <= moe::kGemvMaxTokens)
+      return fail(MOE_ERR_UNSUPPORTED, "the unfused path needs T > %d", moe::kGemvMaxTokens);
+    if (!aligned16(expanded)) return fail(MOE_ERR_ALIGN, "expanded weights not 16-byte aligned");
+    if (expanded_bytes < unfused_bytes(d))
+      return fail(MOE_ERR_WORKSPACE, "expanded buffer %zu < %zu bytes", expanded_bytes, unfused_bytes(d));
+  }
   if (host) {
     if (d.T <= moe::kGemvMaxTokens)
       return fail(MOE_ERR_UNSUPPORTED, "the host block map path needs T > %d", moe::kGemvMaxTokens);
@@ -427,6 +439,20 @@ int ffn_forward_impl(const moe_layer* layer, const uint16_t* x, const float* rou
                    h, layer->down, layer->down, sorted_pairs, w, blocks, num_blocks, y_sorted,
                    !gemv, grid_tiles};
   if ((err = mark(events, MOE_STAGE_GATE_UP, s)) != hipSuccess) return hip_status(err, "event");
+  if (expanded) {
+    // unfused ablation: every expert's banks expanded to fp16 in HBM first
+    uint32_t* eg = expanded;
+    uint32_t* eu = eg + (size_t)d.E * d.I * d.H / 2;
+    uint32_t* ed = eu + (size_t)d.E * d.I * d.H / 2;
+    if ((err = moe::launch_expand(layer->gate, d.E, d.I, d.H, d.group_size, eg, s)) != hipSuccess ||
+        (err = moe::launch_expand(layer->up, d.E, d.I, d.H, d.group_size, eu, s)) != hipSuccess ||
+        (err = moe::launch_expand(layer->down, d.E, d.H, d.I, d.group_size, ed, s)) != hipSuccess)
+      return hip_status(err, "expand");
+    g1.b0 = moe_w4_packed{eg, nullptr};
+    g1.b1 = moe_w4_packed{eu, nullptr};
+    g2.b0 = g2.b1 = moe_w4_packed{ed, nullptr};
+    g1.dense = g2.dense = true;
+  }
   err = gemv ? moe::launch_w4_gemv(g1, s) : moe::launch_w4_mfma(g1, s);
   if (err != hipSuccess) return hip_status(err, "gate_up");
   if ((err = mark(events, MOE_STAGE_DOWN, s)) != hipSuccess) return hip_status(err, "event");
@@ -448,6 +474,20 @@ int moe_ffn_forward(const moe_layer* layer, const uint16_t* x, const float* rout
                     void* stream) {
   return ffn_forward_impl(layer, x, router_logits, y, info, workspace, workspace_bytes, nullptr,
                           (hipStream_t)stream);
+}
+
+size_t moe_ffn_unfused_bytes(const moe_dims* d) {
+  if (!d || check_dims(d) != MOE_OK || d->T <= moe::kGemvMaxTokens) return 0;
+  return unfused_bytes(*d);
+}
+
+int moe_ffn_forward_unfused(const moe_layer* layer, const uint16_t* x, const float* router_logits,
+                            float* y, moe_route_info* info, void* workspace,
+                            size_t workspace_bytes, void* expanded, size_t expanded_bytes,
+                            void* stream) {
+  if (!expanded) return fail(MOE_ERR_NULL, "expanded is NULL");
+  return ffn_forward_impl(layer, x, router_logits, y, info, workspace, workspace_bytes, nullptr,
+                          (hipStream_t)stream, nullptr, 0, (uint32_t*)expanded, expanded_bytes);
 }
 
 size_t moe_ffn_host_blockmap_ints(const moe_dims* d) {

@@ -64,19 +64,24 @@ struct MfmaParams {
 // STAGES: depth of the LDS ring (STAGES - 1 slabs in flight); WGS_PER_CU:
 // workgroups meant to share a CU (register budget).
 // PACK (S7 only): out is packed 24-bit instead of fp32.
-template <int MODE, int MB, int WAVES, bool G32, int STAGES, int WGS_PER_CU, bool PACK = false>
+// DENSE (the unfused ablation): the banks hold weights already expanded to
+// fp16 in operand order (moe_w4_expand: per 32-column block and slab, four
+// 1 KiB pieces, piece i the dequantised word i of every (column, half)), and
+// the kernel copies and multiplies them with no dequantisation.
+template <int MODE, int MB, int WAVES, bool G32, int STAGES, int WGS_PER_CU, bool PACK = false,
+          bool DENSE = false>
 __global__ __launch_bounds__(64 * WAVES, WGS_PER_CU) void w4_mfma_kernel(const MfmaParams p) {
   constexpr bool GATE_UP = MODE == MOE_GEMM_GATE_UP_SWIGLU;
   constexpr int BM = MB * 32;
   constexpr int kBCols = 64 * WAVES;                     // weight columns per workgroup
-  constexpr int kBStage = kBCols * 32;                   // bytes of codes per stage
-  constexpr int kSStage = kBCols * 4 * (G32 ? 2 : 1);    // bytes of scale / bias words per stage
+  constexpr int kBStage = kBCols * (DENSE ? 128 : 32);   // bytes of codes (or fp16 weights) per stage
+  constexpr int kSStage = DENSE ? 0 : kBCols * 4 * (G32 ? 2 : 1);  // bytes of scale / bias words per stage
   constexpr int A_BYTES = BM * 128;                      // per stage
   constexpr int STAGE = A_BYTES + kBStage + kSStage;
   constexpr int A_INSTR = BM / 8;                        // 1 KiB A loads per stage
   constexpr int A_PER_WAVE = A_INSTR >= WAVES ? A_INSTR / WAVES : 1;
-  constexpr int B_PER_WAVE = 2;                          // 1 KiB code blocks per wave
-  constexpr int S_PER_WAVE = G32 ? 2 : 1;                // 256 B scale-word loads per wave
+  constexpr int B_PER_WAVE = DENSE ? 8 : 2;              // 1 KiB code blocks (or fp16 pieces) per wave
+  constexpr int S_PER_WAVE = DENSE ? 0 : G32 ? 2 : 1;    // 256 B scale-word loads per wave
   constexpr int OUT_COLS = GATE_UP ? kBCols / 2 : kBCols; // output columns per workgroup
   __shared__ __attribute__((aligned(16))) char lds[STAGES * STAGE];
   __shared__ float row_w[BM];
@@ -146,10 +151,13 @@ __global__ __launch_bounds__(64 * WAVES, WGS_PER_CU) void w4_mfma_kernel(const M
   const uint32_t* bsrc[B_PER_WAVE];
 #pragma unroll
   for (int b = 0; b < B_PER_WAVE; b++) {
-    const int j = B_PER_WAVE * wave + b;
+    const int j = DENSE ? 2 * wave + (b >> 2) : B_PER_WAVE * wave + b;
     const moe_w4_packed* bank;
     const int blk = block_of(j, bank);
-    bsrc[b] = bank->words + ((size_t)(blk >> 2) * slabs * 4 + (blk & 3)) * 256 + 4 * lane;
+    if (DENSE)  // piece b & 3 of the block's 4 KiB per slab
+      bsrc[b] = bank->words + ((size_t)(blk >> 2) * slabs * 4 + (blk & 3)) * 1024 + 256 * (b & 3) + 4 * lane;
+    else
+      bsrc[b] = bank->words + ((size_t)(blk >> 2) * slabs * 4 + (blk & 3)) * 256 + 4 * lane;
   }
 
   // ---- scale / bias words: stage layout [reduction half t][kBCols columns];
@@ -190,7 +198,7 @@ __global__ __launch_bounds__(64 * WAVES, WGS_PER_CU) void w4_mfma_kernel(const M
       for (int a = 0; a < APW; a++) lds_load16(asrc[a] + s * kSlabK, base + a_lds[a]);
 #pragma unroll
       for (int b = 0; b < B_PER_WAVE; b++)
-        lds_load16(bsrc[b] + s * 1024, base + A_BYTES + 1024 * (B_PER_WAVE * wave + b));
+        lds_load16(bsrc[b] + s * (DENSE ? 4096 : 1024), base + A_BYTES + 1024 * (B_PER_WAVE * wave + b));
 #pragma unroll
       for (int t = 0; t < S_PER_WAVE; t++)
         lds_load4(ssrc + ((s * kSlabK + 32 * t) >> log2G) * 128,
@@ -200,23 +208,30 @@ __global__ __launch_bounds__(64 * WAVES, WGS_PER_CU) void w4_mfma_kernel(const M
     auto compute = [&](int stage) {
       const char* base = lds + stage * STAGE;
       u32x4 q[2];
-#pragma unroll
-      for (int cb = 0; cb < 2; cb++)
-        q[cb] = *reinterpret_cast<const u32x4*>(base + A_BYTES + (wave * 64 + cb * 32 + col) * 32 +
-                                                16 * khalf);
       half2_t s2[2], b2[2];
+      if constexpr (!DENSE) {
 #pragma unroll
-      for (int cb = 0; cb < 2; cb++) {
-        const uint32_t sb = reinterpret_cast<const uint32_t*>(
-            base + A_BYTES + kBStage)[(G32 ? khalf : 0) * kBCols + wave * 64 + cb * 32 + col];
-        sb_pairs(sb, s2[cb], b2[cb]);
+        for (int cb = 0; cb < 2; cb++)
+          q[cb] = *reinterpret_cast<const u32x4*>(base + A_BYTES + (wave * 64 + cb * 32 + col) * 32 +
+                                                  16 * khalf);
+#pragma unroll
+        for (int cb = 0; cb < 2; cb++) {
+          const uint32_t sb = reinterpret_cast<const uint32_t*>(
+              base + A_BYTES + kBStage)[(G32 ? khalf : 0) * kBCols + wave * 64 + cb * 32 + col];
+          sb_pairs(sb, s2[cb], b2[cb]);
+        }
       }
 #pragma unroll
       for (int i = 0; i < 4; i++) {
         half8_t bf[2];
 #pragma unroll
-        for (int cb = 0; cb < 2; cb++)
-          bf[cb] = __builtin_bit_cast(half8_t, dequant_word(q[cb][i], s2[cb], b2[cb]));
+        for (int cb = 0; cb < 2; cb++) {
+          if constexpr (DENSE)
+            bf[cb] = *reinterpret_cast<const half8_t*>(base + A_BYTES + (2 * wave + cb) * 4096 +
+                                                       1024 * i + 16 * (2 * col + khalf));
+          else
+            bf[cb] = __builtin_bit_cast(half8_t, dequant_word(q[cb][i], s2[cb], b2[cb]));
+        }
 #pragma unroll
         for (int mb = 0; mb < MBA; mb++) {
           const int r = mb * 32 + col;
@@ -376,6 +391,15 @@ hipError_t launch_mode(const GemmArgs& a, hipStream_t s) {
   const int64_t items = max_blocks * ((a.N + out_cols - 1) / out_cols);
   const int64_t grid = ((items + kNumXcd - 1) / kNumXcd) * kNumXcd;
   const bool g32 = a.G == 32;
+  if (a.dense) {  // expanded fp16 weights: larger B stages, one workgroup per CU
+    switch (a.block_m) {
+      case 32: w4_mfma_kernel<MODE, 1, 4, false, 4, 1, PACK, true><<<grid, 256, 0, s>>>(p); break;
+      case 64: w4_mfma_kernel<MODE, 2, 4, false, 3, 1, PACK, true><<<grid, 256, 0, s>>>(p); break;
+      case 128: w4_mfma_kernel<MODE, 4, 4, false, 3, 1, PACK, true><<<grid, 256, 0, s>>>(p); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   switch (a.block_m * 2 + (g32 ? 1 : 0)) {
     case 64: w4_mfma_kernel<MODE, 1, 4, false, 4, 2, PACK><<<grid, 256, 0, s>>>(p); break;
     case 65: w4_mfma_kernel<MODE, 1, 4, true, 4, 2, PACK><<<grid, 256, 0, s>>>(p); break;

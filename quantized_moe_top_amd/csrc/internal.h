@@ -208,6 +208,13 @@ hipError_t launch_stage_x(const uint16_t* x, half_t* xh, int64_t n_elems, hipStr
 hipError_t launch_pack(const moe_w4_bank& src, int E, int N, int K, int G, uint32_t* words,
                        uint32_t* sb, hipStream_t s);
 
+// The unfused ablation: expands a packed bank (moe_w4_pack layout) to fp16
+// weights in the GEMM's operand order, 4 KiB per 32-column block and slab
+// (N * K * 2 bytes per expert): piece i of a block holds the dequantised word
+// i of each (column, reduction half), 16 bytes each.
+hipError_t launch_expand(const moe_w4_packed& bank, int E, int N, int K, int G, uint32_t* out,
+                         hipStream_t s);
+
 struct GemmArgs {
   int mode;  // MOE_GEMM_*
   int T, top_k, E, N, K, G, block_m;
@@ -220,6 +227,7 @@ struct GemmArgs {
   void* out;
   bool pack24 = false;       // down: out is packed 24-bit [P][N] instead of fp32
   int64_t grid_tiles = -1;   // >= 0: exact tile count known on the host (grid sized to it)
+  bool dense = false;        // banks hold expanded fp16 weights (moe_w4_expand layout), words only
 };
 hipError_t launch_w4_mfma(const GemmArgs& a, hipStream_t s);
 hipError_t launch_w4_gemv(const GemmArgs& a, hipStream_t s);

@@ -58,7 +58,40 @@ __global__ __launch_bounds__(256) void pack_scales_kernel(const uint16_t* __rest
   out[i] = (uint32_t)__builtin_bit_cast(uint16_t, hs) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
 }
 
+// One thread per 16-byte unit of packed codes (the 4 words of one column and
+// reduction half in one slab): the same exact dequantisation as the GEMMs,
+// written as 4 x 16 bytes of fp16.
+__global__ __launch_bounds__(256) void expand_kernel(const uint32_t* __restrict__ words,
+                                                     const uint32_t* __restrict__ sb,
+                                                     uint32_t* __restrict__ out, int64_t units,
+                                                     int slabs, int gpr, int log2G) {
+  const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (u >= units) return;
+  // u = ((ec * slabs + s) * 4 + blk) * 64 + 2 col + h, ec = e * N/128 + chunk
+  const int ch = (int)(u & 63), blk = (int)((u >> 6) & 3);
+  const int64_t rest = u >> 8;
+  const int s = (int)(rest % slabs);
+  const int64_t ec = rest / slabs;
+  const int col = ch >> 1, h = ch & 1;
+  const u32x4 q = reinterpret_cast<const u32x4*>(words)[u];
+  const int g = (64 * s + 32 * h) >> log2G;
+  half2_t s2, b2;
+  sb_pairs(sb[(ec * gpr + g) * 128 + blk * 32 + col], s2, b2);
+  uint4* o = reinterpret_cast<uint4*>(out) + (rest * 4 + blk) * 256 + ch;
+#pragma unroll
+  for (int i = 0; i < 4; i++) o[64 * i] = dequant_word(q[i], s2, b2);
+}
+
 }  // namespace
+
+hipError_t launch_expand(const moe_w4_packed& bank, int E, int N, int K, int G, uint32_t* out,
+                         hipStream_t s) {
+  const int64_t units = (int64_t)E * N * K / 32;  // 16-byte units of codes
+  const int log2G = G == 32 ? 5 : G == 64 ? 6 : 7;
+  expand_kernel<<<(units + 255) / 256, 256, 0, s>>>(bank.words, bank.sb, out, units, K / 64, K / G,
+                                                    log2G);
+  return hipGetLastError();
+}
 
 hipError_t launch_pack(const moe_w4_bank& src, int E, int N, int K, int G, uint32_t* words,
                        uint32_t* sb, hipStream_t s) {

@@ -375,6 +375,22 @@ def test_ffn_host_blockmap_identical(case):
     assert torch.equal(y1, y2)
 
 
+@pytest.mark.parametrize("case", ["prefill_t512", "ragged_g32", "imbalanced_t8192"])
+def test_ffn_unfused_identical(case):
+    """The unfused ablation multiplies the same fp16 weights (expanded to
+    HBM first) in the same order: output bit-identical to the fused layer."""
+    if case == "ragged_g32":
+        lay = synth.make_custom(T=333, H=512, I=256, E=16, k=2, G=32, seed=62)
+    else:
+        lay = synth.make_layer(case)
+    lay = api.pack_layer(on_dev(lay))
+    y1 = api.ffn_forward(lay).clone()
+    ex = torch.empty(api.unfused_bytes(lay), dtype=torch.uint8, device=DEV)
+    y2 = api.ffn_forward(lay, expanded=ex)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+
+
 def test_ffn_t0():
     lay = synth.make_custom(T=0, H=256, I=128, E=8, k=2, G=32, seed=34)
     y = api.ffn_forward(on_dev(lay))
