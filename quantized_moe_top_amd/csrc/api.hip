@@ -410,12 +410,12 @@ int ffn_forward_impl(const moe_layer* layer, const uint16_t* x, const float* rou
   int64_t grid_tiles = -1;  // host-known tile count (host block map path)
   float* part = L.router_ks > 1 ? (float*)(ws + L.logits_part) : nullptr;  // router partial sums
   if ((err = mark(events, MOE_STAGE_ROUTE, s)) != hipSuccess) return hip_status(err, "event");
-  if (moe::route_build_fused(d.T)) {
-    // one routing chunk: S1-S5 in one launch (the build stage is empty)
-    if ((err = moe::launch_route_build(x, layer->router_weight, logits, d.T, d.H, d.E, d.top_k, ids,
-                                       w, xh, chunk_hist, block_m, counts, offsets, sorted_pairs,
-                                       pair_slot, blocks, num_blocks, part, s)) != hipSuccess)
-      return hip_status(err, "route_build");
+  if (gemv) {
+    // decode sizes: the router GEMM (when given), then S1-S6 in one launch
+    // (the build stage and the routing inside the gate/up stage)
+    if (has_router && (err = moe::launch_router_logits(x, layer->router_weight, part ? part : logits,
+                                                       d.T, d.H, d.E, L.router_ks, s)) != hipSuccess)
+      return hip_status(err, "router");
     if ((err = mark(events, MOE_STAGE_BUILD_BLOCKS, s)) != hipSuccess) return hip_status(err, "event");
   } else {
     if ((err = moe::launch_route(x, layer->router_weight, logits, d.T, d.H, d.E, d.top_k, ids, w, xh,
@@ -439,7 +439,12 @@ int ffn_forward_impl(const moe_layer* layer, const uint16_t* x, const float* rou
                    h, layer->down, layer->down, sorted_pairs, w, blocks, num_blocks, y_sorted,
                    !gemv, grid_tiles};
   if ((err = mark(events, MOE_STAGE_GATE_UP, s)) != hipSuccess) return hip_status(err, "event");
-  if (expanded) {
+  if (gemv) {
+    g1.a = (const moe::half_t*)x;  // bf16, converted while staged
+    const moe::DecodeRouting dr{part ? part : logits, logits, L.router_ks, ids, w, counts, offsets,
+                                sorted_pairs, pair_slot, blocks, num_blocks};
+    err = moe::launch_decode_gate_up(dr, g1, s);
+  } else if (expanded) {
     // unfused ablation: every expert's banks expanded to fp16 in HBM first
     uint32_t* eg = expanded;
     uint32_t* eu = eg + (size_t)d.E * d.I * d.H / 2;
@@ -453,7 +458,7 @@ int ffn_forward_impl(const moe_layer* layer, const uint16_t* x, const float* rou
     g2.b0 = g2.b1 = moe_w4_packed{ed, nullptr};
     g1.dense = g2.dense = true;
   }
-  err = gemv ? moe::launch_w4_gemv(g1, s) : moe::launch_w4_mfma(g1, s);
+  if (!gemv) err = moe::launch_w4_mfma(g1, s);
   if (err != hipSuccess) return hip_status(err, "gate_up");
   if ((err = mark(events, MOE_STAGE_DOWN, s)) != hipSuccess) return hip_status(err, "event");
   err = gemv ? moe::launch_w4_gemv(g2, s) : moe::launch_w4_mfma(g2, s);

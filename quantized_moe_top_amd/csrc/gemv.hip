@@ -17,6 +17,7 @@
 // The waves' partial sums meet in LDS and are added in wave order, so the
 // result does not depend on timing.
 #include "internal.h"
+#include "topk.h"
 
 namespace moe {
 namespace {
@@ -32,12 +33,19 @@ struct DecParams {
   const int32_t* num_blocks;
   void* out;
   int N, K, log2_G, top_k, E, P, max_blocks;
+  int red_off;  // byte offset of the partial-sum area in the dynamic LDS
 };
 
+// One (tile, 32-column block) of the product: tile rows [row0, row0 + rows)
+// of expert e (rows <= kGemvMaxTokens), output columns [32 blk, 32 blk + 32).
 // SPW: 64-wide slabs per wave and pass.  PACK (S7 only): out is packed
-// 24-bit instead of fp32.
-template <int MODE, int SPW, bool PACK = false>
-__global__ __launch_bounds__(64 * kDecWavesMax) void w4_gemv_kernel(const DecParams p) {
+// 24-bit instead of fp32.  XBF16 (S6 only): p.a is x itself (bf16 [T][K]),
+// converted to fp16 operand order while staged, instead of the fp16 copy.
+// sorted_pairs: slot -> pair (global memory, or LDS in the fused kernel).
+// dsm: the dynamic LDS, sized by the launch.
+template <int MODE, int SPW, bool PACK, bool XBF16>
+__device__ __forceinline__ void gemv_tile(const DecParams& p, const int32_t* sorted_pairs, int e,
+                                          int row0, int rows, int blk, char* dsm) {
   constexpr bool GATE_UP = MODE == MOE_GEMM_GATE_UP_SWIGLU;
   constexpr int NB = GATE_UP ? 2 : 1;  // banks read: gate and up, or down
   const int tid = threadIdx.x, lane = tid & 63;
@@ -45,25 +53,14 @@ __global__ __launch_bounds__(64 * kDecWavesMax) void w4_gemv_kernel(const DecPar
   const int nwaves = blockDim.x >> 6;
   const int pass_slabs = nwaves * SPW;  // slabs per pass
   const int xw = pass_slabs * 64;       // row stride of xs
-  // LDS, sized by the launch: xs = this pass's activation rows (<= 8 rows x
-  // xw reduction indices, operand order), staged once for all waves; red =
+  // LDS: xs = this pass's activation rows (<= 8 rows x xw reduction
+  // indices, operand order), staged once for all waves; red (at red_off) =
   // rows 0..7 of each wave's 32x32 partial (register r < 4 of lane l holds
   // row 4 (l / 32) + r, column l % 32), [wave][bank][r][lane]
-  extern __shared__ __attribute__((aligned(16))) char dsm[];
   half_t* xs = reinterpret_cast<half_t*>(dsm);
-  float* red = reinterpret_cast<float*>(dsm + (size_t)kGemvMaxTokens * xw * 2);
+  float* red = reinterpret_cast<float*>(dsm + p.red_off);
   const int col = lane & 31, khalf = lane >> 5;
   const int nbl = p.N / 32;
-  const int tile = blockIdx.x / nbl, blk = blockIdx.x % nbl;
-
-  // the block count and this tile's entry are read together (the grid only
-  // covers tiles below max_blocks, inside the map's allocation)
-  const int nbm = *p.num_blocks;
-  const int e = p.blocks[3 * tile], row0 = p.blocks[3 * tile + 1], rows = p.blocks[3 * tile + 2];
-  if (tile >= min(nbm, p.max_blocks)) return;
-  // a malformed block map is skipped, never dereferenced out of bounds
-  if (e < 0 || e >= p.E || rows <= 0 || rows > kGemvMaxTokens || row0 < 0 || row0 > p.P - rows)
-    return;
   const int K = p.K, S = K / 64, gpr = K >> p.log2_G;
 
   // packed block of this output block in each bank (chunked layout: 4 KiB
@@ -105,11 +102,16 @@ __global__ __launch_bounds__(64 * kDecWavesMax) void w4_gemv_kernel(const DecPar
       const int m = idx / c8n, c8 = idx % c8n;
       int r = row0 + m;
       if (GATE_UP) {
-        const int pair = p.sorted_pairs[r];
+        const int pair = sorted_pairs[r];
         r = (pair >= 0 && pair < p.P) ? pair / p.top_k : 0;
       }
-      *reinterpret_cast<uint4*>(xs + m * xw + 8 * c8) =
-          *reinterpret_cast<const uint4*>(p.a + (size_t)r * K + 64 * base + 8 * c8);
+      if constexpr (XBF16)
+        *reinterpret_cast<uint4*>(xs + m * xw + 8 * c8) = bf16x8_to_half_interleaved(
+            *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p.a) + (size_t)r * K +
+                                            64 * base + 8 * c8));
+      else
+        *reinterpret_cast<uint4*>(xs + m * xw + 8 * c8) =
+            *reinterpret_cast<const uint4*>(p.a + (size_t)r * K + 64 * base + 8 * c8);
     }
     __syncthreads();
     // 3. dequantise and multiply; MFMA rows past the tile are zero
@@ -154,7 +156,7 @@ __global__ __launch_bounds__(64 * kDecWavesMax) void w4_gemv_kernel(const DecPar
         for (int w2 = 1; w2 < nwaves; w2++) v += red[(w2 * 4 + rr) * 64 + ll];
         v4[c] = v;
       }
-      const int pair = p.sorted_pairs[row0 + m];
+      const int pair = sorted_pairs[row0 + m];
       const float wgt = (pair >= 0 && pair < p.P) ? p.topk_weights[pair] : 0.0f;
       reinterpret_cast<uint3*>(p.out)[((size_t)(row0 + m) * p.N + blk * 32) / 4 + q] =
           pack24x4(wgt * v4[0], wgt * v4[1], wgt * v4[2], wgt * v4[3]);
@@ -176,11 +178,124 @@ __global__ __launch_bounds__(64 * kDecWavesMax) void w4_gemv_kernel(const DecPar
       reinterpret_cast<half_t*>(p.out)[(size_t)(row0 + m) * p.N + (n & ~7) + interleaved_pos(n & 7)] =
           (half_t)silu_mul(v[0], v[NB - 1]);
     } else {
-      const int pair = p.sorted_pairs[row0 + m];
+      const int pair = sorted_pairs[row0 + m];
       const float wgt = (pair >= 0 && pair < p.P) ? p.topk_weights[pair] : 0.0f;
       reinterpret_cast<float*>(p.out)[(size_t)(row0 + m) * p.N + n] = wgt * v[0];
     }
   }
+}
+
+// The grouped GEMM at decode sizes on a device block map: one workgroup per
+// (tile, 32-column block); tiles past the map's count exit.
+template <int MODE, int SPW, bool PACK = false>
+__global__ __launch_bounds__(64 * kDecWavesMax) void w4_gemv_kernel(const DecParams p) {
+  extern __shared__ __attribute__((aligned(16))) char dsm[];
+  const int nbl = p.N / 32;
+  const int tile = blockIdx.x / nbl, blk = blockIdx.x % nbl;
+  // the block count and this tile's entry are read together (the grid only
+  // covers tiles below max_blocks, inside the map's allocation)
+  const int nbm = *p.num_blocks;
+  const int e = p.blocks[3 * tile], row0 = p.blocks[3 * tile + 1], rows = p.blocks[3 * tile + 2];
+  if (tile >= min(nbm, p.max_blocks)) return;
+  // a malformed block map is skipped, never dereferenced out of bounds
+  if (e < 0 || e >= p.E || rows <= 0 || rows > kGemvMaxTokens || row0 < 0 || row0 > p.P - rows)
+    return;
+  gemv_tile<MODE, SPW, PACK, false>(p, p.sorted_pairs, e, row0, rows, blk, dsm);
+}
+
+struct DecRouteParams {
+  const float* logits;  // [ksplit][T][E]
+  float* logits_out;    // [T][E], written when ksplit > 1
+  int ksplit, T;
+  int32_t* ids;
+  float* w;
+  int32_t *counts, *offsets, *sorted_pairs, *pair_slot, *blocks, *num_blocks;
+};
+
+// Decode sizes, S1-S6 in one launch.  Each workgroup first routes the whole
+// batch (at most kGemvMaxTokens tokens, so at most kSmallPairs pairs) into
+// LDS: the summed logits, the top-k of each token by one wave (topk_token:
+// logit descending, lower expert first on ties, softmax over the chosen
+// logits), the expert counts, then S2-S5 by wave 0 (small_build).  Every
+// workgroup gets the same result (same inputs, same operations), so the
+// block map needs no exchange; workgroup 0 writes it, and the rest of the
+// routing, to global memory for the down projection and the caller.  Then
+// the workgroup runs its (tile, 32-column block) of the gate/up GEMV, the
+// activations read from x (bf16) through the LDS scatter.
+// NK = ceil(E / 64) keys per lane in the top-k.
+template <int NK, int SPW>
+__global__ __launch_bounds__(64 * kDecWavesMax) void decode_gate_up_kernel(const DecRouteParams r,
+                                                                          const DecParams p) {
+  extern __shared__ __attribute__((aligned(16))) char dsm[];
+  __shared__ int cnt[256], next[256];
+  __shared__ int32_t ids_s[kSmallPairs], sp_s[kSmallPairs], ps_s[kSmallPairs];
+  __shared__ float w_s[kSmallPairs];
+  __shared__ int32_t off_s[257];
+  __shared__ int32_t blk_s[3 * kSmallMaxBlocks];
+  __shared__ int32_t nb_s[1];
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nwaves = blockDim.x >> 6;
+  const int T = r.T, E = p.E, k = p.top_k, P = p.P;
+  float* lg = reinterpret_cast<float*>(dsm);  // [T][E]; the activation stage reuses the space
+  // 1. logits: partial sums over ranges of H added in range order
+  const size_t part = (size_t)T * E;
+  for (int i = tid; i < T * E; i += blockDim.x) {
+    float v = r.logits[i];
+    for (int z = 1; z < r.ksplit; z++) v += r.logits[z * part + i];
+    lg[i] = v;
+  }
+  for (int i = tid; i < E; i += blockDim.x) cnt[i] = 0;
+  __syncthreads();
+  // 2. top-k and combine weights, a wave per token, with the expert counts
+  for (int t = wave; t < T; t += nwaves) topk_token<NK>(lg + t * E, E, k, ids_s + t * k, w_s + t * k, cnt);
+  __syncthreads();
+  // 3. offsets, scatter and block map
+  if (wave == 0) small_build(ids_s, cnt, next, P, E, kGemvMaxTokens, nullptr, off_s, sp_s, ps_s, blk_s, nb_s);
+  __syncthreads();
+  // 4. workgroup 0 publishes the routing
+  if (blockIdx.x == 0) {
+    for (int i = tid; i < P; i += blockDim.x) {
+      r.ids[i] = ids_s[i];
+      r.w[i] = w_s[i];
+      r.sorted_pairs[i] = sp_s[i];
+      r.pair_slot[i] = ps_s[i];
+    }
+    for (int i = tid; i < E; i += blockDim.x) r.counts[i] = cnt[i];
+    for (int i = tid; i <= E; i += blockDim.x) r.offsets[i] = off_s[i];
+    for (int i = tid; i < 3 * nb_s[0]; i += blockDim.x) r.blocks[i] = blk_s[i];
+    if (tid == 0) r.num_blocks[0] = nb_s[0];
+    if (r.ksplit > 1)
+      for (int i = tid; i < T * E; i += blockDim.x) r.logits_out[i] = lg[i];
+  }
+  __syncthreads();  // lg is overwritten by the activation stage below
+  // 5. this workgroup's tile and column block
+  const int nbl = p.N / 32;
+  const int tile = blockIdx.x / nbl, blk = blockIdx.x % nbl;
+  if (tile >= nb_s[0]) return;
+  gemv_tile<MOE_GEMM_GATE_UP_SWIGLU, SPW, false, true>(p, sp_s, blk_s[3 * tile], blk_s[3 * tile + 1],
+                                                       blk_s[3 * tile + 2], blk, dsm);
+}
+
+// Slabs per wave and waves per workgroup for a launch of `grid` workgroups
+// over reduction length K: four slabs per wave when the grid fills the chip
+// twice over (two 8-wave workgroups per CU overlap one's loads with the
+// other's MFMAs); otherwise two (up to 16 waves, as many bytes in flight per
+// workgroup as possible).
+struct GemvShape {
+  int spw, waves;
+};
+GemvShape gemv_shape(int K, int64_t grid) {
+  const bool wide = K >= 1024 && grid >= 1024;
+  const int spw = wide ? 4 : 2;
+  const int waves = (int)std::max<int64_t>(1, std::min<int64_t>(kDecWavesMax, K / (64 * spw)));
+  return GemvShape{spw, waves};
+}
+
+DecParams dec_params(const GemmArgs& a, int64_t P, int64_t max_blocks, int xs_bytes) {
+  const int log2_G = a.G == 32 ? 5 : a.G == 64 ? 6 : 7;  // G in {32, 64, 128}
+  return DecParams{a.a, a.b0, a.b1, a.sorted_pairs, a.topk_weights, a.blocks, a.num_blocks, a.out,
+                   a.N, a.K, log2_G, a.top_k, a.E, (int)P, (int)max_blocks, xs_bytes};
 }
 
 }  // namespace
@@ -188,20 +303,15 @@ __global__ __launch_bounds__(64 * kDecWavesMax) void w4_gemv_kernel(const DecPar
 hipError_t launch_w4_gemv(const GemmArgs& a, hipStream_t s) {
   const int64_t P = (int64_t)a.T * a.top_k;
   const int64_t max_blocks = P / a.block_m + (P < a.E ? P : a.E);
-  const int log2_G = a.G == 32 ? 5 : a.G == 64 ? 6 : 7;  // G in {32, 64, 128}
-  DecParams p{a.a, a.b0, a.b1, a.sorted_pairs, a.topk_weights, a.blocks, a.num_blocks, a.out,
-              a.N, a.K, log2_G, a.top_k, a.E, (int)P, (int)max_blocks};
   const int64_t grid = max_blocks * (a.N / 32);
-  // Enough workgroups to fill the chip twice over: four slabs per wave (two
-  // 8-wave workgroups per CU overlap one's loads with the other's MFMAs);
-  // otherwise two (up to 16 waves, as many bytes in flight per workgroup as
-  // possible).
-  const bool wide = a.K >= 1024 && grid >= 1024;
-  const int spw = wide ? 4 : 2;
-  const int waves = (int)std::max<int64_t>(1, std::min<int64_t>(kDecWavesMax, a.K / (64 * spw)));
+  const GemvShape sh = gemv_shape(a.K, grid);
+  const bool wide = sh.spw == 4;
   const int nb = a.mode == MOE_GEMM_GATE_UP_SWIGLU ? 2 : 1;
   // LDS: activation rows of one pass + the waves' partial sums
-  const size_t lds = (size_t)kGemvMaxTokens * waves * spw * 64 * 2 + (size_t)waves * nb * 4 * 64 * 4;
+  const int xs_bytes = kGemvMaxTokens * sh.waves * sh.spw * 64 * 2;
+  const size_t lds = (size_t)xs_bytes + (size_t)sh.waves * nb * 4 * 64 * 4;
+  const DecParams p = dec_params(a, P, max_blocks, xs_bytes);
+  const int waves = sh.waves;
   if (a.mode == MOE_GEMM_GATE_UP_SWIGLU) {
     if (wide) w4_gemv_kernel<MOE_GEMM_GATE_UP_SWIGLU, 4><<<grid, 64 * waves, lds, s>>>(p);
     else w4_gemv_kernel<MOE_GEMM_GATE_UP_SWIGLU, 2><<<grid, 64 * waves, lds, s>>>(p);
@@ -211,6 +321,41 @@ hipError_t launch_w4_gemv(const GemmArgs& a, hipStream_t s) {
   } else {
     if (wide) w4_gemv_kernel<MOE_GEMM_DOWN, 4><<<grid, 64 * waves, lds, s>>>(p);
     else w4_gemv_kernel<MOE_GEMM_DOWN, 2><<<grid, 64 * waves, lds, s>>>(p);
+  }
+  return hipGetLastError();
+}
+
+template <int NK>
+static void launch_decode_nk(const DecRouteParams& r, const DecParams& p, bool wide, int64_t grid,
+                             int threads, size_t lds, hipStream_t s) {
+  if (wide) decode_gate_up_kernel<NK, 4><<<grid, threads, lds, s>>>(r, p);
+  else decode_gate_up_kernel<NK, 2><<<grid, threads, lds, s>>>(r, p);
+}
+
+hipError_t launch_decode_gate_up(const DecodeRouting& dr, const GemmArgs& a, hipStream_t s) {
+  if (a.T <= 0) return hipSuccess;
+  if (a.T > kGemvMaxTokens || a.block_m != kGemvMaxTokens || a.E > 256 ||
+      (int64_t)a.T * a.top_k > kSmallPairs)
+    return hipErrorInvalidValue;
+  const int64_t P = (int64_t)a.T * a.top_k;
+  const int64_t max_blocks = P / a.block_m + (P < a.E ? P : a.E);
+  const int64_t grid = max_blocks * (a.N / 32);
+  const GemvShape sh = gemv_shape(a.K, grid);
+  // LDS: the logits, then (reused) the activation rows of one pass; the
+  // waves' partial sums of both banks
+  const int xs_bytes = std::max(kGemvMaxTokens * sh.waves * sh.spw * 64 * 2, a.T * a.E * 4);
+  const int xs_al = (xs_bytes + 15) & ~15;
+  const size_t lds = (size_t)xs_al + (size_t)sh.waves * 2 * 4 * 64 * 4;
+  const DecParams p = dec_params(a, P, max_blocks, xs_al);
+  const DecRouteParams r{dr.logits, dr.logits_out, dr.ksplit, a.T, dr.ids, dr.w, dr.counts,
+                         dr.offsets, dr.sorted_pairs, dr.pair_slot, dr.blocks, dr.num_blocks};
+  const bool wide = sh.spw == 4;
+  const int threads = 64 * sh.waves;
+  switch ((a.E + 63) / 64) {
+    case 1: launch_decode_nk<1>(r, p, wide, grid, threads, lds, s); break;
+    case 2: launch_decode_nk<2>(r, p, wide, grid, threads, lds, s); break;
+    case 3: launch_decode_nk<3>(r, p, wide, grid, threads, lds, s); break;
+    default: launch_decode_nk<4>(r, p, wide, grid, threads, lds, s); break;
   }
   return hipGetLastError();
 }

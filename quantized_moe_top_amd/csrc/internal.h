@@ -90,6 +90,14 @@ __device__ __forceinline__ uint4 bf16x8_to_half_interleaved(uint4 v) {
                     __builtin_bit_cast(uint32_t, o2), __builtin_bit_cast(uint32_t, o3));
 }
 
+// Makes this wave's LDS writes visible to its own later LDS reads (a wave
+// barrier between two workgroup-scope fences).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
 // global_load_lds_dwordx4 / _dword: each lane's 16 (4) bytes at g land in
 // LDS at l + 16 (4) * lane; l must be the same for the whole wave.
 __device__ __forceinline__ void lds_load16(const void* g, char* l) {
@@ -180,15 +188,10 @@ int router_ksplit(int64_t T, int64_t H, int64_t E);
 hipError_t launch_route(const uint16_t* x, const uint16_t* wr, float* logits, int T, int H, int E,
                         int k, int32_t* ids, float* w, half_t* xh, int32_t* chunk_hist,
                         float* part, hipStream_t s);
-// T small enough for one routing chunk: S1 and S2-S5 in one launch (after the
-// router GEMM when wr is given); same outputs as launch_route followed by
-// launch_scan_scatter.
-bool route_build_fused(int64_t T);
-hipError_t launch_route_build(const uint16_t* x, const uint16_t* wr, float* logits, int T, int H,
-                              int E, int k, int32_t* ids, float* w, half_t* xh,
-                              int32_t* chunk_hist, int block_m, int32_t* counts, int32_t* offsets,
-                              int32_t* sorted_pairs, int32_t* pair_slot, int32_t* blocks,
-                              int32_t* num_blocks, float* part, hipStream_t s);
+// S0 alone: the router logits (ksplit == 1) or ksplit partial sums over
+// ranges of H (ksplit == router_ksplit(T, H, E)) into out, [ksplit][T][E].
+hipError_t launch_router_logits(const uint16_t* x, const uint16_t* wr, float* out, int T, int H,
+                                int E, int ksplit, hipStream_t s);
 // Per-chunk expert histogram of caller-given ids [T][k].
 hipError_t launch_chunk_hist(const int32_t* ids, int T, int k, int E, int32_t* chunk_hist,
                              hipStream_t s);
@@ -231,6 +234,23 @@ struct GemmArgs {
 };
 hipError_t launch_w4_mfma(const GemmArgs& a, hipStream_t s);
 hipError_t launch_w4_gemv(const GemmArgs& a, hipStream_t s);
+
+// Decode sizes (T <= kGemvMaxTokens): S1-S5 and S6 in one launch.  Every
+// workgroup routes all T tokens from the logits (ksplit partial sums
+// [ksplit][T][E] added in range order) into LDS and builds the block map
+// there (block_m = kGemvMaxTokens); workgroup 0 also writes the routing
+// outputs (and, when ksplit > 1, the summed logits to logits_out); each
+// workgroup then runs its (tile, 32-column block) of the gate/up GEMV on x
+// (bf16, converted while staged) and writes h.
+struct DecodeRouting {
+  const float* logits;
+  float* logits_out;
+  int ksplit;
+  int32_t *ids;
+  float* w;
+  int32_t *counts, *offsets, *sorted_pairs, *pair_slot, *blocks, *num_blocks;
+};
+hipError_t launch_decode_gate_up(const DecodeRouting& r, const GemmArgs& a, hipStream_t s);
 
 // S8: y[t] = sum_j y_sorted[pair_slot[t * k + j]], j ascending; y_sorted
 // fp32, or packed 24-bit when pack24.

@@ -23,6 +23,7 @@
 //      do not depend on order), and x bf16 -> fp16 in the interleaved order
 //      the grouped GEMM reads.
 #include "scan_scatter.h"
+#include "topk.h"
 
 namespace moe {
 namespace {
@@ -272,117 +273,6 @@ struct RouteParams {
   bool stage_x;         // write xh here (false when the router kernel did)
 };
 
-// Order-preserving map of an fp32 bit pattern onto unsigned integers
-// (-inf lowest, +inf highest).  -0.0 is folded onto +0.0 first: the two
-// compare equal, so they must tie (and the tie goes to the lower expert).
-__device__ __forceinline__ uint32_t ordered_bits(float v) {
-  uint32_t u = __float_as_uint(v);
-  if (u == 0x80000000u) u = 0u;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-__device__ __forceinline__ float readlane_f(float v, int l) {
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
-}
-
-// Top-k of one token by a whole wave (few tokens per chunk: the serial
-// chain of ballots is shorter than the merges of a lane group), the E
-// logits at l[0..E): a 32-round radix select over the order-preserving
-// keys (each round a ballot count of keys at or above the candidate) finds
-// the k-th largest key; keys above it and the lowest-index keys equal to it
-// are the selection; ranks among the selected give (logit descending, index
-// ascending) order.  The wave writes ids[0..k) and w[0..k) and, when
-// hist != nullptr, counts the chosen experts.
-template <int NK>
-__device__ void topk_token(const float* l, int E, int k, int32_t* ids, float* w, int* hist) {
-  const int lane = threadIdx.x & 63;
-  uint32_t key[NK];
-#pragma unroll
-  for (int i = 0; i < NK; i++) {
-    const int e = lane + 64 * i;
-    key[i] = e < E ? ordered_bits(l[e]) : 0u;  // every real key is > 0
-  }
-  // theta = the k-th largest key: the largest value with >= k keys >= it
-  uint32_t theta = 0;
-  for (int b = 31; b >= 0; b--) {
-    const uint32_t cand = theta | (1u << b);
-    int cnt = 0;
-#pragma unroll
-    for (int i = 0; i < NK; i++) cnt += __popcll(__ballot(key[i] >= cand));
-    if (cnt >= k) theta = cand;
-  }
-  // selection: every key above theta, then keys equal to theta by index
-  uint64_t sel[NK];
-  int need = k;
-#pragma unroll
-  for (int i = 0; i < NK; i++) {
-    sel[i] = __ballot(key[i] > theta);
-    need -= __popcll(sel[i]);
-  }
-#pragma unroll
-  for (int i = 0; i < NK; i++) {
-    uint64_t m = __ballot(key[i] == theta);
-    while (need > 0 && m) {
-      const uint64_t low = m & (~m + 1ull);
-      sel[i] |= low;
-      m ^= low;
-      need--;
-    }
-  }
-  // rank of each selected key among the selected ones; the first maximum in
-  // index order is rank 0
-  int rank[NK];
-#pragma unroll
-  for (int i = 0; i < NK; i++) rank[i] = 0;
-  uint32_t best = 0;
-  int best_e = 0;
-#pragma unroll
-  for (int i2 = 0; i2 < NK; i2++) {
-    uint64_t m = sel[i2];
-    while (m) {
-      const int l2 = __ffsll((long long)m) - 1;
-      m &= m - 1;
-      const uint32_t kv = (uint32_t)__builtin_amdgcn_readlane((int)key[i2], l2);
-      const int e2 = 64 * i2 + l2;
-      if (kv > best) {
-        best = kv;
-        best_e = e2;
-      }
-#pragma unroll
-      for (int i = 0; i < NK; i++) {
-        const int e = 64 * i + lane;
-        rank[i] += (kv > key[i]) || (kv == key[i] && e2 < e);
-      }
-    }
-  }
-  // combine weights: softmax over the k chosen logits, max-subtracted, the
-  // denominator summed in rank order
-  const float mx = l[best_e];
-  float a[NK];
-  bool mine[NK];
-#pragma unroll
-  for (int i = 0; i < NK; i++) {
-    mine[i] = (sel[i] >> lane) & 1ull;
-    a[i] = mine[i] ? expf(l[lane + 64 * i] - mx) : 0.0f;
-  }
-  float sum = 0.0f;
-  for (int j = 0; j < k; j++) {
-#pragma unroll
-    for (int i = 0; i < NK; i++) {
-      const uint64_t m = __ballot(mine[i] && rank[i] == j);
-      if (m) sum += readlane_f(a[i], __ffsll((long long)m) - 1);
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < NK; i++) {
-    if (mine[i]) {
-      const int e = lane + 64 * i;
-      ids[rank[i]] = e;
-      w[rank[i]] = a[i] / sum;
-      if (hist) atomicAdd(&hist[e], 1);
-    }
-  }
-}
 
 // Selection key of expert e with logit v: the order-preserving image of v
 // in the high word and ~e in the low word, so a larger key is a larger logit
@@ -616,112 +506,6 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const RouteParams 
 }
 
 // Outputs of S2-S5 for the fused single-chunk kernel.
-struct BuildParams {
-  int block_m;
-  int32_t *counts, *offsets, *sorted_pairs, *pair_slot, *blocks, *num_blocks;
-};
-
-constexpr int kSmallPairs = 8 * 16;  // decode sizes: T <= 8 tokens, k <= 16
-
-// Inclusive prefix sum over the 64 lanes of a wave.
-__device__ __forceinline__ int wave_inclusive_sum(int x) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int v = __shfl_up(x, d);
-    if (lane >= d) x += v;
-  }
-  return x;
-}
-
-// All tokens in one chunk (decode sizes, at most kSmallPairs pairs): one
-// workgroup routes them (S1) and then builds S2-S5 from LDS: the expert
-// counts by LDS atomics, and one wave does the rest, with no block-wide scan:
-//   - exclusive prefix sums over the E <= 256 experts (4 consecutive experts
-//     per lane, then a wave prefix sum): offsets, and the first tile of each
-//     expert for the block map;
-//   - the stable scatter of the pairs in order, 64 at a time: lanes with the
-//     same expert are matched with ballots over the expert-id bits, and a
-//     lane's slot is its expert's next free slot plus the number of matching
-//     lanes below it (the same counting sort as the multi-chunk kernel).
-template <int NK>
-__global__ __launch_bounds__(kRouteThreads) void route_build_kernel(const RouteParams p,
-                                                                    const BuildParams b) {
-  __shared__ int cnt[256];
-  __shared__ int next[256];
-  __shared__ int ids_s[kSmallPairs];
-  route_chunk<true, NK, 64>(p, 0);  // at most 8 tokens: a wave each
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int P = p.T * p.k, E = p.E;
-  if (tid < 256) cnt[tid] = 0;
-  __threadfence_block();
-  __syncthreads();  // ids of every wave visible
-  if (tid < P) {
-    const int id = p.ids[tid];
-    ids_s[tid] = id;
-    if (id >= 0 && id < E) atomicAdd(&cnt[id], 1);
-  }
-  __syncthreads();
-  if (tid >= 64) return;
-  // expert e = 4 lane + i
-  int c[4], tl[4], cs = 0, ts = 0;
-#pragma unroll
-  for (int i = 0; i < 4; i++) {
-    const int e = 4 * lane + i;
-    c[i] = e < E ? cnt[e] : 0;
-    tl[i] = (c[i] + b.block_m - 1) / b.block_m;
-    cs += c[i];
-    ts += tl[i];
-  }
-  int off = wave_inclusive_sum(cs) - cs, tile = wave_inclusive_sum(ts) - ts;
-#pragma unroll
-  for (int i = 0; i < 4; i++) {
-    const int e = 4 * lane + i;
-    if (e < E) {
-      b.counts[e] = c[i];
-      b.offsets[e] = off;
-      next[e] = off;
-      for (int j = 0; j < tl[i]; j++) {
-        int32_t* blk = b.blocks + 3 * (size_t)(tile + j);
-        blk[0] = e;
-        blk[1] = off + j * b.block_m;
-        blk[2] = min(b.block_m, c[i] - j * b.block_m);
-      }
-    }
-    off += c[i];
-    tile += tl[i];
-  }
-  if (lane == 63) {
-    b.offsets[E] = P;
-    b.num_blocks[0] = tile;  // total tiles (inclusive sum of the last lane)
-  }
-  wave_lds_sync();
-  int bits = 1;
-  while ((1 << bits) < E) bits++;
-  for (int base = 0; base < P; base += 64) {
-    const int q = base + lane;
-    const int id = q < P ? ids_s[q] : -1;
-    const bool active = id >= 0 && id < E;
-    const int ex = active ? id : 0;
-    uint64_t match = __ballot(active);
-    for (int bt = 0; bt < bits; bt++) {
-      const bool bit = (ex >> bt) & 1;
-      const uint64_t bal = __ballot(bit);
-      match &= bit ? bal : ~bal;
-    }
-    const uint64_t below = match & ((1ull << lane) - 1ull);
-    const int start = active ? next[ex] : 0;
-    wave_lds_sync();
-    if (active) {
-      const int slot = start + __popcll(below);
-      b.sorted_pairs[slot] = q;
-      b.pair_slot[q] = slot;
-      if (below == 0) next[ex] = start + __popcll(match);  // lowest lane of its group
-    }
-    wave_lds_sync();
-  }
-}
-
 // List length L of the top-k: the power of two in {2, 4, 8, 16} at or above k.
 template <bool FULL, int L>
 void launch_route_group(const RouteParams& p, int nchunks, hipStream_t s) {
@@ -785,30 +569,10 @@ hipError_t launch_route(const uint16_t* x, const uint16_t* wr, float* logits, in
   return xh ? launch_route_l<true>(p, n, s) : launch_route_l<false>(p, n, s);
 }
 
-bool route_build_fused(int64_t T) { return route_chunks(T) == 1; }
-
-hipError_t launch_route_build(const uint16_t* x, const uint16_t* wr, float* logits, int T, int H,
-                              int E, int k, int32_t* ids, float* w, half_t* xh,
-                              int32_t* chunk_hist, int block_m, int32_t* counts, int32_t* offsets,
-                              int32_t* sorted_pairs, int32_t* pair_slot, int32_t* blocks,
-                              int32_t* num_blocks, float* part, hipStream_t s) {
+hipError_t launch_router_logits(const uint16_t* x, const uint16_t* wr, float* out, int T, int H,
+                                int E, int ksplit, hipStream_t s) {
   if (T <= 0) return hipSuccess;
-  const int ks = wr && part ? router_ksplit(T, H, E) : 1;
-  if (wr) {
-    const hipError_t err = launch_router(x, wr, ks > 1 ? part : logits, xh, T, H, E, ks, s);
-    if (err != hipSuccess) return err;
-  }
-  const int ct = route_chunk_tokens(T);
-  RouteParams p{x, ks > 1 ? part : logits, logits, ks, ids, w, xh, chunk_hist, T, H, E, k, ct,
-                route_lpt_log2(ct, E), wr == nullptr};
-  BuildParams b{block_m, counts, offsets, sorted_pairs, pair_slot, blocks, num_blocks};
-  switch ((E + 63) / 64) {
-    case 1: route_build_kernel<1><<<1, kRouteThreads, 0, s>>>(p, b); break;
-    case 2: route_build_kernel<2><<<1, kRouteThreads, 0, s>>>(p, b); break;
-    case 3: route_build_kernel<3><<<1, kRouteThreads, 0, s>>>(p, b); break;
-    default: route_build_kernel<4><<<1, kRouteThreads, 0, s>>>(p, b); break;
-  }
-  return hipGetLastError();
+  return launch_router(x, wr, out, nullptr, T, H, E, ksplit, s);
 }
 
 }  // namespace moe

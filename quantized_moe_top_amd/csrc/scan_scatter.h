@@ -28,12 +28,6 @@ __device__ int block_exclusive_scan(int v, int* tmp) {
   return incl - v;
 }
 
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-}
-
 // One workgroup of kScanThreads threads, chunk c of nchunks: see
 // build_blocks.hip for the algorithm.  With chunk_start (nchunks x E, the
 // first slot of chunk c's pairs of expert e, computed elsewhere) only the

@@ -332,7 +332,7 @@ def test_ffn_k_equals_e_and_k1(orc):
 def test_ffn_router_split(orc):
     """Router weight at small T: the router sums ranges of H separately (8 or
     4 ranges here) and the routing kernel adds them; decode sizes take the
-    one-launch routing + block map path."""
+    path whose gate/up launch also routes and builds the block map."""
     for (T, H, E, k) in [(5, 2048, 128, 8), (100, 1024, 64, 4), (3, 512, 200, 6)]:
         lay = synth.make_custom(T=T, H=H, I=256, E=E, k=k, G=64, seed=40 + T, router="weight")
         y, info = api.ffn_forward(on_dev(lay), info=True)
@@ -341,7 +341,7 @@ def test_ffn_router_split(orc):
 
 
 def test_ffn_decode_edges(orc):
-    """Decode sizes (one-workgroup routing and block map): the most pairs it
+    """Decode sizes (routing and block map inside the gate/up launch): the most pairs it
     takes (T = 8, k = 16), one expert chosen of two, and an odd E."""
     for (T, E, k) in [(8, 256, 16), (1, 2, 1), (7, 5, 3)]:
         lay = synth.make_custom(T=T, H=256, I=128, E=E, k=k, G=32, seed=50 + T + E)
