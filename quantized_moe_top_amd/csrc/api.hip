@@ -461,11 +461,18 @@ int ffn_forward_impl(const moe_layer* layer, const uint16_t* x, const float* rou
   if (!gemv) err = moe::launch_w4_mfma(g1, s);
   if (err != hipSuccess) return hip_status(err, "gate_up");
   if ((err = mark(events, MOE_STAGE_DOWN, s)) != hipSuccess) return hip_status(err, "event");
-  err = gemv ? moe::launch_w4_gemv(g2, s) : moe::launch_w4_mfma(g2, s);
-  if (err != hipSuccess) return hip_status(err, "down");
-  if ((err = mark(events, MOE_STAGE_COMBINE, s)) != hipSuccess) return hip_status(err, "event");
-  if ((err = moe::launch_combine(y_sorted, !gemv, pair_slot, y, d.T, d.H, d.top_k, s)) != hipSuccess)
-    return hip_status(err, "combine");
+  if (gemv && moe::decode_down_fused(d.I)) {
+    // decode sizes: the down GEMV and the combine in one launch, per token
+    // (the combine stage is empty)
+    if ((err = moe::launch_decode_down(g2, ids, pair_slot, y, s)) != hipSuccess) return hip_status(err, "down");
+    if ((err = mark(events, MOE_STAGE_COMBINE, s)) != hipSuccess) return hip_status(err, "event");
+  } else {
+    err = gemv ? moe::launch_w4_gemv(g2, s) : moe::launch_w4_mfma(g2, s);
+    if (err != hipSuccess) return hip_status(err, "down");
+    if ((err = mark(events, MOE_STAGE_COMBINE, s)) != hipSuccess) return hip_status(err, "event");
+    if ((err = moe::launch_combine(y_sorted, !gemv, pair_slot, y, d.T, d.H, d.top_k, s)) != hipSuccess)
+      return hip_status(err, "combine");
+  }
   if ((err = mark(events, MOE_NUM_STAGES, s)) != hipSuccess) return hip_status(err, "event");
   return ok();
 }

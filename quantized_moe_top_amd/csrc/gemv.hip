@@ -251,7 +251,8 @@ __global__ __launch_bounds__(64 * kDecWavesMax) void decode_gate_up_kernel(const
   for (int t = wave; t < T; t += nwaves) topk_token<NK>(lg + t * E, E, k, ids_s + t * k, w_s + t * k, cnt);
   __syncthreads();
   // 3. offsets, scatter and block map
-  if (wave == 0) small_build(ids_s, cnt, next, P, E, kGemvMaxTokens, nullptr, off_s, sp_s, ps_s, blk_s, nb_s);
+  if (wave == 0) small_build(ids_s, cnt, next, P, E, kGemvMaxTokens, nullptr, off_s, sp_s, ps_s, blk_s, nb_s,
+                              min(p.max_blocks, kSmallMaxBlocks));
   __syncthreads();
   // 4. workgroup 0 publishes the routing
   if (blockIdx.x == 0) {
@@ -269,12 +270,131 @@ __global__ __launch_bounds__(64 * kDecWavesMax) void decode_gate_up_kernel(const
       for (int i = tid; i < T * E; i += blockDim.x) r.logits_out[i] = lg[i];
   }
   __syncthreads();  // lg is overwritten by the activation stage below
-  // 5. this workgroup's tile and column block
+  // 5. the (tile, column block) items of this workgroup: blockIdx.x, then
+  //    every gridDim.x-th after it (the grid is at most what the chip holds
+  //    at once, so the routing above runs once per workgroup)
   const int nbl = p.N / 32;
-  const int tile = blockIdx.x / nbl, blk = blockIdx.x % nbl;
-  if (tile >= nb_s[0]) return;
-  gemv_tile<MOE_GEMM_GATE_UP_SWIGLU, SPW, false, true>(p, sp_s, blk_s[3 * tile], blk_s[3 * tile + 1],
-                                                       blk_s[3 * tile + 2], blk, dsm);
+  const int items = nb_s[0] * nbl;
+  for (int it = blockIdx.x; it < items; it += gridDim.x) {
+    const int tile = it / nbl, blk = it % nbl;
+    gemv_tile<MOE_GEMM_GATE_UP_SWIGLU, SPW, false, true>(p, sp_s, blk_s[3 * tile], blk_s[3 * tile + 1],
+                                                         blk_s[3 * tile + 2], blk, dsm);
+  }
+}
+
+// Decode sizes, S7 and S8 in one launch, organised per token: workgroup
+// (t, 16-column block) computes d_j = h[t, j] . dq(Wd_e)^T over the block
+// for each of the token's k choices (e = its expert, h row at its slot),
+// then y[t] = sum_j w[t, j] * d_j in choice order, and also writes each
+// weighted row w[t, j] * d_j to y_sorted at the slot.  No other workgroup
+// contributes to its outputs, so there is no cross-workgroup exchange; an
+// expert chosen by several tokens of the batch is read once per token (the
+// later reads mostly hit the L2 or the last-level cache).
+// One wave per 64-wide slab of the reduction (K <= 64 * kDecWavesMax, one
+// pass); the choices go in chunks of kDownChunk, all weight loads of a chunk
+// issued at once.  Each d_j runs on v_mfma_f32_16x16x32_f16 (two per slab)
+// with h in MFMA row 0 (zeros elsewhere).  Lane l takes column l % 16 of
+// the block and the 8-byte half q = (l / 16) % 2 of the packed 16-byte unit
+// (column, reduction half (l / 32)): its two words feed the two MFMAs, so
+// MFMA m of a slab covers, for lane group (l / 16), reduction indices
+// 32 (l / 32) + 16 q + 8 m + [0, 8), and the h fragment is read to match.
+// The waves' row-0 partials meet in LDS and are added in wave order.  The
+// weighting and the sum are plain fp32 multiplies and adds (no
+// contraction), so y equals the fp32 sum in choice order of the y_sorted
+// rows exactly.
+constexpr int kDownChunk = 8;
+
+__global__ __launch_bounds__(64 * kDecWavesMax) void decode_down_kernel(
+    const DecParams p, const int32_t* __restrict__ ids, const int32_t* __restrict__ pair_slot,
+    float* __restrict__ y) {
+  extern __shared__ __attribute__((aligned(16))) char dsm[];
+  __shared__ int e_s[16], slot_s[16];
+  __shared__ float w_s[16], v_s[16 * 16];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nwaves = blockDim.x >> 6;
+  const int nbl = p.N / 32, nb16 = p.N / 16;
+  const int t = blockIdx.x / nb16, b16 = blockIdx.x % nb16;
+  const int K = p.K, S = K / 64, gpr = K >> p.log2_G, k = p.top_k;
+  const int c = lane & 15, lg = lane >> 4, khalf = lg >> 1, qh = lg & 1;
+  const int col = 16 * (b16 & 1) + c;  // column within the 32-column packed block
+  // LDS: xs = the h rows of a chunk [kDownChunk][K] (operand order); red
+  // (at red_off) = row 0 of each wave's partial per choice [wave][k][16]
+  half_t* xs = reinterpret_cast<half_t*>(dsm);
+  float* red = reinterpret_cast<float*>(dsm + p.red_off);
+  // the token's choices: expert, slot and combine weight, read once (a
+  // malformed id is replaced by 0 and a malformed slot skipped, never used
+  // out of bounds)
+  if (tid < k) {
+    const int pair = t * k + tid;
+    const int e = ids[pair], slot = pair_slot[pair];
+    e_s[tid] = (e >= 0 && e < p.E) ? e : 0;
+    slot_s[tid] = (slot >= 0 && slot < p.P) ? slot : -1;
+    w_s[tid] = p.topk_weights[pair];
+  }
+  __syncthreads();
+  const int s = wave;  // this wave's slab (nwaves == S)
+  const int g = (64 * s + 32 * khalf) >> p.log2_G;
+  for (int j0 = 0; j0 < k; j0 += kDownChunk) {
+    const int nj = min(kDownChunk, k - j0);
+    // 1. codes (two words) and (scale, bias) word of every choice of the chunk
+    uint2 q[kDownChunk];
+    uint32_t sb[kDownChunk];
+#pragma unroll
+    for (int j = 0; j < kDownChunk; j++) {
+      const int e = j < nj ? e_s[j0 + j] : 0;
+      const size_t bidx = (size_t)e * nbl + (b16 >> 1);
+      q[j] = *reinterpret_cast<const uint2*>(p.b0.words + ((bidx >> 2) * S * 4 + (bidx & 3)) * 256 +
+                                             4 * (2 * col + khalf) + 2 * qh + (size_t)s * 1024);
+      sb[j] = p.b0.sb[(bidx >> 2) * gpr * 128 + (bidx & 3) * 32 + col + (size_t)g * 128];
+    }
+    // 2. the chunk's h rows into LDS, 16 bytes per thread and step
+    const int c8n = K / 8;
+    for (int idx = tid; idx < nj * c8n; idx += blockDim.x) {
+      const int m = idx / c8n, c8 = idx % c8n;
+      const int slot = max(slot_s[j0 + m], 0);
+      *reinterpret_cast<uint4*>(xs + m * K + 8 * c8) =
+          *reinterpret_cast<const uint4*>(p.a + (size_t)slot * K + 8 * c8);
+    }
+    __syncthreads();
+    // 3. per choice: dequantise, multiply, keep row 0
+#pragma unroll
+    for (int j = 0; j < kDownChunk; j++) {
+      if (j >= nj) break;
+      floatx4_t acc = floatx4_t{};
+      half2_t s2, b2;
+      sb_pairs(sb[j], s2, b2);
+#pragma unroll
+      for (int m = 0; m < 2; m++) {
+        const u32x4 x = c == 0 ? *reinterpret_cast<const u32x4*>(xs + j * K + 64 * s + 32 * khalf + 16 * qh + 8 * m)
+                               : u32x4{0, 0, 0, 0};
+        const uint4 d = dequant_word(m == 0 ? q[j].x : q[j].y, s2, b2);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, x),
+                                                     __builtin_bit_cast(half8_t, d), acc, 0, 0, 0);
+      }
+      if (lane < 16) red[(wave * k + j0 + j) * 16 + lane] = acc[0];
+    }
+    __syncthreads();  // the next chunk overwrites xs
+  }
+  // 4. the weighted rows (one thread per choice and column), then their sum
+  //    in choice order
+  {
+#pragma clang fp contract(off)
+    for (int i = tid; i < k * 16; i += blockDim.x) {
+      const int j = i >> 4, cc = i & 15;
+      float d = red[j * 16 + cc];
+      for (int w2 = 1; w2 < nwaves; w2++) d += red[(w2 * k + j) * 16 + cc];
+      const float v = w_s[j] * d;
+      v_s[i] = v;
+      if (slot_s[j] >= 0) reinterpret_cast<float*>(p.out)[(size_t)slot_s[j] * p.N + b16 * 16 + cc] = v;
+    }
+    __syncthreads();
+    if (tid < 16) {
+      float acc = 0.0f;
+      for (int j = 0; j < k; j++) acc = acc + v_s[j * 16 + tid];
+      y[(size_t)t * p.N + b16 * 16 + tid] = acc;
+    }
+  }
 }
 
 // Slabs per wave and waves per workgroup for a launch of `grid` workgroups
@@ -325,6 +445,19 @@ hipError_t launch_w4_gemv(const GemmArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static int cus[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cus[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
 template <int NK>
 static void launch_decode_nk(const DecRouteParams& r, const DecParams& p, bool wide, int64_t grid,
                              int threads, size_t lds, hipStream_t s) {
@@ -339,24 +472,45 @@ hipError_t launch_decode_gate_up(const DecodeRouting& dr, const GemmArgs& a, hip
     return hipErrorInvalidValue;
   const int64_t P = (int64_t)a.T * a.top_k;
   const int64_t max_blocks = P / a.block_m + (P < a.E ? P : a.E);
-  const int64_t grid = max_blocks * (a.N / 32);
-  const GemvShape sh = gemv_shape(a.K, grid);
+  const int64_t max_items = max_blocks * (a.N / 32);
+  const GemvShape sh = gemv_shape(a.K, max_items);
   // LDS: the logits, then (reused) the activation rows of one pass; the
   // waves' partial sums of both banks
   const int xs_bytes = std::max(kGemvMaxTokens * sh.waves * sh.spw * 64 * 2, a.T * a.E * 4);
   const int xs_al = (xs_bytes + 15) & ~15;
   const size_t lds = (size_t)xs_al + (size_t)sh.waves * 2 * 4 * 64 * 4;
   const DecParams p = dec_params(a, P, max_blocks, xs_al);
-  const DecRouteParams r{dr.logits, dr.logits_out, dr.ksplit, a.T, dr.ids, dr.w, dr.counts,
-                         dr.offsets, dr.sorted_pairs, dr.pair_slot, dr.blocks, dr.num_blocks};
+  const DecRouteParams r{dr.logits, dr.logits_out, dr.ksplit, a.T,
+                         dr.ids, dr.w, dr.counts, dr.offsets, dr.sorted_pairs, dr.pair_slot,
+                         dr.blocks, dr.num_blocks};
   const bool wide = sh.spw == 4;
   const int threads = 64 * sh.waves;
+  // at most one round of workgroups (4 waves per SIMD, LDS permitting):
+  // the routing then runs once per workgroup
+  const int per_cu = std::max(1, std::min<int>(16 / sh.waves, (int)((160 * 1024) / (lds + 8 * 1024))));
+  const int64_t grid = std::min<int64_t>(max_items, (int64_t)device_cus() * per_cu);
   switch ((a.E + 63) / 64) {
     case 1: launch_decode_nk<1>(r, p, wide, grid, threads, lds, s); break;
     case 2: launch_decode_nk<2>(r, p, wide, grid, threads, lds, s); break;
     case 3: launch_decode_nk<3>(r, p, wide, grid, threads, lds, s); break;
     default: launch_decode_nk<4>(r, p, wide, grid, threads, lds, s); break;
   }
+  return hipGetLastError();
+}
+
+bool decode_down_fused(int K) { return K % 64 == 0 && K / 64 <= kDecWavesMax; }
+
+hipError_t launch_decode_down(const GemmArgs& a, const int32_t* ids, const int32_t* pair_slot,
+                              float* y, hipStream_t s) {
+  if (a.T <= 0) return hipSuccess;
+  if (a.T > kGemvMaxTokens || !decode_down_fused(a.K)) return hipErrorInvalidValue;
+  const int64_t P = (int64_t)a.T * a.top_k;
+  const int64_t grid = (int64_t)a.T * (a.N / 16);
+  const int waves = a.K / 64;
+  const int xs_bytes = kDownChunk * a.K * 2;
+  const size_t lds = (size_t)xs_bytes + (size_t)waves * a.top_k * 16 * 4;
+  const DecParams p = dec_params(a, P, 0, xs_bytes);
+  decode_down_kernel<<<grid, 64 * waves, lds, s>>>(p, ids, pair_slot, y);
   return hipGetLastError();
 }
 

@@ -251,6 +251,12 @@ struct DecodeRouting {
   int32_t *counts, *offsets, *sorted_pairs, *pair_slot, *blocks, *num_blocks;
 };
 hipError_t launch_decode_gate_up(const DecodeRouting& r, const GemmArgs& a, hipStream_t s);
+// Decode sizes: S7 and S8 in one launch, per token (a.a: h; a.out: y_sorted
+// fp32 [T * k][N], written too; ids, pair_slot: [T * k]; y: [T][N]).  Needs
+// decode_down_fused(K): a reduction of at most 16 slabs of 64.
+bool decode_down_fused(int K);
+hipError_t launch_decode_down(const GemmArgs& a, const int32_t* ids, const int32_t* pair_slot,
+                              float* y, hipStream_t s);
 
 // S8: y[t] = sum_j y_sorted[pair_slot[t * k + j]], j ascending; y_sorted
 // fp32, or packed 24-bit when pack24.

@@ -25,18 +25,37 @@ __device__ __forceinline__ uint32_t ordered_bits(float v) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ __forceinline__ float readlane_f(float v, int l) {
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+// Inverse of ordered_bits (-0.0 comes back as +0.0).
+__device__ __forceinline__ float ordered_value(uint32_t u) {
+  return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
 }
 
-// Top-k of one token by a whole wave (few tokens per chunk: the serial
-// chain of ballots is shorter than the merges of a lane group), the E
-// logits at l[0..E): a 32-round radix select over the order-preserving
-// keys (each round a ballot count of keys at or above the candidate) finds
-// the k-th largest key; keys above it and the lowest-index keys equal to it
-// are the selection; ranks among the selected give (logit descending, index
-// ascending) order.  The wave writes ids[0..k) and w[0..k) and, when
-// hist != nullptr, counts the chosen experts.
+// Largest value over the 64 lanes of a wave, returned to every lane, on DPP
+// lane moves: two quad permutations and two row rotations give each 16-lane
+// row its maximum, then two row broadcasts combine rows 0-1 into lane 31
+// and all rows into lane 63, which is read out.  Lanes a broadcast does not
+// reach compare against 0, the smallest value.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#define MOE_DPP_MAX(ctrl, row_mask) \
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, ctrl, row_mask, 0xF, false))
+  MOE_DPP_MAX(0xB1, 0xF);   // quad_perm 1,0,3,2
+  MOE_DPP_MAX(0x4E, 0xF);   // quad_perm 2,3,0,1
+  MOE_DPP_MAX(0x124, 0xF);  // row_ror:4
+  MOE_DPP_MAX(0x128, 0xF);  // row_ror:8
+  MOE_DPP_MAX(0x142, 0xA);  // row_bcast:15 -> rows 1, 3
+  MOE_DPP_MAX(0x143, 0xC);  // row_bcast:31 -> rows 2, 3
+#undef MOE_DPP_MAX
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// Top-k of one token by a whole wave, the E logits at l[0..E), k <= 64:
+// k rounds, each taking the largest remaining order-preserving key (a wave
+// maximum) and, among the keys equal to it, the lowest expert index, so the
+// choices come out in (logit descending, index ascending) order.  Lane j < k
+// keeps choice j.  The combine weights are a softmax over the k chosen
+// logits, shifted by the largest, the denominator summed in rank order.
+// The wave writes ids[0..k) and w[0..k) and, when hist != nullptr, counts
+// the chosen experts.
 template <int NK>
 __device__ void topk_token(const float* l, int E, int k, int32_t* ids, float* w, int* hist) {
   const int lane = threadIdx.x & 63;
@@ -46,96 +65,50 @@ __device__ void topk_token(const float* l, int E, int k, int32_t* ids, float* w,
     const int e = lane + 64 * i;
     key[i] = e < E ? ordered_bits(l[e]) : 0u;  // every real key is > 0
   }
-  // theta = the k-th largest key: the largest value with >= k keys >= it
-  uint32_t theta = 0;
-  for (int b = 31; b >= 0; b--) {
-    const uint32_t cand = theta | (1u << b);
-    int cnt = 0;
-#pragma unroll
-    for (int i = 0; i < NK; i++) cnt += __popcll(__ballot(key[i] >= cand));
-    if (cnt >= k) theta = cand;
-  }
-  // selection: every key above theta, then keys equal to theta by index
-  uint64_t sel[NK];
-  int need = k;
-#pragma unroll
-  for (int i = 0; i < NK; i++) {
-    sel[i] = __ballot(key[i] > theta);
-    need -= __popcll(sel[i]);
-  }
-#pragma unroll
-  for (int i = 0; i < NK; i++) {
-    uint64_t m = __ballot(key[i] == theta);
-    while (need > 0 && m) {
-      const uint64_t low = m & (~m + 1ull);
-      sel[i] |= low;
-      m ^= low;
-      need--;
-    }
-  }
-  // rank of each selected key among the selected ones; the first maximum in
-  // index order is rank 0
-  int rank[NK];
-#pragma unroll
-  for (int i = 0; i < NK; i++) rank[i] = 0;
-  uint32_t best = 0;
-  int best_e = 0;
-#pragma unroll
-  for (int i2 = 0; i2 < NK; i2++) {
-    uint64_t m = sel[i2];
-    while (m) {
-      const int l2 = __ffsll((long long)m) - 1;
-      m &= m - 1;
-      const uint32_t kv = (uint32_t)__builtin_amdgcn_readlane((int)key[i2], l2);
-      const int e2 = 64 * i2 + l2;
-      if (kv > best) {
-        best = kv;
-        best_e = e2;
-      }
-#pragma unroll
-      for (int i = 0; i < NK; i++) {
-        const int e = 64 * i + lane;
-        rank[i] += (kv > key[i]) || (kv == key[i] && e2 < e);
-      }
-    }
-  }
-  // combine weights: softmax over the k chosen logits, max-subtracted, the
-  // denominator summed in rank order
-  const float mx = l[best_e];
-  float a[NK];
-  bool mine[NK];
-#pragma unroll
-  for (int i = 0; i < NK; i++) {
-    mine[i] = (sel[i] >> lane) & 1ull;
-    a[i] = mine[i] ? expf(l[lane + 64 * i] - mx) : 0.0f;
-  }
-  float sum = 0.0f;
+  uint32_t kj = 0, m0 = 0;  // lane j < k: the j-th chosen key; m0: the largest
+  int ej = 0;               // lane j < k: the j-th chosen expert
   for (int j = 0; j < k; j++) {
+    uint32_t m = key[0];
+#pragma unroll
+    for (int i = 1; i < NK; i++) m = max(m, key[i]);
+    m = wave_max_u32(m);
+    int owner = -1;
 #pragma unroll
     for (int i = 0; i < NK; i++) {
-      const uint64_t m = __ballot(mine[i] && rank[i] == j);
-      if (m) sum += readlane_f(a[i], __ffsll((long long)m) - 1);
+      const uint64_t b = __ballot(key[i] == m);
+      if (owner < 0 && b) owner = 64 * i + __ffsll((long long)b) - 1;
+    }
+#pragma unroll
+    for (int i = 0; i < NK; i++)
+      if (lane + 64 * i == owner) key[i] = 0u;  // taken
+    if (j == 0) m0 = m;
+    if (lane == j) {
+      kj = m;
+      ej = owner;
     }
   }
-#pragma unroll
-  for (int i = 0; i < NK; i++) {
-    if (mine[i]) {
-      const int e = lane + 64 * i;
-      ids[rank[i]] = e;
-      w[rank[i]] = a[i] / sum;
-      if (hist) atomicAdd(&hist[e], 1);
-    }
+  const float mx = ordered_value(m0);
+  const float a = lane < k ? expf(ordered_value(kj) - mx) : 0.0f;
+  float sum = 0.0f;
+  for (int j = 0; j < k; j++) sum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), j));
+  if (lane < k) {
+    ids[lane] = ej;
+    w[lane] = a / sum;
+    if (hist) atomicAdd(&hist[ej], 1);
   }
 }
 
-// Inclusive prefix sum over the 64 lanes of a wave.
+// Inclusive prefix sum over the 64 lanes of a wave, on DPP lane moves: four
+// row shifts build the sums inside each 16-lane row, then two row broadcasts
+// carry lane 15's total into row 1 (and lane 47's into row 3), and lane
+// 31's into rows 2 and 3.  Lanes a move does not reach add 0.
 __device__ __forceinline__ int wave_inclusive_sum(int x) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int v = __shfl_up(x, d);
-    if (lane >= d) x += v;
-  }
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15 -> rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31 -> rows 2, 3
   return x;
 }
 
@@ -143,7 +116,8 @@ __device__ __forceinline__ int wave_inclusive_sum(int x) {
 // caller runs it on one wave only), with no block-wide scan.  ids: the P
 // expert ids in pair order; cnt: the E expert counts (LDS, both filled by
 // the caller); next: LDS scratch of E ints.  Outputs through generic
-// pointers (LDS or global), counts only when non-null:
+// pointers (LDS or global), counts only when non-null; no block-map entry
+// at or past max_tiles (and no slot past P) is written:
 //   - exclusive prefix sums over the E <= 256 experts (4 consecutive experts
 //     per lane, then a wave prefix sum): offsets, and the first tile of each
 //     expert for the block map;
@@ -153,7 +127,8 @@ __device__ __forceinline__ int wave_inclusive_sum(int x) {
 //     lanes below it (a counting sort that keeps pair order in each expert).
 __device__ __forceinline__ void small_build(const int32_t* ids, const int* cnt, int* next, int P, int E,
                                             int block_m, int32_t* counts, int32_t* offsets, int32_t* sorted_pairs,
-                                            int32_t* pair_slot, int32_t* blocks, int32_t* num_blocks) {
+                                            int32_t* pair_slot, int32_t* blocks, int32_t* num_blocks,
+                                            int max_tiles) {
   const int lane = threadIdx.x & 63;
   // expert e = 4 lane + i
   int c[4], tl[4], cs = 0, ts = 0;
@@ -173,7 +148,7 @@ __device__ __forceinline__ void small_build(const int32_t* ids, const int* cnt, 
       if (counts) counts[e] = c[i];
       offsets[e] = off;
       next[e] = off;
-      for (int j = 0; j < tl[i]; j++) {
+      for (int j = 0; j < tl[i] && tile + j < max_tiles; j++) {
         int32_t* blk = blocks + 3 * (size_t)(tile + j);
         blk[0] = e;
         blk[1] = off + j * block_m;
@@ -185,7 +160,7 @@ __device__ __forceinline__ void small_build(const int32_t* ids, const int* cnt, 
   }
   if (lane == 63) {
     offsets[E] = P;
-    num_blocks[0] = tile;  // total tiles (inclusive sum of the last lane)
+    num_blocks[0] = min(tile, max_tiles);  // total tiles (inclusive sum of the last lane)
   }
   wave_lds_sync();
   int bits = 1;
@@ -204,8 +179,8 @@ __device__ __forceinline__ void small_build(const int32_t* ids, const int* cnt, 
     const uint64_t below = match & ((1ull << lane) - 1ull);
     const int start = active ? next[ex] : 0;
     wave_lds_sync();
-    if (active) {
-      const int slot = start + __popcll(below);
+    const int slot = start + __popcll(below);
+    if (active && slot < P) {
       sorted_pairs[slot] = q;
       pair_slot[q] = slot;
       if (below == 0) next[ex] = start + __popcll(match);  // lowest lane of its group
