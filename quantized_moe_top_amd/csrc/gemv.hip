@@ -185,6 +185,159 @@ __device__ __forceinline__ void gemv_tile(const DecParams& p, const int32_t* sor
   }
 }
 
+// The gate/up product of one (tile, 16-column block), on
+// v_mfma_f32_16x16x32_f16, for the fused decode launch: tile rows [row0,
+// row0 + rows) of expert e (rows <= kGemvMaxTokens), output columns
+// [16 b16, 16 b16 + 16) of both banks, then h = silu(gate) * up.  Lane l
+// takes column l % 16 of the block and the 8-byte half q = (l / 16) % 2 of
+// the packed 16-byte unit (column, reduction half (l / 32)): its two words
+// feed the two MFMAs of a slab, so MFMA m covers, for lane group (l / 16),
+// reduction indices 32 (l / 32) + 16 q + 8 m + [0, 8) of the slab, and the
+// activation fragment of tile row l % 16 is read to match (zeros past the
+// tile).  SPW slabs per wave and pass; x is staged from bf16 as in
+// gemv_tile.  The waves' partials (rows 0..7: lanes 0..31, registers 0..3)
+// meet in LDS at red_off and are added in wave order.
+// This wave's packed codes (two words per bank and slab) and (scale, bias)
+// words for one pass (slabs base + SPW wave + [0, SPW); slabs past the end
+// reload the last one and are not multiplied).
+template <int SPW>
+struct Frag16 {
+  uint2 q[2][SPW];
+  uint32_t sb[2][SPW];
+};
+
+template <int SPW>
+__device__ __forceinline__ Frag16<SPW> g16_load(const DecParams& p, int e, int b16, int base) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = lane & 15, lg = lane >> 4, khalf = lg >> 1, qh = lg & 1;
+  const int col = 16 * (b16 & 1) + c;  // column within the 32-column packed block
+  const int S = p.K / 64, gpr = p.K >> p.log2_G;
+  const size_t bidx = (size_t)e * (p.N / 32) + (b16 >> 1);
+  Frag16<SPW> f;
+#pragma unroll
+  for (int b = 0; b < 2; b++) {
+    const moe_w4_packed& bank = b == 0 ? p.b0 : p.b1;
+    const uint32_t* wsrc = bank.words + ((bidx >> 2) * S * 4 + (bidx & 3)) * 256 + 4 * (2 * col + khalf) + 2 * qh;
+    const uint32_t* ssrc = bank.sb + (bidx >> 2) * gpr * 128 + (bidx & 3) * 32 + col;
+#pragma unroll
+    for (int j = 0; j < SPW; j++) {
+      const int s = min(base + SPW * wave + j, S - 1);
+      f.q[b][j] = *reinterpret_cast<const uint2*>(wsrc + (size_t)s * 1024);
+      f.sb[b][j] = ssrc[(size_t)((64 * s + 32 * khalf) >> p.log2_G) * 128];
+    }
+  }
+  return f;
+}
+
+// The tile's x rows for one pass into LDS (bf16 -> fp16 operand order); the
+// caller synchronises before they are read.
+template <int SPW>
+__device__ __forceinline__ void g16_stage(const DecParams& p, const int32_t* sorted_pairs, int row0,
+                                          int rows, int base, char* dsm) {
+  const int pass_slabs = (blockDim.x >> 6) * SPW, xw = pass_slabs * 64;
+  half_t* xs = reinterpret_cast<half_t*>(dsm);
+  const int nsl = min(pass_slabs, p.K / 64 - base);
+  const int c8n = nsl * 8;
+  for (int idx = threadIdx.x; idx < rows * c8n; idx += blockDim.x) {
+    const int m = idx / c8n, c8 = idx % c8n;
+    const int pair = sorted_pairs[row0 + m];
+    const int r = (pair >= 0 && pair < p.P) ? pair / p.top_k : 0;
+    *reinterpret_cast<uint4*>(xs + m * xw + 8 * c8) = bf16x8_to_half_interleaved(
+        *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p.a) + (size_t)r * p.K +
+                                        64 * base + 8 * c8));
+  }
+}
+
+// Dequantise this wave's fragments of one pass and multiply them with the
+// staged rows (zeros past the tile) into acc.
+template <int SPW>
+__device__ __forceinline__ void g16_mma(const DecParams& p, const Frag16<SPW>& f, int rows, int base,
+                                        floatx4_t (&acc)[2], const char* dsm) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int pass_slabs = (blockDim.x >> 6) * SPW, xw = pass_slabs * 64;
+  const half_t* xs = reinterpret_cast<const half_t*>(dsm);
+  const int c = lane & 15, lg = lane >> 4, khalf = lg >> 1, qh = lg & 1;
+#pragma unroll
+  for (int j = 0; j < SPW; j++) {
+    const int sl = SPW * wave + j;
+    if (base + sl >= p.K / 64) break;  // uniform per wave
+    u32x4 x[2];
+#pragma unroll
+    for (int m = 0; m < 2; m++)
+      x[m] = c < rows ? *reinterpret_cast<const u32x4*>(xs + c * xw + 64 * sl + 32 * khalf + 16 * qh + 8 * m)
+                      : u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int b = 0; b < 2; b++) {
+      half2_t s2, b2;
+      sb_pairs(f.sb[b][j], s2, b2);
+#pragma unroll
+      for (int m = 0; m < 2; m++) {
+        const uint4 d = dequant_word(m == 0 ? f.q[b][j].x : f.q[b][j].y, s2, b2);
+        acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, x[m]),
+                                                        __builtin_bit_cast(half8_t, d), acc[b], 0, 0, 0);
+      }
+    }
+  }
+}
+
+// The waves' partials (rows 0..7: lanes 0..31, registers 0..3) meet in LDS
+// at red_off and are added in wave order; h = silu(gate) * up in operand
+// order.  Ends with a barrier (the LDS is reused by the next item).
+__device__ __forceinline__ void g16_epilogue(const DecParams& p, const floatx4_t (&acc)[2], int row0,
+                                             int rows, int b16, char* dsm) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nwaves = blockDim.x >> 6;
+  float* red = reinterpret_cast<float*>(dsm + p.red_off);
+  if (lane < 32)
+#pragma unroll
+    for (int b = 0; b < 2; b++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) red[((wave * 2 + b) * 4 + i) * 32 + lane] = acc[b][i];
+  __syncthreads();
+  for (int t = tid; t < rows * 16; t += blockDim.x) {
+    const int m = t >> 4, cc = t & 15;
+    const int rr = m & 3, ll = cc + 16 * (m >> 2);
+    float v[2];
+#pragma unroll
+    for (int b = 0; b < 2; b++) {
+      v[b] = red[(b * 4 + rr) * 32 + ll];
+      for (int w2 = 1; w2 < nwaves; w2++) v[b] += red[((w2 * 2 + b) * 4 + rr) * 32 + ll];
+    }
+    const int n = b16 * 16 + cc;
+    reinterpret_cast<half_t*>(p.out)[(size_t)(row0 + m) * p.N + (n & ~7) + interleaved_pos(n & 7)] =
+        (half_t)silu_mul(v[0], v[1]);
+  }
+  __syncthreads();
+}
+
+// The gate/up product of one (tile, 16-column block), on
+// v_mfma_f32_16x16x32_f16, for the fused decode launch: tile rows [row0,
+// row0 + rows) of expert e (rows <= kGemvMaxTokens), output columns
+// [16 b16, 16 b16 + 16) of both banks, then h = silu(gate) * up.  Lane l
+// takes column l % 16 of the block and the 8-byte half q = (l / 16) % 2 of
+// the packed 16-byte unit (column, reduction half (l / 32)): its two words
+// feed the two MFMAs of a slab, so MFMA m covers, for lane group (l / 16),
+// reduction indices 32 (l / 32) + 16 q + 8 m + [0, 8) of the slab, and the
+// activation fragment of tile row l % 16 is read to match (zeros past the
+// tile).  SPW slabs per wave and pass.
+template <int SPW>
+__device__ __forceinline__ void gemv_tile16(const DecParams& p, const int32_t* sorted_pairs, int e,
+                                            int row0, int rows, int b16, char* dsm) {
+  const int pass_slabs = (blockDim.x >> 6) * SPW;
+  floatx4_t acc[2] = {floatx4_t{}, floatx4_t{}};
+  for (int base = 0; base < p.K / 64; base += pass_slabs) {
+    const Frag16<SPW> f = g16_load<SPW>(p, e, b16, base);
+    g16_stage<SPW>(p, sorted_pairs, row0, rows, base, dsm);
+    __syncthreads();
+    g16_mma<SPW>(p, f, rows, base, acc, dsm);
+    __syncthreads();  // the next pass overwrites xs
+  }
+  g16_epilogue(p, acc, row0, rows, b16, dsm);
+}
+
 // The grouped GEMM at decode sizes on a device block map: one workgroup per
 // (tile, 32-column block); tiles past the map's count exit.
 template <int MODE, int SPW, bool PACK = false>
@@ -273,12 +426,43 @@ __global__ __launch_bounds__(64 * kDecWavesMax) void decode_gate_up_kernel(const
   // 5. the (tile, column block) items of this workgroup: blockIdx.x, then
   //    every gridDim.x-th after it (the grid is at most what the chip holds
   //    at once, so the routing above runs once per workgroup)
-  const int nbl = p.N / 32;
-  const int items = nb_s[0] * nbl;
-  for (int it = blockIdx.x; it < items; it += gridDim.x) {
-    const int tile = it / nbl, blk = it % nbl;
-    gemv_tile<MOE_GEMM_GATE_UP_SWIGLU, SPW, false, true>(p, sp_s, blk_s[3 * tile], blk_s[3 * tile + 1],
-                                                         blk_s[3 * tile + 2], blk, dsm);
+  const int nb16 = p.N / 16;
+  const int items = nb_s[0] * nb16;
+  const int G = gridDim.x;
+  if (p.K / 64 > nwaves * SPW) {  // more than one pass per item
+    for (int it = blockIdx.x; it < items; it += G) {
+      const int tile = it / nb16;
+      gemv_tile16<SPW>(p, sp_s, blk_s[3 * tile], blk_s[3 * tile + 1], blk_s[3 * tile + 2], it % nb16, dsm);
+    }
+    return;
+  }
+  // one pass per item: the next item's weight loads are issued before this
+  // item's multiplies (two fragment sets, alternating)
+  int it = blockIdx.x;
+  Frag16<SPW> fa, fb;
+  if (it < items) fa = g16_load<SPW>(p, blk_s[3 * (it / nb16)], it % nb16, 0);
+  while (it < items) {
+#pragma unroll
+    for (int half = 0; half < 2; half++) {
+      const int tile = it / nb16, b16 = it % nb16;
+      const int row0 = blk_s[3 * tile + 1], rows = blk_s[3 * tile + 2];
+      const int nx = it + G;
+      g16_stage<SPW>(p, sp_s, row0, rows, 0, dsm);
+      // this item's fragments (issued an item ago) and x rows have landed;
+      // the multiplies below then wait for nothing issued after this point
+      wait_vm<0>();
+      if (nx < items) {
+        if (half == 0) fb = g16_load<SPW>(p, blk_s[3 * (nx / nb16)], nx % nb16, 0);
+        else fa = g16_load<SPW>(p, blk_s[3 * (nx / nb16)], nx % nb16, 0);
+      }
+      __syncthreads();
+      floatx4_t acc[2] = {floatx4_t{}, floatx4_t{}};
+      g16_mma<SPW>(p, half == 0 ? fa : fb, rows, 0, acc, dsm);
+      __syncthreads();
+      g16_epilogue(p, acc, row0, rows, b16, dsm);
+      it = nx;
+      if (it >= items) break;
+    }
   }
 }
 
@@ -472,13 +656,16 @@ hipError_t launch_decode_gate_up(const DecodeRouting& dr, const GemmArgs& a, hip
     return hipErrorInvalidValue;
   const int64_t P = (int64_t)a.T * a.top_k;
   const int64_t max_blocks = P / a.block_m + (P < a.E ? P : a.E);
-  const int64_t max_items = max_blocks * (a.N / 32);
-  const GemvShape sh = gemv_shape(a.K, max_items);
+  const int64_t max_items = max_blocks * (a.N / 16);
+  // four slabs per wave (8 waves cover K = 2048 in one pass, two workgroups
+  // per CU) when K allows it: fewer waves to launch, the same bytes in flight
+  const int spw = a.K >= 1024 ? 4 : 2;
+  const GemvShape sh{spw, std::max(1, std::min(kDecWavesMax, a.K / (64 * spw)))};
   // LDS: the logits, then (reused) the activation rows of one pass; the
-  // waves' partial sums of both banks
+  // waves' partial sums of both banks (rows 0..7 of 16 columns)
   const int xs_bytes = std::max(kGemvMaxTokens * sh.waves * sh.spw * 64 * 2, a.T * a.E * 4);
   const int xs_al = (xs_bytes + 15) & ~15;
-  const size_t lds = (size_t)xs_al + (size_t)sh.waves * 2 * 4 * 64 * 4;
+  const size_t lds = (size_t)xs_al + (size_t)sh.waves * 2 * 4 * 32 * 4;
   const DecParams p = dec_params(a, P, max_blocks, xs_al);
   const DecRouteParams r{dr.logits, dr.logits_out, dr.ksplit, a.T,
                          dr.ids, dr.w, dr.counts, dr.offsets, dr.sorted_pairs, dr.pair_slot,
