@@ -351,6 +351,19 @@ def test_ffn_decode_edges(orc):
         layer_output_check(orc, lay, y, info)
 
 
+def test_ffn_decode_wide_shapes(orc):
+    """Decode sizes at shapes that leave the one-pass kernels: a reduction
+    of 8192 in the gate/up launch (more than one pass per item, no
+    prefetch), and I = 1152 (more than 16 slabs: the down projection falls
+    back to the per-tile GEMV and the combine kernel)."""
+    for (T, H, I, E, k) in [(3, 8192, 128, 6, 2), (5, 256, 1152, 8, 3)]:
+        lay = synth.make_custom(T=T, H=H, I=I, E=E, k=k, G=64, seed=60 + T)
+        y, info = api.ffn_forward(on_dev(lay), info=True)
+        torch.cuda.synchronize()
+        assert info["path"] == 1
+        layer_output_check(orc, lay, y, info)
+
+
 @pytest.mark.parametrize("case", ["prefill_t512", "ragged", "imbalanced_t8192"])
 def test_ffn_host_blockmap_identical(case):
     """The host-round-trip ablation runs the same kernels on a block map the
