@@ -261,8 +261,11 @@ __global__ __launch_bounds__(64 * WAVES, WGS_PER_CU) void w4_mfma_kernel(const M
       compute(s % STAGES);
     }
   };
-  // uniform per workgroup: every wave takes the same branch
-  if (MB > 1 && rows <= BM / 2)
+  // uniform per workgroup: every wave takes the same branch.  The half
+  // pipeline needs the activation copies of the first half to split evenly
+  // over the waves (not so with 8 waves and 64-row tiles).
+  constexpr bool HALF = MB > 1 && (A_PER_WAVE * (MB / 2)) % MB == 0;
+  if (HALF && rows <= BM / 2)
     pipeline(IntTag<(MB > 1 ? MB / 2 : 1)>{});
   else
     pipeline(IntTag<MB>{});
@@ -398,6 +401,12 @@ hipError_t launch_mode(const GemmArgs& a, hipStream_t s) {
       case 128: w4_mfma_kernel<MODE, 4, 4, false, 3, 1, PACK, true><<<grid, 256, 0, s>>>(p); break;
       default: return hipErrorInvalidValue;
     }
+    return hipGetLastError();
+  }
+  if (MODE == MOE_GEMM_DOWN && a.block_m == 64 && !g32 && a.N % 512 == 0) {
+    const int64_t items8 = max_blocks * (a.N / 512);
+    const int64_t grid8 = ((items8 + kNumXcd - 1) / kNumXcd) * kNumXcd;
+    w4_mfma_kernel<MODE, 2, 8, false, 3, 2, PACK><<<grid8, 512, 0, s>>>(p);
     return hipGetLastError();
   }
   switch (a.block_m * 2 + (g32 ? 1 : 0)) {

@@ -98,6 +98,20 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave, on DPP lane moves: four
+// row shifts build the sums inside each 16-lane row, then two row broadcasts
+// carry lane 15's total into row 1 (and lane 47's into row 3), and lane
+// 31's into rows 2 and 3.  Lanes a move does not reach add 0.
+__device__ __forceinline__ int wave_inclusive_sum(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15 -> rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31 -> rows 2, 3
+  return x;
+}
+
 // global_load_lds_dwordx4 / _dword: each lane's 16 (4) bytes at g land in
 // LDS at l + 16 (4) * lane; l must be the same for the whole wave.
 __device__ __forceinline__ void lds_load16(const void* g, char* l) {

@@ -12,20 +12,18 @@ namespace {
 constexpr int kScanThreads = 512;
 constexpr int kScanWaves = kScanThreads / 64;
 
-// Exclusive scan over kScanThreads values held one per thread.
+// Exclusive scan over kScanThreads values held one per thread: a DPP prefix
+// sum inside each wave, then each wave adds the totals of the waves before
+// it (two barriers).
 __device__ int block_exclusive_scan(int v, int* tmp) {
-  const int tid = threadIdx.x;
-  tmp[tid] = v;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int incl = wave_inclusive_sum(v);
+  if (lane == 63) tmp[wave] = incl;
   __syncthreads();
-  for (int off = 1; off < kScanThreads; off <<= 1) {
-    const int add = tid >= off ? tmp[tid - off] : 0;
-    __syncthreads();
-    tmp[tid] += add;
-    __syncthreads();
-  }
-  const int incl = tmp[tid];
-  __syncthreads();
-  return incl - v;
+  int base = 0;
+  for (int w = 0; w < wave; w++) base += tmp[w];
+  __syncthreads();  // tmp is reused by the next scan
+  return base + incl - v;
 }
 
 // One workgroup of kScanThreads threads, chunk c of nchunks: see
