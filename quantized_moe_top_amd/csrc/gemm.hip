@@ -107,11 +107,7 @@ __global__ __launch_bounds__(64 * WAVES, WGS_PER_CU) void w4_mfma_kernel(const M
 
   // ---- A loads: instruction j covers rows 8j..8j+7; lane l fills physical
   // chunk l % 8 of row 8j + l / 8, i.e. logical chunk (l % 8) ^ (l / 8).
-  const half_t* asrc[A_PER_WAVE];
-  int a_lds[A_PER_WAVE];
-#pragma unroll
-  for (int a = 0; a < A_PER_WAVE; a++) {
-    const int j = A_INSTR >= WAVES ? wave + WAVES * a : wave % A_INSTR;
+  auto a_source = [&](int j) {
     const int r = 8 * j + (lane >> 3);
     const int c = (lane & 7) ^ (lane >> 3);
     int srow = row0 + min(r, rows - 1);
@@ -119,8 +115,27 @@ __global__ __launch_bounds__(64 * WAVES, WGS_PER_CU) void w4_mfma_kernel(const M
       const int pair = p.sorted_pairs[srow];
       srow = (pair >= 0 && pair < p.P) ? pair / p.top_k : 0;
     }
-    asrc[a] = p.a + (size_t)srow * K + 8 * c;
+    return p.a + (size_t)srow * K + 8 * c;
+  };
+  const half_t* asrc[A_PER_WAVE];
+  int a_lds[A_PER_WAVE];
+#pragma unroll
+  for (int a = 0; a < A_PER_WAVE; a++) {
+    const int j = A_INSTR >= WAVES ? wave + WAVES * a : wave % A_INSTR;
+    asrc[a] = a_source(j);
     a_lds[a] = 1024 * j;
+  }
+  // the half-height loop (rows < BM / 2) with fewer first-half copies than
+  // waves: wave w issues copy w mod (A_INSTR / 2), the same bytes to the
+  // same LDS place as another wave (a harmless duplicate), so every wave
+  // issues the same number of copies per slab
+  constexpr bool HALF_DUP = MB > 1 && A_PER_WAVE * (MB / 2) < MB;
+  const half_t* asrc_h = nullptr;
+  int a_lds_h = 0;
+  if constexpr (HALF_DUP) {
+    const int j = wave % (A_INSTR / 2);
+    asrc_h = a_source(j);
+    a_lds_h = 1024 * j;
   }
   if (!GATE_UP && tid < BM) {
     const int pair = tid < rows ? p.sorted_pairs[row0 + tid] : -1;
@@ -189,13 +204,15 @@ __global__ __launch_bounds__(64 * WAVES, WGS_PER_CU) void w4_mfma_kernel(const M
   // its rows are never stored).
   auto pipeline = [&](auto mba) {
     constexpr int MBA = decltype(mba)::value;
-    constexpr int APW = A_PER_WAVE * MBA / MB;  // activation copies used (rows < 32 MBA)
+    constexpr bool DUP = HALF_DUP && MBA < MB;
+    constexpr int APW = DUP ? 1 : A_PER_WAVE * MBA / MB;  // activation copies used (rows < 32 MBA)
     constexpr int DA = APW + B_PER_WAVE + S_PER_WAVE;
 
     auto issue = [&](int s, int stage) {
       char* base = lds + stage * STAGE;
 #pragma unroll
-      for (int a = 0; a < APW; a++) lds_load16(asrc[a] + s * kSlabK, base + a_lds[a]);
+      for (int a = 0; a < APW; a++)
+        lds_load16((DUP ? asrc_h : asrc[a]) + s * kSlabK, base + (DUP ? a_lds_h : a_lds[a]));
 #pragma unroll
       for (int b = 0; b < B_PER_WAVE; b++)
         lds_load16(bsrc[b] + s * (DENSE ? 4096 : 1024), base + A_BYTES + 1024 * (B_PER_WAVE * wave + b));
@@ -261,11 +278,8 @@ __global__ __launch_bounds__(64 * WAVES, WGS_PER_CU) void w4_mfma_kernel(const M
       compute(s % STAGES);
     }
   };
-  // uniform per workgroup: every wave takes the same branch.  The half
-  // pipeline needs the activation copies of the first half to split evenly
-  // over the waves (not so with 8 waves and 64-row tiles).
-  constexpr bool HALF = MB > 1 && (A_PER_WAVE * (MB / 2)) % MB == 0;
-  if (HALF && rows <= BM / 2)
+  // uniform per workgroup: every wave takes the same branch
+  if (MB > 1 && rows <= BM / 2)
     pipeline(IntTag<(MB > 1 ? MB / 2 : 1)>{});
   else
     pipeline(IntTag<MB>{});
