@@ -403,11 +403,45 @@ __global__ __launch_bounds__(64 * kDecWavesMax) void decode_gate_up_kernel(const
   // 2. top-k and combine weights, a wave per token, with the expert counts
   for (int t = wave; t < T; t += nwaves) topk_token<NK>(lg + t * E, E, k, ids_s + t * k, w_s + t * k, cnt);
   __syncthreads();
-  // 3. offsets, scatter and block map
+  // 3. with one pass per item, this workgroup's first item's weights are
+  //    requested now, ahead of the block map: at decode sizes every touched
+  //    expert is exactly one tile (at most T <= block_m pairs each), tile i
+  //    the i-th touched expert in ascending order, so the counts name it
+  const int nb16 = p.N / 16;
+  const bool one_pass = p.K / 64 <= nwaves * SPW;
+  Frag16<SPW> fa, fb;
+  if (one_pass) {
+    uint64_t tmask[NK];
+    int ntiles = 0;
+    const int lane = tid & 63;
+#pragma unroll
+    for (int i = 0; i < NK; i++) {
+      const int e = 64 * i + lane;
+      tmask[i] = __ballot(e < E && cnt[e] > 0);
+      ntiles += __popcll(tmask[i]);
+    }
+    const int it0 = blockIdx.x;
+    if (it0 < ntiles * nb16) {
+      int t = it0 / nb16, e0 = 0;
+#pragma unroll
+      for (int i = 0; i < NK; i++) {
+        const int c = __popcll(tmask[i]);
+        if (t >= 0 && t < c) {
+          uint64_t w = tmask[i];
+          for (int n = 0; n < t; n++) w &= w - 1;
+          e0 = 64 * i + __builtin_ctzll(w);
+        }
+        t -= c;
+      }
+      fa = g16_load<SPW>(p, e0, it0 % nb16, 0);
+      asm volatile("" ::: "memory");  // keep the loads here, ahead of the build
+    }
+  }
+  // 4. offsets, scatter and block map
   if (wave == 0) small_build(ids_s, cnt, next, P, E, kGemvMaxTokens, nullptr, off_s, sp_s, ps_s, blk_s, nb_s,
                               min(p.max_blocks, kSmallMaxBlocks));
   __syncthreads();
-  // 4. workgroup 0 publishes the routing
+  // 5. workgroup 0 publishes the routing
   if (blockIdx.x == 0) {
     for (int i = tid; i < P; i += blockDim.x) {
       r.ids[i] = ids_s[i];
@@ -423,13 +457,12 @@ __global__ __launch_bounds__(64 * kDecWavesMax) void decode_gate_up_kernel(const
       for (int i = tid; i < T * E; i += blockDim.x) r.logits_out[i] = lg[i];
   }
   __syncthreads();  // lg is overwritten by the activation stage below
-  // 5. the (tile, column block) items of this workgroup: blockIdx.x, then
+  // 6. the (tile, column block) items of this workgroup: blockIdx.x, then
   //    every gridDim.x-th after it (the grid is at most what the chip holds
   //    at once, so the routing above runs once per workgroup)
-  const int nb16 = p.N / 16;
   const int items = nb_s[0] * nb16;
   const int G = gridDim.x;
-  if (p.K / 64 > nwaves * SPW) {  // more than one pass per item
+  if (!one_pass) {  // more than one pass per item
     for (int it = blockIdx.x; it < items; it += G) {
       const int tile = it / nb16;
       gemv_tile16<SPW>(p, sp_s, blk_s[3 * tile], blk_s[3 * tile + 1], blk_s[3 * tile + 2], it % nb16, dsm);
@@ -437,10 +470,9 @@ __global__ __launch_bounds__(64 * kDecWavesMax) void decode_gate_up_kernel(const
     return;
   }
   // one pass per item: the next item's weight loads are issued before this
-  // item's multiplies (two fragment sets, alternating)
+  // item's multiplies (two fragment sets, alternating; the first item's set
+  // was issued before the block map)
   int it = blockIdx.x;
-  Frag16<SPW> fa, fb;
-  if (it < items) fa = g16_load<SPW>(p, blk_s[3 * (it / nb16)], it % nb16, 0);
   while (it < items) {
 #pragma unroll
     for (int half = 0; half < 2; half++) {
