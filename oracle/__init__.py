@@ -80,6 +80,8 @@ class Oracle:
         L.oracle_expert_hidden.argtypes = [_p, _p, _p, _i64, _i64, _i64, _i64] + [_p] * 6 + [_p]
         L.oracle_expert_down.argtypes = [_p, _p, _i64, _i64, _i64, _i64, _p, _p, _p, _p]
         L.oracle_ffn.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64] + [_p] * 9 + [_p]
+        L.oracle_rmsnorm.argtypes = [_p, _p, ctypes.c_double, _i64, _i64, _p]
+        L.oracle_residual_out.argtypes = [_p, _p, _i64, _p]
 
     def num_threads(self) -> int:
         return int(self.lib.oracle_num_threads())
@@ -179,6 +181,26 @@ class Oracle:
                             _ptr(gq), _ptr(gs), _ptr(gb), _ptr(uq), _ptr(us), _ptr(ub),
                             _ptr(dq), _ptr(ds), _ptr(db), _ptr(y))
         return y
+
+    # -- either side of the layer ------------------------------------------
+    def rmsnorm(self, x, gamma, eps: float) -> np.ndarray:
+        """bf16 bits [T, H] of the RMSNorm of x (bf16 [T, H]) with gain gamma (bf16 [H])."""
+        x = _np(x, np.uint16)
+        g = _np(gamma, np.uint16).ravel()
+        T, H = x.shape
+        assert g.size == H
+        out = np.empty((T, H), np.uint16)
+        self.lib.oracle_rmsnorm(_ptr(x), _ptr(g), float(eps), T, H, _ptr(out))
+        return out
+
+    def residual_out(self, residual, y) -> np.ndarray:
+        """bf16 bits of residual (bf16) + y (fp32), same shape."""
+        r = _np(residual, np.uint16)
+        yy = _np(y, np.float32)
+        assert r.shape == yy.shape
+        out = np.empty(r.shape, np.uint16)
+        self.lib.oracle_residual_out(_ptr(r), _ptr(yy), r.size, _ptr(out))
+        return out
 
     def layer(self, layer, block_m: int, tokens=None) -> dict:
         """Every step of the layer on a ``synth.MoELayer``: logits (from the

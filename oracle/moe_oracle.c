@@ -22,6 +22,13 @@
  *   oracle_ffn            per token, per selected expert:
  *                         y[t] = sum_j w[t,j] * Wd_e (silu(Wg_e x) * Wu_e x)
  *
+ * and the two steps an engine runs on either side of the layer (the pages
+ * give neither; these are their textbook definitions):
+ *
+ *   oracle_rmsnorm        x_n[t,h] = bf16(x[t,h] * gamma[h] / sqrt(mean_h x[t,h]^2 + eps)),
+ *                         fp64, rounded once to bf16 (nearest, ties to even)
+ *   oracle_residual_out   out = bf16(residual + y), fp64 sum rounded once
+ *
  * Nothing is blocked, fused or reordered beyond those definitions; every
  * weight is dequantised scalar by scalar each time it is used.  Shares no
  * code, header or table with the HIP library.
@@ -237,4 +244,44 @@ void oracle_ffn(const uint16_t* x, const int32_t* ids, const float* weights, con
     free(h);
     free(acc);
   }
+}
+
+/* fp64 -> bf16 bits, round to nearest, ties to even, in one step (no
+ * intermediate fp32 rounding).  Finite normal inputs only (zero allowed). */
+static uint16_t double_to_bf16_bits(double v) {
+  if (v == 0.0) return signbit(v) ? 0x8000u : 0u;
+  int e;
+  frexp(v, &e);                      /* |v| in [2^(e-1), 2^e) */
+  const double ulp = ldexp(1.0, e - 8);  /* bf16 keeps 8 significant bits */
+  const double r = nearbyint(v / ulp) * ulp;  /* default rounding: nearest even */
+  const float f = (float)r;          /* exact: r has at most 9 significant bits */
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  return (uint16_t)(u >> 16);
+}
+
+/* RMSNorm of each row of x (bf16 [T][H]) with gain gamma (bf16 [H]):
+ *   r_t = 1 / sqrt(sum_h x[t,h]^2 / H + eps),  x_n[t,h] = x[t,h] * r_t * gamma[h],
+ * all in fp64, rounded once to bf16 into out [T][H]. */
+void oracle_rmsnorm(const uint16_t* x, const uint16_t* gamma, double eps, int64_t T, int64_t H,
+                    uint16_t* out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; t++) {
+    double ss = 0.0;
+    for (int64_t h = 0; h < H; h++) {
+      const double v = (double)bf16_bits_to_float(x[t * H + h]);
+      ss += v * v;
+    }
+    const double r = 1.0 / sqrt(ss / (double)H + eps);
+    for (int64_t h = 0; h < H; h++)
+      out[t * H + h] = double_to_bf16_bits((double)bf16_bits_to_float(x[t * H + h]) * r *
+                                           (double)bf16_bits_to_float(gamma[h]));
+  }
+}
+
+/* out[i] = bf16(residual[i] + y[i]) for n values: the bf16 residual and the
+ * fp32 layer output added in fp64 and rounded once. */
+void oracle_residual_out(const uint16_t* residual, const float* y, int64_t n, uint16_t* out) {
+  for (int64_t i = 0; i < n; i++)
+    out[i] = double_to_bf16_bits((double)bf16_bits_to_float(residual[i]) + (double)y[i]);
 }

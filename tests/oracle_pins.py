@@ -350,6 +350,68 @@ def pin_router_logits(orc):
     assert np.all(np.abs(l.astype(np.float64) - ref) <= _f32_ulp(ref)), np.abs(l - ref).max()
 
 
+# ---------------------------------------------- either side of the layer --
+def _bf16_bits_rne(v: np.ndarray) -> np.ndarray:
+    """fp64 -> bf16 bits, nearest with ties to even, in one step (numpy's
+    rint rounds half to even); written here independently of the oracle."""
+    v = np.asarray(v, np.float64)
+    out = np.zeros(v.shape, np.uint16)
+    nz = v != 0
+    _, e = np.frexp(v[nz])
+    ulp = np.ldexp(1.0, e - 8)
+    r = (np.rint(v[nz] / ulp) * ulp).astype(np.float32)
+    out[nz] = (r.view(np.uint32) >> 16).astype(np.uint16)
+    out[~nz] = np.where(np.signbit(v[~nz]), 0x8000, 0).astype(np.uint16)
+    return out
+
+
+def pin_rmsnorm_library(orc):
+    """RMSNorm equals the library routine (torch rms_norm in fp64) rounded
+    to bf16: bit-exact on seeded rows (both are exact to ~1e-16 before the
+    one rounding), including rows of very different scale."""
+    g = torch.Generator().manual_seed(71)
+    x = torch.randn(40, 384, generator=g, dtype=torch.float64)
+    x[::5] *= 30.0
+    x[1::7] *= 1e-3
+    xb = x.to(torch.bfloat16)
+    gamma = (torch.rand(384, generator=g, dtype=torch.float64) * 2 - 0.5).to(torch.bfloat16)
+    eps = 1e-6
+    ref = torch.nn.functional.rms_norm(xb.double(), (384,), weight=gamma.double(), eps=eps).numpy()
+    got = orc.rmsnorm(xb, gamma, eps)
+    assert np.array_equal(got, _bf16_bits_rne(ref))
+
+
+def pin_rmsnorm_closed_forms(orc):
+    """Constant rows c with eps = 0 normalise to sign(c) * gamma exactly;
+    scaling a row by a power of two changes nothing (eps = 0)."""
+    H = 64
+    x = torch.tensor([[1.5] * H, [-0.375] * H, [96.0] * H], dtype=torch.bfloat16)
+    gamma = torch.tensor([2.0 ** (h % 5 - 2) for h in range(H)], dtype=torch.bfloat16)
+    got = orc.rmsnorm(x, gamma, 0.0)
+    ref = np.stack([gamma.float().numpy(), -gamma.float().numpy(), gamma.float().numpy()])
+    assert np.array_equal(got, _bf16_bits_rne(ref))
+    g = torch.Generator().manual_seed(72)
+    y = torch.randn(6, H, generator=g).to(torch.bfloat16)
+    assert np.array_equal(orc.rmsnorm(y, gamma, 0.0), orc.rmsnorm(y * 8, gamma, 0.0))
+
+
+def pin_residual_out(orc):
+    """bf16(residual + y) rounds the exact sum once, ties to even: 1 + 2^-9
+    is halfway between 1 and 1 + 2^-7 and goes to 1, 1 + 3 * 2^-9 goes up;
+    the rest against an independent fp64 sum and rounding, also on seeded
+    values."""
+    res = torch.tensor([1.0, 1.0, -2.0, 0.5, 3.0], dtype=torch.bfloat16)
+    y = np.array([2.0 ** -9, 3 * 2.0 ** -9, 2.0 ** -8 - 2.0 ** -30, -0.5, 1e-3], np.float32)
+    got = orc.residual_out(res, y)
+    assert list(got[:2]) == [0x3F80, 0x3F81]
+    assert np.array_equal(got, _bf16_bits_rne(res.double().numpy() + y.astype(np.float64)))
+    g = torch.Generator().manual_seed(73)
+    r = torch.randn(50, 32, generator=g).to(torch.bfloat16)
+    yy = (torch.randn(50, 32, generator=g) * 3).numpy()
+    assert np.array_equal(orc.residual_out(r, yy),
+                          _bf16_bits_rne(r.double().numpy() + yy.astype(np.float64)))
+
+
 PINS = [
     pin_route_golden, pin_route_bruteforce, pin_route_argsort, pin_route_weights_softmax,
     pin_blocks_golden, pin_blocks_invariants,
@@ -357,4 +419,5 @@ PINS = [
     pin_ffn_zero, pin_ffn_identity_closed_form, pin_ffn_dense_single_expert,
     pin_ffn_dense_masked, pin_ffn_token_subset, pin_expert_hidden_down,
     pin_router_logits,
+    pin_rmsnorm_library, pin_rmsnorm_closed_forms, pin_residual_out,
 ]

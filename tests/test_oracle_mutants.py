@@ -54,6 +54,18 @@ MUTATIONS = [
      "u += (double)oracle_dequant(gq + row * (H / 8), gs + row * (H / G), gb + row * (H / G), h, G) * xv;"),
     ("softmax sums only the first selected logit",
      "s += a[j];", "s = a[0];"),
+    ("RMSNorm gain dropped",
+     " * r *\n                                           (double)bf16_bits_to_float(gamma[h]));",
+     " * r);"),
+    ("RMSNorm mean over H + 1 terms",
+     "const double r = 1.0 / sqrt(ss / (double)H + eps);", "const double r = 1.0 / sqrt(ss / (double)(H + 1) + eps);"),
+    ("RMSNorm epsilon outside the square root",
+     "const double r = 1.0 / sqrt(ss / (double)H + eps);", "const double r = 1.0 / (sqrt(ss / (double)H) + eps);"),
+    ("bf16 rounding truncates",
+     "const double r = nearbyint(v / ulp) * ulp;", "const double r = trunc(v / ulp) * ulp;"),
+    ("residual dropped",
+     "out[i] = double_to_bf16_bits((double)bf16_bits_to_float(residual[i]) + (double)y[i]);",
+     "out[i] = double_to_bf16_bits((double)y[i]);"),
 ]
 
 
