@@ -240,6 +240,44 @@ int moe_ffn_forward(const moe_layer* layer, const uint16_t* x, const float* rout
                     float* y, moe_route_info* info, void* workspace, size_t workspace_bytes,
                     void* stream);
 
+/* ------------------------------------------- either side of the layer --
+ * The steps a decoder block runs around the MoE layer, so that the layer
+ * drops into an engine (the pages describe the layer only; these are the
+ * textbook definitions).
+ *
+ * moe_rmsnorm: RMSNorm of the activations,
+ *   out[t][h] = bf16(x[t][h] * gamma[h] / sqrt(mean_h x[t][h]^2 + eps)),
+ * computed in fp32 and rounded to nearest even (an fp64 reference rounded
+ * once agrees except, rarely, by one bf16 unit).  x, out: device bf16 [T][H],
+ * 16-byte aligned, out not overlapping x; gamma: device bf16 [H], 16-byte
+ * aligned; H % 8 == 0, H > 0; T >= 0 (T = 0: nothing enqueued).  Enqueued on
+ * stream, nothing allocated.  Errors: MOE_ERR_NULL, MOE_ERR_SHAPE,
+ * MOE_ERR_UNSUPPORTED (H % 8), MOE_ERR_ALIGN, MOE_ERR_HIP. */
+int moe_rmsnorm(const uint16_t* x, const uint16_t* gamma, float eps, int32_t T, int32_t H,
+                uint16_t* out, void* stream);
+
+/* moe_ffn_forward_io: moe_ffn_forward with the steps around it.
+ *  - io->norm_weight (bf16 [H], or NULL): x is first RMS-normalised
+ *    (moe_rmsnorm, eps = io->norm_eps) into the workspace, and the layer
+ *    (router included) runs on the normalised rows;
+ *  - io->out (bf16 [T][H], or NULL; needs io->residual, bf16 [T][H]): also
+ *    out = bf16(residual + y), fp32 sum rounded to nearest even, written by
+ *    the same launch that writes y.  y (fp32) is always written.
+ * All device pointers, 16-byte aligned.  io == NULL behaves as
+ * moe_ffn_forward.  workspace: >= moe_ffn_io_workspace_bytes (the
+ * normalised activations after moe_ffn_forward's workspace).  Errors as
+ * moe_ffn_forward, plus MOE_ERR_NULL (out without residual) and MOE_ERR_ALIGN. */
+typedef struct {
+  const uint16_t* norm_weight;
+  float norm_eps;
+  const uint16_t* residual;
+  uint16_t* out;
+} moe_ffn_io;
+size_t moe_ffn_io_workspace_bytes(const moe_dims* dims, int32_t has_router);
+int moe_ffn_forward_io(const moe_layer* layer, const uint16_t* x, const float* router_logits,
+                       float* y, const moe_ffn_io* io, moe_route_info* info, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------ per-stage timing --
  * The same layer as moe_ffn_forward (identical kernels and results), with a
  * timing event recorded on `stream` at every stage boundary, so that a

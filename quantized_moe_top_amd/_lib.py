@@ -28,6 +28,7 @@ SYMBOLS = (
     "moe_ffn_block_m", "moe_ffn_workspace_bytes", "moe_ffn_forward", "moe_ffn_forward_timed",
     "moe_ffn_host_blockmap_ints", "moe_ffn_forward_host_blockmap",
     "moe_ffn_unfused_bytes", "moe_ffn_forward_unfused",
+    "moe_rmsnorm", "moe_ffn_io_workspace_bytes", "moe_ffn_forward_io",
 )
 
 # Stage boundaries of moe_ffn_forward_timed (enum moe_stage).
@@ -53,6 +54,11 @@ class Packed(ctypes.Structure):
 class Layer(ctypes.Structure):
     _fields_ = [("dims", Dims), ("router_weight", c_p), ("gate", Packed), ("up", Packed),
                 ("down", Packed)]
+
+
+class FfnIO(ctypes.Structure):
+    """The steps around the layer (moe_ffn_io)."""
+    _fields_ = [("norm_weight", c_p), ("norm_eps", ctypes.c_float), ("residual", c_p), ("out", c_p)]
 
 
 class GemmArgs(ctypes.Structure):
@@ -121,9 +127,14 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     L.moe_ffn_unfused_bytes.argtypes = [ctypes.POINTER(Dims)]
     L.moe_ffn_forward_unfused.argtypes = [ctypes.POINTER(Layer), c_p, c_p, c_p,
                                           ctypes.POINTER(RouteInfo), c_p, c_sz, c_p, c_sz, c_p]
+    L.moe_rmsnorm.argtypes = [c_p, c_p, ctypes.c_float, c_i32, c_i32, c_p, c_p]
+    L.moe_ffn_io_workspace_bytes.restype = c_sz
+    L.moe_ffn_io_workspace_bytes.argtypes = [ctypes.POINTER(Dims), c_i32]
+    L.moe_ffn_forward_io.argtypes = [ctypes.POINTER(Layer), c_p, c_p, c_p, ctypes.POINTER(FfnIO),
+                                     ctypes.POINTER(RouteInfo), c_p, c_sz, c_p]
     for name in ("moe_w4_pack", "moe_route", "moe_build_blocks", "moe_w4_grouped_gemm",
                  "moe_ffn_forward", "moe_ffn_forward_timed", "moe_ffn_forward_host_blockmap",
-                 "moe_ffn_forward_unfused"):
+                 "moe_ffn_forward_unfused", "moe_rmsnorm", "moe_ffn_forward_io"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L

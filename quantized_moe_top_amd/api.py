@@ -245,10 +245,31 @@ def host_blockmap_ints(layer, T: Optional[int] = None) -> int:
     return int(_L().moe_ffn_host_blockmap_ints(ctypes.byref(_dims(layer, layer.T if T is None else T))))
 
 
+def rmsnorm(x: torch.Tensor, gamma: torch.Tensor, eps: float,
+            out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """``moe_rmsnorm``: bf16 [T, H] rows of x normalised by their rms and
+    scaled by gamma (bf16 [H])."""
+    T, H = x.shape
+    if out is None:
+        out = torch.empty_like(x)
+    _lib.check(_L().moe_rmsnorm(_dev(x, "x", torch.bfloat16), _dev(gamma, "gamma", torch.bfloat16),
+                                float(eps), T, H, _dev(out, "out", torch.bfloat16), _stream()),
+               "moe_rmsnorm")
+    return out
+
+
+def ffn_io_workspace_bytes(layer, T: Optional[int] = None) -> int:
+    T = layer.T if T is None else T
+    return int(_L().moe_ffn_io_workspace_bytes(ctypes.byref(_dims(layer, T)),
+                                                int(layer.router_weight is not None)))
+
+
 def ffn_forward(layer, x: Optional[torch.Tensor] = None, logits: Optional[torch.Tensor] = None,
                 y: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
                 info: bool = False, stage_events=None, host_blockmap: Optional[torch.Tensor] = None,
-                expanded: Optional[torch.Tensor] = None):
+                expanded: Optional[torch.Tensor] = None, norm_weight: Optional[torch.Tensor] = None,
+                norm_eps: float = 1e-6, residual: Optional[torch.Tensor] = None,
+                out: Optional[torch.Tensor] = None):
     """The whole layer (S0/S1-S8) for a ``PackedLayer`` (a device
     ``synth.MoELayer`` is packed first).  ``x`` and ``logits`` default to the
     layer's own.  Returns y
@@ -259,7 +280,10 @@ def ffn_forward(layer, x: Optional[torch.Tensor] = None, logits: Optional[torch.
     elements) runs the host-round-trip ablation
     ``moe_ffn_forward_host_blockmap`` instead (it synchronises the stream).
     ``expanded`` (a device uint8 tensor of ``unfused_bytes``) runs the
-    unfused-dequantisation ablation ``moe_ffn_forward_unfused`` instead."""
+    unfused-dequantisation ablation ``moe_ffn_forward_unfused`` instead.
+    ``norm_weight`` (bf16 [H]) and/or ``residual`` with ``out`` (bf16 [T, H])
+    run ``moe_ffn_forward_io``: RMSNorm in front, out = bf16(residual + y)
+    behind."""
     if not isinstance(layer, PackedLayer):
         layer = pack_layer(layer)
     x = layer.x if x is None else x
@@ -268,7 +292,8 @@ def ffn_forward(layer, x: Optional[torch.Tensor] = None, logits: Optional[torch.
         logits = layer.logits
     if y is None:
         y = torch.empty((T, H), dtype=torch.float32, device=x.device)
-    wsb = ffn_workspace_bytes(layer, T)
+    use_io = norm_weight is not None or out is not None
+    wsb = ffn_io_workspace_bytes(layer, T) if use_io else ffn_workspace_bytes(layer, T)
     if workspace is None:
         workspace = torch.empty(max(wsb, 1), dtype=torch.uint8, device=x.device)
     if workspace.numel() < wsb:
@@ -279,7 +304,14 @@ def ffn_forward(layer, x: Optional[torch.Tensor] = None, logits: Optional[torch.
             _dev(logits, "logits", torch.float32) if layer.router_weight is None else 0,
             _dev(y, "y", torch.float32), ctypes.byref(ri),
             _dev(workspace, "workspace", torch.uint8), workspace.numel())
-    if expanded is not None:
+    if use_io:
+        io = _lib.FfnIO(_dev(norm_weight, "norm_weight", torch.bfloat16) if norm_weight is not None else 0,
+                        float(norm_eps),
+                        _dev(residual, "residual", torch.bfloat16) if residual is not None else 0,
+                        _dev(out, "out", torch.bfloat16) if out is not None else 0)
+        _lib.check(_L().moe_ffn_forward_io(args[0], args[1], args[2], args[3], ctypes.byref(io),
+                                           *args[4:], _stream()), "moe_ffn_forward_io")
+    elif expanded is not None:
         _lib.check(_L().moe_ffn_forward_unfused(*args, _dev(expanded, "expanded", torch.uint8),
                                                 expanded.numel(), _stream()),
                    "moe_ffn_forward_unfused")

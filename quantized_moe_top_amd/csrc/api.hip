@@ -347,7 +347,7 @@ int ffn_forward_impl(const moe_layer* layer, const uint16_t* x, const float* rou
                      float* y, moe_route_info* info, void* workspace, size_t workspace_bytes,
                      void* const* events, hipStream_t s, int32_t* host = nullptr,
                      size_t host_ints = 0, uint32_t* expanded = nullptr,
-                     size_t expanded_bytes = 0) {
+                     size_t expanded_bytes = 0, const moe_ffn_io* io = nullptr) {
   if (!layer) return fail(MOE_ERR_NULL, "layer is NULL");
   const moe_dims& d = layer->dims;
   int st = check_dims(&d);
@@ -368,9 +368,16 @@ int ffn_forward_impl(const moe_layer* layer, const uint16_t* x, const float* rou
       (st = check_bank(layer->down, "down")))
     return st;
   const FfnLayout L = ffn_layout(d, has_router, block_m);
+  const bool norm = io && io->norm_weight;
+  const size_t need = L.total + (norm ? round_up((size_t)d.T * d.H * 2) : 0);
+  if (io) {
+    if (io->out && !io->residual) return fail(MOE_ERR_NULL, "io->out given without io->residual");
+    if ((norm && !aligned16(io->norm_weight)) || (io->out && (!aligned16(io->out) || !aligned16(io->residual))))
+      return fail(MOE_ERR_ALIGN, "io->norm_weight, residual or out not 16-byte aligned");
+  }
   if (!workspace) return fail(MOE_ERR_NULL, "workspace is NULL");
   if ((uintptr_t)workspace & 255u) return fail(MOE_ERR_ALIGN, "workspace not 256-byte aligned");
-  if (workspace_bytes < L.total) return fail(MOE_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, L.total);
+  if (workspace_bytes < need) return fail(MOE_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
   if (expanded) {
     if (d.T <= moe::kGemvMaxTokens)
       return fail(MOE_ERR_UNSUPPORTED, "the unfused path needs T > %d", moe::kGemvMaxTokens);
@@ -410,6 +417,15 @@ int ffn_forward_impl(const moe_layer* layer, const uint16_t* x, const float* rou
   int64_t grid_tiles = -1;  // host-known tile count (host block map path)
   float* part = L.router_ks > 1 ? (float*)(ws + L.logits_part) : nullptr;  // router partial sums
   if ((err = mark(events, MOE_STAGE_ROUTE, s)) != hipSuccess) return hip_status(err, "event");
+  if (norm) {
+    // RMSNorm in front: the layer runs on the normalised rows
+    uint16_t* xn = (uint16_t*)(ws + L.total);
+    if ((err = moe::launch_rmsnorm(x, io->norm_weight, io->norm_eps, d.T, d.H, xn, s)) != hipSuccess)
+      return hip_status(err, "rmsnorm");
+    x = xn;
+  }
+  const uint16_t* residual = io && io->out ? io->residual : nullptr;
+  uint16_t* out = io ? io->out : nullptr;
   if (gemv) {
     // decode sizes: the router GEMM (when given), then S1-S6 in one launch
     // (the build stage and the routing inside the gate/up stage)
@@ -464,13 +480,15 @@ int ffn_forward_impl(const moe_layer* layer, const uint16_t* x, const float* rou
   if (gemv && moe::decode_down_fused(d.I)) {
     // decode sizes: the down GEMV and the combine in one launch, per token
     // (the combine stage is empty)
-    if ((err = moe::launch_decode_down(g2, ids, pair_slot, y, s)) != hipSuccess) return hip_status(err, "down");
+    if ((err = moe::launch_decode_down(g2, ids, pair_slot, y, s, residual, out)) != hipSuccess)
+      return hip_status(err, "down");
     if ((err = mark(events, MOE_STAGE_COMBINE, s)) != hipSuccess) return hip_status(err, "event");
   } else {
     err = gemv ? moe::launch_w4_gemv(g2, s) : moe::launch_w4_mfma(g2, s);
     if (err != hipSuccess) return hip_status(err, "down");
     if ((err = mark(events, MOE_STAGE_COMBINE, s)) != hipSuccess) return hip_status(err, "event");
-    if ((err = moe::launch_combine(y_sorted, !gemv, pair_slot, y, d.T, d.H, d.top_k, s)) != hipSuccess)
+    if ((err = moe::launch_combine(y_sorted, !gemv, pair_slot, y, d.T, d.H, d.top_k, s, residual, out)) !=
+        hipSuccess)
       return hip_status(err, "combine");
   }
   if ((err = mark(events, MOE_NUM_STAGES, s)) != hipSuccess) return hip_status(err, "event");
@@ -514,6 +532,28 @@ int moe_ffn_forward_host_blockmap(const moe_layer* layer, const uint16_t* x,
   if (!host_pinned) return fail(MOE_ERR_NULL, "host_pinned is NULL");
   return ffn_forward_impl(layer, x, router_logits, y, info, workspace, workspace_bytes, nullptr,
                           (hipStream_t)stream, host_pinned, host_ints);
+}
+
+int moe_rmsnorm(const uint16_t* x, const uint16_t* gamma, float eps, int32_t T, int32_t H,
+                uint16_t* out, void* stream) {
+  if (T < 0 || H <= 0) return fail(MOE_ERR_SHAPE, "need T >= 0 and H > 0");
+  if (H % 8) return fail(MOE_ERR_UNSUPPORTED, "H = %d not a multiple of 8", H);
+  if (T == 0) return ok();
+  if (!x || !gamma || !out) return fail(MOE_ERR_NULL, "x, gamma or out is NULL");
+  if (!aligned16(x) || !aligned16(gamma) || !aligned16(out)) return fail(MOE_ERR_ALIGN, "x, gamma or out not 16-byte aligned");
+  return hip_status(moe::launch_rmsnorm(x, gamma, eps, T, H, out, (hipStream_t)stream), "rmsnorm");
+}
+
+size_t moe_ffn_io_workspace_bytes(const moe_dims* d, int32_t has_router) {
+  if (!d || check_dims(d) != MOE_OK) return 0;
+  return ffn_layout(*d, has_router != 0, moe_ffn_block_m(d)).total + round_up((size_t)d->T * d->H * 2);
+}
+
+int moe_ffn_forward_io(const moe_layer* layer, const uint16_t* x, const float* router_logits,
+                       float* y, const moe_ffn_io* io, moe_route_info* info, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  return ffn_forward_impl(layer, x, router_logits, y, info, workspace, workspace_bytes, nullptr,
+                          (hipStream_t)stream, nullptr, 0, nullptr, 0, io);
 }
 
 int moe_ffn_forward_timed(const moe_layer* layer, const uint16_t* x, const float* router_logits,

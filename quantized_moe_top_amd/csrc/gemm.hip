@@ -442,11 +442,13 @@ hipError_t launch_mode(const GemmArgs& a, hipStream_t s) {
 // indices and then all k rows are loaded before the sum (KMAX >= k, guards
 // for j >= k), so a thread has k row loads in flight instead of k round
 // trips.
+// With out: also out = bf16(residual + y), four values per thread.
 template <int KMAX, bool PACK>
 __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y_sorted,
                                                       const int32_t* __restrict__ pair_slot,
                                                       float4* __restrict__ y, int T, int H4,
-                                                      int k) {
+                                                      int k, const uint2* __restrict__ residual,
+                                                      uint2* __restrict__ out) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= (int64_t)T * H4) return;
   const int t = (int)(i / H4), c = (int)(i % H4);
@@ -475,6 +477,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
     acc.w += v[j].w;
   }
   y[i] = acc;
+  if (out) out[i] = residual_add_bf16x4(residual[i], acc);
 }
 
 }  // namespace
@@ -493,20 +496,24 @@ hipError_t launch_stage_x(const uint16_t* x, half_t* xh, int64_t n_elems, hipStr
 
 template <bool PACK>
 void launch_combine_k(const void* ys, const int32_t* pair_slot, float4* yo, int T, int H4, int k,
+                      const uint2* res, uint2* out,
                       int64_t grid, hipStream_t s) {
-  if (k <= 2) combine_kernel<2, PACK><<<grid, 256, 0, s>>>(ys, pair_slot, yo, T, H4, k);
-  else if (k <= 4) combine_kernel<4, PACK><<<grid, 256, 0, s>>>(ys, pair_slot, yo, T, H4, k);
-  else if (k <= 8) combine_kernel<8, PACK><<<grid, 256, 0, s>>>(ys, pair_slot, yo, T, H4, k);
-  else combine_kernel<16, PACK><<<grid, 256, 0, s>>>(ys, pair_slot, yo, T, H4, k);  // k <= 16
+  if (k <= 2) combine_kernel<2, PACK><<<grid, 256, 0, s>>>(ys, pair_slot, yo, T, H4, k, res, out);
+  else if (k <= 4) combine_kernel<4, PACK><<<grid, 256, 0, s>>>(ys, pair_slot, yo, T, H4, k, res, out);
+  else if (k <= 8) combine_kernel<8, PACK><<<grid, 256, 0, s>>>(ys, pair_slot, yo, T, H4, k, res, out);
+  else combine_kernel<16, PACK><<<grid, 256, 0, s>>>(ys, pair_slot, yo, T, H4, k, res, out);  // k <= 16
 }
 
 hipError_t launch_combine(const void* y_sorted, bool pack24, const int32_t* pair_slot, float* y,
-                          int T, int H, int k, hipStream_t s) {
+                          int T, int H, int k, hipStream_t s, const uint16_t* residual,
+                          uint16_t* out) {
   const int64_t n = (int64_t)T * (H / 4);
   const int64_t grid = (n + 255) / 256;
   float4* yo = reinterpret_cast<float4*>(y);
-  if (pack24) launch_combine_k<true>(y_sorted, pair_slot, yo, T, H / 4, k, grid, s);
-  else launch_combine_k<false>(y_sorted, pair_slot, yo, T, H / 4, k, grid, s);
+  const uint2* res = reinterpret_cast<const uint2*>(residual);
+  uint2* o = reinterpret_cast<uint2*>(out);
+  if (pack24) launch_combine_k<true>(y_sorted, pair_slot, yo, T, H / 4, k, res, o, grid, s);
+  else launch_combine_k<false>(y_sorted, pair_slot, yo, T, H / 4, k, res, o, grid, s);
   return hipGetLastError();
 }
 

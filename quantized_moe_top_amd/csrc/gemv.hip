@@ -522,7 +522,7 @@ constexpr int kDownChunk = 8;
 
 __global__ __launch_bounds__(64 * kDecWavesMax) void decode_down_kernel(
     const DecParams p, const int32_t* __restrict__ ids, const int32_t* __restrict__ pair_slot,
-    float* __restrict__ y) {
+    float* __restrict__ y, const uint16_t* __restrict__ residual, uint16_t* __restrict__ out) {
   extern __shared__ __attribute__((aligned(16))) char dsm[];
   __shared__ int e_s[16], slot_s[16];
   __shared__ float w_s[16], v_s[16 * 16];
@@ -609,6 +609,10 @@ __global__ __launch_bounds__(64 * kDecWavesMax) void decode_down_kernel(
       float acc = 0.0f;
       for (int j = 0; j < k; j++) acc = acc + v_s[j * 16 + tid];
       y[(size_t)t * p.N + b16 * 16 + tid] = acc;
+      if (out) {
+        const size_t at = (size_t)t * p.N + b16 * 16 + tid;
+        out[at] = (uint16_t)f32_to_bf16_rne(__uint_as_float((uint32_t)residual[at] << 16) + acc);
+      }
     }
   }
 }
@@ -720,7 +724,7 @@ hipError_t launch_decode_gate_up(const DecodeRouting& dr, const GemmArgs& a, hip
 bool decode_down_fused(int K) { return K % 64 == 0 && K / 64 <= kDecWavesMax; }
 
 hipError_t launch_decode_down(const GemmArgs& a, const int32_t* ids, const int32_t* pair_slot,
-                              float* y, hipStream_t s) {
+                              float* y, hipStream_t s, const uint16_t* residual, uint16_t* out) {
   if (a.T <= 0) return hipSuccess;
   if (a.T > kGemvMaxTokens || !decode_down_fused(a.K)) return hipErrorInvalidValue;
   const int64_t P = (int64_t)a.T * a.top_k;
@@ -729,7 +733,7 @@ hipError_t launch_decode_down(const GemmArgs& a, const int32_t* ids, const int32
   const int xs_bytes = kDownChunk * a.K * 2;
   const size_t lds = (size_t)xs_bytes + (size_t)waves * a.top_k * 16 * 4;
   const DecParams p = dec_params(a, P, 0, xs_bytes);
-  decode_down_kernel<<<grid, 64 * waves, lds, s>>>(p, ids, pair_slot, y);
+  decode_down_kernel<<<grid, 64 * waves, lds, s>>>(p, ids, pair_slot, y, residual, out);
   return hipGetLastError();
 }
 

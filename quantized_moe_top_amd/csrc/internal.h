@@ -179,6 +179,20 @@ __device__ __forceinline__ float4 unpack24x4(uint3 w) {
                      __uint_as_float(w.z & 0xFFFFFF00u));
 }
 
+// fp32 -> bf16 bits, round to nearest, ties to even (finite values).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float v) {
+  const uint32_t u = __float_as_uint(v);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Four bf16 residual values (8 bytes) plus four fp32 values, rounded to bf16.
+__device__ __forceinline__ uint2 residual_add_bf16x4(uint2 r, float4 y) {
+  const float r0 = __uint_as_float(r.x << 16), r1 = __uint_as_float(r.x & 0xFFFF0000u);
+  const float r2 = __uint_as_float(r.y << 16), r3 = __uint_as_float(r.y & 0xFFFF0000u);
+  return make_uint2(f32_to_bf16_rne(r0 + y.x) | (f32_to_bf16_rne(r1 + y.y) << 16),
+                    f32_to_bf16_rne(r2 + y.z) | (f32_to_bf16_rne(r3 + y.w) << 16));
+}
+
 // silu(g) * u = g / (1 + e^-g) * u, with the hardware exponential and
 // reciprocal (about 1 ulp each; the result is then rounded to fp16).
 __device__ __forceinline__ float silu_mul(float g, float u) {
@@ -270,12 +284,20 @@ hipError_t launch_decode_gate_up(const DecodeRouting& r, const GemmArgs& a, hipS
 // decode_down_fused(K): a reduction of at most 16 slabs of 64.
 bool decode_down_fused(int K);
 hipError_t launch_decode_down(const GemmArgs& a, const int32_t* ids, const int32_t* pair_slot,
-                              float* y, hipStream_t s);
+                              float* y, hipStream_t s, const uint16_t* residual = nullptr,
+                              uint16_t* out = nullptr);
 
 // S8: y[t] = sum_j y_sorted[pair_slot[t * k + j]], j ascending; y_sorted
 // fp32, or packed 24-bit when pack24.
+// With out (bf16 [T][H]): also out = bf16(residual + y) (residual bf16 [T][H]).
 hipError_t launch_combine(const void* y_sorted, bool pack24, const int32_t* pair_slot, float* y,
-                          int T, int H, int k, hipStream_t s);
+                          int T, int H, int k, hipStream_t s, const uint16_t* residual = nullptr,
+                          uint16_t* out = nullptr);
+
+// RMSNorm in front of the layer: out[t][h] = bf16(x[t][h] * gamma[h] /
+// sqrt(mean_h x[t][h]^2 + eps)) (bf16 in and out, fp32 arithmetic, H % 8 == 0).
+hipError_t launch_rmsnorm(const uint16_t* x, const uint16_t* gamma, float eps, int T, int H,
+                          uint16_t* out, hipStream_t s);
 
 
 }  // namespace moe

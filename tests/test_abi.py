@@ -178,3 +178,28 @@ def test_pack_queries_and_validation(L):
     assert pk(G=16) == UNSUP
     assert pk(E=0) == SHAPE
     assert pk(w=A + 4) == ALIGN
+
+
+def test_rmsnorm_and_io_validation(L):
+    norm = lambda x=A, g=A, T=4, H=256, out=A: L.moe_rmsnorm(x, g, 1e-6, T, H, out, None)
+    assert norm(H=0) == SHAPE
+    assert norm(T=-1) == SHAPE
+    assert norm(H=100) == UNSUP                    # H % 8
+    assert norm(g=0) == NULL
+    assert norm(out=A + 2) == ALIGN
+    assert norm(T=0) == OK                         # nothing enqueued
+    bank = Packed(A, A)
+    lay = Layer(Dims(16, 256, 128, 8, 2, 32), 0, bank, bank, bank)
+    d = Dims(16, 256, 128, 8, 2, 32)
+    extra = L.moe_ffn_io_workspace_bytes(ctypes.byref(d), 0) - L.moe_ffn_workspace_bytes(ctypes.byref(d), 0)
+    assert extra >= 16 * 256 * 2                   # the normalised activations
+
+    def io_call(io, wsb=1 << 30):
+        return L.moe_ffn_forward_io(ctypes.byref(lay), A, A, A, ctypes.byref(io), None, A, wsb, None)
+    assert io_call(_lib.FfnIO(0, 1e-6, 0, A)) == NULL        # out without residual
+    assert io_call(_lib.FfnIO(A + 2, 1e-6, 0, 0)) == ALIGN   # norm weight misaligned
+    assert io_call(_lib.FfnIO(0, 1e-6, A, A + 4)) == ALIGN   # out misaligned
+    need_plain = L.moe_ffn_workspace_bytes(ctypes.byref(d), 0)
+    assert io_call(_lib.FfnIO(A, 1e-6, 0, 0), wsb=need_plain) == WS  # no room for the normalised x
+    lay.dims.H = 200
+    assert io_call(_lib.FfnIO(0, 1e-6, 0, 0)) == UNSUP       # same checks as moe_ffn_forward

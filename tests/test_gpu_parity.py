@@ -364,6 +364,85 @@ def test_ffn_decode_wide_shapes(orc):
         layer_output_check(orc, lay, y, info)
 
 
+# ------------------------------------------------- either side of the layer --
+def _bf16_ulp(bits: np.ndarray) -> np.ndarray:
+    v = np.abs((bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64))
+    return np.where(v > 0, np.ldexp(1.0, np.frexp(v)[1] - 8), 0.0)
+
+
+def test_rmsnorm(orc):
+    """moe_rmsnorm against the oracle (fp64, one rounding): every value
+    within one bf16 unit, and almost all identical (fp32 arithmetic moves a
+    rounding only for values within ~1e-7 of a rounding boundary)."""
+    g = torch.Generator().manual_seed(80)
+    for T, H in [(1, 2048), (37, 2048), (300, 256), (5, 8)]:
+        x = torch.randn(T, H, generator=g)
+        x[::7] *= 30.0
+        xb = x.to(torch.bfloat16)
+        gamma = (torch.rand(H, generator=g) * 1.5 + 0.25).to(torch.bfloat16)
+        got = cpu(api.rmsnorm(xb.to(DEV), gamma.to(DEV), 1e-6).view(torch.int16)).view(np.uint16)
+        ref = orc.rmsnorm(xb, gamma, 1e-6)
+        gv = (got.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        rv = (ref.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        assert np.all(np.abs(gv - rv) <= _bf16_ulp(ref)), (T, H)
+        same = float(np.mean(got == ref))
+        say(f"  rmsnorm T={T} H={H}: {same * 100:.3f}% bit-identical")
+        assert same >= 0.999, (T, H, same)
+
+
+@pytest.mark.parametrize("case", ["mfma_t300", "decode_t5", "router_t40", "decode_router_t3"])
+def test_ffn_io(orc, case):
+    """moe_ffn_forward_io: RMSNorm in front and out = bf16(residual + y)
+    behind, against the oracle's normalisation, layer and residual sum.
+    Logits given: the routing does not depend on the normalised rows and is
+    compared bit-exactly; with a router weight the GPU's logits (from its own
+    normalised rows) are routed by the oracle and compared bit-exactly, and
+    checked against the oracle's logits to within the normalisation's one
+    bf16 unit."""
+    cfg = {"mfma_t300": dict(T=300, H=512, I=256, E=16, k=4, G=64, seed=81),
+           "decode_t5": dict(T=5, H=512, I=256, E=16, k=4, G=64, seed=82),
+           "router_t40": dict(T=40, H=512, I=256, E=32, k=4, G=64, seed=83, router="weight"),
+           "decode_router_t3": dict(T=3, H=256, I=128, E=8, k=2, G=32, seed=84, router="weight")}[case]
+    lay = synth.make_custom(**cfg)
+    g = torch.Generator().manual_seed(cfg["seed"] + 100)
+    gamma = (torch.rand(lay.H, generator=g) * 1.5 + 0.25).to(torch.bfloat16)
+    res = torch.randn(lay.T, lay.H, generator=g).to(torch.bfloat16)
+    d = on_dev(lay)
+    out = torch.empty((lay.T, lay.H), dtype=torch.bfloat16, device=DEV)
+    y, info = api.ffn_forward(d, info=True, norm_weight=gamma.to(DEV), norm_eps=1e-5,
+                              residual=res.to(DEV), out=out)
+    torch.cuda.synchronize()
+    xn = orc.rmsnorm(lay.x, gamma, 1e-5)
+    l_used = cpu(info["logits"]).astype(np.float32)
+    if lay.router_weight is None:
+        assert np.array_equal(l_used, cpu(lay.logits))
+    else:
+        l_ref = orc.router_logits(xn, lay.router_weight)
+        # each normalised input may differ by one bf16 unit: bound the effect
+        wr = np.abs(lay.router_weight.float().numpy().astype(np.float64))
+        xv = (xn.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        bound = router_error_bound(torch.from_numpy(xv).to(torch.bfloat16), lay.router_weight) + \
+            (_bf16_ulp(xn) @ wr.T) + f32_ulp(l_ref)
+        assert np.all(np.abs(l_used.astype(np.float64) - l_ref) <= bound)
+    rid, rw = orc.route(l_used, lay.k)
+    assert np.array_equal(cpu(info["topk_ids"]), rid)
+    assert_weights_close(cpu(info["topk_weights"]), rw)
+    y_ref = orc.ffn(xn, rid, rw, lay.gate, lay.up, lay.down, lay.G)
+    assert_fp_close(cpu(y), y_ref, f"{case} y")
+    out_ref = orc.residual_out(res, y_ref)
+    ov = (cpu(out.view(torch.int16)).view(np.uint16).astype(np.uint32) << 16).view(np.float32)
+    rv = (out_ref.astype(np.uint32) << 16).view(np.float32)
+    assert_fp_close(ov, rv, f"{case} out")
+    # out is bf16(residual + y) of the y returned beside it: the fp32 sum
+    # rounded to bf16 can differ from the once-rounded exact sum by one unit
+    # (double rounding), rarely
+    got, exact = cpu(out.view(torch.int16)).view(np.uint16), orc.residual_out(res, cpu(y))
+    gv = (got.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    ev = (exact.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    assert np.all(np.abs(gv - ev) <= _bf16_ulp(exact))
+    assert np.mean(got == exact) >= 0.999
+
+
 @pytest.mark.parametrize("case", ["prefill_t512", "ragged", "imbalanced_t8192"])
 def test_ffn_host_blockmap_identical(case):
     """The host-round-trip ablation runs the same kernels on a block map the
