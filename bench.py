@@ -64,6 +64,9 @@ def parse():
     ap.add_argument("--ablation", choices=["host_blockmap", "unfused"], default=None,
                     help="also time the layer with the block map built on the host (a stream "
                          "synchronisation and copies mid-layer), against the same layer eager")
+    ap.add_argument("--io", action="store_true",
+                    help="also time the layer with the steps around it (moe_ffn_forward_io: "
+                         "RMSNorm in front, bf16 residual sum behind), against the layer alone")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, run one plain device copy of 256 MiB, the reference "
                          "kernel for scaling HBM byte counters")
@@ -334,6 +337,32 @@ def main():
         log(f"[bench] host block map: {host_ms / K * 1e3:.2f} us/step vs eager {plain_ms / K * 1e3:.2f} "
             f"and graph {ms_per_step * 1e3:.2f}")
 
+    io_res = None
+    if args.io:
+        # the same steps plus RMSNorm in front and out = bf16(residual + y)
+        # behind, eager, against the layer alone eager
+        gio = torch.Generator().manual_seed(7)
+        gamma = (torch.rand(lay.H, generator=gio) + 0.5).to(torch.bfloat16).to(dev)
+        resid = torch.randn(T, lay.H, generator=gio).to(torch.bfloat16).to(dev)
+        out_bf = torch.empty(T, lay.H, dtype=torch.bfloat16, device=dev)
+        ws_io = torch.empty(api.ffn_io_workspace_bytes(lay), dtype=torch.uint8, device=dev)
+
+        def step_io(i):
+            c = copies[i % R]
+            lg = logit_pool[i % len(logit_pool)] if logit_pool else None
+            return api.ffn_forward(c, logits=lg, y=y, workspace=ws_io, norm_weight=gamma,
+                                   residual=resid, out=out_bf)
+
+        for i in range(args.warmup):
+            step_io(i)
+        plain_ms, _ = timed(lambda i: step(i))
+        io_ms, _ = timed(step_io)
+        io_res = {"ms_per_step": round(io_ms / K, 6), "eager_layer_ms_per_step": round(plain_ms / K, 6),
+                  "added_us_per_step": round((io_ms - plain_ms) / K * 1e3, 3),
+                  "tokens_per_s": round(T * K / (io_ms / 1e3), 1)}
+        log(f"[bench] with RMSNorm + residual: {io_ms / K * 1e3:.2f} us/step vs layer alone "
+            f"{plain_ms / K * 1e3:.2f}")
+
     if args.ablation == "unfused" and api.unfused_bytes(lay) > 0:
         # every step expands all experts' weights to fp16 in HBM, then the
         # grouped GEMMs stream those: eager, against the fused layer eager
@@ -384,6 +413,8 @@ def main():
     }
     if ablations:
         out["ablations"] = ablations
+    if io_res:
+        out["io"] = io_res
     print(json.dumps(out), flush=True)
 
 
