@@ -82,6 +82,7 @@ class Oracle:
         L.oracle_ffn.argtypes = [_p, _p, _p, _p, _i64, _i64, _i64, _i64, _i64] + [_p] * 9 + [_p]
         L.oracle_rmsnorm.argtypes = [_p, _p, ctypes.c_double, _i64, _i64, _p]
         L.oracle_residual_out.argtypes = [_p, _p, _i64, _p]
+        L.oracle_decode_attention.argtypes = [_p, _p, _p, _p, _p] + [_i64] * 6 + [_p]
 
     def num_threads(self) -> int:
         return int(self.lib.oracle_num_threads())
@@ -200,6 +201,24 @@ class Oracle:
         assert r.shape == yy.shape
         out = np.empty(r.shape, np.uint16)
         self.lib.oracle_residual_out(_ptr(r), _ptr(yy), r.size, _ptr(out))
+        return out
+
+    # -- decode attention (second workload) ------------------------------
+    def decode_attention(self, q, kcache, vcache, table, lens) -> np.ndarray:
+        """fp32 [B, Hq, D]: q bf16 [B, Hq, D]; caches bf16 [NB, Hkv, BLK, D];
+        table int32 [B, MB]; lens int32 [B]."""
+        q = _np(q, np.uint16)
+        kc = _np(kcache, np.uint16)
+        vc = _np(vcache, np.uint16)
+        tb = _np(table, np.int32)
+        ln = _np(lens, np.int32).ravel()
+        B, Hq, D = q.shape
+        NB, Hkv, BLK, D2 = kc.shape
+        assert D2 == D and vc.shape == kc.shape and tb.shape[0] == B and ln.size == B and Hq % Hkv == 0
+        assert np.all(ln <= tb.shape[1] * BLK) and np.all((tb >= 0) & (tb < NB))
+        out = np.empty((B, Hq, D), np.float32)
+        self.lib.oracle_decode_attention(_ptr(q), _ptr(kc), _ptr(vc), _ptr(tb), _ptr(ln), B, Hq, Hkv, D,
+                                         BLK, tb.shape[1], _ptr(out))
         return out
 
     def layer(self, layer, block_m: int, tokens=None) -> dict:

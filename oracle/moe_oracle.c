@@ -29,6 +29,16 @@
  *                         fp64, rounded once to bf16 (nearest, ties to even)
  *   oracle_residual_out   out = bf16(residual + y), fp64 sum rounded once
  *
+ * and a second workload the pages' decode gains come from (their
+ * architecture paragraph: coalesced key-cache reads, grouped-query packing,
+ * a fixed-block cache layout), defined plainly:
+ *
+ *   oracle_decode_attention  one query token per sequence against its cached
+ *                         keys and values: o = softmax(q K^T / sqrt(D)) V per
+ *                         query head, the KV head shared by Hq / Hkv query
+ *                         heads, keys and values found through a block table
+ *                         of fixed-size blocks; fp64
+ *
  * Nothing is blocked, fused or reordered beyond those definitions; every
  * weight is dequantised scalar by scalar each time it is used.  Shares no
  * code, header or table with the HIP library.
@@ -284,4 +294,49 @@ void oracle_rmsnorm(const uint16_t* x, const uint16_t* gamma, double eps, int64_
 void oracle_residual_out(const uint16_t* residual, const float* y, int64_t n, uint16_t* out) {
   for (int64_t i = 0; i < n; i++)
     out[i] = double_to_bf16_bits((double)bf16_bits_to_float(residual[i]) + (double)y[i]);
+}
+
+/* Decode attention.  q: bf16 [B][Hq][D]; kc, vc: bf16 [NB][Hkv][BLK][D] (block
+ * n holds cache positions of one sequence, BLK per block); table: int32
+ * [B][MB], table[b][i] = the block holding positions i*BLK .. i*BLK+BLK-1 of
+ * sequence b; lens: int32 [B].  For each sequence b and query head j (KV head
+ * j / (Hq / Hkv)):
+ *   s_t = sum_d q[b][j][d] * K_t[d] / sqrt(D)   for t < lens[b],
+ *   o[b][j][d] = sum_t exp(s_t - max s) V_t[d] / sum_t exp(s_t - max s),
+ * in fp64, rounded once to fp32; a sequence of length 0 gives o = 0. */
+void oracle_decode_attention(const uint16_t* q, const uint16_t* kc, const uint16_t* vc,
+                             const int32_t* table, const int32_t* lens, int64_t B, int64_t Hq,
+                             int64_t Hkv, int64_t D, int64_t BLK, int64_t MB, float* out) {
+  const int64_t group = Hq / Hkv;
+#pragma omp parallel for collapse(2) schedule(dynamic)
+  for (int64_t b = 0; b < B; b++) {
+    for (int64_t j = 0; j < Hq; j++) {
+      const int64_t h = j / group, L = lens[b];
+      double* sc = (double*)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
+      double mx = -INFINITY;
+      for (int64_t t = 0; t < L; t++) {
+        const int64_t blk = table[b * MB + t / BLK];
+        const uint16_t* krow = kc + ((blk * Hkv + h) * BLK + t % BLK) * D;
+        double acc = 0.0;
+        for (int64_t d = 0; d < D; d++)
+          acc += (double)bf16_bits_to_float(q[(b * Hq + j) * D + d]) * (double)bf16_bits_to_float(krow[d]);
+        sc[t] = acc / sqrt((double)D);
+        if (sc[t] > mx) mx = sc[t];
+      }
+      double den = 0.0;
+      for (int64_t t = 0; t < L; t++) {
+        sc[t] = exp(sc[t] - mx);
+        den += sc[t];
+      }
+      for (int64_t d = 0; d < D; d++) {
+        double o = 0.0;
+        for (int64_t t = 0; t < L; t++) {
+          const int64_t blk = table[b * MB + t / BLK];
+          o += sc[t] * (double)bf16_bits_to_float(vc[((blk * Hkv + h) * BLK + t % BLK) * D + d]);
+        }
+        out[(b * Hq + j) * D + d] = L > 0 ? (float)(o / den) : 0.0f;
+      }
+      free(sc);
+    }
+  }
 }

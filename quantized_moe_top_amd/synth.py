@@ -195,3 +195,60 @@ def decode_logits_pool(T: int, E: int, n: int, seed: int) -> torch.Tensor:
     touched experts between timed decode steps."""
     gen = torch.Generator().manual_seed(seed)
     return torch.randn((n, T, E), generator=gen, dtype=torch.float32)
+
+
+# ------------------------------------------------ decode attention inputs --
+@dataclasses.dataclass
+class AttnCase:
+    """One decode-attention step: one query token per sequence against a
+    block-paged key/value cache (``kcache``, ``vcache`` bf16
+    ``[NB, Hkv, BLK, D]``; ``table`` int32 ``[B, MB]`` maps block i of
+    sequence b to a physical block; ``lens`` int32 ``[B]``)."""
+    name: str
+    q: torch.Tensor
+    kcache: torch.Tensor
+    vcache: torch.Tensor
+    table: torch.Tensor
+    lens: torch.Tensor
+    block: int
+
+    def to(self, device) -> "AttnCase":
+        return dataclasses.replace(self, q=self.q.to(device), kcache=self.kcache.to(device),
+                                   vcache=self.vcache.to(device), table=self.table.to(device),
+                                   lens=self.lens.to(device))
+
+
+def make_attention(lens, Hq: int = 32, Hkv: int = 4, D: int = 128, block: int = 64,
+                   seed: int = 90, name: str = "attn") -> AttnCase:
+    """Seeded decode-attention inputs: q, K and V bf16 N(0, 1); each sequence
+    gets ceil(len / block) blocks (at least one), and the physical blocks of
+    all sequences are one seeded permutation, so consecutive positions of a
+    sequence sit in scattered blocks.  Draw order: permutation, q, K, V."""
+    gen = torch.Generator().manual_seed(seed)
+    lens = [int(n) for n in lens]
+    B = len(lens)
+    nblk = [max(1, -(-n // block)) for n in lens]
+    NB, MB = sum(nblk), max(nblk)
+    perm = torch.randperm(NB, generator=gen)
+    table = torch.zeros((B, MB), dtype=torch.int32)
+    pos = 0
+    for b, n in enumerate(nblk):
+        table[b, :n] = perm[pos:pos + n].to(torch.int32)
+        pos += n
+    q = torch.randn(B, Hq, D, generator=gen).to(torch.bfloat16)
+    kc = torch.randn(NB, Hkv, block, D, generator=gen).to(torch.bfloat16)
+    vc = torch.randn(NB, Hkv, block, D, generator=gen).to(torch.bfloat16)
+    return AttnCase(name, q, kc, vc, table, torch.tensor(lens, dtype=torch.int32), block)
+
+
+# Decode-attention workloads: the context lengths the pages quote their
+# decode gains at (32K and 128K), one sequence and a batch of eight.
+ATTN_WORKLOADS = {
+    "attn_decode_32k": dict(lens=[32768], seed=91),
+    "attn_decode_128k": dict(lens=[131072], seed=92),
+    "attn_decode_b8_32k": dict(lens=[32768] * 8, seed=93),
+}
+
+
+def make_attention_workload(name: str) -> AttnCase:
+    return make_attention(name=name, **ATTN_WORKLOADS[name])

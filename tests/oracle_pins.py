@@ -412,6 +412,59 @@ def pin_residual_out(orc):
                           _bf16_bits_rne(r.double().numpy() + yy.astype(np.float64)))
 
 
+# ------------------------------------------------------- decode attention --
+def _gather_kv(case, b):
+    """Logical [Hkv, L, D] keys and values of sequence b (fp64)."""
+    L = int(case.lens[b])
+    blk = case.table[b].long()
+    pos = torch.arange(L)
+    k = case.kcache.double()[blk[pos // case.block], :, pos % case.block, :]  # [L, Hkv, D]
+    v = case.vcache.double()[blk[pos // case.block], :, pos % case.block, :]
+    return k.permute(1, 0, 2), v.permute(1, 0, 2)
+
+
+def pin_attention_library(orc):
+    """Decode attention equals the library routine (torch
+    scaled_dot_product_attention in fp64, the KV heads repeated for their
+    query-head groups) to within fp32 rounding, through a scattered block
+    table, with a sequence of length 0 giving zeros."""
+    case = synth.make_attention([150, 64, 0, 1, 200], Hq=8, Hkv=2, D=32, block=16, seed=94)
+    got = orc.decode_attention(case.q, case.kcache, case.vcache, case.table, case.lens)
+    g = case.q.shape[1] // case.kcache.shape[1]
+    for b in range(case.q.shape[0]):
+        if int(case.lens[b]) == 0:
+            assert np.all(got[b] == 0)
+            continue
+        k, v = _gather_kv(case, b)
+        k, v = k.repeat_interleave(g, 0), v.repeat_interleave(g, 0)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            case.q[b].double()[:, None, :], k, v)[:, 0, :].numpy()
+        assert np.all(np.abs(got[b].astype(np.float64) - ref) <= 2 * _f32_ulp(ref) + 1e-12), b
+
+
+def pin_attention_closed_forms(orc):
+    """Equal keys give a uniform softmax, so every query head returns the
+    mean of its KV head's values; moving physical blocks (and the table with
+    them) changes nothing."""
+    case = synth.make_attention([96, 40], Hq=4, Hkv=2, D=16, block=16, seed=95)
+    kc = case.kcache.clone()
+    kc[:] = kc[0, :, 0:1, :]  # one key row everywhere, per KV head 0's first row
+    got = orc.decode_attention(case.q, kc, case.vcache, case.table, case.lens)
+    for b in range(2):
+        _, v = _gather_kv(case, b)
+        mean = v.mean(dim=1).numpy()  # [Hkv, D]
+        ref = np.repeat(mean, 2, axis=0)
+        assert np.all(np.abs(got[b] - ref) <= 4 * _f32_ulp(ref) + 1e-12)
+    base = orc.decode_attention(case.q, case.kcache, case.vcache, case.table, case.lens)
+    NB = case.kcache.shape[0]
+    perm = torch.randperm(NB, generator=torch.Generator().manual_seed(96))
+    kc2, vc2 = torch.empty_like(case.kcache), torch.empty_like(case.vcache)
+    kc2[perm] = case.kcache
+    vc2[perm] = case.vcache
+    moved = orc.decode_attention(case.q, kc2, vc2, perm[case.table.long()].to(torch.int32), case.lens)
+    assert np.array_equal(base, moved)
+
+
 PINS = [
     pin_route_golden, pin_route_bruteforce, pin_route_argsort, pin_route_weights_softmax,
     pin_blocks_golden, pin_blocks_invariants,
@@ -420,4 +473,5 @@ PINS = [
     pin_ffn_dense_masked, pin_ffn_token_subset, pin_expert_hidden_down,
     pin_router_logits,
     pin_rmsnorm_library, pin_rmsnorm_closed_forms, pin_residual_out,
+    pin_attention_library, pin_attention_closed_forms,
 ]

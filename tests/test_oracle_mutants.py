@@ -63,6 +63,16 @@ MUTATIONS = [
      "const double r = 1.0 / sqrt(ss / (double)H + eps);", "const double r = 1.0 / (sqrt(ss / (double)H) + eps);"),
     ("bf16 rounding truncates",
      "const double r = nearbyint(v / ulp) * ulp;", "const double r = trunc(v / ulp) * ulp;"),
+    ("attention scale dropped",
+     "sc[t] = acc / sqrt((double)D);", "sc[t] = acc;"),
+    ("attention KV head chosen by query head modulo",
+     "const int64_t h = j / group, L = lens[b];", "const int64_t h = j % Hkv, L = lens[b];"),
+    ("attention block offset ignored",
+     "const uint16_t* krow = kc + ((blk * Hkv + h) * BLK + t % BLK) * D;",
+     "const uint16_t* krow = kc + ((blk * Hkv + h) * BLK) * D;"),
+    ("attention softmax not normalised",
+     "out[(b * Hq + j) * D + d] = L > 0 ? (float)(o / den) : 0.0f;",
+     "out[(b * Hq + j) * D + d] = L > 0 ? (float)o : 0.0f;"),
     ("residual dropped",
      "out[i] = double_to_bf16_bits((double)bf16_bits_to_float(residual[i]) + (double)y[i]);",
      "out[i] = double_to_bf16_bits((double)y[i]);"),
