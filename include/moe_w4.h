@@ -278,6 +278,38 @@ int moe_ffn_forward_io(const moe_layer* layer, const uint16_t* x, const float* r
                        float* y, const moe_ffn_io* io, moe_route_info* info, void* workspace,
                        size_t workspace_bytes, void* stream);
 
+/* -------------------------------------------------- decode attention --
+ * A second workload, the one the pages' decode gains come from (page
+ * "Perplexity's Lily engine beats MLX by 35% on M5 Max", architecture
+ * paragraph: coalesced key-cache reads, grouped-query packing, a
+ * fixed-block cache layout).  One query token per sequence:
+ *   o[b][j] = softmax_t(q[b][j] . K_t / sqrt(D)) V  over t < seq_lens[b],
+ * the KV head of query head j being j / (Hq / Hkv); a sequence of length 0
+ * gives o = 0.  fp32 arithmetic, ranges of positions merged in fixed order
+ * (deterministic).
+ *   q:           device bf16 [B][Hq][D]
+ *   kcache, vcache: device bf16 [num_blocks][Hkv][block][D]: block n holds
+ *                block positions of one sequence
+ *   block_table: device int32 [B][max_blocks]: entry i of sequence b is the
+ *                block holding its positions i*block .. i*block+block-1;
+ *                entries outside [0, num_blocks) are skipped, never read
+ *                through
+ *   seq_lens:    device int32 [B], each <= max_len and <= max_blocks*block
+ *                (positions past max_len are not visited)
+ *   out:         device fp32 [B][Hq][D]
+ *   workspace:   device, >= moe_decode_attention_workspace_bytes(B, Hq,
+ *                Hkv, max_len), 16-byte aligned
+ * Supported: D == 128; Hq % Hkv == 0 with Hq / Hkv in {1, 2, 4, 8}; block
+ * >= 1; all pointers 16-byte aligned.  Enqueued on stream; nothing allocated.
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_UNSUPPORTED, MOE_ERR_ALIGN,
+ * MOE_ERR_WORKSPACE, MOE_ERR_HIP. */
+size_t moe_decode_attention_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t max_len);
+int moe_decode_attention(const uint16_t* q, const uint16_t* kcache, const uint16_t* vcache,
+                         const int32_t* block_table, const int32_t* seq_lens, int32_t B,
+                         int32_t Hq, int32_t Hkv, int32_t D, int32_t block, int32_t max_blocks,
+                         int32_t num_blocks, int32_t max_len, float* out, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------ per-stage timing --
  * The same layer as moe_ffn_forward (identical kernels and results), with a
  * timing event recorded on `stream` at every stage boundary, so that a

@@ -258,6 +258,28 @@ def rmsnorm(x: torch.Tensor, gamma: torch.Tensor, eps: float,
     return out
 
 
+def decode_attention(case, out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                     max_len: Optional[int] = None) -> torch.Tensor:
+    """``moe_decode_attention`` on a device ``synth.AttnCase``: fp32 [B, Hq, D]."""
+    B, Hq, D = case.q.shape
+    NB, Hkv, BLK, _ = case.kcache.shape
+    MB = case.table.shape[1]
+    if max_len is None:
+        max_len = int(case.lens.max().item()) if B else 0
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float32, device=case.q.device)
+    wsb = int(_L().moe_decode_attention_workspace_bytes(B, Hq, Hkv, max_len))
+    if workspace is None:
+        workspace = torch.empty(max(wsb, 16), dtype=torch.uint8, device=case.q.device)
+    _lib.check(_L().moe_decode_attention(
+        _dev(case.q, "q", torch.bfloat16), _dev(case.kcache, "kcache", torch.bfloat16),
+        _dev(case.vcache, "vcache", torch.bfloat16), _dev(case.table, "table", torch.int32),
+        _dev(case.lens, "lens", torch.int32), B, Hq, Hkv, D, BLK, MB, NB, max_len,
+        _dev(out, "out", torch.float32), _dev(workspace, "workspace", torch.uint8), workspace.numel(),
+        _stream()), "moe_decode_attention")
+    return out
+
+
 def ffn_io_workspace_bytes(layer, T: Optional[int] = None) -> int:
     T = layer.T if T is None else T
     return int(_L().moe_ffn_io_workspace_bytes(ctypes.byref(_dims(layer, T)),

@@ -544,6 +544,36 @@ int moe_rmsnorm(const uint16_t* x, const uint16_t* gamma, float eps, int32_t T, 
   return hip_status(moe::launch_rmsnorm(x, gamma, eps, T, H, out, (hipStream_t)stream), "rmsnorm");
 }
 
+size_t moe_decode_attention_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t max_len) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || max_len < 0) return 0;
+  const moe::AttnPlan pl = moe::attn_plan(B, Hkv, max_len);
+  return round_up((size_t)B * Hq * pl.nsplit * (128 + 2) * 4);
+}
+
+int moe_decode_attention(const uint16_t* q, const uint16_t* kcache, const uint16_t* vcache,
+                         const int32_t* block_table, const int32_t* seq_lens, int32_t B,
+                         int32_t Hq, int32_t Hkv, int32_t D, int32_t block, int32_t max_blocks,
+                         int32_t num_blocks, int32_t max_len, float* out, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || block < 1 || max_blocks < 1 || num_blocks < 1 || max_len < 0)
+    return fail(MOE_ERR_SHAPE, "need B >= 0, Hq, Hkv, block, max_blocks, num_blocks >= 1, max_len >= 0");
+  if (D != 128) return fail(MOE_ERR_UNSUPPORTED, "D = %d (only 128)", D);
+  const int g = Hq % Hkv ? 0 : Hq / Hkv;
+  if (g != 1 && g != 2 && g != 4 && g != 8)
+    return fail(MOE_ERR_UNSUPPORTED, "Hq / Hkv = %d / %d not in {1, 2, 4, 8}", Hq, Hkv);
+  if (B == 0) return ok();
+  if (!q || !kcache || !vcache || !block_table || !seq_lens || !out || !workspace)
+    return fail(MOE_ERR_NULL, "a pointer argument is NULL");
+  if (!aligned16(q) || !aligned16(kcache) || !aligned16(vcache) || !aligned16(out) || !aligned16(workspace))
+    return fail(MOE_ERR_ALIGN, "q, caches, out or workspace not 16-byte aligned");
+  const size_t need = moe_decode_attention_workspace_bytes(B, Hq, Hkv, max_len);
+  if (workspace_bytes < need) return fail(MOE_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
+  return hip_status(moe::launch_decode_attention(q, kcache, vcache, block_table, seq_lens, B, Hq, Hkv,
+                                                 block, max_blocks, num_blocks, max_len, out,
+                                                 (float*)workspace, (hipStream_t)stream),
+                    "decode_attention");
+}
+
 size_t moe_ffn_io_workspace_bytes(const moe_dims* d, int32_t has_router) {
   if (!d || check_dims(d) != MOE_OK) return 0;
   return ffn_layout(*d, has_router != 0, moe_ffn_block_m(d)).total + round_up((size_t)d->T * d->H * 2);

@@ -1,0 +1,205 @@
+// attn.hip -- a second workload: decode attention over a block-paged KV
+// cache with grouped query heads.  Page "Perplexity's Lily engine beats MLX
+// by 35% on M5 Max", architecture paragraph: the decode gains come from
+// coalesced key-cache reads, packing the query heads that share a KV head,
+// and a fixed-block cache layout.  Here:
+//  - the cache is [block][KV head][BLK positions][D] bf16, so the positions
+//    of one block and head are one contiguous run, found through a block
+//    table (scattered blocks cost nothing extra);
+//  - a workgroup owns (sequence, KV head, range of positions) and all GQ
+//    query heads of that KV head, so every key and value is read once and
+//    used GQ times;
+//  - 16 lanes share a position: lane i holds elements 8i..8i+7 of the 128,
+//    one 16-byte load, and the 16 lane groups of a workgroup read 16
+//    consecutive positions, 4 KiB contiguous per step;
+//  - scores are reduced over the 16 lanes by a butterfly (each step adds the
+//    same two values in every lane), and each lane group keeps a running
+//    maximum, denominator and weighted sum (softmax in base 2, the scores
+//    pre-scaled by log2(e) / sqrt(D));
+//  - the 16 lane groups are merged in LDS in fixed order into one partial
+//    result per range, and a second launch merges the ranges in fixed order,
+//    so the output does not depend on timing.
+#include "internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kAttnD = 128;
+constexpr int kAttnThreads = 256;  // 16 lane groups of 16
+constexpr int kAttnUnroll = 4;     // positions per lane group issued together
+
+struct AttnParams {
+  const uint16_t* q;
+  const uint16_t* kc;
+  const uint16_t* vc;
+  const int32_t* table;
+  const int32_t* lens;
+  float* part_m;    // [B][Hq][nsplit]
+  float* part_l;    // [B][Hq][nsplit]
+  float* part_acc;  // [B][Hq][nsplit][D]
+  int Hq, Hkv, block, max_blocks, num_blocks, nsplit, chunk;
+  float qscale;     // log2(e) / sqrt(D)
+};
+
+__device__ __forceinline__ float bf16f(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+template <int GQ>
+__global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(const AttnParams p) {
+  __shared__ float sm[16][GQ], sl[16][GQ];
+  __shared__ float sacc[16][GQ][kAttnD];
+  const int tid = threadIdx.x, grp = tid >> 4, sub = tid & 15;
+  const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int L = p.lens[b];
+  const int t0 = s * p.chunk, t1 = min(L, t0 + p.chunk);
+  // this lane's 8 query elements of each of the GQ heads, pre-scaled
+  float qf[GQ][8];
+#pragma unroll
+  for (int j = 0; j < GQ; j++) {
+    const uint4 v = *reinterpret_cast<const uint4*>(p.q + ((size_t)b * p.Hq + h * GQ + j) * kAttnD + 8 * sub);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      qf[j][2 * i] = bf16f(w[i] & 0xFFFFu) * p.qscale;
+      qf[j][2 * i + 1] = bf16f(w[i] >> 16) * p.qscale;
+    }
+  }
+  float m[GQ], l[GQ], acc[GQ][8];
+#pragma unroll
+  for (int j = 0; j < GQ; j++) {
+    m[j] = -INFINITY;
+    l[j] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; e++) acc[j][e] = 0.0f;
+  }
+  for (int tb = t0 + grp; tb < t1; tb += 16 * kAttnUnroll) {
+    uint4 kv[kAttnUnroll], vv[kAttnUnroll];
+    bool ok[kAttnUnroll];
+#pragma unroll
+    for (int u = 0; u < kAttnUnroll; u++) {
+      const int t = tb + 16 * u;
+      const int bi = t / p.block;
+      int blk = (t < t1 && bi < p.max_blocks) ? p.table[(size_t)b * p.max_blocks + bi] : -1;
+      ok[u] = blk >= 0 && blk < p.num_blocks;  // uniform over the lane group
+      const size_t row = ((size_t)(ok[u] ? blk : 0) * p.Hkv + h) * p.block + (ok[u] ? t % p.block : 0);
+      kv[u] = *reinterpret_cast<const uint4*>(p.kc + row * kAttnD + 8 * sub);
+      vv[u] = *reinterpret_cast<const uint4*>(p.vc + row * kAttnD + 8 * sub);
+    }
+#pragma unroll
+    for (int u = 0; u < kAttnUnroll; u++) {
+      if (!ok[u]) continue;
+      const uint32_t kw[4] = {kv[u].x, kv[u].y, kv[u].z, kv[u].w};
+      const uint32_t vw[4] = {vv[u].x, vv[u].y, vv[u].z, vv[u].w};
+      float kf[8], vf[8];
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        kf[2 * i] = bf16f(kw[i] & 0xFFFFu);
+        kf[2 * i + 1] = bf16f(kw[i] >> 16);
+        vf[2 * i] = bf16f(vw[i] & 0xFFFFu);
+        vf[2 * i + 1] = bf16f(vw[i] >> 16);
+      }
+#pragma unroll
+      for (int j = 0; j < GQ; j++) {
+        float sc = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; e++) sc += qf[j][e] * kf[e];
+#pragma unroll
+        for (int x = 1; x < 16; x <<= 1) sc += __shfl_xor(sc, x);
+        const float mn = fmaxf(m[j], sc);
+        const float c = exp2f(m[j] - mn), pr = exp2f(sc - mn);
+        l[j] = l[j] * c + pr;
+#pragma unroll
+        for (int e = 0; e < 8; e++) acc[j][e] = acc[j][e] * c + pr * vf[e];
+        m[j] = mn;
+      }
+    }
+  }
+  // merge the 16 lane groups, in group order
+  if (sub == 0)
+#pragma unroll
+    for (int j = 0; j < GQ; j++) {
+      sm[grp][j] = m[j];
+      sl[grp][j] = l[j];
+    }
+#pragma unroll
+  for (int j = 0; j < GQ; j++)
+#pragma unroll
+    for (int e = 0; e < 8; e++) sacc[grp][j][8 * sub + e] = acc[j][e];
+  __syncthreads();
+  const size_t base = ((size_t)b * p.Hq + h * GQ) * p.nsplit + s;
+  for (int i = tid; i < GQ * kAttnD; i += kAttnThreads) {
+    const int j = i / kAttnD, d = i % kAttnD;
+    float M = -INFINITY;
+    for (int g = 0; g < 16; g++) M = fmaxf(M, sm[g][j]);
+    float lt = 0.0f, at = 0.0f;
+    if (M != -INFINITY)
+      for (int g = 0; g < 16; g++) {
+        const float f = exp2f(sm[g][j] - M);  // 0 for an empty group
+        lt += sl[g][j] * f;
+        at += sacc[g][j][d] * f;
+      }
+    const size_t at_idx = base + (size_t)j * p.nsplit;
+    p.part_acc[at_idx * kAttnD + d] = at;
+    if (d == 0) {
+      p.part_m[at_idx] = M;
+      p.part_l[at_idx] = lt;
+    }
+  }
+}
+
+// Merges the ranges of each (sequence, query head), in range order.
+__global__ __launch_bounds__(kAttnD) void attn_combine_kernel(const float* __restrict__ part_m,
+                                                              const float* __restrict__ part_l,
+                                                              const float* __restrict__ part_acc,
+                                                              int nsplit, float* __restrict__ out) {
+  const int bq = blockIdx.x, d = threadIdx.x;
+  const float* pm = part_m + (size_t)bq * nsplit;
+  const float* pl = part_l + (size_t)bq * nsplit;
+  const float* pa = part_acc + (size_t)bq * nsplit * kAttnD;
+  float M = -INFINITY;
+  for (int s = 0; s < nsplit; s++) M = fmaxf(M, pm[s]);
+  float lt = 0.0f, at = 0.0f;
+  if (M != -INFINITY)
+    for (int s = 0; s < nsplit; s++) {
+      const float f = exp2f(pm[s] - M);
+      lt += pl[s] * f;
+      at += pa[(size_t)s * kAttnD + d] * f;
+    }
+  out[(size_t)bq * kAttnD + d] = lt > 0.0f ? at / lt : 0.0f;
+}
+
+}  // namespace
+
+AttnPlan attn_plan(int B, int Hkv, int max_len) {
+  // about 512 workgroups over (sequence, KV head, range), ranges of at
+  // least 64 positions, a multiple of 64
+  const int64_t want = std::max<int64_t>(1, 512 / std::max(1, B * Hkv));
+  int64_t chunk = (std::max(max_len, 1) + want - 1) / want;
+  chunk = std::max<int64_t>(64, (chunk + 63) / 64 * 64);
+  const int nsplit = (int)((std::max(max_len, 1) + chunk - 1) / chunk);
+  return AttnPlan{nsplit, (int)chunk};
+}
+
+hipError_t launch_decode_attention(const uint16_t* q, const uint16_t* kc, const uint16_t* vc,
+                                   const int32_t* table, const int32_t* lens, int B, int Hq,
+                                   int Hkv, int block, int max_blocks, int num_blocks,
+                                   int max_len, float* out, float* ws, hipStream_t s) {
+  if (B <= 0) return hipSuccess;
+  const AttnPlan pl = attn_plan(B, Hkv, max_len);
+  const size_t nq = (size_t)B * Hq * pl.nsplit;
+  AttnParams p{q, kc, vc, table, lens, ws, ws + nq, ws + 2 * nq, Hq, Hkv, block, max_blocks,
+               num_blocks, pl.nsplit, pl.chunk, 1.4426950408889634f / sqrtf((float)kAttnD)};
+  const dim3 grid(pl.nsplit, Hkv, B);
+  switch (Hq / Hkv) {
+    case 1: attn_split_kernel<1><<<grid, kAttnThreads, 0, s>>>(p); break;
+    case 2: attn_split_kernel<2><<<grid, kAttnThreads, 0, s>>>(p); break;
+    case 4: attn_split_kernel<4><<<grid, kAttnThreads, 0, s>>>(p); break;
+    case 8: attn_split_kernel<8><<<grid, kAttnThreads, 0, s>>>(p); break;
+    default: return hipErrorInvalidValue;
+  }
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  attn_combine_kernel<<<B * Hq, kAttnD, 0, s>>>(ws, ws + nq, ws + 2 * nq, pl.nsplit, out);
+  return hipGetLastError();
+}
+
+}  // namespace moe

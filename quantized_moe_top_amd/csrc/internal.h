@@ -294,6 +294,19 @@ hipError_t launch_combine(const void* y_sorted, bool pack24, const int32_t* pair
                           int T, int H, int k, hipStream_t s, const uint16_t* residual = nullptr,
                           uint16_t* out = nullptr);
 
+// Decode attention (a second workload): ranges of positions per workgroup.
+struct AttnPlan {
+  int nsplit, chunk;
+};
+AttnPlan attn_plan(int B, int Hkv, int max_len);
+// q bf16 [B][Hq][128]; kc, vc bf16 [num_blocks][Hkv][block][128]; table int32
+// [B][max_blocks]; lens int32 [B] (<= max_len); out fp32 [B][Hq][128]; ws:
+// B * Hq * nsplit * 130 floats.  Hq / Hkv in {1, 2, 4, 8}.
+hipError_t launch_decode_attention(const uint16_t* q, const uint16_t* kc, const uint16_t* vc,
+                                   const int32_t* table, const int32_t* lens, int B, int Hq,
+                                   int Hkv, int block, int max_blocks, int num_blocks,
+                                   int max_len, float* out, float* ws, hipStream_t s);
+
 // RMSNorm in front of the layer: out[t][h] = bf16(x[t][h] * gamma[h] /
 // sqrt(mean_h x[t][h]^2 + eps)) (bf16 in and out, fp32 arithmetic, H % 8 == 0).
 hipError_t launch_rmsnorm(const uint16_t* x, const uint16_t* gamma, float eps, int T, int H,

@@ -203,3 +203,19 @@ def test_rmsnorm_and_io_validation(L):
     assert io_call(_lib.FfnIO(A, 1e-6, 0, 0), wsb=need_plain) == WS  # no room for the normalised x
     lay.dims.H = 200
     assert io_call(_lib.FfnIO(0, 1e-6, 0, 0)) == UNSUP       # same checks as moe_ffn_forward
+
+
+def test_decode_attention_validation(L):
+    def att(B=2, Hq=32, Hkv=4, D=128, blk=64, mb=4, nb=8, ml=256, ws=A, wsb=1 << 30, q=A):
+        return L.moe_decode_attention(q, A, A, A, A, B, Hq, Hkv, D, blk, mb, nb, ml, A, ws, wsb, None)
+    assert att(D=64) == UNSUP
+    assert att(Hq=12, Hkv=4) == UNSUP               # group of 3
+    assert att(Hq=30, Hkv=4) == UNSUP               # not a multiple
+    assert att(Hq=64, Hkv=4) == UNSUP               # group of 16
+    assert att(blk=0) == SHAPE
+    assert att(nb=0) == SHAPE
+    assert att(q=0) == NULL
+    assert att(q=A + 2) == ALIGN
+    assert att(wsb=8) == WS
+    assert att(B=0) == OK                           # nothing enqueued
+    assert L.moe_decode_attention_workspace_bytes(1, 32, 4, 32768) >= 32 * 130 * 4

@@ -443,6 +443,52 @@ def test_ffn_io(orc, case):
     assert np.mean(got == exact) >= 0.999
 
 
+# ---------------------------------------------------- decode attention --
+# fp32 arithmetic over at most 131072 positions (products of bf16 values are
+# exact in fp32; the sums and the rescaling by exp2 differences carry about
+# 1e-6 relative error each): relative L2 <= 1e-4, max abs <= 1e-3 * rms.
+ATTN_REL_L2, ATTN_MAX_ABS = 1e-4, 1e-3
+
+
+def _attn_check(got, ref, what):
+    got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    err = got - ref
+    rel = np.linalg.norm(err) / max(np.linalg.norm(ref), 1e-30)
+    rms = float(np.sqrt(np.mean(ref ** 2))) if ref.size else 0.0
+    mx = float(np.abs(err).max()) if err.size else 0.0
+    say(f"  {what}: relL2 {rel:.3e} maxabs {mx:.3e} (rms {rms:.3e})")
+    assert rel <= ATTN_REL_L2 and mx <= ATTN_MAX_ABS * rms + 1e-30, what
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(32, 4), (4, 4), (8, 4), (16, 4)])
+def test_decode_attention(orc, Hq, Hkv):
+    """Ragged lengths (empty, one position, partial blocks, a block's last
+    position, several ranges of a workgroup), scattered blocks, every
+    grouped-query factor; element by element against the oracle."""
+    case = synth.make_attention([150, 0, 1, 64, 4097, 200, 63], Hq=Hq, Hkv=Hkv, D=128, block=64,
+                                seed=97 + Hq)
+    out = api.decode_attention(case.to(DEV))
+    torch.cuda.synchronize()
+    ref = orc.decode_attention(case.q, case.kcache, case.vcache, case.table, case.lens)
+    got = cpu(out)
+    assert np.all(got[1] == 0)
+    _attn_check(got, ref, f"attention Hq={Hq} Hkv={Hkv}")
+
+
+@pytest.mark.parametrize("name", ["attn_decode_32k", "attn_decode_128k", "attn_decode_b8_32k"])
+def test_decode_attention_workloads(orc, name):
+    """The benchmark workloads at full size, every output against the
+    oracle, and the output identical on a second call (fixed merge order)."""
+    case = synth.make_attention_workload(name)
+    d = case.to(DEV)
+    out = api.decode_attention(d)
+    out2 = api.decode_attention(d)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
+    ref = orc.decode_attention(case.q, case.kcache, case.vcache, case.table, case.lens)
+    _attn_check(cpu(out), ref, name)
+
+
 @pytest.mark.parametrize("case", ["prefill_t512", "ragged", "imbalanced_t8192"])
 def test_ffn_host_blockmap_identical(case):
     """The host-round-trip ablation runs the same kernels on a block map the
