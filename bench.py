@@ -170,6 +170,8 @@ def main():
     torch.cuda.set_device(dev)
 
     name = args.workload
+    if name in synth.ATTN_WORKLOADS:
+        return bench_attention(args, name, dev)
     log(f"[bench] drawing workload {name}")
     host = synth.make_layer(name)
     # the banks are packed once into the kernels' layout (load time, untimed)
@@ -416,6 +418,72 @@ def main():
     if io_res:
         out["io"] = io_res
     print(json.dumps(out), flush=True)
+
+
+def bench_attention(args, name: str, dev) -> None:
+    """The second workload: one decode-attention step (one query token per
+    sequence against its block-paged KV cache) per step, the cache rotated
+    over copies that together exceed 1 GiB, so every step reads it from
+    HBM.  Prints the same JSON line shape as the layer workloads."""
+    import numpy as np
+    import torch
+
+    from quantized_moe_top_amd import api, synth
+
+    host = synth.make_attention_workload(name)
+    case = host.to(dev)
+    B, Hq, D = case.q.shape
+    NB, Hkv, BLK, _ = case.kcache.shape
+    kv_bytes = 2 * int(host.lens.sum()) * Hkv * D * 2  # keys and values read once
+    R = max(1, -(-ROTATE_BYTES // (2 * case.kcache.numel() * 2)))
+    copies = [case] + [synth.AttnCase(name, case.q, case.kcache.clone(), case.vcache.clone(), case.table,
+                                      case.lens, BLK) for _ in range(R - 1)]
+    max_len = int(host.lens.max())
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(16, int(api._L().moe_decode_attention_workspace_bytes(B, Hq, Hkv, max_len))),
+                     dtype=torch.uint8, device=dev)
+    step = lambda i: api.decode_attention(copies[i % R], out=out, workspace=ws, max_len=max_len)
+    log(f"[bench] {name}: B={B} context {max_len} Hq={Hq} Hkv={Hkv} D={D} block={BLK}; "
+        f"{kv_bytes / 2**20:.1f} MiB of K and V per step, {R} copies")
+    for i in range(args.warmup):
+        step(i)
+    K = args.steps
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for i in range(K):
+        step(i)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / K
+    byts = kv_bytes + B * Hq * D * (2 + 4)
+    achieved = byts / (ms * 1e-3) / 1e9
+    line = {
+        "metric": "decode attention tokens/s (one query token per sequence, block-paged KV cache)",
+        "value": round(B / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms, 6), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp32", "data": "synthetic",
+        "config": {"workload": name, "B": B, "context": max_len, "Hq": Hq, "Hkv": Hkv, "D": D,
+                   "block": BLK, "launch": "eager"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "attention step (split + merge launches)",
+                     "algorithmic_bytes": int(byts), "avg_launch_us": round(ms * 1e3, 3)},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        orc = oracle.get()
+        t0 = time.perf_counter()
+        reps = 0
+        while True:
+            orc.decode_attention(host.q, host.kcache, host.vcache, host.table, host.lens)
+            reps += 1
+            if time.perf_counter() - t0 >= args.cpu_seconds or reps >= 20:
+                break
+        dt = (time.perf_counter() - t0) / reps
+        line["cpu_baseline"] = {"value": round(B / dt, 3), "unit": "tokens/s", "cores": orc.num_threads(),
+                                "kind": "oracle", "sample": f"{reps} whole steps, {reps * dt:.1f} s"}
+    print(json.dumps(line), flush=True)
 
 
 def cpu_baseline(host, min_seconds: float) -> dict:

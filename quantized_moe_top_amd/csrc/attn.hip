@@ -12,10 +12,11 @@
 //  - 16 lanes share a position: lane i holds elements 8i..8i+7 of the 128,
 //    one 16-byte load, and the 16 lane groups of a workgroup read 16
 //    consecutive positions, 4 KiB contiguous per step;
-//  - scores are reduced over the 16 lanes by a butterfly (each step adds the
-//    same two values in every lane), and each lane group keeps a running
+//  - scores are reduced over the 16 lanes on DPP moves (each step adds the
+//    same two values in both partners), and each lane group keeps a running
 //    maximum, denominator and weighted sum (softmax in base 2, the scores
-//    pre-scaled by log2(e) / sqrt(D));
+//    pre-scaled by log2(e) / sqrt(D)), rescaled once per step of four
+//    positions;
 //  - the 16 lane groups are merged in LDS in fixed order into one partial
 //    result per range, and a second launch merges the ranges in fixed order,
 //    so the output does not depend on timing.
@@ -42,6 +43,21 @@ struct AttnParams {
 };
 
 __device__ __forceinline__ float bf16f(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// Sum over the 16 lanes of a row, on DPP: partners lane ^ 1 and lane ^ 2 (quad
+// permutations), then the mirrors within 8 and within 16 lanes; each step
+// adds the same two values in both partners, so every lane ends with the
+// same total.
+__device__ __forceinline__ float row16_sum(float v) {
+#define MOE_DPP_ADD(ctrl) \
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), ctrl, 0xF, 0xF, false))
+  MOE_DPP_ADD(0xB1);   // quad_perm 1,0,3,2
+  MOE_DPP_ADD(0x4E);   // quad_perm 2,3,0,1
+  MOE_DPP_ADD(0x141);  // row_half_mirror
+  MOE_DPP_ADD(0x140);  // row_mirror
+#undef MOE_DPP_ADD
+  return v;
+}
 
 template <int GQ>
 __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(const AttnParams p) {
@@ -84,32 +100,56 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(const AttnPara
       kv[u] = *reinterpret_cast<const uint4*>(p.kc + row * kAttnD + 8 * sub);
       vv[u] = *reinterpret_cast<const uint4*>(p.vc + row * kAttnD + 8 * sub);
     }
+    // scores of the step's positions (skipped ones: -inf), then per head one
+    // rescale of the running sums for the whole step
+    float sc[kAttnUnroll][GQ];
 #pragma unroll
     for (int u = 0; u < kAttnUnroll; u++) {
-      if (!ok[u]) continue;
       const uint32_t kw[4] = {kv[u].x, kv[u].y, kv[u].z, kv[u].w};
-      const uint32_t vw[4] = {vv[u].x, vv[u].y, vv[u].z, vv[u].w};
-      float kf[8], vf[8];
+      float kf[8];
 #pragma unroll
       for (int i = 0; i < 4; i++) {
         kf[2 * i] = bf16f(kw[i] & 0xFFFFu);
         kf[2 * i + 1] = bf16f(kw[i] >> 16);
+      }
+#pragma unroll
+      for (int j = 0; j < GQ; j++) {
+        float d = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; e++) d += qf[j][e] * kf[e];
+        sc[u][j] = ok[u] ? row16_sum(d) : -INFINITY;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < GQ; j++) {
+      float mn = m[j];
+#pragma unroll
+      for (int u = 0; u < kAttnUnroll; u++) mn = fmaxf(mn, sc[u][j]);
+      if (mn == -INFINITY) continue;  // nothing yet (uniform over the lane group)
+      const float c = exp2f(m[j] - mn);
+      l[j] *= c;
+#pragma unroll
+      for (int e = 0; e < 8; e++) acc[j][e] *= c;
+      m[j] = mn;
+#pragma unroll
+      for (int u = 0; u < kAttnUnroll; u++) sc[u][j] = exp2f(sc[u][j] - mn);  // 0 when skipped
+    }
+#pragma unroll
+    for (int u = 0; u < kAttnUnroll; u++) {
+      const uint32_t vw[4] = {vv[u].x, vv[u].y, vv[u].z, vv[u].w};
+      float vf[8];
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
         vf[2 * i] = bf16f(vw[i] & 0xFFFFu);
         vf[2 * i + 1] = bf16f(vw[i] >> 16);
       }
 #pragma unroll
       for (int j = 0; j < GQ; j++) {
-        float sc = 0.0f;
+        if (m[j] == -INFINITY) continue;
+        const float pr = sc[u][j];
+        l[j] += pr;
 #pragma unroll
-        for (int e = 0; e < 8; e++) sc += qf[j][e] * kf[e];
-#pragma unroll
-        for (int x = 1; x < 16; x <<= 1) sc += __shfl_xor(sc, x);
-        const float mn = fmaxf(m[j], sc);
-        const float c = exp2f(m[j] - mn), pr = exp2f(sc - mn);
-        l[j] = l[j] * c + pr;
-#pragma unroll
-        for (int e = 0; e < 8; e++) acc[j][e] = acc[j][e] * c + pr * vf[e];
-        m[j] = mn;
+        for (int e = 0; e < 8; e++) acc[j][e] += pr * vf[e];
       }
     }
   }
