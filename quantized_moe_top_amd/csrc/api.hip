@@ -566,6 +566,8 @@ int moe_decode_attention(const uint16_t* q, const uint16_t* kcache, const uint16
     return fail(MOE_ERR_NULL, "a pointer argument is NULL");
   if (!aligned16(q) || !aligned16(kcache) || !aligned16(vcache) || !aligned16(out) || !aligned16(workspace))
     return fail(MOE_ERR_ALIGN, "q, caches, out or workspace not 16-byte aligned");
+  if (moe::attn_plan(B, Hkv, max_len).nsplit > 4096)
+    return fail(MOE_ERR_UNSUPPORTED, "max_len = %d above 4194304", max_len);
   const size_t need = moe_decode_attention_workspace_bytes(B, Hq, Hkv, max_len);
   if (workspace_bytes < need) return fail(MOE_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
   return hip_status(moe::launch_decode_attention(q, kcache, vcache, block_table, seq_lens, B, Hq, Hkv,

@@ -15,8 +15,9 @@
 //  - scores are reduced over the 16 lanes on DPP moves (each step adds the
 //    same two values in both partners), and each lane group keeps a running
 //    maximum, denominator and weighted sum (softmax in base 2, the scores
-//    pre-scaled by log2(e) / sqrt(D)), rescaled once per step of four
-//    positions;
+//    scaled by log2(e) / sqrt(D)), rescaled once per step of four positions;
+//    the dot products take bf16 pairs straight from the loads
+//    (v_dot2_f32_bf16, fp32 sums);
 //  - the 16 lane groups are merged in LDS in fixed order into one partial
 //    result per range, and a second launch merges the ranges in fixed order,
 //    so the output does not depend on timing.
@@ -28,6 +29,7 @@ namespace {
 constexpr int kAttnD = 128;
 constexpr int kAttnThreads = 256;  // 16 lane groups of 16
 constexpr int kAttnUnroll = 4;     // positions per lane group issued together
+constexpr int kAttnTable = 1026;   // block-table entries of one range held in LDS (1024 / block + 2)
 
 struct AttnParams {
   const uint16_t* q;
@@ -43,6 +45,12 @@ struct AttnParams {
 };
 
 __device__ __forceinline__ float bf16f(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,
+                                         false);
+}
 
 // Sum over the 16 lanes of a row, on DPP: partners lane ^ 1 and lane ^ 2 (quad
 // permutations), then the mirrors within 8 and within 16 lanes; each step
@@ -67,18 +75,11 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(const AttnPara
   const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int L = p.lens[b];
   const int t0 = s * p.chunk, t1 = min(L, t0 + p.chunk);
-  // this lane's 8 query elements of each of the GQ heads, pre-scaled
-  float qf[GQ][8];
+  // this lane's 8 query elements of each of the GQ heads, as bf16 pairs
+  uint4 qp[GQ];
 #pragma unroll
-  for (int j = 0; j < GQ; j++) {
-    const uint4 v = *reinterpret_cast<const uint4*>(p.q + ((size_t)b * p.Hq + h * GQ + j) * kAttnD + 8 * sub);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-      qf[j][2 * i] = bf16f(w[i] & 0xFFFFu) * p.qscale;
-      qf[j][2 * i + 1] = bf16f(w[i] >> 16) * p.qscale;
-    }
-  }
+  for (int j = 0; j < GQ; j++)
+    qp[j] = *reinterpret_cast<const uint4*>(p.q + ((size_t)b * p.Hq + h * GQ + j) * kAttnD + 8 * sub);
   float m[GQ], l[GQ], acc[GQ][8];
 #pragma unroll
   for (int j = 0; j < GQ; j++) {
@@ -87,37 +88,44 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(const AttnPara
 #pragma unroll
     for (int e = 0; e < 8; e++) acc[j][e] = 0.0f;
   }
-  for (int tb = t0 + grp; tb < t1; tb += 16 * kAttnUnroll) {
-    uint4 kv[kAttnUnroll], vv[kAttnUnroll];
-    bool ok[kAttnUnroll];
+  // the block-table entries of this range, once, in LDS (the loads below
+  // then depend on nothing but LDS)
+  __shared__ int tbl[kAttnTable];
+  const int bi0 = t0 / p.block;
+  const int nbi = t1 > t0 ? (t1 - 1) / p.block - bi0 + 1 : 0;  // <= kAttnTable (host plan)
+  for (int i = tid; i < nbi; i += kAttnThreads) {
+    const int bi = bi0 + i;
+    const int blk = bi < p.max_blocks ? p.table[(size_t)b * p.max_blocks + bi] : -1;
+    tbl[i] = (blk >= 0 && blk < p.num_blocks) ? blk : -1;
+  }
+  __syncthreads();
+  // one step: positions tb + 16 u of this lane group; past the range or in
+  // a malformed block: a valid row is read and not used
+  auto load_step = [&](int tb, uint4 (&kv)[kAttnUnroll], uint4 (&vv)[kAttnUnroll], bool (&ok)[kAttnUnroll]) {
 #pragma unroll
     for (int u = 0; u < kAttnUnroll; u++) {
       const int t = tb + 16 * u;
-      const int bi = t / p.block;
-      int blk = (t < t1 && bi < p.max_blocks) ? p.table[(size_t)b * p.max_blocks + bi] : -1;
-      ok[u] = blk >= 0 && blk < p.num_blocks;  // uniform over the lane group
+      const int blk = t < t1 ? tbl[t / p.block - bi0] : -1;
+      ok[u] = blk >= 0;  // uniform over the lane group
       const size_t row = ((size_t)(ok[u] ? blk : 0) * p.Hkv + h) * p.block + (ok[u] ? t % p.block : 0);
       kv[u] = *reinterpret_cast<const uint4*>(p.kc + row * kAttnD + 8 * sub);
       vv[u] = *reinterpret_cast<const uint4*>(p.vc + row * kAttnD + 8 * sub);
     }
+  };
+  auto compute_step = [&](const uint4 (&kv)[kAttnUnroll], const uint4 (&vv)[kAttnUnroll], const bool (&ok)[kAttnUnroll]) {
     // scores of the step's positions (skipped ones: -inf), then per head one
     // rescale of the running sums for the whole step
     float sc[kAttnUnroll][GQ];
 #pragma unroll
     for (int u = 0; u < kAttnUnroll; u++) {
-      const uint32_t kw[4] = {kv[u].x, kv[u].y, kv[u].z, kv[u].w};
-      float kf[8];
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        kf[2 * i] = bf16f(kw[i] & 0xFFFFu);
-        kf[2 * i + 1] = bf16f(kw[i] >> 16);
-      }
 #pragma unroll
       for (int j = 0; j < GQ; j++) {
-        float d = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 8; e++) d += qf[j][e] * kf[e];
-        sc[u][j] = ok[u] ? row16_sum(d) : -INFINITY;
+        // products of bf16 pairs summed in fp32 (v_dot2_f32_bf16)
+        float d = dot2_bf16(qp[j].x, kv[u].x, 0.0f);
+        d = dot2_bf16(qp[j].y, kv[u].y, d);
+        d = dot2_bf16(qp[j].z, kv[u].z, d);
+        d = dot2_bf16(qp[j].w, kv[u].w, d);
+        sc[u][j] = ok[u] ? row16_sum(d) * p.qscale : -INFINITY;
       }
     }
 #pragma unroll
@@ -151,6 +159,28 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(const AttnPara
 #pragma unroll
         for (int e = 0; e < 8; e++) acc[j][e] += pr * vf[e];
       }
+    }
+  };
+  // two register sets: the next step's loads are in flight while this one
+  // is computed (every step issues the same 2 * kAttnUnroll loads, so one
+  // count-based wait leaves exactly the newer set outstanding)
+  uint4 ka[kAttnUnroll], va[kAttnUnroll], kb[kAttnUnroll], vb[kAttnUnroll];
+  bool oa[kAttnUnroll], ob[kAttnUnroll];
+  constexpr int kStep = 16 * kAttnUnroll;
+  int tb = t0 + grp;
+  if (t1 > t0) {
+    load_step(tb, ka, va, oa);
+    while (true) {
+      load_step(tb + kStep, kb, vb, ob);
+      wait_vm<2 * kAttnUnroll>();
+      compute_step(ka, va, oa);
+      tb += kStep;
+      if (tb - grp >= t1) break;
+      load_step(tb + kStep, ka, va, oa);
+      wait_vm<2 * kAttnUnroll>();
+      compute_step(kb, vb, ob);
+      tb += kStep;
+      if (tb - grp >= t1) break;
     }
   }
   // merge the 16 lane groups, in group order
@@ -186,35 +216,58 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_kernel(const AttnPara
   }
 }
 
-// Merges the ranges of each (sequence, query head), in range order.
+// Merges the ranges of each (sequence, query head), in range order: the
+// ranges' maxima and denominators go through LDS (loaded in parallel), then
+// each thread sums its output element over the ranges with independent loads.
+constexpr int kMaxSplit = 4096;
+
 __global__ __launch_bounds__(kAttnD) void attn_combine_kernel(const float* __restrict__ part_m,
                                                               const float* __restrict__ part_l,
                                                               const float* __restrict__ part_acc,
                                                               int nsplit, float* __restrict__ out) {
+  __shared__ float fm[kMaxSplit];
+  __shared__ float red[kAttnD];
   const int bq = blockIdx.x, d = threadIdx.x;
   const float* pm = part_m + (size_t)bq * nsplit;
   const float* pl = part_l + (size_t)bq * nsplit;
   const float* pa = part_acc + (size_t)bq * nsplit * kAttnD;
   float M = -INFINITY;
-  for (int s = 0; s < nsplit; s++) M = fmaxf(M, pm[s]);
+  for (int s = d; s < nsplit; s += kAttnD) {
+    fm[s] = pm[s];
+    M = fmaxf(M, fm[s]);
+  }
+  red[d] = M;
+  __syncthreads();
+  M = -INFINITY;
+  for (int i = 0; i < kAttnD; i++) M = fmaxf(M, red[i]);
+  // factors exp2(m_s - M) (0 for empty ranges), and the denominator in range order
+  for (int s = d; s < nsplit; s += kAttnD) fm[s] = M == -INFINITY ? 0.0f : exp2f(fm[s] - M);
+  __syncthreads();
   float lt = 0.0f, at = 0.0f;
-  if (M != -INFINITY)
-    for (int s = 0; s < nsplit; s++) {
-      const float f = exp2f(pm[s] - M);
-      lt += pl[s] * f;
-      at += pa[(size_t)s * kAttnD + d] * f;
-    }
+  constexpr int U = 8;
+  for (int s0 = 0; s0 < nsplit; s0 += U) {
+    float v[U];
+#pragma unroll
+    for (int u = 0; u < U; u++) v[u] = s0 + u < nsplit ? pa[(size_t)(s0 + u) * kAttnD + d] : 0.0f;
+#pragma unroll
+    for (int u = 0; u < U; u++)
+      if (s0 + u < nsplit) {
+        lt += pl[s0 + u] * fm[s0 + u];
+        at += v[u] * fm[s0 + u];
+      }
+  }
   out[(size_t)bq * kAttnD + d] = lt > 0.0f ? at / lt : 0.0f;
 }
 
 }  // namespace
 
 AttnPlan attn_plan(int B, int Hkv, int max_len) {
-  // about 512 workgroups over (sequence, KV head, range), ranges of at
-  // least 64 positions, a multiple of 64
+  // about 512 workgroups over (sequence, KV head, range); ranges of 64 to
+  // 1024 positions, a multiple of 64 (so a range spans at most 1024 / block
+  // + 2 table entries)
   const int64_t want = std::max<int64_t>(1, 512 / std::max(1, B * Hkv));
   int64_t chunk = (std::max(max_len, 1) + want - 1) / want;
-  chunk = std::max<int64_t>(64, (chunk + 63) / 64 * 64);
+  chunk = std::min<int64_t>(1024, std::max<int64_t>(64, (chunk + 63) / 64 * 64));
   const int nsplit = (int)((std::max(max_len, 1) + chunk - 1) / chunk);
   return AttnPlan{nsplit, (int)chunk};
 }
