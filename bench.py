@@ -462,7 +462,7 @@ def bench_attention(args, name: str, dev) -> None:
         "metric": "decode attention tokens/s (one query token per sequence, block-paged KV cache)",
         "value": round(B / (ms * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": K,
         "warmup": args.warmup, "ms_per_step": round(ms, 6), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "fp32", "data": "synthetic",
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": name, "B": B, "context": max_len, "Hq": Hq, "Hkv": Hkv, "D": D,
                    "block": BLK, "launch": "eager"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,

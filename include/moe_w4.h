@@ -288,8 +288,9 @@ int moe_ffn_forward_io(const moe_layer* layer, const uint16_t* x, const float* r
  * gives o = 0.  fp32 arithmetic, ranges of positions merged in fixed order
  * (deterministic).
  *   q:           device bf16 [B][Hq][D]
- *   kcache, vcache: device bf16 [num_blocks][Hkv][block][D]: block n holds
- *                block positions of one sequence
+ *   kcache:      device bf16 [num_blocks][Hkv][block][D] (position-major)
+ *   vcache:      device bf16 [num_blocks][Hkv][D][block] (element-major);
+ *                block n of either holds block positions of one sequence
  *   block_table: device int32 [B][max_blocks]: entry i of sequence b is the
  *                block holding its positions i*block .. i*block+block-1;
  *                entries outside [0, num_blocks) are skipped, never read
@@ -299,8 +300,8 @@ int moe_ffn_forward_io(const moe_layer* layer, const uint16_t* x, const float* r
  *   out:         device fp32 [B][Hq][D]
  *   workspace:   device, >= moe_decode_attention_workspace_bytes(B, Hq,
  *                Hkv, max_len), 16-byte aligned
- * Supported: D == 128; Hq % Hkv == 0 with Hq / Hkv in {1, 2, 4, 8}; block
- * >= 1; all pointers 16-byte aligned.  Enqueued on stream; nothing allocated.
+ * Supported: D == 128; Hq % Hkv == 0 with Hq / Hkv in {1, 2, 4, 8}; block a
+ * multiple of 8; all pointers 16-byte aligned.  Enqueued on stream; nothing allocated.
  * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_UNSUPPORTED, MOE_ERR_ALIGN,
  * MOE_ERR_WORKSPACE, MOE_ERR_HIP. */
 size_t moe_decode_attention_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t max_len);

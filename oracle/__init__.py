@@ -205,8 +205,8 @@ class Oracle:
 
     # -- decode attention (second workload) ------------------------------
     def decode_attention(self, q, kcache, vcache, table, lens) -> np.ndarray:
-        """fp32 [B, Hq, D]: q bf16 [B, Hq, D]; caches bf16 [NB, Hkv, BLK, D];
-        table int32 [B, MB]; lens int32 [B]."""
+        """fp32 [B, Hq, D]: q bf16 [B, Hq, D]; keys bf16 [NB, Hkv, BLK, D];
+        values bf16 [NB, Hkv, D, BLK]; table int32 [B, MB]; lens int32 [B]."""
         q = _np(q, np.uint16)
         kc = _np(kcache, np.uint16)
         vc = _np(vcache, np.uint16)
@@ -214,7 +214,7 @@ class Oracle:
         ln = _np(lens, np.int32).ravel()
         B, Hq, D = q.shape
         NB, Hkv, BLK, D2 = kc.shape
-        assert D2 == D and vc.shape == kc.shape and tb.shape[0] == B and ln.size == B and Hq % Hkv == 0
+        assert D2 == D and vc.shape == (NB, Hkv, D, BLK) and tb.shape[0] == B and ln.size == B and Hq % Hkv == 0
         assert np.all(ln <= tb.shape[1] * BLK) and np.all((tb >= 0) & (tb < NB))
         out = np.empty((B, Hq, D), np.float32)
         self.lib.oracle_decode_attention(_ptr(q), _ptr(kc), _ptr(vc), _ptr(tb), _ptr(ln), B, Hq, Hkv, D,

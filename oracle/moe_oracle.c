@@ -296,8 +296,9 @@ void oracle_residual_out(const uint16_t* residual, const float* y, int64_t n, ui
     out[i] = double_to_bf16_bits((double)bf16_bits_to_float(residual[i]) + (double)y[i]);
 }
 
-/* Decode attention.  q: bf16 [B][Hq][D]; kc, vc: bf16 [NB][Hkv][BLK][D] (block
- * n holds cache positions of one sequence, BLK per block); table: int32
+/* Decode attention.  q: bf16 [B][Hq][D]; kc: bf16 [NB][Hkv][BLK][D] and vc:
+ * bf16 [NB][Hkv][D][BLK] (block n holds BLK cache positions of one sequence;
+ * keys position-major, values element-major); table: int32
  * [B][MB], table[b][i] = the block holding positions i*BLK .. i*BLK+BLK-1 of
  * sequence b; lens: int32 [B].  For each sequence b and query head j (KV head
  * j / (Hq / Hkv)):
@@ -332,7 +333,7 @@ void oracle_decode_attention(const uint16_t* q, const uint16_t* kc, const uint16
         double o = 0.0;
         for (int64_t t = 0; t < L; t++) {
           const int64_t blk = table[b * MB + t / BLK];
-          o += sc[t] * (double)bf16_bits_to_float(vc[((blk * Hkv + h) * BLK + t % BLK) * D + d]);
+          o += sc[t] * (double)bf16_bits_to_float(vc[((blk * Hkv + h) * D + d) * BLK + t % BLK]);
         }
         out[(b * Hq + j) * D + d] = L > 0 ? (float)(o / den) : 0.0f;
       }

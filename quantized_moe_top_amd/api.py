@@ -263,6 +263,8 @@ def decode_attention(case, out: Optional[torch.Tensor] = None, workspace: Option
     """``moe_decode_attention`` on a device ``synth.AttnCase``: fp32 [B, Hq, D]."""
     B, Hq, D = case.q.shape
     NB, Hkv, BLK, _ = case.kcache.shape
+    if tuple(case.vcache.shape) != (NB, Hkv, D, BLK):
+        raise ValueError(f"vcache shape {tuple(case.vcache.shape)}, expected {(NB, Hkv, D, BLK)}")
     MB = case.table.shape[1]
     if max_len is None:
         max_len = int(case.lens.max().item()) if B else 0

@@ -558,6 +558,7 @@ int moe_decode_attention(const uint16_t* q, const uint16_t* kcache, const uint16
   if (B < 0 || Hq <= 0 || Hkv <= 0 || block < 1 || max_blocks < 1 || num_blocks < 1 || max_len < 0)
     return fail(MOE_ERR_SHAPE, "need B >= 0, Hq, Hkv, block, max_blocks, num_blocks >= 1, max_len >= 0");
   if (D != 128) return fail(MOE_ERR_UNSUPPORTED, "D = %d (only 128)", D);
+  if (block % 8) return fail(MOE_ERR_UNSUPPORTED, "block = %d not a multiple of 8", block);
   const int g = Hq % Hkv ? 0 : Hq / Hkv;
   if (g != 1 && g != 2 && g != 4 && g != 8)
     return fail(MOE_ERR_UNSUPPORTED, "Hq / Hkv = %d / %d not in {1, 2, 4, 8}", Hq, Hkv);

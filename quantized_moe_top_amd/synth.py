@@ -201,9 +201,10 @@ def decode_logits_pool(T: int, E: int, n: int, seed: int) -> torch.Tensor:
 @dataclasses.dataclass
 class AttnCase:
     """One decode-attention step: one query token per sequence against a
-    block-paged key/value cache (``kcache``, ``vcache`` bf16
-    ``[NB, Hkv, BLK, D]``; ``table`` int32 ``[B, MB]`` maps block i of
-    sequence b to a physical block; ``lens`` int32 ``[B]``)."""
+    block-paged key/value cache (``kcache`` bf16 ``[NB, Hkv, BLK, D]``,
+    position-major; ``vcache`` bf16 ``[NB, Hkv, D, BLK]``, element-major;
+    ``table`` int32 ``[B, MB]`` maps block i of sequence b to a physical
+    block; ``lens`` int32 ``[B]``)."""
     name: str
     q: torch.Tensor
     kcache: torch.Tensor
@@ -223,7 +224,8 @@ def make_attention(lens, Hq: int = 32, Hkv: int = 4, D: int = 128, block: int = 
     """Seeded decode-attention inputs: q, K and V bf16 N(0, 1); each sequence
     gets ceil(len / block) blocks (at least one), and the physical blocks of
     all sequences are one seeded permutation, so consecutive positions of a
-    sequence sit in scattered blocks.  Draw order: permutation, q, K, V."""
+    sequence sit in scattered blocks.  Draw order: permutation, q, K, V (V
+    drawn position-major, stored element-major)."""
     gen = torch.Generator().manual_seed(seed)
     lens = [int(n) for n in lens]
     B = len(lens)
@@ -237,7 +239,7 @@ def make_attention(lens, Hq: int = 32, Hkv: int = 4, D: int = 128, block: int = 
         pos += n
     q = torch.randn(B, Hq, D, generator=gen).to(torch.bfloat16)
     kc = torch.randn(NB, Hkv, block, D, generator=gen).to(torch.bfloat16)
-    vc = torch.randn(NB, Hkv, block, D, generator=gen).to(torch.bfloat16)
+    vc = torch.randn(NB, Hkv, block, D, generator=gen).to(torch.bfloat16).transpose(2, 3).contiguous()
     return AttnCase(name, q, kc, vc, table, torch.tensor(lens, dtype=torch.int32), block)
 
 

@@ -419,7 +419,7 @@ def _gather_kv(case, b):
     blk = case.table[b].long()
     pos = torch.arange(L)
     k = case.kcache.double()[blk[pos // case.block], :, pos % case.block, :]  # [L, Hkv, D]
-    v = case.vcache.double()[blk[pos // case.block], :, pos % case.block, :]
+    v = case.vcache.double()[blk[pos // case.block], :, :, pos % case.block]  # [L, Hkv, D]
     return k.permute(1, 0, 2), v.permute(1, 0, 2)
 
 

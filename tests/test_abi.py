@@ -213,6 +213,7 @@ def test_decode_attention_validation(L):
     assert att(Hq=30, Hkv=4) == UNSUP               # not a multiple
     assert att(Hq=64, Hkv=4) == UNSUP               # group of 16
     assert att(blk=0) == SHAPE
+    assert att(blk=12) == UNSUP                     # value runs of 8 positions
     assert att(nb=0) == SHAPE
     assert att(q=0) == NULL
     assert att(q=A + 2) == ALIGN

@@ -446,7 +446,9 @@ def test_ffn_io(orc, case):
 # ---------------------------------------------------- decode attention --
 # fp32 arithmetic over at most 131072 positions (products of bf16 values are
 # exact in fp32; the sums and the rescaling by exp2 differences carry about
-# 1e-6 relative error each): relative L2 <= 1e-4, max abs <= 1e-3 * rms.
+# 1e-6 relative error each; the probabilities enter the value sums as a bf16
+# pair hi + lo, within 2^-16 of the fp32 value): relative L2 <= 1e-4, max
+# abs <= 1e-3 * rms.
 ATTN_REL_L2, ATTN_MAX_ABS = 1e-4, 1e-3
 
 
@@ -473,6 +475,17 @@ def test_decode_attention(orc, Hq, Hkv):
     got = cpu(out)
     assert np.all(got[1] == 0)
     _attn_check(got, ref, f"attention Hq={Hq} Hkv={Hkv}")
+
+
+@pytest.mark.parametrize("block", [8, 24])
+def test_decode_attention_block_sizes(orc, block):
+    """Blocks shorter than a step of 32 positions and of a length that is no
+    power of two: runs of 8 positions found through the table."""
+    case = synth.make_attention([150, 1, 300, 63, 1000], Hq=32, Hkv=4, D=128, block=block, seed=71 + block)
+    out = api.decode_attention(case.to(DEV))
+    torch.cuda.synchronize()
+    ref = orc.decode_attention(case.q, case.kcache, case.vcache, case.table, case.lens)
+    _attn_check(cpu(out), ref, f"attention block={block}")
 
 
 @pytest.mark.parametrize("name", ["attn_decode_32k", "attn_decode_128k", "attn_decode_b8_32k"])
