@@ -119,11 +119,13 @@ def layer_work(lay, touched: int) -> dict:
 
 
 # ---------------------------------------------------------- traffic file --
-def kernel_source_digest() -> str:
-    """Digest of the sources the grouped GEMM kernels are built from."""
+def kernel_source_digest(stage: str = "gate_up") -> str:
+    """Digest of the sources the stage's kernels are built from (the grouped
+    GEMM kernels, or the decode-attention kernels)."""
     h = hashlib.sha256()
-    for rel in ("quantized_moe_top_amd/csrc/gemm.hip", "quantized_moe_top_amd/csrc/gemv.hip",
-                "quantized_moe_top_amd/csrc/internal.h"):
+    files = (("quantized_moe_top_amd/csrc/attn.hip",) if stage == "attention" else
+             ("quantized_moe_top_amd/csrc/gemm.hip", "quantized_moe_top_amd/csrc/gemv.hip"))
+    for rel in files + ("quantized_moe_top_amd/csrc/internal.h",):
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -142,7 +144,7 @@ def measured_traffic(workload: str, stage: str):
             if "=" in line and not line.lstrip().startswith("#"):
                 key, val = line.split("=", 1)
                 kv[key.strip()] = val.strip()
-    if kv.get("source_digest") != kernel_source_digest():
+    if kv.get("source_digest") != kernel_source_digest(stage):
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -456,6 +458,13 @@ def bench_attention(args, name: str, dev) -> None:
     end.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / K
+    if args.copy_calibration:
+        src = torch.empty(64 << 20, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] copy calibration: 268435456 bytes read and written")
     byts = kv_bytes + B * Hq * D * (2 + 4)
     achieved = byts / (ms * 1e-3) / 1e9
     line = {
@@ -466,8 +475,9 @@ def bench_attention(args, name: str, dev) -> None:
         "config": {"workload": name, "B": B, "context": max_len, "Hq": Hq, "Hkv": Hkv, "D": D,
                    "block": BLK, "launch": "eager"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "attention step (split + merge launches)",
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(name, "attention"),
+                     "kernel": "attention", "launches": "attn_split_kernel + attn_combine_kernel (one step)",
                      "algorithmic_bytes": int(byts), "avg_launch_us": round(ms * 1e3, 3)},
     }
     if not args.no_cpu_baseline:
