@@ -57,18 +57,20 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_split_kernel(const AttnP
   const int tid = threadIdx.x, r = tid & 15, g = (tid >> 4) & 3;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int L = p.lens[b];
-  const int t0 = s * p.chunk, t1 = min(L, t0 + p.chunk);
+  const int t0 = s * p.chunk;
   // each run of 8 positions of the range (t0 and the block length are
   // multiples of 8, so a run lies in one block): its block and KV head as
-  // one index (-1: skipped block) and its offset in the block, once, in LDS
-  const int ngr = t1 > t0 ? (t1 - t0 + 7) / 8 : 0;  // <= kAttnGroups (host plan)
+  // one index (-1: skipped block) and its offset in the block, once, in LDS.
+  // The whole range's entries are read without waiting for the sequence
+  // length (entries past it are never used).
+  const int ngr = p.chunk / 8;  // <= kAttnGroups (host plan)
   for (int i = tid; i < ngr; i += kAttnThreads) {
     const int t = t0 + 8 * i, bi = t / p.block;
     const int blk = bi < p.max_blocks ? p.table[(size_t)b * p.max_blocks + bi] : -1;
     gslab[i] = (blk >= 0 && blk < p.num_blocks) ? blk * p.Hkv + h : -1;
     goff[i] = t % p.block;
   }
+  const int t1 = min(p.lens[b], t0 + p.chunk);
   // second operand of the scores: lane (r, g) holds elements 32c + 8g .. +7
   // of query head r (zero for the padding heads r >= GQ)
   u32x4 qop[4];
