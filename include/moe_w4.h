@@ -285,8 +285,9 @@ int moe_ffn_forward_io(const moe_layer* layer, const uint16_t* x, const float* r
  * fixed-block cache layout).  One query token per sequence:
  *   o[b][j] = softmax_t(q[b][j] . K_t / sqrt(D)) V  over t < seq_lens[b],
  * the KV head of query head j being j / (Hq / Hkv); a sequence of length 0
- * gives o = 0.  fp32 arithmetic, ranges of positions merged in fixed order
- * (deterministic).
+ * gives o = 0.  Products of bf16 values summed in fp32 (the softmax
+ * weights enter the value sums within 2^-16 of their fp32 value); ranges of
+ * positions merged in fixed order (deterministic).
  *   q:           device bf16 [B][Hq][D]
  *   kcache:      device bf16 [num_blocks][Hkv][block][D] (position-major)
  *   vcache:      device bf16 [num_blocks][Hkv][D][block] (element-major);

@@ -299,7 +299,8 @@ struct AttnPlan {
   int nsplit, chunk;
 };
 AttnPlan attn_plan(int B, int Hkv, int max_len);
-// q bf16 [B][Hq][128]; kc, vc bf16 [num_blocks][Hkv][block][128]; table int32
+// q bf16 [B][Hq][128]; kc bf16 [num_blocks][Hkv][block][128]; vc bf16
+// [num_blocks][Hkv][128][block]; block a multiple of 8; table int32
 // [B][max_blocks]; lens int32 [B] (<= max_len); out fp32 [B][Hq][128]; ws:
 // B * Hq * nsplit * 130 floats.  Hq / Hkv in {1, 2, 4, 8}.
 hipError_t launch_decode_attention(const uint16_t* q, const uint16_t* kc, const uint16_t* vc,
