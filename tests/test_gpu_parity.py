@@ -488,6 +488,49 @@ def test_decode_attention_block_sizes(orc, block):
     _attn_check(cpu(out), ref, f"attention block={block}")
 
 
+def test_decode_attention_skipped_blocks(orc):
+    """Table entries outside [0, num_blocks) are skipped: a sequence whose
+    second and fourth blocks are -1 and num_blocks gives the attention over
+    its first and third blocks alone (the oracle on those 128 positions)."""
+    import dataclasses
+    full = synth.make_attention([256], Hq=32, Hkv=4, D=128, block=64, seed=57)
+    NB = full.kcache.shape[0]
+    bad = full.table.clone()
+    bad[0, 1], bad[0, 3] = -1, NB
+    case = dataclasses.replace(full, table=bad)
+    out = api.decode_attention(case.to(DEV))
+    torch.cuda.synchronize()
+    kept = dataclasses.replace(full, table=full.table[:, [0, 2]].contiguous(),
+                               lens=torch.tensor([128], dtype=torch.int32))
+    ref = orc.decode_attention(kept.q, kept.kcache, kept.vcache, kept.table, kept.lens)
+    _attn_check(cpu(out), ref, "attention with skipped blocks")
+
+
+def test_decode_attention_graph_replay():
+    """Both launches captured in a HIP graph (no allocation, no memset)
+    replay to the eager result, bit for bit, with other attention work on the
+    same workspace between replays."""
+    a = synth.make_attention([3000, 17, 900], seed=58).to(DEV)
+    b = synth.make_attention([700, 5000, 1], seed=59).to(DEV)
+    B, Hq, D = a.q.shape
+    Hkv = a.kcache.shape[1]
+    ws = torch.empty(int(api._L().moe_decode_attention_workspace_bytes(B, Hq, Hkv, 5000)),
+                     dtype=torch.uint8, device=DEV)
+    eager = api.decode_attention(a, workspace=ws, max_len=3000).clone()
+    out = torch.empty_like(eager)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        api.decode_attention(a, out=out, workspace=ws, max_len=3000)
+    for r in range(4):
+        out.fill_(float("nan"))
+        api.decode_attention(b, workspace=ws, max_len=5000)  # rewrites the shared workspace
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {r}"
+
+
 @pytest.mark.parametrize("name", ["attn_decode_32k", "attn_decode_128k", "attn_decode_b8_32k"])
 def test_decode_attention_workloads(orc, name):
     """The benchmark workloads at full size, every output against the
