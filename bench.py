@@ -57,6 +57,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="prefill_t512")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-targets", action="store_true",
+                    help="skip the decode and large-prefill workloads reported beside prefill_t512")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches only (no HIP graph replays)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -152,6 +154,217 @@ def measured_traffic(workload: str, stage: str):
         return None
 
 
+# ------------------------------------------------------------ trace file --
+def trace_average_us(workload: str, role_prefix: str):
+    """Average duration (us) of the kernel whose role starts with
+    `role_prefix` in the committed kernel-trace summary
+    profiles/kernels_<workload>.md, or None when there is none or the
+    kernels changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"kernels_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    digest, avg = None, None
+    with open(path) as f:
+        for line in f:
+            if line.startswith("source_digest"):
+                digest = line.split("=", 1)[1].strip()
+            cells = [c.strip() for c in line.split("|")]
+            if len(cells) > 6 and cells[2].startswith(role_prefix) and avg is None:
+                try:
+                    avg = float(cells[5])
+                except ValueError:
+                    pass
+    if digest != kernel_source_digest("gate_up"):
+        return None
+    return avg
+
+
+ROLE_OF_STAGE = {"gate_up": "S6", "down": "S7", "combine": "S8"}
+
+
+# -------------------------------------------------------------- workloads --
+class Case:
+    """A workload's device-resident inputs: the packed layer(s) rotated over
+    enough copies (>= 1 GiB of weights in total) that every step reads its
+    experts cold from HBM, and for decode sizes a pool of logit sets, so the
+    touched experts change every step.  The long-context workload rotates
+    its four independently seeded layers (weights and activations)."""
+
+    def __init__(self, name, dev):
+        import torch
+
+        from quantized_moe_top_amd import api, synth
+
+        self.name = name
+        n_layers = synth.WORKLOADS[name].get("layers", 1)
+        self.hosts = [synth.make_layer(name, i) for i in range(n_layers)]
+        base = [api.pack_layer(h.to(dev)) for h in self.hosts]
+        torch.cuda.synchronize()
+        lay = base[0]
+        self.lay = lay
+        nbytes = lambda b: (b.words.numel() + b.sb.numel()) * 4
+        per_copy = nbytes(lay.gate) + nbytes(lay.up) + nbytes(lay.down) + \
+            (lay.router_weight.numel() * 2 if lay.router_weight is not None else 0)
+        self.per_copy = per_copy
+        R = max(len(base), -(-ROTATE_BYTES // per_copy))
+        copies = list(base)
+        while len(copies) < R:
+            src = base[len(copies) % len(base)]
+            gate, up, down = (dataclasses.replace(b, words=b.words.clone(), sb=b.sb.clone())
+                              for b in (src.gate, src.up, src.down))
+            wr = src.router_weight.clone() if src.router_weight is not None else None
+            copies.append(dataclasses.replace(src, gate=gate, up=up, down=down, router_weight=wr))
+        self.copies = copies
+        self.R = R
+        self.logit_pool = None
+        if lay.logits is not None and lay.T <= 8:
+            self.logit_pool = [lay.logits] + list(
+                synth.decode_logits_pool(lay.T, lay.E, 63, seed=1000 + lay.T).to(dev))
+        self.y = torch.empty((lay.T, lay.H), dtype=torch.float32, device=dev)
+        wsb = max(api.ffn_workspace_bytes(c) for c in copies)
+        self.ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+        # touched experts per step (routing is identical for every copy of
+        # one layer; decode rotates logit sets)
+        self.touched = []
+        for i in range(self.n_variants()):
+            _, inf = self.step(i, info=True)
+            self.touched.append(int((inf["counts"] > 0).sum().item()))
+        torch.cuda.synchronize()
+
+    def n_variants(self):
+        return len(self.logit_pool) if self.logit_pool else len(self.hosts)
+
+    def step(self, i, evs=None, info=False):
+        from quantized_moe_top_amd import api
+        c = self.copies[i % self.R]
+        lg = self.logit_pool[i % len(self.logit_pool)] if self.logit_pool else None
+        return api.ffn_forward(c, logits=lg, y=self.y, workspace=self.ws, stage_events=evs, info=info)
+
+    def mean_touched(self, K):
+        if self.logit_pool:
+            return float(sum(self.touched[i % len(self.touched)] for i in range(K)) / K)
+        return float(sum(self.touched[(i % self.R) % len(self.hosts)] for i in range(K)) / K)
+
+
+def time_steps(run, K, repeats=3):
+    """Median over `repeats` runs of K back-to-back steps between two events
+    (ms for the K steps), and the host wall time of that run."""
+    import torch
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    res = []
+    for _ in range(repeats):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        start.record()
+        for i in range(K):
+            run(i)
+        end.record()
+        torch.cuda.synchronize()
+        res.append((start.elapsed_time(end), time.perf_counter() - t0))
+    res.sort()
+    return res[len(res) // 2]
+
+
+def measure(case, K, warmup, graph=True, repeats=3):
+    """Eager launches and HIP graph replays of the same steps, each the
+    median of `repeats` timed runs; returns both and the faster."""
+    import torch
+    for i in range(warmup):
+        case.step(i)
+    torch.cuda.synchronize()
+    graphs = None
+    if graph:
+        # one graph per (weight copy, logit set) that the steps use
+        n_graphs = len(case.logit_pool) if case.logit_pool else case.R
+        graphs = []
+        for i in range(n_graphs):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                case.step(i)
+            graphs.append(g)
+        for i in range(max(min(warmup, n_graphs), 1)):
+            graphs[i % n_graphs].replay()
+        torch.cuda.synchronize()
+    eager_ms, eager_wall = time_steps(lambda i: case.step(i), K, repeats)
+    graph_ms = graph_wall = None
+    if graphs is not None:
+        graph_ms, graph_wall = time_steps(lambda i: graphs[i % len(graphs)].replay(), K, repeats)
+    if graph_ms is not None and graph_ms < eager_ms:
+        best = (graph_ms, graph_wall, "hip_graph")
+    else:
+        best = (eager_ms, eager_wall, "eager")
+    del graphs
+    return {"eager_ms": eager_ms, "graph_ms": graph_ms, "best_ms": best[0], "wall_s": best[1],
+            "launch": best[2]}
+
+
+def stage_times(case, K):
+    """Per-stage averages (us) from an eager pass of the same steps with an
+    event recorded on the layer's stream at every stage boundary."""
+    import numpy as np
+    import torch
+
+    from quantized_moe_top_amd import _lib, api
+    nst = _lib.MOE_NUM_STAGES
+    ev = [api.stage_events(nst + 1) for _ in range(K)]
+    ms, _ = time_steps(lambda i: case.step(i, ev[i]), K, repeats=1)
+    stage_ms = np.array([[ev[i][s].elapsed_time(ev[i][s + 1]) for s in range(nst)] for i in range(K)])
+    return ms, {st: round(float(stage_ms[:, j].mean()) * 1e3, 3) for j, st in enumerate(_lib.STAGES)}
+
+
+def layer_fractions(lay, touched, ms_per_step):
+    lw = layer_work(lay, 0)
+    lw_t = layer_work(lay, 1)["bytes"] - lw["bytes"]
+    lbytes = lw["bytes"] + touched * lw_t
+    t_step = ms_per_step * 1e-3
+    return {"hbm_frac": round(lbytes / t_step / (HBM_PEAK_GBS * 1e9), 4),
+            "mfma_frac": round(lw["flops"] / t_step / (MFMA_FP16_PEAK_TFLOPS * 1e12), 4),
+            "bytes": int(lbytes), "flops": int(lw["flops"]), "touched_experts": touched}
+
+
+def launch_floors(dev, K):
+    """What one launch costs at the least on this stream: K eager launches
+    of a one-element fill kernel, and K replays of a graph holding one."""
+    import torch
+    floor = torch.zeros(1, device=dev)
+    for _ in range(10):
+        floor.fill_(1.0)
+    eager_ms, _ = time_steps(lambda i: floor.fill_(1.0), K)
+    gf = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gf):
+        floor.fill_(1.0)
+    gf.replay()
+    graph_ms, _ = time_steps(lambda i: gf.replay(), K)
+    return round(eager_ms / K * 1e3, 3), round(graph_ms / K * 1e3, 3)
+
+
+# Workloads the bench line reports beside the headline one (the targets:
+# decode T=1 and T=8 at >= 60% of HBM, prefill T >= 8192 at >= 50% of the
+# dense fp16/bf16 MFMA peak), with the steps timed per run.
+TARGETS = {"decode_t1": 200, "decode_t8": 200, "imbalanced_t8192": 20, "longctx_t32768": 20}
+
+
+def target_line(name, dev, steps, warmup):
+    import torch
+    log(f"[bench] target workload {name}: drawing and packing")
+    case = Case(name, dev)
+    m = measure(case, steps, warmup)
+    ms = m["best_ms"] / steps
+    _, st = stage_times(case, steps)
+    lay = case.lay
+    out = {"ms_per_step": round(ms, 6), "tokens_per_s": round(lay.T / (ms * 1e-3), 1),
+           "launch": m["launch"], "eager_ms_per_step": round(m["eager_ms"] / steps, 6),
+           "graph_ms_per_step": round(m["graph_ms"] / steps, 6) if m["graph_ms"] else None,
+           "steps": steps, "weight_copies": case.R, "layers_rotated": len(case.hosts),
+           "layer_roofline": layer_fractions(lay, case.mean_touched(steps), ms), "stage_us": st}
+    log(f"[bench] {name}: {ms * 1e3:.2f} us/step ({m['launch']}), layer fractions "
+        f"{out['layer_roofline']['mfma_frac']} MFMA / {out['layer_roofline']['hbm_frac']} HBM; stages {st}")
+    del case
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
 # ------------------------------------------------------------------ main --
 def main():
     args = parse()
@@ -175,119 +388,35 @@ def main():
     if name in synth.ATTN_WORKLOADS:
         return bench_attention(args, name, dev)
     log(f"[bench] drawing workload {name}")
-    host = synth.make_layer(name)
-    # the banks are packed once into the kernels' layout (load time, untimed)
-    lay = api.pack_layer(host.to(dev))
-    torch.cuda.synchronize()
+    case = Case(name, dev)
+    lay, host = case.lay, case.hosts[0]
     T, E, k = lay.T, lay.E, lay.k
-
-    # weight copies for cold reads
-    nbytes = lambda b: (b.words.numel() + b.sb.numel()) * 4
-    per_copy = nbytes(lay.gate) + nbytes(lay.up) + nbytes(lay.down) + \
-        (lay.router_weight.numel() * 2 if lay.router_weight is not None else 0)
-    R = max(1, -(-ROTATE_BYTES // per_copy))
-    copies = [lay]
-    for _ in range(R - 1):
-        gate, up, down = (dataclasses.replace(b, words=b.words.clone(), sb=b.sb.clone())
-                          for b in (lay.gate, lay.up, lay.down))
-        wr = lay.router_weight.clone() if lay.router_weight is not None else None
-        copies.append(dataclasses.replace(lay, gate=gate, up=up, down=down, router_weight=wr))
-    logit_pool = None
-    if lay.logits is not None and T <= 8:
-        logit_pool = [lay.logits] + list(synth.decode_logits_pool(T, E, 63, seed=1000 + T).to(dev))
-    log(f"[bench] {R} weight copies of {per_copy / 2**20:.1f} MiB; "
-        f"logit sets {len(logit_pool) if logit_pool else 1}")
-
-    y = torch.empty((T, lay.H), dtype=torch.float32, device=dev)
-    wsb = api.ffn_workspace_bytes(lay)
-    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
-    nst = _lib.MOE_NUM_STAGES
-
-    def step(i, evs=None, info=False):
-        c = copies[i % R]
-        lg = logit_pool[i % len(logit_pool)] if logit_pool else None
-        return api.ffn_forward(c, logits=lg, y=y, workspace=ws, stage_events=evs, info=info)
-
-    # touched experts per step (for the algorithmic byte counts): routing is
-    # identical for every copy; decode rotates logit sets
-    touched = []
-    for i in range(len(logit_pool) if logit_pool else 1):
-        _, inf = step(i, info=True)
-        touched.append(int((inf["counts"] > 0).sum().item()))
-    torch.cuda.synchronize()
-
-    log(f"[bench] warmup {args.warmup}")
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
+    R = case.R
+    log(f"[bench] {R} weight copies of {case.per_copy / 2**20:.1f} MiB; "
+        f"logit sets {len(case.logit_pool) if case.logit_pool else 1}; layers {len(case.hosts)}")
+    y, ws, step = case.y, case.ws, case.step
+    copies, logit_pool = case.copies, case.logit_pool
 
     K = args.steps
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    graphs = None
-    if not args.no_graph:
-        # one graph per (weight copy, logit set) that the steps use
-        n_graphs = len(logit_pool) if logit_pool else R
-        graphs = []
-        for i in range(n_graphs):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                step(i)
-            graphs.append(g)
-        for i in range(min(args.warmup, n_graphs) or 1):
-            graphs[i % n_graphs].replay()
-        torch.cuda.synchronize()
-
-    def timed(run):
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        start.record()
-        for i in range(K):
-            run(i)
-        end.record()
-        torch.cuda.synchronize()
-        return start.elapsed_time(end), time.perf_counter() - t0
-
-    # Two ways to launch the same layer on one stream: eager (the host
-    # enqueues every kernel of every step, running ahead of the GPU) and HIP
-    # graph replay (one launch per step; each replay has a fixed cost of its
-    # own, see launch_floor_us).  Both are timed and the faster is reported:
-    # eager wins when a step's GPU time hides the host's enqueueing (prefill),
-    # replay when it does not (decode).
-    log(f"[bench] timing {K} steps eager" + ("" if graphs is None else " and by graph replay"))
-    eager_plain_ms, eager_wall = timed(lambda i: step(i))
-    graph_ms = None
-    if graphs is not None:
-        graph_ms, graph_wall = timed(lambda i: graphs[i % len(graphs)].replay())
-    if graph_ms is not None and graph_ms < eager_plain_ms:
-        elapsed_ms, wall, launch = graph_ms, graph_wall, "hip_graph"
-    else:
-        elapsed_ms, wall, launch = eager_plain_ms, eager_wall, "eager"
+    log(f"[bench] timing {K} steps eager" + ("" if args.no_graph else " and by graph replay") +
+        ", median of 3 runs each")
+    m = measure(case, K, args.warmup, graph=not args.no_graph)
+    elapsed_ms, wall, launch = m["best_ms"], m["wall_s"], m["launch"]
+    eager_plain_ms, graph_ms = m["eager_ms"], m["graph_ms"]
     ms_per_step = elapsed_ms / K
     value = T * K / (elapsed_ms / 1e3)
 
-    # launch floor: the same number of steps replaying a graph of one
-    # one-element fill kernel (what a step of the layer costs at the very
-    # least per kernel it launches)
-    floor = torch.zeros(1, device=dev)
-    gf = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(gf):
-        floor.fill_(1.0)
-    gf.replay()
-    floor_ms, _ = timed(lambda i: gf.replay())
-    launch_floor_us = floor_ms / K * 1e3
+    floor_eager_us, floor_graph_us = launch_floors(dev, K)
 
     # per-stage durations: an eager pass of the same steps with events
     # recorded between the stages on the layer's stream
-    ev = [api.stage_events(nst + 1) for _ in range(K)]
-    eager_ms, _ = timed(lambda i: step(i, ev[i]))
-    stage_ms = np.array([[ev[i][s].elapsed_time(ev[i][s + 1]) for s in range(nst)] for i in range(K)])
-    stage_us = {st: round(float(stage_ms[:, j].mean()) * 1e3, 3) for j, st in enumerate(_lib.STAGES)}
+    eager_ms, stage_us = stage_times(case, K)
     log(f"[bench] {ms_per_step * 1e3:.2f} us/step ({launch}; wall {wall / K * 1e6:.2f}; eager "
         f"{eager_plain_ms / K * 1e3:.2f}, graph {graph_ms / K * 1e3 if graph_ms else float('nan'):.2f}); "
         f"eager with stage events {eager_ms / K * 1e3:.2f} us/step; stages us {stage_us}")
 
     # roofline of the dominant single-kernel stage
-    mean_touched = float(np.mean([touched[i % len(touched)] for i in range(K)]))
+    mean_touched = case.mean_touched(K)
     alg = algorithmic(lay, 0)
     alg_t = {s: dict(bytes=algorithmic(lay, 1)[s]["bytes"] - alg[s]["bytes"], flops=alg[s]["flops"])
              for s in alg}  # bytes per touched expert
@@ -302,21 +431,21 @@ def main():
     hbm_time = byts / (HBM_PEAK_GBS * 1e9)
     mfma_time = flops / (MFMA_FP16_PEAK_TFLOPS * 1e12)
     if hbm_time >= mfma_time:
-        achieved, peak, unit, bound = byts / dur_s / 1e9, HBM_PEAK_GBS, "GB/s", "hbm"
+        work, peak, unit, bound, scale = byts, HBM_PEAK_GBS, "GB/s", "hbm", 1e9
     else:
-        achieved, peak, unit, bound = flops / dur_s / 1e12, MFMA_FP16_PEAK_TFLOPS, "TFLOP/s", "mfma"
+        work, peak, unit, bound, scale = flops, MFMA_FP16_PEAK_TFLOPS, "TFLOP/s", "mfma", 1e12
+    achieved = work / dur_s / scale
     traffic = measured_traffic(name, dom)
+    trace_us = trace_average_us(name, ROLE_OF_STAGE[dom])
     roofline = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                 "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": dom,
                 "algorithmic_bytes": int(byts), "algorithmic_flops": int(flops),
-                "avg_launch_us": stage_us[dom]}
-    lw = layer_work(lay, 0)
-    lw_t = layer_work(lay, 1)["bytes"] - lw["bytes"]
-    lbytes = lw["bytes"] + mean_touched * lw_t
-    t_step = ms_per_step * 1e-3
-    layer_roof = {"hbm_frac": round(lbytes / t_step / (HBM_PEAK_GBS * 1e9), 4),
-                  "mfma_frac": round(lw["flops"] / t_step / (MFMA_FP16_PEAK_TFLOPS * 1e12), 4),
-                  "bytes": int(lbytes), "flops": int(lw["flops"]), "touched_experts": mean_touched}
+                "avg_launch_us": stage_us[dom],
+                # the same kernel's average from the committed rocprofv3
+                # trace (profiles/kernels_<workload>.md), and the fraction it gives
+                "trace_avg_us": trace_us,
+                "frac_from_trace": round(work / (trace_us * 1e-6) / scale / peak, 4) if trace_us else None}
+    layer_roof = layer_fractions(lay, mean_touched, ms_per_step)
 
     ablations = None
     if args.ablation == "host_blockmap" and api.host_blockmap_ints(lay) > 0:
@@ -331,8 +460,8 @@ def main():
 
         for i in range(args.warmup):
             step_host(i)
-        plain_ms, _ = timed(lambda i: step(i))
-        host_ms, _ = timed(step_host)
+        plain_ms, _ = time_steps(lambda i: step(i), K)
+        host_ms, _ = time_steps(step_host, K)
         ablations = {"host_blockmap": {
             "ms_per_step": round(host_ms / K, 6),
             "eager_single_submission_ms_per_step": round(plain_ms / K, 6),
@@ -359,8 +488,8 @@ def main():
 
         for i in range(args.warmup):
             step_io(i)
-        plain_ms, _ = timed(lambda i: step(i))
-        io_ms, _ = timed(step_io)
+        plain_ms, _ = time_steps(lambda i: step(i), K)
+        io_ms, _ = time_steps(step_io, K)
         io_res = {"ms_per_step": round(io_ms / K, 6), "eager_layer_ms_per_step": round(plain_ms / K, 6),
                   "added_us_per_step": round((io_ms - plain_ms) / K * 1e3, 3),
                   "tokens_per_s": round(T * K / (io_ms / 1e3), 1)}
@@ -379,8 +508,8 @@ def main():
 
         for i in range(args.warmup):
             step_unfused(i)
-        plain_ms, _ = timed(lambda i: step(i))
-        unf_ms, _ = timed(step_unfused)
+        plain_ms, _ = time_steps(lambda i: step(i), K)
+        unf_ms, _ = time_steps(step_unfused, K)
         ablations = dict(ablations or {})
         ablations["unfused"] = {
             "ms_per_step": round(unf_ms / K, 6),
@@ -396,6 +525,15 @@ def main():
         torch.cuda.synchronize()
         log("[bench] copy calibration: 268435456 bytes read and written")
 
+    del case, copies, y, ws
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    targets = None
+    if not args.no_targets and name == "prefill_t512":
+        targets = {}
+        for tname, tsteps in TARGETS.items():
+            targets[tname] = target_line(tname, dev, tsteps, min(args.warmup, 10))
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(host, args.cpu_seconds)
@@ -407,12 +545,14 @@ def main():
         "data": "synthetic",
         "config": {"workload": name, "T": T, "H": lay.H, "I": lay.I, "E": E, "top_k": k,
                    "group_size": lay.G, "router": "weight" if lay.router_weight is not None else "logits",
-                   "weight_copies": R, "block_m": api.ffn_block_m(lay), "launch": launch},
+                   "weight_copies": R, "block_m": api.ffn_block_m(lay), "launch": launch,
+                   "timing": "median of 3 runs of the timed steps, eager and graph replay each"},
         "roofline": roofline, "layer_roofline": layer_roof, "stage_us": stage_us,
         "eager_ms_per_step": round(eager_plain_ms / K, 6),
         "graph_ms_per_step": round(graph_ms / K, 6) if graph_ms else None,
         "eager_with_stage_events_ms_per_step": round(eager_ms / K, 6),
-        "launch_floor_us": round(launch_floor_us, 3),
+        "launch_floor_us": {"eager_fill_kernel": floor_eager_us, "graph_replay_of_fill": floor_graph_us},
+        "targets": targets,
         "cpu_baseline": cpu,
     }
     if ablations:
@@ -496,10 +636,22 @@ def bench_attention(args, name: str, dev) -> None:
     print(json.dumps(line), flush=True)
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(host, min_seconds: float) -> dict:
     """The CPU oracle on the host cores: the whole layer on a sample of the
-    tokens (all of them when T <= 512), with routing over every token;
-    repeated until `min_seconds` of work.  Scaled to whole-layer tokens/s."""
+    tokens (all of them when T <= 512), with routing over every token.  Three
+    timed passes, each repeated until `min_seconds` / 3 of work; the median
+    pass is scaled to whole-layer tokens/s."""
     import numpy as np
 
     import oracle
@@ -509,27 +661,35 @@ def cpu_baseline(host, min_seconds: float) -> dict:
     n = min(T, 512)
     tokens = np.linspace(0, T - 1, n).round().astype(np.int32) if n < T else np.arange(T, dtype=np.int32)
     log(f"[bench] cpu baseline: oracle on {n} of {T} tokens, {orc.num_threads()} threads")
-    t_route = t_ffn = 0.0
-    reps = 0
-    while True:
-        t0 = time.perf_counter()
-        logits = (orc.router_logits(host.x, host.router_weight) if host.router_weight is not None
-                  else np.ascontiguousarray(host.logits.numpy()))
-        ids, w = orc.route(logits, host.k)
-        orc.build_blocks(ids, host.E, 64)
-        t1 = time.perf_counter()
-        orc.ffn(host.x, ids, w, host.gate, host.up, host.down, host.G, tokens=tokens)
-        t2 = time.perf_counter()
-        t_route += t1 - t0
-        t_ffn += t2 - t1
-        reps += 1
-        if t_route + t_ffn >= min_seconds or reps >= 50:
-            break
-    per_layer = t_route / reps + (t_ffn / reps) * T / n
+    passes = []
+    total = 0.0
+    for _ in range(3):
+        t_route = t_ffn = 0.0
+        reps = 0
+        while True:
+            t0 = time.perf_counter()
+            logits = (orc.router_logits(host.x, host.router_weight) if host.router_weight is not None
+                      else np.ascontiguousarray(host.logits.numpy()))
+            ids, w = orc.route(logits, host.k)
+            orc.build_blocks(ids, host.E, 64)
+            t1 = time.perf_counter()
+            orc.ffn(host.x, ids, w, host.gate, host.up, host.down, host.G, tokens=tokens)
+            t2 = time.perf_counter()
+            t_route += t1 - t0
+            t_ffn += t2 - t1
+            reps += 1
+            if t_route + t_ffn >= min_seconds / 3 or reps >= 50:
+                break
+        total += t_route + t_ffn
+        passes.append(t_route / reps + (t_ffn / reps) * T / n)
+    per_layer = sorted(passes)[1]
     return {"value": round(T / per_layer, 2), "unit": "tokens/s", "cores": orc.num_threads(),
-            "kind": "oracle",
-            "sample": f"{reps} x (routing of all {T} tokens + layer output of {n} tokens); "
-                      f"{t_route + t_ffn:.1f} s of CPU work, scaled to the whole layer"}
+            "nproc": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)),
+            "cpu_model": cpu_model(), "kind": "oracle",
+            "passes_tokens_per_s": [round(T / p, 2) for p in passes],
+            "sample": f"median of 3 passes, each routing all {T} tokens and computing the layer output "
+                      f"of {n} tokens (repeated to >= {min_seconds / 3:.1f} s); {total:.1f} s of CPU "
+                      f"work in all, scaled to the whole layer"}
 
 
 if __name__ == "__main__":

@@ -128,7 +128,7 @@ def pack_codes(q: np.ndarray) -> np.ndarray:
 
 
 def _draw_bank(gen: torch.Generator, E: int, N: int, K: int, G: int,
-               scale_lo: float, scale_hi: float, codes=None) -> W4Bank:
+               scale_lo: float, scale_hi: float, codes=None, bias: str = "m8") -> W4Bank:
     words = np.empty((E, N, K // 8), dtype=np.uint32)
     for e in range(E):
         if codes is None:
@@ -138,8 +138,19 @@ def _draw_bank(gen: torch.Generator, E: int, N: int, K: int, G: int,
         words[e] = pack_codes(q)
     u = torch.rand((E, N, K // G), generator=gen, dtype=torch.float32)
     scales = (scale_lo + (scale_hi - scale_lo) * u).to(torch.bfloat16)
-    # bias = -8 * scale: exact in bf16 (a power-of-two multiple of a bf16 value)
-    biases = (-8.0 * scales.float()).to(torch.bfloat16)
+    if bias == "m8":
+        # bias = -8 * scale: exact in bf16 (a power-of-two multiple of a bf16 value)
+        biases = (-8.0 * scales.float()).to(torch.bfloat16)
+    elif bias == "zeropoint":
+        # bias = -m * scale with a zero point m ~ U(2, 14) drawn per group
+        m = 2.0 + 12.0 * torch.rand((E, N, K // G), generator=gen, dtype=torch.float32)
+        biases = (-m * scales.float()).to(torch.bfloat16)
+    elif bias == "free":
+        # bias drawn independently of the scale: N(0, (4 * mean scale)^2)
+        sd = 2.0 * (scale_lo + scale_hi)
+        biases = (sd * torch.randn((E, N, K // G), generator=gen, dtype=torch.float32)).to(torch.bfloat16)
+    else:
+        raise ValueError(bias)
     qweight = torch.from_numpy(words.view(np.int32).copy())
     return W4Bank(qweight, scales, biases)
 
@@ -147,15 +158,18 @@ def _draw_bank(gen: torch.Generator, E: int, N: int, K: int, G: int,
 def make_custom(T: int, H: int, I: int, E: int, k: int, G: int, seed: int, *,
                 router: str = "logits", scale=(0.002, 0.01), zipf: bool = False,
                 empty_mod4: bool = False, heavy_frac: float = 0.0, heavy_mul: float = 1.0,
-                name: Optional[str] = None) -> MoELayer:
+                bias: str = "m8", name: Optional[str] = None) -> MoELayer:
     """Draw one layer; ``router`` is ``"logits"`` (fp32 N(0,1) logits given)
-    or ``"weight"`` (bf16 router weight N(0, 0.02), logits computed on device)."""
+    or ``"weight"`` (bf16 router weight N(0, 0.02), logits computed on device).
+    ``bias`` picks the per-group bias: ``"m8"`` (-8 * scale, the benchmark
+    workloads), ``"zeropoint"`` (-m * scale, m ~ U(2, 14) per group) or
+    ``"free"`` (N(0, (4 * mean scale)^2), independent of the scale)."""
     if H % G or I % G or H % 8 or I % 8:
         raise ValueError("H and I must be multiples of G and 8")
     gen = torch.Generator().manual_seed(seed)
-    gate = _draw_bank(gen, E, I, H, G, *scale)
-    up = _draw_bank(gen, E, I, H, G, *scale)
-    down = _draw_bank(gen, E, H, I, G, *scale)
+    gate = _draw_bank(gen, E, I, H, G, *scale, bias=bias)
+    up = _draw_bank(gen, E, I, H, G, *scale, bias=bias)
+    down = _draw_bank(gen, E, H, I, G, *scale, bias=bias)
     router_weight = None
     if router == "weight":
         router_weight = (0.02 * torch.randn((E, H), generator=gen)).to(torch.bfloat16)

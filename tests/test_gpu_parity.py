@@ -234,10 +234,13 @@ def layer_output_check(orc, lay, y, info, tokens=None, strata=None):
     rms of the full oracle output is estimated per stratum."""
     l_used = cpu(info["logits"]).astype(np.float32)
     if lay.router_weight is not None:
-        l_ref = orc.router_logits(lay.x, lay.router_weight) if lay.T <= 4096 else None
-        if l_ref is not None:
-            bound = router_error_bound(lay.x, lay.router_weight) + f32_ulp(l_ref)
-            assert np.all(np.abs(l_used.astype(np.float64) - l_ref) <= bound)
+        # the device logits within the fp32 summation bound of the oracle's,
+        # on every row (or, for large T, on the rows whose output is checked)
+        rows = np.arange(lay.T) if lay.T <= 4096 or tokens is None else np.asarray(tokens)
+        xr = lay.x[torch.from_numpy(rows.astype(np.int64))]
+        l_ref = orc.router_logits(xr, lay.router_weight)
+        bound = router_error_bound(xr, lay.router_weight) + f32_ulp(l_ref)
+        assert np.all(np.abs(l_used[rows].astype(np.float64) - l_ref) <= bound)
     else:
         assert np.array_equal(l_used, cpu(lay.logits))
     rid, rw = orc.route(l_used, lay.k)
@@ -284,29 +287,37 @@ def test_ffn_forward_full(orc, name):
 
 
 def test_ffn_forward_imbalanced_t8192(orc):
+    """Zipf load with a quarter of the experts empty: routing structures
+    bit-exact and every one of the 8192 output rows against the oracle."""
     lay = synth.make_layer("imbalanced_t8192")
     y, info = api.ffn_forward(on_dev(lay), info=True)
     torch.cuda.synchronize()
     counts = cpu(info["counts"])
     assert np.all(counts[3::4] == 0) and counts.sum() == lay.T * lay.k
-    g = np.random.default_rng(8192)
-    tokens = np.sort(g.choice(lay.T, 48, replace=False))
-    layer_output_check(orc, lay, y, info, tokens=tokens)
+    layer_output_check(orc, lay, y, info)
 
 
-def test_ffn_forward_longctx_t32768(orc):
-    lay = synth.make_layer("longctx_t32768")
+@pytest.mark.parametrize("layer_index", [0, 1, 2, 3])
+def test_ffn_forward_longctx_t32768(orc, layer_index):
+    """Each of the four independently seeded long-context layers.  The 1% of
+    rows scaled x30 are the precision canary: every one of them (328) is
+    checked against the oracle, with 64 of the other rows.  The max abs error
+    is taken over every checked row; the rms of the whole oracle output
+    combines the exact mean square of the heavy rows with an estimate of the
+    normal rows' from the 64 checked (the heavy rows carry more than 99.9% of
+    the mean square, so the estimate moves the bound by well under 0.1%)."""
+    lay = synth.make_layer("longctx_t32768", layer_index)
     y, info = api.ffn_forward(on_dev(lay), info=True)
     torch.cuda.synchronize()
     x = lay.x.float()
     heavy = torch.nonzero(x.abs().amax(1) > 12.0).flatten().numpy()  # the x30 rows
+    assert len(heavy) == round(0.01 * lay.T)
     normal = np.setdiff1d(np.arange(lay.T), heavy)
-    g = np.random.default_rng(32768)
-    th = np.sort(g.choice(heavy, 8, replace=False))
-    tn = np.sort(g.choice(normal, 32, replace=False))
+    g = np.random.default_rng(32768 + layer_index)
+    tn = np.sort(g.choice(normal, 64, replace=False))
     share_h = len(heavy) / lay.T
-    layer_output_check(orc, lay, y, info, tokens=np.concatenate([th, tn]),
-                       strata=[(th, share_h), (tn, 1 - share_h)])
+    layer_output_check(orc, lay, y, info, tokens=np.concatenate([heavy, tn]),
+                       strata=[(heavy, share_h), (tn, 1 - share_h)])
 
 
 # ------------------------------------------------------------ edge cases ---
