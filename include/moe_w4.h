@@ -30,8 +30,11 @@
  *    and workspaces must be 16-byte aligned.
  *  - Logits may contain -inf (never selected while top_k finite logits
  *    exist); NaN logits give unspecified routing.
- *  - Activations and the hidden vector are carried in fp16 inside the
- *    grouped GEMM: |x| and |h| must stay below 65504.
+ *  - Activations x are carried in fp16 inside the grouped GEMM: |x| must
+ *    stay below 65504 (bf16 values beyond it have no fp16 form), and values
+ *    below 2^-14 in magnitude keep fewer bits (fp16 subnormals).  The hidden
+ *    vector h between the two GEMMs carries a power-of-two exponent per row
+ *    and 16 columns (moe_w4_h_exp_bytes), so it has no such limit.
  *
  * Notation: T tokens, H hidden size, I expert intermediate size, E experts,
  * top_k experts per token, G quantisation group size, P = T * top_k
@@ -92,17 +95,28 @@ typedef struct {
  *         the four row-major words holding codes 64s + 32h .. 64s + 32h + 31
  *         (same nibble order), each word rotated left by 5 bits; each chunk
  *         is one contiguous 4 KiB run per slab.
- *  sb:    uint32 [E][N/128][K/G][128 columns]: the scale as fp16 in the low
- *         16 bits, bias - 32 * scale as fp16 in the high 16 bits (rounded to
- *         nearest; exact for bias = -8 * scale).
+ *  sb:    uint32 [E][N/128][K/G][128 columns], then a tail.  Each expert's
+ *         scales and biases are first multiplied by a power of two 2^c
+ *         (exact), the one that puts the expert's largest |bias| +
+ *         32 |scale| in [2^13, 2^14) (|c| <= 100): every fp16 value of the
+ *         dequantisation is then a normal number well below overflow,
+ *         whatever the range of the bank.  Word: s' = 2^c scale as fp16 in
+ *         the low 16 bits; in the high 16 bits b' - 32 s' (b' = 2^c bias)
+ *         when that is an fp16 value for every group of the expert (an
+ *         "exact" expert, e.g. bias = -8 * scale: the kernels form
+ *         q s' + b' with one rounding), else b' itself (a "general" expert:
+ *         q s' is rounded, then b' added and rounded).  Tail, after the
+ *         E * N * K/G words: float 2^-c [E], then uint32 general [E] (1 for
+ *         a general expert), zero-padded to 16 bytes.  The kernels multiply
+ *         their fp32 sums by 2^-c.  Scales and biases must be finite.
  * Requires N % 128 == 0, K % 128 == 0, G in {32, 64, 128}, K % G == 0. */
 typedef struct {
   const uint32_t* words;
   const uint32_t* sb;
 } moe_w4_packed;
 
-/* Byte sizes of the two packed buffers of one bank (host-only; 0 for
- * unsupported sizes). */
+/* Byte sizes of the two packed buffers of one bank, sb with its tail
+ * (host-only; 0 for unsupported sizes). */
 size_t moe_w4_packed_words_bytes(int32_t E, int32_t N, int32_t K);
 size_t moe_w4_packed_sb_bytes(int32_t E, int32_t N, int32_t K, int32_t group_size);
 /* Packs `src` (device, row-major) into words / sb (device buffers of the
@@ -167,20 +181,31 @@ int moe_build_blocks(const int32_t* topk_ids, int32_t T, int32_t top_k, int32_t 
  * MOE_GEMM_GATE_UP_SWIGLU: for every slot s of every tile (expert e), with
  *   token t = sorted_pairs[s] / top_k,
  *     g = W_gate[e] x[t],  u = W_up[e] x[t],  h[s][n] = silu(g_n) * u_n
- *   silu(z) = z / (1 + exp(-z)); a = x bf16 [T][K]; out = h fp16 [P][N]
- *   in operand order: within every run of 8 columns 8c..8c+7 the stored
- *   order is (8c+0, 8c+4, 8c+1, 8c+5, 8c+2, 8c+6, 8c+3, 8c+7);
- *   N = I, K = H; bank0 = gate, bank1 = up.
+ *   silu(z) = z / (1 + exp(-z)); a = x bf16 [T][K]; N = I, K = H; bank0 =
+ *   gate, bank1 = up.  h is written as out = h16 fp16 [P][N] and h_exp:
+ *     h[s][n] = h16[s][n] * 2^h_exp[s][n / 16]
+ *   h16 in operand order: within every run of 8 columns 8c..8c+7 the stored
+ *   order is (8c+0, 8c+4, 8c+1, 8c+5, 8c+2, 8c+6, 8c+3, 8c+7).  h_exp is
+ *   int8 [P][N / 16] (16-byte padded), then one int32 per tile of the block
+ *   map, nonzero when a row of the tile has a nonzero exponent.  An exponent
+ *   is 0 unless the 16-column block's largest |h| is at least 2^15, or below
+ *   2^-10 and not 0: then the block is scaled so that its largest |h| lies in
+ *   [2^14, 2^15).
  * MOE_GEMM_DOWN: for every slot s of every tile (expert e), pair
  *   p = sorted_pairs[s],
  *     out[s][n] = topk_weights[p] * (W_down[e] h[s])_n
- *   a = h fp16 [P][K] (slot order, operand order as written above); out =
- *   y_sorted fp32 [P][N]; N = H, K = I; bank0 = down; bank1 unused.
+ *   a = h16 fp16 [P][K] (slot order, operand order) and h_exp as written by
+ *   the gate/up mode with the same block map; out = y_sorted fp32 [P][N];
+ *   N = H, K = I; bank0 = down; bank1 unused.
  * T <= 8 runs a bandwidth-bound GEMV-style kernel that reads each touched
  * expert's packed rows once; larger T runs fp16 MFMA tiles of block_m rows
  * (block_m in {32, 64, 128}, equal to the block map's).  K % 128 == 0.
  * Slots outside every tile are not written.  workspace: device, >=
- * moe_w4_grouped_gemm_workspace_bytes(args). */
+ * moe_w4_grouped_gemm_workspace_bytes(args).  h_exp: device, 16-byte
+ * aligned, >= moe_w4_h_exp_bytes(T, top_k, E, I, block_m) bytes (both
+ * modes).  Page "Perplexity's Lily engine beats MLX by 35% on M5 Max",
+ * architecture paragraph: the grouped expert GEMM with the 4-bit
+ * dequantisation fused in. */
 typedef enum { MOE_GEMM_GATE_UP_SWIGLU = 0, MOE_GEMM_DOWN = 1 } moe_gemm_mode;
 
 typedef struct {
@@ -197,9 +222,14 @@ typedef struct {
   void* out;
   void* workspace;
   size_t workspace_bytes;
+  void* h_exp;                 /* h's exponents and tile flags (see the modes); device */
+  size_t h_exp_bytes;
 } moe_w4_gemm_args;
 
 size_t moe_w4_grouped_gemm_workspace_bytes(const moe_w4_gemm_args* args);
+/* Bytes of h_exp for P = T * top_k slots, I = h's columns and the block map
+ * of block_m rows per tile: round16(P * I / 16) + 4 * moe_max_blocks(...). */
+size_t moe_w4_h_exp_bytes(int32_t T, int32_t top_k, int32_t E, int32_t I, int32_t block_m);
 int moe_w4_grouped_gemm(const moe_w4_gemm_args* args, void* stream);
 
 /* -------------------------------------------------------------- whole layer --
@@ -223,7 +253,7 @@ typedef struct {
   const int32_t* pair_slot;     /* [P] */
   const int32_t* blocks;        /* [max_blocks][3] */
   const int32_t* num_blocks;    /* [1] */
-  const uint16_t* h;            /* fp16 [P][I], slot order, operand order */
+  const uint16_t* h;            /* h16 fp16 [P][I], slot order, operand order */
   const uint8_t* y_sorted;      /* [P][H] weighted, slot order, y_sorted_bytes
                                    per value: 4 = fp32 (path 1); 3 = packed
                                    24-bit (path 0): little-endian, the top 3
@@ -231,6 +261,7 @@ typedef struct {
                                    ties away from zero (relative error
                                    <= 2^-16) */
   int32_t y_sorted_bytes;
+  const int8_t* h_exp;          /* [P][I / 16]: h = h16 * 2^h_exp (see S6 above) */
 } moe_route_info;
 
 /* Tile rows moe_ffn_forward uses for these sizes (host-only). */

@@ -24,7 +24,7 @@ SYMBOLS = (
     "moe_status_string", "moe_last_error", "moe_version",
     "moe_w4_packed_words_bytes", "moe_w4_packed_sb_bytes", "moe_w4_pack",
     "moe_route", "moe_max_blocks", "moe_build_blocks_workspace_bytes", "moe_build_blocks",
-    "moe_w4_grouped_gemm_workspace_bytes", "moe_w4_grouped_gemm",
+    "moe_w4_grouped_gemm_workspace_bytes", "moe_w4_h_exp_bytes", "moe_w4_grouped_gemm",
     "moe_ffn_block_m", "moe_ffn_workspace_bytes", "moe_ffn_forward", "moe_ffn_forward_timed",
     "moe_ffn_host_blockmap_ints", "moe_ffn_forward_host_blockmap",
     "moe_ffn_unfused_bytes", "moe_ffn_forward_unfused",
@@ -67,14 +67,14 @@ class GemmArgs(ctypes.Structure):
                 ("K", c_i32), ("group_size", c_i32), ("block_m", c_i32), ("a", c_p),
                 ("bank0", Packed), ("bank1", Packed), ("sorted_pairs", c_p), ("topk_weights", c_p),
                 ("blocks", c_p), ("num_blocks", c_p), ("out", c_p), ("workspace", c_p),
-                ("workspace_bytes", c_sz)]
+                ("workspace_bytes", c_sz), ("h_exp", c_p), ("h_exp_bytes", c_sz)]
 
 
 class RouteInfo(ctypes.Structure):
     _fields_ = [("block_m", c_i32), ("path", c_i32), ("logits", c_p), ("topk_ids", c_p),
                 ("topk_weights", c_p), ("counts", c_p), ("offsets", c_p), ("sorted_pairs", c_p),
                 ("pair_slot", c_p), ("blocks", c_p), ("num_blocks", c_p), ("h", c_p),
-                ("y_sorted", c_p), ("y_sorted_bytes", c_i32)]
+                ("y_sorted", c_p), ("y_sorted_bytes", c_i32), ("h_exp", c_p)]
 
 
 class MoEError(RuntimeError):
@@ -111,6 +111,8 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     L.moe_w4_grouped_gemm_workspace_bytes.restype = c_sz
     L.moe_w4_grouped_gemm_workspace_bytes.argtypes = [ctypes.POINTER(GemmArgs)]
     L.moe_w4_grouped_gemm.argtypes = [ctypes.POINTER(GemmArgs), c_p]
+    L.moe_w4_h_exp_bytes.restype = c_sz
+    L.moe_w4_h_exp_bytes.argtypes = [c_i32] * 5
     L.moe_ffn_block_m.restype = c_i32
     L.moe_ffn_block_m.argtypes = [ctypes.POINTER(Dims)]
     L.moe_ffn_workspace_bytes.restype = c_sz

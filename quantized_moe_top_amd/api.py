@@ -20,7 +20,8 @@ from ._lib import (MOE_GEMM_DOWN, MOE_GEMM_GATE_UP_SWIGLU, Bank, Dims, GemmArgs,
 
 __all__ = ["pack_bank", "pack_layer", "PackedBank", "PackedLayer",
            "route", "build_blocks", "w4_grouped_gemm", "ffn_forward", "ffn_workspace_bytes",
-           "ffn_block_m", "max_blocks", "stage_events", "MOE_GEMM_GATE_UP_SWIGLU", "MOE_GEMM_DOWN"]
+           "ffn_block_m", "max_blocks", "stage_events", "h_exp_bytes", "MOE_GEMM_GATE_UP_SWIGLU",
+           "MOE_GEMM_DOWN"]
 
 
 def _L():
@@ -161,19 +162,30 @@ def build_blocks(topk_ids: torch.Tensor, E: int, block_m: int) -> dict:
     return out
 
 
+def h_exp_bytes(T: int, top_k: int, E: int, I: int, block_m: int) -> int:
+    return int(_L().moe_w4_h_exp_bytes(T, top_k, E, I, block_m))
+
+
 def w4_grouped_gemm(mode: int, a: torch.Tensor, bank0, bank1, sorted_pairs: torch.Tensor,
                     blocks: torch.Tensor, num_blocks: torch.Tensor, *, T: int, top_k: int, E: int,
                     group_size: int, block_m: int, topk_weights: Optional[torch.Tensor] = None,
-                    out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """S6 (mode MOE_GEMM_GATE_UP_SWIGLU: a = x bf16 [T, H], returns h fp16
-    [P, I] in operand order) or S7 (MOE_GEMM_DOWN: a = h fp16 [P, I],
-    returns y_sorted fp32 [P, H]).  Slots outside every tile are left as they
-    were in ``out``."""
+                    out: Optional[torch.Tensor] = None, h_exp: Optional[torch.Tensor] = None):
+    """S6 (mode MOE_GEMM_GATE_UP_SWIGLU: a = x bf16 [T, H]; returns
+    ``(h16, h_exp)``: h16 fp16 [P, I] in operand order and h_exp, a uint8
+    device tensor of ``h_exp_bytes`` holding the int8 exponents [P, I / 16]
+    and the per-tile flags, h = h16 * 2^exp) or S7 (MOE_GEMM_DOWN: a = h16,
+    with ``h_exp`` from the S6 call; returns y_sorted fp32 [P, H]).  Slots
+    outside every tile are left as they were in ``out``."""
     gate_up = mode == MOE_GEMM_GATE_UP_SWIGLU
     bank0 = _packed(bank0, group_size)
     bank1 = _packed(bank1, group_size) if bank1 is not None else None
     N, K = bank0.N, bank0.K
     P = T * top_k
+    hb = h_exp_bytes(T, top_k, E, N if gate_up else K, block_m)
+    if h_exp is None:
+        if not gate_up:
+            raise ValueError("the down mode needs h_exp from the gate/up call")
+        h_exp = torch.empty(max(hb, 16), dtype=torch.uint8, device=a.device)
     if out is None:
         out = torch.empty((P, N), dtype=torch.float16 if gate_up else torch.float32, device=a.device)
     args = GemmArgs(mode=mode, T=T, top_k=top_k, E=E, N=N, K=K, group_size=group_size,
@@ -190,8 +202,10 @@ def w4_grouped_gemm(mode: int, a: torch.Tensor, bank0, bank1, sorted_pairs: torc
     ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=a.device)
     args.workspace = ws.data_ptr()
     args.workspace_bytes = wsb
+    args.h_exp = _dev(h_exp, "h_exp", torch.uint8)
+    args.h_exp_bytes = h_exp.numel()
     _lib.check(_L().moe_w4_grouped_gemm(ctypes.byref(args), _stream()), "moe_w4_grouped_gemm")
-    return out
+    return (out, h_exp) if gate_up else out
 
 
 def _dims(layer, T: int) -> Dims:
@@ -380,6 +394,8 @@ def _info_views(ri: RouteInfo, ws: torch.Tensor, layer, T: int, logits) -> dict:
         blocks=view(ri.blocks, mb * 3, torch.int32, (mb, 3)),
         num_blocks=view(ri.num_blocks, 1, torch.int32, (1,)),
         h=view(ri.h, P * layer.I, torch.float16, (P, layer.I)),
+        # h = h * 2^h_exp per 16-column block
+        h_exp=view(ri.h_exp, P * (layer.I // 16), torch.int8, (P, layer.I // 16)),
         # fp32, or packed 24-bit (3 bytes a value, unpack_y24 gives fp32)
         y_sorted=(view(ri.y_sorted, P * layer.H, torch.float32, (P, layer.H))
                   if ri.y_sorted_bytes == 4 else

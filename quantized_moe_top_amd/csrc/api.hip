@@ -78,10 +78,17 @@ size_t gemm_workspace(int mode, int64_t T, int64_t K) {
   return mode == MOE_GEMM_GATE_UP_SWIGLU ? round_up((size_t)T * K * 2) : 0;
 }
 
+// h's exponents [P][I / 16] (16-byte padded), then one flag per tile.
+size_t hexp_part(int64_t P, int64_t I) { return ((size_t)P * (I / 16) + 15) & ~(size_t)15; }
+size_t hexp_bytes(int64_t T, int k, int E, int64_t I, int block_m) {
+  const int64_t P = T * k;
+  return hexp_part(P, I) + 4 * (size_t)max_blocks(P, E, block_m);
+}
+
 // Workspace layout of moe_ffn_forward.
 struct FfnLayout {
   size_t logits, logits_part, ids, w, counts, offsets, sorted_pairs, pair_slot, blocks,
-      num_blocks, scratch, xh, h, y_sorted, total;
+      num_blocks, scratch, xh, h, hexp, tflags, y_sorted, total;
   int router_ks;  // ranges of H the router sums separately (1: no partial sums)
 };
 
@@ -108,6 +115,8 @@ FfnLayout ffn_layout(const moe_dims& d, bool has_router, int block_m) {
   L.scratch = take((size_t)moe::route_chunks(d.T) * E * 4);
   L.xh = take(T * H * 2);
   L.h = take(P * I * 2);
+  L.hexp = take(P * (I / 16));                                          // h's exponents
+  L.tflags = take((size_t)max_blocks((int64_t)P, d.E, block_m) * 4);  // per-tile flags
   L.y_sorted = take(P * H * (d.T <= moe::kGemvMaxTokens ? 4 : 3));  // fp32 or packed 24-bit
   L.total = o;
   return L;
@@ -170,7 +179,8 @@ size_t moe_w4_packed_words_bytes(int32_t E, int32_t N, int32_t K) {
 
 size_t moe_w4_packed_sb_bytes(int32_t E, int32_t N, int32_t K, int32_t group_size) {
   if (!pack_sizes_ok(E, N, K, group_size)) return 0;
-  return (size_t)E * N * (K / group_size) * 4;
+  // the words, then per expert 2^-c and the dequantisation form (16-byte padded)
+  return (size_t)E * N * (K / group_size) * 4 + (((size_t)E * 8 + 15) & ~(size_t)15);
 }
 
 int moe_w4_pack(const moe_w4_bank* src, int32_t E, int32_t N, int32_t K, int32_t group_size,
@@ -235,6 +245,11 @@ int moe_w4_grouped_gemm(const moe_w4_gemm_args* a, void* stream) {
     return fail(MOE_ERR_UNSUPPORTED, "N = %d not a multiple of %d", a->N, gate_up ? 128 : 256);
   if ((st = gemm_block_ok(a->T, a->block_m))) return st;
   if (a->T == 0) return ok();
+  const int64_t hI = gate_up ? a->N : a->K;  // h's columns
+  const size_t hneed = hexp_bytes(a->T, a->top_k, a->E, hI, a->block_m);
+  if (!a->h_exp) return fail(MOE_ERR_NULL, "h_exp is NULL");
+  if (!aligned16(a->h_exp)) return fail(MOE_ERR_ALIGN, "h_exp not 16-byte aligned");
+  if (a->h_exp_bytes < hneed) return fail(MOE_ERR_WORKSPACE, "h_exp %zu < %zu bytes", a->h_exp_bytes, hneed);
   if (!a->a || !a->sorted_pairs || !a->blocks || !a->num_blocks || !a->out)
     return fail(MOE_ERR_NULL, "a/sorted_pairs/blocks/num_blocks/out NULL");
   if (!gate_up && !a->topk_weights) return fail(MOE_ERR_NULL, "topk_weights NULL");
@@ -249,14 +264,25 @@ int moe_w4_grouped_gemm(const moe_w4_gemm_args* a, void* stream) {
   moe::GemmArgs g{a->mode, a->T, a->top_k, a->E, a->N, a->K, a->group_size, a->block_m,
                   (const moe::half_t*)a->a, a->bank0, a->bank1, a->sorted_pairs,
                   a->topk_weights, a->blocks, a->num_blocks, a->out};
+  g.t0 = moe::bank_tail(a->bank0, a->E, a->N, a->K, a->group_size);
+  g.t1 = gate_up ? moe::bank_tail(a->bank1, a->E, a->N, a->K, a->group_size) : g.t0;
+  g.hexp = (int8_t*)a->h_exp;
+  g.tflags = (int32_t*)((char*)a->h_exp + hexp_part((int64_t)a->T * a->top_k, hI));
   if (gate_up) {
+    // the fp16 operand copy of x; the tile flags the kernel sets start cleared
     hipError_t err = moe::launch_stage_x((const uint16_t*)a->a, (moe::half_t*)a->workspace,
-                                         (int64_t)a->T * a->K, s);
+                                         (int64_t)a->T * a->K, g.tflags,
+                                         max_blocks((int64_t)a->T * a->top_k, a->E, a->block_m), s);
     if (err != hipSuccess) return hip_status(err, "stage_x");
     g.a = (const moe::half_t*)a->workspace;
   }
   const hipError_t err = a->T <= moe::kGemvMaxTokens ? moe::launch_w4_gemv(g, s) : moe::launch_w4_mfma(g, s);
   return hip_status(err, "w4_grouped_gemm");
+}
+
+size_t moe_w4_h_exp_bytes(int32_t T, int32_t top_k, int32_t E, int32_t I, int32_t block_m) {
+  if (T <= 0 || top_k <= 0 || E <= 0 || I <= 0 || I % 16 || block_m <= 0) return 0;
+  return hexp_bytes(T, top_k, E, I, block_m);
 }
 
 int32_t moe_ffn_block_m(const moe_dims* d) {
@@ -356,7 +382,7 @@ int ffn_forward_impl(const moe_layer* layer, const uint16_t* x, const float* rou
   const int block_m = moe_ffn_block_m(&d);
   if (d.T == 0) {  // empty tensors may carry NULL data pointers
     if (info) *info = moe_route_info{block_m, 1, router_logits, nullptr, nullptr, nullptr, nullptr,
-                                     nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 4};
+                                     nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 4, nullptr};
     return ok();
   }
   if (has_router == (router_logits != nullptr))
@@ -405,11 +431,14 @@ int ffn_forward_impl(const moe_layer* layer, const uint16_t* x, const float* rou
   moe::half_t* xh = (moe::half_t*)(ws + L.xh);
   moe::half_t* h = (moe::half_t*)(ws + L.h);
   uint8_t* y_sorted = (uint8_t*)(ws + L.y_sorted);
+  int8_t* hexp = (int8_t*)(ws + L.hexp);
+  int32_t* tflags = (int32_t*)(ws + L.tflags);
+  const int64_t nflags = max_blocks((int64_t)d.T * d.top_k, d.E, block_m);
   const bool gemv = d.T <= moe::kGemvMaxTokens;
   if (info) {
     *info = moe_route_info{block_m, gemv ? 1 : 0, logits, ids, w, counts, offsets, sorted_pairs,
                            pair_slot, blocks, num_blocks, (const uint16_t*)h, y_sorted,
-                           gemv ? 4 : 3};
+                           gemv ? 4 : 3, hexp};
   }
 
   hipError_t err;
@@ -445,7 +474,7 @@ int ffn_forward_impl(const moe_layer* layer, const uint16_t* x, const float* rou
     }
     if ((err = moe::launch_scan_scatter(ids, d.T, d.top_k, d.E, chunk_hist, block_m, counts, offsets,
                                         sorted_pairs, pair_slot, blocks, num_blocks, s,
-                                        host ? chunk_hist : nullptr)) != hipSuccess)
+                                        host ? chunk_hist : nullptr, tflags, nflags)) != hipSuccess)
       return hip_status(err, "scan_scatter");
   }
   moe::GemmArgs g1{MOE_GEMM_GATE_UP_SWIGLU, d.T, d.top_k, d.E, d.I, d.H, d.group_size, block_m,
@@ -454,6 +483,11 @@ int ffn_forward_impl(const moe_layer* layer, const uint16_t* x, const float* rou
   moe::GemmArgs g2{MOE_GEMM_DOWN, d.T, d.top_k, d.E, d.H, d.I, d.group_size, block_m,
                    h, layer->down, layer->down, sorted_pairs, w, blocks, num_blocks, y_sorted,
                    !gemv, grid_tiles};
+  g1.hexp = g2.hexp = hexp;
+  g1.tflags = g2.tflags = tflags;
+  g1.t0 = moe::bank_tail(layer->gate, d.E, d.I, d.H, d.group_size);
+  g1.t1 = moe::bank_tail(layer->up, d.E, d.I, d.H, d.group_size);
+  g2.t0 = g2.t1 = moe::bank_tail(layer->down, d.E, d.H, d.I, d.group_size);
   if ((err = mark(events, MOE_STAGE_GATE_UP, s)) != hipSuccess) return hip_status(err, "event");
   if (gemv) {
     g1.a = (const moe::half_t*)x;  // bf16, converted while staged

@@ -46,7 +46,10 @@ __global__ __launch_bounds__(kScanThreads) void scan_scatter_kernel(
     const int32_t* __restrict__ chunk_hist, int block_m, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pairs,
     int32_t* __restrict__ pair_slot, int32_t* __restrict__ blocks, int32_t* __restrict__ num_blocks,
-    const int32_t* __restrict__ chunk_start) {
+    const int32_t* __restrict__ chunk_start, int32_t* __restrict__ tflags, int nflags) {
+  // the per-tile flags the gate/up kernel sets start cleared
+  for (int i = blockIdx.x * kScanThreads + threadIdx.x; i < nflags; i += gridDim.x * kScanThreads)
+    tflags[i] = 0;
   scan_scatter_chunk(ids, P, E, chunk_pairs, nchunks, chunk_hist, block_m, counts, offsets,
                      sorted_pairs, pair_slot, blocks, num_blocks, blockIdx.x, chunk_start);
 }
@@ -64,13 +67,14 @@ hipError_t launch_chunk_hist(const int32_t* ids, int T, int k, int E, int32_t* c
 hipError_t launch_scan_scatter(const int32_t* ids, int T, int k, int E, const int32_t* chunk_hist,
                                int block_m, int32_t* counts, int32_t* offsets,
                                int32_t* sorted_pairs, int32_t* pair_slot, int32_t* blocks,
-                               int32_t* num_blocks, hipStream_t s, const int32_t* chunk_start) {
+                               int32_t* num_blocks, hipStream_t s, const int32_t* chunk_start,
+                               int32_t* tflags, int64_t nflags) {
   if (T <= 0) return hipSuccess;
   const int chunk_pairs = route_chunk_tokens(T) * k;
   const int n = route_chunks(T);
   scan_scatter_kernel<<<n, kScanThreads, 0, s>>>(ids, T * k, E, chunk_pairs, n, chunk_hist, block_m, counts,
                                         offsets, sorted_pairs, pair_slot, blocks, num_blocks,
-                                        chunk_start);
+                                        chunk_start, tflags, tflags ? (int)nflags : 0);
   return hipGetLastError();
 }
 

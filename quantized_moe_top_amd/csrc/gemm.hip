@@ -32,6 +32,8 @@
 // Work items (tile, column block) are spread over the 8 XCDs in contiguous
 // ranges, so the column blocks of one tile, and the tiles of one expert, run
 // on the same XCD at about the same time and share its L2.
+#include <algorithm>
+
 #include "internal.h"
 
 namespace moe {
@@ -52,6 +54,9 @@ struct MfmaParams {
   const int32_t* blocks;
   const int32_t* num_blocks;
   void* out;
+  BankTail t0, t1;  // per-expert 2^-c and dequantisation form of b0 / b1
+  int8_t* hexp;     // h's exponents [P][I / 16]: written by S6, read by S7
+  int32_t* tflags;  // per tile: a row of it has a nonzero exponent
   int N, K, log2_G, top_k, E, P, max_blocks;
 };
 
@@ -85,6 +90,8 @@ __global__ __launch_bounds__(64 * WAVES, WGS_PER_CU) void w4_mfma_kernel(const M
   constexpr int OUT_COLS = GATE_UP ? kBCols / 2 : kBCols; // output columns per workgroup
   __shared__ __attribute__((aligned(16))) char lds[STAGES * STAGE];
   __shared__ float row_w[BM];
+  __shared__ int erow[GATE_UP ? 1 : BM];  // S7, tiles with scaled h rows: each row's largest exponent
+  static_assert(!GATE_UP || BM * OUT_COLS * 4 <= STAGES * STAGE, "fp32 h tile must fit the ring");
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS and block addresses stay scalar
@@ -104,6 +111,13 @@ __global__ __launch_bounds__(64 * WAVES, WGS_PER_CU) void w4_mfma_kernel(const M
   const int e = p.blocks[3 * tile], row0 = p.blocks[3 * tile + 1], rows = p.blocks[3 * tile + 2];
   // a malformed block map is skipped, never dereferenced out of bounds
   if (e < 0 || e >= p.E || rows <= 0 || rows > BM || row0 < 0 || row0 > p.P - rows) return;
+  // the expert's factors 2^-c (its weights were scaled by 2^c at pack time)
+  // and dequantisation form (uniform: scalar loads)
+  const float us0 = p.t0.unscale[e], us1 = GATE_UP ? p.t1.unscale[e] : 1.0f;
+  const bool gen = !DENSE && (p.t0.general[e] | (GATE_UP ? p.t1.general[e] : 0u)) != 0;
+  // S7: a tile some of whose h rows carry nonzero exponents takes the scaled
+  // path below (uniform)
+  const bool scaled = !GATE_UP && p.tflags[tile] != 0;
 
   // ---- A loads: instruction j covers rows 8j..8j+7; lane l fills physical
   // chunk l % 8 of row 8j + l / 8, i.e. logical chunk (l % 8) ^ (l / 8).
@@ -139,7 +153,7 @@ __global__ __launch_bounds__(64 * WAVES, WGS_PER_CU) void w4_mfma_kernel(const M
   }
   if (!GATE_UP && tid < BM) {
     const int pair = tid < rows ? p.sorted_pairs[row0 + tid] : -1;
-    row_w[tid] = (pair >= 0 && pair < p.P) ? p.topk_weights[pair] : 0.0f;
+    row_w[tid] = (pair >= 0 && pair < p.P) ? p.topk_weights[pair] * us0 : 0.0f;
   }
 
   // packed 32-column block (index into the bank's N/32) of weight-column
@@ -202,8 +216,14 @@ __global__ __launch_bounds__(64 * WAVES, WGS_PER_CU) void w4_mfma_kernel(const M
   // tile's rows fit in the first half: the copies of the other half's
   // activations and its MFMAs are skipped; its accumulators stay zero and
   // its rows are never stored).
-  auto pipeline = [&](auto mba) {
+  // GEN: the general dequantisation (see dequant_word_gen).  SCALED (S7):
+  // h rows with nonzero exponents; each slab's activations are brought to
+  // their row's largest exponent in LDS before the multiplies (one stage, no
+  // copies in flight across slabs: such tiles are rare).
+  auto pipeline = [&](auto mba, auto gen_tag, auto scaled_tag) {
     constexpr int MBA = decltype(mba)::value;
+    constexpr bool GEN = decltype(gen_tag)::value != 0;
+    constexpr bool SCALED = decltype(scaled_tag)::value != 0;
     constexpr bool DUP = HALF_DUP && MBA < MB;
     constexpr int APW = DUP ? 1 : A_PER_WAVE * MBA / MB;  // activation copies used (rows < 32 MBA)
     constexpr int DA = APW + B_PER_WAVE + S_PER_WAVE;
@@ -225,7 +245,7 @@ __global__ __launch_bounds__(64 * WAVES, WGS_PER_CU) void w4_mfma_kernel(const M
     auto compute = [&](int stage) {
       const char* base = lds + stage * STAGE;
       u32x4 q[2];
-      half2_t s2[2], b2[2];
+      half2_t s2[2], b2[2], n2[2];
       if constexpr (!DENSE) {
 #pragma unroll
         for (int cb = 0; cb < 2; cb++)
@@ -236,6 +256,7 @@ __global__ __launch_bounds__(64 * WAVES, WGS_PER_CU) void w4_mfma_kernel(const M
           const uint32_t sb = reinterpret_cast<const uint32_t*>(
               base + A_BYTES + kBStage)[(G32 ? khalf : 0) * kBCols + wave * 64 + cb * 32 + col];
           sb_pairs(sb, s2[cb], b2[cb]);
+          if constexpr (GEN) n2[cb] = s2[cb] * half2_t{(half_t)-32.0f, (half_t)-32.0f};
         }
       }
 #pragma unroll
@@ -246,6 +267,8 @@ __global__ __launch_bounds__(64 * WAVES, WGS_PER_CU) void w4_mfma_kernel(const M
           if constexpr (DENSE)
             bf[cb] = *reinterpret_cast<const half8_t*>(base + A_BYTES + (2 * wave + cb) * 4096 +
                                                        1024 * i + 16 * (2 * col + khalf));
+          else if constexpr (GEN)
+            bf[cb] = __builtin_bit_cast(half8_t, dequant_word_gen(q[cb][i], s2[cb], n2[cb], b2[cb]));
           else
             bf[cb] = __builtin_bit_cast(half8_t, dequant_word(q[cb][i], s2[cb], b2[cb]));
         }
@@ -270,30 +293,76 @@ __global__ __launch_bounds__(64 * WAVES, WGS_PER_CU) void w4_mfma_kernel(const M
     // (s + STAGES - 1) % STAGES (computed last at slab s - 1, by every wave)
     // is refilled with slab s + STAGES - 1.
     const int S = slabs;
+    if constexpr (SCALED) {
+      const int nbk = K / 16;  // exponent bytes per h row
+      for (int s = 0; s < S; s++) {
+        issue(s, 0);
+        wait_vm_barrier<0>();
+        // activation chunk (row r, physical chunk pc) holds reduction indices
+        // 64 s + 8 (pc ^ (r % 8)) .. + 7, inside 16-column block 4 s + lc / 2
+        for (int c = tid; c < 32 * MBA * 8; c += 64 * WAVES) {
+          const int r = c >> 3, pc = c & 7, lc = pc ^ (r & 7);
+          const int d = p.hexp[(size_t)(row0 + min(r, rows - 1)) * nbk + 4 * s + (lc >> 1)] - erow[r];
+          if (d != 0) {
+            uint4* at = reinterpret_cast<uint4*>(lds + r * 128 + pc * 16);
+            *at = scale_half8(*at, d);
+          }
+        }
+        // the exponent loads and the rescaled LDS writes complete, then all waves meet
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        compute(0);
+        asm volatile("s_barrier" ::: "memory");  // stage 0 is refilled next
+      }
+    } else {
 #pragma unroll
-    for (int j = 0; j < STAGES - 1; j++) issue(min(j, S - 1), j);
-    for (int s = 0; s < S; s++) {
-      wait_vm_barrier<(STAGES - 2) * DA>();
-      issue(min(s + STAGES - 1, S - 1), (s + STAGES - 1) % STAGES);
-      compute(s % STAGES);
+      for (int j = 0; j < STAGES - 1; j++) issue(min(j, S - 1), j);
+      for (int s = 0; s < S; s++) {
+        wait_vm_barrier<(STAGES - 2) * DA>();
+        issue(min(s + STAGES - 1, S - 1), (s + STAGES - 1) % STAGES);
+        compute(s % STAGES);
+      }
     }
   };
+  if (!GATE_UP && scaled) {
+    // each row's largest exponent (rows past the tile repeat its last row);
+    // the row's output is scaled by 2^that (with the routing weight)
+    const int nbk = K / 16;
+    for (int r = tid; r < BM; r += 64 * WAVES) {
+      const uint32_t* er = reinterpret_cast<const uint32_t*>(p.hexp + (size_t)(row0 + min(r, rows - 1)) * nbk);
+      int m = -128;
+      for (int b = 0; b < nbk / 4; b++) m = max(m, max_i8x4(er[b]));
+      erow[r] = m;
+      row_w[r] = ldexpf(row_w[r], m);
+    }
+    __syncthreads();
+  }
   // uniform per workgroup: every wave takes the same branch
-  if (MB > 1 && rows <= BM / 2)
-    pipeline(IntTag<(MB > 1 ? MB / 2 : 1)>{});
-  else
-    pipeline(IntTag<MB>{});
+  if (!GATE_UP && scaled) {
+    if (gen) pipeline(IntTag<MB>{}, IntTag<DENSE ? 0 : 1>{}, IntTag<1>{});
+    else pipeline(IntTag<MB>{}, IntTag<0>{}, IntTag<1>{});
+  } else if (gen) {
+    if (MB > 1 && rows <= BM / 2)
+      pipeline(IntTag<(MB > 1 ? MB / 2 : 1)>{}, IntTag<DENSE ? 0 : 1>{}, IntTag<0>{});
+    else
+      pipeline(IntTag<MB>{}, IntTag<DENSE ? 0 : 1>{}, IntTag<0>{});
+  } else {
+    if (MB > 1 && rows <= BM / 2)
+      pipeline(IntTag<(MB > 1 ? MB / 2 : 1)>{}, IntTag<0>{}, IntTag<0>{});
+    else
+      pipeline(IntTag<MB>{}, IntTag<0>{}, IntTag<0>{});
+  }
 
   // ---- epilogue.  Accumulator register r of lane l holds row
   // 8*(r/4) + 4*(l/32) + r%4 and column l%32 of each 32x32 block.
   if (GATE_UP) {
-    // h = silu(gate) * up into an LDS tile [BM][OUT_COLS] (operand order:
-    // column 8g + j at 8g + interleaved_pos(j)), then out with 16-byte row
-    // stores.  The ring is free once every copy has landed (the last steps
-    // reloaded the last slab) and every wave has finished its MFMAs.
+    // h = silu(gate) * up in fp32 into an LDS tile [BM][OUT_COLS] (operand
+    // order: column 8g + j at 8g + interleaved_pos(j)), then stored as fp16
+    // with one exponent per row and 16-column block (h_block_exp), 16-byte
+    // row stores.  The ring is free once every copy has landed (the last
+    // steps reloaded the last slab) and every wave has finished its MFMAs.
     wait_vm<0>();
     __syncthreads();
-    half_t* tile_h = reinterpret_cast<half_t*>(lds);
+    float* tile_f = reinterpret_cast<float*>(lds);
     if (active) {
       const int lc = wave * 32 + (col & ~7) + interleaved_pos(col & 7);
 #pragma unroll
@@ -301,17 +370,39 @@ __global__ __launch_bounds__(64 * WAVES, WGS_PER_CU) void w4_mfma_kernel(const M
 #pragma unroll
         for (int r = 0; r < 16; r++) {
           const int row = mb * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3);
-          tile_h[row * OUT_COLS + lc] = (half_t)silu_mul(acc[mb][0][r], acc[mb][1][r]);
+          tile_f[row * OUT_COLS + lc] = silu_mul(acc[mb][0][r] * us0, acc[mb][1][r] * us1);
         }
     }
     __syncthreads();
     const int n0 = nb * OUT_COLS;
-    const int chunks = min(OUT_COLS, N - n0) / 8;  // 16-byte pieces per row
-    for (int idx = tid; idx < rows * chunks; idx += 64 * WAVES) {
-      const int row = idx / chunks, ch = idx % chunks;
-      *reinterpret_cast<uint4*>(reinterpret_cast<half_t*>(p.out) + (size_t)(row0 + row) * N + n0 + 8 * ch) =
-          *reinterpret_cast<const uint4*>(tile_h + row * OUT_COLS + 8 * ch);
+    const int chunks = min(OUT_COLS, N - n0) / 8;  // 16-byte pieces per row (an even count)
+    const int total8 = rows * chunks;
+    bool any = false;
+    // every lane runs every round, so that lane pairs (2i, 2i + 1) -- the two
+    // 8-column pieces of one 16-column block -- exchange their maxima
+    for (int base = 0; base < total8; base += 64 * WAVES) {
+      const int idx = base + tid;
+      const bool ok = idx < total8;
+      const int row = ok ? idx / chunks : 0, ch = ok ? idx % chunks : 0;
+      const float4 v0 = *reinterpret_cast<const float4*>(tile_f + row * OUT_COLS + 8 * ch);
+      const float4 v1 = *reinterpret_cast<const float4*>(tile_f + row * OUT_COLS + 8 * ch + 4);
+      float m = fmaxf(fmaxf(fmaxf(fabsf(v0.x), fabsf(v0.y)), fmaxf(fabsf(v0.z), fabsf(v0.w))),
+                      fmaxf(fmaxf(fabsf(v1.x), fabsf(v1.y)), fmaxf(fabsf(v1.z), fabsf(v1.w))));
+      m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0xB1, 0xF, 0xF, true)));
+      const int ex = h_block_exp(m);
+      if (ok) {
+        const half2_t o0 = {(half_t)ldexpf(v0.x, -ex), (half_t)ldexpf(v0.y, -ex)};
+        const half2_t o1 = {(half_t)ldexpf(v0.z, -ex), (half_t)ldexpf(v0.w, -ex)};
+        const half2_t o2 = {(half_t)ldexpf(v1.x, -ex), (half_t)ldexpf(v1.y, -ex)};
+        const half2_t o3 = {(half_t)ldexpf(v1.z, -ex), (half_t)ldexpf(v1.w, -ex)};
+        *reinterpret_cast<uint4*>(reinterpret_cast<half_t*>(p.out) + (size_t)(row0 + row) * N + n0 + 8 * ch) =
+            make_uint4(__builtin_bit_cast(uint32_t, o0), __builtin_bit_cast(uint32_t, o1),
+                       __builtin_bit_cast(uint32_t, o2), __builtin_bit_cast(uint32_t, o3));
+        if (!(ch & 1)) p.hexp[(size_t)(row0 + row) * (N / 16) + (n0 + 8 * ch) / 16] = (int8_t)ex;
+        any |= ex != 0;
+      }
     }
+    if (any) p.tflags[tile] = 1;
   } else if constexpr (PACK) {
     if (!active) return;
     // Registers 4g .. 4g + 3 of a lane hold 4 consecutive rows of one
@@ -383,10 +474,13 @@ __global__ __launch_bounds__(64 * WAVES, WGS_PER_CU) void w4_mfma_kernel(const M
 }
 
 
-// x bf16 -> fp16, each 8-element chunk interleaved (0,4,1,5,2,6,3,7).
+// x bf16 -> fp16, each 8-element chunk interleaved (0,4,1,5,2,6,3,7); the
+// per-tile flags of the gate/up kernel cleared.
 __global__ __launch_bounds__(256) void stage_x_kernel(const uint4* __restrict__ in,
-                                                      uint4* __restrict__ out, int64_t n8) {
+                                                      uint4* __restrict__ out, int64_t n8,
+                                                      int32_t* __restrict__ tflags, int64_t nflags) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < nflags) tflags[i] = 0;
   if (i >= n8) return;
   out[i] = bf16x8_to_half_interleaved(in[i]);
 }
@@ -398,7 +492,7 @@ hipError_t launch_mode(const GemmArgs& a, hipStream_t s) {
   if (max_blocks == 0) return hipSuccess;
   const int log2_G = a.G == 32 ? 5 : a.G == 64 ? 6 : 7;  // G in {32, 64, 128}
   MfmaParams p{a.a, a.b0, a.b1, a.sorted_pairs, a.topk_weights, a.blocks, a.num_blocks, a.out,
-               a.N, a.K, log2_G, a.top_k, a.E, (int)P, (int)max_blocks};
+               a.t0, a.t1, a.hexp, a.tflags, a.N, a.K, log2_G, a.top_k, a.E, (int)P, (int)max_blocks};
   // 4 waves (256 weight columns) per workgroup and two or three workgroups
   // per CU, so one workgroup's prologue and epilogue overlap another's main
   // loop; 64- and 128-row tiles use a 3-stage ring to fit three and two
@@ -427,7 +521,9 @@ hipError_t launch_mode(const GemmArgs& a, hipStream_t s) {
     case 64: w4_mfma_kernel<MODE, 1, 4, false, 4, 2, PACK><<<grid, 256, 0, s>>>(p); break;
     case 65: w4_mfma_kernel<MODE, 1, 4, true, 4, 2, PACK><<<grid, 256, 0, s>>>(p); break;
     case 128: w4_mfma_kernel<MODE, 2, 4, false, 3, 3, PACK><<<grid, 256, 0, s>>>(p); break;
-    case 129: w4_mfma_kernel<MODE, 2, 4, true, 3, 3, PACK><<<grid, 256, 0, s>>>(p); break;
+    // group size 32 stages two (scale, bias) copies per slab: three 64-row
+    // workgroups would need 166 KB of LDS, so two share a CU, with a deeper ring
+    case 129: w4_mfma_kernel<MODE, 2, 4, true, 4, 2, PACK><<<grid, 256, 0, s>>>(p); break;
     case 256: w4_mfma_kernel<MODE, 4, 4, false, 3, 2, PACK><<<grid, 256, 0, s>>>(p); break;
     case 257: w4_mfma_kernel<MODE, 4, 4, true, 3, 2, PACK><<<grid, 256, 0, s>>>(p); break;
     default: return hipErrorInvalidValue;
@@ -487,10 +583,13 @@ hipError_t launch_w4_mfma(const GemmArgs& a, hipStream_t s) {
   return a.pack24 ? launch_mode<MOE_GEMM_DOWN, true>(a, s) : launch_mode<MOE_GEMM_DOWN, false>(a, s);
 }
 
-hipError_t launch_stage_x(const uint16_t* x, half_t* xh, int64_t n_elems, hipStream_t s) {
+hipError_t launch_stage_x(const uint16_t* x, half_t* xh, int64_t n_elems, int32_t* tflags,
+                          int64_t nflags, hipStream_t s) {
   const int64_t n8 = n_elems / 8;
-  stage_x_kernel<<<(n8 + 255) / 256, 256, 0, s>>>(reinterpret_cast<const uint4*>(x),
-                                                  reinterpret_cast<uint4*>(xh), n8);
+  const int64_t n = std::max(n8, tflags ? nflags : 0);
+  stage_x_kernel<<<(n + 255) / 256, 256, 0, s>>>(reinterpret_cast<const uint4*>(x),
+                                                 reinterpret_cast<uint4*>(xh), n8, tflags,
+                                                 tflags ? nflags : 0);
   return hipGetLastError();
 }
 

@@ -16,6 +16,8 @@
 // only dequantises (same exact fp16 dequantisation as the prefill path).
 // The waves' partial sums meet in LDS and are added in wave order, so the
 // result does not depend on timing.
+#include <type_traits>
+
 #include "internal.h"
 #include "topk.h"
 
@@ -32,6 +34,9 @@ struct DecParams {
   const int32_t* blocks;
   const int32_t* num_blocks;
   void* out;
+  BankTail t0, t1;  // per-expert 2^-c and dequantisation form of b0 / b1
+  int8_t* hexp;     // h's exponents [P][I / 16] (h_block_exp): written by S6, read by S7
+  int32_t* tflags;  // per tile: a row has a nonzero exponent (written by S6 when given)
   int N, K, log2_G, top_k, E, P, max_blocks;
   int red_off;  // byte offset of the partial-sum area in the dynamic LDS
 };
@@ -43,7 +48,8 @@ struct DecParams {
 // converted to fp16 operand order while staged, instead of the fp16 copy.
 // sorted_pairs: slot -> pair (global memory, or LDS in the fused kernel).
 // dsm: the dynamic LDS, sized by the launch.
-template <int MODE, int SPW, bool PACK, bool XBF16>
+// GEN: the expert takes the general dequantisation (dequant_word_gen).
+template <int MODE, int SPW, bool PACK, bool XBF16, bool GEN>
 __device__ __forceinline__ void gemv_tile(const DecParams& p, const int32_t* sorted_pairs, int e,
                                           int row0, int rows, int blk, char* dsm) {
   constexpr bool GATE_UP = MODE == MOE_GEMM_GATE_UP_SWIGLU;
@@ -76,6 +82,20 @@ __device__ __forceinline__ void gemv_tile(const DecParams& p, const int32_t* sor
     ssrc[b] = bank.sb + (bidx >> 2) * gpr * 128 + (bidx & 3) * 32 + col;
   }
 
+  // the expert's factors 2^-c
+  const float us0 = p.t0.unscale[e], us1 = GATE_UP ? p.t1.unscale[e] : 1.0f;
+  // S7: each h row's largest exponent; its blocks are brought to it while
+  // staged, and the row's output is scaled by 2^it
+  __shared__ int em_s[kGemvMaxTokens];
+  if (!GATE_UP) {
+    if (tid < rows) {
+      const uint32_t* er = reinterpret_cast<const uint32_t*>(p.hexp + (size_t)(row0 + tid) * (K / 16));
+      int m = -128;
+      for (int b = 0; b < K / 64; b++) m = max(m, max_i8x4(er[b]));
+      em_s[tid] = m;
+    }
+    __syncthreads();
+  }
   floatx16_t acc[NB];
 #pragma unroll
   for (int b = 0; b < NB; b++) acc[b] = floatx16_t{};
@@ -109,9 +129,14 @@ __device__ __forceinline__ void gemv_tile(const DecParams& p, const int32_t* sor
         *reinterpret_cast<uint4*>(xs + m * xw + 8 * c8) = bf16x8_to_half_interleaved(
             *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p.a) + (size_t)r * K +
                                             64 * base + 8 * c8));
-      else
+      else if constexpr (GATE_UP)
         *reinterpret_cast<uint4*>(xs + m * xw + 8 * c8) =
             *reinterpret_cast<const uint4*>(p.a + (size_t)r * K + 64 * base + 8 * c8);
+      else {
+        const uint4 v = *reinterpret_cast<const uint4*>(p.a + (size_t)r * K + 64 * base + 8 * c8);
+        const int d = p.hexp[(size_t)r * (K / 16) + (64 * base + 8 * c8) / 16] - em_s[m];
+        *reinterpret_cast<uint4*>(xs + m * xw + 8 * c8) = d ? scale_half8(v, d) : v;
+      }
     }
     __syncthreads();
     // 3. dequantise and multiply; MFMA rows past the tile are zero
@@ -126,11 +151,12 @@ __device__ __forceinline__ void gemv_tile(const DecParams& p, const int32_t* sor
                           : u32x4{0, 0, 0, 0};
 #pragma unroll
       for (int b = 0; b < NB; b++) {
-        half2_t s2, b2;
-        sb_pairs(sb[b][j], s2, b2);
+        const SbPair sp = sb_unpack(sb[b][j], GEN);
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-          const uint4 d = dequant_word(q[b][j][i], s2, b2);
+          uint4 d;
+          if constexpr (GEN) d = dequant_word_gen(q[b][j][i], sp.s2, sp.c2, sp.b2);
+          else d = dequant_word(q[b][j][i], sp.s2, sp.c2);
           acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
               __builtin_bit_cast(half8_t, x[i]), __builtin_bit_cast(half8_t, d), acc[b], 0, 0, 0);
         }
@@ -157,31 +183,55 @@ __device__ __forceinline__ void gemv_tile(const DecParams& p, const int32_t* sor
         v4[c] = v;
       }
       const int pair = sorted_pairs[row0 + m];
-      const float wgt = (pair >= 0 && pair < p.P) ? p.topk_weights[pair] : 0.0f;
+      const float wgt = (pair >= 0 && pair < p.P) ? ldexpf(p.topk_weights[pair] * us0, em_s[m]) : 0.0f;
       reinterpret_cast<uint3*>(p.out)[((size_t)(row0 + m) * p.N + blk * 32) / 4 + q] =
           pack24x4(wgt * v4[0], wgt * v4[1], wgt * v4[2], wgt * v4[3]);
     }
     return;
   }
+  if constexpr (GATE_UP) {
+    // h in fp32 per (row, column) into LDS (the activation stage is free),
+    // then stored as fp16 with one exponent per 16 columns (h_block_exp), in
+    // operand order (see the MFMA kernel)
+    float* hs = reinterpret_cast<float*>(dsm);
+    for (int t = tid; t < rows * 32; t += blockDim.x) {
+      const int m = t >> 5, cc = t & 31;
+      const int rr = m & 3, ll = cc + 32 * (m >> 2);
+      float v[NB];
+#pragma unroll
+      for (int b = 0; b < NB; b++) {
+        v[b] = red[((0 * NB + b) * 4 + rr) * 64 + ll];
+        for (int w2 = 1; w2 < nwaves; w2++) v[b] += red[((w2 * NB + b) * 4 + rr) * 64 + ll];
+      }
+      hs[t] = silu_mul(v[0] * us0, v[NB - 1] * us1);
+    }
+    __syncthreads();
+    bool any = false;
+    for (int t = tid; t < rows * 32; t += blockDim.x) {
+      const int m = t >> 5, cc = t & 31;
+      const float* blk16 = hs + (t & ~15);
+      float mx = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16; i++) mx = fmaxf(mx, fabsf(blk16[i]));
+      const int ex = h_block_exp(mx);
+      const int n = blk * 32 + cc;
+      reinterpret_cast<half_t*>(p.out)[(size_t)(row0 + m) * p.N + (n & ~7) + interleaved_pos(n & 7)] =
+          (half_t)ldexpf(hs[t], -ex);
+      if ((cc & 15) == 0) p.hexp[(size_t)(row0 + m) * (p.N / 16) + n / 16] = (int8_t)ex;
+      any |= ex != 0;
+    }
+    if (any && p.tflags) p.tflags[blockIdx.x / (p.N / 32)] = 1;
+    return;
+  }
   for (int t = tid; t < rows * 32; t += blockDim.x) {
     const int m = t >> 5, cc = t & 31;
     const int rr = m & 3, ll = cc + 32 * (m >> 2);
-    float v[NB];
-#pragma unroll
-    for (int b = 0; b < NB; b++) {
-      v[b] = red[((0 * NB + b) * 4 + rr) * 64 + ll];
-      for (int w2 = 1; w2 < nwaves; w2++) v[b] += red[((w2 * NB + b) * 4 + rr) * 64 + ll];
-    }
+    float v = red[(0 * 4 + rr) * 64 + ll];
+    for (int w2 = 1; w2 < nwaves; w2++) v += red[(w2 * 4 + rr) * 64 + ll];
     const int n = blk * 32 + cc;
-    if (GATE_UP) {
-      // h in operand order (see the MFMA kernel)
-      reinterpret_cast<half_t*>(p.out)[(size_t)(row0 + m) * p.N + (n & ~7) + interleaved_pos(n & 7)] =
-          (half_t)silu_mul(v[0], v[NB - 1]);
-    } else {
-      const int pair = sorted_pairs[row0 + m];
-      const float wgt = (pair >= 0 && pair < p.P) ? p.topk_weights[pair] : 0.0f;
-      reinterpret_cast<float*>(p.out)[(size_t)(row0 + m) * p.N + n] = wgt * v[0];
-    }
+    const int pair = sorted_pairs[row0 + m];
+    const float wgt = (pair >= 0 && pair < p.P) ? ldexpf(p.topk_weights[pair] * us0, em_s[m]) : 0.0f;
+    reinterpret_cast<float*>(p.out)[(size_t)(row0 + m) * p.N + n] = wgt * v;
   }
 }
 
@@ -251,7 +301,7 @@ __device__ __forceinline__ void g16_stage(const DecParams& p, const int32_t* sor
 
 // Dequantise this wave's fragments of one pass and multiply them with the
 // staged rows (zeros past the tile) into acc.
-template <int SPW>
+template <int SPW, bool GEN>
 __device__ __forceinline__ void g16_mma(const DecParams& p, const Frag16<SPW>& f, int rows, int base,
                                         floatx4_t (&acc)[2], const char* dsm) {
   const int lane = threadIdx.x & 63;
@@ -270,11 +320,11 @@ __device__ __forceinline__ void g16_mma(const DecParams& p, const Frag16<SPW>& f
                       : u32x4{0, 0, 0, 0};
 #pragma unroll
     for (int b = 0; b < 2; b++) {
-      half2_t s2, b2;
-      sb_pairs(f.sb[b][j], s2, b2);
+      const SbPair sp = sb_unpack(f.sb[b][j], GEN);
 #pragma unroll
       for (int m = 0; m < 2; m++) {
-        const uint4 d = dequant_word(m == 0 ? f.q[b][j].x : f.q[b][j].y, s2, b2);
+        const uint32_t w = m == 0 ? f.q[b][j].x : f.q[b][j].y;
+        const uint4 d = GEN ? dequant_word_gen(w, sp.s2, sp.c2, sp.b2) : dequant_word(w, sp.s2, sp.c2);
         acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, x[m]),
                                                         __builtin_bit_cast(half8_t, d), acc[b], 0, 0, 0);
       }
@@ -286,7 +336,7 @@ __device__ __forceinline__ void g16_mma(const DecParams& p, const Frag16<SPW>& f
 // at red_off and are added in wave order; h = silu(gate) * up in operand
 // order.  Ends with a barrier (the LDS is reused by the next item).
 __device__ __forceinline__ void g16_epilogue(const DecParams& p, const floatx4_t (&acc)[2], int row0,
-                                             int rows, int b16, char* dsm) {
+                                             int rows, int b16, char* dsm, float us0, float us1) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nwaves = blockDim.x >> 6;
@@ -297,6 +347,9 @@ __device__ __forceinline__ void g16_epilogue(const DecParams& p, const floatx4_t
 #pragma unroll
       for (int i = 0; i < 4; i++) red[((wave * 2 + b) * 4 + i) * 32 + lane] = acc[b][i];
   __syncthreads();
+  // h in fp32 per (row, column) into LDS (the activation stage is free), then
+  // stored as fp16 with the block's exponent (h_block_exp), operand order
+  float* hs = reinterpret_cast<float*>(dsm);
   for (int t = tid; t < rows * 16; t += blockDim.x) {
     const int m = t >> 4, cc = t & 15;
     const int rr = m & 3, ll = cc + 16 * (m >> 2);
@@ -306,9 +359,19 @@ __device__ __forceinline__ void g16_epilogue(const DecParams& p, const floatx4_t
       v[b] = red[(b * 4 + rr) * 32 + ll];
       for (int w2 = 1; w2 < nwaves; w2++) v[b] += red[((w2 * 2 + b) * 4 + rr) * 32 + ll];
     }
+    hs[t] = silu_mul(v[0] * us0, v[1] * us1);
+  }
+  __syncthreads();
+  for (int t = tid; t < rows * 16; t += blockDim.x) {
+    const int m = t >> 4, cc = t & 15;
+    float mx = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; i++) mx = fmaxf(mx, fabsf(hs[16 * m + i]));
+    const int ex = h_block_exp(mx);
     const int n = b16 * 16 + cc;
     reinterpret_cast<half_t*>(p.out)[(size_t)(row0 + m) * p.N + (n & ~7) + interleaved_pos(n & 7)] =
-        (half_t)silu_mul(v[0], v[1]);
+        (half_t)ldexpf(hs[t], -ex);
+    if (cc == 0) p.hexp[(size_t)(row0 + m) * (p.N / 16) + b16] = (int8_t)ex;
   }
   __syncthreads();
 }
@@ -327,15 +390,17 @@ template <int SPW>
 __device__ __forceinline__ void gemv_tile16(const DecParams& p, const int32_t* sorted_pairs, int e,
                                             int row0, int rows, int b16, char* dsm) {
   const int pass_slabs = (blockDim.x >> 6) * SPW;
+  const bool gen = (p.t0.general[e] | p.t1.general[e]) != 0;
   floatx4_t acc[2] = {floatx4_t{}, floatx4_t{}};
   for (int base = 0; base < p.K / 64; base += pass_slabs) {
     const Frag16<SPW> f = g16_load<SPW>(p, e, b16, base);
     g16_stage<SPW>(p, sorted_pairs, row0, rows, base, dsm);
     __syncthreads();
-    g16_mma<SPW>(p, f, rows, base, acc, dsm);
+    if (gen) g16_mma<SPW, true>(p, f, rows, base, acc, dsm);
+    else g16_mma<SPW, false>(p, f, rows, base, acc, dsm);
     __syncthreads();  // the next pass overwrites xs
   }
-  g16_epilogue(p, acc, row0, rows, b16, dsm);
+  g16_epilogue(p, acc, row0, rows, b16, dsm, p.t0.unscale[e], p.t1.unscale[e]);
 }
 
 // The grouped GEMM at decode sizes on a device block map: one workgroup per
@@ -353,7 +418,9 @@ __global__ __launch_bounds__(64 * kDecWavesMax) void w4_gemv_kernel(const DecPar
   // a malformed block map is skipped, never dereferenced out of bounds
   if (e < 0 || e >= p.E || rows <= 0 || rows > kGemvMaxTokens || row0 < 0 || row0 > p.P - rows)
     return;
-  gemv_tile<MODE, SPW, PACK, false>(p, p.sorted_pairs, e, row0, rows, blk, dsm);
+  const bool gen = (p.t0.general[e] | (MODE == MOE_GEMM_GATE_UP_SWIGLU ? p.t1.general[e] : 0u)) != 0;
+  if (gen) gemv_tile<MODE, SPW, PACK, false, true>(p, p.sorted_pairs, e, row0, rows, blk, dsm);
+  else gemv_tile<MODE, SPW, PACK, false, false>(p, p.sorted_pairs, e, row0, rows, blk, dsm);
 }
 
 struct DecRouteParams {
@@ -477,7 +544,7 @@ __global__ __launch_bounds__(64 * kDecWavesMax) void decode_gate_up_kernel(const
 #pragma unroll
     for (int half = 0; half < 2; half++) {
       const int tile = it / nb16, b16 = it % nb16;
-      const int row0 = blk_s[3 * tile + 1], rows = blk_s[3 * tile + 2];
+      const int e = blk_s[3 * tile], row0 = blk_s[3 * tile + 1], rows = blk_s[3 * tile + 2];
       const int nx = it + G;
       g16_stage<SPW>(p, sp_s, row0, rows, 0, dsm);
       // this item's fragments (issued an item ago) and x rows have landed;
@@ -489,9 +556,10 @@ __global__ __launch_bounds__(64 * kDecWavesMax) void decode_gate_up_kernel(const
       }
       __syncthreads();
       floatx4_t acc[2] = {floatx4_t{}, floatx4_t{}};
-      g16_mma<SPW>(p, half == 0 ? fa : fb, rows, 0, acc, dsm);
+      if ((p.t0.general[e] | p.t1.general[e]) != 0) g16_mma<SPW, true>(p, half == 0 ? fa : fb, rows, 0, acc, dsm);
+      else g16_mma<SPW, false>(p, half == 0 ? fa : fb, rows, 0, acc, dsm);
       __syncthreads();
-      g16_epilogue(p, acc, row0, rows, b16, dsm);
+      g16_epilogue(p, acc, row0, rows, b16, dsm, p.t0.unscale[e], p.t1.unscale[e]);
       it = nx;
       if (it >= items) break;
     }
@@ -524,7 +592,7 @@ __global__ __launch_bounds__(64 * kDecWavesMax) void decode_down_kernel(
     const DecParams p, const int32_t* __restrict__ ids, const int32_t* __restrict__ pair_slot,
     float* __restrict__ y, const uint16_t* __restrict__ residual, uint16_t* __restrict__ out) {
   extern __shared__ __attribute__((aligned(16))) char dsm[];
-  __shared__ int e_s[16], slot_s[16];
+  __shared__ int e_s[16], slot_s[16], gen_s[16], em_s[16];
   __shared__ float w_s[16], v_s[16 * 16];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -544,9 +612,21 @@ __global__ __launch_bounds__(64 * kDecWavesMax) void decode_down_kernel(
   if (tid < k) {
     const int pair = t * k + tid;
     const int e = ids[pair], slot = pair_slot[pair];
-    e_s[tid] = (e >= 0 && e < p.E) ? e : 0;
+    const int ec = (e >= 0 && e < p.E) ? e : 0;
+    e_s[tid] = ec;
     slot_s[tid] = (slot >= 0 && slot < p.P) ? slot : -1;
-    w_s[tid] = p.topk_weights[pair];
+    // the largest exponent of the slot's h row (its blocks are brought to it
+    // while staged); the routing weight times the expert's 2^-c and 2^that;
+    // the expert's dequantisation form
+    int em = 0;
+    if (slot >= 0 && slot < p.P) {
+      const uint32_t* er = reinterpret_cast<const uint32_t*>(p.hexp + (size_t)slot * (K / 16));
+      em = -128;
+      for (int b = 0; b < K / 64; b++) em = max(em, max_i8x4(er[b]));
+    }
+    em_s[tid] = em;
+    w_s[tid] = ldexpf(p.topk_weights[pair] * p.t0.unscale[ec], em);
+    gen_s[tid] = p.t0.general[ec] != 0;
   }
   __syncthreads();
   const int s = wave;  // this wave's slab (nwaves == S)
@@ -569,8 +649,9 @@ __global__ __launch_bounds__(64 * kDecWavesMax) void decode_down_kernel(
     for (int idx = tid; idx < nj * c8n; idx += blockDim.x) {
       const int m = idx / c8n, c8 = idx % c8n;
       const int slot = max(slot_s[j0 + m], 0);
-      *reinterpret_cast<uint4*>(xs + m * K + 8 * c8) =
-          *reinterpret_cast<const uint4*>(p.a + (size_t)slot * K + 8 * c8);
+      const uint4 v = *reinterpret_cast<const uint4*>(p.a + (size_t)slot * K + 8 * c8);
+      const int d = p.hexp[(size_t)slot * (K / 16) + c8 / 2] - em_s[j0 + m];
+      *reinterpret_cast<uint4*>(xs + m * K + 8 * c8) = d ? scale_half8(v, d) : v;
     }
     __syncthreads();
     // 3. per choice: dequantise, multiply, keep row 0
@@ -578,16 +659,21 @@ __global__ __launch_bounds__(64 * kDecWavesMax) void decode_down_kernel(
     for (int j = 0; j < kDownChunk; j++) {
       if (j >= nj) break;
       floatx4_t acc = floatx4_t{};
-      half2_t s2, b2;
-      sb_pairs(sb[j], s2, b2);
+      auto multiply = [&](auto gen_tag) {
+        constexpr bool GEN = decltype(gen_tag)::value;
+        const SbPair sp = sb_unpack(sb[j], GEN);
 #pragma unroll
-      for (int m = 0; m < 2; m++) {
-        const u32x4 x = c == 0 ? *reinterpret_cast<const u32x4*>(xs + j * K + 64 * s + 32 * khalf + 16 * qh + 8 * m)
-                               : u32x4{0, 0, 0, 0};
-        const uint4 d = dequant_word(m == 0 ? q[j].x : q[j].y, s2, b2);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, x),
-                                                     __builtin_bit_cast(half8_t, d), acc, 0, 0, 0);
-      }
+        for (int m = 0; m < 2; m++) {
+          const u32x4 x = c == 0 ? *reinterpret_cast<const u32x4*>(xs + j * K + 64 * s + 32 * khalf + 16 * qh + 8 * m)
+                                 : u32x4{0, 0, 0, 0};
+          const uint32_t w = m == 0 ? q[j].x : q[j].y;
+          const uint4 d = GEN ? dequant_word_gen(w, sp.s2, sp.c2, sp.b2) : dequant_word(w, sp.s2, sp.c2);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, x),
+                                                       __builtin_bit_cast(half8_t, d), acc, 0, 0, 0);
+        }
+      };
+      if (gen_s[j0 + j]) multiply(std::true_type{});
+      else multiply(std::false_type{});
       if (lane < 16) red[(wave * k + j0 + j) * 16 + lane] = acc[0];
     }
     __syncthreads();  // the next chunk overwrites xs
@@ -635,7 +721,8 @@ GemvShape gemv_shape(int K, int64_t grid) {
 DecParams dec_params(const GemmArgs& a, int64_t P, int64_t max_blocks, int xs_bytes) {
   const int log2_G = a.G == 32 ? 5 : a.G == 64 ? 6 : 7;  // G in {32, 64, 128}
   return DecParams{a.a, a.b0, a.b1, a.sorted_pairs, a.topk_weights, a.blocks, a.num_blocks, a.out,
-                   a.N, a.K, log2_G, a.top_k, a.E, (int)P, (int)max_blocks, xs_bytes};
+                   a.t0, a.t1, a.hexp, a.tflags, a.N, a.K, log2_G, a.top_k, a.E, (int)P, (int)max_blocks,
+                   xs_bytes};
 }
 
 }  // namespace

@@ -42,18 +42,19 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t mask, uint32_t m
 }
 
 // Dequantises one packed 32-bit word of eight 4-bit codes into eight fp16
-// weights q * scale + bias, in the interleaved order (q0,q4,q1,q5,q2,q6,q3,q7).
+// weights, in the interleaved order (q0,q4,q1,q5,q2,q6,q3,q7), for an
+// "exact" expert (see the (scale, bias) words below): the result is
+// q * s' + b' rounded once, s' and b' the expert's scale and bias times its
+// power of two 2^c.
 // The packed word is the row-major word rotated left by 5 bits, so code j
 // sits at bits (4j + 5) mod 32; a right rotation by 4k brings codes k and
 // k + 4 to bits 5..8 of the low and the high 16-bit half.  OR-ing them into
 // the mantissa of 32.0h (whose mantissa step is 1/32) gives 32 + q exactly,
-// and one fused multiply-add with the packed pair (scale, bias - 32 scale)
-// gives (32 + q) * scale + bias - 32 scale = q * scale + bias with a single
-// rounding.  bias - 32 scale is rounded to fp16 once, at pack time; with
-// bias = -8 * scale it is -40 * scale, exact (5 times an 8-bit scale fits in
-// 11 bits), and so is every weight ((q - 8) * scale needs at most 11
-// significant bits).  11 VALU instructions per word: 3 rotations, 4
-// v_and_or_b32, 4 v_pk_fma_f16.
+// and one fused multiply-add with the packed pair (s', b' - 32 s') gives
+// (32 + q) s' + b' - 32 s' = q s' + b' with a single rounding (b' - 32 s' is
+// an fp16 value exactly for such an expert; with bias = -8 scale it is
+// -40 s', and every weight (q - 8) s' is exact too).  11 VALU instructions
+// per word: 3 rotations, 4 v_and_or_b32, 4 v_pk_fma_f16.
 __device__ __forceinline__ uint4 dequant_word(uint32_t w, half2_t s2, half2_t b2) {
   const uint32_t mask = 0x01E001E0u, k32 = 0x50005000u;  // bits 5..8 of each half; 32.0h
   const half2_t v0 = __builtin_bit_cast(half2_t, and_or(w, mask, k32));  // q0, q4
@@ -66,13 +67,59 @@ __device__ __forceinline__ uint4 dequant_word(uint32_t w, half2_t s2, half2_t b2
                     __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(v3, s2, b2)));
 }
 
-// A packed (scale, bias) word -- fp16 scale in the low half, fp16
-// (bias - 32 scale) in the high half -- as the two broadcast pairs the
-// dequantisation takes.
+// The same for a "general" expert (b' - 32 s' not an fp16 value for some
+// group): t = (32 + q) s' - 32 s' = q s' with one rounding (-32 s' is exact),
+// then t + b' with a second.  n2 = (-32 s', -32 s').  15 VALU instructions
+// per word (4 more v_pk_add_f16).
+__device__ __forceinline__ uint4 dequant_word_gen(uint32_t w, half2_t s2, half2_t n2, half2_t b2) {
+  const uint32_t mask = 0x01E001E0u, k32 = 0x50005000u;
+  const half2_t v0 = __builtin_bit_cast(half2_t, and_or(w, mask, k32));
+  const half2_t v1 = __builtin_bit_cast(half2_t, and_or(__builtin_amdgcn_alignbit(w, w, 4), mask, k32));
+  const half2_t v2 = __builtin_bit_cast(half2_t, and_or(__builtin_amdgcn_alignbit(w, w, 8), mask, k32));
+  const half2_t v3 = __builtin_bit_cast(half2_t, and_or(__builtin_amdgcn_alignbit(w, w, 12), mask, k32));
+  return make_uint4(__builtin_bit_cast(uint32_t, __builtin_elementwise_fma(v0, s2, n2) + b2),
+                    __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(v1, s2, n2) + b2),
+                    __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(v2, s2, n2) + b2),
+                    __builtin_bit_cast(uint32_t, __builtin_elementwise_fma(v3, s2, n2) + b2));
+}
+
+// A packed (scale, bias) word -- fp16 s' in the low half, fp16 b' - 32 s'
+// (exact experts) or b' (general experts) in the high half -- as the two
+// broadcast pairs the exact dequantisation takes.
 __device__ __forceinline__ void sb_pairs(uint32_t sb, half2_t& s2, half2_t& b2) {
   const half2_t v = __builtin_bit_cast(half2_t, sb);
   s2 = half2_t{v[0], v[0]};
   b2 = half2_t{v[1], v[1]};
+}
+
+// Both forms behind one type, for the kernels that pick per expert at run
+// time: gen selects the general form; c2 = (b' - 32 s') pairs (exact) or
+// (-32 s') pairs (general).
+struct SbPair {
+  half2_t s2, c2, b2;
+  bool gen;
+};
+__device__ __forceinline__ SbPair sb_unpack(uint32_t sb, bool gen) {
+  SbPair r;
+  sb_pairs(sb, r.s2, r.b2);
+  r.gen = gen;
+  r.c2 = gen ? r.s2 * half2_t{(half_t)-32.0f, (half_t)-32.0f} : r.b2;
+  return r;
+}
+__device__ __forceinline__ uint4 dequant_word_any(uint32_t w, const SbPair& p) {
+  return p.gen ? dequant_word_gen(w, p.s2, p.c2, p.b2) : dequant_word(w, p.s2, p.c2);
+}
+
+// The tail of a packed (scale, bias) buffer: per expert the factor 2^-c
+// that undoes the expert's scaling, and whether it takes the general
+// dequantisation.
+struct BankTail {
+  const float* unscale;
+  const uint32_t* general;
+};
+__host__ __device__ __forceinline__ BankTail bank_tail(const moe_w4_packed& b, int E, int N, int K, int G) {
+  const uint32_t* t = b.sb + (size_t)E * N * (K / G);
+  return BankTail{reinterpret_cast<const float*>(t), t + E};
 }
 
 // Position of column j (0..7) of an 8-column run in the interleaved order.
@@ -193,6 +240,36 @@ __device__ __forceinline__ uint2 residual_add_bf16x4(uint2 r, float4 y) {
                     f32_to_bf16_rne(r2 + y.z) | (f32_to_bf16_rne(r3 + y.w) << 16));
 }
 
+// The hidden vector h leaves the gate/up kernels as fp16 values with a
+// power-of-two exponent per row and 16-column block: h = h16 * 2^e.  e is 0
+// unless the block's largest |h| (m) is at least 2^15 or below 2^-10 (and
+// not 0); then m * 2^-e lies in [2^14, 2^15), so no block overflows fp16 or
+// sinks into its subnormals, whatever the magnitudes of x and the weights.
+// Rows with a nonzero exponent mark their tile of the block map, so the
+// down kernels can keep the plain path for every other tile.
+__device__ __forceinline__ int h_block_exp(float m) {
+  if (m < 32768.0f && (m >= 0x1p-10f || m == 0.0f)) return 0;
+  if (m != m) return 0;          // NaN propagates unscaled
+  if (m > 3.0e38f) return 127;   // inf stays inf
+  int ex;
+  frexpf(m, &ex);                // m in [2^(ex-1), 2^ex)
+  return max(-128, min(127, ex - 15));
+}
+// The largest of the four signed bytes of w.
+__device__ __forceinline__ int max_i8x4(uint32_t w) {
+  return max(max((int)(int8_t)(w & 0xFF), (int)(int8_t)((w >> 8) & 0xFF)),
+             max((int)(int8_t)((w >> 16) & 0xFF), (int)(int8_t)(w >> 24)));
+}
+// Eight fp16 values (16 bytes) times 2^d, d <= 0 (d below -24 gives 0).
+__device__ __forceinline__ uint4 scale_half8(uint4 v, int d) {
+  const half_t f = (half_t)ldexpf(1.0f, max(d, -25));
+  const half2_t f2 = {f, f};
+  return make_uint4(__builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, v.x) * f2),
+                    __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, v.y) * f2),
+                    __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, v.z) * f2),
+                    __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, v.w) * f2));
+}
+
 // silu(g) * u = g / (1 + e^-g) * u, with the hardware exponential and
 // reciprocal (about 1 ulp each; the result is then rounded to fp16).
 __device__ __forceinline__ float silu_mul(float g, float u) {
@@ -225,14 +302,18 @@ hipError_t launch_chunk_hist(const int32_t* ids, int T, int k, int E, int32_t* c
                              hipStream_t s);
 // S2 (totals) - S5 from the per-chunk histograms; with chunk_start
 // ([chunks][E] first slots, computed by the caller) only the S4 scatter.
+// With tflags, also clears the gate/up kernel's per-tile flags [nflags].
 hipError_t launch_scan_scatter(const int32_t* ids, int T, int k, int E, const int32_t* chunk_hist,
                                int block_m, int32_t* counts, int32_t* offsets,
                                int32_t* sorted_pairs, int32_t* pair_slot, int32_t* blocks,
                                int32_t* num_blocks, hipStream_t s,
-                               const int32_t* chunk_start = nullptr);
+                               const int32_t* chunk_start = nullptr, int32_t* tflags = nullptr,
+                               int64_t nflags = 0);
 
 // x bf16 [T][H] -> fp16 [T][H] with every 8-chunk interleaved (see above).
-hipError_t launch_stage_x(const uint16_t* x, half_t* xh, int64_t n_elems, hipStream_t s);
+// Also clears tflags [nflags] (the per-tile flags the gate/up kernel sets).
+hipError_t launch_stage_x(const uint16_t* x, half_t* xh, int64_t n_elems, int32_t* tflags,
+                          int64_t nflags, hipStream_t s);
 
 // One-time repack of a row-major bank into the tile-major layout the GEMM
 // and GEMV kernels read (include/moe_w4.h, moe_w4_pack).
@@ -259,6 +340,12 @@ struct GemmArgs {
   bool pack24 = false;       // down: out is packed 24-bit [P][N] instead of fp32
   int64_t grid_tiles = -1;   // >= 0: exact tile count known on the host (grid sized to it)
   bool dense = false;        // banks hold expanded fp16 weights (moe_w4_expand layout), words only
+  BankTail t0{}, t1{};       // the tails of the packed (scale, bias) buffers of b0 and b1
+  // h's exponents int8 [P][I / 16] and per-tile flags int32 [max_blocks]
+  // (nonzero: a row of the tile has a nonzero exponent): written by gate/up,
+  // read by down
+  int8_t* hexp = nullptr;
+  int32_t* tflags = nullptr;
 };
 hipError_t launch_w4_mfma(const GemmArgs& a, hipStream_t s);
 hipError_t launch_w4_gemv(const GemmArgs& a, hipStream_t s);

@@ -72,6 +72,15 @@ def h_natural(h_stored: np.ndarray) -> np.ndarray:
     return h_stored[..., idx]
 
 
+def h_values(h16: np.ndarray, hexp: np.ndarray) -> np.ndarray:
+    """h in natural column order, fp64, from the library's fp16 values
+    (operand order) and their exponents per 16-column block:
+    h = h16 * 2^exp (include/moe_w4.h)."""
+    v = h_natural(np.asarray(h16).astype(np.float64))
+    e = np.repeat(np.asarray(hexp).astype(np.int64), 16, axis=-1)
+    return np.ldexp(v, e)
+
+
 def router_error_bound(x: torch.Tensor, wr: torch.Tensor) -> np.ndarray:
     """Forward error bound of an fp32 sum of H exact products in any order,
     gamma_H * sum_h |x_h Wr_eh| with gamma_H = H u / (1 - H u), u = 2^-24,

@@ -101,7 +101,7 @@ def gemm_args(**kw):
     bank = Packed(A, A)
     a = GemmArgs(mode=0, T=64, top_k=2, E=8, N=128, K=256, group_size=32, block_m=32, a=A,
                  bank0=bank, bank1=bank, sorted_pairs=A, topk_weights=A, blocks=A, num_blocks=A,
-                 out=A, workspace=A, workspace_bytes=1 << 30)
+                 out=A, workspace=A, workspace_bytes=1 << 30, h_exp=A, h_exp_bytes=1 << 30)
     for k, v in kw.items():
         setattr(a, k, v)
     return a
@@ -122,7 +122,15 @@ def test_gemm_validation(L):
     assert g(bank0=Packed(A + 8, A)) == ALIGN
     assert g(out=A + 2) == ALIGN
     assert g(workspace_bytes=10) == WS
+    assert g(h_exp=0) == NULL
+    assert g(h_exp=A + 4) == ALIGN
+    assert g(h_exp_bytes=10) == WS
+    assert g(mode=1, N=256, h_exp_bytes=10) == WS
     assert g(T=0) == OK
+    # h's exponents: P * I / 16 bytes padded to 16, then one int32 flag per tile
+    assert L.moe_w4_h_exp_bytes(64, 2, 8, 128, 32) == 1024 + 4 * (128 // 32 + 8)
+    assert L.moe_w4_h_exp_bytes(3, 2, 8, 128, 8) == 48 + 4 * (6 // 8 + 6)
+    assert L.moe_w4_h_exp_bytes(0, 2, 8, 128, 32) == 0
     assert L.moe_w4_grouped_gemm_workspace_bytes(ctypes.byref(gemm_args())) >= 64 * 256 * 2
     assert L.moe_w4_grouped_gemm_workspace_bytes(ctypes.byref(gemm_args(mode=1))) == 0
 
@@ -162,7 +170,9 @@ def test_ffn_timed_validation(L):
 
 def test_pack_queries_and_validation(L):
     assert L.moe_w4_packed_words_bytes(128, 512, 2048) == 128 * 512 * 2048 // 2
-    assert L.moe_w4_packed_sb_bytes(128, 512, 2048, 64) == 128 * 512 * 32 * 4
+    # the words, then the tail: 2^-c and the dequantisation form per expert, padded to 16 bytes
+    assert L.moe_w4_packed_sb_bytes(128, 512, 2048, 64) == 128 * 512 * 32 * 4 + 128 * 8
+    assert L.moe_w4_packed_sb_bytes(3, 128, 256, 32) == 3 * 128 * 8 * 4 + 32
     assert L.moe_w4_packed_words_bytes(8, 100, 256) == 0          # N % 128
     assert L.moe_w4_packed_words_bytes(8, 96, 256) == 0
     assert L.moe_w4_packed_sb_bytes(8, 128, 192, 64) == 0         # K % 128

@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_helpers import (assert_fp_close, assert_weights_close, cpu, f32_ulp, h_natural,
+from gpu_helpers import (assert_fp_close, assert_weights_close, cpu, f32_ulp, h_natural, h_values,
                          router_error_bound, say)
 from oracle_pins import check_blocks_invariants
 from quantized_moe_top_amd import api, synth
@@ -46,14 +46,52 @@ def compare_blocks(gpu: dict, ref: dict, tag: str):
 
 
 # -------------------------------------------------------------- weight pack --
-@pytest.mark.parametrize("E,N,K,G", [(3, 128, 256, 32), (2, 384, 384, 128), (4, 256, 128, 64)])
-def test_pack_layout(E, N, K, G):
+def packed_sb_reference(scales: torch.Tensor, biases: torch.Tensor, G: int) -> np.ndarray:
+    """The packed (scale, bias) words and tail of include/moe_w4.h, derived
+    with NumPy: per expert the power of two 2^c that puts the largest
+    |bias| + 32 |scale| in [2^13, 2^14); each word fp16(2^c s) | fp16(2^c b -
+    32 2^c s) << 16 when that offset is an fp16 value for every group of the
+    expert, else fp16(2^c s) | fp16(2^c b) << 16; tail float 2^-c [E], then
+    the general flags [E], padded to 16 bytes."""
+    E, N, gpr = scales.shape
+    s = scales.float().numpy().astype(np.float64)
+    b = biases.float().numpy().astype(np.float64)
+    words = np.empty((E, N, gpr), np.uint32)
+    unscale = np.empty(E, np.float32)
+    general = np.empty(E, np.uint32)
+    for e in range(E):
+        m = float(np.max(np.abs(b[e]) + 32.0 * np.abs(s[e])))
+        c = 0 if m == 0 else int(np.clip(14 - np.frexp(m)[1], -100, 100))
+        se, be = np.ldexp(s[e], c), np.ldexp(b[e], c)
+        off = be - 32.0 * se
+        exact = bool(np.all(off.astype(np.float16).astype(np.float64) == off))
+        hs = se.astype(np.float32).astype(np.float16).view(np.uint16).astype(np.uint32)
+        hi = (off if exact else be).astype(np.float32).astype(np.float16).view(np.uint16).astype(np.uint32)
+        words[e] = hs | (hi << 16)
+        unscale[e] = np.float32(np.ldexp(1.0, -c))
+        general[e] = 0 if exact else 1
+    body = words.reshape(E, N // 128, 128, gpr).transpose(0, 1, 3, 2).reshape(-1)
+    tail = np.concatenate([unscale.view(np.uint32), general])
+    pad = (-len(tail)) % 4
+    return np.concatenate([body, tail, np.zeros(pad, np.uint32)])
+
+
+@pytest.mark.parametrize("E,N,K,G,bias", [(3, 128, 256, 32, "free"), (2, 384, 384, 128, "free"),
+                                          (4, 256, 128, 64, "m8"), (3, 128, 256, 64, "mixed")])
+def test_pack_layout(E, N, K, G, bias):
     """moe_w4_pack against the packed layout's definition (include/moe_w4.h),
-    rearranged independently with NumPy."""
+    rearranged independently with NumPy: codes, (scale, bias) words, each
+    expert's power of two and dequantisation form."""
     g = torch.Generator().manual_seed(E * 1000 + N + K + G)
+    scales = (torch.randn((E, N, K // G), generator=g) * 0.01).to(torch.bfloat16)
+    if bias == "m8":
+        biases = (-8.0 * scales.float()).to(torch.bfloat16)
+    else:
+        biases = torch.randn((E, N, K // G), generator=g).to(torch.bfloat16)
+        if bias == "mixed":  # expert 0 exact (bias = -8 scale), the others general
+            biases[0] = (-8.0 * scales[0].float()).to(torch.bfloat16)
     bank = synth.W4Bank(torch.randint(-2**31, 2**31 - 1, (E, N, K // 8), generator=g, dtype=torch.int64).to(torch.int32),
-                        torch.randn((E, N, K // G), generator=g).to(torch.bfloat16),
-                        torch.randn((E, N, K // G), generator=g).to(torch.bfloat16))
+                        scales, biases)
     pb = api.pack_bank(bank.to(DEV), G)
     torch.cuda.synchronize()
     q = bank.qweight.numpy().view(np.uint32)
@@ -62,13 +100,15 @@ def test_pack_layout(E, N, K, G):
     want = q.reshape(E, N // 128, 4, 32, K // 64, 2, 4).transpose(0, 1, 4, 2, 3, 5, 6).reshape(-1)
     want = (want << np.uint32(5)) | (want >> np.uint32(27))  # each word rotated left by 5 bits
     assert np.array_equal(cpu(pb.words).view(np.uint32), want)
-    # (scale, bias - 32 scale) as fp16, rounded to nearest from the fp32 values of the bf16 inputs
-    s32 = bank.scales.float().numpy()
-    b32 = bank.biases.float().numpy()
-    hs = s32.astype(np.float16).view(np.uint16).astype(np.uint32)
-    hb = (b32 - np.float32(32.0) * s32).astype(np.float16).view(np.uint16).astype(np.uint32)
-    sbw = (hs | (hb << 16)).reshape(E, N // 128, 128, K // G).transpose(0, 1, 3, 2).reshape(-1)
-    assert np.array_equal(cpu(pb.sb).view(np.uint32), sbw)
+    ref = packed_sb_reference(scales, biases, G)
+    got = cpu(pb.sb).view(np.uint32)
+    assert got.shape == ref.shape
+    assert np.array_equal(got, ref)
+    tail = ref[E * N * (K // G):]
+    if bias == "m8":
+        assert np.all(tail[E:2 * E] == 0)  # every expert exact
+    if bias == "mixed":
+        assert tail[E] == 0 and np.all(tail[E + 1:2 * E] == 1)
 
 
 # ------------------------------------------------------------------ routing --
@@ -191,6 +231,19 @@ GEMM_CASES = {
     "ragged_t77_g32": lambda: synth.make_custom(T=77, H=512, I=384, E=8, k=2, G=32, seed=23),
     "gemv_t5_g32": lambda: synth.make_custom(T=5, H=768, I=384, E=16, k=4, G=32, seed=24),
     "mfma_t9": lambda: synth.make_custom(T=9, H=512, I=256, E=4, k=2, G=64, seed=25),
+    # general affine weights (the general dequantisation): zero points m ~ U(2, 14), free biases
+    "zeropoint_t300_g64": lambda: synth.make_custom(T=300, H=512, I=256, E=16, k=4, G=64, seed=26,
+                                                    bias="zeropoint"),
+    "free_t100_g128": lambda: synth.make_custom(T=100, H=1024, I=256, E=32, k=6, G=128, seed=27,
+                                                bias="free"),
+    "zeropoint_gemv_t5_g32": lambda: synth.make_custom(T=5, H=768, I=384, E=16, k=4, G=32, seed=28,
+                                                       bias="zeropoint"),
+    # |h| past the fp16 range on the x30 rows (scaled h blocks, the down
+    # kernels' scaled path), and h far below fp16's normal range
+    "large_h_t300": lambda: synth.make_custom(T=300, H=512, I=256, E=16, k=4, G=64, seed=29,
+                                              scale=(0.1, 0.4), heavy_frac=0.05, heavy_mul=30.0),
+    "tiny_h_gemv_t5": lambda: synth.make_custom(T=5, H=768, I=384, E=16, k=4, G=32, seed=30,
+                                                scale=(5e-6, 2e-5)),
 }
 
 
@@ -211,16 +264,17 @@ def test_grouped_gemms(orc, name):
         say(f"  {name}: block_m {BM}")
         bb = api.build_blocks(ids, lay.E, BM)
         kw = dict(T=lay.T, top_k=lay.k, E=lay.E, group_size=lay.G, block_m=BM)
-        h = api.w4_grouped_gemm(api.MOE_GEMM_GATE_UP_SWIGLU, d.x, d.gate, d.up, bb["sorted_pairs"],
-                                bb["blocks"], bb["num_blocks"], **kw)
+        h, hx = api.w4_grouped_gemm(api.MOE_GEMM_GATE_UP_SWIGLU, d.x, d.gate, d.up, bb["sorted_pairs"],
+                                    bb["blocks"], bb["num_blocks"], **kw)
         ys = api.w4_grouped_gemm(api.MOE_GEMM_DOWN, h, d.down, None, bb["sorted_pairs"],
-                                 bb["blocks"], bb["num_blocks"], topk_weights=w.reshape(-1), **kw)
+                                 bb["blocks"], bb["num_blocks"], topk_weights=w.reshape(-1), h_exp=hx, **kw)
         torch.cuda.synchronize()
         sp = cpu(bb["sorted_pairs"])
         tokens = (sp // lay.k).astype(np.int32)
         experts = rid.reshape(-1)[sp].astype(np.int32)
         h_ref = orc.expert_hidden(lay.x, tokens, experts, lay.gate, lay.up, lay.G)
-        h_gpu = h_natural(cpu(h).astype(np.float64))
+        P = lay.T * lay.k
+        h_gpu = h_values(cpu(h), cpu(hx)[:P * (lay.I // 16)].view(np.int8).reshape(P, lay.I // 16))
         assert_fp_close(h_gpu, h_ref, f"{name} BM={BM} h")
         # down projection fed with the device's own h (isolates S7)
         o_ref = orc.expert_down(h_gpu, experts, lay.down, lay.G) * rw.reshape(-1)[sp][:, None]
@@ -318,6 +372,60 @@ def test_ffn_forward_longctx_t32768(orc, layer_index):
     share_h = len(heavy) / lay.T
     layer_output_check(orc, lay, y, info, tokens=np.concatenate([heavy, tn]),
                        strata=[(heavy, share_h), (tn, 1 - share_h)])
+
+
+# ------------------------------------------------- general affine weights ---
+# Banks whose bias is not -8 * scale: zero points m ~ U(2, 14) per group
+# (bias = -m * scale) or biases drawn independently of the scale, at the
+# prefill workload's shape, at group sizes 32 and 128, at decode sizes, and
+# with x30 rows.  The library takes the general dequantisation for them.
+GENERAL_CASES = {
+    "prefill_t512_zeropoint": dict(T=512, H=2048, I=512, E=128, k=8, G=64, seed=101, router="weight",
+                                   bias="zeropoint"),
+    "g32_zeropoint": dict(T=300, H=512, I=256, E=16, k=4, G=32, seed=102, bias="zeropoint"),
+    "g128_free": dict(T=100, H=1024, I=256, E=32, k=6, G=128, seed=103, bias="free"),
+    "g32_free_t77": dict(T=77, H=512, I=384, E=8, k=2, G=32, seed=104, bias="free"),
+    "decode_t1_zeropoint": dict(T=1, H=2048, I=512, E=128, k=8, G=64, seed=105, bias="zeropoint"),
+    "decode_t8_free_g128": dict(T=8, H=1024, I=256, E=32, k=4, G=128, seed=106, bias="free"),
+    "zeropoint_t2000": dict(T=2000, H=2048, I=512, E=32, k=4, G=64, seed=107, router="weight",
+                            bias="zeropoint"),
+}
+
+
+@pytest.mark.parametrize("case", list(GENERAL_CASES))
+def test_ffn_general_bias(orc, case):
+    lay = synth.make_custom(**GENERAL_CASES[case])
+    y, info = api.ffn_forward(on_dev(lay), info=True)
+    torch.cuda.synchronize()
+    layer_output_check(orc, lay, y, info)
+
+
+# --------------------------------------------------- ranges of h and weights --
+# Scales far from the workloads' (2e-3 .. 1e-2): tiny ones put h far below
+# fp16's normal range, large ones with x30 rows put |h| far beyond 65504
+# (up to about 1e9 here); the packed weights are rescaled per expert and h
+# carries exponents per 16 columns, so both stay within the bar, on the
+# MFMA path (T = 300, 512) and at decode sizes (T = 1, 8).
+RANGE_CASES = {
+    "tiny_scales_t300": dict(T=300, H=512, I=256, E=16, k=4, G=64, seed=111, scale=(5e-6, 2e-5)),
+    "tiny_scales_decode_t1": dict(T=1, H=2048, I=512, E=128, k=8, G=64, seed=112, scale=(5e-6, 2e-5)),
+    "large_h_t512": dict(T=512, H=2048, I=512, E=128, k=8, G=64, seed=113, router="weight",
+                         scale=(0.1, 0.4), heavy_frac=0.01, heavy_mul=30.0),
+    "large_h_decode_t8": dict(T=8, H=2048, I=512, E=128, k=8, G=64, seed=114, scale=(0.1, 0.4),
+                              heavy_frac=0.25, heavy_mul=30.0),
+    "huge_scales_t300": dict(T=300, H=512, I=256, E=16, k=4, G=32, seed=115, scale=(200.0, 800.0),
+                             bias="zeropoint"),
+}
+
+
+@pytest.mark.parametrize("case", list(RANGE_CASES))
+def test_ffn_scale_range(orc, case):
+    lay = synth.make_custom(**RANGE_CASES[case])
+    y, info = api.ffn_forward(on_dev(lay), info=True)
+    torch.cuda.synchronize()
+    hx = cpu(info["h_exp"])
+    say(f"  {case}: h exponents in [{hx.min()}, {hx.max()}], {np.mean(hx != 0) * 100:.1f}% nonzero")
+    layer_output_check(orc, lay, y, info)
 
 
 # ------------------------------------------------------------ edge cases ---
@@ -580,12 +688,15 @@ def test_ffn_host_blockmap_identical(case):
     assert torch.equal(y1, y2)
 
 
-@pytest.mark.parametrize("case", ["prefill_t512", "ragged_g32", "imbalanced_t8192"])
+@pytest.mark.parametrize("case", ["prefill_t512", "ragged_g32", "imbalanced_t8192", "ragged_zeropoint"])
 def test_ffn_unfused_identical(case):
     """The unfused ablation multiplies the same fp16 weights (expanded to
-    HBM first) in the same order: output bit-identical to the fused layer."""
+    HBM first, in the expert's exact or general form) in the same order:
+    output bit-identical to the fused layer."""
     if case == "ragged_g32":
         lay = synth.make_custom(T=333, H=512, I=256, E=16, k=2, G=32, seed=62)
+    elif case == "ragged_zeropoint":
+        lay = synth.make_custom(T=333, H=512, I=256, E=16, k=2, G=64, seed=63, bias="zeropoint")
     else:
         lay = synth.make_layer(case)
     lay = api.pack_layer(on_dev(lay))
