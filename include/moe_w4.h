@@ -404,6 +404,27 @@ int moe_ffn_forward_unfused(const moe_layer* layer, const uint16_t* x, const flo
                             size_t workspace_bytes, void* expanded, size_t expanded_bytes,
                             void* stream);
 
+/* --------------------------------------------- no-allocation variant --
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * layer as moe_ffn_forward (same kernels, same results, bit for bit), with
+ * its workspace in a fixed device area of the library instead of a caller's
+ * buffer.  The area is moe_ffn_noalloc_max_bytes() (40 MiB) per GPU, held
+ * by the library from the first call on that GPU until the process ends; a
+ * layer whose workspace (moe_ffn_workspace_bytes) is larger returns
+ * MOE_ERR_UNSUPPORTED before anything is enqueued.  Nothing in it needs to
+ * start cleared: every piece the layer reads is written earlier in the same
+ * call.  The call allocates nothing; its first call on a GPU looks up the
+ * area's device address (hipGetSymbolAddress) and fails with MOE_ERR_HIP if
+ * that fails.  Every call on one GPU shares the one area: calls that overlap
+ * on a GPU (on different streams, or from different threads without ordering)
+ * race and give undefined results, and the device pointers `info` receives
+ * stay valid only until the next call on that GPU.  Arguments and errors
+ * otherwise as moe_ffn_forward. */
+size_t moe_ffn_noalloc_max_bytes(void);
+int moe_ffn_forward_noalloc(const moe_layer* layer, const uint16_t* x, const float* router_logits,
+                            float* y, moe_route_info* info, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -404,3 +404,25 @@ def _info_views(ri: RouteInfo, ws: torch.Tensor, layer, T: int, logits) -> dict:
     out["logits"] = (view(ri.logits, T * layer.E, torch.float32, (T, layer.E))
                      if layer.router_weight is not None else logits)
     return out
+
+
+def ffn_forward_noalloc(layer, x: Optional[torch.Tensor] = None, logits: Optional[torch.Tensor] = None,
+                        y: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """``moe_ffn_forward_noalloc``: the layer with the library's fixed
+    scratch area as its workspace (no workspace argument; the layer's
+    workspace must fit ``moe_ffn_noalloc_max_bytes``).  Returns y fp32
+    [T, H]."""
+    if not isinstance(layer, PackedLayer):
+        layer = pack_layer(layer)
+    x = layer.x if x is None else x
+    T, H = x.shape
+    if layer.router_weight is None and logits is None:
+        logits = layer.logits
+    if y is None:
+        y = torch.empty((T, H), dtype=torch.float32, device=x.device)
+    lay = make_layer_struct(layer, T)
+    _lib.check(_L().moe_ffn_forward_noalloc(
+        ctypes.byref(lay), _dev(x, "x", torch.bfloat16),
+        _dev(logits, "logits", torch.float32) if layer.router_weight is None else 0,
+        _dev(y, "y", torch.float32), None, _stream()), "moe_ffn_forward_noalloc")
+    return y

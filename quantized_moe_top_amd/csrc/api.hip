@@ -7,6 +7,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "internal.h"
 
 namespace {
@@ -629,6 +631,68 @@ int moe_ffn_forward_timed(const moe_layer* layer, const uint16_t* x, const float
   if (!stage_events) return fail(MOE_ERR_NULL, "stage_events is NULL");
   return ffn_forward_impl(layer, x, router_logits, y, info, workspace, workspace_bytes,
                           stage_events, (hipStream_t)stream);
+}
+
+}  // extern "C"
+
+// ------------------------------------------------- no-allocation variant --
+// moe_ffn_forward_noalloc runs the layer with its workspace in this fixed
+// device array instead of a caller's buffer.  Each GPU the library runs on
+// holds its own copy until the process ends.  In host code `scratch` names a
+// host-side stand-in, not device memory: kernels get the device address
+// hipGetSymbolAddress reports for the current device, looked up once per
+// device on its first call.
+namespace {
+
+constexpr size_t kScratchBytes = (size_t)40 << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// The current device's address of `scratch` (looked up on the device's
+// first call, with that device current).
+int scratch_address(void** out) {
+  int dev = -1;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess) return hip_status(err, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(MOE_ERR_UNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess) return hip_status(err, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(MOE_ERR_HIP, "hipGetSymbolAddress(scratch) gave NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_ffn_noalloc_max_bytes(void) { return kScratchBytes; }
+
+int moe_ffn_forward_noalloc(const moe_layer* layer, const uint16_t* x, const float* router_logits,
+                            float* y, moe_route_info* info, void* stream) {
+  if (!layer) return fail(MOE_ERR_NULL, "layer is NULL");
+  int st = check_dims(&layer->dims);
+  if (st) return st;
+  const size_t need = ffn_layout(layer->dims, layer->router_weight != nullptr,
+                                 moe_ffn_block_m(&layer->dims)).total;
+  if (need > kScratchBytes)
+    return fail(MOE_ERR_UNSUPPORTED,
+                "this layer needs %zu bytes of scratch, more than the fixed %zu (use moe_ffn_forward "
+                "with a workspace)", need, kScratchBytes);
+  if (layer->dims.T == 0) return ffn_forward_impl(layer, x, router_logits, y, info, nullptr, 0, nullptr,
+                                                  (hipStream_t)stream);
+  void* ptr = nullptr;
+  if ((st = scratch_address(&ptr))) return st;
+  return ffn_forward_impl(layer, x, router_logits, y, info, ptr, kScratchBytes, nullptr,
+                          (hipStream_t)stream);
 }
 
 }  // extern "C"

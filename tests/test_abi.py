@@ -230,3 +230,15 @@ def test_decode_attention_validation(L):
     assert att(wsb=8) == WS
     assert att(B=0) == OK                           # nothing enqueued
     assert L.moe_decode_attention_workspace_bytes(1, 32, 4, 32768) >= 32 * 130 * 4
+
+
+def test_noalloc_validation(L):
+    """The fixed scratch area's size, and refusals before any device work:
+    no layer, a layer whose workspace exceeds the area, T = 0."""
+    assert L.moe_ffn_noalloc_max_bytes() == 40 << 20
+    assert L.moe_ffn_forward_noalloc(None, A, A, A, None, None) == NULL
+    bank = Packed(A, A)
+    big = Layer(Dims(4096, 2048, 512, 16, 8, 64), 0, bank, bank, bank)
+    assert L.moe_ffn_forward_noalloc(ctypes.byref(big), A, A, A, None, None) == UNSUP
+    empty = Layer(Dims(0, 2048, 512, 16, 8, 64), 0, bank, bank, bank)
+    assert L.moe_ffn_forward_noalloc(ctypes.byref(empty), 0, 0, 0, None, None) == OK
