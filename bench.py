@@ -90,15 +90,17 @@ def algorithmic(lay, touched: int) -> dict:
     T, H, I, E, k = lay.T, lay.H, lay.I, lay.E, lay.k
     P = T * k
     eb = expert_bytes(lay)
-    yb = 4 if T <= 8 else 3  # weighted expert outputs: fp32 (GEMV path) or packed 24-bit
+    # weighted expert outputs: fp32 (GEMV path), or int16 mantissas with an
+    # exponent byte per 16 values
+    yb = 4 if T <= 8 else 2 + 1 / 16
     return {
         # x (fp16 operand copy) read + touched experts' gate and up banks + h fp16 written
         "gate_up": dict(bytes=touched * eb["gate_up"] + T * H * 2 + P * I * 2,
                         flops=4 * P * H * I),
         # h read + touched experts' down bank + weighted y_sorted written
-        "down": dict(bytes=touched * eb["down"] + P * I * 2 + P * H * yb, flops=2 * P * H * I),
+        "down": dict(bytes=touched * eb["down"] + P * I * 2 + int(P * H * yb), flops=2 * P * H * I),
         # y_sorted read + pair_slot read + y written
-        "combine": dict(bytes=P * H * yb + P * 4 + T * H * 4, flops=P * H),
+        "combine": dict(bytes=int(P * H * yb) + P * 4 + T * H * 4, flops=P * H),
         # x bf16 read + fp16 copy written, logits (or router weight) read,
         # ids / weights written
         "route": dict(bytes=T * H * 2 * 2 + (E * H * 2 + T * E * 4 if lay.router_weight is not None

@@ -255,13 +255,16 @@ typedef struct {
   const int32_t* num_blocks;    /* [1] */
   const uint16_t* h;            /* h16 fp16 [P][I], slot order, operand order */
   const uint8_t* y_sorted;      /* [P][H] weighted, slot order, y_sorted_bytes
-                                   per value: 4 = fp32 (path 1); 3 = packed
-                                   24-bit (path 0): little-endian, the top 3
-                                   bytes of the fp32 pattern rounded to nearest,
-                                   ties away from zero (relative error
-                                   <= 2^-16) */
+                                   per value: 4 = fp32 (path 1); 2 = int16
+                                   mantissas q (path 0), value = q * 2^E with E
+                                   = y_sorted_exp[s][n / 16]: block floating
+                                   point, each block's largest |value| in
+                                   [2^14, 2^15) * 2^E (relative error <= 2^-16
+                                   for it, absolute <= 2^(E-1) for every value;
+                                   E = -128 for an all-zero block) */
   int32_t y_sorted_bytes;
   const int8_t* h_exp;          /* [P][I / 16]: h = h16 * 2^h_exp (see S6 above) */
+  const int8_t* y_sorted_exp;   /* [P][H / 16] on path 0, NULL on path 1 */
 } moe_route_info;
 
 /* Tile rows moe_ffn_forward uses for these sizes (host-only). */

@@ -75,7 +75,7 @@ class RouteInfo(ctypes.Structure):
     _fields_ = [("block_m", c_i32), ("path", c_i32), ("logits", c_p), ("topk_ids", c_p),
                 ("topk_weights", c_p), ("counts", c_p), ("offsets", c_p), ("sorted_pairs", c_p),
                 ("pair_slot", c_p), ("blocks", c_p), ("num_blocks", c_p), ("h", c_p),
-                ("y_sorted", c_p), ("y_sorted_bytes", c_i32), ("h_exp", c_p)]
+                ("y_sorted", c_p), ("y_sorted_bytes", c_i32), ("h_exp", c_p), ("y_sorted_exp", c_p)]
 
 
 class MoEError(RuntimeError):

@@ -238,13 +238,12 @@ def stage_events(n: int = _lib.MOE_NUM_STAGES + 1):
     return evs
 
 
-def unpack_y24(packed: torch.Tensor) -> torch.Tensor:
-    """fp32 values of a packed 24-bit tensor [..., 3 n] (the layer's weighted
-    expert outputs in ``info["y_sorted"]``): value i is bytes 3i .. 3i + 2,
-    little-endian, as the top 3 bytes of its fp32 pattern."""
-    b = packed.to(torch.int64).reshape(*packed.shape[:-1], -1, 3)
-    bits = (b[..., 0] << 8) | (b[..., 1] << 16) | (b[..., 2] << 24)
-    return bits.to(torch.int32).view(torch.float32)
+def unpack_y16e(mant: torch.Tensor, exp: torch.Tensor) -> torch.Tensor:
+    """fp32 values of the layer's weighted expert outputs in block floating
+    point (``info["y_sorted"]`` int16 [P, H] and ``info["y_sorted_exp"]`` int8
+    [P, H / 16]): value = mantissa * 2^exponent of its 16-value block."""
+    e = exp.to(torch.int32).repeat_interleave(16, dim=-1)
+    return torch.ldexp(mant.to(torch.float32), e)
 
 
 def unfused_bytes(layer, T: Optional[int] = None) -> int:
@@ -396,10 +395,12 @@ def _info_views(ri: RouteInfo, ws: torch.Tensor, layer, T: int, logits) -> dict:
         h=view(ri.h, P * layer.I, torch.float16, (P, layer.I)),
         # h = h * 2^h_exp per 16-column block
         h_exp=view(ri.h_exp, P * (layer.I // 16), torch.int8, (P, layer.I // 16)),
-        # fp32, or packed 24-bit (3 bytes a value, unpack_y24 gives fp32)
+        # fp32, or int16 mantissas with y_sorted_exp (unpack_y16e gives fp32)
         y_sorted=(view(ri.y_sorted, P * layer.H, torch.float32, (P, layer.H))
                   if ri.y_sorted_bytes == 4 else
-                  view(ri.y_sorted, P * layer.H * 3, torch.uint8, (P, layer.H * 3))),
+                  view(ri.y_sorted, P * layer.H, torch.int16, (P, layer.H))),
+        y_sorted_exp=(view(ri.y_sorted_exp, P * (layer.H // 16), torch.int8, (P, layer.H // 16))
+                      if ri.y_sorted_exp else None),
     )
     out["logits"] = (view(ri.logits, T * layer.E, torch.float32, (T, layer.E))
                      if layer.router_weight is not None else logits)

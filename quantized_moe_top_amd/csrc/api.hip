@@ -90,7 +90,7 @@ size_t hexp_bytes(int64_t T, int k, int E, int64_t I, int block_m) {
 // Workspace layout of moe_ffn_forward.
 struct FfnLayout {
   size_t logits, logits_part, ids, w, counts, offsets, sorted_pairs, pair_slot, blocks,
-      num_blocks, scratch, xh, h, hexp, tflags, y_sorted, total;
+      num_blocks, scratch, xh, h, hexp, tflags, y_sorted, yexp, total;
   int router_ks;  // ranges of H the router sums separately (1: no partial sums)
 };
 
@@ -119,10 +119,16 @@ FfnLayout ffn_layout(const moe_dims& d, bool has_router, int block_m) {
   L.h = take(P * I * 2);
   L.hexp = take(P * (I / 16));                                          // h's exponents
   L.tflags = take((size_t)max_blocks((int64_t)P, d.E, block_m) * 4);  // per-tile flags
-  L.y_sorted = take(P * H * (d.T <= moe::kGemvMaxTokens ? 4 : 3));  // fp32 or packed 24-bit
+  // weighted expert outputs: fp32 (decode path), or int16 mantissas with an
+  // exponent per 16 values (MFMA path)
+  const bool gemv = d.T <= moe::kGemvMaxTokens;
+  L.y_sorted = take(P * H * (gemv ? 4 : 2));
+  L.yexp = take(gemv ? 0 : P * (H / 16));
   L.total = o;
   return L;
 }
+
+bool gemv_path(const moe_dims& d) { return d.T <= moe::kGemvMaxTokens; }
 
 int check_dims(const moe_dims* d) {
   if (!d) return fail(MOE_ERR_NULL, "dims is NULL");
@@ -384,7 +390,8 @@ int ffn_forward_impl(const moe_layer* layer, const uint16_t* x, const float* rou
   const int block_m = moe_ffn_block_m(&d);
   if (d.T == 0) {  // empty tensors may carry NULL data pointers
     if (info) *info = moe_route_info{block_m, 1, router_logits, nullptr, nullptr, nullptr, nullptr,
-                                     nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 4, nullptr};
+                                     nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 4, nullptr,
+                                     nullptr};
     return ok();
   }
   if (has_router == (router_logits != nullptr))
@@ -434,13 +441,14 @@ int ffn_forward_impl(const moe_layer* layer, const uint16_t* x, const float* rou
   moe::half_t* h = (moe::half_t*)(ws + L.h);
   uint8_t* y_sorted = (uint8_t*)(ws + L.y_sorted);
   int8_t* hexp = (int8_t*)(ws + L.hexp);
+  int8_t* yexp = gemv_path(d) ? nullptr : (int8_t*)(ws + L.yexp);
   int32_t* tflags = (int32_t*)(ws + L.tflags);
   const int64_t nflags = max_blocks((int64_t)d.T * d.top_k, d.E, block_m);
   const bool gemv = d.T <= moe::kGemvMaxTokens;
   if (info) {
     *info = moe_route_info{block_m, gemv ? 1 : 0, logits, ids, w, counts, offsets, sorted_pairs,
                            pair_slot, blocks, num_blocks, (const uint16_t*)h, y_sorted,
-                           gemv ? 4 : 3, hexp};
+                           gemv ? 4 : 2, hexp, yexp};
   }
 
   hipError_t err;
@@ -486,6 +494,7 @@ int ffn_forward_impl(const moe_layer* layer, const uint16_t* x, const float* rou
                    h, layer->down, layer->down, sorted_pairs, w, blocks, num_blocks, y_sorted,
                    !gemv, grid_tiles};
   g1.hexp = g2.hexp = hexp;
+  g2.yexp = yexp;
   g1.tflags = g2.tflags = tflags;
   g1.t0 = moe::bank_tail(layer->gate, d.E, d.I, d.H, d.group_size);
   g1.t1 = moe::bank_tail(layer->up, d.E, d.I, d.H, d.group_size);
@@ -523,7 +532,7 @@ int ffn_forward_impl(const moe_layer* layer, const uint16_t* x, const float* rou
     err = gemv ? moe::launch_w4_gemv(g2, s) : moe::launch_w4_mfma(g2, s);
     if (err != hipSuccess) return hip_status(err, "down");
     if ((err = mark(events, MOE_STAGE_COMBINE, s)) != hipSuccess) return hip_status(err, "event");
-    if ((err = moe::launch_combine(y_sorted, !gemv, pair_slot, y, d.T, d.H, d.top_k, s, residual, out)) !=
+    if ((err = moe::launch_combine(y_sorted, yexp, pair_slot, y, d.T, d.H, d.top_k, s, residual, out)) !=
         hipSuccess)
       return hip_status(err, "combine");
   }

@@ -57,6 +57,7 @@ struct MfmaParams {
   BankTail t0, t1;  // per-expert 2^-c and dequantisation form of b0 / b1
   int8_t* hexp;     // h's exponents [P][I / 16]: written by S6, read by S7
   int32_t* tflags;  // per tile: a row of it has a nonzero exponent
+  int8_t* yexp;     // S7 with PACK: y16e exponents [P][N / 16]
   int N, K, log2_G, top_k, E, P, max_blocks;
 };
 
@@ -68,7 +69,8 @@ struct MfmaParams {
 // (scale, bias) words; for G >= 64 one word serves both and is copied once.
 // STAGES: depth of the LDS ring (STAGES - 1 slabs in flight); WGS_PER_CU:
 // workgroups meant to share a CU (register budget).
-// PACK (S7 only): out is packed 24-bit instead of fp32.
+// PACK (S7 only): out is y16e block floating point (int16 mantissas, exponents
+// at yexp) instead of fp32.
 // DENSE (the unfused ablation): the banks hold weights already expanded to
 // fp16 in operand order (moe_w4_expand: per 32-column block and slab, four
 // 1 KiB pieces, piece i the dequantised word i of every (column, half)), and
@@ -89,13 +91,18 @@ __global__ __launch_bounds__(64 * WAVES, WGS_PER_CU) void w4_mfma_kernel(const M
   constexpr int S_PER_WAVE = DENSE ? 0 : G32 ? 2 : 1;    // 256 B scale-word loads per wave
   constexpr int OUT_COLS = GATE_UP ? kBCols / 2 : kBCols; // output columns per workgroup
   __shared__ __attribute__((aligned(16))) char lds[STAGES * STAGE];
-  __shared__ float row_w[BM];
+  __shared__ float row_w[BM];  // S7: routing weight of each row
   __shared__ int erow[GATE_UP ? 1 : BM];  // S7, tiles with scaled h rows: each row's largest exponent
   static_assert(!GATE_UP || BM * OUT_COLS * 4 <= STAGES * STAGE, "fp32 h tile must fit the ring");
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS and block addresses stay scalar
   const int col = lane & 31, khalf = lane >> 5;
+
+  // the pointers of the first dependent reads are fetched with the kernel
+  // arguments, not one by one between those reads
+  asm volatile("" ::"s"(p.num_blocks), "s"(p.blocks), "s"(p.tflags), "s"(p.sorted_pairs), "s"(p.topk_weights),
+               "s"(p.t0.unscale), "s"(p.t0.general), "s"(p.t1.unscale), "s"(p.t1.general));
 
   // ---- work item: XCD-contiguous ranges over (tile, column block)
   const int nblk = min(*p.num_blocks, p.max_blocks);
@@ -109,51 +116,56 @@ __global__ __launch_bounds__(64 * WAVES, WGS_PER_CU) void w4_mfma_kernel(const M
   if (item >= total) return;
   const int tile = item / nbn, nb = item % nbn;
   const int e = p.blocks[3 * tile], row0 = p.blocks[3 * tile + 1], rows = p.blocks[3 * tile + 2];
-  // a malformed block map is skipped, never dereferenced out of bounds
-  if (e < 0 || e >= p.E || rows <= 0 || rows > BM || row0 < 0 || row0 > p.P - rows) return;
-  // the expert's factors 2^-c (its weights were scaled by 2^c at pack time)
-  // and dequantisation form (uniform: scalar loads)
-  const float us0 = p.t0.unscale[e], us1 = GATE_UP ? p.t1.unscale[e] : 1.0f;
-  const bool gen = !DENSE && (p.t0.general[e] | (GATE_UP ? p.t1.general[e] : 0u)) != 0;
   // S7: a tile some of whose h rows carry nonzero exponents takes the scaled
   // path below (uniform)
-  const bool scaled = !GATE_UP && p.tflags[tile] != 0;
+  const int tflag = GATE_UP ? 0 : p.tflags[tile];
+  // the entry's words and the flag are read in one round trip (else the
+  // compiler reads rows only after the checks on e)
+  asm volatile("" ::"s"(e), "s"(row0), "s"(rows), "s"(tflag));
+  const bool scaled = tflag != 0;
+  // a malformed block map is skipped, never dereferenced out of bounds
+  if (e < 0 || e >= p.E || rows <= 0 || rows > BM || row0 < 0 || row0 > p.P - rows) return;
+  // the expert's factors 2^-c (its weights were scaled by 2^c at pack time),
+  // used by the epilogue, and dequantisation form, used from the first
+  // multiply on: the loads are issued here and waited for only there, after
+  // the first copies of the ring are in flight (uniform: scalar loads)
+  const float us0 = p.t0.unscale[e], us1 = GATE_UP ? p.t1.unscale[e] : 1.0f;
+  const bool gen = !DENSE && (p.t0.general[e] | (GATE_UP ? p.t1.general[e] : 0u)) != 0;
 
   // ---- A loads: instruction j covers rows 8j..8j+7; lane l fills physical
   // chunk l % 8 of row 8j + l / 8, i.e. logical chunk (l % 8) ^ (l / 8).
-  auto a_source = [&](int j) {
-    const int r = 8 * j + (lane >> 3);
-    const int c = (lane & 7) ^ (lane >> 3);
-    int srow = row0 + min(r, rows - 1);
-    if (GATE_UP) {
-      const int pair = p.sorted_pairs[srow];
-      srow = (pair >= 0 && pair < p.P) ? pair / p.top_k : 0;
-    }
-    return p.a + (size_t)srow * K + 8 * c;
-  };
-  const half_t* asrc[A_PER_WAVE];
-  int a_lds[A_PER_WAVE];
-#pragma unroll
-  for (int a = 0; a < A_PER_WAVE; a++) {
-    const int j = A_INSTR >= WAVES ? wave + WAVES * a : wave % A_INSTR;
-    asrc[a] = a_source(j);
-    a_lds[a] = 1024 * j;
-  }
-  // the half-height loop (rows < BM / 2) with fewer first-half copies than
+  // The half-height loop (rows < BM / 2) with fewer first-half copies than
   // waves: wave w issues copy w mod (A_INSTR / 2), the same bytes to the
   // same LDS place as another wave (a harmless duplicate), so every wave
-  // issues the same number of copies per slab
+  // issues the same number of copies per slab.
   constexpr bool HALF_DUP = MB > 1 && A_PER_WAVE * (MB / 2) < MB;
-  const half_t* asrc_h = nullptr;
-  int a_lds_h = 0;
-  if constexpr (HALF_DUP) {
-    const int j = wave % (A_INSTR / 2);
-    asrc_h = a_source(j);
-    a_lds_h = 1024 * j;
+  constexpr int NA = A_PER_WAVE + (HALF_DUP ? 1 : 0);
+  int arow[NA], a_lds[NA];
+#pragma unroll
+  for (int a = 0; a < NA; a++) {
+    const int j = a == A_PER_WAVE ? wave % (A_INSTR / 2) : A_INSTR >= WAVES ? wave + WAVES * a : wave % A_INSTR;
+    arow[a] = row0 + min(8 * j + (lane >> 3), rows - 1);
+    a_lds[a] = 1024 * j;
   }
+  if constexpr (GATE_UP) {
+    // token rows of the slots' pairs: every pair is read before any is used
+    // (one round trip); an invalid pair reads a valid row (never stored)
+    int pr[NA];
+#pragma unroll
+    for (int a = 0; a < NA; a++) pr[a] = p.sorted_pairs[arow[a]];
+#pragma unroll
+    for (int a = 0; a < NA; a++) arow[a] = min(max(pr[a], 0), p.P - 1) / p.top_k;
+  }
+  const half_t* asrc[NA];
+#pragma unroll
+  for (int a = 0; a < NA; a++) asrc[a] = p.a + (size_t)arow[a] * K + 8 * ((lane & 7) ^ (lane >> 3));
+  const half_t* const asrc_h = HALF_DUP ? asrc[NA - 1] : nullptr;
+  const int a_lds_h = HALF_DUP ? a_lds[NA - 1] : 0;
+
+  // ---- S7 routing weights of the tile's rows (0 past the tile)
   if (!GATE_UP && tid < BM) {
     const int pair = tid < rows ? p.sorted_pairs[row0 + tid] : -1;
-    row_w[tid] = (pair >= 0 && pair < p.P) ? p.topk_weights[pair] * us0 : 0.0f;
+    row_w[tid] = (pair >= 0 && pair < p.P) ? p.topk_weights[pair] : 0.0f;
   }
 
   // packed 32-column block (index into the bank's N/32) of weight-column
@@ -219,11 +231,14 @@ __global__ __launch_bounds__(64 * WAVES, WGS_PER_CU) void w4_mfma_kernel(const M
   // GEN: the general dequantisation (see dequant_word_gen).  SCALED (S7):
   // h rows with nonzero exponents; each slab's activations are brought to
   // their row's largest exponent in LDS before the multiplies (one stage, no
-  // copies in flight across slabs: such tiles are rare).
-  auto pipeline = [&](auto mba, auto gen_tag, auto scaled_tag) {
+  // copies in flight across slabs: such tiles are rare).  PRO: this call
+  // issues the ring's first copies itself (else the caller did, through
+  // prologue() with the same MBA, before choosing GEN).
+  auto pipeline = [&](auto mba, auto gen_tag, auto scaled_tag, auto pro_tag) {
     constexpr int MBA = decltype(mba)::value;
     constexpr bool GEN = decltype(gen_tag)::value != 0;
     constexpr bool SCALED = decltype(scaled_tag)::value != 0;
+    constexpr bool PRO = decltype(pro_tag)::value != 0;
     constexpr bool DUP = HALF_DUP && MBA < MB;
     constexpr int APW = DUP ? 1 : A_PER_WAVE * MBA / MB;  // activation copies used (rows < 32 MBA)
     constexpr int DA = APW + B_PER_WAVE + S_PER_WAVE;
@@ -314,8 +329,10 @@ __global__ __launch_bounds__(64 * WAVES, WGS_PER_CU) void w4_mfma_kernel(const M
         asm volatile("s_barrier" ::: "memory");  // stage 0 is refilled next
       }
     } else {
+      if constexpr (PRO) {
 #pragma unroll
-      for (int j = 0; j < STAGES - 1; j++) issue(min(j, S - 1), j);
+        for (int j = 0; j < STAGES - 1; j++) issue(min(j, S - 1), j);
+      }
       for (int s = 0; s < S; s++) {
         wait_vm_barrier<(STAGES - 2) * DA>();
         issue(min(s + STAGES - 1, S - 1), (s + STAGES - 1) % STAGES);
@@ -325,31 +342,51 @@ __global__ __launch_bounds__(64 * WAVES, WGS_PER_CU) void w4_mfma_kernel(const M
   };
   if (!GATE_UP && scaled) {
     // each row's largest exponent (rows past the tile repeat its last row);
-    // the row's output is scaled by 2^that (with the routing weight)
+    // the epilogue scales the row's output by 2^that (with the routing weight)
     const int nbk = K / 16;
     for (int r = tid; r < BM; r += 64 * WAVES) {
       const uint32_t* er = reinterpret_cast<const uint32_t*>(p.hexp + (size_t)(row0 + min(r, rows - 1)) * nbk);
       int m = -128;
       for (int b = 0; b < nbk / 4; b++) m = max(m, max_i8x4(er[b]));
       erow[r] = m;
-      row_w[r] = ldexpf(row_w[r], m);
     }
     __syncthreads();
   }
-  // uniform per workgroup: every wave takes the same branch
+  // uniform per workgroup: every wave takes the same branch.  The ring's
+  // first copies are issued (for the chosen tile height) before the branch on
+  // the dequantisation form, whose scalar loads then overlap them.
+  auto prologue = [&](auto mba) {
+    constexpr int MBA = decltype(mba)::value;
+    constexpr bool DUP = HALF_DUP && MBA < MB;
+    constexpr int APW = DUP ? 1 : A_PER_WAVE * MBA / MB;
+#pragma unroll
+    for (int j = 0; j < STAGES - 1; j++) {
+      const int s = min(j, slabs - 1);
+      char* base = lds + j * STAGE;
+#pragma unroll
+      for (int a = 0; a < APW; a++)
+        lds_load16((DUP ? asrc_h : asrc[a]) + s * kSlabK, base + (DUP ? a_lds_h : a_lds[a]));
+#pragma unroll
+      for (int b = 0; b < B_PER_WAVE; b++)
+        lds_load16(bsrc[b] + s * (DENSE ? 4096 : 1024), base + A_BYTES + 1024 * (B_PER_WAVE * wave + b));
+#pragma unroll
+      for (int t = 0; t < S_PER_WAVE; t++)
+        lds_load4(ssrc + ((s * kSlabK + 32 * t) >> log2G) * 128,
+                  base + A_BYTES + kBStage + 4 * kBCols * t + 256 * wave);
+    }
+  };
+  constexpr int MBH = MB > 1 ? MB / 2 : 1;
   if (!GATE_UP && scaled) {
-    if (gen) pipeline(IntTag<MB>{}, IntTag<DENSE ? 0 : 1>{}, IntTag<1>{});
-    else pipeline(IntTag<MB>{}, IntTag<0>{}, IntTag<1>{});
-  } else if (gen) {
-    if (MB > 1 && rows <= BM / 2)
-      pipeline(IntTag<(MB > 1 ? MB / 2 : 1)>{}, IntTag<DENSE ? 0 : 1>{}, IntTag<0>{});
-    else
-      pipeline(IntTag<MB>{}, IntTag<DENSE ? 0 : 1>{}, IntTag<0>{});
+    if (gen) pipeline(IntTag<MB>{}, IntTag<DENSE ? 0 : 1>{}, IntTag<1>{}, IntTag<1>{});
+    else pipeline(IntTag<MB>{}, IntTag<0>{}, IntTag<1>{}, IntTag<1>{});
+  } else if (MB > 1 && rows <= BM / 2) {
+    prologue(IntTag<MBH>{});
+    if (gen) pipeline(IntTag<MBH>{}, IntTag<DENSE ? 0 : 1>{}, IntTag<0>{}, IntTag<0>{});
+    else pipeline(IntTag<MBH>{}, IntTag<0>{}, IntTag<0>{}, IntTag<0>{});
   } else {
-    if (MB > 1 && rows <= BM / 2)
-      pipeline(IntTag<(MB > 1 ? MB / 2 : 1)>{}, IntTag<0>{}, IntTag<0>{});
-    else
-      pipeline(IntTag<MB>{}, IntTag<0>{}, IntTag<0>{});
+    prologue(IntTag<MB>{});
+    if (gen) pipeline(IntTag<MB>{}, IntTag<DENSE ? 0 : 1>{}, IntTag<0>{}, IntTag<0>{});
+    else pipeline(IntTag<MB>{}, IntTag<0>{}, IntTag<0>{}, IntTag<0>{});
   }
 
   // ---- epilogue.  Accumulator register r of lane l holds row
@@ -408,26 +445,35 @@ __global__ __launch_bounds__(64 * WAVES, WGS_PER_CU) void w4_mfma_kernel(const M
     // Registers 4g .. 4g + 3 of a lane hold 4 consecutive rows of one
     // column; a 4 x 4 transpose inside each lane quad (two DPP exchange
     // steps, partners lane ^ 2 then lane ^ 1) gives lane 4q + j row j of
-    // them at columns 4q .. 4q + 3, which it weights, packs and stores as
-    // 12 bytes.
+    // them at columns 4q .. 4q + 3, which it weights.  The four lanes holding
+    // one row's 16-column block (q = 4b .. 4b + 3: lanes j, j + 4, j + 8,
+    // j + 12 of a 16-lane DPP row) share its exponent (two row rotations
+    // give their maximum); each lane stores its 4 int16 mantissas (8 bytes),
+    // the lane with q % 4 == 0 the block's exponent.
     const int j4 = col & 3, q = col >> 2;
     const bool hi2 = (j4 & 2) != 0, hi1 = (j4 & 1) != 0;
     auto xchg = [](float v, int ctrl) {
       return ctrl == 0x4E ? __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true))
                           : __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
     };
-    // byte address of this lane's rows 4 khalf + j4 (+ 32 mb + 8 g) at
-    // columns 4q .. 4q + 3 of its 64-column slice (row stride 3 N bytes)
-    const size_t rstride = (size_t)N * 3;
-    char* const lane_out = reinterpret_cast<char*>(p.out) + (size_t)(row0 + 4 * khalf + j4) * rstride +
-                           (size_t)(nb * OUT_COLS + wave * 64 + 4 * q) * 3;
+    // this lane's rows 4 khalf + j4 (+ 32 mb + 8 g) at columns 4q .. 4q + 3
+    // of its 64-column slice: mantissas (row stride 2 N bytes) and exponents
+    // (row stride N / 16)
+    const size_t mstride = (size_t)N * 2, estride = (size_t)N / 16;
+    const int c0 = nb * OUT_COLS + wave * 64;
+    char* const lane_out = reinterpret_cast<char*>(p.out) + (size_t)(row0 + 4 * khalf + j4) * mstride +
+                           (size_t)(c0 + 4 * q) * 2;
+    int8_t* const lane_exp = p.yexp + (size_t)(row0 + 4 * khalf + j4) * estride + c0 / 16 + (q >> 2);
     // the routing weights of this lane's rows after the transposes, read
     // from LDS once
     float wr[MB][4];
 #pragma unroll
     for (int mb = 0; mb < MB; mb++)
 #pragma unroll
-      for (int g = 0; g < 4; g++) wr[mb][g] = row_w[mb * 32 + 8 * g + 4 * khalf + j4];
+      for (int g = 0; g < 4; g++) {
+        const int r = mb * 32 + 8 * g + 4 * khalf + j4;
+        wr[mb][g] = (scaled ? ldexpf(row_w[r], erow[r]) : row_w[r]) * us0;
+      }
 #pragma unroll
     for (int mb = 0; mb < MB; mb++)
 #pragma unroll
@@ -449,10 +495,16 @@ __global__ __launch_bounds__(64 * WAVES, WGS_PER_CU) void w4_mfma_kernel(const M
           a2 = hi1 ? r1 : a2;
           a1 = hi1 ? a1 : r0;
           a3 = hi1 ? a3 : r1;
+          const float w = wr[mb][g];
+          const float v0 = w * a0, v1 = w * a1, v2 = w * a2, v3 = w * a3;
+          float m = fmaxf(fmaxf(fabsf(v0), fabsf(v1)), fmaxf(fabsf(v2), fabsf(v3)));
+          m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0x124, 0xF, 0xF, true)));  // row_ror:4
+          m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0x128, 0xF, 0xF, true)));  // row_ror:8
+          const int ex = y16_exp(m);
           if (mb * 32 + 8 * g + 4 * khalf + j4 < rows) {
-            const float w = wr[mb][g];
-            *reinterpret_cast<uint3*>(lane_out + (size_t)(mb * 32 + 8 * g) * rstride + cb * 96) =
-                pack24x4(w * a0, w * a1, w * a2, w * a3);
+            *reinterpret_cast<uint2*>(lane_out + (size_t)(mb * 32 + 8 * g) * mstride + cb * 64) =
+                y16_pack4(v0, v1, v2, v3, ex);
+            if ((q & 3) == 0) lane_exp[(size_t)(mb * 32 + 8 * g) * estride + cb * 2] = (int8_t)ex;
           }
         }
   } else {
@@ -463,7 +515,7 @@ __global__ __launch_bounds__(64 * WAVES, WGS_PER_CU) void w4_mfma_kernel(const M
       for (int r = 0; r < 16; r++) {
         const int row = mb * 32 + 8 * (r >> 2) + 4 * khalf + (r & 3);
         if (row >= rows) continue;
-        const float w = row_w[row];
+        const float w = (scaled ? ldexpf(row_w[row], erow[row]) : row_w[row]) * us0;
         float* orow = reinterpret_cast<float*>(p.out) + (size_t)(row0 + row) * N;
 #pragma unroll
         for (int cb = 0; cb < 2; cb++)
@@ -492,7 +544,8 @@ hipError_t launch_mode(const GemmArgs& a, hipStream_t s) {
   if (max_blocks == 0) return hipSuccess;
   const int log2_G = a.G == 32 ? 5 : a.G == 64 ? 6 : 7;  // G in {32, 64, 128}
   MfmaParams p{a.a, a.b0, a.b1, a.sorted_pairs, a.topk_weights, a.blocks, a.num_blocks, a.out,
-               a.t0, a.t1, a.hexp, a.tflags, a.N, a.K, log2_G, a.top_k, a.E, (int)P, (int)max_blocks};
+               a.t0, a.t1, a.hexp, a.tflags, a.yexp, a.N, a.K, log2_G, a.top_k, a.E, (int)P,
+               (int)max_blocks};
   // 4 waves (256 weight columns) per workgroup and two or three workgroups
   // per CU, so one workgroup's prologue and epilogue overlap another's main
   // loop; 64- and 128-row tiles use a 3-stage ring to fit three and two
@@ -533,14 +586,14 @@ hipError_t launch_mode(const GemmArgs& a, hipStream_t s) {
 
 // y[t][:] = sum_j y_sorted[pair_slot[t*k + j]][:], j ascending, fp32: the
 // k weighted expert outputs of a token added in a fixed order, so the layer
-// output is deterministic.  One thread per 4 columns of y (16 bytes out;
-// 16 bytes in per slot, or 12 when y_sorted is packed 24-bit); all k slot
-// indices and then all k rows are loaded before the sum (KMAX >= k, guards
-// for j >= k), so a thread has k row loads in flight instead of k round
-// trips.
-// With out: also out = bf16(residual + y), four values per thread.
-template <int KMAX, bool PACK>
-__global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y_sorted,
+// output is deterministic.  All k slot indices and then all k rows are
+// loaded before the sum (KMAX >= k, guards for j >= k), so a thread has k
+// row loads in flight instead of k round trips.  Out-of-range slots are
+// skipped.
+// fp32 y_sorted: one thread per 4 columns of y (16 bytes in per slot, 16
+// out).  With out: also out = bf16(residual + y), four values per thread.
+template <int KMAX>
+__global__ __launch_bounds__(256) void combine_kernel(const float4* __restrict__ y_sorted,
                                                       const int32_t* __restrict__ pair_slot,
                                                       float4* __restrict__ y, int T, int H4,
                                                       int k, const uint2* __restrict__ residual,
@@ -553,16 +606,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
 #pragma unroll
   for (int j = 0; j < KMAX; j++) {
     slot[j] = j < k ? pair_slot[(size_t)t * k + j] : -1;
-    if (slot[j] >= P) slot[j] = -1;  // out-of-range slots are skipped
+    if (slot[j] >= P) slot[j] = -1;
   }
   float4 v[KMAX];
 #pragma unroll
-  for (int j = 0; j < KMAX; j++) {
-    const size_t at = (size_t)slot[j] * H4 + c;
-    if (slot[j] < 0) v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-    else if constexpr (PACK) v[j] = unpack24x4(reinterpret_cast<const uint3*>(y_sorted)[at]);
-    else v[j] = reinterpret_cast<const float4*>(y_sorted)[at];
-  }
+  for (int j = 0; j < KMAX; j++)
+    v[j] = slot[j] < 0 ? make_float4(0.f, 0.f, 0.f, 0.f) : y_sorted[(size_t)slot[j] * H4 + c];
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
   for (int j = 0; j < KMAX; j++) {
@@ -576,11 +625,59 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ y
   if (out) out[i] = residual_add_bf16x4(residual[i], acc);
 }
 
+// The same over y16e block floating point: one thread per 8 columns of y
+// (per slot 16 bytes of mantissas and the block's exponent byte in, 32
+// bytes out); the decoded values are exact in fp32, so the sum is the fp32
+// sum of the decoded rows in choice order.
+template <int KMAX>
+__global__ __launch_bounds__(256) void combine16_kernel(const uint4* __restrict__ ym,
+                                                        const int8_t* __restrict__ ye,
+                                                        const int32_t* __restrict__ pair_slot,
+                                                        float4* __restrict__ y, int T, int H8,
+                                                        int k, const uint2* __restrict__ residual,
+                                                        uint2* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)T * H8) return;
+  const int t = (int)(i / H8), c = (int)(i % H8);
+  const int P = T * k;
+  int slot[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; j++) {
+    slot[j] = j < k ? pair_slot[(size_t)t * k + j] : -1;
+    if (slot[j] >= P) slot[j] = -1;
+  }
+  uint4 m[KMAX];
+  int ex[KMAX];
+#pragma unroll
+  for (int j = 0; j < KMAX; j++) {
+    const size_t row = (size_t)(slot[j] < 0 ? 0 : slot[j]);
+    m[j] = ym[row * H8 + c];
+    ex[j] = ye[row * (H8 / 2) + (c >> 1)];
+  }
+  float acc[8];
+#pragma unroll
+  for (int q = 0; q < 8; q++) acc[q] = 0.0f;
+#pragma unroll
+  for (int j = 0; j < KMAX; j++) {
+    if (slot[j] < 0) continue;
+    float v[8];
+    y16_unpack8(m[j], ex[j], v);
+#pragma unroll
+    for (int q = 0; q < 8; q++) acc[q] += v[q];
+  }
+#pragma unroll
+  for (int h = 0; h < 2; h++) {
+    const float4 a4 = make_float4(acc[4 * h], acc[4 * h + 1], acc[4 * h + 2], acc[4 * h + 3]);
+    y[2 * i + h] = a4;
+    if (out) out[2 * i + h] = residual_add_bf16x4(residual[2 * i + h], a4);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_w4_mfma(const GemmArgs& a, hipStream_t s) {
   if (a.mode == MOE_GEMM_GATE_UP_SWIGLU) return launch_mode<MOE_GEMM_GATE_UP_SWIGLU, false>(a, s);
-  return a.pack24 ? launch_mode<MOE_GEMM_DOWN, true>(a, s) : launch_mode<MOE_GEMM_DOWN, false>(a, s);
+  return a.y16e ? launch_mode<MOE_GEMM_DOWN, true>(a, s) : launch_mode<MOE_GEMM_DOWN, false>(a, s);
 }
 
 hipError_t launch_stage_x(const uint16_t* x, half_t* xh, int64_t n_elems, int32_t* tflags,
@@ -593,26 +690,30 @@ hipError_t launch_stage_x(const uint16_t* x, half_t* xh, int64_t n_elems, int32_
   return hipGetLastError();
 }
 
-template <bool PACK>
-void launch_combine_k(const void* ys, const int32_t* pair_slot, float4* yo, int T, int H4, int k,
-                      const uint2* res, uint2* out,
-                      int64_t grid, hipStream_t s) {
-  if (k <= 2) combine_kernel<2, PACK><<<grid, 256, 0, s>>>(ys, pair_slot, yo, T, H4, k, res, out);
-  else if (k <= 4) combine_kernel<4, PACK><<<grid, 256, 0, s>>>(ys, pair_slot, yo, T, H4, k, res, out);
-  else if (k <= 8) combine_kernel<8, PACK><<<grid, 256, 0, s>>>(ys, pair_slot, yo, T, H4, k, res, out);
-  else combine_kernel<16, PACK><<<grid, 256, 0, s>>>(ys, pair_slot, yo, T, H4, k, res, out);  // k <= 16
+template <int KMAX>
+void launch_combine_k(const void* ys, const int8_t* yexp, const int32_t* pair_slot, float4* yo, int T,
+                      int H, int k, const uint2* res, uint2* out, hipStream_t s) {
+  if (yexp) {
+    const int64_t n = (int64_t)T * (H / 8);
+    combine16_kernel<KMAX><<<(n + 255) / 256, 256, 0, s>>>(reinterpret_cast<const uint4*>(ys), yexp,
+                                                           pair_slot, yo, T, H / 8, k, res, out);
+  } else {
+    const int64_t n = (int64_t)T * (H / 4);
+    combine_kernel<KMAX><<<(n + 255) / 256, 256, 0, s>>>(reinterpret_cast<const float4*>(ys), pair_slot,
+                                                         yo, T, H / 4, k, res, out);
+  }
 }
 
-hipError_t launch_combine(const void* y_sorted, bool pack24, const int32_t* pair_slot, float* y,
+hipError_t launch_combine(const void* y_sorted, const int8_t* yexp, const int32_t* pair_slot, float* y,
                           int T, int H, int k, hipStream_t s, const uint16_t* residual,
                           uint16_t* out) {
-  const int64_t n = (int64_t)T * (H / 4);
-  const int64_t grid = (n + 255) / 256;
   float4* yo = reinterpret_cast<float4*>(y);
   const uint2* res = reinterpret_cast<const uint2*>(residual);
   uint2* o = reinterpret_cast<uint2*>(out);
-  if (pack24) launch_combine_k<true>(y_sorted, pair_slot, yo, T, H / 4, k, res, o, grid, s);
-  else launch_combine_k<false>(y_sorted, pair_slot, yo, T, H / 4, k, res, o, grid, s);
+  if (k <= 2) launch_combine_k<2>(y_sorted, yexp, pair_slot, yo, T, H, k, res, o, s);
+  else if (k <= 4) launch_combine_k<4>(y_sorted, yexp, pair_slot, yo, T, H, k, res, o, s);
+  else if (k <= 8) launch_combine_k<8>(y_sorted, yexp, pair_slot, yo, T, H, k, res, o, s);
+  else launch_combine_k<16>(y_sorted, yexp, pair_slot, yo, T, H, k, res, o, s);  // k <= 16
   return hipGetLastError();
 }
 

@@ -38,18 +38,18 @@ struct DecParams {
   int8_t* hexp;     // h's exponents [P][I / 16] (h_block_exp): written by S6, read by S7
   int32_t* tflags;  // per tile: a row has a nonzero exponent (written by S6 when given)
   int N, K, log2_G, top_k, E, P, max_blocks;
-  int red_off;  // byte offset of the partial-sum area in the dynamic LDS
+  int red_off;     // byte offset of the partial-sum area in the dynamic LDS
+  int lg_off = 0;  // fused decode gate/up: byte offset of the logits in the dynamic LDS
+  bool x_res = false;  // fused decode gate/up: every x row resident in LDS ([T][K] at 0)
 };
 
 // One (tile, 32-column block) of the product: tile rows [row0, row0 + rows)
 // of expert e (rows <= kGemvMaxTokens), output columns [32 blk, 32 blk + 32).
-// SPW: 64-wide slabs per wave and pass.  PACK (S7 only): out is packed
-// 24-bit instead of fp32.  XBF16 (S6 only): p.a is x itself (bf16 [T][K]),
-// converted to fp16 operand order while staged, instead of the fp16 copy.
+// SPW: 64-wide slabs per wave and pass.
 // sorted_pairs: slot -> pair (global memory, or LDS in the fused kernel).
 // dsm: the dynamic LDS, sized by the launch.
 // GEN: the expert takes the general dequantisation (dequant_word_gen).
-template <int MODE, int SPW, bool PACK, bool XBF16, bool GEN>
+template <int MODE, int SPW, bool GEN>
 __device__ __forceinline__ void gemv_tile(const DecParams& p, const int32_t* sorted_pairs, int e,
                                           int row0, int rows, int blk, char* dsm) {
   constexpr bool GATE_UP = MODE == MOE_GEMM_GATE_UP_SWIGLU;
@@ -125,11 +125,7 @@ __device__ __forceinline__ void gemv_tile(const DecParams& p, const int32_t* sor
         const int pair = sorted_pairs[r];
         r = (pair >= 0 && pair < p.P) ? pair / p.top_k : 0;
       }
-      if constexpr (XBF16)
-        *reinterpret_cast<uint4*>(xs + m * xw + 8 * c8) = bf16x8_to_half_interleaved(
-            *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p.a) + (size_t)r * K +
-                                            64 * base + 8 * c8));
-      else if constexpr (GATE_UP)
+      if constexpr (GATE_UP)
         *reinterpret_cast<uint4*>(xs + m * xw + 8 * c8) =
             *reinterpret_cast<const uint4*>(p.a + (size_t)r * K + 64 * base + 8 * c8);
       else {
@@ -169,31 +165,11 @@ __device__ __forceinline__ void gemv_tile(const DecParams& p, const int32_t* sor
 #pragma unroll
     for (int r = 0; r < 4; r++) red[((wave * NB + b) * 4 + r) * 64 + lane] = acc[b][r];
   __syncthreads();
-  if constexpr (PACK) {
-    // 4 consecutive columns per thread, weighted, packed into 12 bytes
-    for (int t = tid; t < rows * 8; t += blockDim.x) {
-      const int m = t >> 3, q = t & 7;
-      const int rr = m & 3;
-      float v4[4];
-#pragma unroll
-      for (int c = 0; c < 4; c++) {
-        const int ll = 4 * q + c + 32 * (m >> 2);
-        float v = red[rr * 64 + ll];
-        for (int w2 = 1; w2 < nwaves; w2++) v += red[(w2 * 4 + rr) * 64 + ll];
-        v4[c] = v;
-      }
-      const int pair = sorted_pairs[row0 + m];
-      const float wgt = (pair >= 0 && pair < p.P) ? ldexpf(p.topk_weights[pair] * us0, em_s[m]) : 0.0f;
-      reinterpret_cast<uint3*>(p.out)[((size_t)(row0 + m) * p.N + blk * 32) / 4 + q] =
-          pack24x4(wgt * v4[0], wgt * v4[1], wgt * v4[2], wgt * v4[3]);
-    }
-    return;
-  }
   if constexpr (GATE_UP) {
-    // h in fp32 per (row, column) into LDS (the activation stage is free),
-    // then stored as fp16 with one exponent per 16 columns (h_block_exp), in
+    // h in fp32 per (row, column), stored as fp16 with one exponent per 16
+    // columns (h_block_exp; a row's 32 columns are two 16-lane DPP rows), in
     // operand order (see the MFMA kernel)
-    float* hs = reinterpret_cast<float*>(dsm);
+    bool any = false;
     for (int t = tid; t < rows * 32; t += blockDim.x) {
       const int m = t >> 5, cc = t & 31;
       const int rr = m & 3, ll = cc + 32 * (m >> 2);
@@ -203,20 +179,11 @@ __device__ __forceinline__ void gemv_tile(const DecParams& p, const int32_t* sor
         v[b] = red[((0 * NB + b) * 4 + rr) * 64 + ll];
         for (int w2 = 1; w2 < nwaves; w2++) v[b] += red[((w2 * NB + b) * 4 + rr) * 64 + ll];
       }
-      hs[t] = silu_mul(v[0] * us0, v[NB - 1] * us1);
-    }
-    __syncthreads();
-    bool any = false;
-    for (int t = tid; t < rows * 32; t += blockDim.x) {
-      const int m = t >> 5, cc = t & 31;
-      const float* blk16 = hs + (t & ~15);
-      float mx = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 16; i++) mx = fmaxf(mx, fabsf(blk16[i]));
-      const int ex = h_block_exp(mx);
+      const float hv = silu_mul(v[0] * us0, v[NB - 1] * us1);
+      const int ex = h_block_exp(row16_max(fabsf(hv)));
       const int n = blk * 32 + cc;
       reinterpret_cast<half_t*>(p.out)[(size_t)(row0 + m) * p.N + (n & ~7) + interleaved_pos(n & 7)] =
-          (half_t)ldexpf(hs[t], -ex);
+          (half_t)ldexpf(hv, -ex);
       if ((cc & 15) == 0) p.hexp[(size_t)(row0 + m) * (p.N / 16) + n / 16] = (int8_t)ex;
       any |= ex != 0;
     }
@@ -347,9 +314,9 @@ __device__ __forceinline__ void g16_epilogue(const DecParams& p, const floatx4_t
 #pragma unroll
       for (int i = 0; i < 4; i++) red[((wave * 2 + b) * 4 + i) * 32 + lane] = acc[b][i];
   __syncthreads();
-  // h in fp32 per (row, column) into LDS (the activation stage is free), then
-  // stored as fp16 with the block's exponent (h_block_exp), operand order
-  float* hs = reinterpret_cast<float*>(dsm);
+  // h in fp32 per (row, column), stored as fp16 with the block's exponent
+  // (h_block_exp; the 16 columns of a row are one 16-lane DPP row), operand
+  // order
   for (int t = tid; t < rows * 16; t += blockDim.x) {
     const int m = t >> 4, cc = t & 15;
     const int rr = m & 3, ll = cc + 16 * (m >> 2);
@@ -359,18 +326,11 @@ __device__ __forceinline__ void g16_epilogue(const DecParams& p, const floatx4_t
       v[b] = red[(b * 4 + rr) * 32 + ll];
       for (int w2 = 1; w2 < nwaves; w2++) v[b] += red[((w2 * 2 + b) * 4 + rr) * 32 + ll];
     }
-    hs[t] = silu_mul(v[0] * us0, v[1] * us1);
-  }
-  __syncthreads();
-  for (int t = tid; t < rows * 16; t += blockDim.x) {
-    const int m = t >> 4, cc = t & 15;
-    float mx = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 16; i++) mx = fmaxf(mx, fabsf(hs[16 * m + i]));
-    const int ex = h_block_exp(mx);
+    const float hv = silu_mul(v[0] * us0, v[1] * us1);
+    const int ex = h_block_exp(row16_max(fabsf(hv)));
     const int n = b16 * 16 + cc;
     reinterpret_cast<half_t*>(p.out)[(size_t)(row0 + m) * p.N + (n & ~7) + interleaved_pos(n & 7)] =
-        (half_t)ldexpf(hs[t], -ex);
+        (half_t)ldexpf(hv, -ex);
     if (cc == 0) p.hexp[(size_t)(row0 + m) * (p.N / 16) + b16] = (int8_t)ex;
   }
   __syncthreads();
@@ -386,11 +346,12 @@ __device__ __forceinline__ void g16_epilogue(const DecParams& p, const floatx4_t
 // reduction indices 32 (l / 32) + 16 q + 8 m + [0, 8) of the slab, and the
 // activation fragment of tile row l % 16 is read to match (zeros past the
 // tile).  SPW slabs per wave and pass.
+// gen, us0, us1: the expert's dequantisation form and factors 2^-c.
 template <int SPW>
 __device__ __forceinline__ void gemv_tile16(const DecParams& p, const int32_t* sorted_pairs, int e,
-                                            int row0, int rows, int b16, char* dsm) {
+                                            int row0, int rows, int b16, char* dsm, bool gen,
+                                            float us0, float us1) {
   const int pass_slabs = (blockDim.x >> 6) * SPW;
-  const bool gen = (p.t0.general[e] | p.t1.general[e]) != 0;
   floatx4_t acc[2] = {floatx4_t{}, floatx4_t{}};
   for (int base = 0; base < p.K / 64; base += pass_slabs) {
     const Frag16<SPW> f = g16_load<SPW>(p, e, b16, base);
@@ -400,12 +361,12 @@ __device__ __forceinline__ void gemv_tile16(const DecParams& p, const int32_t* s
     else g16_mma<SPW, false>(p, f, rows, base, acc, dsm);
     __syncthreads();  // the next pass overwrites xs
   }
-  g16_epilogue(p, acc, row0, rows, b16, dsm, p.t0.unscale[e], p.t1.unscale[e]);
+  g16_epilogue(p, acc, row0, rows, b16, dsm, us0, us1);
 }
 
 // The grouped GEMM at decode sizes on a device block map: one workgroup per
 // (tile, 32-column block); tiles past the map's count exit.
-template <int MODE, int SPW, bool PACK = false>
+template <int MODE, int SPW>
 __global__ __launch_bounds__(64 * kDecWavesMax) void w4_gemv_kernel(const DecParams p) {
   extern __shared__ __attribute__((aligned(16))) char dsm[];
   const int nbl = p.N / 32;
@@ -419,8 +380,8 @@ __global__ __launch_bounds__(64 * kDecWavesMax) void w4_gemv_kernel(const DecPar
   if (e < 0 || e >= p.E || rows <= 0 || rows > kGemvMaxTokens || row0 < 0 || row0 > p.P - rows)
     return;
   const bool gen = (p.t0.general[e] | (MODE == MOE_GEMM_GATE_UP_SWIGLU ? p.t1.general[e] : 0u)) != 0;
-  if (gen) gemv_tile<MODE, SPW, PACK, false, true>(p, p.sorted_pairs, e, row0, rows, blk, dsm);
-  else gemv_tile<MODE, SPW, PACK, false, false>(p, p.sorted_pairs, e, row0, rows, blk, dsm);
+  if (gen) gemv_tile<MODE, SPW, true>(p, p.sorted_pairs, e, row0, rows, blk, dsm);
+  else gemv_tile<MODE, SPW, false>(p, p.sorted_pairs, e, row0, rows, blk, dsm);
 }
 
 struct DecRouteParams {
@@ -432,32 +393,93 @@ struct DecRouteParams {
   int32_t *counts, *offsets, *sorted_pairs, *pair_slot, *blocks, *num_blocks;
 };
 
+// Dequantise this wave's fragments of one item and multiply them with x rows
+// resident in LDS ([T][K], operand order): tile row c (lane group row c < rows)
+// reads token xrow_c's row, rows past the tile read zeros.
+template <int SPW, bool GEN>
+__device__ __forceinline__ void g16_mma_res(const DecParams& p, const Frag16<SPW>& f, int xrow_c,
+                                            floatx4_t (&acc)[2], const char* dsm) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const half_t* xs = reinterpret_cast<const half_t*>(dsm) + (size_t)max(xrow_c, 0) * p.K;
+  const int lg = (lane & 63) >> 4, khalf = lg >> 1, qh = lg & 1;
+#pragma unroll
+  for (int j = 0; j < SPW; j++) {
+    const int sl = SPW * wave + j;
+    if (sl >= p.K / 64) break;  // uniform per wave
+    u32x4 x[2];
+#pragma unroll
+    for (int m = 0; m < 2; m++) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(xs + 64 * sl + 32 * khalf + 16 * qh + 8 * m);
+      x[m] = xrow_c >= 0 ? v : u32x4{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int b = 0; b < 2; b++) {
+      const SbPair sp = sb_unpack(f.sb[b][j], GEN);
+#pragma unroll
+      for (int m = 0; m < 2; m++) {
+        const uint32_t w = m == 0 ? f.q[b][j].x : f.q[b][j].y;
+        const uint4 d = GEN ? dequant_word_gen(w, sp.s2, sp.c2, sp.b2) : dequant_word(w, sp.s2, sp.c2);
+        acc[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, x[m]),
+                                                        __builtin_bit_cast(half8_t, d), acc[b], 0, 0, 0);
+      }
+    }
+  }
+}
+
 // Decode sizes, S1-S6 in one launch.  Each workgroup first routes the whole
 // batch (at most kGemvMaxTokens tokens, so at most kSmallPairs pairs) into
-// LDS: the summed logits, the top-k of each token by one wave (topk_token:
-// logit descending, lower expert first on ties, softmax over the chosen
-// logits), the expert counts, then S2-S5 by wave 0 (small_build).  Every
-// workgroup gets the same result (same inputs, same operations), so the
-// block map needs no exchange; workgroup 0 writes it, and the rest of the
-// routing, to global memory for the down projection and the caller.  Then
-// the workgroup runs its (tile, 32-column block) of the gate/up GEMV, the
-// activations read from x (bf16) through the LDS scatter.
+// LDS: the summed logits, the top-k of each token by one wave
+// (topk_token: logit descending, lower expert first on ties, softmax over
+// the chosen logits), the expert counts, then S2-S5 by the whole workgroup
+// (decode_build_wg).  Every workgroup gets the same result (same
+// inputs, same operations), so the block map needs no exchange; workgroup 0 writes it,
+// and the rest of the routing, to global memory for the down projection and
+// the caller.  Then the workgroup runs its (tile, 16-column block) items of
+// the gate/up GEMV.  When the reduction fits one pass (x_res), all T rows of
+// x (bf16 -> fp16 operand order) are staged into LDS once, read in the same
+// round trip as the logits, and every item reads its tile's rows from there;
+// otherwise each pass stages the tile's rows through the LDS scatter.
 // NK = ceil(E / 64) keys per lane in the top-k.
 template <int NK, int SPW>
 __global__ __launch_bounds__(64 * kDecWavesMax) void decode_gate_up_kernel(const DecRouteParams r,
                                                                           const DecParams p) {
   extern __shared__ __attribute__((aligned(16))) char dsm[];
-  __shared__ int cnt[256], next[256];
+  __shared__ int cnt[256], wsc[8];
+  __shared__ uint32_t tokmask[256];
   __shared__ int32_t ids_s[kSmallPairs], sp_s[kSmallPairs], ps_s[kSmallPairs];
   __shared__ float w_s[kSmallPairs];
   __shared__ int32_t off_s[257];
   __shared__ int32_t blk_s[3 * kSmallMaxBlocks];
   __shared__ int32_t nb_s[1];
+  __shared__ float us_s[2][256];  // every expert's 2^-c for gate and up
+  __shared__ int gen_s[256];      // and dequantisation form (general if either bank's is)
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nwaves = blockDim.x >> 6;
-  const int T = r.T, E = p.E, k = p.top_k, P = p.P;
-  float* lg = reinterpret_cast<float*>(dsm);  // [T][E]; the activation stage reuses the space
+  const int T = r.T, E = p.E, k = p.top_k, P = p.P, K = p.K;
+  // [T][E] logits; without x_res the activation stage reuses the space
+  float* lg = reinterpret_cast<float*>(dsm + p.lg_off);
+  // 0. the per-expert tables of both banks, the logits and (x_res) the x
+  //    rows: every load issued before any is stored (E <= 256, blockDim.x
+  //    >= 64, T * K / 8 <= 4 blockDim.x with x_res)
+  float ua[4], ub[4];
+  uint32_t ga[4];
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const int x = min(tid + i * (int)blockDim.x, E - 1);
+    ua[i] = p.t0.unscale[x];
+    ub[i] = p.t1.unscale[x];
+    ga[i] = p.t0.general[x] | p.t1.general[x];
+  }
+  const int c8n = K / 8, nx8 = p.x_res ? T * c8n : 0;
+  uint4 xv[4];
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const int idx = min(tid + i * (int)blockDim.x, max(nx8 - 1, 0));
+    xv[i] = p.x_res ? *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p.a) + 8 * (size_t)idx)
+                    : make_uint4(0, 0, 0, 0);
+  }
   // 1. logits: partial sums over ranges of H added in range order
   const size_t part = (size_t)T * E;
   for (int i = tid; i < T * E; i += blockDim.x) {
@@ -465,7 +487,22 @@ __global__ __launch_bounds__(64 * kDecWavesMax) void decode_gate_up_kernel(const
     for (int z = 1; z < r.ksplit; z++) v += r.logits[z * part + i];
     lg[i] = v;
   }
-  for (int i = tid; i < E; i += blockDim.x) cnt[i] = 0;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const int x = tid + i * blockDim.x;
+    if (x < E) {
+      us_s[0][x] = ua[i];
+      us_s[1][x] = ub[i];
+      gen_s[x] = ga[i] != 0;
+    }
+    const int idx = tid + i * blockDim.x;
+    if (idx < nx8)  // x row idx / c8n, 8-element chunk idx % c8n (row stride K)
+      *reinterpret_cast<uint4*>(reinterpret_cast<half_t*>(dsm) + 8 * (size_t)idx) = bf16x8_to_half_interleaved(xv[i]);
+  }
+  for (int i = tid; i < E; i += blockDim.x) {
+    cnt[i] = 0;
+    tokmask[i] = 0u;
+  }
   __syncthreads();
   // 2. top-k and combine weights, a wave per token, with the expert counts
   for (int t = wave; t < T; t += nwaves) topk_token<NK>(lg + t * E, E, k, ids_s + t * k, w_s + t * k, cnt);
@@ -475,40 +512,37 @@ __global__ __launch_bounds__(64 * kDecWavesMax) void decode_gate_up_kernel(const
   //    expert is exactly one tile (at most T <= block_m pairs each), tile i
   //    the i-th touched expert in ascending order, so the counts name it
   const int nb16 = p.N / 16;
-  const bool one_pass = p.K / 64 <= nwaves * SPW;
+  const bool one_pass = K / 64 <= nwaves * SPW;
   Frag16<SPW> fa, fb;
   if (one_pass) {
-    uint64_t tmask[NK];
-    int ntiles = 0;
     const int lane = tid & 63;
+    int t = blockIdx.x / nb16, e0 = -1;
 #pragma unroll
     for (int i = 0; i < NK; i++) {
-      const int e = 64 * i + lane;
-      tmask[i] = __ballot(e < E && cnt[e] > 0);
-      ntiles += __popcll(tmask[i]);
-    }
-    const int it0 = blockIdx.x;
-    if (it0 < ntiles * nb16) {
-      int t = it0 / nb16, e0 = 0;
-#pragma unroll
-      for (int i = 0; i < NK; i++) {
-        const int c = __popcll(tmask[i]);
-        if (t >= 0 && t < c) {
-          uint64_t w = tmask[i];
-          for (int n = 0; n < t; n++) w &= w - 1;
-          e0 = 64 * i + __builtin_ctzll(w);
-        }
-        t -= c;
+      const uint64_t m = __ballot(64 * i + lane < E && cnt[64 * i + lane] > 0);
+      const int c = __popcll(m);
+      if (e0 < 0 && t < c) {
+        uint64_t w = m;
+        for (int n = 0; n < t; n++) w &= w - 1;
+        e0 = 64 * i + __builtin_ctzll(w);
       }
-      fa = g16_load<SPW>(p, e0, it0 % nb16, 0);
+      t -= c;
+    }
+    if (e0 >= 0) {
+      fa = g16_load<SPW>(p, e0, blockIdx.x % nb16, 0);
       asm volatile("" ::: "memory");  // keep the loads here, ahead of the build
     }
   }
   // 4. offsets, scatter and block map
-  if (wave == 0) small_build(ids_s, cnt, next, P, E, kGemvMaxTokens, nullptr, off_s, sp_s, ps_s, blk_s, nb_s,
-                              min(p.max_blocks, kSmallMaxBlocks));
+  decode_build_wg(ids_s, cnt, tokmask, wsc, P, E, k, off_s, sp_s, ps_s, blk_s, nb_s,
+                  min(p.max_blocks, kSmallMaxBlocks));
   __syncthreads();
-  // 5. workgroup 0 publishes the routing
+  // 5. the (tile, column block) items of this workgroup: blockIdx.x, then
+  //    every gridDim.x-th after it (the grid is at most what the chip holds
+  //    at once, so the routing above runs once per workgroup)
+  const int items = nb_s[0] * nb16;
+  const int G = gridDim.x;
+  // 6. workgroup 0 publishes the routing
   if (blockIdx.x == 0) {
     for (int i = tid; i < P; i += blockDim.x) {
       r.ids[i] = ids_s[i];
@@ -523,43 +557,52 @@ __global__ __launch_bounds__(64 * kDecWavesMax) void decode_gate_up_kernel(const
     if (r.ksplit > 1)
       for (int i = tid; i < T * E; i += blockDim.x) r.logits_out[i] = lg[i];
   }
-  __syncthreads();  // lg is overwritten by the activation stage below
-  // 6. the (tile, column block) items of this workgroup: blockIdx.x, then
-  //    every gridDim.x-th after it (the grid is at most what the chip holds
-  //    at once, so the routing above runs once per workgroup)
-  const int items = nb_s[0] * nb16;
-  const int G = gridDim.x;
+  if (!p.x_res) __syncthreads();  // lg is overwritten by the activation stage below
   if (!one_pass) {  // more than one pass per item
     for (int it = blockIdx.x; it < items; it += G) {
       const int tile = it / nb16;
-      gemv_tile16<SPW>(p, sp_s, blk_s[3 * tile], blk_s[3 * tile + 1], blk_s[3 * tile + 2], it % nb16, dsm);
+      const int e = blk_s[3 * tile];
+      gemv_tile16<SPW>(p, sp_s, e, blk_s[3 * tile + 1], blk_s[3 * tile + 2], it % nb16, dsm, gen_s[e] != 0,
+                       us_s[0][e], us_s[1][e]);
     }
     return;
   }
   // one pass per item: the next item's weight loads are issued before this
-  // item's multiplies (two fragment sets, alternating; the first item's set
-  // was issued before the block map)
+  // item's multiplies (two fragment sets, alternating)
   int it = blockIdx.x;
+  const int c = tid & 15;
   while (it < items) {
 #pragma unroll
     for (int half = 0; half < 2; half++) {
       const int tile = it / nb16, b16 = it % nb16;
       const int e = blk_s[3 * tile], row0 = blk_s[3 * tile + 1], rows = blk_s[3 * tile + 2];
       const int nx = it + G;
-      g16_stage<SPW>(p, sp_s, row0, rows, 0, dsm);
-      // this item's fragments (issued an item ago) and x rows have landed;
-      // the multiplies below then wait for nothing issued after this point
+      int xrow_c = -1;  // this lane's tile row: its token, or -1 past the tile
+      if (p.x_res) {
+        const int pair = c < rows ? sp_s[row0 + c] : -1;
+        xrow_c = (pair >= 0 && pair < P) ? pair / k : -1;
+      } else {
+        g16_stage<SPW>(p, sp_s, row0, rows, 0, dsm);
+      }
+      // this item's fragments (issued an item ago) and any staged x rows
+      // have landed; the multiplies below then wait for nothing issued
+      // after this point
       wait_vm<0>();
       if (nx < items) {
         if (half == 0) fb = g16_load<SPW>(p, blk_s[3 * (nx / nb16)], nx % nb16, 0);
         else fa = g16_load<SPW>(p, blk_s[3 * (nx / nb16)], nx % nb16, 0);
       }
-      __syncthreads();
+      if (!p.x_res) __syncthreads();
       floatx4_t acc[2] = {floatx4_t{}, floatx4_t{}};
-      if ((p.t0.general[e] | p.t1.general[e]) != 0) g16_mma<SPW, true>(p, half == 0 ? fa : fb, rows, 0, acc, dsm);
-      else g16_mma<SPW, false>(p, half == 0 ? fa : fb, rows, 0, acc, dsm);
-      __syncthreads();
-      g16_epilogue(p, acc, row0, rows, b16, dsm, p.t0.unscale[e], p.t1.unscale[e]);
+      if (p.x_res) {
+        if (gen_s[e]) g16_mma_res<SPW, true>(p, half == 0 ? fa : fb, xrow_c, acc, dsm);
+        else g16_mma_res<SPW, false>(p, half == 0 ? fa : fb, xrow_c, acc, dsm);
+      } else {
+        if (gen_s[e]) g16_mma<SPW, true>(p, half == 0 ? fa : fb, rows, 0, acc, dsm);
+        else g16_mma<SPW, false>(p, half == 0 ? fa : fb, rows, 0, acc, dsm);
+        __syncthreads();
+      }
+      g16_epilogue(p, acc, row0, rows, b16, dsm, us_s[0][e], us_s[1][e]);
       it = nx;
       if (it >= items) break;
     }
@@ -592,8 +635,11 @@ __global__ __launch_bounds__(64 * kDecWavesMax) void decode_down_kernel(
     const DecParams p, const int32_t* __restrict__ ids, const int32_t* __restrict__ pair_slot,
     float* __restrict__ y, const uint16_t* __restrict__ residual, uint16_t* __restrict__ out) {
   extern __shared__ __attribute__((aligned(16))) char dsm[];
-  __shared__ int e_s[16], slot_s[16], gen_s[16], em_s[16];
+  __shared__ int e_s[16], slot_s[16];
   __shared__ float w_s[16], v_s[16 * 16];
+  __shared__ float us_s[256];  // every expert's 2^-c and dequantisation form
+  __shared__ int genx_s[256];
+  __shared__ __attribute__((aligned(16))) half_t zrow[16];  // zeros: the MFMA's rows other than 0
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nwaves = blockDim.x >> 6;
@@ -606,76 +652,122 @@ __global__ __launch_bounds__(64 * kDecWavesMax) void decode_down_kernel(
   // (at red_off) = row 0 of each wave's partial per choice [wave][k][16]
   half_t* xs = reinterpret_cast<half_t*>(dsm);
   float* red = reinterpret_cast<float*>(dsm + p.red_off);
-  // the token's choices: expert, slot and combine weight, read once (a
-  // malformed id is replaced by 0 and a malformed slot skipped, never used
-  // out of bounds)
-  if (tid < k) {
-    const int pair = t * k + tid;
-    const int e = ids[pair], slot = pair_slot[pair];
-    const int ec = (e >= 0 && e < p.E) ? e : 0;
-    e_s[tid] = ec;
-    slot_s[tid] = (slot >= 0 && slot < p.P) ? slot : -1;
-    // the largest exponent of the slot's h row (its blocks are brought to it
-    // while staged); the routing weight times the expert's 2^-c and 2^that;
-    // the expert's dequantisation form
-    int em = 0;
-    if (slot >= 0 && slot < p.P) {
-      const uint32_t* er = reinterpret_cast<const uint32_t*>(p.hexp + (size_t)slot * (K / 16));
-      em = -128;
-      for (int b = 0; b < K / 64; b++) em = max(em, max_i8x4(er[b]));
-    }
-    em_s[tid] = em;
-    w_s[tid] = ldexpf(p.topk_weights[pair] * p.t0.unscale[ec], em);
-    gen_s[tid] = p.t0.general[ec] != 0;
+  // the token's choices (expert, slot and combine weight) and every
+  // expert's 2^-c and dequantisation form, read in one round trip with
+  // clamped indices, no branches (a malformed id is replaced by 0 and a
+  // malformed slot skipped, never used out of bounds); blockDim.x >= 128 and
+  // E <= 256
+  float ut[2];
+  int gt[2];
+#pragma unroll
+  for (int i = 0; i < 2; i++) {
+    const int x = min(tid + i * (int)blockDim.x, p.E - 1);
+    ut[i] = p.t0.unscale[x];
+    gt[i] = p.t0.general[x] != 0;
   }
+  const int pair = t * k + min(tid, k - 1);
+  const int e = ids[pair], slot = pair_slot[pair];
+  const float wt = p.topk_weights[pair];
+#pragma unroll
+  for (int i = 0; i < 2; i++) {
+    const int x = tid + i * blockDim.x;
+    if (x < p.E) {
+      us_s[x] = ut[i];
+      genx_s[x] = gt[i];
+    }
+  }
+  if (tid < k) {
+    e_s[tid] = (e >= 0 && e < p.E) ? e : 0;
+    slot_s[tid] = (slot >= 0 && slot < p.P) ? slot : -1;
+    w_s[tid] = wt;
+  }
+  if (tid < 8) reinterpret_cast<uint32_t*>(zrow)[tid] = 0u;
   __syncthreads();
+  // lane j < k of every wave holds choice j's expert, slot and 2^-c, read
+  // once; choice j's values are taken from lane j (uniform), its
+  // dequantisation form is bit j of gmask
+  const int jl = lane < k ? lane : 0;
+  const int e_l = e_s[jl], slot_l = max(slot_s[jl], 0);
+  const float us_l = us_s[e_l];
+  const uint64_t gmask = __ballot(lane < k && genx_s[e_l] != 0);
   const int s = wave;  // this wave's slab (nwaves == S)
   const int g = (64 * s + 32 * khalf) >> p.log2_G;
   for (int j0 = 0; j0 < k; j0 += kDownChunk) {
     const int nj = min(kDownChunk, k - j0);
-    // 1. codes (two words) and (scale, bias) word of every choice of the chunk
+    // 1. the chunk's h rows, 16 bytes per thread (nj * K / 8 <= 64 * S
+    //    threads), requested first: their LDS write then waits for them
+    //    alone, not for the weights requested after them
+    const int c8n = K / 8;
+    const bool stager = tid < nj * c8n;
+    const int hm = stager ? tid / c8n : 0, hc8 = stager ? tid % c8n : 0;
+    uint4 hv = make_uint4(0, 0, 0, 0);
+    if (stager) hv = *reinterpret_cast<const uint4*>(p.a + (size_t)max(slot_s[j0 + hm], 0) * K + 8 * hc8);
+    // 2. codes (two words) and (scale, bias) word of every choice of the
+    //    chunk, and the exponents of the slab's four 16-column blocks of its
+    //    h row (one word: a scalar load)
     uint2 q[kDownChunk];
-    uint32_t sb[kDownChunk];
+    uint32_t sb[kDownChunk], hx[kDownChunk];
 #pragma unroll
     for (int j = 0; j < kDownChunk; j++) {
-      const int e = j < nj ? e_s[j0 + j] : 0;
-      const size_t bidx = (size_t)e * nbl + (b16 >> 1);
+      const int jj = min(j0 + j, k - 1);
+      const int ej = __builtin_amdgcn_readlane(e_l, jj);
+      const int sl = __builtin_amdgcn_readlane(slot_l, jj);
+      const size_t bidx = (size_t)ej * nbl + (b16 >> 1);
       q[j] = *reinterpret_cast<const uint2*>(p.b0.words + ((bidx >> 2) * S * 4 + (bidx & 3)) * 256 +
                                              4 * (2 * col + khalf) + 2 * qh + (size_t)s * 1024);
       sb[j] = p.b0.sb[(bidx >> 2) * gpr * 128 + (bidx & 3) * 32 + col + (size_t)g * 128];
+      hx[j] = reinterpret_cast<const uint32_t*>(p.hexp + (size_t)sl * (K / 16))[s];
     }
-    // 2. the chunk's h rows into LDS, 16 bytes per thread and step
-    const int c8n = K / 8;
-    for (int idx = tid; idx < nj * c8n; idx += blockDim.x) {
-      const int m = idx / c8n, c8 = idx % c8n;
-      const int slot = max(slot_s[j0 + m], 0);
-      const uint4 v = *reinterpret_cast<const uint4*>(p.a + (size_t)slot * K + 8 * c8);
-      const int d = p.hexp[(size_t)slot * (K / 16) + c8 / 2] - em_s[j0 + m];
-      *reinterpret_cast<uint4*>(xs + m * K + 8 * c8) = d ? scale_half8(v, d) : v;
-    }
+    if (stager) *reinterpret_cast<uint4*>(xs + hm * K + 8 * hc8) = hv;
     __syncthreads();
-    // 3. per choice: dequantise, multiply, keep row 0
+    // 3. per choice: dequantise, multiply, keep row 0 (lanes with c == 0
+    //    read the h fragment, the others the zero row).  The slab's blocks
+    //    are brought to their largest exponent es (skipped when all four are
+    //    0, the usual case) and the partial scaled by 2^es and the expert's
+    //    2^-c (powers of two: exact in fp32 short of its range)
+    const half_t* xrow = c == 0 ? xs + 64 * s + 32 * khalf + 16 * qh : zrow;
+    const int xstride = c == 0 ? K : 0;
+    auto run = [&](auto gen_tag) {
+      constexpr bool ANY_GEN = decltype(gen_tag)::value;
 #pragma unroll
-    for (int j = 0; j < kDownChunk; j++) {
-      if (j >= nj) break;
-      floatx4_t acc = floatx4_t{};
-      auto multiply = [&](auto gen_tag) {
-        constexpr bool GEN = decltype(gen_tag)::value;
-        const SbPair sp = sb_unpack(sb[j], GEN);
+      for (int j = 0; j < kDownChunk; j++) {
+        if (j >= nj) break;
+        u32x4 xf[2];
 #pragma unroll
-        for (int m = 0; m < 2; m++) {
-          const u32x4 x = c == 0 ? *reinterpret_cast<const u32x4*>(xs + j * K + 64 * s + 32 * khalf + 16 * qh + 8 * m)
-                                 : u32x4{0, 0, 0, 0};
-          const uint32_t w = m == 0 ? q[j].x : q[j].y;
-          const uint4 d = GEN ? dequant_word_gen(w, sp.s2, sp.c2, sp.b2) : dequant_word(w, sp.s2, sp.c2);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, x),
-                                                       __builtin_bit_cast(half8_t, d), acc, 0, 0, 0);
+        for (int m = 0; m < 2; m++) xf[m] = *reinterpret_cast<const u32x4*>(xrow + j * xstride + 8 * m);
+        const uint32_t hw = hx[j];
+        int es = 0;
+        if (hw) {
+          es = max_i8x4(hw);
+          // the exponent of the block this lane's h values come from
+          const int d = (int)(int8_t)(hw >> (8 * (2 * khalf + qh))) - es;
+#pragma unroll
+          for (int m = 0; m < 2; m++) xf[m] = __builtin_bit_cast(u32x4, scale_half8(__builtin_bit_cast(uint4, xf[m]), d));
         }
-      };
-      if (gen_s[j0 + j]) multiply(std::true_type{});
-      else multiply(std::false_type{});
-      if (lane < 16) red[(wave * k + j0 + j) * 16 + lane] = acc[0];
-    }
+        floatx4_t acc = floatx4_t{};
+        auto multiply = [&](auto g_tag) {
+          constexpr bool GEN = decltype(g_tag)::value;
+          const SbPair sp = sb_unpack(sb[j], GEN);
+#pragma unroll
+          for (int m = 0; m < 2; m++) {
+            const uint32_t w = m == 0 ? q[j].x : q[j].y;
+            const uint4 dq = GEN ? dequant_word_gen(w, sp.s2, sp.c2, sp.b2) : dequant_word(w, sp.s2, sp.c2);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, xf[m]),
+                                                         __builtin_bit_cast(half8_t, dq), acc, 0, 0, 0);
+          }
+        };
+        if constexpr (ANY_GEN) {
+          if ((gmask >> (j0 + j)) & 1) multiply(std::true_type{});
+          else multiply(std::false_type{});
+        } else {
+          multiply(std::false_type{});
+        }
+        const float us = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(us_l), j0 + j));
+        if (lane < 16) red[(wave * k + j0 + j) * 16 + lane] = ldexpf(acc[0] * us, es);
+      }
+    };
+    if ((gmask >> j0) & ((1ull << nj) - 1)) run(std::true_type{});
+    else run(std::false_type{});
     __syncthreads();  // the next chunk overwrites xs
   }
   // 4. the weighted rows (one thread per choice and column), then their sum
@@ -742,9 +834,8 @@ hipError_t launch_w4_gemv(const GemmArgs& a, hipStream_t s) {
   if (a.mode == MOE_GEMM_GATE_UP_SWIGLU) {
     if (wide) w4_gemv_kernel<MOE_GEMM_GATE_UP_SWIGLU, 4><<<grid, 64 * waves, lds, s>>>(p);
     else w4_gemv_kernel<MOE_GEMM_GATE_UP_SWIGLU, 2><<<grid, 64 * waves, lds, s>>>(p);
-  } else if (a.pack24) {
-    if (wide) w4_gemv_kernel<MOE_GEMM_DOWN, 4, true><<<grid, 64 * waves, lds, s>>>(p);
-    else w4_gemv_kernel<MOE_GEMM_DOWN, 2, true><<<grid, 64 * waves, lds, s>>>(p);
+  } else if (a.y16e) {
+    return hipErrorInvalidValue;  // the decode path keeps the weighted outputs in fp32
   } else {
     if (wide) w4_gemv_kernel<MOE_GEMM_DOWN, 4><<<grid, 64 * waves, lds, s>>>(p);
     else w4_gemv_kernel<MOE_GEMM_DOWN, 2><<<grid, 64 * waves, lds, s>>>(p);
@@ -784,20 +875,37 @@ hipError_t launch_decode_gate_up(const DecodeRouting& dr, const GemmArgs& a, hip
   // per CU) when K allows it: fewer waves to launch, the same bytes in flight
   const int spw = a.K >= 1024 ? 4 : 2;
   const GemvShape sh{spw, std::max(1, std::min(kDecWavesMax, a.K / (64 * spw)))};
-  // LDS: the logits, then (reused) the activation rows of one pass; the
-  // waves' partial sums of both banks (rows 0..7 of 16 columns)
-  const int xs_bytes = std::max(kGemvMaxTokens * sh.waves * sh.spw * 64 * 2, a.T * a.E * 4);
-  const int xs_al = (xs_bytes + 15) & ~15;
-  const size_t lds = (size_t)xs_al + (size_t)sh.waves * 2 * 4 * 32 * 4;
-  const DecParams p = dec_params(a, P, max_blocks, xs_al);
+  // LDS, one pass with every x row resident (x_res): the T x rows, the
+  // logits, the waves' partial sums of both banks (rows 0..7 of 16 columns);
+  // otherwise the logits, then (reused) the activation rows of one pass, and
+  // the partial sums
+  const int red_bytes = sh.waves * 2 * 4 * 32 * 4;
+  const int lg_bytes = (a.T * a.E * 4 + 15) & ~15;
+  const int xres_bytes = (a.T * a.K * 2 + 15) & ~15;
+  const bool one_pass = a.K <= sh.waves * sh.spw * 64;
+  const bool x_res = one_pass && xres_bytes + lg_bytes + red_bytes <= 64 * 1024;
+  int red_off, lg_off;
+  if (x_res) {
+    lg_off = xres_bytes;
+    red_off = xres_bytes + lg_bytes;
+  } else {
+    const int xs_bytes = std::max(kGemvMaxTokens * sh.waves * sh.spw * 64 * 2, a.T * a.E * 4);
+    lg_off = 0;
+    red_off = (xs_bytes + 15) & ~15;
+  }
+  const size_t lds = (size_t)red_off + red_bytes;
+  DecParams p = dec_params(a, P, max_blocks, red_off);
+  p.lg_off = lg_off;
+  p.x_res = x_res;
   const DecRouteParams r{dr.logits, dr.logits_out, dr.ksplit, a.T,
                          dr.ids, dr.w, dr.counts, dr.offsets, dr.sorted_pairs, dr.pair_slot,
                          dr.blocks, dr.num_blocks};
   const bool wide = sh.spw == 4;
   const int threads = 64 * sh.waves;
-  // at most one round of workgroups (4 waves per SIMD, LDS permitting):
+  // at most one round of workgroups (4 waves per SIMD, LDS permitting, with
+  // about 10 KiB of static LDS per workgroup):
   // the routing then runs once per workgroup
-  const int per_cu = std::max(1, std::min<int>(16 / sh.waves, (int)((160 * 1024) / (lds + 8 * 1024))));
+  const int per_cu = std::max(1, std::min<int>(16 / sh.waves, (int)((160 * 1024) / (lds + 12 * 1024))));
   const int64_t grid = std::min<int64_t>(max_items, (int64_t)device_cus() * per_cu);
   switch ((a.E + 63) / 64) {
     case 1: launch_decode_nk<1>(r, p, wide, grid, threads, lds, s); break;

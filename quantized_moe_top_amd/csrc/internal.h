@@ -204,26 +204,36 @@ __device__ __forceinline__ void lds_wait(u32x4& a, u32x4& b) {
   asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b));
 }
 
-// Packed 24-bit values ("y24"): the top 3 bytes of an fp32 pattern after
-// rounding the low byte off to nearest, ties away from zero (sign, 8
-// exponent bits, 15 mantissa bits: relative error at most 2^-16), 4 values
-// in 12 bytes, little-endian.  Used for the weighted expert outputs between
-// the down projection and the combine inside the layer.
-// Adding 0x80 to the sign-magnitude pattern rounds the magnitude at bit 8
-// (a carry into the exponent is the correct rounding up; past the largest
-// finite value it gives infinity).
-__device__ __forceinline__ uint32_t round24_bits(float v) { return __float_as_uint(v) + 0x80u; }
-// Bytes 1..3 of each rounded pattern, concatenated: three byte permutes.
-__device__ __forceinline__ uint3 pack24x4(float a, float b, float c, float d) {
-  const uint32_t r0 = round24_bits(a), r1 = round24_bits(b), r2 = round24_bits(c), r3 = round24_bits(d);
-  // v_perm_b32(hi, lo, sel): selector byte i picks byte sel_i of {lo: 0-3, hi: 4-7}
-  return make_uint3(__builtin_amdgcn_perm(r1, r0, 0x05030201u), __builtin_amdgcn_perm(r2, r1, 0x06050302u),
-                    __builtin_amdgcn_perm(r3, r2, 0x07060503u));
+// Block floating point for the weighted expert outputs between the down
+// projection and the combine inside the layer ("y16e"): per row, each block
+// of 16 consecutive values shares one exponent E (int8) and each value is an
+// int16 mantissa q, value = q * 2^E.  E puts the block's largest |v| in
+// [2^14, 2^15) * 2^E, so that value keeps 15 bits (relative error at most
+// 2^-16) and every other value of the block an absolute error of at most
+// 2^(E-1); 2 + 1/16 bytes a value.  An all-zero block has E = -128.
+__device__ __forceinline__ int y16_exp(float m) {
+  if (!(m > 0.0f)) return -128;
+  int ex;
+  frexpf(m, &ex);  // m in [2^(ex-1), 2^ex)
+  return max(-128, min(127, ex - 15));
 }
-__device__ __forceinline__ float4 unpack24x4(uint3 w) {
-  return make_float4(__uint_as_float(w.x << 8), __uint_as_float(((w.x >> 16) & 0x0000FF00u) | (w.y << 16)),
-                     __uint_as_float(((w.y >> 8) & 0x00FFFF00u) | (w.z << 24)),
-                     __uint_as_float(w.z & 0xFFFFFF00u));
+// Four values of one block -> four int16 mantissas (8 bytes), nearest.
+__device__ __forceinline__ uint2 y16_pack4(float a, float b, float c, float d, int E) {
+  auto q = [E](float v) {
+    const float r = __builtin_rintf(ldexpf(v, -E));
+    return (uint32_t)(int)fminf(fmaxf(r, -32767.0f), 32767.0f) & 0xFFFFu;
+  };
+  return make_uint2(q(a) | (q(b) << 16), q(c) | (q(d) << 16));
+}
+// Eight int16 mantissas (16 bytes) of one block times 2^E, exact.
+__device__ __forceinline__ void y16_unpack8(uint4 m, int E, float* out) {
+  const float f = ldexpf(1.0f, E);
+  const uint32_t w[4] = {m.x, m.y, m.z, m.w};
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    out[2 * i] = (float)(int)(int16_t)(w[i] & 0xFFFFu) * f;
+    out[2 * i + 1] = (float)(int)(int16_t)(w[i] >> 16) * f;
+  }
 }
 
 // fp32 -> bf16 bits, round to nearest, ties to even (finite values).
@@ -254,6 +264,15 @@ __device__ __forceinline__ int h_block_exp(float m) {
   int ex;
   frexpf(m, &ex);                // m in [2^(ex-1), 2^ex)
   return max(-128, min(127, ex - 15));
+}
+// The largest v over each 16-lane DPP row (four row rotations; every lane
+// of the row gets it, so all 16 lanes must be active).
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x121, 0xF, 0xF, true)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x122, 0xF, 0xF, true)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x124, 0xF, 0xF, true)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xF, 0xF, true)));
+  return v;
 }
 // The largest of the four signed bytes of w.
 __device__ __forceinline__ int max_i8x4(uint32_t w) {
@@ -337,7 +356,7 @@ struct GemmArgs {
   const int32_t* blocks;
   const int32_t* num_blocks;
   void* out;
-  bool pack24 = false;       // down: out is packed 24-bit [P][N] instead of fp32
+  bool y16e = false;       // down: out is y16e mantissas [P][N] (exponents at yexp) instead of fp32
   int64_t grid_tiles = -1;   // >= 0: exact tile count known on the host (grid sized to it)
   bool dense = false;        // banks hold expanded fp16 weights (moe_w4_expand layout), words only
   BankTail t0{}, t1{};       // the tails of the packed (scale, bias) buffers of b0 and b1
@@ -346,6 +365,7 @@ struct GemmArgs {
   // read by down
   int8_t* hexp = nullptr;
   int32_t* tflags = nullptr;
+  int8_t* yexp = nullptr;    // down with y16e: the exponents [P][N / 16]
 };
 hipError_t launch_w4_mfma(const GemmArgs& a, hipStream_t s);
 hipError_t launch_w4_gemv(const GemmArgs& a, hipStream_t s);
@@ -375,9 +395,10 @@ hipError_t launch_decode_down(const GemmArgs& a, const int32_t* ids, const int32
                               uint16_t* out = nullptr);
 
 // S8: y[t] = sum_j y_sorted[pair_slot[t * k + j]], j ascending; y_sorted
-// fp32, or packed 24-bit when pack24.
+// fp32 (yexp == nullptr), or block floating point: int16 mantissas [P][H]
+// with exponents yexp [P][H / 16] (y16e above).
 // With out (bf16 [T][H]): also out = bf16(residual + y) (residual bf16 [T][H]).
-hipError_t launch_combine(const void* y_sorted, bool pack24, const int32_t* pair_slot, float* y,
+hipError_t launch_combine(const void* y_sorted, const int8_t* yexp, const int32_t* pair_slot, float* y,
                           int T, int H, int k, hipStream_t s, const uint16_t* residual = nullptr,
                           uint16_t* out = nullptr);
 

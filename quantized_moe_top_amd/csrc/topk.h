@@ -99,80 +99,84 @@ __device__ void topk_token(const float* l, int E, int k, int32_t* ids, float* w,
 }
 
 
-// S2-S5 for at most kSmallPairs pairs, by the 64 lanes of one wave (the
-// caller runs it on one wave only), with no block-wide scan.  ids: the P
-// expert ids in pair order; cnt: the E expert counts (LDS, both filled by
-// the caller); next: LDS scratch of E ints.  Outputs through generic
-// pointers (LDS or global), counts only when non-null; no block-map entry
-// at or past max_tiles (and no slot past P) is written:
-//   - exclusive prefix sums over the E <= 256 experts (4 consecutive experts
-//     per lane, then a wave prefix sum): offsets, and the first tile of each
-//     expert for the block map;
-//   - the stable scatter of the pairs in order, 64 at a time: lanes with the
-//     same expert are matched with ballots over the expert-id bits, and a
-//     lane's slot is its expert's next free slot plus the number of matching
-//     lanes below it (a counting sort that keeps pair order in each expert).
-__device__ __forceinline__ void small_build(const int32_t* ids, const int* cnt, int* next, int P, int E,
-                                            int block_m, int32_t* counts, int32_t* offsets, int32_t* sorted_pairs,
-                                            int32_t* pair_slot, int32_t* blocks, int32_t* num_blocks,
-                                            int max_tiles) {
-  const int lane = threadIdx.x & 63;
-  // expert e = 4 lane + i
-  int c[4], tl[4], cs = 0, ts = 0;
-#pragma unroll
-  for (int i = 0; i < 4; i++) {
-    const int e = 4 * lane + i;
-    c[i] = e < E ? cnt[e] : 0;
-    tl[i] = (c[i] + block_m - 1) / block_m;
-    cs += c[i];
-    ts += tl[i];
+// S2-S5 at decode sizes by a whole workgroup, in three phases separated by
+// barriers (the caller's barrier ends the third).  ids: the P <= kSmallPairs
+// expert ids in pair order p = t * k + j, T <= block_m tokens, every token
+// choosing distinct experts; cnt: the E <= 256 expert counts; tokmask: LDS,
+// E words, zero on entry; wsc: LDS, 8 ints.  So each expert holds at most
+// block_m pairs: one tile.  Outputs (LDS): offsets[0..E], the stable scatter
+// (sorted_pairs, pair_slot), the block map (at most max_tiles tiles, in
+// expert order) and its tile count.
+//   A. per pair, the token's bit in its expert's token mask; per 64-expert
+//      chunk (one wave), the inclusive prefix of the counts and a ballot of
+//      the touched experts, the chunk's totals to wsc;
+//   B. per expert, its offset (the chunks before it plus the prefix) and,
+//      when touched, its tile (the touched experts before it);
+//   C. per pair, its slot: the expert's offset plus the tokens before it
+//      that chose the same expert (pair order within an expert is token
+//      order), which is the stable counting sort.
+__device__ __forceinline__ void decode_build_wg(const int32_t* ids, const int* cnt, uint32_t* tokmask,
+                                                int* wsc, int P, int E, int k, int32_t* offsets,
+                                                int32_t* sorted_pairs, int32_t* pair_slot, int32_t* blocks,
+                                                int32_t* num_blocks, int max_tiles) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), nwaves = blockDim.x >> 6;
+  const int nch = (E + 63) / 64;
+  for (int p = tid; p < P; p += blockDim.x) {
+    const int e = ids[p];
+    if (e >= 0 && e < E) atomicOr(&tokmask[e], 1u << (p / k));
   }
-  int off = wave_inclusive_sum(cs) - cs, tile = wave_inclusive_sum(ts) - ts;
+  int incl[4] = {0, 0, 0, 0};
+  uint64_t touched[4] = {0, 0, 0, 0};
 #pragma unroll
   for (int i = 0; i < 4; i++) {
-    const int e = 4 * lane + i;
-    if (e < E) {
-      if (counts) counts[e] = c[i];
-      offsets[e] = off;
-      next[e] = off;
-      for (int j = 0; j < tl[i] && tile + j < max_tiles; j++) {
-        int32_t* blk = blocks + 3 * (size_t)(tile + j);
-        blk[0] = e;
-        blk[1] = off + j * block_m;
-        blk[2] = min(block_m, c[i] - j * block_m);
-      }
+    const int c = wave + i * nwaves;
+    if (c >= nch) break;
+    const int e = 64 * c + lane;
+    const int n = e < E ? cnt[e] : 0;
+    incl[i] = wave_inclusive_sum(n);
+    touched[i] = __ballot(n > 0);
+    if (lane == 63) {
+      wsc[c] = incl[i];
+      wsc[4 + c] = __popcll(touched[i]);
     }
-    off += c[i];
-    tile += tl[i];
   }
-  if (lane == 63) {
+  __syncthreads();
+  int ntiles = 0;
+  for (int c = 0; c < nch; c++) ntiles += wsc[4 + c];
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const int c = wave + i * nwaves;
+    if (c >= nch) break;
+    const int e = 64 * c + lane;
+    int base = 0, tbase = 0;
+    for (int c2 = 0; c2 < c; c2++) {
+      base += wsc[c2];
+      tbase += wsc[4 + c2];
+    }
+    const int n = e < E ? cnt[e] : 0;
+    const int off = base + incl[i] - n;
+    if (e < E) offsets[e] = off;
+    const int tile = tbase + __popcll(touched[i] & ((1ull << lane) - 1ull));
+    if (n > 0 && tile < max_tiles) {
+      blocks[3 * tile] = e;
+      blocks[3 * tile + 1] = off;
+      blocks[3 * tile + 2] = n;
+    }
+  }
+  if (tid == 0) {
     offsets[E] = P;
-    num_blocks[0] = min(tile, max_tiles);  // total tiles (inclusive sum of the last lane)
+    num_blocks[0] = min(ntiles, max_tiles);
   }
-  wave_lds_sync();
-  int bits = 1;
-  while ((1 << bits) < E) bits++;
-  for (int base = 0; base < P; base += 64) {
-    const int q = base + lane;
-    const int id = q < P ? ids[q] : -1;
-    const bool active = id >= 0 && id < E;
-    const int ex = active ? id : 0;
-    uint64_t match = __ballot(active);
-    for (int bt = 0; bt < bits; bt++) {
-      const bool bit = (ex >> bt) & 1;
-      const uint64_t bal = __ballot(bit);
-      match &= bit ? bal : ~bal;
+  __syncthreads();
+  for (int p = tid; p < P; p += blockDim.x) {
+    const int e = ids[p];
+    if (e < 0 || e >= E) continue;
+    const int slot = offsets[e] + __popc(tokmask[e] & ((1u << (p / k)) - 1u));
+    if (slot < P) {
+      sorted_pairs[slot] = p;
+      pair_slot[p] = slot;
     }
-    const uint64_t below = match & ((1ull << lane) - 1ull);
-    const int start = active ? next[ex] : 0;
-    wave_lds_sync();
-    const int slot = start + __popcll(below);
-    if (active && slot < P) {
-      sorted_pairs[slot] = q;
-      pair_slot[q] = slot;
-      if (below == 0) next[ex] = start + __popcll(match);  // lowest lane of its group
-    }
-    wave_lds_sync();
   }
 }
 

@@ -330,9 +330,10 @@ def test_ffn_forward_full(orc, name):
     assert info["path"] == (1 if lay.T <= 8 else 0)
     layer_output_check(orc, lay, y, info)
     # the combine is exactly the fp32 sum, in choice order, of the weighted
-    # expert outputs at each token's slots (packed 24-bit on the MFMA path)
+    # expert outputs at each token's slots (block floating point on the MFMA
+    # path: its values are exact in fp32)
     ys = info["y_sorted"]
-    ys = cpu(ys if ys.dtype == torch.float32 else api.unpack_y24(ys))
+    ys = cpu(ys if ys.dtype == torch.float32 else api.unpack_y16e(ys, info["y_sorted_exp"]))
     ps = cpu(info["pair_slot"]).reshape(lay.T, lay.k)
     acc = np.zeros((lay.T, lay.H), np.float32)
     for j in range(lay.k):
