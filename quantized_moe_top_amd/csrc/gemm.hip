@@ -68,7 +68,8 @@ struct MfmaParams {
 // G32: group size 32, the two reduction halves of a slab have their own
 // (scale, bias) words; for G >= 64 one word serves both and is copied once.
 // STAGES: depth of the LDS ring (STAGES - 1 slabs in flight); WGS_PER_CU:
-// workgroups meant to share a CU (register budget).
+// workgroups meant to share a CU, passed to the compiler as the waves per
+// SIMD that budget implies (WGS_PER_CU * WAVES / 4).
 // PACK (S7 only): out is y16e block floating point (int16 mantissas, exponents
 // at yexp) instead of fp32.
 // DENSE (the unfused ablation): the banks hold weights already expanded to
@@ -77,7 +78,7 @@ struct MfmaParams {
 // the kernel copies and multiplies them with no dequantisation.
 template <int MODE, int MB, int WAVES, bool G32, int STAGES, int WGS_PER_CU, bool PACK = false,
           bool DENSE = false>
-__global__ __launch_bounds__(64 * WAVES, WGS_PER_CU) void w4_mfma_kernel(const MfmaParams p) {
+__global__ __launch_bounds__(64 * WAVES, WGS_PER_CU * WAVES / 4) void w4_mfma_kernel(const MfmaParams p) {
   constexpr bool GATE_UP = MODE == MOE_GEMM_GATE_UP_SWIGLU;
   constexpr int BM = MB * 32;
   constexpr int kBCols = 64 * WAVES;                     // weight columns per workgroup
@@ -259,43 +260,110 @@ __global__ __launch_bounds__(64 * WAVES, WGS_PER_CU) void w4_mfma_kernel(const M
 
     auto compute = [&](int stage) {
       const char* base = lds + stage * STAGE;
-      u32x4 q[2];
-      half2_t s2[2], b2[2], n2[2];
-      if constexpr (!DENSE) {
-#pragma unroll
-        for (int cb = 0; cb < 2; cb++)
-          q[cb] = *reinterpret_cast<const u32x4*>(base + A_BYTES + (wave * 64 + cb * 32 + col) * 32 +
-                                                  16 * khalf);
-#pragma unroll
-        for (int cb = 0; cb < 2; cb++) {
-          const uint32_t sb = reinterpret_cast<const uint32_t*>(
-              base + A_BYTES + kBStage)[(G32 ? khalf : 0) * kBCols + wave * 64 + cb * 32 + col];
-          sb_pairs(sb, s2[cb], b2[cb]);
-          if constexpr (GEN) n2[cb] = s2[cb] * half2_t{(half_t)-32.0f, (half_t)-32.0f};
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        half8_t bf[2];
-#pragma unroll
-        for (int cb = 0; cb < 2; cb++) {
-          if constexpr (DENSE)
-            bf[cb] = *reinterpret_cast<const half8_t*>(base + A_BYTES + (2 * wave + cb) * 4096 +
-                                                       1024 * i + 16 * (2 * col + khalf));
-          else if constexpr (GEN)
-            bf[cb] = __builtin_bit_cast(half8_t, dequant_word_gen(q[cb][i], s2[cb], n2[cb], b2[cb]));
-          else
-            bf[cb] = __builtin_bit_cast(half8_t, dequant_word(q[cb][i], s2[cb], b2[cb]));
-        }
-#pragma unroll
-        for (int mb = 0; mb < MBA; mb++) {
-          const int r = mb * 32 + col;
-          const half8_t af = *reinterpret_cast<const half8_t*>(
-              base + r * 128 + (((4 * khalf + i) ^ (col & 7)) << 4));
+      if constexpr (DENSE || GATE_UP || WAVES == 8) {
+        // reads placed by the compiler: the expanded weights of the unfused
+        // ablation; 8-wave tiles, whose register budget holds no fragments
+        // ahead; and the gate/up GEMM, where reading ahead measured 3-8%
+        // slower (its 32-slab loop keeps the copy addresses in registers
+        // only without the extra fragments)
+        u32x4 q[2];
+        half2_t s2[2], b2[2], n2[2];
+        if constexpr (!DENSE) {
 #pragma unroll
           for (int cb = 0; cb < 2; cb++)
-            acc[mb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, bf[cb], acc[mb][cb], 0, 0, 0);
+            q[cb] = *reinterpret_cast<const u32x4*>(base + A_BYTES + (wave * 64 + cb * 32 + col) * 32 +
+                                                    16 * khalf);
+#pragma unroll
+          for (int cb = 0; cb < 2; cb++) {
+            const uint32_t sb = reinterpret_cast<const uint32_t*>(
+                base + A_BYTES + kBStage)[(G32 ? khalf : 0) * kBCols + wave * 64 + cb * 32 + col];
+            sb_pairs(sb, s2[cb], b2[cb]);
+            if constexpr (GEN) n2[cb] = s2[cb] * half2_t{(half_t)-32.0f, (half_t)-32.0f};
+          }
         }
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+          half8_t bf[2];
+#pragma unroll
+          for (int cb = 0; cb < 2; cb++) {
+            if constexpr (DENSE)
+              bf[cb] = *reinterpret_cast<const half8_t*>(base + A_BYTES + (2 * wave + cb) * 4096 +
+                                                         1024 * i + 16 * (2 * col + khalf));
+            else if constexpr (GEN)
+              bf[cb] = __builtin_bit_cast(half8_t, dequant_word_gen(q[cb][i], s2[cb], n2[cb], b2[cb]));
+            else
+              bf[cb] = __builtin_bit_cast(half8_t, dequant_word(q[cb][i], s2[cb], b2[cb]));
+          }
+#pragma unroll
+          for (int mb = 0; mb < MBA; mb++) {
+            const int r = mb * 32 + col;
+            const half8_t af = *reinterpret_cast<const half8_t*>(
+                base + r * 128 + (((4 * khalf + i) ^ (col & 7)) << 4));
+#pragma unroll
+            for (int cb = 0; cb < 2; cb++)
+              acc[mb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, bf[cb], acc[mb][cb], 0, 0, 0);
+          }
+        }
+      } else {
+        // the slab's LDS reads are issued ahead, in use order: the two code
+        // blocks, the two (scale, bias) words, then the activation fragments
+        // of the first PD = 2 steps, and at each later step those of step +
+        // 1; step i then waits only until its own fragments have landed (LDS
+        // reads complete in order), instead of a full round trip before
+        // every pair of MFMAs (S7: 255-260 -> 241 us at T = 8192; reading
+        // all four steps ahead gained less, 251)
+        constexpr int PD = 2;
+        u32x4 q[2], af[4][MBA];
+        uint32_t sbw[2];
+#pragma unroll
+        for (int cb = 0; cb < 2; cb++)
+          q[cb] = lds_read16(base + A_BYTES + (wave * 64 + cb * 32 + col) * 32 + 16 * khalf);
+#pragma unroll
+        for (int cb = 0; cb < 2; cb++)
+          sbw[cb] = lds_read4(base + A_BYTES + kBStage + 4 * ((G32 ? khalf : 0) * kBCols + wave * 64 + cb * 32 + col));
+        auto read_a = [&](int i) {
+#pragma unroll
+          for (int mb = 0; mb < MBA; mb++)
+            af[i][mb] = lds_read16(base + (mb * 32 + col) * 128 + (((4 * khalf + i) ^ (col & 7)) << 4));
+        };
+#pragma unroll
+        for (int i = 0; i < PD; i++) read_a(i);
+        half2_t s2[2], b2[2], n2[2];
+        auto step = [&](auto itag) {
+          constexpr int I = decltype(itag)::value;
+          constexpr int LAST = I + PD - 1 < 3 ? I + PD - 1 : 3;  // last step whose fragments are issued
+          if constexpr (I >= 1 && I + PD - 1 <= 3) read_a(I + PD - 1);
+          lds_wait_n<MBA * (LAST - I)>(af[I][0]);
+#pragma unroll
+          for (int mb = 1; mb < MBA; mb++) lds_tie(af[I][mb]);
+          if constexpr (I == 0) {
+#pragma unroll
+            for (int cb = 0; cb < 2; cb++) {
+              lds_tie(q[cb]);
+              lds_tie(sbw[cb]);
+              sb_pairs(sbw[cb], s2[cb], b2[cb]);
+              if constexpr (GEN) n2[cb] = s2[cb] * half2_t{(half_t)-32.0f, (half_t)-32.0f};
+            }
+          }
+          half8_t bf[2];
+#pragma unroll
+          for (int cb = 0; cb < 2; cb++) {
+            if constexpr (GEN)
+              bf[cb] = __builtin_bit_cast(half8_t, dequant_word_gen(q[cb][I], s2[cb], n2[cb], b2[cb]));
+            else
+              bf[cb] = __builtin_bit_cast(half8_t, dequant_word(q[cb][I], s2[cb], b2[cb]));
+          }
+#pragma unroll
+          for (int mb = 0; mb < MBA; mb++)
+#pragma unroll
+            for (int cb = 0; cb < 2; cb++)
+              acc[mb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8_t, af[I][mb]), bf[cb],
+                                                                   acc[mb][cb], 0, 0, 0);
+        };
+        step(IntTag<0>{});
+        step(IntTag<1>{});
+        step(IntTag<2>{});
+        step(IntTag<3>{});
       }
     };
 
@@ -495,15 +563,17 @@ __global__ __launch_bounds__(64 * WAVES, WGS_PER_CU) void w4_mfma_kernel(const M
           a2 = hi1 ? r1 : a2;
           a1 = hi1 ? a1 : r0;
           a3 = hi1 ? a3 : r1;
+          // the block's largest |a w| (the weight is one per row), then the
+          // weight and 2^-E folded into one factor for the packing
           const float w = wr[mb][g];
-          const float v0 = w * a0, v1 = w * a1, v2 = w * a2, v3 = w * a3;
-          float m = fmaxf(fmaxf(fabsf(v0), fabsf(v1)), fmaxf(fabsf(v2), fabsf(v3)));
+          float m = fmaxf(fmaxf(fabsf(a0), fabsf(a1)), fmaxf(fabsf(a2), fabsf(a3)));
           m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0x124, 0xF, 0xF, true)));  // row_ror:4
           m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0x128, 0xF, 0xF, true)));  // row_ror:8
-          const int ex = y16_exp(m);
+          const int ex = y16_exp(m * fabsf(w));
+          const float ws = ex == -128 ? 0.0f : ldexpf(w, -ex);
           if (mb * 32 + 8 * g + 4 * khalf + j4 < rows) {
             *reinterpret_cast<uint2*>(lane_out + (size_t)(mb * 32 + 8 * g) * mstride + cb * 64) =
-                y16_pack4(v0, v1, v2, v3, ex);
+                y16_pack4(a0, a1, a2, a3, ws);
             if ((q & 3) == 0) lane_exp[(size_t)(mb * 32 + 8 * g) * estride + cb * 2] = (int8_t)ex;
           }
         }

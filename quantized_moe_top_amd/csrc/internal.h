@@ -198,6 +198,23 @@ __device__ __forceinline__ u32x4 lds_read16(const void* p) {
   asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(off));
   return v;
 }
+// 4-byte LDS read, hidden the same way.
+__device__ __forceinline__ uint32_t lds_read4(const void* p) {
+  uint32_t v;
+  const uint32_t off = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+  asm volatile("ds_read_b32 %0, %1" : "=v"(v) : "v"(off));
+  return v;
+}
+// Waits until at most N of this wave's LDS reads are outstanding (they
+// complete in issue order); the value passed becomes usable.  lds_tie marks
+// further values as usable from that point on.
+template <int N>
+__device__ __forceinline__ void lds_wait_n(u32x4& a) {
+  static_assert(N >= 0 && N < 16, "lgkmcnt range");
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(a) : "n"(N));
+}
+__device__ __forceinline__ void lds_tie(u32x4& a) { asm volatile("" : "+v"(a)); }
+__device__ __forceinline__ void lds_tie(uint32_t& a) { asm volatile("" : "+v"(a)); }
 // Waits for every LDS read of this wave; the values passed become usable.
 __device__ __forceinline__ void lds_wait(u32x4& a) { asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a)); }
 __device__ __forceinline__ void lds_wait(u32x4& a, u32x4& b) {
@@ -207,23 +224,25 @@ __device__ __forceinline__ void lds_wait(u32x4& a, u32x4& b) {
 // Block floating point for the weighted expert outputs between the down
 // projection and the combine inside the layer ("y16e"): per row, each block
 // of 16 consecutive values shares one exponent E (int8) and each value is an
-// int16 mantissa q, value = q * 2^E.  E puts the block's largest |v| in
-// [2^14, 2^15) * 2^E, so that value keeps 15 bits (relative error at most
-// 2^-16) and every other value of the block an absolute error of at most
-// 2^(E-1); 2 + 1/16 bytes a value.  An all-zero block has E = -128.
+// int16 mantissa q, value = q * 2^E.  E puts the block's largest |v| times
+// (1 + 2^-15) in [2^14, 2^15) * 2^E, so that value keeps 15 bits (relative
+// error at most 2^-16), no mantissa rounds beyond 32767, and every other
+// value of the block has an absolute error of at most 2^(E-1); 2 + 1/16
+// bytes a value.  An all-zero block has E = -128.
 __device__ __forceinline__ int y16_exp(float m) {
-  if (!(m > 0.0f)) return -128;
-  int ex;
-  frexpf(m, &ex);  // m in [2^(ex-1), 2^ex)
-  return max(-128, min(127, ex - 15));
+  // selects, not branches: m (1 + 2^-15) in [2^(ex-1), 2^ex)
+  const int ex = __builtin_amdgcn_frexp_expf(m * (1.0f + 0x1p-15f));
+  const int e = max(-128, min(127, ex - 15));
+  return m >= 0x1p127f ? 127 : m > 0.0f ? e : -128;
 }
-// Four values of one block -> four int16 mantissas (8 bytes), nearest.
-__device__ __forceinline__ uint2 y16_pack4(float a, float b, float c, float d, int E) {
-  auto q = [E](float v) {
-    const float r = __builtin_rintf(ldexpf(v, -E));
-    return (uint32_t)(int)fminf(fmaxf(r, -32767.0f), 32767.0f) & 0xFFFFu;
-  };
-  return make_uint2(q(a) | (q(b) << 16), q(c) | (q(d) << 16));
+// Four values a_i * w of one block -> four int16 mantissas (8 bytes), to
+// nearest: with ws = w 2^-E, one FMA a ws + 1.5 2^23 rounds the product
+// once to an integer held in the low mantissa bits (|a ws| < 2^15), whose
+// low 16 bits are the two's-complement mantissa; two of them are packed by
+// one byte permute.  ws = 0 for an all-zero block.
+__device__ __forceinline__ uint2 y16_pack4(float a, float b, float c, float d, float ws) {
+  auto q = [ws](float v) { return __float_as_uint(fmaf(v, ws, 0x1.8p23f)); };
+  return make_uint2(__builtin_amdgcn_perm(q(b), q(a), 0x05040100u), __builtin_amdgcn_perm(q(d), q(c), 0x05040100u));
 }
 // Eight int16 mantissas (16 bytes) of one block times 2^E, exact.
 __device__ __forceinline__ void y16_unpack8(uint4 m, int E, float* out) {
