@@ -18,7 +18,7 @@
 // for slab s + R - 1 are issued while slab s is computed, so R - 1 slabs of
 // loads are in flight and the compute reads only LDS.  Per slab and stage:
 //  - A: BM rows x 64 fp16 activations (operand order), 128 bytes a row, the
-//    16-byte chunk c of row r at position c ^ (r % 8).  Rows past the tile's
+//    16-byte chunk c of row r at position c ^ a_swz(r).  Rows past the tile's
 //    end load a valid row whose results are never stored.
 //  - B: packed codes (tile-major, see moe_w4_pack): per 32-column block one
 //    contiguous 1 KiB piece [32 columns][2 reduction halves] x 16 bytes.
@@ -40,6 +40,16 @@ namespace moe {
 namespace {
 
 constexpr int kSlabK = 64;
+
+// A tiles in LDS: the 16-byte chunk c of tile row r sits at position
+// c ^ a_swz(r) of the row's 128 bytes.  A fragment read takes one logical
+// chunk of 16 consecutive rows in each 16-lane group; the LDS serves 16 lanes
+// of a 16-byte read per cycle over 64 four-byte banks, so the even rows of the
+// 16 must use 8 distinct positions (they share banks 0..31 of a 256-byte
+// line) and so must the odd rows (banks 32..63): rows 2m and 2m + 1 take
+// pattern m.  (r % 8 gave rows r and r + 8 the same position: a two-way
+// conflict on every fragment read.)
+__device__ __forceinline__ int a_swz(int r) { return (r >> 1) & 7; }
 
 template <int V>
 struct IntTag {
@@ -134,19 +144,20 @@ __global__ __launch_bounds__(64 * WAVES, WGS_PER_CU * WAVES / 4) void w4_mfma_ke
   const bool gen = !DENSE && (p.t0.general[e] | (GATE_UP ? p.t1.general[e] : 0u)) != 0;
 
   // ---- A loads: instruction j covers rows 8j..8j+7; lane l fills physical
-  // chunk l % 8 of row 8j + l / 8, i.e. logical chunk (l % 8) ^ (l / 8).
+  // chunk l % 8 of row r = 8j + l / 8, i.e. logical chunk (l % 8) ^ a_swz(r).
   // The half-height loop (rows < BM / 2) with fewer first-half copies than
   // waves: wave w issues copy w mod (A_INSTR / 2), the same bytes to the
   // same LDS place as another wave (a harmless duplicate), so every wave
   // issues the same number of copies per slab.
   constexpr bool HALF_DUP = MB > 1 && A_PER_WAVE * (MB / 2) < MB;
   constexpr int NA = A_PER_WAVE + (HALF_DUP ? 1 : 0);
-  int arow[NA], a_lds[NA];
+  int arow[NA], a_lds[NA], achunk[NA];
 #pragma unroll
   for (int a = 0; a < NA; a++) {
     const int j = a == A_PER_WAVE ? wave % (A_INSTR / 2) : A_INSTR >= WAVES ? wave + WAVES * a : wave % A_INSTR;
     arow[a] = row0 + min(8 * j + (lane >> 3), rows - 1);
     a_lds[a] = 1024 * j;
+    achunk[a] = (lane & 7) ^ a_swz(8 * j + (lane >> 3));
   }
   if constexpr (GATE_UP) {
     // token rows of the slots' pairs: every pair is read before any is used
@@ -159,7 +170,7 @@ __global__ __launch_bounds__(64 * WAVES, WGS_PER_CU * WAVES / 4) void w4_mfma_ke
   }
   const half_t* asrc[NA];
 #pragma unroll
-  for (int a = 0; a < NA; a++) asrc[a] = p.a + (size_t)arow[a] * K + 8 * ((lane & 7) ^ (lane >> 3));
+  for (int a = 0; a < NA; a++) asrc[a] = p.a + (size_t)arow[a] * K + 8 * achunk[a];
   const half_t* const asrc_h = HALF_DUP ? asrc[NA - 1] : nullptr;
   const int a_lds_h = HALF_DUP ? a_lds[NA - 1] : 0;
 
@@ -298,7 +309,7 @@ __global__ __launch_bounds__(64 * WAVES, WGS_PER_CU * WAVES / 4) void w4_mfma_ke
           for (int mb = 0; mb < MBA; mb++) {
             const int r = mb * 32 + col;
             const half8_t af = *reinterpret_cast<const half8_t*>(
-                base + r * 128 + (((4 * khalf + i) ^ (col & 7)) << 4));
+                base + r * 128 + (((4 * khalf + i) ^ a_swz(col)) << 4));
 #pragma unroll
             for (int cb = 0; cb < 2; cb++)
               acc[mb][cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af, bf[cb], acc[mb][cb], 0, 0, 0);
@@ -324,7 +335,7 @@ __global__ __launch_bounds__(64 * WAVES, WGS_PER_CU * WAVES / 4) void w4_mfma_ke
         auto read_a = [&](int i) {
 #pragma unroll
           for (int mb = 0; mb < MBA; mb++)
-            af[i][mb] = lds_read16(base + (mb * 32 + col) * 128 + (((4 * khalf + i) ^ (col & 7)) << 4));
+            af[i][mb] = lds_read16(base + (mb * 32 + col) * 128 + (((4 * khalf + i) ^ a_swz(col)) << 4));
         };
 #pragma unroll
         for (int i = 0; i < PD; i++) read_a(i);
@@ -382,9 +393,9 @@ __global__ __launch_bounds__(64 * WAVES, WGS_PER_CU * WAVES / 4) void w4_mfma_ke
         issue(s, 0);
         wait_vm_barrier<0>();
         // activation chunk (row r, physical chunk pc) holds reduction indices
-        // 64 s + 8 (pc ^ (r % 8)) .. + 7, inside 16-column block 4 s + lc / 2
+        // 64 s + 8 (pc ^ a_swz(r)) .. + 7, inside 16-column block 4 s + lc / 2
         for (int c = tid; c < 32 * MBA * 8; c += 64 * WAVES) {
-          const int r = c >> 3, pc = c & 7, lc = pc ^ (r & 7);
+          const int r = c >> 3, pc = c & 7, lc = pc ^ a_swz(r);
           const int d = p.hexp[(size_t)(row0 + min(r, rows - 1)) * nbk + 4 * s + (lc >> 1)] - erow[r];
           if (d != 0) {
             uint4* at = reinterpret_cast<uint4*>(lds + r * 128 + pc * 16);
