@@ -407,6 +407,31 @@ int moe_ffn_forward_unfused(const moe_layer* layer, const uint16_t* x, const flo
                             size_t workspace_bytes, void* expanded, size_t expanded_bytes,
                             void* stream);
 
+/* ------------------------------------- single-launch decode layer --
+ * The decode-size layer (T <= 8) as one kernel launch instead of two: the
+ * gate/up workgroups and the down workgroups run side by side in one grid,
+ * and each down workgroup waits on per-expert device counters until every
+ * gate/up item of the experts its token chose has stored its h columns.
+ * Page "Perplexity Lily: 1.35x Faster Local AI Than MLX on Mac", section
+ * "Why MLX Falls Behind", sets decode apart as a latency-bound workload of
+ * its own; page "Perplexity's Lily engine beats MLX by 35% on M5 Max",
+ * architecture paragraph, keeps the whole MoE step in one GPU submission.
+ * Same kernels' arithmetic, same results as moe_ffn_forward, bit for bit.
+ * sync: device int32 [moe_ffn_single_sync_ints()], 4-byte aligned, all
+ * zero before its first use; every call leaves the counters at zero again,
+ * so a sync buffer is reusable without clearing.  Calls that share a sync
+ * buffer must be ordered (one stream, or synchronised): overlapping calls
+ * race on it.  sync[257] is set to 1 if a wait ever gave up (each wait is
+ * bounded, about a second; never reached in a correct run, and the layer's
+ * results are then undefined); it is never cleared by the library.  T > 8 returns MOE_ERR_UNSUPPORTED, and
+ * so do shapes whose two halves need workgroups of different sizes
+ * (H >= 1024 needs I = H / 4, smaller H needs I = H / 2).  Arguments and
+ * other errors as moe_ffn_forward; MOE_ERR_NULL for a NULL sync. */
+size_t moe_ffn_single_sync_ints(void);
+int moe_ffn_forward_single(const moe_layer* layer, const uint16_t* x, const float* router_logits,
+                           float* y, moe_route_info* info, void* workspace, size_t workspace_bytes,
+                           int32_t* sync, void* stream);
+
 /* --------------------------------------------- no-allocation variant --
  * For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the same

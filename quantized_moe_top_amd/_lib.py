@@ -30,6 +30,7 @@ SYMBOLS = (
     "moe_ffn_unfused_bytes", "moe_ffn_forward_unfused",
     "moe_rmsnorm", "moe_ffn_io_workspace_bytes", "moe_ffn_forward_io",
     "moe_decode_attention_workspace_bytes", "moe_decode_attention",
+    "moe_ffn_single_sync_ints", "moe_ffn_forward_single",
     "moe_ffn_noalloc_max_bytes", "moe_ffn_forward_noalloc",
 )
 
@@ -139,6 +140,10 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     L.moe_decode_attention_workspace_bytes.restype = c_sz
     L.moe_decode_attention_workspace_bytes.argtypes = [c_i32] * 4
     L.moe_decode_attention.argtypes = [c_p] * 5 + [c_i32] * 8 + [c_p, c_p, c_sz, c_p]
+    L.moe_ffn_single_sync_ints.restype = c_sz
+    L.moe_ffn_single_sync_ints.argtypes = []
+    L.moe_ffn_forward_single.argtypes = [ctypes.POINTER(Layer), c_p, c_p, c_p, ctypes.POINTER(RouteInfo),
+                                         c_p, c_sz, c_p, c_p]
     L.moe_ffn_noalloc_max_bytes.restype = c_sz
     L.moe_ffn_noalloc_max_bytes.argtypes = []
     L.moe_ffn_forward_noalloc.argtypes = [ctypes.POINTER(Layer), c_p, c_p, c_p, ctypes.POINTER(RouteInfo),
@@ -146,7 +151,7 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     for name in ("moe_w4_pack", "moe_route", "moe_build_blocks", "moe_w4_grouped_gemm",
                  "moe_ffn_forward", "moe_ffn_forward_timed", "moe_ffn_forward_host_blockmap",
                  "moe_ffn_forward_unfused", "moe_rmsnorm", "moe_ffn_forward_io",
-                 "moe_decode_attention", "moe_ffn_forward_noalloc"):
+                 "moe_decode_attention", "moe_ffn_forward_single", "moe_ffn_forward_noalloc"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
     return L

@@ -20,6 +20,7 @@ from ._lib import (MOE_GEMM_DOWN, MOE_GEMM_GATE_UP_SWIGLU, Bank, Dims, GemmArgs,
 
 __all__ = ["pack_bank", "pack_layer", "PackedBank", "PackedLayer",
            "route", "build_blocks", "w4_grouped_gemm", "ffn_forward", "ffn_workspace_bytes",
+           "single_sync", "single_sync_ints",
            "ffn_block_m", "max_blocks", "stage_events", "h_exp_bytes", "MOE_GEMM_GATE_UP_SWIGLU",
            "MOE_GEMM_DOWN"]
 
@@ -306,7 +307,7 @@ def ffn_forward(layer, x: Optional[torch.Tensor] = None, logits: Optional[torch.
                 info: bool = False, stage_events=None, host_blockmap: Optional[torch.Tensor] = None,
                 expanded: Optional[torch.Tensor] = None, norm_weight: Optional[torch.Tensor] = None,
                 norm_eps: float = 1e-6, residual: Optional[torch.Tensor] = None,
-                out: Optional[torch.Tensor] = None):
+                out: Optional[torch.Tensor] = None, sync: Optional[torch.Tensor] = None):
     """The whole layer (S0/S1-S8) for a ``PackedLayer`` (a device
     ``synth.MoELayer`` is packed first).  ``x`` and ``logits`` default to the
     layer's own.  Returns y
@@ -320,7 +321,8 @@ def ffn_forward(layer, x: Optional[torch.Tensor] = None, logits: Optional[torch.
     unfused-dequantisation ablation ``moe_ffn_forward_unfused`` instead.
     ``norm_weight`` (bf16 [H]) and/or ``residual`` with ``out`` (bf16 [T, H])
     run ``moe_ffn_forward_io``: RMSNorm in front, out = bf16(residual + y)
-    behind."""
+    behind.  ``sync`` (``single_sync()``: device int32 counters, zero between
+    calls) runs the single-launch decode layer ``moe_ffn_forward_single``."""
     if not isinstance(layer, PackedLayer):
         layer = pack_layer(layer)
     x = layer.x if x is None else x
@@ -348,6 +350,11 @@ def ffn_forward(layer, x: Optional[torch.Tensor] = None, logits: Optional[torch.
                         _dev(out, "out", torch.bfloat16) if out is not None else 0)
         _lib.check(_L().moe_ffn_forward_io(args[0], args[1], args[2], args[3], ctypes.byref(io),
                                            *args[4:], _stream()), "moe_ffn_forward_io")
+    elif sync is not None:
+        if sync.dtype != torch.int32 or sync.numel() < single_sync_ints():
+            raise ValueError("sync must be a device int32 tensor of single_sync_ints() elements")
+        _lib.check(_L().moe_ffn_forward_single(*args, _dev(sync, "sync", torch.int32), _stream()),
+                   "moe_ffn_forward_single")
     elif expanded is not None:
         _lib.check(_L().moe_ffn_forward_unfused(*args, _dev(expanded, "expanded", torch.uint8),
                                                 expanded.numel(), _stream()),
@@ -405,6 +412,25 @@ def _info_views(ri: RouteInfo, ws: torch.Tensor, layer, T: int, logits) -> dict:
     out["logits"] = (view(ri.logits, T * layer.E, torch.float32, (T, layer.E))
                      if layer.router_weight is not None else logits)
     return out
+
+
+def single_sync_ints() -> int:
+    return int(_L().moe_ffn_single_sync_ints())
+
+
+_SYNC = {}
+
+
+def single_sync(device=None) -> torch.Tensor:
+    """The counters of the single-launch decode layer for ``device``: one
+    zeroed int32 tensor per device, kept for the process (every call leaves
+    it zero again).  Calls that share it must be ordered, as on one stream."""
+    dev = torch.device("cuda") if device is None else torch.device(device)
+    if dev.index is None:
+        dev = torch.device(dev.type, torch.cuda.current_device())
+    if dev not in _SYNC:
+        _SYNC[dev] = torch.zeros(single_sync_ints(), dtype=torch.int32, device=dev)
+    return _SYNC[dev]
 
 
 def ffn_forward_noalloc(layer, x: Optional[torch.Tensor] = None, logits: Optional[torch.Tensor] = None,

@@ -381,7 +381,8 @@ int ffn_forward_impl(const moe_layer* layer, const uint16_t* x, const float* rou
                      float* y, moe_route_info* info, void* workspace, size_t workspace_bytes,
                      void* const* events, hipStream_t s, int32_t* host = nullptr,
                      size_t host_ints = 0, uint32_t* expanded = nullptr,
-                     size_t expanded_bytes = 0, const moe_ffn_io* io = nullptr) {
+                     size_t expanded_bytes = 0, const moe_ffn_io* io = nullptr,
+                     int32_t* sync = nullptr) {
   if (!layer) return fail(MOE_ERR_NULL, "layer is NULL");
   const moe_dims& d = layer->dims;
   int st = check_dims(&d);
@@ -419,6 +420,11 @@ int ffn_forward_impl(const moe_layer* layer, const uint16_t* x, const float* rou
     if (!aligned16(expanded)) return fail(MOE_ERR_ALIGN, "expanded weights not 16-byte aligned");
     if (expanded_bytes < unfused_bytes(d))
       return fail(MOE_ERR_WORKSPACE, "expanded buffer %zu < %zu bytes", expanded_bytes, unfused_bytes(d));
+  }
+  if (sync) {
+    if (d.T > moe::kGemvMaxTokens)
+      return fail(MOE_ERR_UNSUPPORTED, "the single-launch layer needs T <= %d", moe::kGemvMaxTokens);
+    if ((uintptr_t)sync & 3u) return fail(MOE_ERR_ALIGN, "sync not 4-byte aligned");
   }
   if (host) {
     if (d.T <= moe::kGemvMaxTokens)
@@ -504,6 +510,18 @@ int ffn_forward_impl(const moe_layer* layer, const uint16_t* x, const float* rou
     g1.a = (const moe::half_t*)x;  // bf16, converted while staged
     const moe::DecodeRouting dr{part ? part : logits, logits, L.router_ks, ids, w, counts, offsets,
                                 sorted_pairs, pair_slot, blocks, num_blocks};
+    if (sync) {
+      // the whole layer in one launch (the down and combine stages are empty)
+      if (!moe::decode_layer_supported(g1, g2))
+        return fail(MOE_ERR_UNSUPPORTED, "the single-launch layer needs H and I on workgroups of one size");
+      if ((err = moe::launch_decode_layer(dr, g1, g2, y, sync, s, residual, out)) != hipSuccess)
+        return hip_status(err, "decode layer");
+      if ((err = mark(events, MOE_STAGE_DOWN, s)) != hipSuccess ||
+          (err = mark(events, MOE_STAGE_COMBINE, s)) != hipSuccess ||
+          (err = mark(events, MOE_NUM_STAGES, s)) != hipSuccess)
+        return hip_status(err, "event");
+      return ok();
+    }
     err = moe::launch_decode_gate_up(dr, g1, s);
   } else if (expanded) {
     // unfused ablation: every expert's banks expanded to fp16 in HBM first
@@ -549,6 +567,16 @@ int moe_ffn_forward(const moe_layer* layer, const uint16_t* x, const float* rout
                     void* stream) {
   return ffn_forward_impl(layer, x, router_logits, y, info, workspace, workspace_bytes, nullptr,
                           (hipStream_t)stream);
+}
+
+size_t moe_ffn_single_sync_ints(void) { return moe::kDecodeSyncInts; }
+
+int moe_ffn_forward_single(const moe_layer* layer, const uint16_t* x, const float* router_logits,
+                           float* y, moe_route_info* info, void* workspace, size_t workspace_bytes,
+                           int32_t* sync, void* stream) {
+  if (!sync) return fail(MOE_ERR_NULL, "sync is NULL");
+  return ffn_forward_impl(layer, x, router_logits, y, info, workspace, workspace_bytes, nullptr,
+                          (hipStream_t)stream, nullptr, 0, nullptr, 0, nullptr, sync);
 }
 
 size_t moe_ffn_unfused_bytes(const moe_dims* d) {

@@ -302,6 +302,10 @@ __device__ __forceinline__ void g16_mma(const DecParams& p, const Frag16<SPW>& f
 // The waves' partials (rows 0..7: lanes 0..31, registers 0..3) meet in LDS
 // at red_off and are added in wave order; h = silu(gate) * up in operand
 // order.  Ends with a barrier (the LDS is reused by the next item).
+// COHERENT: h and its exponents are stored with device-scope (write-through)
+// stores, so a workgroup of the same launch on another XCD can read them once
+// it has seen the tile's ready count (the single-launch decode layer).
+template <bool COHERENT = false>
 __device__ __forceinline__ void g16_epilogue(const DecParams& p, const floatx4_t (&acc)[2], int row0,
                                              int rows, int b16, char* dsm, float us0, float us1) {
   const int tid = threadIdx.x, lane = tid & 63;
@@ -329,9 +333,17 @@ __device__ __forceinline__ void g16_epilogue(const DecParams& p, const floatx4_t
     const float hv = silu_mul(v[0] * us0, v[1] * us1);
     const int ex = h_block_exp(row16_max(fabsf(hv)));
     const int n = b16 * 16 + cc;
-    reinterpret_cast<half_t*>(p.out)[(size_t)(row0 + m) * p.N + (n & ~7) + interleaved_pos(n & 7)] =
-        (half_t)ldexpf(hv, -ex);
-    if (cc == 0) p.hexp[(size_t)(row0 + m) * (p.N / 16) + b16] = (int8_t)ex;
+    half_t* hp = reinterpret_cast<half_t*>(p.out) + (size_t)(row0 + m) * p.N + (n & ~7) + interleaved_pos(n & 7);
+    int8_t* ep = p.hexp + (size_t)(row0 + m) * (p.N / 16) + b16;
+    const half_t hq = (half_t)ldexpf(hv, -ex);
+    if constexpr (COHERENT) {
+      __hip_atomic_store(reinterpret_cast<uint16_t*>(hp), __builtin_bit_cast(uint16_t, hq), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+      if (cc == 0) __hip_atomic_store(ep, (int8_t)ex, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else {
+      *hp = hq;
+      if (cc == 0) *ep = (int8_t)ex;
+    }
   }
   __syncthreads();
 }
@@ -347,7 +359,7 @@ __device__ __forceinline__ void g16_epilogue(const DecParams& p, const floatx4_t
 // activation fragment of tile row l % 16 is read to match (zeros past the
 // tile).  SPW slabs per wave and pass.
 // gen, us0, us1: the expert's dequantisation form and factors 2^-c.
-template <int SPW>
+template <int SPW, bool COHERENT = false>
 __device__ __forceinline__ void gemv_tile16(const DecParams& p, const int32_t* sorted_pairs, int e,
                                             int row0, int rows, int b16, char* dsm, bool gen,
                                             float us0, float us1) {
@@ -361,7 +373,7 @@ __device__ __forceinline__ void gemv_tile16(const DecParams& p, const int32_t* s
     else g16_mma<SPW, false>(p, f, rows, base, acc, dsm);
     __syncthreads();  // the next pass overwrites xs
   }
-  g16_epilogue(p, acc, row0, rows, b16, dsm, us0, us1);
+  g16_epilogue<COHERENT>(p, acc, row0, rows, b16, dsm, us0, us1);
 }
 
 // The grouped GEMM at decode sizes on a device block map: one workgroup per
@@ -441,17 +453,44 @@ __device__ __forceinline__ void g16_mma_res(const DecParams& p, const Frag16<SPW
 // round trip as the logits, and every item reads its tile's rows from there;
 // otherwise each pass stages the tile's rows through the LDS scatter.
 // NK = ceil(E / 64) keys per lane in the top-k.
-template <int NK, int SPW>
-__global__ __launch_bounds__(64 * kDecWavesMax) void decode_gate_up_kernel(const DecRouteParams r,
-                                                                          const DecParams p) {
-  extern __shared__ __attribute__((aligned(16))) char dsm[];
-  __shared__ int cnt[256], wsc[8];
-  __shared__ uint32_t tokmask[256];
-  __shared__ int32_t ids_s[kSmallPairs], sp_s[kSmallPairs], ps_s[kSmallPairs];
-  __shared__ float w_s[kSmallPairs];
-  __shared__ int32_t off_s[257];
-  __shared__ int32_t blk_s[3 * kSmallMaxBlocks];
-  __shared__ int32_t nb_s[1];
+// The routing of a decode batch in LDS: per-expert counts and token masks,
+// the top-k ids and combine weights, offsets, the stable scatter (both
+// directions) and the block map.
+struct DecRouteLds {
+  int cnt[256], wsc[8];
+  uint32_t tokmask[256];
+  int32_t ids[kSmallPairs], sp[kSmallPairs], ps[kSmallPairs];
+  float w[kSmallPairs];
+  int32_t off[257];
+  int32_t blk[3 * kSmallMaxBlocks];
+  int32_t nb[1];
+};
+
+// Device-scope counters of the single-launch decode layer: per expert, the
+// gate/up items whose h columns are stored; the workgroups that finished;
+// a flag set when a wait gave up (never in a correct run).
+constexpr int kSyncDone = 256, kSyncErr = 257;
+// Bound on the polls of one wait (each a device-scope round trip of about a
+// microsecond, then s_sleep 2): about a second, so every wait ends.
+constexpr int kSpinLimit = 1 << 20;
+
+// The gate/up half of the decode layer for workgroup bid of G: routing into
+// rl, then items bid, bid + G, ....  READY (the single-launch layer): h is
+// stored device-coherent and, once a workgroup's item is stored, the item's
+// expert's count in ready is raised.
+template <int NK, int SPW, bool READY>
+__device__ __forceinline__ void decode_gate_up_body(const DecRouteParams& r, const DecParams& p, int bid,
+                                                    int G, char* dsm, DecRouteLds& rl, int32_t* ready) {
+  int* const cnt = rl.cnt;
+  int* const wsc = rl.wsc;
+  uint32_t* const tokmask = rl.tokmask;
+  int32_t* const ids_s = rl.ids;
+  int32_t* const sp_s = rl.sp;
+  int32_t* const ps_s = rl.ps;
+  float* const w_s = rl.w;
+  int32_t* const off_s = rl.off;
+  int32_t* const blk_s = rl.blk;
+  int32_t* const nb_s = rl.nb;
   __shared__ float us_s[2][256];  // every expert's 2^-c for gate and up
   __shared__ int gen_s[256];      // and dequantisation form (general if either bank's is)
   const int tid = threadIdx.x;
@@ -516,7 +555,7 @@ __global__ __launch_bounds__(64 * kDecWavesMax) void decode_gate_up_kernel(const
   Frag16<SPW> fa, fb;
   if (one_pass) {
     const int lane = tid & 63;
-    int t = blockIdx.x / nb16, e0 = -1;
+    int t = bid / nb16, e0 = -1;
 #pragma unroll
     for (int i = 0; i < NK; i++) {
       const uint64_t m = __ballot(64 * i + lane < E && cnt[64 * i + lane] > 0);
@@ -529,7 +568,7 @@ __global__ __launch_bounds__(64 * kDecWavesMax) void decode_gate_up_kernel(const
       t -= c;
     }
     if (e0 >= 0) {
-      fa = g16_load<SPW>(p, e0, blockIdx.x % nb16, 0);
+      fa = g16_load<SPW>(p, e0, bid % nb16, 0);
       asm volatile("" ::: "memory");  // keep the loads here, ahead of the build
     }
   }
@@ -537,13 +576,12 @@ __global__ __launch_bounds__(64 * kDecWavesMax) void decode_gate_up_kernel(const
   decode_build_wg(ids_s, cnt, tokmask, wsc, P, E, k, off_s, sp_s, ps_s, blk_s, nb_s,
                   min(p.max_blocks, kSmallMaxBlocks));
   __syncthreads();
-  // 5. the (tile, column block) items of this workgroup: blockIdx.x, then
-  //    every gridDim.x-th after it (the grid is at most what the chip holds
-  //    at once, so the routing above runs once per workgroup)
+  // 5. the (tile, column block) items of this workgroup: bid, then every
+  //    G-th after it (G is at most what the chip holds at once, so the
+  //    routing above runs once per workgroup)
   const int items = nb_s[0] * nb16;
-  const int G = gridDim.x;
   // 6. workgroup 0 publishes the routing
-  if (blockIdx.x == 0) {
+  if (bid == 0) {
     for (int i = tid; i < P; i += blockDim.x) {
       r.ids[i] = ids_s[i];
       r.w[i] = w_s[i];
@@ -558,19 +596,33 @@ __global__ __launch_bounds__(64 * kDecWavesMax) void decode_gate_up_kernel(const
       for (int i = tid; i < T * E; i += blockDim.x) r.logits_out[i] = lg[i];
   }
   if (!p.x_res) __syncthreads();  // lg is overwritten by the activation stage below
+  // READY: raise expert e's count once every wave's stores of its item
+  // have completed (vmcnt counts stores; the count is raised by one thread
+  // after the barrier)
+  auto signal = [&](int e) {
+    if constexpr (READY) {
+      wait_vm<0>();
+      __syncthreads();
+      if (tid == 0) __hip_atomic_fetch_add(ready + e, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  };
   if (!one_pass) {  // more than one pass per item
-    for (int it = blockIdx.x; it < items; it += G) {
+    for (int it = bid; it < items; it += G) {
       const int tile = it / nb16;
       const int e = blk_s[3 * tile];
-      gemv_tile16<SPW>(p, sp_s, e, blk_s[3 * tile + 1], blk_s[3 * tile + 2], it % nb16, dsm, gen_s[e] != 0,
-                       us_s[0][e], us_s[1][e]);
+      gemv_tile16<SPW, READY>(p, sp_s, e, blk_s[3 * tile + 1], blk_s[3 * tile + 2], it % nb16, dsm,
+                              gen_s[e] != 0, us_s[0][e], us_s[1][e]);
+      signal(e);
     }
     return;
   }
   // one pass per item: the next item's weight loads are issued before this
-  // item's multiplies (two fragment sets, alternating)
-  int it = blockIdx.x;
+  // item's multiplies (two fragment sets, alternating).  READY: an item's
+  // count is raised at the next item's wait for its fragments (which also
+  // covers the stores before it), or after the last item.
+  int it = bid;
   const int c = tid & 15;
+  int pending = -1;  // READY: the expert of the item stored last, not yet counted
   while (it < items) {
 #pragma unroll
     for (int half = 0; half < 2; half++) {
@@ -588,6 +640,10 @@ __global__ __launch_bounds__(64 * kDecWavesMax) void decode_gate_up_kernel(const
       // have landed; the multiplies below then wait for nothing issued
       // after this point
       wait_vm<0>();
+      if (READY && pending >= 0) {
+        signal(pending);
+        pending = -1;
+      }
       if (nx < items) {
         if (half == 0) fb = g16_load<SPW>(p, blk_s[3 * (nx / nb16)], nx % nb16, 0);
         else fa = g16_load<SPW>(p, blk_s[3 * (nx / nb16)], nx % nb16, 0);
@@ -602,11 +658,21 @@ __global__ __launch_bounds__(64 * kDecWavesMax) void decode_gate_up_kernel(const
         else g16_mma<SPW, false>(p, half == 0 ? fa : fb, rows, 0, acc, dsm);
         __syncthreads();
       }
-      g16_epilogue(p, acc, row0, rows, b16, dsm, us_s[0][e], us_s[1][e]);
+      g16_epilogue<READY>(p, acc, row0, rows, b16, dsm, us_s[0][e], us_s[1][e]);
+      pending = e;
       it = nx;
       if (it >= items) break;
     }
   }
+  if (READY && pending >= 0) signal(pending);
+}
+
+template <int NK, int SPW>
+__global__ __launch_bounds__(64 * kDecWavesMax) void decode_gate_up_kernel(const DecRouteParams r,
+                                                                          const DecParams p) {
+  extern __shared__ __attribute__((aligned(16))) char dsm[];
+  __shared__ DecRouteLds rl;
+  decode_gate_up_body<NK, SPW, false>(r, p, blockIdx.x, gridDim.x, dsm, rl, nullptr);
 }
 
 // Decode sizes, S7 and S8 in one launch, organised per token: workgroup
@@ -631,10 +697,20 @@ __global__ __launch_bounds__(64 * kDecWavesMax) void decode_gate_up_kernel(const
 // rows exactly.
 constexpr int kDownChunk = 8;
 
-__global__ __launch_bounds__(64 * kDecWavesMax) void decode_down_kernel(
-    const DecParams p, const int32_t* __restrict__ ids, const int32_t* __restrict__ pair_slot,
-    float* __restrict__ y, const uint16_t* __restrict__ residual, uint16_t* __restrict__ out) {
-  extern __shared__ __attribute__((aligned(16))) char dsm[];
+// The down half for (token t, 16-column block b16).  ids, pair_slot,
+// topk_w: the routing (global or LDS).  WAIT (the single-launch layer): the
+// weights of a chunk of choices are requested first, then the workgroup
+// waits until each chosen expert's count in ready reaches need (every
+// gate/up item of its tile stored), then reads h and its exponents with
+// device-scope loads.
+template <bool WAIT>
+__device__ __forceinline__ void decode_down_body(const DecParams& p, int t, int b16,
+                                                 const int32_t* __restrict__ ids,
+                                                 const int32_t* __restrict__ pair_slot,
+                                                 const float* __restrict__ topk_w, float* __restrict__ y,
+                                                 const uint16_t* __restrict__ residual,
+                                                 uint16_t* __restrict__ out, char* dsm, int32_t* ready,
+                                                 int need, int32_t* err, int done_target) {
   __shared__ int e_s[16], slot_s[16];
   __shared__ float w_s[16], v_s[16 * 16];
   __shared__ float us_s[256];  // every expert's 2^-c and dequantisation form
@@ -643,8 +719,7 @@ __global__ __launch_bounds__(64 * kDecWavesMax) void decode_down_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nwaves = blockDim.x >> 6;
-  const int nbl = p.N / 32, nb16 = p.N / 16;
-  const int t = blockIdx.x / nb16, b16 = blockIdx.x % nb16;
+  const int nbl = p.N / 32;
   const int K = p.K, S = K / 64, gpr = K >> p.log2_G, k = p.top_k;
   const int c = lane & 15, lg = lane >> 4, khalf = lg >> 1, qh = lg & 1;
   const int col = 16 * (b16 & 1) + c;  // column within the 32-column packed block
@@ -667,7 +742,7 @@ __global__ __launch_bounds__(64 * kDecWavesMax) void decode_down_kernel(
   }
   const int pair = t * k + min(tid, k - 1);
   const int e = ids[pair], slot = pair_slot[pair];
-  const float wt = p.topk_weights[pair];
+  const float wt = topk_w[pair];
 #pragma unroll
   for (int i = 0; i < 2; i++) {
     const int x = tid + i * blockDim.x;
@@ -692,6 +767,7 @@ __global__ __launch_bounds__(64 * kDecWavesMax) void decode_down_kernel(
   const uint64_t gmask = __ballot(lane < k && genx_s[e_l] != 0);
   const int s = wave;  // this wave's slab (nwaves == S)
   const int g = (64 * s + 32 * khalf) >> p.log2_G;
+  int done_old = -1;  // WAIT: the done count before this workgroup's (thread 0)
   for (int j0 = 0; j0 < k; j0 += kDownChunk) {
     const int nj = min(kDownChunk, k - j0);
     // 1. the chunk's h rows, 16 bytes per thread (nj * K / 8 <= 64 * S
@@ -701,7 +777,7 @@ __global__ __launch_bounds__(64 * kDecWavesMax) void decode_down_kernel(
     const bool stager = tid < nj * c8n;
     const int hm = stager ? tid / c8n : 0, hc8 = stager ? tid % c8n : 0;
     uint4 hv = make_uint4(0, 0, 0, 0);
-    if (stager) hv = *reinterpret_cast<const uint4*>(p.a + (size_t)max(slot_s[j0 + hm], 0) * K + 8 * hc8);
+    if (!WAIT && stager) hv = *reinterpret_cast<const uint4*>(p.a + (size_t)max(slot_s[j0 + hm], 0) * K + 8 * hc8);
     // 2. codes (two words) and (scale, bias) word of every choice of the
     //    chunk, and the exponents of the slab's four 16-column blocks of its
     //    h row (one word: a scalar load)
@@ -716,7 +792,46 @@ __global__ __launch_bounds__(64 * kDecWavesMax) void decode_down_kernel(
       q[j] = *reinterpret_cast<const uint2*>(p.b0.words + ((bidx >> 2) * S * 4 + (bidx & 3)) * 256 +
                                              4 * (2 * col + khalf) + 2 * qh + (size_t)s * 1024);
       sb[j] = p.b0.sb[(bidx >> 2) * gpr * 128 + (bidx & 3) * 32 + col + (size_t)g * 128];
-      hx[j] = reinterpret_cast<const uint32_t*>(p.hexp + (size_t)sl * (K / 16))[s];
+      if (!WAIT) hx[j] = reinterpret_cast<const uint32_t*>(p.hexp + (size_t)sl * (K / 16))[s];
+    }
+    if constexpr (WAIT) {
+      // the chunk's experts: lane j of wave 0 polls expert j's count (a
+      // malformed choice reads expert 0's, whose wait then gives up)
+      if (tid < nj) {
+        const int32_t* rp = ready + e_s[j0 + tid];
+        int polls = 0;
+        while (__hip_atomic_load(rp, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need) {
+          if (++polls > kSpinLimit) {
+            __hip_atomic_store(err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(2);
+        }
+      }
+      __syncthreads();
+      // after its last wait, the workgroup counts itself done; the last down
+      // workgroup to do so returns the counts to zero (every count it
+      // clears has reached its final value: each touched expert's producers
+      // finished before its consumers' waits ended, and every consumer has
+      // passed its waits)
+      // (the count's old value is read at the end, so its round trip
+      // overlaps the multiplies)
+      if (j0 + kDownChunk >= k && tid == 0)
+        done_old = __hip_atomic_fetch_add(ready + kSyncDone, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      // h rows and exponents with device-scope loads: they miss any stale
+      // line another XCD's L2 may hold
+      if (stager) {
+        const uint64_t* hs = reinterpret_cast<const uint64_t*>(p.a + (size_t)max(slot_s[j0 + hm], 0) * K + 8 * hc8);
+        const uint64_t lo = __hip_atomic_load(hs, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint64_t hi = __hip_atomic_load(hs + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        hv = make_uint4((uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32));
+      }
+#pragma unroll
+      for (int j = 0; j < kDownChunk; j++) {
+        const int sl = __builtin_amdgcn_readlane(slot_l, min(j0 + j, k - 1));
+        hx[j] = __hip_atomic_load(reinterpret_cast<const uint32_t*>(p.hexp + (size_t)sl * (K / 16)) + s,
+                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
     if (stager) *reinterpret_cast<uint4*>(xs + hm * K + 8 * hc8) = hv;
     __syncthreads();
@@ -793,6 +908,81 @@ __global__ __launch_bounds__(64 * kDecWavesMax) void decode_down_kernel(
       }
     }
   }
+  if constexpr (WAIT) {
+    // the last down workgroup clears the counts, one per thread
+    __shared__ int last_s;
+    if (tid == 0) last_s = done_old == done_target - 1;
+    __syncthreads();
+    if (last_s) {
+      for (int e2 = tid; e2 < p.E; e2 += blockDim.x)
+        __hip_atomic_store(ready + e2, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (tid == 0) __hip_atomic_store(ready + kSyncDone, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+__global__ __launch_bounds__(64 * kDecWavesMax) void decode_down_kernel(
+    const DecParams p, const int32_t* __restrict__ ids, const int32_t* __restrict__ pair_slot,
+    float* __restrict__ y, const uint16_t* __restrict__ residual, uint16_t* __restrict__ out) {
+  extern __shared__ __attribute__((aligned(16))) char dsm[];
+  const int nb16 = p.N / 16;
+  decode_down_body<false>(p, blockIdx.x / nb16, blockIdx.x % nb16, ids, pair_slot, p.topk_weights, y,
+                          residual, out, dsm, nullptr, 0, nullptr, 0);
+}
+
+// The routing of the batch into rl, as every gate/up workgroup computes it
+// (same loads, same order of the partial sums, same top-k and build), for a
+// workgroup that runs the down half; lg: T * E floats of LDS.
+template <int NK>
+__device__ __forceinline__ void decode_route_only(const DecRouteParams& r, const DecParams& p, float* lg,
+                                                  DecRouteLds& rl) {
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), nwaves = blockDim.x >> 6;
+  const int T = r.T, E = p.E, k = p.top_k;
+  const size_t part = (size_t)T * E;
+  for (int i = tid; i < T * E; i += blockDim.x) {
+    float v = r.logits[i];
+    for (int z = 1; z < r.ksplit; z++) v += r.logits[z * part + i];
+    lg[i] = v;
+  }
+  for (int i = tid; i < E; i += blockDim.x) {
+    rl.cnt[i] = 0;
+    rl.tokmask[i] = 0u;
+  }
+  __syncthreads();
+  for (int t = wave; t < T; t += nwaves) topk_token<NK>(lg + t * E, E, k, rl.ids + t * k, rl.w + t * k, rl.cnt);
+  __syncthreads();
+  decode_build_wg(rl.ids, rl.cnt, rl.tokmask, rl.wsc, p.P, E, k, rl.off, rl.sp, rl.ps, rl.blk, rl.nb,
+                  min(p.max_blocks, kSmallMaxBlocks));
+  __syncthreads();
+}
+
+// Decode sizes, the whole layer (S1-S8) in one launch.  Workgroups [0, G1)
+// run the gate/up half (decode_gate_up_body with ready counts), the
+// workgroups after them the down half of (token, 16-column block)
+// (decode_down_body, waiting on the counts of the token's experts), after
+// routing the batch themselves.  Workgroups are dispatched in index order
+// on each XCD, so every gate/up workgroup holds a slot before a down
+// workgroup that waits on it does, and the gate/up half waits on nothing:
+// the waits end.  h crosses XCDs through device-scope stores and loads, no
+// cache writeback or invalidation.  Each down workgroup counts itself done
+// after its last wait; the last returns the counts to zero, so sync is zero
+// again for the next call.
+template <int NK, int SPW>
+__global__ __launch_bounds__(64 * kDecWavesMax) void decode_layer_kernel(
+    const DecRouteParams r, const DecParams pg, const DecParams pd, float* __restrict__ y,
+    const uint16_t* __restrict__ residual, uint16_t* __restrict__ out, int32_t* __restrict__ sync, int G1) {
+  extern __shared__ __attribute__((aligned(16))) char dsm[];
+  __shared__ DecRouteLds rl;
+  const int bid = blockIdx.x;
+  if (bid < G1) {
+    decode_gate_up_body<NK, SPW, true>(r, pg, bid, G1, dsm, rl, sync);
+  } else {
+    decode_route_only<NK>(r, pg, reinterpret_cast<float*>(dsm), rl);
+    const int nb16 = pd.N / 16, item = bid - G1;
+    decode_down_body<true>(pd, item / nb16, item % nb16, rl.ids, rl.ps, rl.w, y, residual, out, dsm, sync,
+                           pg.N / 16, sync + kSyncErr, (int)gridDim.x - G1);
+  }
 }
 
 // Slabs per wave and waves per workgroup for a launch of `grid` workgroups
@@ -863,14 +1053,23 @@ static void launch_decode_nk(const DecRouteParams& r, const DecParams& p, bool w
   else decode_gate_up_kernel<NK, 2><<<grid, threads, lds, s>>>(r, p);
 }
 
-hipError_t launch_decode_gate_up(const DecodeRouting& dr, const GemmArgs& a, hipStream_t s) {
-  if (a.T <= 0) return hipSuccess;
+// Launch shape of the gate/up half at decode sizes.
+namespace {
+struct DecGateUpPlan {
+  DecParams p;
+  bool wide;
+  int threads;
+  size_t lds;     // dynamic LDS
+  int64_t items;  // (tile, 16-column block) items at most
+};
+}  // namespace
+static bool decode_gate_up_plan(const GemmArgs& a, DecGateUpPlan& pl) {
   if (a.T > kGemvMaxTokens || a.block_m != kGemvMaxTokens || a.E > 256 ||
       (int64_t)a.T * a.top_k > kSmallPairs)
-    return hipErrorInvalidValue;
+    return false;
   const int64_t P = (int64_t)a.T * a.top_k;
   const int64_t max_blocks = P / a.block_m + (P < a.E ? P : a.E);
-  const int64_t max_items = max_blocks * (a.N / 16);
+  pl.items = max_blocks * (a.N / 16);
   // four slabs per wave (8 waves cover K = 2048 in one pass, two workgroups
   // per CU) when K allows it: fewer waves to launch, the same bytes in flight
   const int spw = a.K >= 1024 ? 4 : 2;
@@ -893,25 +1092,37 @@ hipError_t launch_decode_gate_up(const DecodeRouting& dr, const GemmArgs& a, hip
     lg_off = 0;
     red_off = (xs_bytes + 15) & ~15;
   }
-  const size_t lds = (size_t)red_off + red_bytes;
-  DecParams p = dec_params(a, P, max_blocks, red_off);
-  p.lg_off = lg_off;
-  p.x_res = x_res;
+  pl.lds = (size_t)red_off + red_bytes;
+  pl.p = dec_params(a, P, max_blocks, red_off);
+  pl.p.lg_off = lg_off;
+  pl.p.x_res = x_res;
+  pl.wide = sh.spw == 4;
+  pl.threads = 64 * sh.waves;
+  return true;
+}
+
+// Workgroups of `threads` threads with `lds` bytes of dynamic LDS (plus
+// about `static_kib` KiB of static LDS) that one CU holds at once, at most
+// 4 waves per SIMD.
+static int decode_per_cu(int threads, size_t lds, int static_kib) {
+  return std::max(1, std::min<int>(16 / (threads / 64), (int)((160 * 1024) / (lds + static_kib * 1024))));
+}
+
+hipError_t launch_decode_gate_up(const DecodeRouting& dr, const GemmArgs& a, hipStream_t s) {
+  if (a.T <= 0) return hipSuccess;
+  DecGateUpPlan pl;
+  if (!decode_gate_up_plan(a, pl)) return hipErrorInvalidValue;
   const DecRouteParams r{dr.logits, dr.logits_out, dr.ksplit, a.T,
                          dr.ids, dr.w, dr.counts, dr.offsets, dr.sorted_pairs, dr.pair_slot,
                          dr.blocks, dr.num_blocks};
-  const bool wide = sh.spw == 4;
-  const int threads = 64 * sh.waves;
-  // at most one round of workgroups (4 waves per SIMD, LDS permitting, with
-  // about 10 KiB of static LDS per workgroup):
-  // the routing then runs once per workgroup
-  const int per_cu = std::max(1, std::min<int>(16 / sh.waves, (int)((160 * 1024) / (lds + 12 * 1024))));
-  const int64_t grid = std::min<int64_t>(max_items, (int64_t)device_cus() * per_cu);
+  // at most one round of workgroups: the routing then runs once per
+  // workgroup
+  const int64_t grid = std::min<int64_t>(pl.items, (int64_t)device_cus() * decode_per_cu(pl.threads, pl.lds, 12));
   switch ((a.E + 63) / 64) {
-    case 1: launch_decode_nk<1>(r, p, wide, grid, threads, lds, s); break;
-    case 2: launch_decode_nk<2>(r, p, wide, grid, threads, lds, s); break;
-    case 3: launch_decode_nk<3>(r, p, wide, grid, threads, lds, s); break;
-    default: launch_decode_nk<4>(r, p, wide, grid, threads, lds, s); break;
+    case 1: launch_decode_nk<1>(r, pl.p, pl.wide, grid, pl.threads, pl.lds, s); break;
+    case 2: launch_decode_nk<2>(r, pl.p, pl.wide, grid, pl.threads, pl.lds, s); break;
+    case 3: launch_decode_nk<3>(r, pl.p, pl.wide, grid, pl.threads, pl.lds, s); break;
+    default: launch_decode_nk<4>(r, pl.p, pl.wide, grid, pl.threads, pl.lds, s); break;
   }
   return hipGetLastError();
 }
@@ -929,6 +1140,50 @@ hipError_t launch_decode_down(const GemmArgs& a, const int32_t* ids, const int32
   const size_t lds = (size_t)xs_bytes + (size_t)waves * a.top_k * 16 * 4;
   const DecParams p = dec_params(a, P, 0, xs_bytes);
   decode_down_kernel<<<grid, 64 * waves, lds, s>>>(p, ids, pair_slot, y, residual, out);
+  return hipGetLastError();
+}
+
+template <int NK>
+static void launch_layer_nk(const DecRouteParams& r, const DecParams& pg, const DecParams& pd, bool wide,
+                            int64_t grid, int threads, size_t lds, float* y, const uint16_t* residual,
+                            uint16_t* out, int32_t* sync, int G1, hipStream_t s) {
+  if (wide) decode_layer_kernel<NK, 4><<<grid, threads, lds, s>>>(r, pg, pd, y, residual, out, sync, G1);
+  else decode_layer_kernel<NK, 2><<<grid, threads, lds, s>>>(r, pg, pd, y, residual, out, sync, G1);
+}
+
+bool decode_layer_supported(const GemmArgs& g, const GemmArgs& d) {
+  DecGateUpPlan pl;
+  return decode_gate_up_plan(g, pl) && decode_down_fused(d.K) && pl.threads == 64 * (d.K / 64);
+}
+
+hipError_t launch_decode_layer(const DecodeRouting& dr, const GemmArgs& g, const GemmArgs& d, float* y,
+                               int32_t* sync, hipStream_t s, const uint16_t* residual, uint16_t* out) {
+  if (g.T <= 0) return hipSuccess;
+  DecGateUpPlan pl;
+  if (!decode_gate_up_plan(g, pl) || !decode_down_fused(d.K) || pl.threads != 64 * (d.K / 64))
+    return hipErrorInvalidValue;
+  const int64_t P = (int64_t)d.T * d.top_k;
+  const int xs_bytes = kDownChunk * d.K * 2;
+  const size_t lds_d = (size_t)xs_bytes + (size_t)(d.K / 64) * d.top_k * 16 * 4;
+  const size_t lds = std::max({pl.lds, lds_d, (size_t)g.T * g.E * 4});
+  const DecParams pd = dec_params(d, P, 0, xs_bytes);
+  const DecRouteParams r{dr.logits, dr.logits_out, dr.ksplit, g.T,
+                         dr.ids, dr.w, dr.counts, dr.offsets, dr.sorted_pairs, dr.pair_slot,
+                         dr.blocks, dr.num_blocks};
+  // gate/up workgroups: what the chip holds at once, less the down
+  // workgroups when those take at most half of it, so the down half starts
+  // with the gate/up half (routing, its first weights in flight) instead of
+  // after it
+  const int64_t slots = (int64_t)device_cus() * decode_per_cu(pl.threads, lds, 16);
+  const int64_t G2 = (int64_t)d.T * (d.N / 16);
+  const int64_t G1 = std::min<int64_t>(pl.items, 2 * G2 <= slots ? slots - G2 : slots);
+  const int64_t grid = G1 + G2;
+  switch ((g.E + 63) / 64) {
+    case 1: launch_layer_nk<1>(r, pl.p, pd, pl.wide, grid, pl.threads, lds, y, residual, out, sync, (int)G1, s); break;
+    case 2: launch_layer_nk<2>(r, pl.p, pd, pl.wide, grid, pl.threads, lds, y, residual, out, sync, (int)G1, s); break;
+    case 3: launch_layer_nk<3>(r, pl.p, pd, pl.wide, grid, pl.threads, lds, y, residual, out, sync, (int)G1, s); break;
+    default: launch_layer_nk<4>(r, pl.p, pd, pl.wide, grid, pl.threads, lds, y, residual, out, sync, (int)G1, s); break;
+  }
   return hipGetLastError();
 }
 

@@ -412,6 +412,17 @@ bool decode_down_fused(int K);
 hipError_t launch_decode_down(const GemmArgs& a, const int32_t* ids, const int32_t* pair_slot,
                               float* y, hipStream_t s, const uint16_t* residual = nullptr,
                               uint16_t* out = nullptr);
+// Decode sizes, the whole layer in one launch (launch_decode_gate_up's and
+// launch_decode_down's work, identical results): g the gate/up product, d
+// the down product.  sync: device int32 [kDecodeSyncInts], zero before the
+// first call and left zero by every call (launches that share it must not
+// overlap); sync[257] is set if a wait gave up.  Needs
+// decode_layer_supported(g, d): both halves on workgroups of one size.
+constexpr int kDecodeSyncInts = 258;
+bool decode_layer_supported(const GemmArgs& g, const GemmArgs& d);
+hipError_t launch_decode_layer(const DecodeRouting& r, const GemmArgs& g, const GemmArgs& d, float* y,
+                               int32_t* sync, hipStream_t s, const uint16_t* residual = nullptr,
+                               uint16_t* out = nullptr);
 
 // S8: y[t] = sum_j y_sorted[pair_slot[t * k + j]], j ascending; y_sorted
 // fp32 (yexp == nullptr), or block floating point: int16 mantissas [P][H]

@@ -484,6 +484,65 @@ def test_ffn_decode_wide_shapes(orc):
         layer_output_check(orc, lay, y, info)
 
 
+# ---------------------------------------------- single-launch decode layer --
+def _single_vs_two(lay_dev, logits, sync, tag):
+    """One call of each path on the same inputs: every output and routing
+    structure identical, bit for bit; the counters back at zero, no wait
+    given up.  Returns the single-launch y and info."""
+    y2, i2 = api.ffn_forward(lay_dev, logits=logits, info=True)
+    y1, i1 = api.ffn_forward(lay_dev, logits=logits, info=True, sync=sync)
+    torch.cuda.synchronize()
+    assert i1["path"] == 1
+    assert torch.equal(y1, y2), f"{tag}: y differs"
+    for key in ("topk_ids", "topk_weights", "counts", "offsets", "sorted_pairs", "pair_slot"):
+        assert torch.equal(i1[key], i2[key]), f"{tag}: {key} differs"
+    nb = int(cpu(i1["num_blocks"])[0])
+    assert nb == int(cpu(i2["num_blocks"])[0])
+    assert torch.equal(i1["blocks"][:nb], i2["blocks"][:nb]), f"{tag}: block map differs"
+    assert torch.equal(i1["h"], i2["h"]) and torch.equal(i1["h_exp"], i2["h_exp"]), f"{tag}: h differs"
+    assert torch.equal(i1["y_sorted"], i2["y_sorted"]), f"{tag}: y_sorted differs"
+    s = cpu(sync)
+    assert not s.any(), f"{tag}: counters left {s[np.nonzero(s)]} at {np.nonzero(s)}"
+    return y1, i1
+
+
+@pytest.mark.parametrize("name", ["decode_t1", "decode_t8"])
+def test_ffn_single_launch_decode(orc, name):
+    """moe_ffn_forward_single (gate/up and down halves in one grid, down
+    workgroups waiting on per-expert counters): identical to the two-launch
+    layer on every output, on the oracle's bar, and on eight calls in a row
+    with fresh logits each (the counters return to zero; h is never read
+    before it is stored)."""
+    lay = synth.make_layer(name)
+    d = on_dev(lay)
+    sync = torch.zeros(api.single_sync_ints(), dtype=torch.int32, device=DEV)
+    y, info = _single_vs_two(d, d.logits, sync, name)
+    layer_output_check(orc, lay, y, info)
+    g = torch.Generator().manual_seed(97)
+    for i in range(8):
+        lg = torch.randn((lay.T, lay.E), generator=g).to(DEV)
+        _single_vs_two(d, lg, sync, f"{name} call {i}")
+
+
+def test_ffn_single_launch_shapes(orc):
+    """The single-launch layer at other decode shapes (the most pairs, one
+    expert of two, an odd E, a router weight with partial sums), against the
+    oracle and the two-launch path; shapes whose halves need workgroups of
+    different sizes are refused."""
+    sync = torch.zeros(api.single_sync_ints(), dtype=torch.int32, device=DEV)
+    cases = [dict(T=8, H=256, I=128, E=256, k=16, G=32, seed=91), dict(T=1, H=256, I=128, E=2, k=1, G=32, seed=92),
+             dict(T=7, H=512, I=256, E=5, k=3, G=64, seed=93),
+             dict(T=3, H=2048, I=512, E=64, k=4, G=64, seed=94, router="weight")]
+    for cfg in cases:
+        lay = synth.make_custom(**cfg)
+        d = on_dev(lay)
+        y, info = _single_vs_two(d, None if lay.router_weight is not None else d.logits, sync, str(cfg))
+        layer_output_check(orc, lay, y, info)
+    lay = on_dev(synth.make_custom(T=3, H=8192, I=128, E=6, k=2, G=64, seed=95))
+    with pytest.raises(RuntimeError, match="workgroups of one size"):
+        api.ffn_forward(lay, sync=sync)
+
+
 # ------------------------------------------------- either side of the layer --
 def _bf16_ulp(bits: np.ndarray) -> np.ndarray:
     v = np.abs((bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64))
