@@ -291,14 +291,20 @@ int moe_rmsnorm(const uint16_t* x, const uint16_t* gamma, float eps, int32_t T, 
                 uint16_t* out, void* stream);
 
 /* moe_ffn_forward_io: moe_ffn_forward with the steps around it.
- *  - io->norm_weight (bf16 [H], or NULL): x is first RMS-normalised
- *    (moe_rmsnorm, eps = io->norm_eps) into the workspace, and the layer
- *    (router included) runs on the normalised rows;
+ *  - io->norm_weight (bf16 [H], or NULL): the layer runs on the RMS-
+ *    normalised rows x_n = bf16(x * r * gamma), r = 1 / sqrt(mean x^2 +
+ *    io->norm_eps), computed as moe_rmsnorm computes them.  Where x is
+ *    staged anyway the normalisation is folded in (no launch of its own): at
+ *    T > 8 in the routing kernel, and at T <= 8 with logits given in the
+ *    gate/up launch; otherwise moe_rmsnorm runs first into the workspace.
+ *    At T > 8 with a router weight, the router sums r * bf16(x * gamma) * wr
+ *    (r applied after the sum), which is within 1.5 bf16 units of x_n per
+ *    term; the logits it returns in `info` are the ones routed;
  *  - io->out (bf16 [T][H], or NULL; needs io->residual, bf16 [T][H]): also
  *    out = bf16(residual + y), fp32 sum rounded to nearest even, written by
  *    the same launch that writes y.  y (fp32) is always written.
  * All device pointers, 16-byte aligned.  io == NULL behaves as
- * moe_ffn_forward.  workspace: >= moe_ffn_io_workspace_bytes (the
+ * moe_ffn_forward.  workspace: >= moe_ffn_io_workspace_bytes (room for the
  * normalised activations after moe_ffn_forward's workspace).  Errors as
  * moe_ffn_forward, plus MOE_ERR_NULL (out without residual) and MOE_ERR_ALIGN. */
 typedef struct {

@@ -462,8 +462,18 @@ int ffn_forward_impl(const moe_layer* layer, const uint16_t* x, const float* rou
   int64_t grid_tiles = -1;  // host-known tile count (host block map path)
   float* part = L.router_ks > 1 ? (float*)(ws + L.logits_part) : nullptr;  // router partial sums
   if ((err = mark(events, MOE_STAGE_ROUTE, s)) != hipSuccess) return hip_status(err, "event");
-  if (norm) {
-    // RMSNorm in front: the layer runs on the normalised rows
+  // RMSNorm in front: at prefill sizes folded into the routing front end
+  // (the router multiplies bf16(x * gamma), the routing kernel scales each
+  // row's logits by its 1 / rms and stages the normalised rows); otherwise
+  // its own launch, and the layer runs on the normalised rows
+  moe::GemmArgs shape{MOE_GEMM_GATE_UP_SWIGLU, d.T, d.top_k, d.E, d.I, d.H, d.group_size, block_m,
+                      nullptr, layer->gate, layer->up, nullptr, nullptr, nullptr, nullptr, nullptr};
+  // at decode sizes (logits given, every x row resident in the gate/up
+  // launch's LDS) folded into that launch's staging of x
+  const bool norm_folded = norm && !host && !expanded && !sync &&
+                           (gemv ? !has_router && moe::decode_norm_fits(shape)
+                                 : moe::route_norm_fits(d.T, d.H, d.E, has_router, L.router_ks > 1));
+  if (norm && !norm_folded) {
     uint16_t* xn = (uint16_t*)(ws + L.total);
     if ((err = moe::launch_rmsnorm(x, io->norm_weight, io->norm_eps, d.T, d.H, xn, s)) != hipSuccess)
       return hip_status(err, "rmsnorm");
@@ -480,7 +490,8 @@ int ffn_forward_impl(const moe_layer* layer, const uint16_t* x, const float* rou
     if ((err = mark(events, MOE_STAGE_BUILD_BLOCKS, s)) != hipSuccess) return hip_status(err, "event");
   } else {
     if ((err = moe::launch_route(x, layer->router_weight, logits, d.T, d.H, d.E, d.top_k, ids, w, xh,
-                                 chunk_hist, part, s)) != hipSuccess)
+                                 chunk_hist, part, s, norm_folded ? io->norm_weight : nullptr,
+                                 norm_folded ? io->norm_eps : 0.0f)) != hipSuccess)
       return hip_status(err, "route");
     if ((err = mark(events, MOE_STAGE_BUILD_BLOCKS, s)) != hipSuccess) return hip_status(err, "event");
     if (host) {
@@ -522,7 +533,8 @@ int ffn_forward_impl(const moe_layer* layer, const uint16_t* x, const float* rou
         return hip_status(err, "event");
       return ok();
     }
-    err = moe::launch_decode_gate_up(dr, g1, s);
+    err = moe::launch_decode_gate_up(dr, g1, s, norm_folded ? io->norm_weight : nullptr,
+                                     norm_folded ? io->norm_eps : 0.0f);
   } else if (expanded) {
     // unfused ablation: every expert's banks expanded to fp16 in HBM first
     uint32_t* eg = expanded;

@@ -41,6 +41,10 @@ struct DecParams {
   int red_off;     // byte offset of the partial-sum area in the dynamic LDS
   int lg_off = 0;  // fused decode gate/up: byte offset of the logits in the dynamic LDS
   bool x_res = false;  // fused decode gate/up: every x row resident in LDS ([T][K] at 0)
+  // fused decode gate/up with x_res: RMSNorm of the x rows in front (bf16
+  // [K], or nullptr), 1 / sqrt(mean x^2 + eps)
+  const uint16_t* gamma = nullptr;
+  float eps = 0.0f;
 };
 
 // One (tile, 32-column block) of the product: tile rows [row0, row0 + rows)
@@ -478,7 +482,7 @@ constexpr int kSpinLimit = 1 << 20;
 // rl, then items bid, bid + G, ....  READY (the single-launch layer): h is
 // stored device-coherent and, once a workgroup's item is stored, the item's
 // expert's count in ready is raised.
-template <int NK, int SPW, bool READY>
+template <int NK, int SPW, bool READY, bool NORM = false>
 __device__ __forceinline__ void decode_gate_up_body(const DecRouteParams& r, const DecParams& p, int bid,
                                                     int G, char* dsm, DecRouteLds& rl, int32_t* ready) {
   int* const cnt = rl.cnt;
@@ -512,12 +516,14 @@ __device__ __forceinline__ void decode_gate_up_body(const DecRouteParams& r, con
     ga[i] = p.t0.general[x] | p.t1.general[x];
   }
   const int c8n = K / 8, nx8 = p.x_res ? T * c8n : 0;
-  uint4 xv[4];
+  constexpr bool norm = NORM;  // (with x_res and gamma, checked by the launcher)
+  uint4 xv[4], gv[4];
 #pragma unroll
   for (int i = 0; i < 4; i++) {
     const int idx = min(tid + i * (int)blockDim.x, max(nx8 - 1, 0));
     xv[i] = p.x_res ? *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p.a) + 8 * (size_t)idx)
                     : make_uint4(0, 0, 0, 0);
+    if constexpr (NORM) gv[i] = reinterpret_cast<const uint4*>(p.gamma)[idx % c8n];
   }
   // 1. logits: partial sums over ranges of H added in range order
   const size_t part = (size_t)T * E;
@@ -535,14 +541,57 @@ __device__ __forceinline__ void decode_gate_up_body(const DecRouteParams& r, con
       gen_s[x] = ga[i] != 0;
     }
     const int idx = tid + i * blockDim.x;
-    if (idx < nx8)  // x row idx / c8n, 8-element chunk idx % c8n (row stride K)
-      *reinterpret_cast<uint4*>(reinterpret_cast<half_t*>(dsm) + 8 * (size_t)idx) = bf16x8_to_half_interleaved(xv[i]);
+    if (idx < nx8)  // x row idx / c8n, 8-element chunk idx % c8n (row stride K); raw bf16 with RMSNorm
+      *reinterpret_cast<uint4*>(reinterpret_cast<half_t*>(dsm) + 8 * (size_t)idx) =
+          norm ? xv[i] : bf16x8_to_half_interleaved(xv[i]);
   }
   for (int i = tid; i < E; i += blockDim.x) {
     cnt[i] = 0;
     tokmask[i] = 0u;
   }
   __syncthreads();
+  if constexpr (NORM) {
+    // RMSNorm in front: each row's 1 / rms by a wave, from the raw rows in
+    // LDS, in moe_rmsnorm's order of operations (so the normalised rows equal
+    // its output bit for bit); then every thread writes its pieces as the
+    // normalised fp16 operand over the raw ones
+    __shared__ float rn_s[kGemvMaxTokens];
+    const int lane = tid & 63;
+    const uint4* xr = reinterpret_cast<const uint4*>(dsm);
+    for (int t = wave; t < T; t += nwaves) {
+      float ss = 0.0f;
+      for (int c = lane; c < c8n; c += 64) {
+        const uint4 v = xr[t * c8n + c];
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 4; e++) {
+          const float a = __uint_as_float(w[e] << 16), b = __uint_as_float(w[e] & 0xFFFF0000u);
+          ss += a * a;
+          ss += b * b;
+        }
+      }
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
+      if (lane == 0) rn_s[t] = 1.0f / sqrtf(ss / (float)K + p.eps);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int idx = tid + i * blockDim.x;
+      if (idx < nx8) {
+        const float rr = rn_s[idx / c8n];
+        const uint32_t w[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w}, g[4] = {gv[i].x, gv[i].y, gv[i].z, gv[i].w};
+        uint32_t o[4];
+#pragma unroll
+        for (int e = 0; e < 4; e++)
+          o[e] = f32_to_bf16_rne(__uint_as_float(w[e] << 16) * rr * __uint_as_float(g[e] << 16)) |
+                 (f32_to_bf16_rne(__uint_as_float(w[e] & 0xFFFF0000u) * rr * __uint_as_float(g[e] & 0xFFFF0000u))
+                  << 16);
+        *reinterpret_cast<uint4*>(reinterpret_cast<half_t*>(dsm) + 8 * (size_t)idx) =
+            bf16x8_to_half_interleaved(make_uint4(o[0], o[1], o[2], o[3]));
+      }
+    }
+  }
   // 2. top-k and combine weights, a wave per token, with the expert counts
   for (int t = wave; t < T; t += nwaves) topk_token<NK>(lg + t * E, E, k, ids_s + t * k, w_s + t * k, cnt);
   __syncthreads();
@@ -667,12 +716,12 @@ __device__ __forceinline__ void decode_gate_up_body(const DecRouteParams& r, con
   if (READY && pending >= 0) signal(pending);
 }
 
-template <int NK, int SPW>
+template <int NK, int SPW, bool NORM>
 __global__ __launch_bounds__(64 * kDecWavesMax) void decode_gate_up_kernel(const DecRouteParams r,
                                                                           const DecParams p) {
   extern __shared__ __attribute__((aligned(16))) char dsm[];
   __shared__ DecRouteLds rl;
-  decode_gate_up_body<NK, SPW, false>(r, p, blockIdx.x, gridDim.x, dsm, rl, nullptr);
+  decode_gate_up_body<NK, SPW, false, NORM>(r, p, blockIdx.x, gridDim.x, dsm, rl, nullptr);
 }
 
 // Decode sizes, S7 and S8 in one launch, organised per token: workgroup
@@ -1049,8 +1098,13 @@ int device_cus() {
 template <int NK>
 static void launch_decode_nk(const DecRouteParams& r, const DecParams& p, bool wide, int64_t grid,
                              int threads, size_t lds, hipStream_t s) {
-  if (wide) decode_gate_up_kernel<NK, 4><<<grid, threads, lds, s>>>(r, p);
-  else decode_gate_up_kernel<NK, 2><<<grid, threads, lds, s>>>(r, p);
+  if (p.gamma) {
+    if (wide) decode_gate_up_kernel<NK, 4, true><<<grid, threads, lds, s>>>(r, p);
+    else decode_gate_up_kernel<NK, 2, true><<<grid, threads, lds, s>>>(r, p);
+  } else {
+    if (wide) decode_gate_up_kernel<NK, 4, false><<<grid, threads, lds, s>>>(r, p);
+    else decode_gate_up_kernel<NK, 2, false><<<grid, threads, lds, s>>>(r, p);
+  }
 }
 
 // Launch shape of the gate/up half at decode sizes.
@@ -1108,10 +1162,19 @@ static int decode_per_cu(int threads, size_t lds, int static_kib) {
   return std::max(1, std::min<int>(16 / (threads / 64), (int)((160 * 1024) / (lds + static_kib * 1024))));
 }
 
-hipError_t launch_decode_gate_up(const DecodeRouting& dr, const GemmArgs& a, hipStream_t s) {
+bool decode_norm_fits(const GemmArgs& a) {
+  DecGateUpPlan pl;
+  return decode_gate_up_plan(a, pl) && pl.p.x_res;
+}
+
+hipError_t launch_decode_gate_up(const DecodeRouting& dr, const GemmArgs& a, hipStream_t s,
+                                 const uint16_t* gamma, float eps) {
   if (a.T <= 0) return hipSuccess;
   DecGateUpPlan pl;
   if (!decode_gate_up_plan(a, pl)) return hipErrorInvalidValue;
+  if (gamma && !pl.p.x_res) return hipErrorInvalidValue;
+  pl.p.gamma = gamma;
+  pl.p.eps = eps;
   const DecRouteParams r{dr.logits, dr.logits_out, dr.ksplit, a.T,
                          dr.ids, dr.w, dr.counts, dr.offsets, dr.sorted_pairs, dr.pair_slot,
                          dr.blocks, dr.num_blocks};

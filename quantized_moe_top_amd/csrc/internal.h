@@ -328,9 +328,14 @@ int router_ksplit(int64_t T, int64_t H, int64_t E);
 // S0 (when wr) + S1 over all T tokens; with xh and chunk_hist (both or
 // neither) also the per-chunk expert histogram and the fp16 staging of x.
 // part (or nullptr): scratch for the router's partial sums.
+// gamma (bf16 [H], with xh): RMSNorm in front, folded in: the router sums
+// bf16(x * gamma) * wr and the routing kernel scales each row's logits by
+// its 1 / sqrt(mean x^2 + eps) (written back to logits), and xh holds the
+// normalised rows bf16(x * r * gamma); needs route_norm_fits.
+bool route_norm_fits(int64_t T, int64_t H, int64_t E, bool has_router, bool split);
 hipError_t launch_route(const uint16_t* x, const uint16_t* wr, float* logits, int T, int H, int E,
                         int k, int32_t* ids, float* w, half_t* xh, int32_t* chunk_hist,
-                        float* part, hipStream_t s);
+                        float* part, hipStream_t s, const uint16_t* gamma = nullptr, float eps = 0.0f);
 // S0 alone: the router logits (ksplit == 1) or ksplit partial sums over
 // ranges of H (ksplit == router_ksplit(T, H, E)) into out, [ksplit][T][E].
 hipError_t launch_router_logits(const uint16_t* x, const uint16_t* wr, float* out, int T, int H,
@@ -404,7 +409,11 @@ struct DecodeRouting {
   float* w;
   int32_t *counts, *offsets, *sorted_pairs, *pair_slot, *blocks, *num_blocks;
 };
-hipError_t launch_decode_gate_up(const DecodeRouting& r, const GemmArgs& a, hipStream_t s);
+// gamma (bf16 [K], or nullptr): RMSNorm of x in front, folded into the
+// staging of the x rows; needs decode_norm_fits(a) (every row resident).
+bool decode_norm_fits(const GemmArgs& a);
+hipError_t launch_decode_gate_up(const DecodeRouting& r, const GemmArgs& a, hipStream_t s,
+                                 const uint16_t* gamma = nullptr, float eps = 0.0f);
 // Decode sizes: S7 and S8 in one launch, per token (a.a: h; a.out: y_sorted
 // fp32 [T * k][N], written too; ids, pair_slot: [T * k]; y: [T][N]).  Needs
 // decode_down_fused(K): a reduction of at most 16 slabs of 64.

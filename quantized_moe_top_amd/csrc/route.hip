@@ -63,13 +63,31 @@ __device__ __forceinline__ void wait_vm_barrier_n(int n) {
 struct RouterParams {
   const uint16_t* x;   // bf16 [T][H]
   const uint16_t* wr;  // bf16 [E][H]
+  const uint16_t* gamma;  // bf16 [H]: the A operand is bf16(x * gamma) (NORM), or nullptr
   float* logits;       // fp32 [ksplit][T][E]: the logits, or partial sums over H / ksplit
   half_t* xh;          // fp16 [T][H] operand copy, or nullptr
   int T, H, E, n_et;   // n_et: expert tiles
   int ksplit;          // H ranges (the grid is token tiles x n_et x ksplit)
 };
 
-template <int TMB, int TEB, int R>
+// Elementwise bf16(a * g) of eight bf16 pairs, rounded to nearest even.
+__device__ __forceinline__ u32x4 bf16x8_mul(u32x4 a, u32x4 g) {
+  typedef __bf16 bf16x2_v __attribute__((ext_vector_type(2)));
+  typedef float float2_v __attribute__((ext_vector_type(2)));
+  u32x4 o;
+#pragma unroll
+  for (int i = 0; i < 4; i++) {
+    const float2_v v = {__uint_as_float(a[i] << 16) * __uint_as_float(g[i] << 16),
+                        __uint_as_float(a[i] & 0xFFFF0000u) * __uint_as_float(g[i] & 0xFFFF0000u)};
+    o[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_v));
+  }
+  return o;
+}
+
+// Gamma values one workgroup of the router stages (its range of H).
+constexpr int kRouterGamma = 4096;
+
+template <int TMB, int TEB, int R, bool NORM>
 __global__ __launch_bounds__(256) void router_kernel(const RouterParams p) {
   constexpr int NBLK = TMB * TEB;
   static_assert(NBLK == 1 || ((TMB == 2 || TMB == 4) && (TEB == 2 || TEB == 4)), "block split");
@@ -84,6 +102,7 @@ __global__ __launch_bounds__(256) void router_kernel(const RouterParams p) {
   constexpr int X = TMB;                        // operand-copy stores per thread and slab
   static_assert(R >= 3 && (R - 1) * (D + X) < 64, "ring depth within the vmcnt range");
   __shared__ __attribute__((aligned(16))) char ring[R * STAGE];
+  __shared__ __attribute__((aligned(16))) uint16_t gam[NORM ? kRouterGamma : 8];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kz = blockIdx.x % p.ksplit, tile = blockIdx.x / p.ksplit;
@@ -125,6 +144,18 @@ __global__ __launch_bounds__(256) void router_kernel(const RouterParams p) {
   floatx16_t acc[NBW];
 #pragma unroll
   for (int b = 0; b < NBW; b++) acc[b] = floatx16_t{};
+  if constexpr (NORM) {
+    // gamma over this workgroup's slabs (128 S bytes <= sizeof gam) into LDS
+    // ahead of the ring: every wave's wait for slab 0 also covers these
+    // copies, since loads complete in issue order
+    const int nb = 128 * S;
+    for (int q = wave; 1024 * q < nb; q += 4)
+      lds_load16(reinterpret_cast<const char*>(p.gamma + 64 * s0) + min(1024 * q + 16 * lane, nb - 16),
+                 reinterpret_cast<char*>(gam) + 1024 * q);
+  }
+  // NORM: the gamma fragment matching frag(.., j): columns 16 j + 8 half .. + 7
+  // of slab s
+  auto gfrag = [&](int s, int j) { return lds_read16(gam + 64 * s + 16 * j + 8 * (lane >> 5)); };
 #pragma unroll
   for (int j = 0; j < R - 1; j++) issue(min(j, S - 1), j);
   for (int s = 0; s < S; s++) {
@@ -137,7 +168,14 @@ __global__ __launch_bounds__(256) void router_kernel(const RouterParams p) {
     const char* base = ring + (s % R) * STAGE;
     if constexpr (KSPLIT) {
       u32x4 a = frag(base, 0, wave), b = frag(base, RX, wave);
-      lds_wait(a, b);
+      if constexpr (NORM) {
+        u32x4 g = gfrag(s, wave);
+        lds_wait(a, b);
+        lds_tie(g);
+        a = bf16x8_mul(a, g);
+      } else {
+        lds_wait(a, b);
+      }
       acc[0] = mfma(a, b, acc[0]);
     } else {
       // every fragment of the slab first, one wait, then the MFMAs
@@ -149,13 +187,23 @@ __global__ __launch_bounds__(256) void router_kernel(const RouterParams p) {
 #pragma unroll
         for (int e = 0; e < EW; e++) b[j][e] = frag(base, RX + 32 * (EW * (wave >> 1) + e), j);
       }
+      u32x4 g[4];
+      if constexpr (NORM)
+#pragma unroll
+        for (int j = 0; j < 4; j++) g[j] = gfrag(s, j);
 #pragma unroll
       for (int j = 0; j < 4; j++) {
 #pragma unroll
         for (int m = 0; m < MW; m++) lds_wait(a[j][m]);
 #pragma unroll
         for (int e = 0; e < EW; e++) lds_wait(b[j][e]);
+        if constexpr (NORM) lds_wait(g[j]);
       }
+      if constexpr (NORM)
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+#pragma unroll
+          for (int m = 0; m < MW; m++) a[j][m] = bf16x8_mul(a[j][m], g[j]);
 #pragma unroll
       for (int j = 0; j < 4; j++)
 #pragma unroll
@@ -245,16 +293,25 @@ RouterPlan router_plan(int64_t T, int64_t H, int64_t E, bool split) {
   return RouterPlan{cand[best][0], cand[best][1], ks};
 }
 
+template <bool NORM>
+void launch_router_plan(const RouterPlan& pl, const RouterParams& p, int64_t grid, hipStream_t s) {
+  if (pl.tm == 1) router_kernel<1, 1, 9, NORM><<<grid, 256, 0, s>>>(p);  // ring depths: <= 128 KiB
+  else if (pl.te == 2) router_kernel<2, 2, 8, NORM><<<grid, 256, 0, s>>>(p);
+  else if (pl.tm == 2) router_kernel<2, 4, 5, NORM><<<grid, 256, 0, s>>>(p);
+  else router_kernel<4, 4, 4, NORM><<<grid, 256, 0, s>>>(p);
+}
+
+// gamma (bf16 [H], or nullptr): the router multiplies bf16(x * gamma); its
+// range of H per workgroup must fit kRouterGamma (router_gamma_fits).
 hipError_t launch_router(const uint16_t* x, const uint16_t* wr, float* logits, half_t* xh, int T,
-                         int H, int E, int ksplit, hipStream_t s) {
+                         int H, int E, int ksplit, hipStream_t s, const uint16_t* gamma = nullptr) {
   const RouterPlan pl = router_plan(T, H, E, ksplit > 1);
   if (pl.ksplit != ksplit) return hipErrorInvalidValue;  // the caller sized its buffer for ksplit
-  RouterParams p{x, wr, logits, xh, T, H, E, (E + 32 * pl.te - 1) / (32 * pl.te), ksplit};
+  if (gamma && H / ksplit > kRouterGamma) return hipErrorInvalidValue;
+  RouterParams p{x, wr, gamma, logits, xh, T, H, E, (E + 32 * pl.te - 1) / (32 * pl.te), ksplit};
   const int64_t grid = (int64_t)((T + 32 * pl.tm - 1) / (32 * pl.tm)) * p.n_et * ksplit;
-  if (pl.tm == 1) router_kernel<1, 1, 9><<<grid, 256, 0, s>>>(p);  // ring depths: <= 128 KiB
-  else if (pl.te == 2) router_kernel<2, 2, 8><<<grid, 256, 0, s>>>(p);
-  else if (pl.tm == 2) router_kernel<2, 4, 5><<<grid, 256, 0, s>>>(p);
-  else router_kernel<4, 4, 4><<<grid, 256, 0, s>>>(p);
+  if (gamma) launch_router_plan<true>(pl, p, grid, s);
+  else launch_router_plan<false>(pl, p, grid, s);
   return hipGetLastError();
 }
 
@@ -271,6 +328,12 @@ struct RouteParams {
   int T, H, E, k, chunk_tokens;
   int lpt_log2;         // lanes per token in the top-k (log2)
   bool stage_x;         // write xh here (false when the router kernel did)
+  // RMSNorm in front (gamma != nullptr): xh holds the normalised rows, and
+  // with scale_logits the logits (the router's sums over bf16(x * gamma))
+  // are multiplied by each row's 1 / rms
+  const uint16_t* gamma;
+  float eps;
+  bool scale_logits;
 };
 
 
@@ -414,22 +477,108 @@ __device__ __forceinline__ void topk_group(const float* l, int E, int k, int sub
   }
 }
 
+// bf16(x * r * gamma), nearest even, of eight bf16 pairs (the normalised
+// values, in moe_rmsnorm's order of operations).
+__device__ __forceinline__ uint4 norm_bf16x8(uint4 v, uint4 g, float r) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w}, gw[4] = {g.x, g.y, g.z, g.w};
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; i++)
+    o[i] = f32_to_bf16_rne(__uint_as_float(w[i] << 16) * r * __uint_as_float(gw[i] << 16)) |
+           (f32_to_bf16_rne(__uint_as_float(w[i] & 0xFFFF0000u) * r * __uint_as_float(gw[i] & 0xFFFF0000u))
+            << 16);
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// The RMSNorm of the RMSNorm step's definition, row by row: 1 / rms of
+// tokens [t0, t0 + nt) into rn[0 .. nt), a wave per row.  The same
+// arithmetic as moe_rmsnorm (fp32 squares of each lane's 16-byte pieces in
+// order, a butterfly over the lanes, 1 / sqrt(mean + eps)), so the
+// normalised rows equal its output bit for bit.
+// Each wave takes two rows at a time and requests up to 8 pieces per lane
+// of both before adding (H <= 4096 in one round trip per row pair).  With
+// stage (and H <= 4096), the wave also writes the pair's normalised rows
+// to xh from the pieces it holds, so x is read once.
+// The calling wave is wave w of NW taking part.
+__device__ void norm_rows(const RouteParams& p, int t0, int nt, float* rn, bool stage, int w, int NW) {
+  constexpr int B = 8;
+  const int lane = threadIdx.x & 63, H8 = p.H / 8;
+  const uint4* gam = reinterpret_cast<const uint4*>(p.gamma);
+  for (int r = w; r < nt; r += 2 * NW) {
+    const int r2 = min(r + NW, nt - 1);  // the pair's second row (a repeat past the pass)
+    const uint4* xa = reinterpret_cast<const uint4*>(p.x + (size_t)(t0 + r) * p.H);
+    const uint4* xb = reinterpret_cast<const uint4*>(p.x + (size_t)(t0 + r2) * p.H);
+    float ss[2] = {0.0f, 0.0f};
+    uint4 v[2][B], g[B];
+    for (int c0 = 0; c0 < H8; c0 += 64 * B) {
+#pragma unroll
+      for (int i = 0; i < B; i++) {
+        const int c = min(c0 + lane + 64 * i, H8 - 1);
+        v[0][i] = xa[c];
+        v[1][i] = xb[c];
+        if (stage) g[i] = gam[c];
+      }
+#pragma unroll
+      for (int q = 0; q < 2; q++)
+#pragma unroll
+        for (int i = 0; i < B; i++) {
+          if (c0 + lane + 64 * i >= H8) break;
+          const uint32_t w[4] = {v[q][i].x, v[q][i].y, v[q][i].z, v[q][i].w};
+#pragma unroll
+          for (int e = 0; e < 4; e++) {
+            const float a = __uint_as_float(w[e] << 16), b = __uint_as_float(w[e] & 0xFFFF0000u);
+            ss[q] += a * a;
+            ss[q] += b * b;
+          }
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < 2; q++) {
+#pragma unroll
+      for (int m = 32; m >= 1; m >>= 1) ss[q] += __shfl_xor(ss[q], m);
+    }
+    const float ra = 1.0f / sqrtf(ss[0] / (float)p.H + p.eps), rb = 1.0f / sqrtf(ss[1] / (float)p.H + p.eps);
+    if (lane == 0) {
+      rn[r] = ra;
+      if (r + NW < nt) rn[r + NW] = rb;
+    }
+    if (stage) {  // H8 <= 64 B: v holds the whole pair
+      uint4* oa = reinterpret_cast<uint4*>(p.xh + (size_t)(t0 + r) * p.H);
+      uint4* ob = reinterpret_cast<uint4*>(p.xh + (size_t)(t0 + r2) * p.H);
+#pragma unroll
+      for (int i = 0; i < B; i++) {
+        const int c = lane + 64 * i;
+        if (c >= H8) break;
+        oa[c] = bf16x8_to_half_interleaved(norm_bf16x8(v[0][i], g[i], ra));
+        if (r + NW < nt) ob[c] = bf16x8_to_half_interleaved(norm_bf16x8(v[1][i], g[i], rb));
+      }
+    }
+  }
+}
+
 // bf16 -> fp16 of tokens [t0, t0 + nt), each 8-element chunk reordered to
-// (0,4,1,5,2,6,3,7).  Loads use clamped indices so that each batch of U is
-// issued together.
-__device__ void stage_rows(const RouteParams& p, int t0, int nt) {
-  const int n = nt * (p.H / 8);
+// (0,4,1,5,2,6,3,7); with gamma, of the normalised rows (rn: each row's
+// 1 / rms).  Loads use clamped indices so that each batch of U is issued
+// together.
+// Threads [0, nth) take part; the caller's index is tid.
+__device__ void stage_rows(const RouteParams& p, int t0, int nt, const float* rn, int tid, int nth) {
+  const int H8 = p.H / 8, n = nt * H8;
   const uint4* in = reinterpret_cast<const uint4*>(p.x + (size_t)t0 * p.H);
+  const uint4* gam = reinterpret_cast<const uint4*>(p.gamma);
   uint4* out = reinterpret_cast<uint4*>(p.xh + (size_t)t0 * p.H);
   constexpr int U = 8;
-  for (int i0 = threadIdx.x; i0 < n; i0 += kRouteThreads * U) {
-    uint4 v[U];
-#pragma unroll
-    for (int u = 0; u < U; u++) v[u] = in[min(i0 + u * kRouteThreads, n - 1)];
+  for (int i0 = tid; i0 < n; i0 += nth * U) {
+    uint4 v[U], g[U];
 #pragma unroll
     for (int u = 0; u < U; u++) {
-      const int i = i0 + u * kRouteThreads;
-      if (i < n) out[i] = bf16x8_to_half_interleaved(v[u]);
+      const int i = min(i0 + u * nth, n - 1);
+      v[u] = in[i];
+      if (gam) g[u] = gam[i % H8];
+    }
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      const int i = i0 + u * nth;
+      if (i < n) out[i] = bf16x8_to_half_interleaved(gam ? norm_bf16x8(v[u], g[u], rn[i / H8]) : v[u]);
     }
   }
 }
@@ -438,12 +587,14 @@ __device__ void stage_rows(const RouteParams& p, int t0, int nt) {
 // the lane groups of a wave read different LDS banks).  With partial sums
 // over ranges of H, they are added in range order (deterministic) and the
 // sums also written to logits_out.
-__device__ void load_logits(const RouteParams& p, int t0, int nt, float* lg, int stride) {
+// Threads [0, nth) take part; the caller's index is tid.  With
+// scale_logits the sums are left unscaled (scale_logits_pass follows).
+__device__ void load_logits(const RouteParams& p, int t0, int nt, float* lg, int stride, int tid, int nth) {
   const int n = nt * p.E;
   const size_t part = (size_t)p.T * p.E;
   const float* src = p.logits + (size_t)t0 * p.E;
   constexpr int U = 8;
-  for (int i0 = threadIdx.x; i0 < n; i0 += kRouteThreads * U) {
+  for (int i0 = tid; i0 < n; i0 += nth * U) {
     // every partial of the batch is loaded before the first add (one round
     // trip); at most kMaxSplit ranges
     float v[kMaxSplit][U];
@@ -451,7 +602,7 @@ __device__ void load_logits(const RouteParams& p, int t0, int nt, float* lg, int
     for (int z = 0; z < kMaxSplit; z++)
       if (z < p.ksplit)
 #pragma unroll
-        for (int u = 0; u < U; u++) v[z][u] = src[z * part + min(i0 + u * kRouteThreads, n - 1)];
+        for (int u = 0; u < U; u++) v[z][u] = src[z * part + min(i0 + u * nth, n - 1)];
 #pragma unroll
     for (int z = 1; z < kMaxSplit; z++)
       if (z < p.ksplit)
@@ -459,13 +610,24 @@ __device__ void load_logits(const RouteParams& p, int t0, int nt, float* lg, int
         for (int u = 0; u < U; u++) v[0][u] += v[z][u];
 #pragma unroll
     for (int u = 0; u < U; u++) {
-      const int i = i0 + u * kRouteThreads;
+      const int i = i0 + u * nth;
       if (i < n) {
         const int r = i / p.E;
         lg[r * stride + (i - r * p.E)] = v[0][u];
-        if (p.ksplit > 1) p.logits_out[(size_t)t0 * p.E + i] = v[0][u];
+        if (p.ksplit > 1 && !p.scale_logits) p.logits_out[(size_t)t0 * p.E + i] = v[0][u];
       }
     }
+  }
+}
+
+// The pass's logits times each row's 1 / rms, in LDS and to logits_out.
+__device__ void scale_logits_pass(const RouteParams& p, int t0, int nt, float* lg, int stride, const float* rn) {
+  const int n = nt * p.E;
+  for (int i = threadIdx.x; i < n; i += kRouteThreads) {
+    const int r = i / p.E;
+    float& l = lg[r * stride + (i - r * p.E)];
+    l = l * rn[r];
+    p.logits_out[(size_t)t0 * p.E + i] = l;
   }
 }
 
@@ -476,6 +638,7 @@ template <bool FULL, int A, int LPT>
 __device__ __forceinline__ void route_chunk(const RouteParams& p, int chunk) {
   __shared__ float lg[kLgFloats];
   __shared__ int hist[256];
+  __shared__ float rn[kRouteThreads / 8];  // 1 / rms of the pass's rows (gamma)
   const int tid = threadIdx.x;
   constexpr int tp = kRouteThreads / LPT;
   const int stride = p.E + LPT;
@@ -485,9 +648,23 @@ __device__ __forceinline__ void route_chunk(const RouteParams& p, int chunk) {
   const int c1 = min(p.T, c0 + p.chunk_tokens);
   for (int t0 = c0; t0 < c1; t0 += tp) {
     const int nt = min(tp, c1 - t0);
-    load_logits(p, t0, nt, lg, stride);
-    if (FULL && p.stage_x) stage_rows(p, t0, nt);
+    // with rows to stage or normalise, waves 0-3 load the logits while
+    // waves 4-7 stage the rows, or (RMSNorm) take the rows' 1 / rms and, for
+    // H <= 4096, stage the normalised rows from the same loads; then (with
+    // a router weight) the logits are scaled by 1 / rms
+    const int wave = tid >> 6;
+    const bool stage = FULL && p.stage_x;
+    const bool fused_stage = stage && p.gamma && p.H <= 64 * 8 * 8;
+    if (!stage && !p.gamma) load_logits(p, t0, nt, lg, stride, tid, kRouteThreads);
+    else if (wave < 4) load_logits(p, t0, nt, lg, stride, tid, 256);
+    else if (p.gamma) norm_rows(p, t0, nt, rn, fused_stage, wave - 4, 4);
+    else stage_rows(p, t0, nt, rn, tid - 256, 256);
     __syncthreads();
+    if (p.gamma) {
+      if (p.scale_logits) scale_logits_pass(p, t0, nt, lg, stride, rn);
+      if (stage && !fused_stage) stage_rows(p, t0, nt, rn, tid, kRouteThreads);
+      __syncthreads();
+    }
     if (grp < nt)
     {
       int32_t* ids = p.ids + (size_t)(t0 + grp) * p.k;
@@ -553,18 +730,27 @@ int route_chunks(int64_t T) {
 
 int router_ksplit(int64_t T, int64_t H, int64_t E) { return router_plan(T, H, E, true).ksplit; }
 
+bool route_norm_fits(int64_t T, int64_t H, int64_t E, bool has_router, bool split) {
+  return !has_router || H / router_plan(T, H, E, split).ksplit <= kRouterGamma;
+}
+
 hipError_t launch_route(const uint16_t* x, const uint16_t* wr, float* logits, int T, int H, int E,
                         int k, int32_t* ids, float* w, half_t* xh, int32_t* chunk_hist,
-                        float* part, hipStream_t s) {
+                        float* part, hipStream_t s, const uint16_t* gamma, float eps) {
   if (T <= 0) return hipSuccess;
+  if (gamma && !xh) return hipErrorInvalidValue;  // the normalised rows exist only as xh
   const int ks = wr && part ? router_ksplit(T, H, E) : 1;
   if (wr) {
-    const hipError_t err = launch_router(x, wr, ks > 1 ? part : logits, xh, T, H, E, ks, s);
+    // with RMSNorm the routing kernel writes xh (it knows each row's rms);
+    // otherwise the router does, from the slabs it stages anyway
+    const hipError_t err = launch_router(x, wr, ks > 1 ? part : logits, gamma ? nullptr : xh, T, H, E, ks,
+                                         s, gamma);
     if (err != hipSuccess) return err;
   }
   const int ct = route_chunk_tokens(T);
   RouteParams p{x, ks > 1 ? part : logits, logits, ks, ids, w, xh, chunk_hist, T, H, E, k, ct,
-                route_lpt_log2(ct, E), wr == nullptr};
+                route_lpt_log2(ct, E), wr == nullptr || gamma != nullptr, gamma, eps,
+                wr != nullptr && gamma != nullptr};
   const int n = route_chunks(T);
   return xh ? launch_route_l<true>(p, n, s) : launch_route_l<false>(p, n, s);
 }

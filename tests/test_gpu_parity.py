@@ -11,8 +11,8 @@ import pytest
 import torch
 
 import oracle
-from gpu_helpers import (assert_fp_close, assert_weights_close, cpu, f32_ulp, h_natural, h_values,
-                         router_error_bound, say)
+from gpu_helpers import (MAX_ABS_OVER_RMS, REL_L2_MAX, assert_fp_close, assert_weights_close, cpu, f32_ulp,
+                         h_natural, h_values, router_error_bound, say)
 from oracle_pins import check_blocks_invariants
 from quantized_moe_top_amd import api, synth
 
@@ -569,19 +569,32 @@ def test_rmsnorm(orc):
         assert same >= 0.999, (T, H, same)
 
 
-@pytest.mark.parametrize("case", ["mfma_t300", "decode_t5", "router_t40", "decode_router_t3"])
+@pytest.mark.parametrize("case", ["mfma_t300", "decode_t5", "router_t40", "decode_router_t3", "router_t9000",
+                                  "mfma_t20001", "decode_t1_full", "decode_t8_full"])
 def test_ffn_io(orc, case):
     """moe_ffn_forward_io: RMSNorm in front and out = bf16(residual + y)
     behind, against the oracle's normalisation, layer and residual sum.
     Logits given: the routing does not depend on the normalised rows and is
-    compared bit-exactly; with a router weight the GPU's logits (from its own
-    normalised rows) are routed by the oracle and compared bit-exactly, and
-    checked against the oracle's logits to within the normalisation's one
-    bf16 unit."""
+    compared bit-exactly; with a router weight the GPU's logits are routed by
+    the oracle and compared bit-exactly, and checked against the oracle's
+    logits.  At prefill sizes the router sums r * bf16(x * gamma) * wr (the
+    row's factor r applied after the sum): each term's normalised input is
+    within 1.5 bf16 units of the oracle's bf16(x * gamma * r) (half a unit of
+    x * gamma, scaled by r, is at most one unit of the product; plus the
+    oracle's own half unit), and r carries a few fp32 roundings; at decode
+    sizes the rows are normalised first (within one unit)."""
     cfg = {"mfma_t300": dict(T=300, H=512, I=256, E=16, k=4, G=64, seed=81),
            "decode_t5": dict(T=5, H=512, I=256, E=16, k=4, G=64, seed=82),
            "router_t40": dict(T=40, H=512, I=256, E=32, k=4, G=64, seed=83, router="weight"),
-           "decode_router_t3": dict(T=3, H=256, I=128, E=8, k=2, G=32, seed=84, router="weight")}[case]
+           "decode_router_t3": dict(T=3, H=256, I=128, E=8, k=2, G=32, seed=84, router="weight"),
+           # routing chunks of 40 and 80 tokens: passes of 64 rows, several
+           # row pairs per wave in the folded normalisation, a partial pass
+           "router_t9000": dict(T=9000, H=256, I=128, E=16, k=4, G=64, seed=85, router="weight"),
+           "mfma_t20001": dict(T=20001, H=256, I=128, E=8, k=2, G=32, seed=86),
+           # the decode workloads' shape: the normalisation folded into the
+           # gate/up launch's staging of x
+           "decode_t1_full": dict(T=1, H=2048, I=512, E=128, k=8, G=64, seed=87),
+           "decode_t8_full": dict(T=8, H=2048, I=512, E=128, k=8, G=64, seed=88)}[case]
     lay = synth.make_custom(**cfg)
     g = torch.Generator().manual_seed(cfg["seed"] + 100)
     gamma = (torch.rand(lay.H, generator=g) * 1.5 + 0.25).to(torch.bfloat16)
@@ -601,7 +614,7 @@ def test_ffn_io(orc, case):
         wr = np.abs(lay.router_weight.float().numpy().astype(np.float64))
         xv = (xn.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
         bound = router_error_bound(torch.from_numpy(xv).to(torch.bfloat16), lay.router_weight) + \
-            (_bf16_ulp(xn) @ wr.T) + f32_ulp(l_ref)
+            1.5 * (_bf16_ulp(xn) @ wr.T) + 4 * f32_ulp(np.abs(xv) @ wr.T)
         assert np.all(np.abs(l_used.astype(np.float64) - l_ref) <= bound)
     rid, rw = orc.route(l_used, lay.k)
     assert np.array_equal(cpu(info["topk_ids"]), rid)
@@ -611,7 +624,13 @@ def test_ffn_io(orc, case):
     out_ref = orc.residual_out(res, y_ref)
     ov = (cpu(out.view(torch.int16)).view(np.uint16).astype(np.uint32) << 16).view(np.float32)
     rv = (out_ref.astype(np.uint32) << 16).view(np.float32)
-    assert_fp_close(ov, rv, f"{case} out")
+    # out is rounded to bf16 on both sides: any difference in y can move a
+    # sum across a rounding boundary, so each element may also differ by one
+    # bf16 unit of out (2^-5 where |out| is in [4, 8))
+    ovd, rvd = ov.astype(np.float64), rv.astype(np.float64)
+    rms_out = float(np.sqrt(np.mean(rvd ** 2)))
+    assert np.linalg.norm(ovd - rvd) <= REL_L2_MAX * np.linalg.norm(rvd), f"{case} out rel L2"
+    assert np.all(np.abs(ovd - rvd) <= MAX_ABS_OVER_RMS * rms_out + _bf16_ulp(out_ref)), f"{case} out max abs"
     # out is bf16(residual + y) of the y returned beside it: the fp32 sum
     # rounded to bf16 can differ from the once-rounded exact sum by one unit
     # (double rounding), rarely
