@@ -143,7 +143,17 @@ typedef struct {
  * the softmax over the top_k selected logits.
  * Device pointers: x bf16 [T][H]; router_weight bf16 [E][H]; logits fp32
  * [T][E]; topk_ids int32 [T][top_k]; topk_weights fp32 [T][top_k].
- * With a router weight, H must be a positive multiple of 128. */
+ * With a router weight, H must be a positive multiple of 128.  The caller
+ * owns every buffer; nothing is allocated.  Errors (before anything is
+ * enqueued): MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_UNSUPPORTED, MOE_ERR_ALIGN;
+ * MOE_ERR_HIP for a failed launch.
+ * Source: page "Perplexity's Lily engine beats MLX by 35% on M5 Max",
+ * architecture paragraph (expert routing runs on the GPU in the layer's one
+ * submission), and page "Perplexity's Lily beats MLX by 1.35x by doing one
+ * thing: single-model Rust/Metal engines", section "Why one model on one
+ * chip is faster" (the routing of one MoE model, hardcoded).  The pages do
+ * not define the selection itself; top-k with the lower index on ties and a
+ * softmax over the chosen logits is the plainest reading. */
 int moe_route(const uint16_t* x, const uint16_t* router_weight, float* logits, int32_t T,
               int32_t H, int32_t E, int32_t top_k, int32_t* topk_ids, float* topk_weights,
               void* stream);
@@ -168,7 +178,14 @@ size_t moe_build_blocks_workspace_bytes(int32_t T, int32_t top_k, int32_t E);
  *                      rows <= block_m, none for empty experts; entries past
  *                      num_blocks are unspecified
  *   num_blocks[1]      number of tiles written
- * block_m >= 1.  workspace: device, >= moe_build_blocks_workspace_bytes. */
+ * block_m >= 1.  workspace: device, >= moe_build_blocks_workspace_bytes,
+ * owned by the caller.  Ids outside [0, E) are not counted and get no slot.
+ * Errors (before anything is enqueued): MOE_ERR_NULL, MOE_ERR_SHAPE,
+ * MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE; MOE_ERR_HIP for a failed launch.
+ * Source: page "Perplexity's Lily engine beats MLX by 35% on M5 Max",
+ * architecture paragraph: the prefix scan, the scatter and the block map
+ * stay on the GPU inside the one submission of the layer (credited there
+ * with +89% at 512 tokens). */
 int moe_build_blocks(const int32_t* topk_ids, int32_t T, int32_t top_k, int32_t E,
                      int32_t block_m, int32_t* counts, int32_t* offsets, int32_t* sorted_pairs,
                      int32_t* pair_slot, int32_t* blocks, int32_t* num_blocks, void* workspace,
@@ -203,9 +220,16 @@ int moe_build_blocks(const int32_t* topk_ids, int32_t T, int32_t top_k, int32_t 
  * Slots outside every tile are not written.  workspace: device, >=
  * moe_w4_grouped_gemm_workspace_bytes(args).  h_exp: device, 16-byte
  * aligned, >= moe_w4_h_exp_bytes(T, top_k, E, I, block_m) bytes (both
- * modes).  Page "Perplexity's Lily engine beats MLX by 35% on M5 Max",
+ * modes).  All buffers are the caller's.  Errors (before anything is
+ * enqueued): MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_UNSUPPORTED, MOE_ERR_ALIGN,
+ * MOE_ERR_WORKSPACE; MOE_ERR_HIP for a failed launch.
+ * Source: page "Perplexity's Lily engine beats MLX by 35% on M5 Max",
  * architecture paragraph: the grouped expert GEMM with the 4-bit
- * dequantisation fused in. */
+ * dequantisation fused in, so expanded 16-bit weights never reach memory
+ * (credited there with +77.4% prefill); page "Perplexity's Lily beats MLX by
+ * 1.35x by doing one thing: single-model Rust/Metal engines", section "Why
+ * one model on one chip is faster": tiles picked for the model's exact
+ * shapes. */
 typedef enum { MOE_GEMM_GATE_UP_SWIGLU = 0, MOE_GEMM_DOWN = 1 } moe_gemm_mode;
 
 typedef struct {
@@ -240,7 +264,16 @@ int moe_w4_grouped_gemm(const moe_w4_gemm_args* args, void* stream);
  * no host round trip.  x bf16 [T][H]; y fp32 [T][H] (overwritten).
  * info (host struct, may be NULL) receives the block size used and device
  * pointers into the workspace where the routing structures were written.
- * workspace: device, >= moe_ffn_workspace_bytes(&layer->dims, has_router). */
+ * workspace: device, 256-byte aligned, >= moe_ffn_workspace_bytes(&layer->dims,
+ * has_router), owned by the caller (its contents are valid until it is
+ * reused).  Errors (before anything is enqueued): MOE_ERR_NULL,
+ * MOE_ERR_SHAPE, MOE_ERR_UNSUPPORTED, MOE_ERR_ALIGN, MOE_ERR_WORKSPACE;
+ * MOE_ERR_HIP for a failed launch.
+ * Source: page "Perplexity's Lily engine beats MLX by 35% on M5 Max",
+ * architecture paragraph: routing, prefix scan, scatter and block map, then
+ * the grouped GEMMs with fused dequantisation, all in one GPU submission.
+ * SwiGLU and the routing-weighted sum are the standard MoE expert and
+ * combine; the pages name the model family, not these formulas. */
 typedef struct {
   int32_t block_m;
   int32_t path;                 /* 0 = MFMA tiles, 1 = GEMV (T <= 8) */
