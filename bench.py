@@ -182,6 +182,9 @@ def trace_average_us(workload: str, role_prefix: str):
 
 
 ROLE_OF_STAGE = {"gate_up": "S6", "down": "S7", "combine": "S8"}
+# at decode sizes the routing runs inside the gate/up launch and the combine
+# inside the down launch
+ROLE_OF_STAGE_DECODE = {"gate_up": "S1-S6", "down": "S7-S8", "combine": "S7-S8"}
 
 
 # -------------------------------------------------------------- workloads --
@@ -438,7 +441,7 @@ def main():
         work, peak, unit, bound, scale = flops, MFMA_FP16_PEAK_TFLOPS, "TFLOP/s", "mfma", 1e12
     achieved = work / dur_s / scale
     traffic = measured_traffic(name, dom)
-    trace_us = trace_average_us(name, ROLE_OF_STAGE[dom])
+    trace_us = trace_average_us(name, (ROLE_OF_STAGE_DECODE if T <= 8 else ROLE_OF_STAGE)[dom])
     roofline = {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                 "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": dom,
                 "algorithmic_bytes": int(byts), "algorithmic_flops": int(flops),
