@@ -752,7 +752,7 @@ constexpr int kDownChunk = 8;
 // waits until each chosen expert's count in ready reaches need (every
 // gate/up item of its tile stored), then reads h and its exponents with
 // device-scope loads.
-template <bool WAIT>
+template <bool WAIT, int SPW = 1>
 __device__ __forceinline__ void decode_down_body(const DecParams& p, int t, int b16,
                                                  const int32_t* __restrict__ ids,
                                                  const int32_t* __restrict__ pair_slot,
@@ -767,7 +767,6 @@ __device__ __forceinline__ void decode_down_body(const DecParams& p, int t, int 
   __shared__ __attribute__((aligned(16))) half_t zrow[16];  // zeros: the MFMA's rows other than 0
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int nwaves = blockDim.x >> 6;
   const int nbl = p.N / 32;
   const int K = p.K, S = K / 64, gpr = K >> p.log2_G, k = p.top_k;
   const int c = lane & 15, lg = lane >> 4, khalf = lg >> 1, qh = lg & 1;
@@ -814,8 +813,13 @@ __device__ __forceinline__ void decode_down_body(const DecParams& p, int t, int 
   const int e_l = e_s[jl], slot_l = max(slot_s[jl], 0);
   const float us_l = us_s[e_l];
   const uint64_t gmask = __ballot(lane < k && genx_s[e_l] != 0);
-  const int s = wave;  // this wave's slab (nwaves == S)
-  const int g = (64 * s + 32 * khalf) >> p.log2_G;
+  // this wave's slabs wave * SPW + i (nwaves * SPW == S) and their groups
+  int sl_[SPW], g_[SPW];
+#pragma unroll
+  for (int i = 0; i < SPW; i++) {
+    sl_[i] = wave * SPW + i;
+    g_[i] = (64 * sl_[i] + 32 * khalf) >> p.log2_G;
+  }
   int done_old = -1;  // WAIT: the done count before this workgroup's (thread 0)
   for (int j0 = 0; j0 < k; j0 += kDownChunk) {
     const int nj = min(kDownChunk, k - j0);
@@ -823,25 +827,37 @@ __device__ __forceinline__ void decode_down_body(const DecParams& p, int t, int 
     //    threads), requested first: their LDS write then waits for them
     //    alone, not for the weights requested after them
     const int c8n = K / 8;
-    const bool stager = tid < nj * c8n;
-    const int hm = stager ? tid / c8n : 0, hc8 = stager ? tid % c8n : 0;
-    uint4 hv = make_uint4(0, 0, 0, 0);
-    if (!WAIT && stager) hv = *reinterpret_cast<const uint4*>(p.a + (size_t)max(slot_s[j0 + hm], 0) * K + 8 * hc8);
+    bool stager[SPW];
+    int hm[SPW], hc8[SPW];
+    uint4 hv[SPW];
+#pragma unroll
+    for (int u = 0; u < SPW; u++) {  // nj * K / 8 <= SPW * blockDim.x pieces
+      const int idx = tid + u * (int)blockDim.x;
+      stager[u] = idx < nj * c8n;
+      hm[u] = stager[u] ? idx / c8n : 0;
+      hc8[u] = stager[u] ? idx % c8n : 0;
+      hv[u] = make_uint4(0, 0, 0, 0);
+      if (!WAIT && stager[u])
+        hv[u] = *reinterpret_cast<const uint4*>(p.a + (size_t)max(slot_s[j0 + hm[u]], 0) * K + 8 * hc8[u]);
+    }
     // 2. codes (two words) and (scale, bias) word of every choice of the
     //    chunk, and the exponents of the slab's four 16-column blocks of its
     //    h row (one word: a scalar load)
-    uint2 q[kDownChunk];
-    uint32_t sb[kDownChunk], hx[kDownChunk];
+    uint2 q[kDownChunk][SPW];
+    uint32_t sb[kDownChunk][SPW], hx[kDownChunk][SPW];
 #pragma unroll
     for (int j = 0; j < kDownChunk; j++) {
       const int jj = min(j0 + j, k - 1);
       const int ej = __builtin_amdgcn_readlane(e_l, jj);
       const int sl = __builtin_amdgcn_readlane(slot_l, jj);
       const size_t bidx = (size_t)ej * nbl + (b16 >> 1);
-      q[j] = *reinterpret_cast<const uint2*>(p.b0.words + ((bidx >> 2) * S * 4 + (bidx & 3)) * 256 +
-                                             4 * (2 * col + khalf) + 2 * qh + (size_t)s * 1024);
-      sb[j] = p.b0.sb[(bidx >> 2) * gpr * 128 + (bidx & 3) * 32 + col + (size_t)g * 128];
-      if (!WAIT) hx[j] = reinterpret_cast<const uint32_t*>(p.hexp + (size_t)sl * (K / 16))[s];
+#pragma unroll
+      for (int i = 0; i < SPW; i++) {
+        q[j][i] = *reinterpret_cast<const uint2*>(p.b0.words + ((bidx >> 2) * S * 4 + (bidx & 3)) * 256 +
+                                                  4 * (2 * col + khalf) + 2 * qh + (size_t)sl_[i] * 1024);
+        sb[j][i] = p.b0.sb[(bidx >> 2) * gpr * 128 + (bidx & 3) * 32 + col + (size_t)g_[i] * 128];
+        if (!WAIT) hx[j][i] = reinterpret_cast<const uint32_t*>(p.hexp + (size_t)sl * (K / 16))[sl_[i]];
+      }
     }
     if constexpr (WAIT) {
       // the chunk's experts: lane j of wave 0 polls expert j's count (a
@@ -869,65 +885,78 @@ __device__ __forceinline__ void decode_down_body(const DecParams& p, int t, int 
         done_old = __hip_atomic_fetch_add(ready + kSyncDone, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       // h rows and exponents with device-scope loads: they miss any stale
       // line another XCD's L2 may hold
-      if (stager) {
-        const uint64_t* hs = reinterpret_cast<const uint64_t*>(p.a + (size_t)max(slot_s[j0 + hm], 0) * K + 8 * hc8);
-        const uint64_t lo = __hip_atomic_load(hs, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const uint64_t hi = __hip_atomic_load(hs + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        hv = make_uint4((uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32));
-      }
+#pragma unroll
+      for (int u = 0; u < SPW; u++)
+        if (stager[u]) {
+          const uint64_t* hs =
+              reinterpret_cast<const uint64_t*>(p.a + (size_t)max(slot_s[j0 + hm[u]], 0) * K + 8 * hc8[u]);
+          const uint64_t lo = __hip_atomic_load(hs, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          const uint64_t hi = __hip_atomic_load(hs + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          hv[u] = make_uint4((uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32));
+        }
 #pragma unroll
       for (int j = 0; j < kDownChunk; j++) {
         const int sl = __builtin_amdgcn_readlane(slot_l, min(j0 + j, k - 1));
-        hx[j] = __hip_atomic_load(reinterpret_cast<const uint32_t*>(p.hexp + (size_t)sl * (K / 16)) + s,
-                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+        for (int i = 0; i < SPW; i++)
+          hx[j][i] = __hip_atomic_load(reinterpret_cast<const uint32_t*>(p.hexp + (size_t)sl * (K / 16)) + sl_[i],
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
-    if (stager) *reinterpret_cast<uint4*>(xs + hm * K + 8 * hc8) = hv;
+#pragma unroll
+    for (int u = 0; u < SPW; u++)
+      if (stager[u]) *reinterpret_cast<uint4*>(xs + hm[u] * K + 8 * hc8[u]) = hv[u];
     __syncthreads();
     // 3. per choice: dequantise, multiply, keep row 0 (lanes with c == 0
     //    read the h fragment, the others the zero row).  The slab's blocks
     //    are brought to their largest exponent es (skipped when all four are
     //    0, the usual case) and the partial scaled by 2^es and the expert's
     //    2^-c (powers of two: exact in fp32 short of its range)
-    const half_t* xrow = c == 0 ? xs + 64 * s + 32 * khalf + 16 * qh : zrow;
     const int xstride = c == 0 ? K : 0;
     auto run = [&](auto gen_tag) {
       constexpr bool ANY_GEN = decltype(gen_tag)::value;
 #pragma unroll
       for (int j = 0; j < kDownChunk; j++) {
         if (j >= nj) break;
-        u32x4 xf[2];
-#pragma unroll
-        for (int m = 0; m < 2; m++) xf[m] = *reinterpret_cast<const u32x4*>(xrow + j * xstride + 8 * m);
-        const uint32_t hw = hx[j];
-        int es = 0;
-        if (hw) {
-          es = max_i8x4(hw);
-          // the exponent of the block this lane's h values come from
-          const int d = (int)(int8_t)(hw >> (8 * (2 * khalf + qh))) - es;
-#pragma unroll
-          for (int m = 0; m < 2; m++) xf[m] = __builtin_bit_cast(u32x4, scale_half8(__builtin_bit_cast(uint4, xf[m]), d));
-        }
-        floatx4_t acc = floatx4_t{};
-        auto multiply = [&](auto g_tag) {
-          constexpr bool GEN = decltype(g_tag)::value;
-          const SbPair sp = sb_unpack(sb[j], GEN);
-#pragma unroll
-          for (int m = 0; m < 2; m++) {
-            const uint32_t w = m == 0 ? q[j].x : q[j].y;
-            const uint4 dq = GEN ? dequant_word_gen(w, sp.s2, sp.c2, sp.b2) : dequant_word(w, sp.s2, sp.c2);
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, xf[m]),
-                                                         __builtin_bit_cast(half8_t, dq), acc, 0, 0, 0);
-          }
-        };
-        if constexpr (ANY_GEN) {
-          if ((gmask >> (j0 + j)) & 1) multiply(std::true_type{});
-          else multiply(std::false_type{});
-        } else {
-          multiply(std::false_type{});
-        }
         const float us = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(us_l), j0 + j));
-        if (lane < 16) red[(wave * k + j0 + j) * 16 + lane] = ldexpf(acc[0] * us, es);
+#pragma unroll
+        for (int i = 0; i < SPW; i++) {
+          const half_t* xrow = c == 0 ? xs + 64 * sl_[i] + 32 * khalf + 16 * qh : zrow;
+          u32x4 xf[2];
+#pragma unroll
+          for (int m = 0; m < 2; m++) xf[m] = *reinterpret_cast<const u32x4*>(xrow + j * xstride + 8 * m);
+          const uint32_t hw = hx[j][i];
+          int es = 0;
+          if (hw) {
+            es = max_i8x4(hw);
+            // the exponent of the block this lane's h values come from
+            const int d = (int)(int8_t)(hw >> (8 * (2 * khalf + qh))) - es;
+#pragma unroll
+            for (int m = 0; m < 2; m++)
+              xf[m] = __builtin_bit_cast(u32x4, scale_half8(__builtin_bit_cast(uint4, xf[m]), d));
+          }
+          floatx4_t acc = floatx4_t{};
+          auto multiply = [&](auto g_tag) {
+            constexpr bool GEN = decltype(g_tag)::value;
+            const SbPair sp = sb_unpack(sb[j][i], GEN);
+#pragma unroll
+            for (int m = 0; m < 2; m++) {
+              const uint32_t w = m == 0 ? q[j][i].x : q[j][i].y;
+              const uint4 dq = GEN ? dequant_word_gen(w, sp.s2, sp.c2, sp.b2) : dequant_word(w, sp.s2, sp.c2);
+              acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, xf[m]),
+                                                           __builtin_bit_cast(half8_t, dq), acc, 0, 0, 0);
+            }
+          };
+          if constexpr (ANY_GEN) {
+            if ((gmask >> (j0 + j)) & 1) multiply(std::true_type{});
+            else multiply(std::false_type{});
+          } else {
+            multiply(std::false_type{});
+          }
+          // one partial per slab, so the sum below adds them in slab order
+          // whatever the slabs per wave
+          if (lane < 16) red[(sl_[i] * k + j0 + j) * 16 + lane] = ldexpf(acc[0] * us, es);
+        }
       }
     };
     if ((gmask >> j0) & ((1ull << nj) - 1)) run(std::true_type{});
@@ -941,7 +970,7 @@ __device__ __forceinline__ void decode_down_body(const DecParams& p, int t, int 
     for (int i = tid; i < k * 16; i += blockDim.x) {
       const int j = i >> 4, cc = i & 15;
       float d = red[j * 16 + cc];
-      for (int w2 = 1; w2 < nwaves; w2++) d += red[(w2 * k + j) * 16 + cc];
+      for (int s2 = 1; s2 < S; s2++) d += red[(s2 * k + j) * 16 + cc];
       const float v = w_s[j] * d;
       v_s[i] = v;
       if (slot_s[j] >= 0) reinterpret_cast<float*>(p.out)[(size_t)slot_s[j] * p.N + b16 * 16 + cc] = v;
@@ -970,13 +999,14 @@ __device__ __forceinline__ void decode_down_body(const DecParams& p, int t, int 
   }
 }
 
+template <int SPW>
 __global__ __launch_bounds__(64 * kDecWavesMax) void decode_down_kernel(
     const DecParams p, const int32_t* __restrict__ ids, const int32_t* __restrict__ pair_slot,
     float* __restrict__ y, const uint16_t* __restrict__ residual, uint16_t* __restrict__ out) {
   extern __shared__ __attribute__((aligned(16))) char dsm[];
   const int nb16 = p.N / 16;
-  decode_down_body<false>(p, blockIdx.x / nb16, blockIdx.x % nb16, ids, pair_slot, p.topk_weights, y,
-                          residual, out, dsm, nullptr, 0, nullptr, 0);
+  decode_down_body<false, SPW>(p, blockIdx.x / nb16, blockIdx.x % nb16, ids, pair_slot, p.topk_weights, y,
+                               residual, out, dsm, nullptr, 0, nullptr, 0);
 }
 
 // The routing of the batch into rl, as every gate/up workgroup computes it
@@ -1198,11 +1228,18 @@ hipError_t launch_decode_down(const GemmArgs& a, const int32_t* ids, const int32
   if (a.T > kGemvMaxTokens || !decode_down_fused(a.K)) return hipErrorInvalidValue;
   const int64_t P = (int64_t)a.T * a.top_k;
   const int64_t grid = (int64_t)a.T * (a.N / 16);
-  const int waves = a.K / 64;
+  // one wave per slab; two slabs per wave when the grid would otherwise
+  // need more than one round of three 8-wave workgroups per CU (half the
+  // waves, so four workgroups share a CU: at H = 2048 and T = 8 the 1,024
+  // workgroups then run in one round)
+  const int S = a.K / 64;
+  const int spw = (S % 2 == 0 && S >= 4 && grid > 3 * (int64_t)device_cus()) ? 2 : 1;
+  const int waves = S / spw;
   const int xs_bytes = kDownChunk * a.K * 2;
-  const size_t lds = (size_t)xs_bytes + (size_t)waves * a.top_k * 16 * 4;
+  const size_t lds = (size_t)xs_bytes + (size_t)S * a.top_k * 16 * 4;  // one partial per slab and choice
   const DecParams p = dec_params(a, P, 0, xs_bytes);
-  decode_down_kernel<<<grid, 64 * waves, lds, s>>>(p, ids, pair_slot, y, residual, out);
+  if (spw == 2) decode_down_kernel<2><<<grid, 64 * waves, lds, s>>>(p, ids, pair_slot, y, residual, out);
+  else decode_down_kernel<1><<<grid, 64 * waves, lds, s>>>(p, ids, pair_slot, y, residual, out);
   return hipGetLastError();
 }
 
