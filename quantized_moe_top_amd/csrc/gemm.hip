@@ -645,10 +645,12 @@ hipError_t launch_mode(const GemmArgs& a, hipStream_t s) {
     }
     return hipGetLastError();
   }
-  if (MODE == MOE_GEMM_DOWN && a.block_m == 64 && !g32 && a.N % 512 == 0) {
-    const int64_t items8 = max_blocks * (a.N / 512);
-    const int64_t grid8 = ((items8 + kNumXcd - 1) / kNumXcd) * kNumXcd;
-    w4_mfma_kernel<MODE, 2, 8, false, 3, 2, PACK><<<grid8, 512, 0, s>>>(p);
+  if (MODE == MOE_GEMM_DOWN && a.block_m == 64 && !g32) {
+    // S7 on 64-row tiles (K = I: few slabs per item, so an item is mostly its
+    // prologue, first copies and epilogue): four 4-wave workgroups per CU on
+    // a 2-stage ring, so at T = 512 every item is resident in one round
+    // (36 -> 32 us against 8-wave workgroups with 512 columns, two per CU)
+    w4_mfma_kernel<MODE, 2, 4, false, 2, 4, PACK><<<grid, 256, 0, s>>>(p);
     return hipGetLastError();
   }
   switch (a.block_m * 2 + (g32 ? 1 : 0)) {
