@@ -641,6 +641,36 @@ def test_ffn_io(orc, case):
     assert np.mean(got == exact) >= 0.999
 
 
+@pytest.mark.parametrize("T", [8192, 16384, 32768])
+def test_ffn_io_router_tiles(orc, T):
+    """RMSNorm folded into the router at its larger tile shapes (64x64,
+    64x128 and 128x128 blocks of tokens x experts at E = 128, where gamma
+    multiplies the A fragments of every k step a wave reads): the logits
+    within the bound of test_ffn_io, the routing of the GPU's logits
+    bit-exact with the oracle's, and y on 96 sampled tokens."""
+    lay = synth.make_custom(T=T, H=256, I=128, E=128, k=8, G=64, seed=T + 7, router="weight")
+    g = torch.Generator().manual_seed(T + 8)
+    gamma = (torch.rand(lay.H, generator=g) * 1.5 + 0.25).to(torch.bfloat16)
+    y, info = api.ffn_forward(on_dev(lay), info=True, norm_weight=gamma.to(DEV), norm_eps=1e-5)
+    torch.cuda.synchronize()
+    xn = orc.rmsnorm(lay.x, gamma, 1e-5)
+    l_used = cpu(info["logits"]).astype(np.float32)
+    l_ref = orc.router_logits(xn, lay.router_weight)
+    wr = np.abs(lay.router_weight.float().numpy().astype(np.float64))
+    xv = (xn.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    bound = router_error_bound(torch.from_numpy(xv).to(torch.bfloat16), lay.router_weight) + \
+        1.5 * (_bf16_ulp(xn) @ wr.T) + 4 * f32_ulp(np.abs(xv) @ wr.T)
+    err = np.abs(l_used.astype(np.float64) - l_ref)
+    say(f"  T={T}: logits max err {err.max():.3e}, min slack {(bound - err).min():.3e}")
+    assert np.all(err <= bound)
+    rid, rw = orc.route(l_used, lay.k)
+    assert np.array_equal(cpu(info["topk_ids"]), rid)
+    assert_weights_close(cpu(info["topk_weights"]), rw)
+    tokens = np.sort(np.random.default_rng(T).choice(T, 96, replace=False)).astype(np.int32)
+    y_ref = orc.ffn(xn, rid, rw, lay.gate, lay.up, lay.down, lay.G, tokens=tokens)
+    assert_fp_close(cpu(y)[tokens], y_ref, f"T={T} y (96 sampled rows)")
+
+
 # ---------------------------------------------------- decode attention --
 # fp32 arithmetic over at most 131072 positions (products of bf16 values are
 # exact in fp32; the sums and the rescaling by exp2 differences carry about
