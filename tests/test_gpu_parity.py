@@ -471,6 +471,19 @@ def test_ffn_decode_edges(orc):
         layer_output_check(orc, lay, y, info)
 
 
+def test_ffn_decode_two_slabs_per_wave(orc):
+    """Decode sizes whose down launch takes two slabs per wave (more
+    workgroups than three 8-wave ones per CU hold): T = 7 and 8 at H = 2048,
+    and H = 4096 with I = 256 (two 2-slab waves per workgroup), against the
+    oracle."""
+    for (T, H, I, E, k) in [(7, 2048, 512, 64, 8), (8, 4096, 256, 32, 4)]:
+        lay = synth.make_custom(T=T, H=H, I=I, E=E, k=k, G=64, seed=70 + T + H // 1024)
+        y, info = api.ffn_forward(on_dev(lay), info=True)
+        torch.cuda.synchronize()
+        assert info["path"] == 1
+        layer_output_check(orc, lay, y, info)
+
+
 def test_ffn_decode_wide_shapes(orc):
     """Decode sizes at shapes that leave the one-pass kernels: a reduction
     of 8192 in the gate/up launch (more than one pass per item, no
