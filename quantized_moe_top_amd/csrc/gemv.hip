@@ -309,13 +309,19 @@ __device__ __forceinline__ void g16_mma(const DecParams& p, const Frag16<SPW>& f
 // COHERENT: h and its exponents are stored with device-scope (write-through)
 // stores, so a workgroup of the same launch on another XCD can read them once
 // it has seen the tile's ready count (the single-launch decode layer).
+// buf >= 0: the partials go to half buf of a doubled area and the epilogue
+// ends without a barrier (the caller alternates the halves, so the next
+// item's partials never overwrite values still being read, and the item
+// after that writes this half only past the next item's barrier); buf < 0:
+// one area and a closing barrier.
 template <bool COHERENT = false>
 __device__ __forceinline__ void g16_epilogue(const DecParams& p, const floatx4_t (&acc)[2], int row0,
-                                             int rows, int b16, char* dsm, float us0, float us1) {
+                                             int rows, int b16, char* dsm, float us0, float us1,
+                                             int buf = -1) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nwaves = blockDim.x >> 6;
-  float* red = reinterpret_cast<float*>(dsm + p.red_off);
+  float* red = reinterpret_cast<float*>(dsm + p.red_off) + (buf > 0 ? nwaves * 2 * 4 * 32 : 0);
   if (lane < 32)
 #pragma unroll
     for (int b = 0; b < 2; b++)
@@ -349,7 +355,7 @@ __device__ __forceinline__ void g16_epilogue(const DecParams& p, const floatx4_t
       if (cc == 0) *ep = (int8_t)ex;
     }
   }
-  __syncthreads();
+  if (buf < 0) __syncthreads();
 }
 
 // The gate/up product of one (tile, 16-column block), on
@@ -707,7 +713,7 @@ __device__ __forceinline__ void decode_gate_up_body(const DecRouteParams& r, con
         else g16_mma<SPW, false>(p, half == 0 ? fa : fb, rows, 0, acc, dsm);
         __syncthreads();
       }
-      g16_epilogue<READY>(p, acc, row0, rows, b16, dsm, us_s[0][e], us_s[1][e]);
+      g16_epilogue<READY>(p, acc, row0, rows, b16, dsm, us_s[0][e], us_s[1][e], p.x_res ? half : -1);
       pending = e;
       it = nx;
       if (it >= items) break;
@@ -1162,7 +1168,7 @@ static bool decode_gate_up_plan(const GemmArgs& a, DecGateUpPlan& pl) {
   // logits, the waves' partial sums of both banks (rows 0..7 of 16 columns);
   // otherwise the logits, then (reused) the activation rows of one pass, and
   // the partial sums
-  const int red_bytes = sh.waves * 2 * 4 * 32 * 4;
+  const int red_bytes = 2 * sh.waves * 2 * 4 * 32 * 4;  // two halves (alternating items, x_res)
   const int lg_bytes = (a.T * a.E * 4 + 15) & ~15;
   const int xres_bytes = (a.T * a.K * 2 + 15) & ~15;
   const bool one_pass = a.K <= sh.waves * sh.spw * 64;
