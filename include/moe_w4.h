@@ -369,8 +369,9 @@ int moe_ffn_forward_io(const moe_layer* layer, const uint16_t* x, const float* r
  *                block holding its positions i*block .. i*block+block-1;
  *                entries outside [0, num_blocks) are skipped, never read
  *                through
- *   seq_lens:    device int32 [B], each <= max_len and <= max_blocks*block
- *                (positions past max_len are not visited)
+ *   seq_lens:    device int32 [B], each <= max_blocks*block; a length
+ *                above max_len is taken as max_len (positions at or past
+ *                max_len are never visited)
  *   out:         device fp32 [B][Hq][D]
  *   workspace:   device, >= moe_decode_attention_workspace_bytes(B, Hq,
  *                Hkv, max_len), 16-byte aligned

@@ -45,6 +45,7 @@ struct AttnParams {
   float* part_acc;  // [B][Hq][nsplit][D]
   int Hq, Hkv, block, max_blocks, num_blocks, nsplit, chunk;
   float qscale;     // log2(e) / sqrt(D)
+  int max_len;      // positions at or past it are never visited
 };
 
 template <int GQ>
@@ -70,7 +71,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void attn_split_kernel(const AttnP
     gslab[i] = (blk >= 0 && blk < p.num_blocks) ? blk * p.Hkv + h : -1;
     goff[i] = t % p.block;
   }
-  const int t1 = min(p.lens[b], t0 + p.chunk);
+  const int t1 = min(min(p.lens[b], p.max_len), t0 + p.chunk);
   // second operand of the scores: lane (r, g) holds elements 32c + 8g .. +7
   // of query head r (zero for the padding heads r >= GQ)
   u32x4 qop[4];
@@ -337,7 +338,7 @@ hipError_t launch_decode_attention(const uint16_t* q, const uint16_t* kc, const 
   const AttnPlan pl = attn_plan(B, Hkv, max_len);
   const size_t nq = (size_t)B * Hq * pl.nsplit;
   AttnParams p{q, kc, vc, table, lens, ws, ws + nq, ws + 2 * nq, Hq, Hkv, block, max_blocks,
-               num_blocks, pl.nsplit, pl.chunk, 1.4426950408889634f / sqrtf((float)kAttnD)};
+               num_blocks, pl.nsplit, pl.chunk, 1.4426950408889634f / sqrtf((float)kAttnD), max_len};
   const dim3 grid(pl.nsplit, Hkv, B);
   switch (Hq / Hkv) {
     case 1: attn_split_kernel<1><<<grid, kAttnThreads, 0, s>>>(p); break;

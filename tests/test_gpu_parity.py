@@ -747,6 +747,20 @@ def test_decode_attention_skipped_blocks(orc):
     _attn_check(cpu(out), ref, "attention with skipped blocks")
 
 
+def test_decode_attention_max_len_clamp(orc):
+    """A sequence length above max_len is taken as max_len: with lengths
+    (300, 90) and max_len 200 the first sequence is attended over its first
+    200 positions only (the oracle on lengths (200, 90)), the second in
+    full."""
+    import dataclasses
+    case = synth.make_attention([300, 90], Hq=8, Hkv=4, D=128, block=16, seed=58)
+    out = api.decode_attention(case.to(DEV), max_len=200)
+    torch.cuda.synchronize()
+    clamped = dataclasses.replace(case, lens=torch.tensor([200, 90], dtype=torch.int32))
+    ref = orc.decode_attention(clamped.q, clamped.kcache, clamped.vcache, clamped.table, clamped.lens)
+    _attn_check(cpu(out), ref, "attention with a length above max_len")
+
+
 def test_decode_attention_graph_replay():
     """Both launches captured in a HIP graph (no allocation, no memset)
     replay to the eager result, bit for bit, with other attention work on the
