@@ -520,74 +520,68 @@ __global__ __launch_bounds__(64 * WAVES, WGS_PER_CU * WAVES / 4) void w4_mfma_ke
     }
     if (any) p.tflags[tile] = 1;
   } else if constexpr (PACK) {
+    // The accumulators go through a wave-private fp32 LDS tile of 32 rows x
+    // 64 columns (one 32-row block at a time) and come back as 4 consecutive
+    // columns of one row per lane: lane l takes row 4k + l / 16 of the block
+    // (k = 0..7) at columns 4 (l % 16) .. + 3 of the wave's 64.  Row pitch 64
+    // words, columns XOR 32 on rows with bit 2 set: the two half-waves of a
+    // column write (rows r and r + 4) fall on disjoint banks, and each
+    // 16-lane row read covers all 64 banks.  The four lanes of one row's
+    // 16-column block are a DPP quad: two quad exchanges give the block's
+    // largest |a w|, hence its exponent; each lane stores its 4 int16
+    // mantissas (16 lanes: 128 contiguous bytes of a row) and the block's
+    // exponent byte (the quad's lanes store the same byte).  The ring is free
+    // once every copy has landed and every wave has finished its MFMAs.
+    static_assert(WAVES * 32 * 64 * 4 <= STAGES * STAGE, "epilogue tile must fit the ring");
+    wait_vm<0>();
+    __syncthreads();
     if (!active) return;
-    // Registers 4g .. 4g + 3 of a lane hold 4 consecutive rows of one
-    // column; a 4 x 4 transpose inside each lane quad (two DPP exchange
-    // steps, partners lane ^ 2 then lane ^ 1) gives lane 4q + j row j of
-    // them at columns 4q .. 4q + 3, which it weights.  The four lanes holding
-    // one row's 16-column block (q = 4b .. 4b + 3: lanes j, j + 4, j + 8,
-    // j + 12 of a 16-lane DPP row) share its exponent (two row rotations
-    // give their maximum); each lane stores its 4 int16 mantissas (8 bytes),
-    // the lane with q % 4 == 0 the block's exponent.
-    const int j4 = col & 3, q = col >> 2;
-    const bool hi2 = (j4 & 2) != 0, hi1 = (j4 & 1) != 0;
-    auto xchg = [](float v, int ctrl) {
-      return ctrl == 0x4E ? __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true))
-                          : __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));
-    };
-    // this lane's rows 4 khalf + j4 (+ 32 mb + 8 g) at columns 4q .. 4q + 3
-    // of its 64-column slice: mantissas (row stride 2 N bytes) and exponents
-    // (row stride N / 16)
+    float* const tile = reinterpret_cast<float*>(lds) + wave * 32 * 64;
+    const int q = lane & 15, rq = lane >> 4;  // column quad, row within 4
     const size_t mstride = (size_t)N * 2, estride = (size_t)N / 16;
     const int c0 = nb * OUT_COLS + wave * 64;
-    char* const lane_out = reinterpret_cast<char*>(p.out) + (size_t)(row0 + 4 * khalf + j4) * mstride +
-                           (size_t)(c0 + 4 * q) * 2;
-    int8_t* const lane_exp = p.yexp + (size_t)(row0 + 4 * khalf + j4) * estride + c0 / 16 + (q >> 2);
-    // the routing weights of this lane's rows after the transposes, read
-    // from LDS once
-    float wr[MB][4];
+    // this lane's row rq of the tile: the later rows are uniform offsets from it
+    char* const lane_out = reinterpret_cast<char*>(p.out) + (size_t)(row0 + rq) * mstride + (size_t)(c0 + 4 * q) * 2;
+    int8_t* const lane_exp = p.yexp + (size_t)(row0 + rq) * estride + c0 / 16 + (q >> 2);
+    auto block = [&](auto full_tag) {
+      constexpr bool FULL = decltype(full_tag)::value != 0;
 #pragma unroll
-    for (int mb = 0; mb < MB; mb++)
+      for (int mb = 0; mb < MB; mb++) {
+        if (!FULL && mb * 32 >= rows) break;  // (uniform) no row of this block is stored
+        // register r of lane l: row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32
 #pragma unroll
-      for (int g = 0; g < 4; g++) {
-        const int r = mb * 32 + 8 * g + 4 * khalf + j4;
-        wr[mb][g] = (scaled ? ldexpf(row_w[r], erow[r]) : row_w[r]) * us0;
-      }
+        for (int cb = 0; cb < 2; cb++)
 #pragma unroll
-    for (int mb = 0; mb < MB; mb++)
+          for (int r = 0; r < 16; r++) {
+            const int row = 8 * (r >> 2) + 4 * khalf + (r & 3);
+            tile[row * 64 + ((cb * 32 + col) ^ (row & 4 ? 32 : 0))] = acc[mb][cb][r];
+          }
 #pragma unroll
-      for (int cb = 0; cb < 2; cb++)
-#pragma unroll
-        for (int g = 0; g < 4; g++) {
-          float a0 = acc[mb][cb][4 * g], a1 = acc[mb][cb][4 * g + 1];
-          float a2 = acc[mb][cb][4 * g + 2], a3 = acc[mb][cb][4 * g + 3];
-          // step 1, partner lane ^ 2: send the rows the partner keeps
-          float r0 = xchg(hi2 ? a0 : a2, 0x4E), r1 = xchg(hi2 ? a1 : a3, 0x4E);  // quad_perm 2,3,0,1
-          a0 = hi2 ? r0 : a0;
-          a1 = hi2 ? r1 : a1;
-          a2 = hi2 ? a2 : r0;
-          a3 = hi2 ? a3 : r1;
-          // step 2, partner lane ^ 1
-          r0 = xchg(hi1 ? a0 : a1, 0xB1);  // quad_perm 1,0,3,2
-          r1 = xchg(hi1 ? a2 : a3, 0xB1);
-          a0 = hi1 ? r0 : a0;
-          a2 = hi1 ? r1 : a2;
-          a1 = hi1 ? a1 : r0;
-          a3 = hi1 ? a3 : r1;
-          // the block's largest |a w| (the weight is one per row), then the
-          // weight and 2^-E folded into one factor for the packing
-          const float w = wr[mb][g];
-          float m = fmaxf(fmaxf(fabsf(a0), fabsf(a1)), fmaxf(fabsf(a2), fabsf(a3)));
-          m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0x124, 0xF, 0xF, true)));  // row_ror:4
-          m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0x128, 0xF, 0xF, true)));  // row_ror:8
-          const int ex = y16_exp(m * fabsf(w));
+        for (int k = 0; k < 8; k++) {
+          const int rr = 4 * k + rq;
+          const float4 v = *reinterpret_cast<const float4*>(tile + rr * 64 + ((4 * q) ^ (rr & 4 ? 32 : 0)));
+          const int row = mb * 32 + rr;
+          const float w = (scaled ? ldexpf(row_w[row], erow[row]) : row_w[row]) * us0;
+          // the block's largest |a|: the bits of non-negative floats order as
+          // unsigned integers, so the quad exchanges take integer maxima
+          float m4;
+          asm("v_max3_f32 %0, |%1|, |%2|, |%3|\n\tv_max_f32 %0, %0, |%4|"
+              : "=&v"(m4) : "v"(v.x), "v"(v.y), "v"(v.z), "v"(v.w));
+          uint32_t m = __float_as_uint(m4);
+          m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0xB1, 0xF, 0xF, true));  // quad_perm 1,0,3,2
+          m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x4E, 0xF, 0xF, true));  // quad_perm 2,3,0,1
+          const int ex = y16_exp_bits(__uint_as_float(m) * fabsf(w));
           const float ws = ex == -128 ? 0.0f : ldexpf(w, -ex);
-          if (mb * 32 + 8 * g + 4 * khalf + j4 < rows) {
-            *reinterpret_cast<uint2*>(lane_out + (size_t)(mb * 32 + 8 * g) * mstride + cb * 64) =
-                y16_pack4(a0, a1, a2, a3, ws);
-            if ((q & 3) == 0) lane_exp[(size_t)(mb * 32 + 8 * g) * estride + cb * 2] = (int8_t)ex;
+          const uint2 pk = y16_pack4(v.x, v.y, v.z, v.w, ws);
+          if (FULL || row < rows) {
+            *reinterpret_cast<uint2*>(lane_out + (size_t)(mb * 32 + 4 * k) * mstride) = pk;
+            lane_exp[(size_t)(mb * 32 + 4 * k) * estride] = (int8_t)ex;
           }
         }
+      }
+    };
+    if (rows == BM) block(IntTag<1>{});
+    else block(IntTag<0>{});
   } else {
     if (!active) return;
 #pragma unroll
