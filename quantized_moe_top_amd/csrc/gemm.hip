@@ -492,32 +492,43 @@ __global__ __launch_bounds__(64 * WAVES, WGS_PER_CU * WAVES / 4) void w4_mfma_ke
     __syncthreads();
     const int n0 = nb * OUT_COLS;
     const int chunks = min(OUT_COLS, N - n0) / 8;  // 16-byte pieces per row (an even count)
-    const int total8 = rows * chunks;
     bool any = false;
     // every lane runs every round, so that lane pairs (2i, 2i + 1) -- the two
-    // 8-column pieces of one 16-column block -- exchange their maxima
-    for (int base = 0; base < total8; base += 64 * WAVES) {
-      const int idx = base + tid;
-      const bool ok = idx < total8;
-      const int row = ok ? idx / chunks : 0, ch = ok ? idx % chunks : 0;
-      const float4 v0 = *reinterpret_cast<const float4*>(tile_f + row * OUT_COLS + 8 * ch);
-      const float4 v1 = *reinterpret_cast<const float4*>(tile_f + row * OUT_COLS + 8 * ch + 4);
-      float m = fmaxf(fmaxf(fmaxf(fabsf(v0.x), fabsf(v0.y)), fmaxf(fabsf(v0.z), fabsf(v0.w))),
-                      fmaxf(fmaxf(fabsf(v1.x), fabsf(v1.y)), fmaxf(fabsf(v1.z), fabsf(v1.w))));
-      m = fmaxf(m, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(m), 0xB1, 0xF, 0xF, true)));
-      const int ex = h_block_exp(m);
-      if (ok) {
-        const half2_t o0 = {(half_t)ldexpf(v0.x, -ex), (half_t)ldexpf(v0.y, -ex)};
-        const half2_t o1 = {(half_t)ldexpf(v0.z, -ex), (half_t)ldexpf(v0.w, -ex)};
-        const half2_t o2 = {(half_t)ldexpf(v1.x, -ex), (half_t)ldexpf(v1.y, -ex)};
-        const half2_t o3 = {(half_t)ldexpf(v1.z, -ex), (half_t)ldexpf(v1.w, -ex)};
-        *reinterpret_cast<uint4*>(reinterpret_cast<half_t*>(p.out) + (size_t)(row0 + row) * N + n0 + 8 * ch) =
-            make_uint4(__builtin_bit_cast(uint32_t, o0), __builtin_bit_cast(uint32_t, o1),
-                       __builtin_bit_cast(uint32_t, o2), __builtin_bit_cast(uint32_t, o3));
-        if (!(ch & 1)) p.hexp[(size_t)(row0 + row) * (N / 16) + (n0 + 8 * ch) / 16] = (int8_t)ex;
-        any |= ex != 0;
+    // 8-column pieces of one 16-column block -- exchange their maxima (both
+    // store the block's exponent byte)
+    auto rounds = [&](auto full_tag) {
+      constexpr bool FULLC = decltype(full_tag)::value != 0;  // chunks == OUT_COLS / 8 (a power of two)
+      constexpr int LOGC = __builtin_ctz(OUT_COLS / 8);
+      const int total8 = rows * chunks;
+      for (int base = 0; base < total8; base += 64 * WAVES) {
+        const int idx = base + tid;
+        const bool ok = idx < total8;
+        const int row = !ok ? 0 : FULLC ? idx >> LOGC : idx / chunks;
+        const int ch = !ok ? 0 : FULLC ? idx & (OUT_COLS / 8 - 1) : idx % chunks;
+        const float4 v0 = *reinterpret_cast<const float4*>(tile_f + row * OUT_COLS + 8 * ch);
+        const float4 v1 = *reinterpret_cast<const float4*>(tile_f + row * OUT_COLS + 8 * ch + 4);
+        float m8;
+        asm("v_max3_f32 %0, |%1|, |%2|, |%3|\n\tv_max3_f32 %0, %0, |%4|, |%5|\n\tv_max3_f32 %0, %0, |%6|, |%7|\n\t"
+            "v_max_f32 %0, %0, |%8|"
+            : "=&v"(m8) : "v"(v0.x), "v"(v0.y), "v"(v0.z), "v"(v0.w), "v"(v1.x), "v"(v1.y), "v"(v1.z), "v"(v1.w));
+        uint32_t mu = __float_as_uint(m8);
+        mu = max(mu, (uint32_t)__builtin_amdgcn_mov_dpp((int)mu, 0xB1, 0xF, 0xF, true));
+        const int ex = h_block_exp_bits(mu);
+        if (ok) {
+          const half2_t o0 = {(half_t)ldexpf(v0.x, -ex), (half_t)ldexpf(v0.y, -ex)};
+          const half2_t o1 = {(half_t)ldexpf(v0.z, -ex), (half_t)ldexpf(v0.w, -ex)};
+          const half2_t o2 = {(half_t)ldexpf(v1.x, -ex), (half_t)ldexpf(v1.y, -ex)};
+          const half2_t o3 = {(half_t)ldexpf(v1.z, -ex), (half_t)ldexpf(v1.w, -ex)};
+          *reinterpret_cast<uint4*>(reinterpret_cast<half_t*>(p.out) + (size_t)(row0 + row) * N + n0 + 8 * ch) =
+              make_uint4(__builtin_bit_cast(uint32_t, o0), __builtin_bit_cast(uint32_t, o1),
+                         __builtin_bit_cast(uint32_t, o2), __builtin_bit_cast(uint32_t, o3));
+          p.hexp[(size_t)(row0 + row) * (N / 16) + (n0 + 8 * ch) / 16] = (int8_t)ex;
+          any |= ex != 0;
+        }
       }
-    }
+    };
+    if (chunks == OUT_COLS / 8) rounds(IntTag<1>{});
+    else rounds(IntTag<0>{});
     if (any) p.tflags[tile] = 1;
   } else if constexpr (PACK) {
     // The accumulators go through a wave-private fp32 LDS tile of 32 rows x

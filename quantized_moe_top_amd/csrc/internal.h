@@ -293,6 +293,14 @@ __device__ __forceinline__ int h_block_exp(float m) {
   frexpf(m, &ex);                // m in [2^(ex-1), 2^ex)
   return max(-128, min(127, ex - 15));
 }
+// h_block_exp of m >= 0 given as its bits (no branches): 0 when m is 0,
+// in [2^-10, 2^15) or NaN; 127 above 3e38; else the frexp exponent (biased
+// exponent - 126; subnormals land below -128) less 15, clamped.
+__device__ __forceinline__ int h_block_exp_bits(uint32_t u) {
+  const bool keep = u == 0u || u - 0x3A800000u < 0x47000000u - 0x3A800000u || u > 0x7F800000u;
+  const int e = max(-128, min(127, (int)(u >> 23) - 141));
+  return keep ? 0 : u > 0x7F61B1E6u ? 127 : e;
+}
 // The largest v over each 16-lane DPP row (four row rotations; every lane
 // of the row gets it, so all 16 lanes must be active).
 __device__ __forceinline__ float row16_max(float v) {
