@@ -86,6 +86,24 @@ struct MfmaParams {
 // fp16 in operand order (moe_w4_expand: per 32-column block and slab, four
 // 1 KiB pieces, piece i the dequantised word i of every (column, half)), and
 // the kernel copies and multiplies them with no dequantisation.
+// y16_exp (internal.h) for m >= 0 (not NaN) from the float's bits: for m (1 + 2^-15)
+// normal its frexp exponent is the biased exponent - 126; zero and subnormal
+// products land below -128 and clamp there, as y16_exp's m > 0 test and
+// clamp give.
+__device__ __forceinline__ int y16_exp_bits(float m) {
+  const uint32_t u = __float_as_uint(m * (1.0f + 0x1p-15f));
+  const int e = max(-128, min(127, (int)(u >> 23) - 141));
+  return __float_as_uint(m) >= 0x7F000000u ? 127 : e;
+}
+// h_block_exp (internal.h) of m >= 0 given as its bits (no branches): 0 when m is 0,
+// in [2^-10, 2^15) or NaN; 127 above 3e38; else the frexp exponent (biased
+// exponent - 126; subnormals land below -128) less 15, clamped.
+__device__ __forceinline__ int h_block_exp_bits(uint32_t u) {
+  const bool keep = u == 0u || u - 0x3A800000u < 0x47000000u - 0x3A800000u || u > 0x7F800000u;
+  const int e = max(-128, min(127, (int)(u >> 23) - 141));
+  return keep ? 0 : u > 0x7F61B1E6u ? 127 : e;
+}
+
 template <int MODE, int MB, int WAVES, bool G32, int STAGES, int WGS_PER_CU, bool PACK = false,
           bool DENSE = false>
 __global__ __launch_bounds__(64 * WAVES, WGS_PER_CU * WAVES / 4) void w4_mfma_kernel(const MfmaParams p) {

@@ -235,15 +235,6 @@ __device__ __forceinline__ int y16_exp(float m) {
   const int e = max(-128, min(127, ex - 15));
   return m >= 0x1p127f ? 127 : m > 0.0f ? e : -128;
 }
-// y16_exp for m >= 0 (not NaN) from the float's bits: for m (1 + 2^-15)
-// normal its frexp exponent is the biased exponent - 126; zero and subnormal
-// products land below -128 and clamp there, as y16_exp's m > 0 test and
-// clamp give.
-__device__ __forceinline__ int y16_exp_bits(float m) {
-  const uint32_t u = __float_as_uint(m * (1.0f + 0x1p-15f));
-  const int e = max(-128, min(127, (int)(u >> 23) - 141));
-  return __float_as_uint(m) >= 0x7F000000u ? 127 : e;
-}
 // Four values a_i * w of one block -> four int16 mantissas (8 bytes), to
 // nearest: with ws = w 2^-E, one FMA a ws + 1.5 2^23 rounds the product
 // once to an integer held in the low mantissa bits (|a ws| < 2^15), whose
@@ -292,14 +283,6 @@ __device__ __forceinline__ int h_block_exp(float m) {
   int ex;
   frexpf(m, &ex);                // m in [2^(ex-1), 2^ex)
   return max(-128, min(127, ex - 15));
-}
-// h_block_exp of m >= 0 given as its bits (no branches): 0 when m is 0,
-// in [2^-10, 2^15) or NaN; 127 above 3e38; else the frexp exponent (biased
-// exponent - 126; subnormals land below -128) less 15, clamped.
-__device__ __forceinline__ int h_block_exp_bits(uint32_t u) {
-  const bool keep = u == 0u || u - 0x3A800000u < 0x47000000u - 0x3A800000u || u > 0x7F800000u;
-  const int e = max(-128, min(127, (int)(u >> 23) - 141));
-  return keep ? 0 : u > 0x7F61B1E6u ? 127 : e;
 }
 // The largest v over each 16-lane DPP row (four row rotations; every lane
 // of the row gets it, so all 16 lanes must be active).
