@@ -4,6 +4,8 @@
 // with routing.  Device code only; included by build_blocks.hip and
 // route.hip.
 #pragma once
+#include <type_traits>
+
 #include "internal.h"
 
 namespace moe {
@@ -41,31 +43,53 @@ __device__ __forceinline__ void scan_scatter_chunk(
   __shared__ int wnext[kScanWaves][256];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int e = tid;
+  // The chunk's pairs, one contiguous segment per wave, read first: their
+  // loads and the histogram loads below share one round trip, and the
+  // counting and ranking passes both use the ids held in registers (the
+  // first kIdRounds rounds of 64; longer segments read the rest in place).
+  constexpr int kIdRounds = 4;
+  const int p0 = c * chunk_pairs;
+  const int p1 = min(P, p0 + chunk_pairs);
+  const int q = (((p1 - p0) + 64 * kScanWaves - 1) / (64 * kScanWaves)) * 64;
+  const int w0 = min(p1, p0 + wave * q), w1 = min(p1, w0 + q);
+  int idr[kIdRounds];
+#pragma unroll
+  for (int r = 0; r < kIdRounds; r++) {
+    const int p = w0 + 64 * r + lane;
+    idr[r] = p < w1 ? ids[p] : -1;
+  }
   int first = 0;  // first slot of this chunk's pairs of expert e
   if (chunk_start) {
     if (e < E) first = chunk_start[(size_t)c * E + e];
   } else {
   // ---- per expert: histogram rows of the chunks before this one, and of
-  // all chunks.  Thread (g, e) sums chunks g, g + G, ... (8 loads in flight).
+  // all chunks.  Thread (g, e) sums chunks g, g + G, ...; the U loads of a
+  // batch are issued together (indexes clamped, so no load sits behind a
+  // branch), U the smallest of 8, 16, 32, 64 that covers every chunk in one
+  // batch (batches of 64 beyond).
   {
     const int G = kScanThreads / E;
     const int e = tid % E, g = tid / E;
     int pre = 0, tot = 0;
-    if (g < G) {
-      constexpr int U = 8;
+    auto sums = [&](auto utag) {
+      constexpr int U = decltype(utag)::value;
       for (int cc0 = g; cc0 < nchunks; cc0 += G * U) {
         int v[U];
 #pragma unroll
-        for (int u = 0; u < U; u++) {
-          const int cc = cc0 + u * G;
-          v[u] = cc < nchunks ? chunk_hist[(size_t)cc * E + e] : 0;
-        }
+        for (int u = 0; u < U; u++) v[u] = chunk_hist[(size_t)min(cc0 + u * G, nchunks - 1) * E + e];
 #pragma unroll
         for (int u = 0; u < U; u++) {
-          tot += v[u];
-          pre += cc0 + u * G < c ? v[u] : 0;
+          const int cc = cc0 + u * G;
+          tot += cc < nchunks ? v[u] : 0;
+          pre += cc < c ? v[u] : 0;
         }
       }
+    };
+    if (g < G) {
+      if (nchunks <= 8 * G) sums(std::integral_constant<int, 8>{});
+      else if (nchunks <= 16 * G) sums(std::integral_constant<int, 16>{});
+      else if (nchunks <= 32 * G) sums(std::integral_constant<int, 32>{});
+      else sums(std::integral_constant<int, 64>{});
     }
     spre[tid] = pre;
     stot[tid] = tot;
@@ -102,17 +126,16 @@ __device__ __forceinline__ void scan_scatter_chunk(
   first = off + pre;
   }
 
-  // ---- the chunk's pairs in one contiguous segment per wave
-  const int p0 = c * chunk_pairs;
-  const int p1 = min(P, p0 + chunk_pairs);
-  const int q = (((p1 - p0) + 64 * kScanWaves - 1) / (64 * kScanWaves)) * 64;
-  const int w0 = min(p1, p0 + wave * q), w1 = min(p1, w0 + q);
+  // ---- the chunk's pairs: counts per wave, then ranks
   for (int i = lane; i < E; i += 64) wnext[wave][i] = 0;
   __syncthreads();
-  for (int p = w0 + lane; p < w1; p += 64) {
-    const int id = ids[p];
-    if (id >= 0 && id < E) atomicAdd(&wnext[wave][id], 1);
-  }
+  auto count = [&](int p, int id) {
+    if (p < w1 && id >= 0 && id < E) atomicAdd(&wnext[wave][id], 1);
+  };
+#pragma unroll
+  for (int r = 0; r < kIdRounds; r++)
+    if (w0 + 64 * r < w1) count(w0 + 64 * r + lane, idr[r]);  // (uniform test)
+  for (int p = w0 + 64 * kIdRounds + lane; p - lane < w1; p += 64) count(p, p < w1 ? ids[p] : -1);
   __syncthreads();
   if (e < E) {
     int run = first;
@@ -128,10 +151,8 @@ __device__ __forceinline__ void scan_scatter_chunk(
   int bits = 1;
   while ((1 << bits) < E) bits++;
   int* next = wnext[wave];
-  for (int base = w0; base < w1; base += 64) {
-    const int p = base + lane;
-    const int id = p < w1 ? ids[p] : -1;
-    const bool active = id >= 0 && id < E;
+  auto rank = [&](int p, int id) {
+    const bool active = p < w1 && id >= 0 && id < E;
     const int ex = active ? id : 0;
     uint64_t match = __ballot(active);
     for (int b = 0; b < bits; b++) {
@@ -140,17 +161,21 @@ __device__ __forceinline__ void scan_scatter_chunk(
       match &= bit ? bal : ~bal;
     }
     const uint64_t below = match & ((1ull << lane) - 1ull);
-    const int rank = __popcll(below);
+    const int rk = __popcll(below);
     const int start = active ? next[ex] : 0;
     wave_lds_sync();
     if (active) {
-      const int slot = start + rank;
+      const int slot = start + rk;
       sorted_pairs[slot] = p;
       pair_slot[p] = slot;
       if (below == 0) next[ex] = start + __popcll(match);  // lowest lane of its group
     }
     wave_lds_sync();
-  }
+  };
+#pragma unroll
+  for (int r = 0; r < kIdRounds; r++)
+    if (w0 + 64 * r < w1) rank(w0 + 64 * r + lane, idr[r]);  // (uniform test)
+  for (int p = w0 + 64 * kIdRounds + lane; p - lane < w1; p += 64) rank(p, p < w1 ? ids[p] : -1);
 }
 
 
