@@ -593,31 +593,40 @@ __device__ void load_logits(const RouteParams& p, int t0, int nt, float* lg, int
   const int n = nt * p.E;
   const size_t part = (size_t)p.T * p.E;
   const float* src = p.logits + (size_t)t0 * p.E;
-  constexpr int U = 8;
-  for (int i0 = tid; i0 < n; i0 += nth * U) {
-    // every partial of the batch is loaded before the first add (one round
-    // trip); at most kMaxSplit ranges
-    float v[kMaxSplit][U];
+  // U values per thread and range in one batch: the smallest of 1, 2, 4, 8
+  // that covers the pass (batches of 8 beyond), so no thread issues loads
+  // past the pass's last value
+  auto batches = [&](auto utag) {
+    constexpr int U = decltype(utag)::value;
+    for (int i0 = tid; i0 < n; i0 += nth * U) {
+      // every partial of the batch is loaded before the first add (one round
+      // trip); at most kMaxSplit ranges
+      float v[kMaxSplit][U];
 #pragma unroll
-    for (int z = 0; z < kMaxSplit; z++)
-      if (z < p.ksplit)
+      for (int z = 0; z < kMaxSplit; z++)
+        if (z < p.ksplit)
 #pragma unroll
-        for (int u = 0; u < U; u++) v[z][u] = src[z * part + min(i0 + u * nth, n - 1)];
+          for (int u = 0; u < U; u++) v[z][u] = src[z * part + min(i0 + u * nth, n - 1)];
 #pragma unroll
-    for (int z = 1; z < kMaxSplit; z++)
-      if (z < p.ksplit)
+      for (int z = 1; z < kMaxSplit; z++)
+        if (z < p.ksplit)
 #pragma unroll
-        for (int u = 0; u < U; u++) v[0][u] += v[z][u];
+          for (int u = 0; u < U; u++) v[0][u] += v[z][u];
 #pragma unroll
-    for (int u = 0; u < U; u++) {
-      const int i = i0 + u * nth;
-      if (i < n) {
-        const int r = i / p.E;
-        lg[r * stride + (i - r * p.E)] = v[0][u];
-        if (p.ksplit > 1 && !p.scale_logits) p.logits_out[(size_t)t0 * p.E + i] = v[0][u];
+      for (int u = 0; u < U; u++) {
+        const int i = i0 + u * nth;
+        if (i < n) {
+          const int r = i / p.E;
+          lg[r * stride + (i - r * p.E)] = v[0][u];
+          if (p.ksplit > 1 && !p.scale_logits) p.logits_out[(size_t)t0 * p.E + i] = v[0][u];
+        }
       }
     }
-  }
+  };
+  if (n <= nth) batches(std::integral_constant<int, 1>{});
+  else if (n <= 2 * nth) batches(std::integral_constant<int, 2>{});
+  else if (n <= 4 * nth) batches(std::integral_constant<int, 4>{});
+  else batches(std::integral_constant<int, 8>{});
 }
 
 // The pass's logits times each row's 1 / rms, in LDS and to logits_out.
