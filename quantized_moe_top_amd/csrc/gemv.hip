@@ -512,14 +512,21 @@ __device__ __forceinline__ void decode_gate_up_body(const DecRouteParams& r, con
   // 0. the per-expert tables of both banks, the logits and (x_res) the x
   //    rows: every load issued before any is stored (E <= 256, blockDim.x
   //    >= 64, T * K / 8 <= 4 blockDim.x with x_res)
+  // (a wave whose first index is past the end issues no load: the test is
+  // uniform, so it is a scalar branch; indices inside a wave stay clamped)
+  const int wt0 = wave * 64;
+  // (nothing loaded is combined before the stores below, so no branch waits)
   float ua[4], ub[4];
-  uint32_t ga[4];
+  uint32_t ga[4], gb[4];
 #pragma unroll
   for (int i = 0; i < 4; i++) {
     const int x = min(tid + i * (int)blockDim.x, E - 1);
-    ua[i] = p.t0.unscale[x];
-    ub[i] = p.t1.unscale[x];
-    ga[i] = p.t0.general[x] | p.t1.general[x];
+    if (wt0 + i * (int)blockDim.x < E) {
+      ua[i] = p.t0.unscale[x];
+      ub[i] = p.t1.unscale[x];
+      ga[i] = p.t0.general[x];
+      gb[i] = p.t1.general[x];
+    }
   }
   const int c8n = K / 8, nx8 = p.x_res ? T * c8n : 0;
   constexpr bool norm = NORM;  // (with x_res and gamma, checked by the launcher)
@@ -527,9 +534,10 @@ __device__ __forceinline__ void decode_gate_up_body(const DecRouteParams& r, con
 #pragma unroll
   for (int i = 0; i < 4; i++) {
     const int idx = min(tid + i * (int)blockDim.x, max(nx8 - 1, 0));
-    xv[i] = p.x_res ? *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p.a) + 8 * (size_t)idx)
-                    : make_uint4(0, 0, 0, 0);
-    if constexpr (NORM) gv[i] = reinterpret_cast<const uint4*>(p.gamma)[idx % c8n];
+    if (wt0 + i * (int)blockDim.x < nx8) {
+      xv[i] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p.a) + 8 * (size_t)idx);
+      if constexpr (NORM) gv[i] = reinterpret_cast<const uint4*>(p.gamma)[idx % c8n];
+    }
   }
   // 1. logits: partial sums over ranges of H added in range order
   const size_t part = (size_t)T * E;
@@ -544,7 +552,7 @@ __device__ __forceinline__ void decode_gate_up_body(const DecRouteParams& r, con
     if (x < E) {
       us_s[0][x] = ua[i];
       us_s[1][x] = ub[i];
-      gen_s[x] = ga[i] != 0;
+      gen_s[x] = (ga[i] | gb[i]) != 0;
     }
     const int idx = tid + i * blockDim.x;
     if (idx < nx8)  // x row idx / c8n, 8-element chunk idx % c8n (row stride K); raw bf16 with RMSNorm
