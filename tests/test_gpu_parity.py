@@ -200,7 +200,10 @@ def test_router_tiles(orc, T, E, H, k):
 # ------------------------------------------- histogram / scan / scatter ---
 @pytest.mark.parametrize("T,k,E,BM", [(16, 2, 8, 32), (1, 8, 128, 8), (8, 8, 128, 8), (512, 8, 128, 64),
                                       (300, 4, 16, 16), (8192, 8, 128, 128), (2500, 3, 7, 1),
-                                      (1025, 8, 256, 128), (4097, 16, 64, 32)])
+                                      (1025, 8, 256, 128), (4097, 16, 64, 32),
+                                      # chunks of 2,240 and 2,560 pairs: each wave ranks 5 rounds of 64,
+                                      # past the 4 whose ids are read up front
+                                      (70000, 8, 128, 128), (40000, 16, 64, 64)])
 def test_build_blocks(orc, T, k, E, BM):
     g = torch.Generator().manual_seed(T + 7 * E + BM)
     l = torch.randn((T, E), generator=g)
