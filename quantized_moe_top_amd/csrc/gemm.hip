@@ -550,28 +550,30 @@ __global__ __launch_bounds__(64 * WAVES, WGS_PER_CU * WAVES / 4) void w4_mfma_ke
     if (any) p.tflags[tile] = 1;
   } else if constexpr (PACK) {
     // The accumulators go through a wave-private fp32 LDS tile of 32 rows x
-    // 64 columns (one 32-row block at a time) and come back as 4 consecutive
-    // columns of one row per lane: lane l takes row 4k + l / 16 of the block
-    // (k = 0..7) at columns 4 (l % 16) .. + 3 of the wave's 64.  Row pitch 64
-    // words, columns XOR 32 on rows with bit 2 set: the two half-waves of a
-    // column write (rows r and r + 4) fall on disjoint banks, and each
-    // 16-lane row read covers all 64 banks.  The four lanes of one row's
-    // 16-column block are a DPP quad: two quad exchanges give the block's
-    // largest |a w|, hence its exponent; each lane stores its 4 int16
-    // mantissas (16 lanes: 128 contiguous bytes of a row) and the block's
-    // exponent byte (the quad's lanes store the same byte).  The ring is free
-    // once every copy has landed and every wave has finished its MFMAs.
+    // 64 columns (one 32-row block at a time) and come back as 8 consecutive
+    // columns of one row per lane: lane l takes row 8k + l / 8 of the block
+    // (k = 0..3) at columns 8 (l % 8) .. + 7 of the wave's 64.  Row pitch 64
+    // words; a row's columns are XORed with 32 when its bit 2 is set and with
+    // 4 when its bit 0 is, so the two half-waves of a column write (rows r
+    // and r + 4) fall on disjoint banks, and so do the two rows each 16-lane
+    // group of a 16-byte read covers.  The two lanes of one row's 16-column
+    // block exchange their maxima (one DPP step), hence its exponent; each
+    // lane stores its 8 int16 mantissas (8 lanes: 128 contiguous bytes of a
+    // row) and the block's exponent byte (both lanes store the same byte).
+    // The ring is free once every copy has landed and every wave has
+    // finished its MFMAs.
     static_assert(WAVES * 32 * 64 * 4 <= STAGES * STAGE, "epilogue tile must fit the ring");
     wait_vm<0>();
     __syncthreads();
     if (!active) return;
     float* const tile = reinterpret_cast<float*>(lds) + wave * 32 * 64;
-    const int q = lane & 15, rq = lane >> 4;  // column quad, row within 4
+    auto swz = [](int row) { return (row & 4 ? 32 : 0) ^ (row & 1 ? 4 : 0); };
+    const int q = lane & 7, rq = lane >> 3;  // column octet, row within 8
     const size_t mstride = (size_t)N * 2, estride = (size_t)N / 16;
     const int c0 = nb * OUT_COLS + wave * 64;
     // this lane's row rq of the tile: the later rows are uniform offsets from it
-    char* const lane_out = reinterpret_cast<char*>(p.out) + (size_t)(row0 + rq) * mstride + (size_t)(c0 + 4 * q) * 2;
-    int8_t* const lane_exp = p.yexp + (size_t)(row0 + rq) * estride + c0 / 16 + (q >> 2);
+    char* const lane_out = reinterpret_cast<char*>(p.out) + (size_t)(row0 + rq) * mstride + (size_t)(c0 + 8 * q) * 2;
+    int8_t* const lane_exp = p.yexp + (size_t)(row0 + rq) * estride + c0 / 16 + (q >> 1);
     auto block = [&](auto full_tag) {
       constexpr bool FULL = decltype(full_tag)::value != 0;
 #pragma unroll
@@ -583,28 +585,29 @@ __global__ __launch_bounds__(64 * WAVES, WGS_PER_CU * WAVES / 4) void w4_mfma_ke
 #pragma unroll
           for (int r = 0; r < 16; r++) {
             const int row = 8 * (r >> 2) + 4 * khalf + (r & 3);
-            tile[row * 64 + ((cb * 32 + col) ^ (row & 4 ? 32 : 0))] = acc[mb][cb][r];
+            tile[row * 64 + ((cb * 32 + col) ^ swz(row))] = acc[mb][cb][r];
           }
 #pragma unroll
-        for (int k = 0; k < 8; k++) {
-          const int rr = 4 * k + rq;
-          const float4 v = *reinterpret_cast<const float4*>(tile + rr * 64 + ((4 * q) ^ (rr & 4 ? 32 : 0)));
+        for (int k = 0; k < 4; k++) {
+          const int rr = 8 * k + rq;
+          const float4 v0 = *reinterpret_cast<const float4*>(tile + rr * 64 + ((8 * q) ^ swz(rr)));
+          const float4 v1 = *reinterpret_cast<const float4*>(tile + rr * 64 + ((8 * q + 4) ^ swz(rr)));
           const int row = mb * 32 + rr;
           const float w = (scaled ? ldexpf(row_w[row], erow[row]) : row_w[row]) * us0;
           // the block's largest |a|: the bits of non-negative floats order as
-          // unsigned integers, so the quad exchanges take integer maxima
-          float m4;
-          asm("v_max3_f32 %0, |%1|, |%2|, |%3|\n\tv_max_f32 %0, %0, |%4|"
-              : "=&v"(m4) : "v"(v.x), "v"(v.y), "v"(v.z), "v"(v.w));
-          uint32_t m = __float_as_uint(m4);
+          // unsigned integers, so the pair exchange takes an integer maximum
+          float m8;
+          asm("v_max3_f32 %0, |%1|, |%2|, |%3|\n\tv_max3_f32 %0, %0, |%4|, |%5|\n\tv_max3_f32 %0, %0, |%6|, |%7|\n\t"
+              "v_max_f32 %0, %0, |%8|"
+              : "=&v"(m8) : "v"(v0.x), "v"(v0.y), "v"(v0.z), "v"(v0.w), "v"(v1.x), "v"(v1.y), "v"(v1.z), "v"(v1.w));
+          uint32_t m = __float_as_uint(m8);
           m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0xB1, 0xF, 0xF, true));  // quad_perm 1,0,3,2
-          m = max(m, (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x4E, 0xF, 0xF, true));  // quad_perm 2,3,0,1
           const int ex = y16_exp_bits(__uint_as_float(m) * fabsf(w));
           const float ws = ex == -128 ? 0.0f : ldexpf(w, -ex);
-          const uint2 pk = y16_pack4(v.x, v.y, v.z, v.w, ws);
+          const uint2 lo = y16_pack4(v0.x, v0.y, v0.z, v0.w, ws), hi = y16_pack4(v1.x, v1.y, v1.z, v1.w, ws);
           if (FULL || row < rows) {
-            *reinterpret_cast<uint2*>(lane_out + (size_t)(mb * 32 + 4 * k) * mstride) = pk;
-            lane_exp[(size_t)(mb * 32 + 4 * k) * estride] = (int8_t)ex;
+            *reinterpret_cast<uint4*>(lane_out + (size_t)(mb * 32 + 8 * k) * mstride) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+            lane_exp[(size_t)(mb * 32 + 8 * k) * estride] = (int8_t)ex;
           }
         }
       }
