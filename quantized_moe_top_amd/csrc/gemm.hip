@@ -430,22 +430,10 @@ __global__ __launch_bounds__(64 * WAVES, WGS_PER_CU * WAVES / 4) void w4_mfma_ke
 #pragma unroll
         for (int j = 0; j < STAGES - 1; j++) issue(min(j, S - 1), j);
       }
-      if constexpr (STAGES == 2) {
-        // one stage to refill: once every wave is past slab s - 1 its stage
-        // takes slab s + 1 before slab s is waited for, so two slabs are in
-        // flight during that wait (one more barrier per slab)
-        for (int s = 0; s < S; s++) {
-          asm volatile("s_barrier" ::: "memory");
-          issue(min(s + 1, S - 1), (s + 1) % 2);
-          wait_vm_barrier<DA>();
-          compute(s % 2);
-        }
-      } else {
-        for (int s = 0; s < S; s++) {
-          wait_vm_barrier<(STAGES - 2) * DA>();
-          issue(min(s + STAGES - 1, S - 1), (s + STAGES - 1) % STAGES);
-          compute(s % STAGES);
-        }
+      for (int s = 0; s < S; s++) {
+        wait_vm_barrier<(STAGES - 2) * DA>();
+        issue(min(s + STAGES - 1, S - 1), (s + STAGES - 1) % STAGES);
+        compute(s % STAGES);
       }
     }
   };
