@@ -474,6 +474,33 @@ def test_ffn_decode_edges(orc):
         layer_output_check(orc, lay, y, info)
 
 
+@pytest.mark.parametrize("T", [1, 2, 4, 8])
+def test_ffn_decode_ties(orc, T):
+    """Decode-size routing inside the gate/up launch on logits with exact
+    ties, a row of equal values, signed zeros and -inf entries, at E = 128,
+    256, 5 and k = E = 16: ids bit-exact with the oracle, and ids and weights
+    identical, bit for bit, to moe_route's top-k on the same logits."""
+    import dataclasses
+    for (E, k) in [(128, 8), (256, 16), (5, 3), (16, 16)]:
+        if T * k > 128:
+            continue
+        lay = synth.make_custom(T=T, H=256, I=128, E=E, k=k, G=32, seed=80 + T + E)
+        g = torch.Generator().manual_seed(7 * E + T)
+        l = torch.randn((T, E), generator=g)
+        l[::2, : E // 2] = torch.round(l[::2, : E // 2])       # exact ties, signed zeros
+        l[T - 1, E // 3:] = 0.25                                # equal values
+        if E > k + 4:
+            l[0, k + 1::2] = float("-inf")
+        lay = dataclasses.replace(lay, logits=l)
+        y, info = api.ffn_forward(on_dev(lay), info=True)
+        torch.cuda.synchronize()
+        assert info["path"] == 1
+        layer_output_check(orc, lay, y, info)
+        ids, w, _ = api.route(k, logits=l.to(DEV))
+        assert torch.equal(info["topk_ids"], ids), (E, k)
+        assert torch.equal(info["topk_weights"], w), (E, k)
+
+
 def test_ffn_decode_two_slabs_per_wave(orc):
     """Decode sizes whose down launch takes two slabs per wave (more
     workgroups than three 8-wave ones per CU hold): T = 7 and 8 at H = 2048,
