@@ -186,6 +186,19 @@ __global__ __launch_bounds__(64 * WAVES, WGS_PER_CU * WAVES / 4) void w4_mfma_ke
 #pragma unroll
     for (int a = 0; a < NA; a++) arow[a] = min(max(pr[a], 0), p.P - 1) / p.top_k;
   }
+  // A copies a wave issues for a tile of `rows` rows: instruction j is
+  // needed only while 8 j < rows (with j = wave + WAVES a, the copies of 8-row
+  // groups past the tile are skipped; those LDS rows then hold stale values
+  // whose products land only in rows that are never stored).  Uniform per
+  // wave, so the slab waits below count this wave's own copies.  Only for
+  // tiles of up to 64 rows: at T = 512 a tile's rows are spread around 32
+  // (gate/up -4%, down -3%), while 128-row tiles, nearly all full at the T
+  // that selects them, measured 1-2% slower with the runtime count.
+  auto a_copies = [&](int apw) -> int {
+    if constexpr (HALF_DUP || A_INSTR < WAVES || MB > 2) return apw;
+    const int ng = (rows + 7) >> 3;
+    return min(apw, max(0, (ng - wave + WAVES - 1) / WAVES));
+  };
   const half_t* asrc[NA];
 #pragma unroll
   for (int a = 0; a < NA; a++) asrc[a] = p.a + (size_t)arow[a] * K + 8 * achunk[a];
@@ -271,13 +284,13 @@ __global__ __launch_bounds__(64 * WAVES, WGS_PER_CU * WAVES / 4) void w4_mfma_ke
     constexpr bool PRO = decltype(pro_tag)::value != 0;
     constexpr bool DUP = HALF_DUP && MBA < MB;
     constexpr int APW = DUP ? 1 : A_PER_WAVE * MBA / MB;  // activation copies used (rows < 32 MBA)
-    constexpr int DA = APW + B_PER_WAVE + S_PER_WAVE;
-
+    // this wave's copies per slab: DA = na + B_PER_WAVE + S_PER_WAVE
+    const int na = a_copies(APW);
     auto issue = [&](int s, int stage) {
       char* base = lds + stage * STAGE;
 #pragma unroll
       for (int a = 0; a < APW; a++)
-        lds_load16((DUP ? asrc_h : asrc[a]) + s * kSlabK, base + (DUP ? a_lds_h : a_lds[a]));
+        if (a < na) lds_load16((DUP ? asrc_h : asrc[a]) + s * kSlabK, base + (DUP ? a_lds_h : a_lds[a]));
 #pragma unroll
       for (int b = 0; b < B_PER_WAVE; b++)
         lds_load16(bsrc[b] + s * (DENSE ? 4096 : 1024), base + A_BYTES + 1024 * (B_PER_WAVE * wave + b));
@@ -396,9 +409,9 @@ __global__ __launch_bounds__(64 * WAVES, WGS_PER_CU * WAVES / 4) void w4_mfma_ke
       }
     };
 
-    // slab s lives in stage s % STAGES.  Every slab step issues the same
-    // copies (slabs past the end reload the last slab into a stage that is
-    // never read again), so when slab s is about to be computed exactly the
+    // slab s lives in stage s % STAGES.  Every slab step of a wave issues the
+    // same copies (slabs past the end reload the last slab into a stage that
+    // is never read again), so when slab s is about to be computed exactly the
     // copies of STAGES - 2 later slabs ((STAGES - 2) * DA instructions of this
     // wave) were issued after its own: waiting until at most that many are
     // outstanding means slab s has landed.  Right after the barrier, stage
@@ -431,7 +444,7 @@ __global__ __launch_bounds__(64 * WAVES, WGS_PER_CU * WAVES / 4) void w4_mfma_ke
         for (int j = 0; j < STAGES - 1; j++) issue(min(j, S - 1), j);
       }
       for (int s = 0; s < S; s++) {
-        wait_vm_barrier<(STAGES - 2) * DA>();
+        wait_vm_barrier_n<(STAGES - 2) * (B_PER_WAVE + S_PER_WAVE), STAGES - 2, APW>(na);
         issue(min(s + STAGES - 1, S - 1), (s + STAGES - 1) % STAGES);
         compute(s % STAGES);
       }
@@ -456,13 +469,14 @@ __global__ __launch_bounds__(64 * WAVES, WGS_PER_CU * WAVES / 4) void w4_mfma_ke
     constexpr int MBA = decltype(mba)::value;
     constexpr bool DUP = HALF_DUP && MBA < MB;
     constexpr int APW = DUP ? 1 : A_PER_WAVE * MBA / MB;
+    const int na = a_copies(APW);
 #pragma unroll
     for (int j = 0; j < STAGES - 1; j++) {
       const int s = min(j, slabs - 1);
       char* base = lds + j * STAGE;
 #pragma unroll
       for (int a = 0; a < APW; a++)
-        lds_load16((DUP ? asrc_h : asrc[a]) + s * kSlabK, base + (DUP ? a_lds_h : a_lds[a]));
+        if (a < na) lds_load16((DUP ? asrc_h : asrc[a]) + s * kSlabK, base + (DUP ? a_lds_h : a_lds[a]));
 #pragma unroll
       for (int b = 0; b < B_PER_WAVE; b++)
         lds_load16(bsrc[b] + s * (DENSE ? 4096 : 1024), base + A_BYTES + 1024 * (B_PER_WAVE * wave + b));

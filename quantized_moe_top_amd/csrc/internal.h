@@ -187,6 +187,18 @@ __device__ __forceinline__ void wait_vm_barrier() {
   asm volatile("s_barrier" ::: "memory");
 }
 
+// s_waitcnt vmcnt(BASE + n X), then a workgroup barrier, for a runtime n in
+// [0, K] (n is uniform, so the choice is a scalar branch).
+template <int BASE, int X, int K>
+__device__ __forceinline__ void wait_vm_barrier_n(int n) {
+  if constexpr (K == 0) {
+    wait_vm_barrier<BASE>();
+  } else {
+    if (n >= K) wait_vm_barrier<BASE + K * X>();
+    else wait_vm_barrier_n<BASE, X, K - 1>(n);
+  }
+}
+
 // 16-byte LDS read hidden from the compiler's memory model.  Reading a ring
 // that LDS-DMA copies are still filling, the compiler cannot tell the stages
 // apart and would wait for every copy in flight first; the ring's own

@@ -48,17 +48,6 @@ constexpr int kRouteThreads = 512;
 // its x rows.  The workgroups of expert tile 0 also convert every staged x
 // slab to fp16 in operand order for the grouped GEMM, so x is read from
 // HBM once.
-// s_waitcnt vmcnt(BASE + n X), then a workgroup barrier, for a runtime n in
-// [0, K].
-template <int BASE, int X, int K>
-__device__ __forceinline__ void wait_vm_barrier_n(int n) {
-  if constexpr (K == 0) {
-    wait_vm_barrier<BASE>();
-  } else {
-    if (n >= K) wait_vm_barrier<BASE + K * X>();
-    else wait_vm_barrier_n<BASE, X, K - 1>(n);
-  }
-}
 
 struct RouterParams {
   const uint16_t* x;   // bf16 [T][H]
